@@ -1,0 +1,72 @@
+"""CPU oracle for the quantized matrix-vector product (QMV).
+
+TEST INFRASTRUCTURE ONLY. Nothing in the library's product path imports, calls,
+links or executes anything in this package; only the test suite, the smoke
+check and the benchmark's CPU-baseline leg may use it.
+
+What it computes, in plain fp64 NumPy and from the definitions on the source
+pages (no blocking, fusion or reordering beyond what the definition states):
+
+    y[b, n] = sum_k x[b, k] * dequant(W)[n, k]
+
+Sources (cited by page title and section; every function docstring names the
+passage it follows):
+
+* "wh-iron kernel-op coverage audit", section "Quantization precision
+  coverage": the Track-1 format table (nvfp4 / mxfp4 / mxfp8_e4m3), the rule
+  that sub-byte codes are packed LSB-first, Track 2 (affine w = scale*q + bias),
+  the E2M1 codebook of the fp_quantized_nax row and the E4M3 constants of the
+  kv_cache row of the op-coverage table, and the "Model-format decode" table
+  (NaN sentinel kept explicit; DSv4 mxfp4 = OCP mxfp4).
+* "mlx 1.0.0 - quantized_nax.h": `get_pack_factor` / `get_bytes_per_pack`
+  (packed geometry), `dequantize` and `qdot` (bit masks of every width and the
+  affine dot identity scale*sum(x*q) + bias*sum(x)), `adjust_matrix_offsets`
+  (gather semantics: x row from lhs_indices, weight matrix from rhs_indices).
+* "ml-explore/mlx pull request 4516": the bias term uses sum(x) with every
+  element widened before accumulation; NVFP4 calls carry a global scale.
+* "@lgrammel/ds4-provider - moe.metal": `kernel_mul_mv_id` (the routed expert
+  of each slot picks the weight matrix; no per-expert host dispatch).
+* "ferrum-kernels - primitives.rs" tests: an out-of-range index yields a row
+  of zeros rather than a fault.
+
+Pins that tie this oracle to something other than itself live in
+``tests/test_oracle_pins.py`` (run with ``-m "not gpu"``).
+"""
+
+from .codes import (
+    packed_row_bytes,
+    unpack_codes,
+    pack_codes,
+    storage_to_f64,
+    round_f64_to_bf16_bits,
+    round_f64_to_f16,
+    round_f64_to_f32,
+    round_f64_to,
+    ulp_of,
+)
+from .formats import (
+    e2m1_value,
+    e4m3_value,
+    e8m0_value,
+    e4m3_encode_nearest,
+)
+from .qmv import (
+    dequant_affine,
+    dequant_mxfp4,
+    dequant_nvfp4,
+    dequant_mxfp8,
+    dequant,
+    qmv,
+    qmv_rows,
+    gather_qmv,
+    abs_dot,
+)
+
+__all__ = [
+    "packed_row_bytes", "unpack_codes", "pack_codes", "storage_to_f64",
+    "round_f64_to_bf16_bits", "round_f64_to_f16", "round_f64_to_f32",
+    "round_f64_to", "ulp_of",
+    "e2m1_value", "e4m3_value", "e8m0_value", "e4m3_encode_nearest",
+    "dequant_affine", "dequant_mxfp4", "dequant_nvfp4", "dequant_mxfp8",
+    "dequant", "qmv", "qmv_rows", "gather_qmv", "abs_dot",
+]

@@ -1,0 +1,315 @@
+"""Seeded synthetic inputs for the QMV workloads (NumPy, host memory).
+
+Shared by the tests, the benchmark and the smoke check. This module holds no
+part of the product's arithmetic: it draws random bytes and values and stores
+them in the input dtypes, nothing more. Packed weight codes are drawn as
+uniform random bytes, which makes every code of any width 2..8 uniform over
+{0 .. 2^b - 1} without any packing step (each code is a bit field of a
+uniform random bit stream).
+
+Every draw comes from np.random.default_rng(SeedSequence([cfg_id,
+crc32(case_key)])) in the fixed order codes -> scales -> biases -> x, so a case
+is reproducible from its (cfg_id, key) alone.
+
+Workloads (shapes and value distributions):
+  cfg 1  affine 4-bit, group 64, K=512, N=256, B=1, f32 x ~ N(0,1);
+         q uniform, scales ~ U(0.01, 0.1), bias = -8*scale + U(-0.01, 0.01)
+  cfg 2  affine 8-bit, group 64, K=2560, bf16 x ~ N(0,1), N=2560 plus tails
+         N in {1,3,5,12,17}; norm-preserving scales for a 100-call chain
+  cfg 3  block-scaled, bf16 x ~ N(0,1), K=4096, N=14336, B in {1,4}:
+         MXFP4 (E2M1 codes uniform, E8M0 exponents uniform 120..130),
+         NVFP4 (E4M3 block scales ~ |N(0,1)|, fp32 global scale 0.5),
+         MXFP8 (E4M3 codes uniform over the 254 finite bytes, E8M0 120..130)
+  cfg 4  affine sweep: bits {2,3,4,5,6,8} x group {32,64,128}, K=N=4096,
+         B {1,2,4,8}, x dtype {f32,f16,bf16}; scales ~ U(0.005, 0.05),
+         biases ~ N(0, 0.05)
+  cfg 5  routed MoE: 64 experts, hidden 4096, expert FFN 1536 (gate/up
+         4096->1536, down 1536->4096), MXFP4 and 4-bit affine g64; 16 tokens,
+         top-8 experts per token from N(0,1) router logits; bf16 x
+"""
+
+from __future__ import annotations
+
+import zlib
+from dataclasses import dataclass, field
+
+import numpy as np
+
+DTYPES = ("f32", "f16", "bf16")
+AFFINE_BITS = (2, 3, 4, 5, 6, 8)
+AFFINE_GROUPS = (32, 64, 128)
+
+
+def rng_for(cfg_id: int, case_key: str) -> np.random.Generator:
+    seq = np.random.SeedSequence([int(cfg_id), zlib.crc32(case_key.encode())])
+    return np.random.default_rng(seq)
+
+
+# ---------------------------------------------------------------------------
+# storing drawn fp64 values in the input dtypes
+# ---------------------------------------------------------------------------
+
+def to_storage(v64: np.ndarray, dtype: str) -> np.ndarray:
+    """Store fp64 draws as T. f32 / f16 use NumPy's casts; bf16 is returned as
+    uint16 bit patterns, rounded to nearest-even from the fp32 pattern (these
+    are random inputs, so the path they take to a bf16 value is immaterial)."""
+    v64 = np.asarray(v64, dtype=np.float64)
+    if dtype == "f32":
+        return v64.astype(np.float32)
+    if dtype == "f16":
+        return v64.astype(np.float16)
+    if dtype == "bf16":
+        u = v64.astype(np.float32).view(np.uint32).astype(np.uint64)
+        u = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+        return u.astype(np.uint16)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def storage_nbytes(dtype: str) -> int:
+    return {"f32": 4, "f16": 2, "bf16": 2}[dtype]
+
+
+def _e4m3_byte_for(v: np.ndarray) -> np.ndarray:
+    """Pick the E4M3 byte for non-negative draws v (used only to draw NVFP4
+    block scales): round to nearest-even on the 3-bit-mantissa grid, saturating
+    at 448; draws below 2^-10 become 0."""
+    v = np.asarray(v, dtype=np.float64)
+    out = np.zeros(v.shape, dtype=np.uint8)
+    big = v >= 448.0
+    sub = (v < 2.0 ** -6) & ~big
+    nrm = ~big & ~sub
+    out[big] = 0x7E
+    out[sub] = np.rint(v[sub] * 2.0 ** 9).astype(np.uint8)      # 0..8 (8 = 2^-6)
+    _, ex = np.frexp(v[nrm])
+    e = ex.astype(np.int64) - 1
+    m = np.rint((v[nrm] / np.ldexp(1.0, e.astype(np.int32)) - 1.0) * 8.0).astype(np.int64)
+    e = np.where(m == 8, e + 1, e)
+    m = np.where(m == 8, 0, m)
+    code = np.minimum(((e + 7) << 3) | m, 0x7E)
+    out[nrm] = code.astype(np.uint8)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# case containers
+# ---------------------------------------------------------------------------
+
+@dataclass
+class QmvCase:
+    """One QMV problem in host memory. `fmt` is 'affine' | 'mxfp4' | 'nvfp4' |
+    'mxfp8'; `x` [B, K] and affine `scales`/`biases` are stored in `dtype`;
+    block scales are uint8; `global_scale` is a Python float or None."""
+    fmt: str
+    dtype: str
+    B: int
+    K: int
+    N: int
+    w: np.ndarray
+    scales: np.ndarray
+    x: np.ndarray
+    biases: np.ndarray | None = None
+    bits: int = 4
+    group: int = 32
+    global_scale: float | None = None
+    key: str = ""
+    meta: dict = field(default_factory=dict)
+
+    def algorithmic_bytes(self) -> int:
+        """Bytes one call must move: packed weights + scales (+ biases) + x
+        read + y written."""
+        t = storage_nbytes(self.dtype)
+        n = self.w.nbytes + self.scales.nbytes
+        if self.biases is not None:
+            n += self.biases.nbytes
+        return n + self.B * self.K * t + self.B * self.N * t
+
+
+def affine_case(cfg_id: int, key: str, *, bits: int, group: int, K: int, N: int, B: int,
+                dtype: str, scale_range=(0.005, 0.05), bias_mode: str = "normal",
+                bias_sigma: float = 0.05) -> QmvCase:
+    """Affine problem. bias_mode: 'normal' (biases ~ N(0, bias_sigma)),
+    'centred8' (bias = -8*scale + U(-0.01, 0.01), with the stored scale), or
+    'chain' (norm-preserving weights for a dependent chain: scale = s0*U(0.5,
+    1.5), bias = -127.5*scale + scale*U(-0.5, 0.5), s0 = 1/(73.9*sqrt(K)))."""
+    rng = rng_for(cfg_id, key)
+    w = rng.integers(0, 256, size=(N, K * bits // 8), dtype=np.uint8)
+    G = K // group
+    if bias_mode == "chain":
+        s0 = 1.0 / (73.9 * np.sqrt(K))
+        s64 = s0 * rng.uniform(0.5, 1.5, size=(N, G))
+    else:
+        s64 = rng.uniform(scale_range[0], scale_range[1], size=(N, G))
+    scales = to_storage(s64, dtype)
+    if bias_mode == "normal":
+        b64 = rng.normal(0.0, bias_sigma, size=(N, G))
+    elif bias_mode == "centred8":
+        s_stored = _stored_f64(scales, dtype)
+        b64 = -8.0 * s_stored + rng.uniform(-0.01, 0.01, size=(N, G))
+    elif bias_mode == "chain":
+        s_stored = _stored_f64(scales, dtype)
+        b64 = -127.5 * s_stored + s_stored * rng.uniform(-0.5, 0.5, size=(N, G))
+    else:
+        raise ValueError(bias_mode)
+    biases = to_storage(b64, dtype)
+    x = to_storage(rng.normal(0.0, 1.0, size=(B, K)), dtype)
+    return QmvCase("affine", dtype, B, K, N, w, scales, x, biases=biases, bits=bits,
+                   group=group, key=key)
+
+
+def _stored_f64(a: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return (a.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def mxfp4_case(cfg_id: int, key: str, *, K: int, N: int, B: int, dtype: str = "bf16",
+               exp_range=(120, 130)) -> QmvCase:
+    rng = rng_for(cfg_id, key)
+    w = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(exp_range[0], exp_range[1] + 1, size=(N, K // 32), dtype=np.uint8)
+    x = to_storage(rng.normal(0.0, 1.0, size=(B, K)), dtype)
+    return QmvCase("mxfp4", dtype, B, K, N, w, scales, x, key=key)
+
+
+def nvfp4_case(cfg_id: int, key: str, *, K: int, N: int, B: int, dtype: str = "bf16",
+               global_scale: float | None = 0.5) -> QmvCase:
+    rng = rng_for(cfg_id, key)
+    w = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = _e4m3_byte_for(np.abs(rng.normal(0.0, 1.0, size=(N, K // 16))))
+    x = to_storage(rng.normal(0.0, 1.0, size=(B, K)), dtype)
+    return QmvCase("nvfp4", dtype, B, K, N, w, scales, x, global_scale=global_scale, key=key)
+
+
+def mxfp8_case(cfg_id: int, key: str, *, K: int, N: int, B: int, dtype: str = "bf16",
+               exp_range=(120, 130)) -> QmvCase:
+    rng = rng_for(cfg_id, key)
+    # uniform over the 254 finite E4M3 bytes: skip 0x7F and 0xFF
+    r = rng.integers(0, 254, size=(N, K), dtype=np.int64)
+    w = (r + (r >= 0x7F)).astype(np.uint8)
+    scales = rng.integers(exp_range[0], exp_range[1] + 1, size=(N, K // 32), dtype=np.uint8)
+    x = to_storage(rng.normal(0.0, 1.0, size=(B, K)), dtype)
+    return QmvCase("mxfp8", dtype, B, K, N, w, scales, x, key=key)
+
+
+# ---------------------------------------------------------------------------
+# the five workloads
+# ---------------------------------------------------------------------------
+
+def config1() -> QmvCase:
+    return affine_case(1, "c1", bits=4, group=64, K=512, N=256, B=1, dtype="f32",
+                       scale_range=(0.01, 0.1), bias_mode="centred8")
+
+
+C2_TAILS = (1, 3, 5, 12, 17)
+
+
+def config2(N: int = 2560) -> QmvCase:
+    return affine_case(2, f"c2-N{N}", bits=8, group=64, K=2560, N=N, B=1, dtype="bf16",
+                       bias_mode="chain")
+
+
+def config3(fmt: str, B: int, K: int = 4096, N: int = 14336) -> QmvCase:
+    key = f"c3-{fmt}-B{B}"
+    if fmt == "mxfp4":
+        return mxfp4_case(3, key, K=K, N=N, B=B)
+    if fmt == "nvfp4":
+        return nvfp4_case(3, key, K=K, N=N, B=B, global_scale=0.5)
+    if fmt == "mxfp8":
+        return mxfp8_case(3, key, K=K, N=N, B=B)
+    raise ValueError(fmt)
+
+
+def config4(bits: int, group: int, B: int, dtype: str, K: int = 4096, N: int = 4096) -> QmvCase:
+    return affine_case(4, f"c4-b{bits}-g{group}-B{B}-{dtype}", bits=bits, group=group, K=K,
+                       N=N, B=B, dtype=dtype)
+
+
+@dataclass
+class MoeCase:
+    """Routed-MoE gathered QMV inputs for one projection. Weights are
+    expert-stacked: w [E, N, row_bytes], scales [E, N, K/block] (+ biases)."""
+    fmt: str
+    dtype: str
+    E: int
+    K: int
+    N: int
+    w: np.ndarray
+    scales: np.ndarray
+    x: np.ndarray                 # [n_x_rows, K]
+    lhs: np.ndarray               # [n_slots] uint32: x row per slot
+    rhs: np.ndarray               # [n_slots] uint32: expert per slot
+    biases: np.ndarray | None = None
+    bits: int = 4
+    group: int = 64
+    key: str = ""
+
+    def expert_case(self, e: int) -> QmvCase:
+        """Expert e's matrix as a QMV problem with x rows all of x."""
+        return QmvCase(self.fmt, self.dtype, self.x.shape[0], self.K, self.N, self.w[e],
+                       self.scales[e], self.x,
+                       biases=None if self.biases is None else self.biases[e],
+                       bits=self.bits, group=self.group, key=f"{self.key}-e{e}")
+
+    def distinct_experts(self) -> np.ndarray:
+        r = self.rhs.astype(np.int64)
+        return np.unique(r[(r >= 0) & (r < self.E)])
+
+    def algorithmic_bytes(self) -> int:
+        """Weights of the distinct experts used (each read once) + x rows read
+        per slot + y written + both index arrays."""
+        t = storage_nbytes(self.dtype)
+        d = len(self.distinct_experts())
+        per = self.w[0].nbytes + self.scales[0].nbytes
+        if self.biases is not None:
+            per += self.biases[0].nbytes
+        ns = self.lhs.shape[0]
+        return d * per + ns * self.K * t + ns * self.N * t + 8 * ns
+
+
+def route_topk(logits: np.ndarray, k: int) -> np.ndarray:
+    """Top-k expert ids per token by descending logit (softmax is monotone, so
+    ranking the logits ranks the router probabilities); ties go to the lower
+    expert index. Returns [tokens, k] int64."""
+    order = np.argsort(-logits, axis=1, kind="stable")
+    return order[:, :k]
+
+
+def config5(fmt: str, proj: str, *, E: int = 64, hidden: int = 4096, ffn: int = 1536,
+            tokens: int = 16, top_k: int = 8, dtype: str = "bf16") -> MoeCase:
+    """proj 'gate_up': K=hidden, N=ffn, x = token activations [tokens, hidden],
+    slot s = (token s // top_k, its (s % top_k)-th expert). proj 'down':
+    K=ffn, N=hidden, x = per-slot hidden states [tokens*top_k, ffn] ~ N(0,1),
+    lhs[s] = s. The routing (router logits ~ N(0,1), top_k) is drawn from its
+    own stream so both projections share it."""
+    route_rng = rng_for(5, "c5-router")
+    logits = route_rng.normal(0.0, 1.0, size=(tokens, E))
+    experts = route_topk(logits, top_k)                      # [tokens, top_k]
+    rhs = experts.reshape(-1).astype(np.uint32)
+    n_slots = tokens * top_k
+    if proj == "gate_up":
+        K, N = hidden, ffn
+        lhs = (np.arange(n_slots) // top_k).astype(np.uint32)
+        n_x = tokens
+    elif proj == "down":
+        K, N = ffn, hidden
+        lhs = np.arange(n_slots, dtype=np.uint32)
+        n_x = n_slots
+    else:
+        raise ValueError(proj)
+    key = f"c5-{fmt}-{proj}"
+    rng = rng_for(5, key)
+    if fmt == "mxfp4":
+        w = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+        scales = rng.integers(120, 131, size=(E, N, K // 32), dtype=np.uint8)
+        biases = None
+        bits, group = 4, 32
+    elif fmt == "affine":
+        bits, group = 4, 64
+        w = rng.integers(0, 256, size=(E, N, K * bits // 8), dtype=np.uint8)
+        scales = to_storage(rng.uniform(0.005, 0.05, size=(E, N, K // group)), dtype)
+        biases = to_storage(rng.normal(0.0, 0.05, size=(E, N, K // group)), dtype)
+    else:
+        raise ValueError(fmt)
+    x = to_storage(rng.normal(0.0, 1.0, size=(n_x, K)), dtype)
+    return MoeCase(fmt, dtype, E, K, N, w, scales, x, lhs, rhs, biases=biases, bits=bits,
+                   group=group, key=key)
