@@ -1,0 +1,272 @@
+"""Benchmark of the quantized matrix-vector product on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline workload: MXFP4 QMV, batch 1, K=4096, N=14336, bf16 activations.
+A step is one call of the library's entry point (host validation + launch +
+kernel). Weights are cold: each step reads a different one of >= 1 GiB of
+resident weight copies, so nothing is served from the 256 MB Infinity Cache.
+
+Printed: one JSON line with the headline metric, the roofline of the kernel
+(algorithmic bytes / HIP-event kernel time vs 8 TB/s), the oracle timed on the
+host (cpu_baseline) and the other K=4096 batch-1 cases for context.
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+METRIC = "QMV µs/call + achieved HBM GB/s (% of peak), batch 1, K=4096"
+
+
+def _dev(a, dtype=None):
+    import torch
+    a = np.ascontiguousarray(a)
+    if dtype == "bf16":
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    return torch.from_numpy(a).to("cuda:0")
+
+
+class Runner:
+    """Pre-marshalled calls of one case over rotating weight copies."""
+
+    def __init__(self, bmv, case, min_bytes: int = 1 << 30):
+        import torch
+        self.case = case
+        self.lib = bmv.load()
+        self.x = _dev(case.x, case.dtype)
+        w0 = _dev(case.w)
+        s0 = _dev(case.scales, case.dtype if case.fmt == "affine" else None)
+        b0 = _dev(case.biases, case.dtype) if case.biases is not None else None
+        per = w0.nbytes + s0.nbytes + (b0.nbytes if b0 is not None else 0)
+        self.copies = max(2, -(-min_bytes // per))
+        self.w = [w0] + [w0.clone() for _ in range(self.copies - 1)]
+        self.s = [s0] + [s0.clone() for _ in range(self.copies - 1)]
+        self.b = None if b0 is None else [b0] + [b0.clone() for _ in range(self.copies - 1)]
+        self.g = (torch.tensor([case.global_scale], dtype=torch.float32, device="cuda:0")
+                  if case.fmt == "nvfp4" and case.global_scale is not None else None)
+        self.y = torch.empty((case.B, case.N), dtype=self.x.dtype, device="cuda:0")
+        self.dt = {"f32": 0, "f16": 1, "bf16": 2}[case.dtype]
+        vp = ctypes.c_void_p
+        self.args = []
+        for i in range(self.copies):
+            common = (vp(self.x.data_ptr()), vp(self.w[i].data_ptr()), vp(self.s[i].data_ptr()))
+            if case.fmt == "affine":
+                self.args.append(common + (vp(self.b[i].data_ptr()), case.bits, case.group,
+                                           vp(self.y.data_ptr())))
+            elif case.fmt == "nvfp4":
+                self.args.append(common + (vp(self.g.data_ptr()) if self.g is not None else None,
+                                           vp(self.y.data_ptr())))
+            else:
+                self.args.append(common + (vp(self.y.data_ptr()),))
+        self.fn = {"affine": self.lib.qmv_affine, "mxfp4": self.lib.qmv_fp_mxfp4,
+                   "nvfp4": self.lib.qmv_fp_nvfp4, "mxfp8": self.lib.qmv_fp_mxfp8}[case.fmt]
+        self.bytes = case.algorithmic_bytes()
+
+    def call(self, i: int, stream) -> None:
+        c = self.case
+        st = self.fn(stream, self.dt, c.B, c.K, c.N, *self.args[i % self.copies])
+        if st != 0:
+            raise RuntimeError(self.lib.qmv_last_error().decode())
+
+    def free(self):
+        self.w = self.s = self.b = None
+
+
+def time_case(runner: Runner, steps: int, warmup: int) -> dict:
+    import torch
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    for i in range(warmup):
+        runner.call(i, sp)
+    torch.cuda.synchronize()
+
+    # (1) whole-job rate: `steps` back-to-back launches, plain stream order
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        runner.call(i, sp)
+    t1.record()
+    torch.cuda.synchronize()
+    wall_us = t0.elapsed_time(t1) * 1e3 / steps
+
+    # (2) the same launches captured once in a HIP graph and replayed
+    g = torch.cuda.CUDAGraph()
+    n_cap = min(steps, 256)
+    cap_stream = torch.cuda.Stream()
+    cap_stream.wait_stream(stream)
+    with torch.cuda.graph(g, stream=cap_stream):
+        csp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for i in range(n_cap):
+            runner.call(i, csp)
+    torch.cuda.synchronize()
+    reps = max(1, steps // n_cap)
+    g.replay()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    graph_us = t0.elapsed_time(t1) * 1e3 / (reps * n_cap)
+
+    # (3) kernel time: an event pair around each launch, on the launch stream
+    n_ev = min(steps, 500)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_ev)]
+    for i in range(n_ev):
+        ev[i][0].record()
+        runner.call(i, sp)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    dev = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
+    dev_us = float(np.mean(dev))
+    del g
+    return {
+        "bytes": runner.bytes,
+        "us_per_call": wall_us,
+        "us_per_call_graph": graph_us,
+        "kernel_us_mean": dev_us,
+        "kernel_us_p10": float(np.percentile(dev, 10)),
+        "kernel_us_p50": float(np.percentile(dev, 50)),
+        "kernel_us_p90": float(np.percentile(dev, 90)),
+        "gbps_kernel": runner.bytes / dev_us / 1e3,
+        "gbps_wall": runner.bytes / wall_us / 1e3,
+        "gbps_graph": runner.bytes / graph_us / 1e3,
+        "copies": runner.copies,
+    }
+
+
+def check_once(bmv, case) -> None:
+    """The timed entry point gives the oracle's answer on sampled rows."""
+    import oracle
+    import torch
+    x = _dev(case.x, case.dtype)
+    w = _dev(case.w)
+    s = _dev(case.scales)
+    y = bmv.qmv_fp_mxfp4(x, w, s)
+    rows = np.arange(0, case.N, 97)
+    got = oracle.storage_to_f64(y.cpu().view(torch.int16).numpy().view(np.uint16)[:, rows], "bf16")
+    want = oracle.qmv_rows("mxfp4", case.x, "bf16", case.K, rows, case.w, case.scales)
+    rel = np.max(np.abs(got - want)) / np.max(np.abs(want))
+    if not rel < 2 ** -7:
+        raise RuntimeError(f"bench case disagrees with the oracle (rel {rel:.3g})")
+
+
+def cpu_baseline(case, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle on the host: whole calls of the headline case (decode
+    every weight row to fp64, then the product), single-threaded, repeated
+    until `budget_s` seconds have passed."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # pragma: no cover
+        threadpool_limits = None
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    calls = 0
+    t0 = time.perf_counter()
+    try:
+        while True:
+            for r0 in range(0, case.N, 2048):
+                rows = np.arange(r0, min(case.N, r0 + 2048))
+                oracle.qmv_rows(case.fmt, case.x, case.dtype, case.K, rows, case.w, case.scales,
+                                case.biases, bits=case.bits, group=case.group,
+                                global_scale=case.global_scale)
+            calls += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    el = time.perf_counter() - t0
+    return {"value": round(case.algorithmic_bytes() * calls / el / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{calls} whole calls of the headline case ({case.N} rows x K={case.K}), "
+                      f"{el:.1f} s, {el / calls * 1e6:.0f} us/call"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the QMV path here has "
+              "no multi-GPU mode", file=sys.stderr)
+        return 2
+
+    import torch
+    import bit_matrix_vector_amd as bmv
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    bmv.load()
+    head = workloads.config3("mxfp4", 1)
+    check_once(bmv, head)
+    runner = Runner(bmv, head)
+    res = time_case(runner, args.steps, args.warmup)
+    runner.free()
+    print(f"[bench] headline mxfp4 B1: {json.dumps(res)}", file=sys.stderr, flush=True)
+
+    cases = []
+    if not args.headline_only:
+        for name, c in (("nvfp4 B1 K4096 N14336 bf16", workloads.config3("nvfp4", 1)),
+                        ("mxfp8 B1 K4096 N14336 bf16", workloads.config3("mxfp8", 1)),
+                        ("affine 4b g64 B1 K4096 N4096 bf16", workloads.config4(4, 64, 1, "bf16")),
+                        ("mxfp4 B4 K4096 N14336 bf16", workloads.config3("mxfp4", 4))):
+            r = Runner(bmv, c)
+            cr = time_case(r, max(200, args.steps // 4), args.warmup)
+            r.free()
+            cr["case"] = name
+            cr["pct_peak_kernel"] = round(100 * cr["gbps_kernel"] / PEAK_HBM_GBPS, 1)
+            cases.append(cr)
+            print(f"[bench] {name}: {json.dumps(cr)}", file=sys.stderr, flush=True)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline(head)
+    line = {
+        "metric": METRIC,
+        "value": round(res["gbps_graph"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["us_per_call_graph"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4(e2m1,e8m0) x bf16 -> f32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": "MXFP4 QMV, batch 1, K=4096, N=14336, bf16 x/y, cold HBM "
+                               f"({res['copies']} rotating weight copies)",
+                   "B": 1, "K": 4096, "N": 14336, "format": "mxfp4"},
+        "us_per_call": round(res["us_per_call_graph"], 3),
+        "us_per_call_plain_launch": round(res["us_per_call"], 3),
+        "kernel_us": round(res["kernel_us_mean"], 3),
+        "pct_peak": round(100 * res["gbps_graph"] / PEAK_HBM_GBPS, 1),
+        "roofline": {"bound": "hbm", "achieved": round(res["gbps_kernel"], 1),
+                     "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(res["gbps_kernel"] / PEAK_HBM_GBPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "cases": cases,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,303 @@
+"""Python binding of libqmv (the MI355X quantized matrix-vector product).
+
+Argument marshalling only: every function here checks tensor placement and
+contiguity, takes device pointers and the current HIP stream from PyTorch, and
+calls the C ABI of include/qmv.h with the same name. All computation runs in
+the library's HIP kernels (or, for the host codecs, in its C++ code). There is
+no fallback: if libqmv.so is not built, every call raises.
+
+Weight tensors are uint8. x / y / affine scales and biases are torch.float32,
+torch.float16 or torch.bfloat16 and share one dtype.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libqmv.so")
+HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "qmv.h")
+
+QMV_F32, QMV_F16, QMV_BF16 = 0, 1, 2
+QMV_AFFINE, QMV_MXFP4, QMV_NVFP4, QMV_MXFP8 = 0, 1, 2, 3
+FORMATS = {"affine": QMV_AFFINE, "mxfp4": QMV_MXFP4, "nvfp4": QMV_NVFP4, "mxfp8": QMV_MXFP8}
+STATUS = {0: "QMV_OK", 1: "QMV_ERR_INVALID_ARGUMENT", 2: "QMV_ERR_UNSUPPORTED",
+          3: "QMV_ERR_MISALIGNED", 4: "QMV_ERR_HIP"}
+
+
+class QmvError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class QmvWeights(ctypes.Structure):
+    """Mirror of qmv_weights_t."""
+    _fields_ = [
+        ("format", ctypes.c_int), ("bits", ctypes.c_int), ("group_size", ctypes.c_int),
+        ("n_experts", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+        ("w", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+        ("global_scale", ctypes.c_void_p),
+    ]
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libqmv.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"libqmv.so is not built ({LIB_PATH}); run `python -m bit_matrix_vector_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    sig = {
+        "qmv_affine": [vp, i32, i64, i64, i64, vp, vp, vp, vp, i32, i32, vp],
+        "qmv_fp_mxfp4": [vp, i32, i64, i64, i64, vp, vp, vp, vp],
+        "qmv_fp_nvfp4": [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp],
+        "qmv_fp_mxfp8": [vp, i32, i64, i64, i64, vp, vp, vp, vp],
+        "gather_qmv": [vp, i32, ctypes.POINTER(QmvWeights), vp, i64, vp, vp, i64, vp],
+        "qmv_pack_codes": [vp, i64, i64, i32, vp],
+        "qmv_unpack_codes": [vp, i64, i64, i32, vp],
+        "qmv_encode_e4m3": [vp, i64, vp],
+        "qmv_unpack_codes_device": [vp, vp, i64, i64, i32, vp],
+        "qmv_dequant_device": [vp, i32, ctypes.POINTER(QmvWeights), vp],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    lib.qmv_packed_row_bytes.argtypes = [i32, i32, i64]
+    lib.qmv_packed_row_bytes.restype = i64
+    lib.qmv_last_error.argtypes = []
+    lib.qmv_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions include/qmv.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmv_\w+|gather_qmv)\s*\(", text)))
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        msg = load().qmv_last_error().decode(errors="replace")
+        raise QmvError(status, msg)
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    m = {torch.float32: QMV_F32, torch.float16: QMV_F16, torch.bfloat16: QMV_BF16}
+    if t.dtype not in m:
+        raise TypeError(f"activation dtype must be float32/float16/bfloat16, got {t.dtype}")
+    return m[t.dtype]
+
+
+def _dev(t, name: str, dtype=None):
+    torch = _torch()
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _ptr(t):
+    return None if t is None or t.numel() == 0 else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _xy(x, N, y):
+    torch = _torch()
+    x = _dev(x, "x")
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    if x.dim() != 2:
+        raise ValueError("x must be [B, K]")
+    B = x.shape[0]
+    if y is None:
+        y = torch.empty((B, N), dtype=x.dtype, device=x.device)
+    _dev(y, "y", x.dtype)
+    if tuple(y.shape) != (B, N):
+        raise ValueError(f"y must be [{B}, {N}]")
+    return x, y
+
+
+def qmv_affine(x, w, scales, biases, bits: int, group_size: int, y=None):
+    """y[B, N] = x[B, K] . dequant(W)^T for affine codes (see include/qmv.h)."""
+    torch = _torch()
+    _dev(w, "w", torch.uint8)
+    N = w.shape[0]
+    x, y = _xy(x, N, y)
+    _dev(scales, "scales", x.dtype)
+    _dev(biases, "biases", x.dtype)
+    _check(load().qmv_affine(_stream(x.device), _dtype_code(x), x.shape[0], x.shape[1], N,
+                             _ptr(x), _ptr(w), _ptr(scales), _ptr(biases), bits, group_size,
+                             _ptr(y)))
+    return y
+
+
+def qmv_fp_mxfp4(x, w, scales, y=None):
+    torch = _torch()
+    _dev(w, "w", torch.uint8)
+    _dev(scales, "scales", torch.uint8)
+    x, y = _xy(x, w.shape[0], y)
+    _check(load().qmv_fp_mxfp4(_stream(x.device), _dtype_code(x), x.shape[0], x.shape[1],
+                               w.shape[0], _ptr(x), _ptr(w), _ptr(scales), _ptr(y)))
+    return y
+
+
+def qmv_fp_nvfp4(x, w, scales, global_scale=None, y=None):
+    """global_scale: a one-element float32 GPU tensor, or None for 1.0."""
+    torch = _torch()
+    _dev(w, "w", torch.uint8)
+    _dev(scales, "scales", torch.uint8)
+    _dev(global_scale, "global_scale", torch.float32)
+    x, y = _xy(x, w.shape[0], y)
+    _check(load().qmv_fp_nvfp4(_stream(x.device), _dtype_code(x), x.shape[0], x.shape[1],
+                               w.shape[0], _ptr(x), _ptr(w), _ptr(scales), _ptr(global_scale),
+                               _ptr(y)))
+    return y
+
+
+def qmv_fp_mxfp8(x, w, scales, y=None):
+    torch = _torch()
+    _dev(w, "w", torch.uint8)
+    _dev(scales, "scales", torch.uint8)
+    x, y = _xy(x, w.shape[0], y)
+    _check(load().qmv_fp_mxfp8(_stream(x.device), _dtype_code(x), x.shape[0], x.shape[1],
+                               w.shape[0], _ptr(x), _ptr(w), _ptr(scales), _ptr(y)))
+    return y
+
+
+def make_weights(fmt: str, w, scales, biases=None, *, K: int, bits: int = 4,
+                 group_size: int = 32, global_scale=None) -> QmvWeights:
+    """qmv_weights_t for expert-stacked (or single, 2-D) weights. The tensors
+    must stay alive while the struct is in use."""
+    torch = _torch()
+    _dev(w, "w", torch.uint8)
+    n_exp = 1 if w.dim() == 2 else w.shape[0]
+    N = w.shape[-2]
+    return QmvWeights(FORMATS[fmt], bits, group_size, n_exp, N, K,
+                      w.data_ptr() if w.numel() else None,
+                      scales.data_ptr() if scales is not None and scales.numel() else None,
+                      biases.data_ptr() if biases is not None and biases.numel() else None,
+                      global_scale.data_ptr() if global_scale is not None else None)
+
+
+def gather_qmv(x, weights: QmvWeights, lhs_indices, rhs_indices, y=None):
+    """y[s] = W[rhs[s]] . x[lhs[s]] (indices: uint32 stored in int32 tensors)."""
+    torch = _torch()
+    x = _dev(x, "x")
+    _dev(lhs_indices, "lhs_indices", torch.int32)
+    _dev(rhs_indices, "rhs_indices", torch.int32)
+    n_slots = lhs_indices.numel()
+    if rhs_indices.numel() != n_slots:
+        raise ValueError("lhs_indices and rhs_indices differ in length")
+    N = weights.N
+    if y is None:
+        y = torch.empty((n_slots, N), dtype=x.dtype, device=x.device)
+    _dev(y, "y", x.dtype)
+    _check(load().gather_qmv(_stream(x.device), _dtype_code(x), ctypes.byref(weights), _ptr(x),
+                             x.shape[0], _ptr(lhs_indices), _ptr(rhs_indices), n_slots,
+                             _ptr(y)))
+    return y
+
+
+def qmv_unpack_codes_device(packed, K: int, bits: int, codes=None):
+    torch = _torch()
+    _dev(packed, "packed", torch.uint8)
+    rows = packed.shape[0]
+    if codes is None:
+        codes = torch.empty((rows, K), dtype=torch.uint8, device=packed.device)
+    _dev(codes, "codes", torch.uint8)
+    _check(load().qmv_unpack_codes_device(_stream(packed.device), _ptr(packed), rows, K, bits,
+                                          _ptr(codes)))
+    return codes
+
+
+def qmv_dequant_device(weights: QmvWeights, dtype_code: int, device, out=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty((weights.N, weights.K), dtype=torch.float32, device=device)
+    _dev(out, "out", torch.float32)
+    _check(load().qmv_dequant_device(_stream(out.device), dtype_code, ctypes.byref(weights),
+                                     _ptr(out)))
+    return out
+
+
+# ---------------------------------------------------------------------------
+# host codecs (NumPy arrays in host memory)
+# ---------------------------------------------------------------------------
+
+def qmv_packed_row_bytes(fmt: str, bits: int, K: int) -> int:
+    return int(load().qmv_packed_row_bytes(FORMATS[fmt], bits, K))
+
+
+def _np_ptr(a):
+    return ctypes.c_void_p(a.ctypes.data) if a.size else None
+
+
+def qmv_pack_codes(codes, bits: int):
+    import numpy as np
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    rows, K = codes.shape
+    out = np.zeros((rows, K * bits // 8), dtype=np.uint8)
+    _check(load().qmv_pack_codes(_np_ptr(codes), rows, K, bits, _np_ptr(out)))
+    return out
+
+
+def qmv_unpack_codes(packed, K: int, bits: int):
+    import numpy as np
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    rows = packed.shape[0]
+    out = np.zeros((rows, K), dtype=np.uint8)
+    _check(load().qmv_unpack_codes(_np_ptr(packed), rows, K, bits, _np_ptr(out)))
+    return out
+
+
+def qmv_encode_e4m3(v):
+    import numpy as np
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.zeros(v.shape, dtype=np.uint8)
+    _check(load().qmv_encode_e4m3(_np_ptr(v), v.size, _np_ptr(out)))
+    return out
+
+
+__all__ = [
+    "qmv_affine", "qmv_fp_mxfp4", "qmv_fp_nvfp4", "qmv_fp_mxfp8", "gather_qmv",
+    "make_weights", "qmv_unpack_codes_device", "qmv_dequant_device", "qmv_packed_row_bytes",
+    "qmv_pack_codes", "qmv_unpack_codes", "qmv_encode_e4m3", "QmvError", "QmvWeights", "load",
+    "header_functions", "library_path",
+]

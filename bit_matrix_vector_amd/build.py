@@ -1,0 +1,83 @@
+"""Builds the HIP library libqmv.so in-tree for gfx950.
+
+    python -m bit_matrix_vector_amd.build
+
+Compiles the kernel instantiation slices in parallel (one hipcc process per
+(dtype, format family) slice), the dispatch unit, and the host API with g++,
+then links them into bit_matrix_vector_amd/libqmv.so.
+"""
+
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import shutil
+import subprocess
+import sys
+import time
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(PKG, "_build")
+LIB = os.path.join(PKG, "libqmv.so")
+
+ARCH = "gfx950"
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+    # keep hipcc from forming packed fp32 VALU ops
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}",
+]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
+def _jobs() -> list[tuple[list[str], str]]:
+    jobs = []
+    for dt in (0, 1, 2):
+        for fam in (0, 1):
+            obj = os.path.join(BUILD, f"qmv_inst_{dt}_{fam}.o")
+            jobs.append(([HIPCC, *HIP_FLAGS, f"-DQMV_DT={dt}", f"-DQMV_FAM={fam}", "-c",
+                          os.path.join(CSRC, "qmv_inst.hip"), "-o", obj], obj))
+    obj = os.path.join(BUILD, "qmv_dispatch.o")
+    jobs.append(([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "qmv_dispatch.hip"), "-o", obj],
+                 obj))
+    obj = os.path.join(BUILD, "qmv_api.o")
+    jobs.append((["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "qmv_api.cpp"), "-o", obj], obj))
+    return jobs
+
+
+def _run(cmd: list[str]) -> None:
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile everything and link libqmv.so. Always rebuilds. Returns the
+    library path."""
+    if shutil.which(HIPCC) is None and not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    os.makedirs(BUILD, exist_ok=True)
+    t0 = time.time()
+    jobs = _jobs()
+    workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        futs = [ex.submit(_run, cmd) for cmd, _ in jobs]
+        for f in futs:
+            f.result()
+    objs = [o for _, o in jobs]
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    if verbose:
+        print(f"built {LIB} in {time.time() - t0:.1f} s", flush=True)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

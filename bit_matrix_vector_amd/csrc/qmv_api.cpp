@@ -1,0 +1,363 @@
+// Host side of the C ABI declared in include/qmv.h: argument validation,
+// variant selection, error reporting and the host codecs. Validation is pure
+// host code and runs before any HIP call, so a rejected call touches no
+// device state and no output.
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/qmv.h"
+#include "qmv_common.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+qmv_status_t fail(qmv_status_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int dtype_bytes(int dtype) { return dtype == QMV_F32 ? 4 : 2; }
+
+bool valid_bits(int bits) {
+    return bits == 2 || bits == 3 || bits == 4 || bits == 5 || bits == 6 || bits == 8;
+}
+
+qmv_status_t launch_status(int err, const char* what) {
+    if (err == 0) return QMV_OK;
+    return fail(QMV_ERR_HIP, "%s: HIP launch failed: %s", what, qmv::hip_error_string(err));
+}
+
+// Checks shared by every compute call. `block` is the scale block length.
+qmv_status_t check_common(const char* fn, int dtype, int64_t B, int64_t K, int64_t N,
+                          int64_t max_b) {
+    if (dtype != QMV_F32 && dtype != QMV_F16 && dtype != QMV_BF16)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: dtype %d is not QMV_F32/F16/BF16", fn, dtype);
+    if (B < 0 || K < 0 || N < 0)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: negative size (B=%lld K=%lld N=%lld)", fn,
+                    (long long)B, (long long)K, (long long)N);
+    if (B > max_b)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: B=%lld exceeds the decode batch limit %lld", fn,
+                    (long long)B, (long long)max_b);
+    if (K % 32)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: K=%lld is not a multiple of 32", fn,
+                    (long long)K);
+    if (K > (int64_t)1 << 28 || N > (int64_t)1 << 28)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: K or N above 2^28", fn);
+    return QMV_OK;
+}
+
+qmv_status_t check_ptr(const char* fn, const char* name, const void* p, bool needed,
+                       uintptr_t align) {
+    if (!needed) return QMV_OK;
+    if (p == nullptr) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: %s is NULL", fn, name);
+    if (!aligned(p, align))
+        return fail(QMV_ERR_MISALIGNED, "%s: %s is not %u-byte aligned", fn, name,
+                    (unsigned)align);
+    return QMV_OK;
+}
+
+#define QMV_TRY(expr)                         \
+    do {                                      \
+        qmv_status_t _st = (expr);            \
+        if (_st != QMV_OK) return _st;        \
+    } while (0)
+
+// Fill the format-dependent geometry of a launch.
+qmv_status_t format_geometry(const char* fn, int format, int bits, int group, int64_t K,
+                             qmv::LaunchParams& lp) {
+    lp.format = format;
+    switch (format) {
+        case QMV_AFFINE:
+            if (!valid_bits(bits))
+                return fail(QMV_ERR_UNSUPPORTED, "%s: bits=%d not in {2,3,4,5,6,8}", fn, bits);
+            if (group != 32 && group != 64 && group != 128)
+                return fail(QMV_ERR_UNSUPPORTED, "%s: group_size=%d not in {32,64,128}", fn,
+                            group);
+            if (K % group)
+                return fail(QMV_ERR_INVALID_ARGUMENT, "%s: K=%lld not a multiple of group %d",
+                            fn, (long long)K, group);
+            lp.bits = bits;
+            lp.group = group;
+            lp.row_bytes = K * bits / 8;
+            lp.sc_per_row = K / group;
+            return QMV_OK;
+        case QMV_MXFP4:
+            lp.bits = 4; lp.group = 32; lp.row_bytes = K / 2; lp.sc_per_row = K / 32;
+            return QMV_OK;
+        case QMV_NVFP4:
+            lp.bits = 4; lp.group = 16; lp.row_bytes = K / 2; lp.sc_per_row = K / 16;
+            return QMV_OK;
+        case QMV_MXFP8:
+            lp.bits = 8; lp.group = 32; lp.row_bytes = K; lp.sc_per_row = K / 32;
+            return QMV_OK;
+        default:
+            return fail(QMV_ERR_INVALID_ARGUMENT, "%s: unknown format %d", fn, format);
+    }
+}
+
+qmv_status_t run_qmv(const char* fn, void* stream, int dtype, int format, int bits, int group,
+                     int64_t B, int64_t K, int64_t N, const void* x, const uint8_t* w,
+                     const void* scales, const void* biases, const float* gscale, void* y) {
+    QMV_TRY(check_common(fn, dtype, B, K, N, 8));
+    qmv::LaunchParams lp{};
+    lp.dtype = dtype;
+    QMV_TRY(format_geometry(fn, format, bits, group, K, lp));
+    if (B == 0 || N == 0) return QMV_OK;
+    const int tb = dtype_bytes(dtype);
+    const bool has_k = K > 0;
+    QMV_TRY(check_ptr(fn, "y", y, true, tb));
+    QMV_TRY(check_ptr(fn, "x", x, has_k, 16));
+    QMV_TRY(check_ptr(fn, "w", w, has_k, 16));
+    if (format == QMV_AFFINE) {
+        QMV_TRY(check_ptr(fn, "scales", scales, has_k, tb));
+        QMV_TRY(check_ptr(fn, "biases", biases, has_k, tb));
+    } else {
+        QMV_TRY(check_ptr(fn, "scales", scales, has_k, format == QMV_NVFP4 ? 2 : 1));
+    }
+    QMV_TRY(check_ptr(fn, "global_scale", gscale, gscale != nullptr, 4));
+    if (x && y && has_k) {
+        const uintptr_t xs = (uintptr_t)x, xe = xs + (uintptr_t)(B * K * tb);
+        const uintptr_t ys = (uintptr_t)y, ye = ys + (uintptr_t)(B * N * tb);
+        if (xs < ye && ys < xe)
+            return fail(QMV_ERR_INVALID_ARGUMENT, "%s: x and y overlap", fn);
+    }
+    lp.B = B; lp.K = K; lp.N = N;
+    lp.x = x; lp.w = w; lp.scales = scales; lp.biases = biases; lp.gscale = gscale; lp.y = y;
+    return launch_status(qmv::launch_qmv(lp, stream), fn);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qmv_last_error(void) { return g_last_error; }
+
+qmv_status_t qmv_affine(void* stream, int dtype, int64_t B, int64_t K, int64_t N, const void* x,
+                        const uint8_t* w, const void* scales, const void* biases, int bits,
+                        int group_size, void* y) {
+    return run_qmv("qmv_affine", stream, dtype, QMV_AFFINE, bits, group_size, B, K, N, x, w,
+                   scales, biases, nullptr, y);
+}
+
+qmv_status_t qmv_fp_mxfp4(void* stream, int dtype, int64_t B, int64_t K, int64_t N,
+                          const void* x, const uint8_t* w, const uint8_t* scales, void* y) {
+    return run_qmv("qmv_fp_mxfp4", stream, dtype, QMV_MXFP4, 4, 32, B, K, N, x, w, scales,
+                   nullptr, nullptr, y);
+}
+
+qmv_status_t qmv_fp_nvfp4(void* stream, int dtype, int64_t B, int64_t K, int64_t N,
+                          const void* x, const uint8_t* w, const uint8_t* scales,
+                          const float* global_scale, void* y) {
+    return run_qmv("qmv_fp_nvfp4", stream, dtype, QMV_NVFP4, 4, 16, B, K, N, x, w, scales,
+                   nullptr, global_scale, y);
+}
+
+qmv_status_t qmv_fp_mxfp8(void* stream, int dtype, int64_t B, int64_t K, int64_t N,
+                          const void* x, const uint8_t* w, const uint8_t* scales, void* y) {
+    return run_qmv("qmv_fp_mxfp8", stream, dtype, QMV_MXFP8, 8, 32, B, K, N, x, w, scales,
+                   nullptr, nullptr, y);
+}
+
+qmv_status_t gather_qmv(void* stream, int dtype, const qmv_weights_t* wt, const void* x,
+                        int64_t n_x_rows, const uint32_t* lhs_indices,
+                        const uint32_t* rhs_indices, int64_t n_slots, void* y) {
+    const char* fn = "gather_qmv";
+    if (wt == nullptr) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: weights struct is NULL", fn);
+    if (n_slots < 0 || n_x_rows < 0 || wt->n_experts < 0)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: negative count", fn);
+    if (n_slots > ((int64_t)1 << 31) || wt->n_experts > 65534)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: n_slots or n_experts too large", fn);
+    QMV_TRY(check_common(fn, dtype, 1, wt->K, wt->N, 1));
+    qmv::LaunchParams lp{};
+    lp.dtype = dtype;
+    QMV_TRY(format_geometry(fn, wt->format, wt->bits, wt->group_size, wt->K, lp));
+    if (n_slots == 0 || wt->N == 0) return QMV_OK;
+    const int tb = dtype_bytes(dtype);
+    const bool has_w = wt->K > 0 && wt->n_experts > 0;
+    QMV_TRY(check_ptr(fn, "y", y, true, tb));
+    QMV_TRY(check_ptr(fn, "lhs_indices", lhs_indices, true, 4));
+    QMV_TRY(check_ptr(fn, "rhs_indices", rhs_indices, true, 4));
+    QMV_TRY(check_ptr(fn, "x", x, wt->K > 0 && n_x_rows > 0, 16));
+    QMV_TRY(check_ptr(fn, "w", wt->w, has_w, 16));
+    if (wt->format == QMV_AFFINE) {
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, has_w, tb));
+        QMV_TRY(check_ptr(fn, "biases", wt->biases, has_w, tb));
+    } else {
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, has_w, wt->format == QMV_NVFP4 ? 2 : 1));
+    }
+    QMV_TRY(check_ptr(fn, "global_scale", wt->global_scale, wt->global_scale != nullptr, 4));
+    lp.B = 1; lp.K = wt->K; lp.N = wt->N;
+    lp.x = x; lp.w = wt->w; lp.scales = wt->scales; lp.biases = wt->biases;
+    lp.gscale = wt->format == QMV_NVFP4 ? wt->global_scale : nullptr;
+    lp.y = y;
+    lp.n_experts = wt->n_experts; lp.n_x_rows = n_x_rows; lp.n_slots = n_slots;
+    lp.lhs = lhs_indices; lp.rhs = rhs_indices;
+    return launch_status(qmv::launch_gather(lp, stream), fn);
+}
+
+// ------------------------------- codecs ----------------------------------
+
+int64_t qmv_packed_row_bytes(int format, int bits, int64_t K) {
+    if (K < 0) return -1;
+    switch (format) {
+        case QMV_AFFINE:
+            if (!valid_bits(bits) || (K * bits) % 8) return -1;
+            return K * bits / 8;
+        case QMV_MXFP4:
+        case QMV_NVFP4:
+            return K % 2 ? -1 : K / 2;
+        case QMV_MXFP8:
+            return K;
+        default:
+            return -1;
+    }
+}
+
+qmv_status_t qmv_pack_codes(const uint8_t* codes, int64_t rows, int64_t K, int bits,
+                            uint8_t* packed) {
+    const char* fn = "qmv_pack_codes";
+    if (!valid_bits(bits)) return fail(QMV_ERR_UNSUPPORTED, "%s: bits=%d", fn, bits);
+    if (rows < 0 || K < 0 || (K * bits) % 8)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: bad shape rows=%lld K=%lld", fn,
+                    (long long)rows, (long long)K);
+    if (rows * K == 0) return QMV_OK;
+    if (!codes || !packed) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
+    const int64_t rb = K * bits / 8;
+    const uint32_t lim = 1u << bits;
+    for (int64_t i = 0; i < rows * K; ++i)
+        if (codes[i] >= lim)
+            return fail(QMV_ERR_INVALID_ARGUMENT, "%s: code %u at %lld does not fit %d bits", fn,
+                        codes[i], (long long)i, bits);
+    for (int64_t r = 0; r < rows; ++r) {
+        uint8_t* out = packed + r * rb;
+        memset(out, 0, (size_t)rb);
+        const uint8_t* c = codes + r * K;
+        // accumulate codes into a 64-bit window and flush whole bytes
+        uint64_t acc = 0;
+        int nacc = 0;
+        int64_t o = 0;
+        for (int64_t j = 0; j < K; ++j) {
+            acc |= (uint64_t)c[j] << nacc;
+            nacc += bits;
+            while (nacc >= 8) {
+                out[o++] = (uint8_t)(acc & 0xFF);
+                acc >>= 8;
+                nacc -= 8;
+            }
+        }
+    }
+    return QMV_OK;
+}
+
+qmv_status_t qmv_unpack_codes(const uint8_t* packed, int64_t rows, int64_t K, int bits,
+                              uint8_t* codes) {
+    const char* fn = "qmv_unpack_codes";
+    if (!valid_bits(bits)) return fail(QMV_ERR_UNSUPPORTED, "%s: bits=%d", fn, bits);
+    if (rows < 0 || K < 0 || (K * bits) % 8)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: bad shape", fn);
+    if (rows * K == 0) return QMV_OK;
+    if (!codes || !packed) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
+    const int64_t rb = K * bits / 8;
+    const uint32_t mask = (1u << bits) - 1u;
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint8_t* in = packed + r * rb;
+        uint64_t acc = 0;
+        int nacc = 0;
+        int64_t i = 0;
+        for (int64_t j = 0; j < K; ++j) {
+            while (nacc < bits) {
+                acc |= (uint64_t)in[i++] << nacc;
+                nacc += 8;
+            }
+            codes[r * K + j] = (uint8_t)(acc & mask);
+            acc >>= bits;
+            nacc -= bits;
+        }
+    }
+    return QMV_OK;
+}
+
+qmv_status_t qmv_encode_e4m3(const float* v, int64_t n, uint8_t* out) {
+    const char* fn = "qmv_encode_e4m3";
+    if (n < 0) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: n < 0", fn);
+    if (n == 0) return QMV_OK;
+    if (!v || !out) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: NULL buffer", fn);
+    for (int64_t i = 0; i < n; ++i) {
+        const float f = v[i];
+        if (isnan(f)) { out[i] = 0x7F; continue; }
+        const uint8_t sign = signbit(f) ? 0x80 : 0x00;
+        double a = fabs((double)f);
+        if (a >= 448.0) { out[i] = sign | 0x7E; continue; }
+        if (a == 0.0) { out[i] = sign; continue; }
+        // a = m * 2^e with m in [1, 2); values below 2^-6 use the subnormal
+        // spacing 2^-9
+        int e2;
+        frexp(a, &e2);
+        int e = e2 - 1;
+        if (e < -6) e = -6;
+        const double step = ldexp(1.0, e - 3);         // 3 mantissa bits
+        double q = a / step;                           // exact: power-of-two step
+        double r = nearbyint(q);                       // ties to even (default mode)
+        int64_t m = (int64_t)r;                        // 8..16 normal, 0..8 subnormal
+        int code;
+        if (e == -6 && m < 8) {
+            code = (int)m;                             // subnormal: exponent field 0
+        } else {
+            if (m == 16) { m = 8; e += 1; }
+            code = ((e + 7) << 3) | (int)(m - 8);
+        }
+        if (code > 0x7E) code = 0x7E;
+        out[i] = sign | (uint8_t)code;
+    }
+    return QMV_OK;
+}
+
+qmv_status_t qmv_unpack_codes_device(void* stream, const uint8_t* packed, int64_t rows,
+                                     int64_t K, int bits, uint8_t* codes) {
+    const char* fn = "qmv_unpack_codes_device";
+    if (!valid_bits(bits)) return fail(QMV_ERR_UNSUPPORTED, "%s: bits=%d", fn, bits);
+    if (rows < 0 || K < 0 || K % 32)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: rows >= 0 and K %% 32 == 0 required", fn);
+    if (rows * K == 0) return QMV_OK;
+    QMV_TRY(check_ptr(fn, "packed", packed, true, 16));
+    QMV_TRY(check_ptr(fn, "codes", codes, true, 1));
+    return launch_status(qmv::launch_unpack_device(packed, rows, K, bits, codes, stream), fn);
+}
+
+qmv_status_t qmv_dequant_device(void* stream, int dtype, const qmv_weights_t* wt, float* out) {
+    const char* fn = "qmv_dequant_device";
+    if (wt == nullptr) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: weights struct is NULL", fn);
+    if (wt->n_experts != 1)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: n_experts must be 1", fn);
+    QMV_TRY(check_common(fn, dtype, 1, wt->K, wt->N, 1));
+    qmv::LaunchParams lp{};
+    lp.dtype = dtype;
+    QMV_TRY(format_geometry(fn, wt->format, wt->bits, wt->group_size, wt->K, lp));
+    if (wt->K == 0 || wt->N == 0) return QMV_OK;
+    const int tb = dtype_bytes(dtype);
+    QMV_TRY(check_ptr(fn, "w", wt->w, true, 16));
+    QMV_TRY(check_ptr(fn, "out", out, true, 4));
+    if (wt->format == QMV_AFFINE) {
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, true, tb));
+        QMV_TRY(check_ptr(fn, "biases", wt->biases, true, tb));
+    } else {
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, true, wt->format == QMV_NVFP4 ? 2 : 1));
+    }
+    QMV_TRY(check_ptr(fn, "global_scale", wt->global_scale, wt->global_scale != nullptr, 4));
+    lp.B = 1; lp.K = wt->K; lp.N = wt->N;
+    lp.w = wt->w; lp.scales = wt->scales; lp.biases = wt->biases;
+    lp.gscale = wt->format == QMV_NVFP4 ? wt->global_scale : nullptr;
+    return launch_status(qmv::launch_dequant_device(lp, out, stream), fn);
+}
+
+}  // extern "C"

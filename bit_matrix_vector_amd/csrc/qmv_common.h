@@ -1,0 +1,46 @@
+// Internal declarations shared by the host API and the HIP kernels.
+// Not part of the public ABI (that is include/qmv.h).
+#pragma once
+
+#include <stdint.h>
+
+namespace qmv {
+
+enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+enum Format { FMT_AFFINE = 0, FMT_MXFP4 = 1, FMT_NVFP4 = 2, FMT_MXFP8 = 3 };
+
+// Everything one launch needs. Filled and validated by the host API.
+struct LaunchParams {
+    int dtype;          // Dtype of x, y and affine scales/biases
+    int format;         // Format
+    int bits;           // affine code width (4 for fp4, 8 for fp8)
+    int group;          // affine group size (scale block for the others)
+    int64_t B;          // batch rows (qmv) ; unused by gather
+    int64_t K, N;
+    int64_t row_bytes;  // packed bytes per weight row
+    int64_t sc_per_row; // scale entries per weight row
+    const void* x;
+    const uint8_t* w;
+    const void* scales;
+    const void* biases;
+    const float* gscale;
+    void* y;
+    // gather only
+    int64_t n_experts, n_x_rows, n_slots;
+    const uint32_t* lhs;
+    const uint32_t* rhs;
+};
+
+// Launchers (defined in the .hip translation units). Return 0 on success or
+// the hipError_t of a failed launch.
+int launch_qmv(const LaunchParams& p, void* stream);
+int launch_gather(const LaunchParams& p, void* stream);
+int launch_unpack_device(const uint8_t* packed, int64_t rows, int64_t K, int bits,
+                         uint8_t* codes, void* stream);
+int launch_dequant_device(const LaunchParams& p, float* out, void* stream);
+const char* hip_error_string(int err);
+
+// Largest LDS footprint of the x staging buffer, in bytes.
+constexpr int kMaxStageBytes = 64 * 1024;
+
+}  // namespace qmv

@@ -1,0 +1,60 @@
+// Routes a validated launch to the translation unit that holds its kernel
+// instances, and launches the device codecs.
+#include "qmv_kernels.cuh"
+
+namespace qmv {
+
+#define QMV_DECL_PART(dt, fam)                                                          \
+    int launch_qmv_part_##dt##_##fam(const LaunchParams&, void*);                       \
+    int launch_gather_part_##dt##_##fam(const LaunchParams&, void*);                    \
+    int launch_dequant_part_##dt##_##fam(const LaunchParams&, float*, void*);
+QMV_DECL_PART(0, 0) QMV_DECL_PART(0, 1) QMV_DECL_PART(1, 0)
+QMV_DECL_PART(1, 1) QMV_DECL_PART(2, 0) QMV_DECL_PART(2, 1)
+#undef QMV_DECL_PART
+
+#define QMV_ROUTE(name, ...)                                                            \
+    do {                                                                                \
+        const int fam = p.format == FMT_AFFINE ? 0 : 1;                                 \
+        switch (p.dtype * 2 + fam) {                                                    \
+            case 0: return name##_0_0(__VA_ARGS__);                                     \
+            case 1: return name##_0_1(__VA_ARGS__);                                     \
+            case 2: return name##_1_0(__VA_ARGS__);                                     \
+            case 3: return name##_1_1(__VA_ARGS__);                                     \
+            case 4: return name##_2_0(__VA_ARGS__);                                     \
+            case 5: return name##_2_1(__VA_ARGS__);                                     \
+            default: return (int)hipErrorInvalidValue;                                  \
+        }                                                                               \
+    } while (0)
+
+int launch_qmv(const LaunchParams& p, void* stream) {
+    QMV_ROUTE(launch_qmv_part, p, stream);
+}
+
+int launch_gather(const LaunchParams& p, void* stream) {
+    QMV_ROUTE(launch_gather_part, p, stream);
+}
+
+int launch_dequant_device(const LaunchParams& p, float* out, void* stream) {
+    QMV_ROUTE(launch_dequant_part, p, out, stream);
+}
+
+int launch_unpack_device(const uint8_t* packed, int64_t rows, int64_t K, int bits,
+                         uint8_t* codes, void* stream) {
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const int64_t n = rows * (K >> 5);
+    const dim3 grid((unsigned)((n + 255) / 256));
+    switch (bits) {
+#define QMV_UNPACK(b)                                                                     \
+    case b:                                                                               \
+        hipLaunchKernelGGL((unpack_kernel<b>), grid, dim3(256), 0, st, packed, rows, K, codes); \
+        break;
+        QMV_UNPACK(2) QMV_UNPACK(3) QMV_UNPACK(4) QMV_UNPACK(5) QMV_UNPACK(6) QMV_UNPACK(8)
+#undef QMV_UNPACK
+        default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
+const char* hip_error_string(int err) { return hipGetErrorString((hipError_t)err); }
+
+}  // namespace qmv

@@ -1,0 +1,69 @@
+// One slice of the kernel instantiations: the dtype QMV_DT (0 f32, 1 f16,
+// 2 bf16) and the format family QMV_FAM (0 affine, 1 block-scaled). The
+// build compiles this file once per (dtype, family) pair, in parallel.
+#include "qmv_kernels.cuh"
+
+#ifndef QMV_DT
+#error "QMV_DT must be defined"
+#endif
+#ifndef QMV_FAM
+#error "QMV_FAM must be defined"
+#endif
+
+#define QMV_CAT3(a, b, c) a##b##_##c
+#define QMV_PART(name, dt, fam) QMV_CAT3(name, dt, fam)
+
+namespace qmv {
+namespace {
+
+template <template <int, int, int> class L, class... A>
+int dispatch_part(const LaunchParams& p, A... a) {
+#if QMV_FAM == 0
+    if (p.format != FMT_AFFINE) return (int)hipErrorInvalidValue;
+    switch (p.bits) {
+        case 2: return L<QMV_DT, FMT_AFFINE, 2>::run(p, a...);
+        case 3: return L<QMV_DT, FMT_AFFINE, 3>::run(p, a...);
+        case 4: return L<QMV_DT, FMT_AFFINE, 4>::run(p, a...);
+        case 5: return L<QMV_DT, FMT_AFFINE, 5>::run(p, a...);
+        case 6: return L<QMV_DT, FMT_AFFINE, 6>::run(p, a...);
+        case 8: return L<QMV_DT, FMT_AFFINE, 8>::run(p, a...);
+        default: return (int)hipErrorInvalidValue;
+    }
+#else
+    switch (p.format) {
+        case FMT_MXFP4: return L<QMV_DT, FMT_MXFP4, 4>::run(p, a...);
+        case FMT_NVFP4: return L<QMV_DT, FMT_NVFP4, 4>::run(p, a...);
+        case FMT_MXFP8: return L<QMV_DT, FMT_MXFP8, 8>::run(p, a...);
+        default: return (int)hipErrorInvalidValue;
+    }
+#endif
+}
+
+template <int DT, int FMT, int BITS> struct QmvL {
+    static int run(const LaunchParams& p, hipStream_t s) { return launch_qmv_t<DT, FMT, BITS>(p, s); }
+};
+template <int DT, int FMT, int BITS> struct GatherL {
+    static int run(const LaunchParams& p, hipStream_t s) {
+        return launch_gather_t<DT, FMT, BITS>(p, s);
+    }
+};
+template <int DT, int FMT, int BITS> struct DequantL {
+    static int run(const LaunchParams& p, float* out, hipStream_t s) {
+        return launch_dequant_t<DT, FMT, BITS>(p, out, s);
+    }
+};
+
+}  // namespace
+
+int QMV_PART(launch_qmv_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, void* stream) {
+    return dispatch_part<QmvL>(p, static_cast<hipStream_t>(stream));
+}
+int QMV_PART(launch_gather_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, void* stream) {
+    return dispatch_part<GatherL>(p, static_cast<hipStream_t>(stream));
+}
+int QMV_PART(launch_dequant_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, float* out,
+                                                     void* stream) {
+    return dispatch_part<DequantL>(p, out, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace qmv

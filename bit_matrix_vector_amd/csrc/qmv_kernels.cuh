@@ -1,0 +1,529 @@
+// QMV kernels for gfx950 (MI355X / CDNA4).
+//
+// y[b, n] = sum_k x[b, k] * dequant(W)[n, k]  for B <= 8 activation rows.
+//
+// The product is bound by HBM bandwidth: every packed weight byte is read
+// once and used B times. The kernel therefore
+//   * streams each weight row with dword-aligned vector loads (16 bytes per
+//     lane for 4-bit codes), consecutive lanes on consecutive bytes, and
+//     issues the next unit's loads before it computes the current one;
+//   * stages x once per block in LDS (in its stored type, in a layout where
+//     the 64 lanes of a wave read consecutive 16-byte chunks), then keeps each
+//     lane's x slice in registers while it is reused for R rows;
+//   * decodes codes in registers (bit-field extracts for affine codes, the
+//     gfx950 FP4/FP8 converters for E2M1/E4M3) and accumulates in fp32;
+//   * folds each 32-code unit with its scale: for affine,
+//     scale * sum(x*q) + bias * sum(x), sum(x) taken over fp32-widened x
+//     ("mlx 1.0.0 - quantized_nax.h" `qdot`; "ml-explore/mlx pull request
+//     4516"), for the block-scaled formats scale * sum(x*e);
+//   * reduces across the lanes of a row with a butterfly, converts to the
+//     output type with round-to-nearest-even and stores only rows < N; rows
+//     past N re-read row N-1 so the loop has no row-dependent branch
+//     ("ml-explore/mlx pull request 4516": the fast-rows tail).
+//
+// Work split: a row is covered by a lane group of LPR lanes (16, 32 or 64,
+// chosen from K so that no lane idles), unit u of the row going to lane
+// u mod LPR. A lane group owns R consecutive rows; a 256-thread block owns
+// 4 * (64 / LPR) * R rows. The lane -> unit map and the order of every sum
+// depend on K only, so a row's result is the same bits whatever N, B, the
+// tile or the slab split is (tail rows equal a padded call bit for bit; the
+// gathered product equals a one-row call bit for bit).
+
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "qmv_common.h"
+#include "qmv_device.h"
+
+namespace qmv {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+
+struct Geom {
+    int lpr;        // lanes per row group (16, 32, 64)
+    int lpr_log2;
+    int ks;         // x slab length in elements (multiple of 32*lpr, or K)
+    int glog2;      // affine: log2(group / 32)
+    int rows_per_block;
+};
+
+// One block's tile: rows [row_base, row_base + rows_per_block) of one weight
+// matrix against NB activation rows. xrow[b] / yrow[b] are the global rows.
+template <int DT, int FMT, int BITS, int NB, int R>
+__device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t row_base,
+                                const uint8_t* __restrict__ w, const void* sc, const void* bi,
+                                const typename Store<DT>::S* const (&xrow)[NB],
+                                typename Store<DT>::S* const (&yrow)[NB], float gmul,
+                                typename Store<DT>::S* lds) {
+    using F = Fmt<FMT, BITS>;
+    using S = typename Store<DT>::S;
+    constexpr int W = F::kWords;
+    constexpr int kUnitBytes = 4 * W;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int grp = lane >> g.lpr_log2;
+    const int gl = lane & (g.lpr - 1);
+    const int groups_per_wave = 64 >> g.lpr_log2;
+    const int64_t N = p.N;
+    const int64_t K = p.K;
+    const int64_t row0 = row_base + (int64_t)(wave * groups_per_wave + grp) * R;
+
+    const uint8_t* wr[R];
+    int64_t rr[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int64_t r = row0 + i;
+        rr[i] = r < N ? r : N - 1;  // tail rows re-read the last valid row
+        wr[i] = w + rr[i] * p.row_bytes;
+    }
+
+    float total[R][NB];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) total[i][b] = 0.0f;
+
+    for (int64_t slab = 0; slab < K; slab += g.ks) {
+        const int ks = (int)((K - slab) < g.ks ? (K - slab) : g.ks);
+        const int us = ks >> 5;  // units in this slab
+        const int64_t u0 = slab >> 5;
+
+        // weight + scale loads of this lane's first unit go out before the
+        // x staging so they overlap it
+        uint32_t dc[R][W];
+        typename F::Scale scur[R];
+        int ul = gl;
+        if (ul < us) {
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                load_words<W>(wr[i] + (u0 + ul) * kUnitBytes, dc[i]);
+                scur[i] = F::template load_scale<DT>(sc, bi, rr[i], p.sc_per_row, u0 + ul,
+                                                     g.glog2);
+            }
+        }
+
+        // stage x[:, slab : slab + ks] into LDS. Layout per batch row: the
+        // 8-value sub-chunk sc of unit u lives at element (sc * us + u) * 8.
+        {
+            constexpr int kPerVec = 16 / Store<DT>::kBytes;  // values per 16 bytes
+            const int vec_per_row = ks / kPerVec;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const uint4* src = reinterpret_cast<const uint4*>(xrow[b] + slab);
+                S* dst = lds + b * ks;
+                for (int v = tid; v < vec_per_row; v += kThreads) {
+                    const int e0 = v * kPerVec;
+                    const int u = e0 >> 5;
+                    const int sub = (e0 >> 3) & 3;
+                    const int j0 = e0 & 7;
+                    *reinterpret_cast<uint4*>(dst + (sub * us + u) * 8 + j0) = src[v];
+                }
+            }
+        }
+        __syncthreads();
+
+        for (; ul < us; ul += g.lpr) {
+            const int un = ul + g.lpr;
+            uint32_t dn[R][W];
+            typename F::Scale snx[R];
+            if (un < us) {
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    load_words<W>(wr[i] + (u0 + un) * kUnitBytes, dn[i]);
+                    snx[i] = F::template load_scale<DT>(sc, bi, rr[i], p.sc_per_row, u0 + un,
+                                                        g.glog2);
+                }
+            }
+
+            float acc[R][NB];
+            float sx[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                sx[b] = 0.0f;
+#pragma unroll
+                for (int i = 0; i < R; ++i) acc[i][b] = 0.0f;
+            }
+
+            static_for<0, 4>([&](auto sc_c) {
+                constexpr int SC = decltype(sc_c)::value;
+                float xv[NB][8];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    lds_load8<DT>(lds + b * ks + (SC * us + ul) * 8, xv[b]);
+                    if constexpr (F::kNeedsSumX) {
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) sx[b] += xv[b][j];
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    float q[8];
+                    F::template decode8<SC>(dc[i], q);
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) acc[i][b] = fmaf(q[j], xv[b][j], acc[i][b]);
+                }
+                if constexpr (FMT == FMT_NVFP4) {
+                    if constexpr (SC == 1) {
+                        // first block of 16 done: fold with its E4M3 scale
+#pragma unroll
+                        for (int i = 0; i < R; ++i)
+#pragma unroll
+                            for (int b = 0; b < NB; ++b) {
+                                total[i][b] = fmaf(scur[i].lo, acc[i][b], total[i][b]);
+                                acc[i][b] = 0.0f;
+                            }
+                    }
+                }
+            });
+
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    if constexpr (FMT == FMT_AFFINE) {
+                        total[i][b] = fmaf(scur[i].s, acc[i][b],
+                                           fmaf(scur[i].b, sx[b], total[i][b]));
+                    } else if constexpr (FMT == FMT_NVFP4) {
+                        total[i][b] = fmaf(scur[i].hi, acc[i][b], total[i][b]);
+                    } else {
+                        total[i][b] = fmaf(scur[i].s, acc[i][b], total[i][b]);
+                    }
+                }
+
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+#pragma unroll
+                for (int k = 0; k < W; ++k) dc[i][k] = dn[i][k];
+                scur[i] = snx[i];
+            }
+        }
+        __syncthreads();  // LDS is restaged for the next slab
+    }
+
+    // butterfly over the LPR lanes of each row group
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float v = total[i][b];
+            for (int off = g.lpr >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+            total[i][b] = v;
+        }
+
+    if (gl == 0) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int64_t r = row0 + i;
+            if (r < N) {
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    float v = total[i][b];
+                    if constexpr (FMT == FMT_NVFP4) v = v * gmul;
+                    yrow[b][r] = Store<DT>::from_f32(v);
+                }
+            }
+        }
+    }
+}
+
+template <int DT, int FMT, int BITS, int NB, int R>
+__global__ __launch_bounds__(kThreads) void qmv_kernel(LaunchParams p, Geom g) {
+    using S = typename Store<DT>::S;
+    extern __shared__ __align__(16) unsigned char smem[];
+    S* lds = reinterpret_cast<S*>(smem);
+    const S* xrow[NB];
+    S* yrow[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        xrow[b] = static_cast<const S*>(p.x) + b * p.K;
+        yrow[b] = static_cast<S*>(p.y) + b * p.N;
+    }
+    const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
+    qmv_tile<DT, FMT, BITS, NB, R>(p, g, (int64_t)blockIdx.x * g.rows_per_block, p.w, p.scales,
+                                   p.biases, xrow, yrow, gmul, lds);
+}
+
+// ---------------------------------------------------------------------------
+// Routed-expert gather. Grid (row tiles, n_experts + 1). Block (t, e) finds
+// the slots routed to expert e (a ballot scan over rhs_indices, in slot
+// order) and runs the tile on chunks of up to 8 of them, so each expert's
+// weights are streamed once per chunk of 8 slots (and for the usual handful
+// of slots per expert, exactly once). The extra column e = n_experts writes
+// the zero rows of slots whose expert or x row is out of range.
+// ---------------------------------------------------------------------------
+constexpr int kGatherChunkMax = 8;
+// Slots per chunk: 8 for 16-bit activations, 4 for f32, so the x staging of
+// a chunk fits kGatherStageBytes.
+__host__ __device__ constexpr int gather_chunk_for(int dt) { return dt == DT_F32 ? 4 : 8; }
+constexpr int kGatherStageBytes = 32 * 1024;
+
+template <int DT, int FMT, int BITS, int R>
+__device__ inline void gather_chunk(const LaunchParams& p, const Geom& g, int64_t row_base,
+                                    const uint8_t* w, const void* sc, const void* bi, float gmul,
+                                    const uint32_t* list, int cnt,
+                                    typename Store<DT>::S* lds) {
+    using S = typename Store<DT>::S;
+    auto run = [&](auto nb_c) {
+        constexpr int NB = decltype(nb_c)::value;
+        const S* xrow[NB];
+        S* yrow[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const uint32_t s = list[b];
+            xrow[b] = static_cast<const S*>(p.x) + (int64_t)p.lhs[s] * p.K;
+            yrow[b] = static_cast<S*>(p.y) + (int64_t)s * p.N;
+        }
+        qmv_tile<DT, FMT, BITS, NB, R>(p, g, row_base, w, sc, bi, xrow, yrow, gmul, lds);
+    };
+    if constexpr (gather_chunk_for(DT) == 4) {
+        switch (cnt) {
+            case 1: run(std::integral_constant<int, 1>{}); break;
+            case 2: run(std::integral_constant<int, 2>{}); break;
+            case 3: run(std::integral_constant<int, 3>{}); break;
+            default: run(std::integral_constant<int, 4>{}); break;
+        }
+    } else {
+        switch (cnt) {
+            case 1: run(std::integral_constant<int, 1>{}); break;
+            case 2: run(std::integral_constant<int, 2>{}); break;
+            case 3: run(std::integral_constant<int, 3>{}); break;
+            case 4: run(std::integral_constant<int, 4>{}); break;
+            case 5: run(std::integral_constant<int, 5>{}); break;
+            case 6: run(std::integral_constant<int, 6>{}); break;
+            case 7: run(std::integral_constant<int, 7>{}); break;
+            default: run(std::integral_constant<int, 8>{}); break;
+        }
+    }
+}
+
+template <int DT, int FMT, int BITS, int R>
+__global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g) {
+    using S = typename Store<DT>::S;
+    extern __shared__ __align__(16) unsigned char smem[];
+    S* lds = reinterpret_cast<S*>(smem);
+    constexpr int kChunk = gather_chunk_for(DT);
+    __shared__ uint32_t list[kChunk + kThreads];
+    __shared__ int wave_cnt[kWaves];
+    __shared__ int count;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t row_base = (int64_t)blockIdx.x * g.rows_per_block;
+    const int64_t e = blockIdx.y;
+
+    if (e == p.n_experts) {
+        // zero rows for slots with an out-of-range expert or x row
+        for (int64_t s = 0; s < p.n_slots; ++s) {
+            const uint32_t ex = p.rhs[s];
+            const uint32_t xr = p.lhs[s];
+            if ((int64_t)ex < p.n_experts && (int64_t)xr < p.n_x_rows) continue;
+            for (int r = tid; r < g.rows_per_block; r += kThreads) {
+                const int64_t n = row_base + r;
+                if (n < p.N) static_cast<S*>(p.y)[s * p.N + n] = Store<DT>::from_f32(0.0f);
+            }
+        }
+        return;
+    }
+
+    const uint8_t* w = p.w + e * p.N * p.row_bytes;
+    const void* sc;
+    const void* bi = nullptr;
+    if constexpr (FMT == FMT_AFFINE) {
+        sc = static_cast<const S*>(p.scales) + e * p.N * p.sc_per_row;
+        bi = static_cast<const S*>(p.biases) + e * p.N * p.sc_per_row;
+    } else {
+        sc = static_cast<const uint8_t*>(p.scales) + e * p.N * p.sc_per_row;
+    }
+    const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
+
+    if (tid == 0) count = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < p.n_slots; base += kThreads) {
+        const int64_t s = base + tid;
+        bool match = false;
+        if (s < p.n_slots) {
+            match = (int64_t)p.rhs[s] == e && (int64_t)p.lhs[s] < p.n_x_rows;
+        }
+        const uint64_t m = __ballot(match);
+        const int before = __popcll(m & ((1ull << lane) - 1ull));
+        if (lane == 0) wave_cnt[wave] = __popcll(m);
+        __syncthreads();
+        int off = count;
+        for (int i = 0; i < wave; ++i) off += wave_cnt[i];
+        if (match) list[off + before] = (uint32_t)s;
+        int added = 0;
+        for (int i = 0; i < kWaves; ++i) added += wave_cnt[i];
+        __syncthreads();
+        int cnt = count + added;
+        while (cnt >= kChunk) {
+            gather_chunk<DT, FMT, BITS, R>(p, g, row_base, w, sc, bi, gmul, list, kChunk, lds);
+            __syncthreads();
+            // move the leftovers to the front
+            const int rest = cnt - kChunk;
+            uint32_t v = 0;
+            if (tid < rest) v = list[kChunk + tid];
+            __syncthreads();
+            if (tid < rest) list[tid] = v;
+            __syncthreads();
+            cnt = rest;
+        }
+        if (tid == 0) count = cnt;
+        __syncthreads();
+    }
+    const int cnt = count;
+    if (cnt > 0) gather_chunk<DT, FMT, BITS, R>(p, g, row_base, w, sc, bi, gmul, list, cnt, lds);
+}
+
+// ---------------------------------------------------------------------------
+// Device codecs: the same extraction and decoders as the kernels above.
+// One thread per (row, unit of 32 codes).
+// ---------------------------------------------------------------------------
+template <int BITS>
+__global__ void unpack_kernel(const uint8_t* __restrict__ packed, int64_t rows, int64_t K,
+                              uint8_t* __restrict__ codes) {
+    const int64_t units = K >> 5;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= rows * units) return;
+    const int64_t r = t / units, u = t % units;
+    uint32_t d[BITS];
+    load_words<BITS>(packed + r * (K * BITS / 8) + u * 4 * BITS, d);
+    uint8_t* out = codes + r * K + u * 32;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) out[j] = (uint8_t)affine_code<BITS>(d, j);
+}
+
+template <int FMT, int SC, class Sc>
+__device__ inline float dequant_value(const Sc& s, float q, float gmul) {
+    if constexpr (FMT == FMT_AFFINE) return fmaf(s.s, q, s.b);
+    else if constexpr (FMT == FMT_NVFP4) return (q * (SC < 2 ? s.lo : s.hi)) * gmul;
+    else return q * s.s;
+}
+
+template <int DT, int FMT, int BITS>
+__global__ void dequant_kernel(LaunchParams p, int glog2, float* __restrict__ out) {
+    using F = Fmt<FMT, BITS>;
+    constexpr int W = F::kWords;
+    const int64_t units = p.K >> 5;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= p.N * units) return;
+    const int64_t r = t / units, u = t % units;
+    uint32_t d[W];
+    load_words<W>(p.w + r * p.row_bytes + u * 4 * W, d);
+    const typename F::Scale s =
+        F::template load_scale<DT>(p.scales, p.biases, r, p.sc_per_row, u, glog2);
+    const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
+    float* o = out + r * p.K + u * 32;
+    static_for<0, 4>([&](auto sc_c) {
+        constexpr int SC = decltype(sc_c)::value;
+        float q[8];
+        F::template decode8<SC>(d, q);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            o[SC * 8 + j] = dequant_value<FMT, SC>(s, q[j], gmul);
+        }
+    });
+}
+
+// ---------------------------------------------------------------------------
+// Host-side launch helpers.
+// ---------------------------------------------------------------------------
+constexpr int kRows = 4;  // rows per lane group
+
+int ilog2(int v) {
+    int r = 0;
+    while ((1 << r) < v) ++r;
+    return r;
+}
+
+// Lanes per row: the widest of 64/32/16 that keeps every lane busy (at least
+// 90% of lane-unit slots used), else the one that wastes least.
+int pick_lpr(int64_t K) {
+    const int64_t U = K >> 5;
+    if (U == 0) return 64;
+    int best = 64;
+    double best_eff = -1.0;
+    for (int lpr : {64, 32, 16}) {
+        const int64_t iters = (U + lpr - 1) / lpr;
+        const double eff = (double)U / (double)(iters * lpr);
+        if (eff >= 0.9) return lpr;
+        if (eff > best_eff + 1e-12) { best_eff = eff; best = lpr; }
+    }
+    return best;
+}
+
+// Geometry of a launch staging nb activation rows in at most `budget` bytes
+// of LDS. The slab length is a multiple of 32 * lpr (or all of K), which keeps
+// the lane -> unit map the same for every slab split.
+Geom make_geom(const LaunchParams& p, int nb, int budget) {
+    Geom g;
+    g.lpr = pick_lpr(p.K);
+    g.lpr_log2 = ilog2(g.lpr);
+    const int tbytes = p.dtype == DT_F32 ? 4 : 2;
+    const int64_t cap = budget / (nb * tbytes);              // elements per batch row
+    const int64_t quantum = 32LL * g.lpr;                    // <= 2048 <= cap always
+    int64_t ks = p.K <= cap ? p.K : (cap / quantum) * quantum;
+    g.ks = (int)(ks > 0 ? ks : 32);
+    g.glog2 = p.format == FMT_AFFINE ? ilog2(p.group / 32) : 0;
+    g.rows_per_block = kWaves * (64 / g.lpr) * kRows;
+    return g;
+}
+
+size_t stage_bytes(const LaunchParams& p, const Geom& g, int nb) {
+    const int tbytes = p.dtype == DT_F32 ? 4 : 2;
+    return (size_t)nb * (size_t)g.ks * (size_t)tbytes;
+}
+
+template <int DT, int FMT, int BITS>
+int launch_qmv_t(const LaunchParams& p, hipStream_t st) {
+    const int nb = (int)p.B;
+    const Geom g = make_geom(p, nb, kMaxStageBytes);
+    const dim3 grid((unsigned)((p.N + g.rows_per_block - 1) / g.rows_per_block));
+    const size_t lds = stage_bytes(p, g, nb);
+    switch (nb) {
+#define QMV_CASE(n)                                                                        \
+    case n:                                                                                \
+        hipLaunchKernelGGL((qmv_kernel<DT, FMT, BITS, n, kRows>), grid, dim3(kThreads), lds, \
+                           st, p, g);                                                      \
+        break;
+        QMV_CASE(1) QMV_CASE(2) QMV_CASE(3) QMV_CASE(4)
+        QMV_CASE(5) QMV_CASE(6) QMV_CASE(7) QMV_CASE(8)
+#undef QMV_CASE
+        default: return (int)hipErrorInvalidValue;
+    }
+    return (int)hipGetLastError();
+}
+
+template <int DT, int FMT, int BITS>
+int launch_gather_t(const LaunchParams& p, hipStream_t st) {
+    constexpr int kChunk = gather_chunk_for(DT);
+    const Geom g = make_geom(p, kChunk, kGatherStageBytes);
+    const dim3 grid((unsigned)((p.N + g.rows_per_block - 1) / g.rows_per_block),
+                    (unsigned)(p.n_experts + 1));
+    const size_t lds = stage_bytes(p, g, kChunk);
+    hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kRows>), grid, dim3(kThreads), lds, st, p,
+                       g);
+    return (int)hipGetLastError();
+}
+
+template <int DT, int FMT, int BITS>
+int launch_dequant_t(const LaunchParams& p, float* out, hipStream_t st) {
+    const int64_t n = p.N * (p.K >> 5);
+    const int glog2 = p.format == FMT_AFFINE ? ilog2(p.group / 32) : 0;
+    hipLaunchKernelGGL((dequant_kernel<DT, FMT, BITS>), dim3((unsigned)((n + 255) / 256)),
+                       dim3(256), 0, st, p, glog2, out);
+    return (int)hipGetLastError();
+}
+
+}  // namespace
+}  // namespace qmv

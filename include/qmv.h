@@ -1,0 +1,178 @@
+/*
+ * qmv.h - C ABI of the MI355X (gfx950) quantized matrix-vector product library.
+ *
+ * Computes the decode-time quantized matrix-vector product
+ *
+ *     y[b, n] = sum_k x[b, k] * dequant(W)[n, k]      0 <= b < B <= 8
+ *
+ * over packed low-bit weights, in four weight formats:
+ *
+ *   affine  2/3/4/5/6/8-bit unsigned codes q, one scale s and one bias beta per
+ *           group of 32/64/128 consecutive k: w = s*q + beta ("wh-iron
+ *           kernel-op coverage audit", section "Quantization precision
+ *           coverage", Track 2; "mlx 1.0.0 - quantized_nax.h", `dequantize`).
+ *           The bias term is beta * sum(x) with every x widened to fp32 before
+ *           it is added ("ml-explore/mlx pull request 4516", description).
+ *   MXFP4   E2M1 elements, one E8M0 power-of-two scale per block of 32.
+ *   NVFP4   E2M1 elements, one E4M3 scale per block of 16, one fp32 global.
+ *   MXFP8   E4M3 elements, one E8M0 scale per block of 32.
+ *           (the three block-scaled formats: the same audit's Track-1 table).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensor pointers of the compute calls are DEVICE pointers to row-major,
+ *   contiguous data. The caller owns all memory; nothing here allocates.
+ * - `stream` is a hipStream_t (NULL = the default stream). Compute calls are
+ *   asynchronous on it and never synchronize.
+ * - x, y and the affine scales/biases share one element type `dtype`
+ *   (f32, f16 or bf16); y is written in that type, rounded to nearest-even
+ *   from an fp32 accumulation.
+ * - Packed weight rows: code j of a row sits at bits [j*b, (j+1)*b) of the
+ *   row's little-endian bit stream (LSB first; for 4-bit codes the even k is
+ *   the low nibble; 8-bit codes are bytes). Row bytes = K*b/8.
+ * - E4M3 is the OCP "fn" variant (bias 7, max 448, NaN only at 0x7F/0xFF,
+ *   no infinity). E8M0 byte e means 2^(e-127); e = 255 is NaN.
+ * - Requirements checked before any HIP call (a failed check returns an
+ *   error, leaves every output untouched and records a message):
+ *     B in [0, 8]; K >= 0, K % 32 == 0 (affine: also K % group == 0);
+ *     N >= 0; bits in {2,3,4,5,6,8}; group in {32,64,128};
+ *     w and x 16-byte aligned, y / scales / biases aligned to their element;
+ *     pointers may be NULL only where the tensor is empty.
+ *   B == 0 or N == 0 is a successful no-op. K == 0 writes y = 0.
+ * - x and y must not overlap.
+ * - Errors: every entry point returns a qmv_status_t; qmv_last_error()
+ *   gives the message of the last failure on the calling thread. A launch
+ *   failure reported by the HIP runtime maps to QMV_ERR_HIP (asynchronous
+ *   faults surface at the caller's next synchronization, as with any kernel).
+ * - Thread safety: the only state is a thread-local error message.
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { QMV_F32 = 0, QMV_F16 = 1, QMV_BF16 = 2 } qmv_dtype_t;
+
+typedef enum { QMV_AFFINE = 0, QMV_MXFP4 = 1, QMV_NVFP4 = 2, QMV_MXFP8 = 3 } qmv_format_t;
+
+typedef enum {
+    QMV_OK = 0,
+    QMV_ERR_INVALID_ARGUMENT = 1,
+    QMV_ERR_UNSUPPORTED = 2,
+    QMV_ERR_MISALIGNED = 3,
+    QMV_ERR_HIP = 4
+} qmv_status_t;
+
+/* Affine QMV ("mlx 1.0.0 - quantized_nax.h": `qdot`, whose per-group result is
+ * scale * sum(x*q) + bias * sum(x); the fp32 widening of sum(x) follows
+ * "ml-explore/mlx pull request 4516").
+ *   x      [B, K]           dtype
+ *   w      [N, K*bits/8]    uint8, packed codes
+ *   scales [N, K/group]     dtype
+ *   biases [N, K/group]     dtype
+ *   y      [B, N]           dtype (output)
+ * Output rows are independent: the result for row n does not depend on N,
+ * so a call with N not a multiple of any tile gives, for rows < N, the same
+ * bits as a padded call ("ml-explore/mlx pull request 4516", Correctness). */
+qmv_status_t qmv_affine(void* stream, int dtype, int64_t B, int64_t K, int64_t N,
+                        const void* x, const uint8_t* w, const void* scales,
+                        const void* biases, int bits, int group_size, void* y);
+
+/* MXFP4 QMV.  w [N, K/2] uint8 (E2M1 codes, even k in the low nibble),
+ * scales [N, K/32] uint8 (E8M0). x [B, K], y [B, N] in dtype. */
+qmv_status_t qmv_fp_mxfp4(void* stream, int dtype, int64_t B, int64_t K, int64_t N,
+                          const void* x, const uint8_t* w, const uint8_t* scales, void* y);
+
+/* NVFP4 QMV.  w [N, K/2] uint8 (E2M1), scales [N, K/16] uint8 (E4M3),
+ * global_scale: DEVICE pointer to one fp32, or NULL for 1.0; it multiplies
+ * each fp32 row sum once ("ml-explore/mlx pull request 4516": NVFP4 calls with
+ * a global scale). K % 32 == 0 is required (two scale blocks per 32 codes). */
+qmv_status_t qmv_fp_nvfp4(void* stream, int dtype, int64_t B, int64_t K, int64_t N,
+                          const void* x, const uint8_t* w, const uint8_t* scales,
+                          const float* global_scale, void* y);
+
+/* MXFP8 (E4M3 elements) QMV.  w [N, K] uint8 (E4M3), scales [N, K/32] uint8
+ * (E8M0). x [B, K], y [B, N] in dtype. */
+qmv_status_t qmv_fp_mxfp8(void* stream, int dtype, int64_t B, int64_t K, int64_t N,
+                          const void* x, const uint8_t* w, const uint8_t* scales, void* y);
+
+/* Expert-stacked quantized weights for gather_qmv. Expert e's N x K matrix
+ * starts at w + e*N*row_bytes, its scales at scales + e*N*(K/block) (and the
+ * affine biases likewise), block = group_size (affine), 32 (MX) or 16 (NV).
+ * `bits` and `group_size` are read for QMV_AFFINE only; `global_scale`
+ * (device fp32 or NULL) for QMV_NVFP4 only and is shared by all experts. */
+typedef struct {
+    int format;              /* qmv_format_t */
+    int bits;
+    int group_size;
+    int64_t n_experts;
+    int64_t N;
+    int64_t K;
+    const uint8_t* w;
+    const void* scales;      /* dtype (affine) or uint8 (block-scaled) */
+    const void* biases;      /* affine only */
+    const float* global_scale;
+} qmv_weights_t;
+
+/* Routed-expert gathered QMV ("mlx 1.0.0 - quantized_nax.h",
+ * `adjust_matrix_offsets` with lhs/rhs indices; "@lgrammel/ds4-provider -
+ * moe.metal", `kernel_mul_mv_id`):
+ *     y[s, :] = W[rhs_indices[s]] . x[lhs_indices[s], :]     0 <= s < n_slots
+ *   x [n_x_rows, K] dtype; indices uint32 [n_slots] (device); y [n_slots, N].
+ * Each expert's weights are read once per call however many slots use it.
+ * An index out of range (expert >= n_experts or x row >= n_x_rows) yields a
+ * row of zeros ("ferrum-kernels - primitives.rs" tests: out-of-range ids give
+ * zeros, not a fault). Each slot's row equals, bit for bit, a one-row
+ * qmv_* call on that expert and x row. `w` points to host memory (the struct
+ * itself); the pointers inside it are device pointers. */
+qmv_status_t gather_qmv(void* stream, int dtype, const qmv_weights_t* w, const void* x,
+                        int64_t n_x_rows, const uint32_t* lhs_indices,
+                        const uint32_t* rhs_indices, int64_t n_slots, void* y);
+
+/* ---------------- codecs: HOST memory, synchronous, no GPU needed -------- */
+
+/* Bytes of one packed row: K*bits/8 for QMV_AFFINE, K/2 for the fp4 formats,
+ * K for MXFP8 ("mlx 1.0.0 - quantized_nax.h", `get_pack_factor` /
+ * `get_bytes_per_pack`). Returns -1 for invalid arguments. */
+int64_t qmv_packed_row_bytes(int format, int bits, int64_t K);
+
+/* Pack codes [rows, K] (uint8, each < 2^bits) into rows of K*bits/8 bytes,
+ * LSB first. Requires K*bits % 8 == 0. Errors: a code that does not fit. */
+qmv_status_t qmv_pack_codes(const uint8_t* codes, int64_t rows, int64_t K, int bits,
+                            uint8_t* packed);
+
+/* Inverse of qmv_pack_codes. */
+qmv_status_t qmv_unpack_codes(const uint8_t* packed, int64_t rows, int64_t K, int bits,
+                              uint8_t* codes);
+
+/* fp32 -> E4M3 (fn) bytes: round to nearest, ties to even; magnitudes above
+ * 448 (and infinities) saturate to +-448; NaN gives 0x7F; the sign of zero is
+ * kept. For building NVFP4 block scales. */
+qmv_status_t qmv_encode_e4m3(const float* v, int64_t n, uint8_t* out);
+
+/* ---------------- codecs: DEVICE memory, asynchronous ---------------------
+ * These run the same decode functions as the QMV kernels, so their bit-exact
+ * agreement with the definitions covers the hot path's decode. */
+
+/* Device unpack: codes [rows, K] uint8 from packed rows (device pointers). */
+qmv_status_t qmv_unpack_codes_device(void* stream, const uint8_t* packed, int64_t rows,
+                                     int64_t K, int bits, uint8_t* codes);
+
+/* Device dequant of one matrix (w->n_experts must be 1) to fp32 [N, K]:
+ * affine fmaf(s, q, beta); MXFP4 e2m1*2^(e-127); NVFP4 (e2m1*e4m3)*global;
+ * MXFP8 e4m3*2^(e-127). Each value is the fp32 rounding of the exact one.
+ * `dtype` is the storage type of the affine scales/biases (ignored otherwise). */
+qmv_status_t qmv_dequant_device(void* stream, int dtype, const qmv_weights_t* w, float* out);
+
+/* Message for the last non-OK status returned on this thread ("" if none). */
+const char* qmv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

@@ -1,0 +1,147 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function
+include/qmv.h declares, rejects bad arguments before any HIP call, and its
+host codecs agree byte for byte with the oracle."""
+
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import pytest
+
+import oracle
+import bit_matrix_vector_amd as bmv
+
+V = ctypes.c_void_p
+OK, INVAL, UNSUP, MISAL = 0, 1, 2, 3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return bmv.load()
+
+
+def test_library_exports_every_header_function(lib):
+    names = bmv.header_functions()
+    assert {"qmv_affine", "qmv_fp_mxfp4", "qmv_fp_nvfp4", "qmv_fp_mxfp8", "gather_qmv",
+            "qmv_pack_codes", "qmv_unpack_codes", "qmv_encode_e4m3",
+            "qmv_unpack_codes_device", "qmv_dequant_device", "qmv_packed_row_bytes",
+            "qmv_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+# fake, suitably aligned device addresses: validation must reject before use
+X, W, S, Bi, Y = V(0x10000), V(0x20000), V(0x30000), V(0x40000), V(0x50000)
+
+
+def _affine(lib, **kw):
+    a = dict(stream=None, dtype=2, B=1, K=64, N=8, x=X, w=W, s=S, b=Bi, bits=4, group=64, y=Y)
+    a.update(kw)
+    return lib.qmv_affine(a["stream"], a["dtype"], a["B"], a["K"], a["N"], a["x"], a["w"],
+                          a["s"], a["b"], a["bits"], a["group"], a["y"])
+
+
+@pytest.mark.parametrize("kw,status,word", [
+    (dict(dtype=7), INVAL, "dtype"),
+    (dict(bits=7), UNSUP, "bits"),
+    (dict(bits=1), UNSUP, "bits"),
+    (dict(group=16), UNSUP, "group"),
+    (dict(K=48), INVAL, "multiple of 32"),
+    (dict(K=96, group=64), INVAL, "group"),
+    (dict(B=9), UNSUP, "batch"),
+    (dict(B=-1), INVAL, "negative"),
+    (dict(N=-2), INVAL, "negative"),
+    (dict(x=None), INVAL, "x is NULL"),
+    (dict(w=None), INVAL, "w is NULL"),
+    (dict(s=None), INVAL, "scales is NULL"),
+    (dict(y=None), INVAL, "y is NULL"),
+    (dict(x=V(0x10008)), MISAL, "x is not 16-byte"),
+    (dict(w=V(0x20004)), MISAL, "w is not 16-byte"),
+    (dict(y=V(0x50001)), MISAL, "y is not 2-byte"),
+    (dict(dtype=0, s=V(0x30002)), MISAL, "scales is not 4-byte"),
+    (dict(x=V(0x50000)), INVAL, "overlap"),
+])
+def test_affine_validation(lib, kw, status, word):
+    assert _affine(lib, **kw) == status
+    assert word in lib.qmv_last_error().decode()
+
+
+def test_empty_calls_are_noops(lib):
+    assert _affine(lib, B=0, x=None, w=None, s=None, b=None, y=None) == OK
+    assert _affine(lib, N=0, x=None, w=None, s=None, b=None, y=None) == OK
+    assert lib.qmv_fp_mxfp4(None, 2, 0, 4096, 16, None, None, None, None) == OK
+
+
+def test_fp_validation(lib):
+    assert lib.qmv_fp_mxfp4(None, 2, 1, 4096, 16, X, W, S, None) == INVAL
+    assert lib.qmv_fp_nvfp4(None, 2, 1, 4096, 16, X, W, V(0x30001), None, Y) == MISAL
+    assert "scales" in lib.qmv_last_error().decode()
+    assert lib.qmv_fp_nvfp4(None, 2, 1, 4096, 16, X, W, S, V(0x60002), Y) == MISAL
+    assert "global_scale" in lib.qmv_last_error().decode()
+    assert lib.qmv_fp_mxfp8(None, 2, 1, 4080, 16, X, W, S, Y) == INVAL
+    assert lib.qmv_fp_mxfp8(None, 2, 12, 4096, 16, X, W, S, Y) == UNSUP
+
+
+def test_gather_validation(lib):
+    wt = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 64, 1536, 4096, 0x20000, 0x30000, None, None)
+    lhs, rhs = V(0x70000), V(0x80000)
+    assert lib.gather_qmv(None, 2, None, X, 16, lhs, rhs, 128, Y) == INVAL
+    assert lib.gather_qmv(None, 2, ctypes.byref(wt), X, 16, None, rhs, 128, Y) == INVAL
+    assert lib.gather_qmv(None, 2, ctypes.byref(wt), X, 16, lhs, V(0x80002), 128, Y) == MISAL
+    assert lib.gather_qmv(None, 2, ctypes.byref(wt), X, 16, lhs, rhs, 0, None) == OK
+    bad = bmv.QmvWeights(bmv.QMV_AFFINE, 7, 64, 4, 16, 4096, 0x20000, 0x30000, 0x40000, None)
+    assert lib.gather_qmv(None, 2, ctypes.byref(bad), X, 16, lhs, rhs, 8, Y) == UNSUP
+    neg = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, -1, 16, 4096, 0x20000, 0x30000, None, None)
+    assert lib.gather_qmv(None, 2, ctypes.byref(neg), X, 16, lhs, rhs, 8, Y) == INVAL
+
+
+def test_device_codec_validation(lib):
+    assert lib.qmv_unpack_codes_device(None, W, 4, 48, 4, V(0x90000)) == INVAL
+    assert lib.qmv_unpack_codes_device(None, W, 4, 64, 7, V(0x90000)) == UNSUP
+    wt = bmv.QmvWeights(bmv.QMV_MXFP8, 8, 32, 2, 16, 64, 0x20000, 0x30000, None, None)
+    assert lib.qmv_dequant_device(None, 2, ctypes.byref(wt), V(0x90000)) == INVAL
+
+
+@pytest.mark.parametrize("fmt,bits,K,expect", [
+    ("affine", 3, 4096, 1536), ("affine", 5, 64, 40), ("affine", 8, 32, 32),
+    ("mxfp4", 4, 4096, 2048), ("nvfp4", 4, 4096, 2048), ("mxfp8", 8, 4096, 4096),
+    ("affine", 7, 64, -1),
+])
+def test_packed_row_bytes(fmt, bits, K, expect):
+    assert bmv.qmv_packed_row_bytes(fmt, bits, K) == expect
+    if expect > 0 and fmt == "affine":
+        assert expect == oracle.packed_row_bytes(K, bits)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
+def test_host_pack_matches_oracle_packer(bits):
+    rng = np.random.default_rng(100 + bits)
+    codes = rng.integers(0, 1 << bits, size=(7, 256), dtype=np.uint8)
+    packed = bmv.qmv_pack_codes(codes, bits)
+    assert np.array_equal(packed, oracle.pack_codes(codes, bits))
+    assert np.array_equal(bmv.qmv_unpack_codes(packed, 256, bits), codes)
+    assert np.array_equal(bmv.qmv_unpack_codes(packed, 256, bits),
+                          oracle.unpack_codes(packed, 256, bits))
+
+
+def test_host_pack_rejects_wide_codes():
+    with pytest.raises(bmv.QmvError) as e:
+        bmv.qmv_pack_codes(np.array([[0, 8] * 16], dtype=np.uint8), 3)
+    assert "does not fit" in str(e.value)
+
+
+def test_host_e4m3_encoder_matches_oracle():
+    rng = np.random.default_rng(11)
+    vals = oracle.e4m3_value(np.arange(0x7F))
+    mids = (vals[1:] + vals[:-1]) / 2
+    v = np.concatenate([
+        rng.normal(0, 1, 5000), rng.normal(0, 100, 2000), rng.uniform(-2 ** -6, 2 ** -6, 2000),
+        rng.uniform(-1e-4, 1e-4, 500), vals, -vals, mids, -mids,
+        [0.0, -0.0, 447.9, 448.0, 449.0, 464.0, 1e9, -1e9, np.inf, -np.inf, np.nan,
+         2.0 ** -10, 2.0 ** -10 * 1.0001, 2.0 ** -11],
+    ]).astype(np.float32)
+    got = bmv.qmv_encode_e4m3(v)
+    ref = oracle.e4m3_encode_nearest(v.astype(np.float64))
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, [(float(v[i]), hex(got[i]), hex(ref[i])) for i in bad[:10]]
