@@ -149,6 +149,53 @@ def time_case(runner: Runner, steps: int, warmup: int) -> dict:
     }
 
 
+def time_stream_read(bmv, nbytes: int, steps: int, warmup: int, min_bytes: int = 1 << 30,
+                     unroll: int = 8):
+    """The measured ceiling: a plain 16-byte streaming read of `nbytes` per
+    launch over rotating, distinct buffers (same cold-HBM method as the QMV
+    timing), with an event pair around each launch."""
+    import torch
+    lib = bmv.load()
+    nbytes = (nbytes + 15) // 16 * 16
+    copies = max(2, -(-min_bytes // nbytes))
+    buf = torch.empty(copies * nbytes, dtype=torch.uint8, device="cuda:0")
+    buf.random_(0, 256)
+    sink = torch.zeros(65536, dtype=torch.int32, device="cuda:0")
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def call(i):
+        st = lib.qmv_bench_stream_read(sp, ctypes.c_void_p(buf.data_ptr() + (i % copies) * nbytes),
+                                       nbytes, ctypes.c_void_p(sink.data_ptr()), unroll)
+        if st != 0:
+            raise RuntimeError(f"stream read launch failed: {st}")
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    n_ev = min(steps, 500)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n_ev)]
+    for i in range(n_ev):
+        ev[i][0].record()
+        call(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    del buf
+    return {"bytes": nbytes, "kernel_us_mean": us, "gbps_kernel": nbytes / us / 1e3,
+            "copies": copies, "unroll": unroll}
+
+
+def ceiling_sweep(bmv, steps: int, warmup: int) -> None:
+    """Streaming-read time against size and per-lane unroll (to stderr)."""
+    for mb in (1, 4, 8, 16, 31.232, 64, 128, 256, 1024):
+        for u in (4, 8, 16):
+            r = time_stream_read(bmv, int(mb * 1e6), steps, warmup, unroll=u,
+                                 min_bytes=max(1 << 30, 2 * int(mb * 1e6)))
+            print(f"[ceiling] {mb:8.3f} MB unroll {u:2d}: {r['kernel_us_mean']:9.2f} us "
+                  f"{r['gbps_kernel']:8.1f} GB/s", file=sys.stderr, flush=True)
+
+
 def check_once(bmv, case) -> None:
     """The timed entry point gives the oracle's answer on sampled rows."""
     import oracle
@@ -204,6 +251,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--ceiling-sweep", action="store_true",
+                    help="only sweep the streaming-read ceiling over sizes and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the QMV path here has "
@@ -216,12 +266,20 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     bmv.load()
+    if args.ceiling_sweep:
+        ceiling_sweep(bmv, min(args.steps, 200), 10)
+        return 0
     head = workloads.config3("mxfp4", 1)
     check_once(bmv, head)
     runner = Runner(bmv, head)
     res = time_case(runner, args.steps, args.warmup)
     runner.free()
     print(f"[bench] headline mxfp4 B1: {json.dumps(res)}", file=sys.stderr, flush=True)
+
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = time_stream_read(bmv, head.algorithmic_bytes(), args.steps, args.warmup)
+        print(f"[bench] stream-read ceiling: {json.dumps(ceiling)}", file=sys.stderr, flush=True)
 
     cases = []
     if not args.headline_only:
@@ -262,6 +320,9 @@ def main() -> int:
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(res["gbps_kernel"] / PEAK_HBM_GBPS, 4), "traffic": None},
         "cpu_baseline": cpu,
+        "stream_read_ceiling": None if ceiling is None else {
+            "gbps": round(ceiling["gbps_kernel"], 1), "us": round(ceiling["kernel_us_mean"], 3),
+            "kernel_frac_of_ceiling": round(res["gbps_kernel"] / ceiling["gbps_kernel"], 4)},
         "cases": cases,
     }
     print(json.dumps(line), flush=True)

@@ -78,6 +78,10 @@ def load() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.qmv_packed_row_bytes.argtypes = [i32, i32, i64]
     lib.qmv_packed_row_bytes.restype = i64
+    lib.qmv_bench_stream_read.argtypes = [vp, vp, i64, vp, i32]
+    lib.qmv_bench_stream_read.restype = ctypes.c_int
+    lib.qmv_bench_copy.argtypes = [vp, vp, vp, i64]
+    lib.qmv_bench_copy.restype = ctypes.c_int
     lib.qmv_last_error.argtypes = []
     lib.qmv_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -85,10 +89,15 @@ def load() -> ctypes.CDLL:
 
 
 def header_functions() -> list[str]:
-    """Names of the functions include/qmv.h declares."""
-    text = open(HEADER_PATH).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(qmv_\w+|gather_qmv)\s*\(", text)))
+    """Names of the functions the headers in include/ declare."""
+    inc = os.path.dirname(HEADER_PATH)
+    names = set()
+    for fn in sorted(os.listdir(inc)):
+        if fn.endswith(".h"):
+            text = open(os.path.join(inc, fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names.update(re.findall(r"\b(qmv_\w+|gather_qmv)\s*\(", text))
+    return sorted(names)
 
 
 def _check(status: int) -> None:

@@ -44,6 +44,8 @@ def _jobs() -> list[tuple[list[str], str]]:
     obj = os.path.join(BUILD, "qmv_dispatch.o")
     jobs.append(([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "qmv_dispatch.hip"), "-o", obj],
                  obj))
+    obj = os.path.join(BUILD, "qmv_bench.o")
+    jobs.append(([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "qmv_bench.hip"), "-o", obj], obj))
     obj = os.path.join(BUILD, "qmv_api.o")
     jobs.append((["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "qmv_api.cpp"), "-o", obj], obj))
     return jobs

@@ -13,6 +13,50 @@
 namespace qmv {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 += a.lo*b.lo + a.hi*b.hi for two packed 16-bit pairs of type DT
+// (v_dot2c_f32_bf16 / v_dot2c_f32_f16: exact products, fp32 accumulation).
+template <int DT>
+__device__ inline float dot2(uint32_t a, uint32_t b, float c) {
+    if constexpr (DT == DT_BF16) {
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                               __builtin_bit_cast(bf16x2_t, b), c, false);
+    } else {
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a),
+                                      __builtin_bit_cast(f16x2_t, b), c, false);
+    }
+}
+
+// The two 16-bit values of a packed pair as fp32 (exact).
+template <int DT>
+__device__ inline float pair_lo(uint32_t v) {
+    if constexpr (DT == DT_BF16) return __uint_as_float(v << 16);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xFFFFu));
+}
+template <int DT>
+__device__ inline float pair_hi(uint32_t v) {
+    if constexpr (DT == DT_BF16) return __uint_as_float(v & 0xFFFF0000u);
+    else return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16));
+}
+
+// 1.0 in both halves of a pair.
+template <int DT>
+__device__ constexpr uint32_t pair_ones() {
+    return DT == DT_BF16 ? 0x3F803F80u : 0x3C003C00u;
+}
+
+// Compile-time loop helper.
+template <int I, int N, class F>
+__device__ inline void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
+}
 
 // ---------------------------------------------------------------------------
 // Storage types of x / y / affine scales and biases.
@@ -23,6 +67,10 @@ template <> struct Store<DT_F32> {
     using S = float;
     static constexpr int kBytes = 4;
     __device__ static inline float load(const S* p) { return *p; }
+    __device__ static inline uint32_t load_bits(const S* p) {
+        return *reinterpret_cast<const uint32_t*>(p);
+    }
+    __device__ static inline float bits_to_f32(uint32_t b) { return __uint_as_float(b); }
     __device__ static inline S from_f32(float v) { return v; }
 };
 
@@ -30,6 +78,12 @@ template <> struct Store<DT_F16> {
     using S = _Float16;
     static constexpr int kBytes = 2;
     __device__ static inline float load(const S* p) { return (float)*p; }
+    __device__ static inline uint32_t load_bits(const S* p) {
+        return *reinterpret_cast<const uint16_t*>(p);
+    }
+    __device__ static inline float bits_to_f32(uint32_t b) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)b);
+    }
     // v_cvt_f16_f32 rounds to nearest-even in the default mode.
     __device__ static inline S from_f32(float v) { return (_Float16)v; }
 };
@@ -40,6 +94,8 @@ template <> struct Store<DT_BF16> {
     __device__ static inline float load(const S* p) {
         return __uint_as_float((uint32_t)*p << 16);
     }
+    __device__ static inline uint32_t load_bits(const S* p) { return *p; }
+    __device__ static inline float bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
     // fp32 -> bf16, round to nearest-even; NaN stays a quiet NaN.
     __device__ static inline S from_f32(float v) {
         uint32_t u = __float_as_uint(v);
@@ -59,7 +115,7 @@ __device__ inline void lds_load8(const typename Store<DT>::S* p, float (&v)[8]) 
         v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
         v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     } else if constexpr (DT == DT_BF16) {
-        const uint4 a = *reinterpret_cast<const uint4*>(p);
+        const v4u a = *reinterpret_cast<const v4u*>(p);
         const uint32_t d[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -87,12 +143,6 @@ __device__ inline float e8m0_to_f32(uint32_t e) {
     return __uint_as_float(b);
 }
 
-// OCP E4M3 byte -> fp32 through the gfx950 FP8 converter (scale 1.0).
-__device__ inline float e4m3_to_f32(uint32_t byte) {
-    const f32x2 r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(byte, 1.0f, false);
-    return r.x;
-}
-
 // ---------------------------------------------------------------------------
 // Packed codes. A unit is 32 consecutive codes of one row; with b-bit codes
 // it is exactly b dwords, so every unit starts on a dword boundary and code j
@@ -112,15 +162,15 @@ __device__ inline uint32_t affine_code(const uint32_t* d, int j) {
 template <int WORDS>
 __device__ inline void load_words(const uint8_t* p, uint32_t (&d)[WORDS]) {
     if constexpr (WORDS == 4) {
-        const uint4 a = *reinterpret_cast<const uint4*>(p);
+        const v4u a = *reinterpret_cast<const v4u*>(p);
         d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
     } else if constexpr (WORDS == 8) {
-        const uint4 a = *reinterpret_cast<const uint4*>(p);
-        const uint4 b = *reinterpret_cast<const uint4*>(p + 16);
+        const v4u a = *reinterpret_cast<const v4u*>(p);
+        const v4u b = *reinterpret_cast<const v4u*>(p + 16);
         d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
         d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
     } else if constexpr (WORDS == 2) {
-        const uint2 a = *reinterpret_cast<const uint2*>(p);
+        const v2u a = *reinterpret_cast<const v2u*>(p);
         d[0] = a.x; d[1] = a.y;
     } else {
         __builtin_memcpy(d, __builtin_assume_aligned(p, 4), 4 * WORDS);
@@ -130,34 +180,77 @@ __device__ inline void load_words(const uint8_t* p, uint32_t (&d)[WORDS]) {
 // ---------------------------------------------------------------------------
 // Formats. Each defines
 //   kWords            dwords of packed codes per unit of 32
-//   Scale             the per-(row, unit) scale data and its loader
+//   Raw / load_raw    the per-(row, unit) scale bytes as loaded (undecoded, so
+//                     a load in flight is not waited on until its use)
+//   Scale / decode    the fp32 scale data of the unit
 //   decode8<SC>(d,q)  fp32 values of codes 8*SC .. 8*SC+7 of the unit
-//   kFoldEvery        sub-chunks of 8 codes per scale block (4, or 2 for NVFP4)
 // ---------------------------------------------------------------------------
 template <int FMT, int BITS> struct Fmt;
 
 template <int BITS> struct Fmt<FMT_AFFINE, BITS> {
     static constexpr int kWords = BITS;
-    static constexpr int kFoldEvery = 4;
     static constexpr bool kNeedsSumX = true;
+    struct Raw { uint32_t s, b; };
     struct Scale { float s, b; };
     template <int DT>
-    __device__ static inline Scale load_scale(const void* sc, const void* bi, int64_t row,
-                                              int64_t sc_per_row, int64_t u, int glog2) {
+    __device__ static inline Raw load_raw(const void* sc, const void* bi, int64_t row,
+                                          int64_t sc_per_row, int64_t u, int glog2) {
         using S = typename Store<DT>::S;
         const int64_t i = row * sc_per_row + (u >> glog2);
-        return Scale{Store<DT>::load(static_cast<const S*>(sc) + i),
-                     Store<DT>::load(static_cast<const S*>(bi) + i)};
+        return Raw{Store<DT>::load_bits(static_cast<const S*>(sc) + i),
+                   Store<DT>::load_bits(static_cast<const S*>(bi) + i)};
+    }
+    template <int DT>
+    __device__ static inline Scale decode(const Raw& r) {
+        return Scale{Store<DT>::bits_to_f32(r.s), Store<DT>::bits_to_f32(r.b)};
     }
     template <int SC>
     __device__ static inline void decode8(const uint32_t (&d)[kWords], float (&q)[8]) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) q[j] = (float)affine_code<BITS>(d, SC * 8 + j);
     }
+    // Packed 16-bit path (4-bit codes only): pair k of sub-chunk SC holds
+    // codes (8SC + k, 8SC + k + 4) as the 16-bit values 1 + q/16, built by
+    // placing the nibble under the leading mantissa bits of 1.0 (exact). The
+    // x pairs in LDS are ordered to match: (x[k], x[k + 4]).
+    template <int SC, int DT>
+    __device__ static inline void pairs(const uint32_t (&d)[kWords], uint32_t (&wp)[4]) {
+        static_assert(BITS == 4, "packed affine path is for 4-bit codes");
+        const uint32_t w = d[SC];
+        if constexpr (DT == DT_BF16) {
+            // bf16 1.0 = 0x3F80; nibble at mantissa bits 6..3
+            wp[0] = ((w << 3) & 0x00780078u) | 0x3F803F80u;
+            wp[1] = ((w >> 1) & 0x00780078u) | 0x3F803F80u;
+            wp[2] = ((w >> 5) & 0x00780078u) | 0x3F803F80u;
+            wp[3] = ((w >> 9) & 0x00780078u) | 0x3F803F80u;
+        } else {
+            // f16 1.0 = 0x3C00; nibble at mantissa bits 9..6
+            wp[0] = ((w << 6) & 0x03C003C0u) | 0x3C003C00u;
+            wp[1] = ((w << 2) & 0x03C003C0u) | 0x3C003C00u;
+            wp[2] = ((w >> 2) & 0x03C003C0u) | 0x3C003C00u;
+            wp[3] = ((w >> 6) & 0x03C003C0u) | 0x3C003C00u;
+        }
+    }
+    // code value of a pair half built by `pairs` (1 + q/16 -> q, exact)
+    __device__ static inline float pair_code(float v) { return (v - 1.0f) * 16.0f; }
 };
 
+// E2M1 packed pairs: pair k = codes (2k, 2k+1) of the dword, as bf16 / f16
+// (every E2M1 value is exact in both).
+template <int DT>
+__device__ inline void e2m1_pairs(const uint32_t w, uint32_t (&wp)[4]) {
+    static_for<0, 4>([&](auto k_c) {
+        constexpr int k = decltype(k_c)::value;
+        if constexpr (DT == DT_BF16)
+            wp[k] = __builtin_bit_cast(uint32_t,
+                                       __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, k));
+        else
+            wp[k] = __builtin_bit_cast(uint32_t,
+                                       __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, k));
+    });
+}
+
 // E2M1 pairs: byte k of a dword holds codes 2k (low nibble) and 2k+1.
-template <int SC>
 __device__ inline void decode_e2m1_8(const uint32_t word, float (&q)[8]) {
     const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
     const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1);
@@ -169,49 +262,66 @@ __device__ inline void decode_e2m1_8(const uint32_t word, float (&q)[8]) {
 
 template <> struct Fmt<FMT_MXFP4, 4> {
     static constexpr int kWords = 4;
-    static constexpr int kFoldEvery = 4;
     static constexpr bool kNeedsSumX = false;
+    struct Raw { uint32_t e; };
     struct Scale { float s; };
     template <int DT>
-    __device__ static inline Scale load_scale(const void* sc, const void*, int64_t row,
-                                              int64_t sc_per_row, int64_t u, int) {
-        return Scale{e8m0_to_f32(static_cast<const uint8_t*>(sc)[row * sc_per_row + u])};
+    __device__ static inline Raw load_raw(const void* sc, const void*, int64_t row,
+                                          int64_t sc_per_row, int64_t u, int) {
+        return Raw{static_cast<const uint8_t*>(sc)[row * sc_per_row + u]};
     }
+    template <int DT>
+    __device__ static inline Scale decode(const Raw& r) { return Scale{e8m0_to_f32(r.e)}; }
     template <int SC>
     __device__ static inline void decode8(const uint32_t (&d)[kWords], float (&q)[8]) {
-        decode_e2m1_8<SC>(d[SC], q);
+        decode_e2m1_8(d[SC], q);
     }
+    template <int SC, int DT>
+    __device__ static inline void pairs(const uint32_t (&d)[kWords], uint32_t (&wp)[4]) {
+        e2m1_pairs<DT>(d[SC], wp);
+    }
+    __device__ static inline float pair_code(float v) { return v; }
 };
 
 template <> struct Fmt<FMT_NVFP4, 4> {
     static constexpr int kWords = 4;
-    static constexpr int kFoldEvery = 2;
     static constexpr bool kNeedsSumX = false;
-    struct Scale { float lo, hi; };  // blocks of 16: codes 0..15 and 16..31
+    struct Raw { uint32_t e; };      // two E4M3 bytes: blocks of codes 0..15, 16..31
+    struct Scale { float lo, hi; };
     template <int DT>
-    __device__ static inline Scale load_scale(const void* sc, const void*, int64_t row,
-                                              int64_t sc_per_row, int64_t u, int) {
+    __device__ static inline Raw load_raw(const void* sc, const void*, int64_t row,
+                                          int64_t sc_per_row, int64_t u, int) {
         const uint8_t* p = static_cast<const uint8_t*>(sc) + row * sc_per_row + 2 * u;
-        const uint32_t v = *reinterpret_cast<const uint16_t*>(p);
-        const f32x2 r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 1.0f, false);
-        return Scale{r.x, r.y};
+        return Raw{*reinterpret_cast<const uint16_t*>(p)};
+    }
+    template <int DT>
+    __device__ static inline Scale decode(const Raw& r) {
+        const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.e, 1.0f, false);
+        return Scale{v.x, v.y};
     }
     template <int SC>
     __device__ static inline void decode8(const uint32_t (&d)[kWords], float (&q)[8]) {
-        decode_e2m1_8<SC>(d[SC], q);
+        decode_e2m1_8(d[SC], q);
     }
+    template <int SC, int DT>
+    __device__ static inline void pairs(const uint32_t (&d)[kWords], uint32_t (&wp)[4]) {
+        e2m1_pairs<DT>(d[SC], wp);
+    }
+    __device__ static inline float pair_code(float v) { return v; }
 };
 
 template <> struct Fmt<FMT_MXFP8, 8> {
     static constexpr int kWords = 8;
-    static constexpr int kFoldEvery = 4;
     static constexpr bool kNeedsSumX = false;
+    struct Raw { uint32_t e; };
     struct Scale { float s; };
     template <int DT>
-    __device__ static inline Scale load_scale(const void* sc, const void*, int64_t row,
-                                              int64_t sc_per_row, int64_t u, int) {
-        return Scale{e8m0_to_f32(static_cast<const uint8_t*>(sc)[row * sc_per_row + u])};
+    __device__ static inline Raw load_raw(const void* sc, const void*, int64_t row,
+                                          int64_t sc_per_row, int64_t u, int) {
+        return Raw{static_cast<const uint8_t*>(sc)[row * sc_per_row + u]};
     }
+    template <int DT>
+    __device__ static inline Scale decode(const Raw& r) { return Scale{e8m0_to_f32(r.e)}; }
     template <int SC>
     __device__ static inline void decode8(const uint32_t (&d)[kWords], float (&q)[8]) {
         // word 2*SC holds codes 8*SC .. 8*SC+3 (one byte each), word 2*SC+1 the next 4
@@ -222,15 +332,57 @@ template <> struct Fmt<FMT_MXFP8, 8> {
         q[0] = a.x; q[1] = a.y; q[2] = b.x; q[3] = b.y;
         q[4] = c.x; q[5] = c.y; q[6] = e.x; q[7] = e.y;
     }
+    // pair k = codes (8SC + 2k, 8SC + 2k + 1): bytes 2(k&1), 2(k&1)+1 of
+    // word 2SC + k/2, as bf16 / f16 (every E4M3 value is exact in both)
+    template <int SC, int DT>
+    __device__ static inline void pairs(const uint32_t (&d)[kWords], uint32_t (&wp)[4]) {
+        static_for<0, 4>([&](auto k_c) {
+            constexpr int k = decltype(k_c)::value;
+            const uint32_t w = d[2 * SC + (k >> 1)];
+            if constexpr (DT == DT_BF16)
+                wp[k] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, (k & 1) != 0));
+            else
+                wp[k] = __builtin_bit_cast(
+                    uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, (k & 1) != 0));
+        });
+    }
+    __device__ static inline float pair_code(float v) { return v; }
 };
 
-// Compile-time loop helper.
-template <int I, int N, class F>
-__device__ inline void static_for(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, N>(f);
-    }
+// Sum of v over each group of `lpr` consecutive lanes (16, 32 or 64), left in
+// the group's last lane, with DPP lane movements (VALU latency; no LDS
+// crossbar). Fixed order: quad swaps, the two row mirrors, then row
+// broadcasts across 16-lane rows.
+__device__ inline float group_sum(float v, int lpr) {
+    auto dpp = [](float x, int ctrl_id) __attribute__((always_inline)) {
+        int r = 0;
+        const int xi = __float_as_int(x);
+        switch (ctrl_id) {
+            case 0: r = __builtin_amdgcn_update_dpp(0, xi, 0xB1, 0xF, 0xF, false); break;   // quad_perm 1,0,3,2
+            case 1: r = __builtin_amdgcn_update_dpp(0, xi, 0x4E, 0xF, 0xF, false); break;   // quad_perm 2,3,0,1
+            case 2: r = __builtin_amdgcn_update_dpp(0, xi, 0x141, 0xF, 0xF, false); break;  // row_half_mirror
+            case 3: r = __builtin_amdgcn_update_dpp(0, xi, 0x140, 0xF, 0xF, false); break;  // row_mirror
+            case 4: r = __builtin_amdgcn_update_dpp(0, xi, 0x142, 0xA, 0xF, false); break;  // row_bcast:15 -> rows 1,3
+            default: r = __builtin_amdgcn_update_dpp(0, xi, 0x143, 0xC, 0xF, false); break; // row_bcast:31 -> rows 2,3
+        }
+        return __int_as_float(r);
+    };
+    v += dpp(v, 0);
+    v += dpp(v, 1);
+    v += dpp(v, 2);
+    v += dpp(v, 3);   // every lane of a 16-lane row holds the row sum
+    if (lpr > 16) v += dpp(v, 4);   // rows 1, 3: sums of rows (0,1), (2,3)
+    if (lpr > 32) v += dpp(v, 5);   // row 3: sum of all four rows
+    return v;
 }
+
+// Which instantiations take the packed 16-bit path: 16-bit activations with
+// block-scaled formats or 4-bit affine codes. kPerm: x pairs in LDS are
+// (x[k], x[k+4]) instead of (x[2k], x[2k+1]).
+template <int FMT, int BITS, int DT> struct Packed {
+    static constexpr bool kOn = DT != DT_F32 && (FMT != FMT_AFFINE || BITS == 4);
+    static constexpr bool kPerm = kOn && FMT == FMT_AFFINE;
+};
 
 }  // namespace qmv

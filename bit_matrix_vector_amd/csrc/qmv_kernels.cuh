@@ -16,7 +16,7 @@
 //     scale * sum(x*q) + bias * sum(x), sum(x) taken over fp32-widened x
 //     ("mlx 1.0.0 - quantized_nax.h" `qdot`; "ml-explore/mlx pull request
 //     4516"), for the block-scaled formats scale * sum(x*e);
-//   * reduces across the lanes of a row with a butterfly, converts to the
+//   * reduces across the lanes of a row with DPP lane moves, converts to the
 //     output type with round-to-nearest-even and stores only rows < N; rows
 //     past N re-read row N-1 so the loop has no row-dependent branch
 //     ("ml-explore/mlx pull request 4516": the fast-rows tail).
@@ -53,24 +53,54 @@ struct Geom {
     int rows_per_block;
 };
 
+// x rows of a tile. Contiguous rows (qmv) or rows picked by an index list
+// held in LDS (gather); `row(b)` is called with a run-time b.
+template <class S> struct XContig {
+    const S* x;
+    int64_t K;
+    __device__ const S* row(int b) const { return x + (int64_t)b * K; }
+};
+template <class S> struct XListed {
+    const S* x;
+    const int64_t* off;  // LDS: element offset of each staged row
+    __device__ const S* row(int b) const { return x + off[b]; }
+};
+
+// Raw loads of one unit (32 codes) for the R rows of a lane group.
+template <int FMT, int BITS, int R> struct UnitRaw {
+    uint32_t d[R][Fmt<FMT, BITS>::kWords];
+    typename Fmt<FMT, BITS>::Raw s[R];
+};
+
 // One block's tile: rows [row_base, row_base + rows_per_block) of one weight
-// matrix against NB activation rows. xrow[b] / yrow[b] are the global rows.
-template <int DT, int FMT, int BITS, int NB, int R>
+// matrix against NB activation rows.
+//
+// Per slab of K: each thread first issues global loads for its first few
+// 16-byte chunks of x, then the lane's raw weight and scale loads for its
+// first two units; only then does it write the x chunks to LDS, which waits
+// for the x loads alone (vector-memory counters retire in order, and x went
+// out first). Scale bytes stay undecoded until the unit is computed, and the
+// next unit's loads are issued under uniform branches before the current unit
+// is consumed, so two units per lane are in flight at every point.
+template <int DT, int FMT, int BITS, int NB, int R, class XR>
 __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t row_base,
                                 const uint8_t* __restrict__ w, const void* sc, const void* bi,
-                                const typename Store<DT>::S* const (&xrow)[NB],
-                                typename Store<DT>::S* const (&yrow)[NB], float gmul,
-                                typename Store<DT>::S* lds) {
+                                const XR& xr, typename Store<DT>::S* const (&yrow)[NB],
+                                float gmul, typename Store<DT>::S* lds) {
     using F = Fmt<FMT, BITS>;
     using S = typename Store<DT>::S;
+    using U = UnitRaw<FMT, BITS, R>;
     constexpr int W = F::kWords;
     constexpr int kUnitBytes = 4 * W;
+    constexpr int kPerVec = 16 / Store<DT>::kBytes;   // x values per 16-byte chunk
+    constexpr int kXAhead = 4;                        // x chunks per thread issued first
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     const int grp = lane >> g.lpr_log2;
     const int gl = lane & (g.lpr - 1);
+    const int lpr = g.lpr;
     const int groups_per_wave = 64 >> g.lpr_log2;
     const int64_t N = p.N;
     const int64_t K = p.K;
@@ -91,69 +121,59 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
 #pragma unroll
         for (int b = 0; b < NB; ++b) total[i][b] = 0.0f;
 
-    for (int64_t slab = 0; slab < K; slab += g.ks) {
-        const int ks = (int)((K - slab) < g.ks ? (K - slab) : g.ks);
-        const int us = ks >> 5;  // units in this slab
-        const int64_t u0 = slab >> 5;
-
-        // weight + scale loads of this lane's first unit go out before the
-        // x staging so they overlap it
-        uint32_t dc[R][W];
-        typename F::Scale scur[R];
-        int ul = gl;
-        if (ul < us) {
+    auto load_unit = [&](U& u_raw, int64_t u) __attribute__((always_inline)) {
 #pragma unroll
-            for (int i = 0; i < R; ++i) {
-                load_words<W>(wr[i] + (u0 + ul) * kUnitBytes, dc[i]);
-                scur[i] = F::template load_scale<DT>(sc, bi, rr[i], p.sc_per_row, u0 + ul,
-                                                     g.glog2);
-            }
+        for (int i = 0; i < R; ++i) {
+            load_words<W>(wr[i] + u * kUnitBytes, u_raw.d[i]);
+            u_raw.s[i] = F::template load_raw<DT>(sc, bi, rr[i], p.sc_per_row, u, g.glog2);
         }
+    };
 
-        // stage x[:, slab : slab + ks] into LDS. Layout per batch row: the
-        // 8-value sub-chunk sc of unit u lives at element (sc * us + u) * 8.
-        {
-            constexpr int kPerVec = 16 / Store<DT>::kBytes;  // values per 16 bytes
-            const int vec_per_row = ks / kPerVec;
+    // LDS layout per batch row: the 8-value sub-chunk sc of unit u sits at
+    // element (sc * us + u) * 8, so the lanes of a wave read consecutive 16 bytes
+    auto lds_slot = [](int e0, int us) __attribute__((always_inline)) {
+        const int u = e0 >> 5;
+        const int sub = (e0 >> 3) & 3;
+        return (sub * us + u) * 8 + (e0 & 7);
+    };
+
+    auto compute_unit = [&](const U& u_raw, int ul, int ks, int us) __attribute__((always_inline)) {
+        float acc[R][NB];
+        float sx[NB];
 #pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                const uint4* src = reinterpret_cast<const uint4*>(xrow[b] + slab);
-                S* dst = lds + b * ks;
-                for (int v = tid; v < vec_per_row; v += kThreads) {
-                    const int e0 = v * kPerVec;
-                    const int u = e0 >> 5;
-                    const int sub = (e0 >> 3) & 3;
-                    const int j0 = e0 & 7;
-                    *reinterpret_cast<uint4*>(dst + (sub * us + u) * 8 + j0) = src[v];
+        for (int b = 0; b < NB; ++b) {
+            sx[b] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < R; ++i) acc[i][b] = 0.0f;
+        }
+        typename F::Scale scl[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) scl[i] = F::template decode<DT>(u_raw.s[i]);
+
+        static_for<0, 4>([&](auto sc_c) {
+            constexpr int SC = decltype(sc_c)::value;
+            if constexpr (Packed<FMT, BITS, DT>::kOn) {
+                // packed 16-bit path: weight pairs against x pairs, 2 MACs per op
+                uint32_t xp[NB][4];
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    const v4u v = *reinterpret_cast<const v4u*>(lds + b * ks + (SC * us + ul) * 8);
+                    xp[b][0] = v.x; xp[b][1] = v.y; xp[b][2] = v.z; xp[b][3] = v.w;
+                    if constexpr (F::kNeedsSumX) {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) sx[b] = dot2<DT>(xp[b][k], pair_ones<DT>(), sx[b]);
+                    }
                 }
-            }
-        }
-        __syncthreads();
-
-        for (; ul < us; ul += g.lpr) {
-            const int un = ul + g.lpr;
-            uint32_t dn[R][W];
-            typename F::Scale snx[R];
-            if (un < us) {
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
-                    load_words<W>(wr[i] + (u0 + un) * kUnitBytes, dn[i]);
-                    snx[i] = F::template load_scale<DT>(sc, bi, rr[i], p.sc_per_row, u0 + un,
-                                                        g.glog2);
+                    uint32_t wp[4];
+                    F::template pairs<SC, DT>(u_raw.d[i], wp);
+#pragma unroll
+                    for (int b = 0; b < NB; ++b)
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) acc[i][b] = dot2<DT>(wp[k], xp[b][k], acc[i][b]);
                 }
-            }
-
-            float acc[R][NB];
-            float sx[NB];
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                sx[b] = 0.0f;
-#pragma unroll
-                for (int i = 0; i < R; ++i) acc[i][b] = 0.0f;
-            }
-
-            static_for<0, 4>([&](auto sc_c) {
-                constexpr int SC = decltype(sc_c)::value;
+            } else {
                 float xv[NB][8];
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
@@ -166,61 +186,140 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
                     float q[8];
-                    F::template decode8<SC>(dc[i], q);
+                    F::template decode8<SC>(u_raw.d[i], q);
 #pragma unroll
                     for (int b = 0; b < NB; ++b)
 #pragma unroll
                         for (int j = 0; j < 8; ++j) acc[i][b] = fmaf(q[j], xv[b][j], acc[i][b]);
                 }
-                if constexpr (FMT == FMT_NVFP4) {
-                    if constexpr (SC == 1) {
-                        // first block of 16 done: fold with its E4M3 scale
-#pragma unroll
-                        for (int i = 0; i < R; ++i)
-#pragma unroll
-                            for (int b = 0; b < NB; ++b) {
-                                total[i][b] = fmaf(scur[i].lo, acc[i][b], total[i][b]);
-                                acc[i][b] = 0.0f;
-                            }
-                    }
-                }
-            });
-
-#pragma unroll
-            for (int i = 0; i < R; ++i)
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    if constexpr (FMT == FMT_AFFINE) {
-                        total[i][b] = fmaf(scur[i].s, acc[i][b],
-                                           fmaf(scur[i].b, sx[b], total[i][b]));
-                    } else if constexpr (FMT == FMT_NVFP4) {
-                        total[i][b] = fmaf(scur[i].hi, acc[i][b], total[i][b]);
-                    } else {
-                        total[i][b] = fmaf(scur[i].s, acc[i][b], total[i][b]);
-                    }
-                }
-
-#pragma unroll
-            for (int i = 0; i < R; ++i) {
-#pragma unroll
-                for (int k = 0; k < W; ++k) dc[i][k] = dn[i][k];
-                scur[i] = snx[i];
             }
+            if constexpr (FMT == FMT_NVFP4) {
+                if constexpr (SC == 1) {
+                    // first block of 16 done: fold it with its E4M3 scale
+#pragma unroll
+                    for (int i = 0; i < R; ++i)
+#pragma unroll
+                        for (int b = 0; b < NB; ++b) {
+                            total[i][b] = fmaf(scl[i].lo, acc[i][b], total[i][b]);
+                            acc[i][b] = 0.0f;
+                        }
+                }
+            }
+        });
+
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if constexpr (FMT == FMT_AFFINE) {
+                    // scale * sum(x*q) + bias * sum(x); on the packed path the
+                    // codes entered as 1 + q/16, so sum(x*q) = 16 (acc - sum(x))
+                    if constexpr (Packed<FMT, BITS, DT>::kOn)
+                        total[i][b] = fmaf(16.0f * scl[i].s, acc[i][b] - sx[b],
+                                           fmaf(scl[i].b, sx[b], total[i][b]));
+                    else
+                        total[i][b] = fmaf(scl[i].s, acc[i][b],
+                                           fmaf(scl[i].b, sx[b], total[i][b]));
+                } else if constexpr (FMT == FMT_NVFP4) {
+                    total[i][b] = fmaf(scl[i].hi, acc[i][b], total[i][b]);
+                } else {
+                    total[i][b] = fmaf(scl[i].s, acc[i][b], total[i][b]);
+                }
+            }
+    };
+
+    // 16 bytes of x (8 values of a 16-bit type) as stored in LDS: reordered to
+    // pairs (x[k], x[k+4]) where the packed affine path expects them
+    auto stage_vec = [](v4u v) __attribute__((always_inline)) {
+        if constexpr (Packed<FMT, BITS, DT>::kPerm) {
+            v4u r;
+            r.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);  // x4 | x0
+            r.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);  // x5 | x1
+            r.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);  // x6 | x2
+            r.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);  // x7 | x3
+            return r;
+        } else {
+            return v;
+        }
+    };
+
+    for (int64_t slab = 0; slab < K; slab += g.ks) {
+        const int ks = (int)((K - slab) < g.ks ? (K - slab) : g.ks);
+        const int us = ks >> 5;                          // units in this slab
+        const int iters = (us + lpr - 1) >> g.lpr_log2;  // per lane, uniform
+        const int64_t u0 = slab >> 5;
+        const int vec_per_row = ks / kPerVec;
+
+        // (1) the first x chunks of this thread (activation row 0). Every
+        // load below is unconditional: an index past the end is clamped to
+        // the last valid chunk or unit (all such lanes read one address, so
+        // it costs one cache line), which keeps the number of loads in flight
+        // the same on every path and lets each wait name exactly the loads it
+        // needs.
+        v4u xs[kXAhead];
+        static_for<0, kXAhead>([&](auto j_c) {
+            constexpr int j = decltype(j_c)::value;
+            const int v = min(tid + j * kThreads, vec_per_row - 1);
+            xs[j] = reinterpret_cast<const v4u*>(xr.row(0) + slab)[v];
+        });
+
+        // (2) raw loads of the lane's first two units (rows clamped to N-1)
+        U A, Bq;
+        load_unit(A, u0 + min(gl, us - 1));
+        load_unit(Bq, u0 + min(gl + lpr, us - 1));
+
+        // (3) x chunks to LDS; the rest of row 0 and the other rows are
+        // loaded and stored here
+        static_for<0, kXAhead>([&](auto j_c) {
+            constexpr int j = decltype(j_c)::value;
+            const int v = tid + j * kThreads;
+            if (v < vec_per_row)
+                *reinterpret_cast<v4u*>(lds + lds_slot(v * kPerVec, us)) = stage_vec(xs[j]);
+        });
+        for (int v = tid + kXAhead * kThreads; v < vec_per_row; v += kThreads)
+            *reinterpret_cast<v4u*>(lds + lds_slot(v * kPerVec, us)) =
+                stage_vec(reinterpret_cast<const v4u*>(xr.row(0) + slab)[v]);
+#pragma unroll
+        for (int b = 1; b < NB; ++b) {
+            const S* src = xr.row(b) + slab;
+            for (int v = tid; v < vec_per_row; v += kThreads)
+                *reinterpret_cast<v4u*>(lds + b * ks + lds_slot(v * kPerVec, us)) =
+                    stage_vec(reinterpret_cast<const v4u*>(src)[v]);
+        }
+        __syncthreads();
+
+        // (4) two units in flight: compute one, then refill its buffer with
+        // the unit two steps ahead. The steady-state body runs while at least
+        // one more unit follows the pair in hand (a refill past the end is
+        // clamped); the last one or two units are consumed by a load-free
+        // epilogue, so no wave ends waiting on loads it does not use.
+        int it = 0;
+        for (; it + 2 < iters; it += 2) {
+            const int ua = gl + it * lpr;
+            const int ub = ua + lpr;
+            if (ua < us) compute_unit(A, ua, ks, us);
+            load_unit(A, u0 + min(ua + 2 * lpr, us - 1));
+            if (ub < us) compute_unit(Bq, ub, ks, us);
+            load_unit(Bq, u0 + min(ub + 2 * lpr, us - 1));
+        }
+        {
+            const int ua = gl + it * lpr;
+            const int ub = ua + lpr;
+            if (ua < us) compute_unit(A, ua, ks, us);
+            if (it + 1 < iters && ub < us) compute_unit(Bq, ub, ks, us);
         }
         __syncthreads();  // LDS is restaged for the next slab
     }
 
-    // butterfly over the LPR lanes of each row group
+    // reduce over the LPR lanes of each row group (result in its last lane)
 #pragma unroll
     for (int i = 0; i < R; ++i)
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            float v = total[i][b];
-            for (int off = g.lpr >> 1; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-            total[i][b] = v;
+            total[i][b] = group_sum(total[i][b], lpr);
         }
 
-    if (gl == 0) {
+    if (gl == lpr - 1) {
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             const int64_t r = row0 + i;
@@ -241,49 +340,41 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(LaunchParams p, Geom g) {
     using S = typename Store<DT>::S;
     extern __shared__ __align__(16) unsigned char smem[];
     S* lds = reinterpret_cast<S*>(smem);
-    const S* xrow[NB];
     S* yrow[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        xrow[b] = static_cast<const S*>(p.x) + b * p.K;
-        yrow[b] = static_cast<S*>(p.y) + b * p.N;
-    }
+    for (int b = 0; b < NB; ++b) yrow[b] = static_cast<S*>(p.y) + b * p.N;
+    const XContig<S> xr{static_cast<const S*>(p.x), p.K};
     const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
     qmv_tile<DT, FMT, BITS, NB, R>(p, g, (int64_t)blockIdx.x * g.rows_per_block, p.w, p.scales,
-                                   p.biases, xrow, yrow, gmul, lds);
+                                   p.biases, xr, yrow, gmul, lds);
 }
 
 // ---------------------------------------------------------------------------
 // Routed-expert gather. Grid (row tiles, n_experts + 1). Block (t, e) finds
 // the slots routed to expert e (a ballot scan over rhs_indices, in slot
-// order) and runs the tile on chunks of up to 8 of them, so each expert's
-// weights are streamed once per chunk of 8 slots (and for the usual handful
-// of slots per expert, exactly once). The extra column e = n_experts writes
-// the zero rows of slots whose expert or x row is out of range.
+// order) and runs the tile on chunks of them (up to 8 slots for 16-bit
+// activations, 4 for f32), so each expert's weights are streamed once per
+// chunk, and exactly once for the usual handful of slots per expert. The
+// extra column e = n_experts writes the zero rows of slots whose expert or x
+// row is out of range.
 // ---------------------------------------------------------------------------
 constexpr int kGatherChunkMax = 8;
-// Slots per chunk: 8 for 16-bit activations, 4 for f32, so the x staging of
-// a chunk fits kGatherStageBytes.
 __host__ __device__ constexpr int gather_chunk_for(int dt) { return dt == DT_F32 ? 4 : 8; }
 constexpr int kGatherStageBytes = 32 * 1024;
 
 template <int DT, int FMT, int BITS, int R>
 __device__ inline void gather_chunk(const LaunchParams& p, const Geom& g, int64_t row_base,
                                     const uint8_t* w, const void* sc, const void* bi, float gmul,
-                                    const uint32_t* list, int cnt,
+                                    const uint32_t* list, const int64_t* xoff, int cnt,
                                     typename Store<DT>::S* lds) {
     using S = typename Store<DT>::S;
+    const XListed<S> xr{static_cast<const S*>(p.x), xoff};
     auto run = [&](auto nb_c) {
         constexpr int NB = decltype(nb_c)::value;
-        const S* xrow[NB];
         S* yrow[NB];
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const uint32_t s = list[b];
-            xrow[b] = static_cast<const S*>(p.x) + (int64_t)p.lhs[s] * p.K;
-            yrow[b] = static_cast<S*>(p.y) + (int64_t)s * p.N;
-        }
-        qmv_tile<DT, FMT, BITS, NB, R>(p, g, row_base, w, sc, bi, xrow, yrow, gmul, lds);
+        for (int b = 0; b < NB; ++b) yrow[b] = static_cast<S*>(p.y) + (int64_t)list[b] * p.N;
+        qmv_tile<DT, FMT, BITS, NB, R>(p, g, row_base, w, sc, bi, xr, yrow, gmul, lds);
     };
     if constexpr (gather_chunk_for(DT) == 4) {
         switch (cnt) {
@@ -313,6 +404,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g
     S* lds = reinterpret_cast<S*>(smem);
     constexpr int kChunk = gather_chunk_for(DT);
     __shared__ uint32_t list[kChunk + kThreads];
+    __shared__ int64_t xoff[kChunk];
     __shared__ int wave_cnt[kWaves];
     __shared__ int count;
 
@@ -326,8 +418,8 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g
         // zero rows for slots with an out-of-range expert or x row
         for (int64_t s = 0; s < p.n_slots; ++s) {
             const uint32_t ex = p.rhs[s];
-            const uint32_t xr = p.lhs[s];
-            if ((int64_t)ex < p.n_experts && (int64_t)xr < p.n_x_rows) continue;
+            const uint32_t xrw = p.lhs[s];
+            if ((int64_t)ex < p.n_experts && (int64_t)xrw < p.n_x_rows) continue;
             for (int r = tid; r < g.rows_per_block; r += kThreads) {
                 const int64_t n = row_base + r;
                 if (n < p.N) static_cast<S*>(p.y)[s * p.N + n] = Store<DT>::from_f32(0.0f);
@@ -346,6 +438,13 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g
         sc = static_cast<const uint8_t*>(p.scales) + e * p.N * p.sc_per_row;
     }
     const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
+
+    auto run_chunk = [&](int cnt) {
+        if (tid < cnt) xoff[tid] = (int64_t)p.lhs[list[tid]] * p.K;
+        __syncthreads();
+        gather_chunk<DT, FMT, BITS, R>(p, g, row_base, w, sc, bi, gmul, list, xoff, cnt, lds);
+        __syncthreads();
+    };
 
     if (tid == 0) count = 0;
     __syncthreads();
@@ -367,8 +466,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g
         __syncthreads();
         int cnt = count + added;
         while (cnt >= kChunk) {
-            gather_chunk<DT, FMT, BITS, R>(p, g, row_base, w, sc, bi, gmul, list, kChunk, lds);
-            __syncthreads();
+            run_chunk(kChunk);
             // move the leftovers to the front
             const int rest = cnt - kChunk;
             uint32_t v = 0;
@@ -382,7 +480,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g
         __syncthreads();
     }
     const int cnt = count;
-    if (cnt > 0) gather_chunk<DT, FMT, BITS, R>(p, g, row_base, w, sc, bi, gmul, list, cnt, lds);
+    if (cnt > 0) run_chunk(cnt);
 }
 
 // ---------------------------------------------------------------------------
@@ -421,13 +519,32 @@ __global__ void dequant_kernel(LaunchParams p, int glog2, float* __restrict__ ou
     uint32_t d[W];
     load_words<W>(p.w + r * p.row_bytes + u * 4 * W, d);
     const typename F::Scale s =
-        F::template load_scale<DT>(p.scales, p.biases, r, p.sc_per_row, u, glog2);
+        F::template decode<DT>(
+            F::template load_raw<DT>(p.scales, p.biases, r, p.sc_per_row, u, glog2));
     const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
     float* o = out + r * p.K + u * 32;
     static_for<0, 4>([&](auto sc_c) {
         constexpr int SC = decltype(sc_c)::value;
         float q[8];
-        F::template decode8<SC>(d, q);
+        if constexpr (Packed<FMT, BITS, DT>::kOn) {
+            // decode through the packed pairs the QMV kernel uses for this dtype
+            uint32_t wp[4];
+            F::template pairs<SC, DT>(d, wp);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float lo = F::pair_code(pair_lo<DT>(wp[k]));
+                const float hi = F::pair_code(pair_hi<DT>(wp[k]));
+                if constexpr (Packed<FMT, BITS, DT>::kPerm) {
+                    q[k] = lo;
+                    q[k + 4] = hi;
+                } else {
+                    q[2 * k] = lo;
+                    q[2 * k + 1] = hi;
+                }
+            }
+        } else {
+            F::template decode8<SC>(d, q);
+        }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             o[SC * 8 + j] = dequant_value<FMT, SC>(s, q[j], gmul);

@@ -95,8 +95,9 @@ def test_device_dequant_affine_bit_exact(bmv, dtype, bits, group):
     _f32_bits_equal(got.cpu().numpy(), _rn32_affine(c))
 
 
-def test_device_dequant_mxfp4_exhaustive(bmv):
-    say("dequant mxfp4 exhaustive")
+@pytest.mark.parametrize("dt", [0, 1, 2])
+def test_device_dequant_mxfp4_exhaustive(bmv, dt):
+    say(f"dequant mxfp4 exhaustive dtype {dt}")
     exps = np.array([0, 1, 2, 100, 120, 126, 127, 128, 130, 200, 253, 254, 255], dtype=np.uint8)
     N = exps.size
     K = 32 * 8
@@ -106,13 +107,14 @@ def test_device_dequant_mxfp4_exhaustive(bmv):
     import torch
     wt_w, wt_s = to_dev(w), to_dev(scales)
     wt = bmv.make_weights("mxfp4", wt_w, wt_s, K=K)
-    got = bmv.qmv_dequant_device(wt, 2, "cuda:0").cpu().numpy()
+    got = bmv.qmv_dequant_device(wt, dt, "cuda:0").cpu().numpy()
     _f32_bits_equal(got, oracle.dequant_mxfp4(w, scales, K))
 
 
+@pytest.mark.parametrize("dt", [0, 1, 2])
 @pytest.mark.parametrize("gscale", [None, 1.0, 0.5, 3.0])
-def test_device_dequant_nvfp4_exhaustive(bmv, gscale):
-    say(f"dequant nvfp4 exhaustive g={gscale}")
+def test_device_dequant_nvfp4_exhaustive(bmv, gscale, dt):
+    say(f"dequant nvfp4 exhaustive g={gscale} dtype {dt}")
     import torch
     N = 256                          # every E4M3 scale byte, one per row
     K = 32
@@ -122,19 +124,20 @@ def test_device_dequant_nvfp4_exhaustive(bmv, gscale):
     gs = None if gscale is None else torch.tensor([gscale], dtype=torch.float32, device="cuda:0")
     dw, ds = to_dev(w), to_dev(scales)
     wt = bmv.make_weights("nvfp4", dw, ds, K=K, global_scale=gs)
-    got = bmv.qmv_dequant_device(wt, 2, "cuda:0").cpu().numpy()
+    got = bmv.qmv_dequant_device(wt, dt, "cuda:0").cpu().numpy()
     _f32_bits_equal(got, oracle.dequant_nvfp4(w, scales, K, gscale))
 
 
-def test_device_dequant_mxfp8_exhaustive(bmv):
-    say("dequant mxfp8 exhaustive")
+@pytest.mark.parametrize("dt", [0, 1, 2])
+def test_device_dequant_mxfp8_exhaustive(bmv, dt):
+    say(f"dequant mxfp8 exhaustive dtype {dt}")
     exps = np.array([0, 1, 7, 120, 127, 130, 254, 255], dtype=np.uint8)
     K = 256
     w = np.tile(np.arange(256, dtype=np.uint8), (exps.size, 1))
     scales = np.repeat(exps[:, None], K // 32, axis=1)
     dw, ds = to_dev(w), to_dev(scales)
     wt = bmv.make_weights("mxfp8", dw, ds, K=K)
-    got = bmv.qmv_dequant_device(wt, 2, "cuda:0").cpu().numpy()
+    got = bmv.qmv_dequant_device(wt, dt, "cuda:0").cpu().numpy()
     _f32_bits_equal(got, oracle.dequant_mxfp8(w, scales, K))
 
 
@@ -236,7 +239,9 @@ def test_config2_dependent_chain(bmv):
         check(y_t, y64, oracle.abs_dot(x_t, "bf16", W), "bf16", f"chain step {t}")
         norms.append(float(np.linalg.norm(oracle.storage_to_f64(y_t, "bf16"))))
         x_t = y_t
-    # the weights are norm-preserving: the chain neither dies nor blows up
+    # the weights preserve the norm in expectation: over 100 calls the chain
+    # neither dies out nor blows up (repeated products drift toward the
+    # largest eigen-direction, so allow a wide band)
     assert 0.05 * norms[0] < norms[-1] < 20 * norms[0], norms[::10]
 
 

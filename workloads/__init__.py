@@ -129,13 +129,16 @@ def affine_case(cfg_id: int, key: str, *, bits: int, group: int, K: int, N: int,
                 bias_sigma: float = 0.05) -> QmvCase:
     """Affine problem. bias_mode: 'normal' (biases ~ N(0, bias_sigma)),
     'centred8' (bias = -8*scale + U(-0.01, 0.01), with the stored scale), or
-    'chain' (norm-preserving weights for a dependent chain: scale = s0*U(0.5,
-    1.5), bias = -127.5*scale + scale*U(-0.5, 0.5), s0 = 1/(73.9*sqrt(K)))."""
+    'chain' (weights for a dependent chain of calls: scale = s0*U(0.5, 1.5),
+    bias = -127.5*scale + scale*U(-0.5, 0.5), so w = scale*(q - 127.5 + u)
+    has mean square scale^2 * (Var(q) + 1/12) = scale^2 * 73.9^2 for 8-bit q;
+    s0 = 1 / (73.9 * sqrt(K * 13/12)) makes E[w^2] = 1/K, i.e. each call
+    preserves the norm of x in expectation (13/12 = E[U(0.5, 1.5)^2]))."""
     rng = rng_for(cfg_id, key)
     w = rng.integers(0, 256, size=(N, K * bits // 8), dtype=np.uint8)
     G = K // group
     if bias_mode == "chain":
-        s0 = 1.0 / (73.9 * np.sqrt(K))
+        s0 = 1.0 / (73.9 * np.sqrt(K * 13.0 / 12.0))
         s64 = s0 * rng.uniform(0.5, 1.5, size=(N, G))
     else:
         s64 = rng.uniform(scale_range[0], scale_range[1], size=(N, G))
