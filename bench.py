@@ -122,29 +122,13 @@ def time_case(runner: Runner, steps: int, warmup: int) -> dict:
     torch.cuda.synchronize()
     graph_us = t0.elapsed_time(t1) * 1e3 / (reps * n_cap)
 
-    # (3) kernel time: an event pair around each launch, on the launch stream
-    n_ev = min(steps, 500)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n_ev)]
-    for i in range(n_ev):
-        ev[i][0].record()
-        runner.call(i, sp)
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    dev = np.array([a.elapsed_time(b) * 1e3 for a, b in ev])
-    dev_us = float(np.mean(dev))
     del g
     return {
         "bytes": runner.bytes,
-        "us_per_call": wall_us,
-        "us_per_call_graph": graph_us,
-        "kernel_us_mean": dev_us,
-        "kernel_us_p10": float(np.percentile(dev, 10)),
-        "kernel_us_p50": float(np.percentile(dev, 50)),
-        "kernel_us_p90": float(np.percentile(dev, 90)),
-        "gbps_kernel": runner.bytes / dev_us / 1e3,
-        "gbps_wall": runner.bytes / wall_us / 1e3,
-        "gbps_graph": runner.bytes / graph_us / 1e3,
+        "us_per_call_plain": wall_us,
+        "us_per_call": graph_us,
+        "gbps": runner.bytes / graph_us / 1e3,
+        "gbps_plain": runner.bytes / wall_us / 1e3,
         "copies": runner.copies,
     }
 
@@ -172,18 +156,17 @@ def time_stream_read(bmv, nbytes: int, steps: int, warmup: int, min_bytes: int =
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
-    n_ev = min(steps, 500)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(n_ev)]
-    for i in range(n_ev):
-        ev[i][0].record()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
         call(i)
-        ev[i][1].record()
+    t1.record()
     torch.cuda.synchronize()
-    us = float(np.mean([a.elapsed_time(b) * 1e3 for a, b in ev]))
+    us = t0.elapsed_time(t1) * 1e3 / steps
     del buf
-    return {"bytes": nbytes, "kernel_us_mean": us, "gbps_kernel": nbytes / us / 1e3,
-            "copies": copies, "unroll": unroll}
+    return {"bytes": nbytes, "us_per_call": us, "gbps": nbytes / us / 1e3, "copies": copies,
+            "unroll": unroll}
 
 
 def ceiling_sweep(bmv, steps: int, warmup: int) -> None:
@@ -192,8 +175,120 @@ def ceiling_sweep(bmv, steps: int, warmup: int) -> None:
         for u in (4, 8, 16):
             r = time_stream_read(bmv, int(mb * 1e6), steps, warmup, unroll=u,
                                  min_bytes=max(1 << 30, 2 * int(mb * 1e6)))
-            print(f"[ceiling] {mb:8.3f} MB unroll {u:2d}: {r['kernel_us_mean']:9.2f} us "
-                  f"{r['gbps_kernel']:8.1f} GB/s", file=sys.stderr, flush=True)
+            print(f"[ceiling] {mb:8.3f} MB unroll {u:2d}: {r['us_per_call']:9.2f} us "
+                  f"{r['gbps']:8.1f} GB/s", file=sys.stderr, flush=True)
+
+
+KERNEL_SOURCES = ("qmv_kernels.cuh", "qmv_device.h", "qmv_common.h", "qmv_inst.hip",
+                  "qmv_dispatch.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mxfp4_b1_k4096_n14336.md")
+
+
+def kernel_fingerprint() -> str:
+    """sha256 (first 16 hex digits) of the QMV kernel sources."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "bit_matrix_vector_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per launch of the headline kernel from the committed counter
+    summary, or None if there is none or it was taken on other kernel sources."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    vals = {}
+    for line in text.splitlines():
+        if line.startswith("traffic_bytes_per_launch:"):
+            vals["t"] = float(line.split(":", 1)[1])
+        if line.startswith("kernel_fingerprint:"):
+            vals["f"] = line.split(":", 1)[1].strip()
+    if vals.get("f") != kernel_fingerprint() or "t" not in vals:
+        return None
+    return round(vals["t"])
+
+
+def pmc_workload(bmv, n: int) -> None:
+    """Launch sequence for hardware-counter runs: n copies of 64 MiB (the
+    calibration kernel of known size), then n headline QMV launches."""
+    import torch
+    import workloads
+    lib = bmv.load()
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = 64 << 20
+    src = torch.empty(nbytes * 4, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    for i in range(n):
+        st = lib.qmv_bench_copy(sp, ctypes.c_void_p(src.data_ptr() + (i % 4) * nbytes),
+                                ctypes.c_void_p(dst.data_ptr()), nbytes)
+        assert st == 0
+    torch.cuda.synchronize()
+    del src, dst
+    r = Runner(bmv, workloads.config3("mxfp4", 1))
+    for i in range(n):
+        r.call(i, sp)
+    torch.cuda.synchronize()
+    print(f"[pmc] {n} copies of {nbytes} bytes, then {n} headline launches of {r.bytes} "
+          f"algorithmic bytes; kernel fingerprint {kernel_fingerprint()}", flush=True)
+
+
+def summarize_trace(trace_csv: str, kernel_substr: str) -> str:
+    """Markdown summary of a rocprofv3 kernel trace for kernels whose name
+    contains kernel_substr: duration statistics and the back-to-back period."""
+    import csv
+    rows = [r for r in csv.DictReader(open(trace_csv)) if kernel_substr in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    st = np.array([int(r["Start_Timestamp"]) for r in rows], dtype=np.int64)
+    en = np.array([int(r["End_Timestamp"]) for r in rows], dtype=np.int64)
+    d = (en - st) / 1e3
+    per = np.diff(st) / 1e3
+    back = per[per < 4 * np.median(per)]
+    name = rows[0]["Kernel_Name"] if rows else "-"
+    return "\n".join([
+        f"kernel: `{name}`",
+        f"dispatches: {len(rows)}",
+        f"duration us: mean {d.mean():.3f}, p10 {np.percentile(d, 10):.3f}, "
+        f"p50 {np.median(d):.3f}, p90 {np.percentile(d, 90):.3f}, min {d.min():.3f}, "
+        f"max {d.max():.3f}",
+        f"back-to-back start-to-start us (gaps > 4x median dropped): mean {back.mean():.3f}, "
+        f"p50 {np.median(back):.3f}",
+        f"VGPRs {rows[0]['VGPR_Count'] if rows else '-'}, grid {rows[0]['Grid_Size_X'] if rows else '-'}"
+        f", workgroup {rows[0]['Workgroup_Size_X'] if rows else '-'}",
+    ])
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, copy_bytes: int, alg_bytes: int) -> str:
+    """Markdown summary of FETCH_SIZE / WRITE_SIZE per dispatch for the copy
+    kernel (calibration, `copy_bytes` read and written) and the QMV kernel."""
+    import csv
+
+    def med(path, counter, sub):
+        v = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+             if r["Counter_Name"] == counter and sub in r["Kernel_Name"]]
+        return float(np.median(v)), len(v)
+
+    fc, nfc = med(fetch_csv, "FETCH_SIZE", "copy_kernel")
+    fq, nfq = med(fetch_csv, "FETCH_SIZE", "qmv_kernel")
+    wc, nwc = med(write_csv, "WRITE_SIZE", "copy_kernel")
+    wq, nwq = med(write_csv, "WRITE_SIZE", "qmv_kernel")
+    kib = copy_bytes / 1024
+    ff, wf = kib / fc, kib / wc
+    t = (fq * ff + wq * wf) * 1024
+    return "\n".join([
+        f"copy kernel ({copy_bytes} bytes read, {copy_bytes} written): FETCH_SIZE {fc:.1f} KiB "
+        f"(n={nfc}), WRITE_SIZE {wc:.1f} KiB (n={nwc}) -> scale factors fetch {ff:.4f}, "
+        f"write {wf:.4f}",
+        f"qmv kernel: FETCH_SIZE {fq:.1f} KiB (n={nfq}), WRITE_SIZE {wq:.1f} KiB (n={nwq}) per "
+        f"dispatch (medians)",
+        f"traffic_bytes_per_launch: {t:.0f}",
+        f"algorithmic_bytes_per_launch: {alg_bytes}",
+        f"traffic / algorithmic: {t / alg_bytes:.4f}",
+        f"kernel_fingerprint: {kernel_fingerprint()}",
+    ])
 
 
 def check_once(bmv, case) -> None:
@@ -254,7 +349,22 @@ def main() -> int:
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--ceiling-sweep", action="store_true",
                     help="only sweep the streaming-read ceiling over sizes and exit")
+    ap.add_argument("--pmc-workload", type=int, default=0, metavar="N",
+                    help="only run the counter workload (N copies, N headline launches)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "KERNEL"),
+                    help="print a summary of a rocprofv3 kernel trace and exit (no GPU)")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the calibrated FETCH/WRITE summary and exit (no GPU)")
     args = ap.parse_args()
+    if args.summarize_trace:
+        print(summarize_trace(*args.summarize_trace))
+        return 0
+    if args.summarize_counters:
+        import workloads
+        K, N, B = 4096, 14336, 1
+        alg = N * K // 2 + N * K // 32 + B * K * 2 + B * N * 2   # codes + E8M0 + x + y
+        print(summarize_counters(*args.summarize_counters, copy_bytes=64 << 20, alg_bytes=alg))
+        return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the QMV path here has "
               "no multi-GPU mode", file=sys.stderr)
@@ -268,6 +378,9 @@ def main() -> int:
     bmv.load()
     if args.ceiling_sweep:
         ceiling_sweep(bmv, min(args.steps, 200), 10)
+        return 0
+    if args.pmc_workload:
+        pmc_workload(bmv, args.pmc_workload)
         return 0
     head = workloads.config3("mxfp4", 1)
     check_once(bmv, head)
@@ -291,19 +404,20 @@ def main() -> int:
             cr = time_case(r, max(200, args.steps // 4), args.warmup)
             r.free()
             cr["case"] = name
-            cr["pct_peak_kernel"] = round(100 * cr["gbps_kernel"] / PEAK_HBM_GBPS, 1)
+            cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
             cases.append(cr)
             print(f"[bench] {name}: {json.dumps(cr)}", file=sys.stderr, flush=True)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(head)
+    traffic = committed_traffic()
     line = {
         "metric": METRIC,
-        "value": round(res["gbps_graph"], 1),
+        "value": round(res["gbps"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(res["us_per_call_graph"] / 1e3, 6),
+        "ms_per_step": round(res["us_per_call"] / 1e3, 6),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -312,17 +426,17 @@ def main() -> int:
         "config": {"workload": "MXFP4 QMV, batch 1, K=4096, N=14336, bf16 x/y, cold HBM "
                                f"({res['copies']} rotating weight copies)",
                    "B": 1, "K": 4096, "N": 14336, "format": "mxfp4"},
-        "us_per_call": round(res["us_per_call_graph"], 3),
-        "us_per_call_plain_launch": round(res["us_per_call"], 3),
-        "kernel_us": round(res["kernel_us_mean"], 3),
-        "pct_peak": round(100 * res["gbps_graph"] / PEAK_HBM_GBPS, 1),
-        "roofline": {"bound": "hbm", "achieved": round(res["gbps_kernel"], 1),
+        "us_per_call": round(res["us_per_call"], 3),
+        "us_per_call_plain_launch": round(res["us_per_call_plain"], 3),
+        "pct_peak": round(100 * res["gbps"] / PEAK_HBM_GBPS, 1),
+        "roofline": {"bound": "hbm", "achieved": round(res["gbps"], 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(res["gbps_kernel"] / PEAK_HBM_GBPS, 4), "traffic": None},
+                     "frac": round(res["gbps"] / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic},
         "cpu_baseline": cpu,
         "stream_read_ceiling": None if ceiling is None else {
-            "gbps": round(ceiling["gbps_kernel"], 1), "us": round(ceiling["kernel_us_mean"], 3),
-            "kernel_frac_of_ceiling": round(res["gbps_kernel"] / ceiling["gbps_kernel"], 4)},
+            "gbps": round(ceiling["gbps"], 1), "us_per_call": round(ceiling["us_per_call"], 3),
+            "qmv_frac_of_ceiling": round(res["gbps"] / ceiling["gbps"], 4)},
         "cases": cases,
     }
     print(json.dumps(line), flush=True)
