@@ -3,9 +3,9 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 Layout of packed codes. "wh-iron kernel-op coverage audit", section
-"Quantization precision coverage" (Track 1): sub-byte codes are packed tightly
-and LSB-first, so a 4-bit stream is the classic nibble layout, and an 8-bit
-code is one byte. The masks of `dequantize` / `qdot` in "mlx 1.0.0 -
+"Quantization precision coverage" (Track 1): sub-byte codes sit back to back,
+least significant bit first (for 4-bit codes that is two codes per byte, the
+low nibble first), and an 8-bit code takes one byte. The masks of `dequantize` / `qdot` in "mlx 1.0.0 -
 quantized_nax.h" read every width (2/3/4/5/6/8) the same way: code j of a row
 occupies bits [j*b, (j+1)*b) of the row's little-endian bit stream. The bytes
 per row follow `get_pack_factor` / `get_bytes_per_pack` of the same listing:
