@@ -182,6 +182,8 @@ __device__ inline void load_words(const uint8_t* p, uint32_t (&d)[WORDS]) {
 //   kWords            dwords of packed codes per unit of 32
 //   Raw / load_raw    the per-(row, unit) scale bytes as loaded (undecoded, so
 //                     a load in flight is not waited on until its use)
+//   kArrays, elem_bytes, elem_of_unit, lds_raw
+//                     the scale arrays as staged in LDS for a tile
 //   Scale / decode    the fp32 scale data of the unit
 //   decode8<SC>(d,q)  fp32 values of codes 8*SC .. 8*SC+7 of the unit
 // ---------------------------------------------------------------------------
@@ -203,6 +205,25 @@ template <int BITS> struct Fmt<FMT_AFFINE, BITS> {
     template <int DT>
     __device__ static inline Scale decode(const Raw& r) {
         return Scale{Store<DT>::bits_to_f32(r.s), Store<DT>::bits_to_f32(r.b)};
+    }
+    // Scale staging in LDS: two arrays (scales, biases) of T, one element per
+    // group of (1 << glog2) units.
+    static constexpr int kArrays = 2;
+    template <int DT> __host__ __device__ static constexpr int elem_bytes() {
+        return Store<DT>::kBytes;
+    }
+    __host__ __device__ static inline int64_t elem_of_unit(int64_t u, int glog2) { return u >> glog2; }
+    // raw scale of unit ul (slab-local) from the staged copy; `row` points at
+    // the row's segment of the first array, `arr` is the distance to the second
+    template <int DT>
+    __device__ static inline Raw lds_raw(const uint8_t* row, int arr, int ul, int glog2) {
+        const int o = (ul >> glog2) * Store<DT>::kBytes;
+        if constexpr (Store<DT>::kBytes == 4)
+            return Raw{*reinterpret_cast<const uint32_t*>(row + o),
+                       *reinterpret_cast<const uint32_t*>(row + arr + o)};
+        else
+            return Raw{*reinterpret_cast<const uint16_t*>(row + o),
+                       *reinterpret_cast<const uint16_t*>(row + arr + o)};
     }
     template <int SC>
     __device__ static inline void decode8(const uint32_t (&d)[kWords], float (&q)[8]) {
@@ -272,6 +293,14 @@ template <> struct Fmt<FMT_MXFP4, 4> {
     }
     template <int DT>
     __device__ static inline Scale decode(const Raw& r) { return Scale{e8m0_to_f32(r.e)}; }
+    // one E8M0 byte per unit
+    static constexpr int kArrays = 1;
+    template <int DT> __host__ __device__ static constexpr int elem_bytes() { return 1; }
+    __host__ __device__ static inline int64_t elem_of_unit(int64_t u, int) { return u; }
+    template <int DT>
+    __device__ static inline Raw lds_raw(const uint8_t* row, int, int ul, int) {
+        return Raw{row[ul]};
+    }
     template <int SC>
     __device__ static inline void decode8(const uint32_t (&d)[kWords], float (&q)[8]) {
         decode_e2m1_8(d[SC], q);
@@ -299,6 +328,14 @@ template <> struct Fmt<FMT_NVFP4, 4> {
         const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(r.e, 1.0f, false);
         return Scale{v.x, v.y};
     }
+    // two E4M3 bytes per unit
+    static constexpr int kArrays = 1;
+    template <int DT> __host__ __device__ static constexpr int elem_bytes() { return 1; }
+    __host__ __device__ static inline int64_t elem_of_unit(int64_t u, int) { return 2 * u; }
+    template <int DT>
+    __device__ static inline Raw lds_raw(const uint8_t* row, int, int ul, int) {
+        return Raw{*reinterpret_cast<const uint16_t*>(row + 2 * ul)};
+    }
     template <int SC>
     __device__ static inline void decode8(const uint32_t (&d)[kWords], float (&q)[8]) {
         decode_e2m1_8(d[SC], q);
@@ -322,6 +359,14 @@ template <> struct Fmt<FMT_MXFP8, 8> {
     }
     template <int DT>
     __device__ static inline Scale decode(const Raw& r) { return Scale{e8m0_to_f32(r.e)}; }
+    // one E8M0 byte per unit
+    static constexpr int kArrays = 1;
+    template <int DT> __host__ __device__ static constexpr int elem_bytes() { return 1; }
+    __host__ __device__ static inline int64_t elem_of_unit(int64_t u, int) { return u; }
+    template <int DT>
+    __device__ static inline Raw lds_raw(const uint8_t* row, int, int ul, int) {
+        return Raw{row[ul]};
+    }
     template <int SC>
     __device__ static inline void decode8(const uint32_t (&d)[kWords], float (&q)[8]) {
         // word 2*SC holds codes 8*SC .. 8*SC+3 (one byte each), word 2*SC+1 the next 4

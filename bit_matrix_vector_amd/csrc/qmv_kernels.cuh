@@ -23,8 +23,8 @@
 //
 // Work split: a row is covered by a lane group of LPR lanes (16, 32 or 64,
 // chosen from K so that no lane idles), unit u of the row going to lane
-// u mod LPR. A lane group owns R consecutive rows; a 256-thread block owns
-// 4 * (64 / LPR) * R rows. The lane -> unit map and the order of every sum
+// u mod LPR. A lane group owns R consecutive rows (2 or 4); a 256-thread
+// block owns 4 * (64 / LPR) * R rows. The lane -> unit map and the order of every sum
 // depend on K only, so a row's result is the same bits whatever N, B, the
 // tile or the slab split is (tail rows equal a padded call bit for bit; the
 // gathered product equals a one-row call bit for bit).
@@ -51,6 +51,8 @@ struct Geom {
     int ks;         // x slab length in elements (multiple of 32*lpr, or K)
     int glog2;      // affine: log2(group / 32)
     int rows_per_block;
+    int sc_lds_off;  // byte offset of the staged scales in LDS
+    int sc_aligned4; // scale rows can be copied in 4-byte words
 };
 
 // x rows of a tile. Contiguous rows (qmv) or rows picked by an index list
@@ -66,10 +68,9 @@ template <class S> struct XListed {
     __device__ const S* row(int b) const { return x + off[b]; }
 };
 
-// Raw loads of one unit (32 codes) for the R rows of a lane group.
+// Raw weight loads of one unit (32 codes) for the R rows of a lane group.
 template <int FMT, int BITS, int R> struct UnitRaw {
     uint32_t d[R][Fmt<FMT, BITS>::kWords];
-    typename Fmt<FMT, BITS>::Raw s[R];
 };
 
 // One block's tile: rows [row_base, row_base + rows_per_block) of one weight
@@ -94,6 +95,7 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
     constexpr int kUnitBytes = 4 * W;
     constexpr int kPerVec = 16 / Store<DT>::kBytes;   // x values per 16-byte chunk
     constexpr int kXAhead = 4;                        // x chunks per thread issued first
+    constexpr int kScAhead = 2;                       // scale words per thread issued first
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -123,11 +125,15 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
 
     auto load_unit = [&](U& u_raw, int64_t u) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < R; ++i) {
-            load_words<W>(wr[i] + u * kUnitBytes, u_raw.d[i]);
-            u_raw.s[i] = F::template load_raw<DT>(sc, bi, rr[i], p.sc_per_row, u, g.glog2);
-        }
+        for (int i = 0; i < R; ++i) load_words<W>(wr[i] + u * kUnitBytes, u_raw.d[i]);
     };
+
+    // Staged scales: per array, per block row, the scale elements of the
+    // slab's units (`seg` bytes), rows clamped to N-1 like the weights.
+    constexpr int kEB = F::template elem_bytes<DT>();
+    const int RB = g.rows_per_block;
+    const int rl0 = (wave * groups_per_wave + grp) * R;   // block-local row of i = 0
+    uint8_t* lds_sc = reinterpret_cast<uint8_t*>(lds) + g.sc_lds_off;
 
     // LDS layout per batch row: the 8-value sub-chunk sc of unit u sits at
     // element (sc * us + u) * 8, so the lanes of a wave read consecutive 16 bytes
@@ -137,7 +143,8 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
         return (sub * us + u) * 8 + (e0 & 7);
     };
 
-    auto compute_unit = [&](const U& u_raw, int ul, int ks, int us) __attribute__((always_inline)) {
+    auto compute_unit = [&](const U& u_raw, int ul, int ks, int us, int seg)
+                            __attribute__((always_inline)) {
         float acc[R][NB];
         float sx[NB];
 #pragma unroll
@@ -148,7 +155,9 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
         }
         typename F::Scale scl[R];
 #pragma unroll
-        for (int i = 0; i < R; ++i) scl[i] = F::template decode<DT>(u_raw.s[i]);
+        for (int i = 0; i < R; ++i)
+            scl[i] = F::template decode<DT>(
+                F::template lds_raw<DT>(lds_sc + (rl0 + i) * seg, RB * seg, ul, g.glog2));
 
         static_for<0, 4>([&](auto sc_c) {
             constexpr int SC = decltype(sc_c)::value;
@@ -263,6 +272,33 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
             xs[j] = reinterpret_cast<const v4u*>(xr.row(0) + slab)[v];
         });
 
+        // (1b) the first words of the tile's scale segment (when the scale
+        // rows are not 4-byte aligned these loads read x instead and are
+        // discarded; the bytes are copied after the barrier-free part below)
+        const int seg = (int)F::elem_of_unit(us, g.glog2) * kEB;   // bytes per row per array
+        const int64_t e0 = F::elem_of_unit(u0, g.glog2);
+        const int wpr = seg >> 2;
+        const int nw = g.sc_aligned4 ? F::kArrays * RB * wpr : 0;
+        auto sc_src = [&](int c) __attribute__((always_inline)) {   // byte c of the segment copy
+            const int per_arr = RB * seg;
+            const int a = c / per_arr;
+            const int rem = c - a * per_arr;
+            const int rl = rem / seg;
+            const int k = rem - rl * seg;
+            const int64_t row = min(row_base + rl, N - 1);
+            const uint8_t* base = (F::kArrays == 2 && a == 1) ? static_cast<const uint8_t*>(bi)
+                                                              : static_cast<const uint8_t*>(sc);
+            return base + (row * p.sc_per_row + e0) * kEB + k;
+        };
+        uint32_t sw[kScAhead];
+        static_for<0, kScAhead>([&](auto j_c) {
+            constexpr int j = decltype(j_c)::value;
+            const int c = min(tid + j * kThreads, nw - 1);
+            const uint32_t* src = nw > 0 ? reinterpret_cast<const uint32_t*>(sc_src(4 * c))
+                                         : reinterpret_cast<const uint32_t*>(xr.row(0) + slab);
+            sw[j] = *src;
+        });
+
         // (2) raw loads of the lane's first two units (rows clamped to N-1)
         U A, Bq;
         load_unit(A, u0 + min(gl, us - 1));
@@ -286,6 +322,20 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
                 *reinterpret_cast<v4u*>(lds + b * ks + lds_slot(v * kPerVec, us)) =
                     stage_vec(reinterpret_cast<const v4u*>(src)[v]);
         }
+        // (3b) scale segment to LDS
+        if (nw > 0) {
+            static_for<0, kScAhead>([&](auto j_c) {
+                constexpr int j = decltype(j_c)::value;
+                const int c = tid + j * kThreads;
+                if (c < nw) reinterpret_cast<uint32_t*>(lds_sc)[c] = sw[j];
+            });
+            for (int c = tid + kScAhead * kThreads; c < nw; c += kThreads)
+                reinterpret_cast<uint32_t*>(lds_sc)[c] =
+                    *reinterpret_cast<const uint32_t*>(sc_src(4 * c));
+        } else {
+            const int nbytes = F::kArrays * RB * seg;
+            for (int c = tid; c < nbytes; c += kThreads) lds_sc[c] = *sc_src(c);
+        }
         __syncthreads();
 
         // (4) two units in flight: compute one, then refill its buffer with
@@ -297,16 +347,16 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
         for (; it + 2 < iters; it += 2) {
             const int ua = gl + it * lpr;
             const int ub = ua + lpr;
-            if (ua < us) compute_unit(A, ua, ks, us);
+            if (ua < us) compute_unit(A, ua, ks, us, seg);
             load_unit(A, u0 + min(ua + 2 * lpr, us - 1));
-            if (ub < us) compute_unit(Bq, ub, ks, us);
+            if (ub < us) compute_unit(Bq, ub, ks, us, seg);
             load_unit(Bq, u0 + min(ub + 2 * lpr, us - 1));
         }
         {
             const int ua = gl + it * lpr;
             const int ub = ua + lpr;
-            if (ua < us) compute_unit(A, ua, ks, us);
-            if (it + 1 < iters && ub < us) compute_unit(Bq, ub, ks, us);
+            if (ua < us) compute_unit(A, ua, ks, us, seg);
+            if (it + 1 < iters && ub < us) compute_unit(Bq, ub, ks, us, seg);
         }
         __syncthreads();  // LDS is restaged for the next slab
     }
@@ -555,7 +605,12 @@ __global__ void dequant_kernel(LaunchParams p, int glog2, float* __restrict__ ou
 // ---------------------------------------------------------------------------
 // Host-side launch helpers.
 // ---------------------------------------------------------------------------
-constexpr int kRows = 4;  // rows per lane group
+// Rows per lane group. Fewer rows per wave means more waves and a shorter
+// compute tail after the last bytes arrive; more rows reuse each x slice read
+// from LDS more often. Measured on MI355X (MXFP4, B=1, K=4096, N=14336):
+// R=2 beats R=1, 3 and 4. Larger batches keep R=4 for the x reuse.
+template <int NB> constexpr int rows_for() { return NB <= 2 ? 2 : 4; }
+constexpr int kGatherRows = 2;
 
 int ilog2(int v) {
     int r = 0;
@@ -579,40 +634,83 @@ int pick_lpr(int64_t K) {
     return best;
 }
 
-// Geometry of a launch staging nb activation rows in at most `budget` bytes
-// of LDS. The slab length is a multiple of 32 * lpr (or all of K), which keeps
-// the lane -> unit map the same for every slab split.
-Geom make_geom(const LaunchParams& p, int nb, int budget) {
+// Geometry of a launch staging nb activation rows (and the tile's scales) in
+// about `budget` bytes of LDS. The slab length is a multiple of 32 * lpr (or
+// all of K), which keeps the lane -> unit map the same for every slab split.
+template <int DT, int FMT, int BITS>
+Geom make_geom(const LaunchParams& p, int nb, int budget, int rows) {
+    using F = Fmt<FMT, BITS>;
     Geom g;
     g.lpr = pick_lpr(p.K);
     g.lpr_log2 = ilog2(g.lpr);
-    const int tbytes = p.dtype == DT_F32 ? 4 : 2;
-    const int64_t cap = budget / (nb * tbytes);              // elements per batch row
-    const int64_t quantum = 32LL * g.lpr;                    // <= 2048 <= cap always
-    int64_t ks = p.K <= cap ? p.K : (cap / quantum) * quantum;
-    g.ks = (int)(ks > 0 ? ks : 32);
-    g.glog2 = p.format == FMT_AFFINE ? ilog2(p.group / 32) : 0;
-    g.rows_per_block = kWaves * (64 / g.lpr) * kRows;
+    g.glog2 = FMT == FMT_AFFINE ? ilog2(p.group / 32) : 0;
+    g.rows_per_block = kWaves * (64 / g.lpr) * rows;
+    const int64_t t = DT == DT_F32 ? 4 : 2;
+    const int64_t eb = F::template elem_bytes<DT>();
+    const int64_t RB = g.rows_per_block;
+    const int64_t U = p.K / 32;
+    auto lds_for = [&](int64_t units) {
+        const int64_t x = (nb * 32 * units * t + 15) / 16 * 16;
+        return x + F::kArrays * RB * F::elem_of_unit(units, g.glog2) * eb;
+    };
+    int64_t ks_units = U;
+    if (U > 0 && lds_for(U) > budget) {
+        int64_t nq = budget / lds_for(g.lpr);
+        if (nq < 1) nq = 1;
+        ks_units = nq * g.lpr < U ? nq * g.lpr : U;
+    }
+    g.ks = (int)(ks_units > 0 ? 32 * ks_units : 32);
+    g.sc_lds_off = (int)((nb * (int64_t)g.ks * t + 15) / 16 * 16);
+    // 4-byte copies of the scale rows need every row start, slab start and
+    // segment length to be a multiple of 4 bytes
+    const int64_t row_stride = p.sc_per_row * eb;
+    const int64_t seg_full = F::elem_of_unit(ks_units, g.glog2) * eb;
+    const int64_t last_units = ks_units > 0 ? U - ((U - 1) / ks_units) * ks_units : 0;
+    const int64_t seg_last = F::elem_of_unit(last_units, g.glog2) * eb;
+    bool al = row_stride % 4 == 0 && seg_full % 4 == 0 && seg_last % 4 == 0 &&
+              (reinterpret_cast<uintptr_t>(p.scales) & 3) == 0;
+    if (F::kArrays == 2) al = al && (reinterpret_cast<uintptr_t>(p.biases) & 3) == 0;
+    g.sc_aligned4 = al ? 1 : 0;
     return g;
 }
 
-size_t stage_bytes(const LaunchParams& p, const Geom& g, int nb) {
-    const int tbytes = p.dtype == DT_F32 ? 4 : 2;
-    return (size_t)nb * (size_t)g.ks * (size_t)tbytes;
+template <int DT, int FMT, int BITS>
+size_t stage_bytes(const LaunchParams& p, const Geom& g) {
+    using F = Fmt<FMT, BITS>;
+    const int64_t units = g.ks / 32;
+    return (size_t)g.sc_lds_off + (size_t)(F::kArrays * (int64_t)g.rows_per_block *
+                                           F::elem_of_unit(units, g.glog2) *
+                                           F::template elem_bytes<DT>());
+}
+
+// Dynamic LDS above 64 KB must be requested per kernel (gfx950 has 160 KB
+// per workgroup); done once per instance.
+template <class Kern>
+int allow_lds(Kern* kern, size_t bytes) {
+    if (bytes <= 64 * 1024) return 0;
+    static size_t granted = 0;
+    if (bytes <= granted) return 0;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)bytes);
+    if (e == hipSuccess) granted = bytes;
+    return (int)e;
 }
 
 template <int DT, int FMT, int BITS>
 int launch_qmv_t(const LaunchParams& p, hipStream_t st) {
     const int nb = (int)p.B;
-    const Geom g = make_geom(p, nb, kMaxStageBytes);
-    const dim3 grid((unsigned)((p.N + g.rows_per_block - 1) / g.rows_per_block));
-    const size_t lds = stage_bytes(p, g, nb);
     switch (nb) {
-#define QMV_CASE(n)                                                                        \
-    case n:                                                                                \
-        hipLaunchKernelGGL((qmv_kernel<DT, FMT, BITS, n, kRows>), grid, dim3(kThreads), lds, \
-                           st, p, g);                                                      \
-        break;
+#define QMV_CASE(n)                                                                         \
+    case n: {                                                                               \
+        const Geom g = make_geom<DT, FMT, BITS>(p, n, kMaxStageBytes, rows_for<n>());       \
+        const dim3 grid((unsigned)((p.N + g.rows_per_block - 1) / g.rows_per_block));      \
+        const size_t lds = stage_bytes<DT, FMT, BITS>(p, g);                                \
+        auto* kern = &qmv_kernel<DT, FMT, BITS, n, rows_for<n>()>;                          \
+        if (const int e = allow_lds(kern, lds)) return e;                                   \
+        hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, p, g);                      \
+        break;                                                                              \
+    }
         QMV_CASE(1) QMV_CASE(2) QMV_CASE(3) QMV_CASE(4)
         QMV_CASE(5) QMV_CASE(6) QMV_CASE(7) QMV_CASE(8)
 #undef QMV_CASE
@@ -624,12 +722,12 @@ int launch_qmv_t(const LaunchParams& p, hipStream_t st) {
 template <int DT, int FMT, int BITS>
 int launch_gather_t(const LaunchParams& p, hipStream_t st) {
     constexpr int kChunk = gather_chunk_for(DT);
-    const Geom g = make_geom(p, kChunk, kGatherStageBytes);
+    const Geom g = make_geom<DT, FMT, BITS>(p, kChunk, kGatherStageBytes, kGatherRows);
     const dim3 grid((unsigned)((p.N + g.rows_per_block - 1) / g.rows_per_block),
                     (unsigned)(p.n_experts + 1));
-    const size_t lds = stage_bytes(p, g, kChunk);
-    hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kRows>), grid, dim3(kThreads), lds, st, p,
-                       g);
+    const size_t lds = stage_bytes<DT, FMT, BITS>(p, g);
+    hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kGatherRows>), grid, dim3(kThreads), lds,
+                       st, p, g);
     return (int)hipGetLastError();
 }
 
