@@ -94,7 +94,7 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
     constexpr int W = F::kWords;
     constexpr int kUnitBytes = 4 * W;
     constexpr int kPerVec = 16 / Store<DT>::kBytes;   // x values per 16-byte chunk
-    constexpr int kXAhead = 4;                        // x chunks per thread issued first
+    constexpr int kXAhead = 2;                        // x chunks per thread issued first
     constexpr int kScAhead = 2;                       // scale words per thread issued first
 
     const int tid = threadIdx.x;
@@ -108,13 +108,14 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
     const int64_t K = p.K;
     const int64_t row0 = row_base + (int64_t)(wave * groups_per_wave + grp) * R;
 
-    const uint8_t* wr[R];
-    int64_t rr[R];
+    // Weight addresses: the block's first row (uniform, in scalar registers)
+    // plus a 32-bit per-lane offset; tail rows re-read the last valid row.
+    const uint8_t* wblk = w + row_base * p.row_bytes;
+    uint32_t wo[R];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         const int64_t r = row0 + i;
-        rr[i] = r < N ? r : N - 1;  // tail rows re-read the last valid row
-        wr[i] = w + rr[i] * p.row_bytes;
+        wo[i] = (uint32_t)(((r < N ? r : N - 1) - row_base) * p.row_bytes);
     }
 
     float total[R][NB];
@@ -125,7 +126,8 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
 
     auto load_unit = [&](U& u_raw, int64_t u) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < R; ++i) load_words<W>(wr[i] + u * kUnitBytes, u_raw.d[i]);
+        for (int i = 0; i < R; ++i)
+            load_words<W>(wblk + (wo[i] + (uint32_t)(u * kUnitBytes)), u_raw.d[i]);
     };
 
     // Staged scales: per array, per block row, the scale elements of the
@@ -290,13 +292,35 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
                                                               : static_cast<const uint8_t*>(sc);
             return base + (row * p.sc_per_row + e0) * kEB + k;
         };
+        // When the slab covers whole rows (one slab), each array's segment for
+        // the block is one contiguous range and a word's source needs no
+        // division; a word past the array end (rows >= N) is clamped to its
+        // last word.
+        const bool whole_rows = g.ks >= K;
+        const int64_t row_stride = p.sc_per_row * kEB;
+        auto sc_word = [&](int c) __attribute__((always_inline)) {
+            const uint8_t* q;
+            if (whole_rows) {
+                const int per_arr = RB * seg;
+                const bool second = F::kArrays == 2 && 4 * c >= per_arr;
+                const uint8_t* base = second ? static_cast<const uint8_t*>(bi)
+                                             : static_cast<const uint8_t*>(sc);
+                const int64_t off = row_base * row_stride + (second ? 4 * c - per_arr : 4 * c);
+                const int64_t last = N * row_stride - 4;
+                q = base + (off < last ? off : last);
+            } else {
+                q = sc_src(4 * c);
+            }
+            return *reinterpret_cast<const uint32_t*>(q);
+        };
         uint32_t sw[kScAhead];
         static_for<0, kScAhead>([&](auto j_c) {
             constexpr int j = decltype(j_c)::value;
-            const int c = min(tid + j * kThreads, nw - 1);
-            const uint32_t* src = nw > 0 ? reinterpret_cast<const uint32_t*>(sc_src(4 * c))
-                                         : reinterpret_cast<const uint32_t*>(xr.row(0) + slab);
-            sw[j] = *src;
+            if (nw > 0) {
+                sw[j] = sc_word(min(tid + j * kThreads, nw - 1));
+            } else {
+                sw[j] = *reinterpret_cast<const uint32_t*>(xr.row(0) + slab);
+            }
         });
 
         // (2) raw loads of the lane's first two units (rows clamped to N-1)
@@ -330,8 +354,7 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
                 if (c < nw) reinterpret_cast<uint32_t*>(lds_sc)[c] = sw[j];
             });
             for (int c = tid + kScAhead * kThreads; c < nw; c += kThreads)
-                reinterpret_cast<uint32_t*>(lds_sc)[c] =
-                    *reinterpret_cast<const uint32_t*>(sc_src(4 * c));
+                reinterpret_cast<uint32_t*>(lds_sc)[c] = sc_word(c);
         } else {
             const int nbytes = F::kArrays * RB * seg;
             for (int c = tid; c < nbytes; c += kThreads) lds_sc[c] = *sc_src(c);
