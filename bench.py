@@ -84,6 +84,102 @@ class Runner:
         self.w = self.s = self.b = None
 
 
+class GatherRunner:
+    """Pre-marshalled gather_qmv calls over rotating copies of the expert-
+    stacked weights (config 5)."""
+
+    def __init__(self, bmv, m, min_bytes: int = 1 << 29):
+        import torch
+        self.m = m
+        self.lib = bmv.load()
+        self.x = _dev(m.x, m.dtype)
+        self.lhs = torch.from_numpy(m.lhs.view(np.int32)).to("cuda:0")
+        self.rhs = torch.from_numpy(m.rhs.view(np.int32)).to("cuda:0")
+        w0 = _dev(m.w)
+        s0 = _dev(m.scales, m.dtype if m.fmt == "affine" else None)
+        b0 = _dev(m.biases, m.dtype) if m.biases is not None else None
+        per = w0.nbytes + s0.nbytes + (b0.nbytes if b0 is not None else 0)
+        self.copies = max(2, -(-min_bytes // per))
+        self.keep = []
+        self.wts = []
+        for i in range(self.copies):
+            w = w0 if i == 0 else w0.clone()
+            sc = s0 if i == 0 else s0.clone()
+            bi = None if b0 is None else (b0 if i == 0 else b0.clone())
+            self.keep.append((w, sc, bi))
+            self.wts.append(bmv.make_weights(m.fmt, w, sc, bi, K=m.K, bits=m.bits,
+                                             group_size=m.group))
+        self.y = torch.empty((m.lhs.size, m.N), dtype=self.x.dtype, device="cuda:0")
+        self.dt = {"f32": 0, "f16": 1, "bf16": 2}[m.dtype]
+        self.bytes = m.algorithmic_bytes()
+
+    def call(self, i: int, stream) -> None:
+        vp = ctypes.c_void_p
+        st = self.lib.gather_qmv(stream, self.dt, ctypes.byref(self.wts[i % self.copies]),
+                                 vp(self.x.data_ptr()), self.x.shape[0],
+                                 vp(self.lhs.data_ptr()), vp(self.rhs.data_ptr()),
+                                 self.m.lhs.size, vp(self.y.data_ptr()))
+        if st != 0:
+            raise RuntimeError(self.lib.qmv_last_error().decode())
+
+    def free(self):
+        self.keep = self.wts = None
+
+
+def time_chain(bmv, steps: int = 100) -> dict:
+    """Config 2: a dependent chain of 100 calls (8-bit affine g64, K=N=2560,
+    bf16), each output the next input; same weights every call (warm), as in
+    a decode loop. Timed as plain launches and as one HIP graph."""
+    import torch
+    import workloads
+    c = workloads.config2(2560)
+    lib = bmv.load()
+    x = _dev(c.x, "bf16")
+    w, s, b = _dev(c.w), _dev(c.scales, "bf16"), _dev(c.biases, "bf16")
+    bufs = [x.clone(), torch.empty_like(x)]
+    vp = ctypes.c_void_p
+
+    def chain(stream):
+        for t in range(steps):
+            st = lib.qmv_affine(stream, 2, 1, c.K, c.N, vp(bufs[t % 2].data_ptr()),
+                                vp(w.data_ptr()), vp(s.data_ptr()), vp(b.data_ptr()), 8, 64,
+                                vp(bufs[(t + 1) % 2].data_ptr()))
+            if st != 0:
+                raise RuntimeError(lib.qmv_last_error().decode())
+
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(3):
+        chain(sp)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    reps = 20
+    t0.record()
+    for _ in range(reps):
+        chain(sp)
+    t1.record()
+    torch.cuda.synchronize()
+    plain = t0.elapsed_time(t1) * 1e3 / (reps * steps)
+    g = torch.cuda.CUDAGraph()
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=cs):
+        chain(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(reps):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    graph = t0.elapsed_time(t1) * 1e3 / (reps * steps)
+    del g
+    return {"case": "config2 chain of 100: affine 8b g64 K=N=2560 bf16, warm weights",
+            "bytes": c.algorithmic_bytes(), "us_per_call_plain": plain,
+            "us_per_call_graph": graph, "gbps_graph": c.algorithmic_bytes() / graph / 1e3}
+
+
 def time_case(runner: Runner, steps: int, warmup: int) -> dict:
     import torch
     stream = torch.cuda.current_stream()
@@ -347,6 +443,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the whole affine sweep (config 4) to stderr")
     ap.add_argument("--ceiling-sweep", action="store_true",
                     help="only sweep the streaming-read ceiling over sizes and exit")
     ap.add_argument("--pmc-workload", type=int, default=0, metavar="N",
@@ -407,6 +505,34 @@ def main() -> int:
             cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
             cases.append(cr)
             print(f"[bench] {name}: {json.dumps(cr)}", file=sys.stderr, flush=True)
+
+    if not args.headline_only:
+        for fmt, proj in (("mxfp4", "gate_up"), ("mxfp4", "down"), ("affine", "gate_up"),
+                          ("affine", "down")):
+            m = workloads.config5(fmt, proj)
+            r = GatherRunner(bmv, m)
+            cr = time_case(r, max(100, args.steps // 10), 10)
+            r.free()
+            cr["case"] = (f"config5 gather {fmt} {proj}: 64 experts, {m.lhs.size} slots, "
+                          f"{len(m.distinct_experts())} distinct, K={m.K} N={m.N} bf16")
+            cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
+            cases.append(cr)
+            print(f"[bench] {cr['case']}: {json.dumps(cr)}", file=sys.stderr, flush=True)
+        ch = time_chain(bmv)
+        cases.append(ch)
+        print(f"[bench] {ch['case']}: {json.dumps(ch)}", file=sys.stderr, flush=True)
+    if args.sweep:
+        for bits in workloads.AFFINE_BITS:
+            for group in workloads.AFFINE_GROUPS:
+                for B in (1, 2, 4, 8):
+                    for dt in workloads.DTYPES:
+                        c = workloads.config4(bits, group, B, dt)
+                        r = Runner(bmv, c, min_bytes=1 << 29)
+                        cr = time_case(r, 200, 10)
+                        r.free()
+                        cr["case"] = f"config4 affine b{bits} g{group} B{B} {dt} K=N=4096"
+                        cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
+                        print(f"[sweep] {json.dumps(cr)}", file=sys.stderr, flush=True)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline(head)
     traffic = committed_traffic()

@@ -425,14 +425,17 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(LaunchParams p, Geom g) {
 // ---------------------------------------------------------------------------
 // Routed-expert gather. Grid (row tiles, n_experts + 1). Block (t, e) finds
 // the slots routed to expert e (a ballot scan over rhs_indices, in slot
-// order) and runs the tile on chunks of them (up to 8 slots for 16-bit
-// activations, 4 for f32), so each expert's weights are streamed once per
-// chunk, and exactly once for the usual handful of slots per expert. The
-// extra column e = n_experts writes the zero rows of slots whose expert or x
-// row is out of range.
+// order) and runs the tile on chunks of up to two of them; each expert's
+// weights come from HBM once per call (further chunks of the same tile re-read
+// them from L2). The extra column e = n_experts writes the zero rows of slots
+// whose expert or x row is out of range.
 // ---------------------------------------------------------------------------
-constexpr int kGatherChunkMax = 8;
-__host__ __device__ constexpr int gather_chunk_for(int dt) { return dt == DT_F32 ? 4 : 8; }
+// Slots per chunk. A kernel carries the register budget of its largest
+// instantiated tile, so chunks stay at two activation rows (the tile of a
+// one- or two-row QMV); an expert with more slots runs several chunks over the
+// same tile, whose weights the repeat reads find in L2.
+constexpr int kGatherChunkMax = 2;
+__host__ __device__ constexpr int gather_chunk_for(int) { return kGatherChunkMax; }
 constexpr int kGatherStageBytes = 32 * 1024;
 
 template <int DT, int FMT, int BITS, int R>
@@ -449,25 +452,10 @@ __device__ inline void gather_chunk(const LaunchParams& p, const Geom& g, int64_
         for (int b = 0; b < NB; ++b) yrow[b] = static_cast<S*>(p.y) + (int64_t)list[b] * p.N;
         qmv_tile<DT, FMT, BITS, NB, R>(p, g, row_base, w, sc, bi, xr, yrow, gmul, lds);
     };
-    if constexpr (gather_chunk_for(DT) == 4) {
-        switch (cnt) {
-            case 1: run(std::integral_constant<int, 1>{}); break;
-            case 2: run(std::integral_constant<int, 2>{}); break;
-            case 3: run(std::integral_constant<int, 3>{}); break;
-            default: run(std::integral_constant<int, 4>{}); break;
-        }
-    } else {
-        switch (cnt) {
-            case 1: run(std::integral_constant<int, 1>{}); break;
-            case 2: run(std::integral_constant<int, 2>{}); break;
-            case 3: run(std::integral_constant<int, 3>{}); break;
-            case 4: run(std::integral_constant<int, 4>{}); break;
-            case 5: run(std::integral_constant<int, 5>{}); break;
-            case 6: run(std::integral_constant<int, 6>{}); break;
-            case 7: run(std::integral_constant<int, 7>{}); break;
-            default: run(std::integral_constant<int, 8>{}); break;
-        }
-    }
+    if (cnt == 1)
+        run(std::integral_constant<int, 1>{});
+    else
+        run(std::integral_constant<int, 2>{});
 }
 
 template <int DT, int FMT, int BITS, int R>
