@@ -51,8 +51,10 @@ qmv_status_t check_common(const char* fn, int dtype, int64_t B, int64_t K, int64
     if (K % 32)
         return fail(QMV_ERR_INVALID_ARGUMENT, "%s: K=%lld is not a multiple of 32", fn,
                     (long long)K);
-    if (K > (int64_t)1 << 28 || N > (int64_t)1 << 28)
-        return fail(QMV_ERR_UNSUPPORTED, "%s: K or N above 2^28", fn);
+    // kernels address a tile's rows with 32-bit offsets from the tile's first
+    // row: up to 64 rows of K bytes stay below 2^30 with K <= 2^24
+    if (K > (int64_t)1 << 24 || N > (int64_t)1 << 28)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: K above 2^24 or N above 2^28", fn);
     return QMV_OK;
 }
 

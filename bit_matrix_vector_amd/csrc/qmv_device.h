@@ -184,6 +184,8 @@ __device__ inline void load_words(const uint8_t* p, uint32_t (&d)[WORDS]) {
 //                     a load in flight is not waited on until its use)
 //   kArrays, elem_bytes, elem_of_unit, lds_raw
 //                     the scale arrays as staged in LDS for a tile
+//   global_raw        the same bytes read from the global arrays at a byte
+//                     offset from uniform bases
 //   Scale / decode    the fp32 scale data of the unit
 //   decode8<SC>(d,q)  fp32 values of codes 8*SC .. 8*SC+7 of the unit
 // ---------------------------------------------------------------------------
@@ -224,6 +226,16 @@ template <int BITS> struct Fmt<FMT_AFFINE, BITS> {
         else
             return Raw{*reinterpret_cast<const uint16_t*>(row + o),
                        *reinterpret_cast<const uint16_t*>(row + arr + o)};
+    }
+    // raw scale of unit u from the global arrays: `row_off` is the row's
+    // byte offset from both bases (a 32-bit lane offset on a uniform base)
+    template <int DT>
+    __device__ static inline Raw global_raw(const uint8_t* sc, const uint8_t* bi,
+                                            uint32_t row_off, int u, int glog2) {
+        const uint32_t o = row_off + (uint32_t)(u >> glog2) * Store<DT>::kBytes;
+        using S = typename Store<DT>::S;
+        return Raw{Store<DT>::load_bits(reinterpret_cast<const S*>(sc + o)),
+                   Store<DT>::load_bits(reinterpret_cast<const S*>(bi + o))};
     }
     template <int SC>
     __device__ static inline void decode8(const uint32_t (&d)[kWords], float (&q)[8]) {
@@ -301,6 +313,11 @@ template <> struct Fmt<FMT_MXFP4, 4> {
     __device__ static inline Raw lds_raw(const uint8_t* row, int, int ul, int) {
         return Raw{row[ul]};
     }
+    template <int DT>
+    __device__ static inline Raw global_raw(const uint8_t* sc, const uint8_t*, uint32_t row_off,
+                                            int u, int) {
+        return Raw{sc[row_off + (uint32_t)u]};
+    }
     template <int SC>
     __device__ static inline void decode8(const uint32_t (&d)[kWords], float (&q)[8]) {
         decode_e2m1_8(d[SC], q);
@@ -336,6 +353,11 @@ template <> struct Fmt<FMT_NVFP4, 4> {
     __device__ static inline Raw lds_raw(const uint8_t* row, int, int ul, int) {
         return Raw{*reinterpret_cast<const uint16_t*>(row + 2 * ul)};
     }
+    template <int DT>
+    __device__ static inline Raw global_raw(const uint8_t* sc, const uint8_t*, uint32_t row_off,
+                                            int u, int) {
+        return Raw{*reinterpret_cast<const uint16_t*>(sc + (row_off + 2u * (uint32_t)u))};
+    }
     template <int SC>
     __device__ static inline void decode8(const uint32_t (&d)[kWords], float (&q)[8]) {
         decode_e2m1_8(d[SC], q);
@@ -366,6 +388,11 @@ template <> struct Fmt<FMT_MXFP8, 8> {
     template <int DT>
     __device__ static inline Raw lds_raw(const uint8_t* row, int, int ul, int) {
         return Raw{row[ul]};
+    }
+    template <int DT>
+    __device__ static inline Raw global_raw(const uint8_t* sc, const uint8_t*, uint32_t row_off,
+                                            int u, int) {
+        return Raw{sc[row_off + (uint32_t)u]};
     }
     template <int SC>
     __device__ static inline void decode8(const uint32_t (&d)[kWords], float (&q)[8]) {

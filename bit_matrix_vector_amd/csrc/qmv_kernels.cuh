@@ -34,6 +34,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "qmv_common.h"
@@ -53,6 +54,7 @@ struct Geom {
     int rows_per_block;
     int sc_lds_off;  // byte offset of the staged scales in LDS
     int sc_aligned4; // scale rows can be copied in 4-byte words
+    int tiles_per_block;  // gather: consecutive row tiles one block runs
 };
 
 // x rows of a tile. Contiguous rows (qmv) or rows picked by an index list
@@ -68,10 +70,132 @@ template <class S> struct XListed {
     __device__ const S* row(int b) const { return x + off[b]; }
 };
 
+// LDS layout of a staged x row: the 8-value sub-chunk sc of unit u sits at
+// element (sc * us + u) * 8 (us = units in the slab), so the lanes of a wave,
+// which walk consecutive units, read consecutive 16 bytes.
+__device__ inline int x_lds_slot(int e0, int us) {
+    const int u = e0 >> 5;
+    const int sub = (e0 >> 3) & 3;
+    return (sub * us + u) * 8 + (e0 & 7);
+}
+
+// 16 bytes of x (8 values of a 16-bit type) as stored in LDS: reordered to
+// pairs (x[k], x[k+4]) where the packed affine path expects them.
+template <int FMT, int BITS, int DT>
+__device__ inline v4u stage_vec(v4u v) {
+    if constexpr (Packed<FMT, BITS, DT>::kPerm) {
+        v4u r;
+        r.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);  // x4 | x0
+        r.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);  // x5 | x1
+        r.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);  // x6 | x2
+        r.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);  // x7 | x3
+        return r;
+    } else {
+        return v;
+    }
+}
+
 // Raw weight loads of one unit (32 codes) for the R rows of a lane group.
 template <int FMT, int BITS, int R> struct UnitRaw {
     uint32_t d[R][Fmt<FMT, BITS>::kWords];
 };
+
+// One unit (32 codes) of R rows against NB staged x rows, folded into the
+// row totals with its scales: fp32 accumulation, then scale * acc (+ bias *
+// sum(x) for affine). `ul` is the unit's index within the staged slab of `us`
+// units and `ks` elements per x row. Shared by every tile loop, so a row's
+// result does not depend on which loop computed it.
+template <int DT, int FMT, int BITS, int NB, int R>
+__device__ inline void unit_fma(const UnitRaw<FMT, BITS, R>& u_raw,
+                                const typename Fmt<FMT, BITS>::Scale (&scl)[R],
+                                const typename Store<DT>::S* lds, int ul, int ks, int us,
+                                float (&total)[R][NB]) {
+    using F = Fmt<FMT, BITS>;
+    float acc[R][NB];
+    float sx[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        sx[b] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < R; ++i) acc[i][b] = 0.0f;
+    }
+    static_for<0, 4>([&](auto sc_c) {
+        constexpr int SC = decltype(sc_c)::value;
+        if constexpr (Packed<FMT, BITS, DT>::kOn) {
+            // packed 16-bit path: weight pairs against x pairs, 2 MACs per op
+            uint32_t xp[NB][4];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const v4u v = *reinterpret_cast<const v4u*>(lds + b * ks + (SC * us + ul) * 8);
+                xp[b][0] = v.x; xp[b][1] = v.y; xp[b][2] = v.z; xp[b][3] = v.w;
+                if constexpr (F::kNeedsSumX) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) sx[b] = dot2<DT>(xp[b][k], pair_ones<DT>(), sx[b]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                uint32_t wp[4];
+                F::template pairs<SC, DT>(u_raw.d[i], wp);
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) acc[i][b] = dot2<DT>(wp[k], xp[b][k], acc[i][b]);
+            }
+        } else {
+            float xv[NB][8];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                lds_load8<DT>(lds + b * ks + (SC * us + ul) * 8, xv[b]);
+                if constexpr (F::kNeedsSumX) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) sx[b] += xv[b][j];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                float q[8];
+                F::template decode8<SC>(u_raw.d[i], q);
+#pragma unroll
+                for (int b = 0; b < NB; ++b)
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) acc[i][b] = fmaf(q[j], xv[b][j], acc[i][b]);
+            }
+        }
+        if constexpr (FMT == FMT_NVFP4) {
+            if constexpr (SC == 1) {
+                // first block of 16 done: fold it with its E4M3 scale
+#pragma unroll
+                for (int i = 0; i < R; ++i)
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        total[i][b] = fmaf(scl[i].lo, acc[i][b], total[i][b]);
+                        acc[i][b] = 0.0f;
+                    }
+            }
+        }
+    });
+
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            if constexpr (FMT == FMT_AFFINE) {
+                // scale * sum(x*q) + bias * sum(x); on the packed path the
+                // codes entered as 1 + q/16, so sum(x*q) = 16 (acc - sum(x))
+                if constexpr (Packed<FMT, BITS, DT>::kOn)
+                    total[i][b] = fmaf(16.0f * scl[i].s, acc[i][b] - sx[b],
+                                       fmaf(scl[i].b, sx[b], total[i][b]));
+                else
+                    total[i][b] = fmaf(scl[i].s, acc[i][b],
+                                       fmaf(scl[i].b, sx[b], total[i][b]));
+            } else if constexpr (FMT == FMT_NVFP4) {
+                total[i][b] = fmaf(scl[i].hi, acc[i][b], total[i][b]);
+            } else {
+                total[i][b] = fmaf(scl[i].s, acc[i][b], total[i][b]);
+            }
+        }
+}
 
 // One block's tile: rows [row_base, row_base + rows_per_block) of one weight
 // matrix against NB activation rows.
@@ -137,121 +261,14 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
     const int rl0 = (wave * groups_per_wave + grp) * R;   // block-local row of i = 0
     uint8_t* lds_sc = reinterpret_cast<uint8_t*>(lds) + g.sc_lds_off;
 
-    // LDS layout per batch row: the 8-value sub-chunk sc of unit u sits at
-    // element (sc * us + u) * 8, so the lanes of a wave read consecutive 16 bytes
-    auto lds_slot = [](int e0, int us) __attribute__((always_inline)) {
-        const int u = e0 >> 5;
-        const int sub = (e0 >> 3) & 3;
-        return (sub * us + u) * 8 + (e0 & 7);
-    };
-
     auto compute_unit = [&](const U& u_raw, int ul, int ks, int us, int seg)
                             __attribute__((always_inline)) {
-        float acc[R][NB];
-        float sx[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            sx[b] = 0.0f;
-#pragma unroll
-            for (int i = 0; i < R; ++i) acc[i][b] = 0.0f;
-        }
         typename F::Scale scl[R];
 #pragma unroll
         for (int i = 0; i < R; ++i)
             scl[i] = F::template decode<DT>(
                 F::template lds_raw<DT>(lds_sc + (rl0 + i) * seg, RB * seg, ul, g.glog2));
-
-        static_for<0, 4>([&](auto sc_c) {
-            constexpr int SC = decltype(sc_c)::value;
-            if constexpr (Packed<FMT, BITS, DT>::kOn) {
-                // packed 16-bit path: weight pairs against x pairs, 2 MACs per op
-                uint32_t xp[NB][4];
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    const v4u v = *reinterpret_cast<const v4u*>(lds + b * ks + (SC * us + ul) * 8);
-                    xp[b][0] = v.x; xp[b][1] = v.y; xp[b][2] = v.z; xp[b][3] = v.w;
-                    if constexpr (F::kNeedsSumX) {
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) sx[b] = dot2<DT>(xp[b][k], pair_ones<DT>(), sx[b]);
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    uint32_t wp[4];
-                    F::template pairs<SC, DT>(u_raw.d[i], wp);
-#pragma unroll
-                    for (int b = 0; b < NB; ++b)
-#pragma unroll
-                        for (int k = 0; k < 4; ++k) acc[i][b] = dot2<DT>(wp[k], xp[b][k], acc[i][b]);
-                }
-            } else {
-                float xv[NB][8];
-#pragma unroll
-                for (int b = 0; b < NB; ++b) {
-                    lds_load8<DT>(lds + b * ks + (SC * us + ul) * 8, xv[b]);
-                    if constexpr (F::kNeedsSumX) {
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) sx[b] += xv[b][j];
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    float q[8];
-                    F::template decode8<SC>(u_raw.d[i], q);
-#pragma unroll
-                    for (int b = 0; b < NB; ++b)
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) acc[i][b] = fmaf(q[j], xv[b][j], acc[i][b]);
-                }
-            }
-            if constexpr (FMT == FMT_NVFP4) {
-                if constexpr (SC == 1) {
-                    // first block of 16 done: fold it with its E4M3 scale
-#pragma unroll
-                    for (int i = 0; i < R; ++i)
-#pragma unroll
-                        for (int b = 0; b < NB; ++b) {
-                            total[i][b] = fmaf(scl[i].lo, acc[i][b], total[i][b]);
-                            acc[i][b] = 0.0f;
-                        }
-                }
-            }
-        });
-
-#pragma unroll
-        for (int i = 0; i < R; ++i)
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                if constexpr (FMT == FMT_AFFINE) {
-                    // scale * sum(x*q) + bias * sum(x); on the packed path the
-                    // codes entered as 1 + q/16, so sum(x*q) = 16 (acc - sum(x))
-                    if constexpr (Packed<FMT, BITS, DT>::kOn)
-                        total[i][b] = fmaf(16.0f * scl[i].s, acc[i][b] - sx[b],
-                                           fmaf(scl[i].b, sx[b], total[i][b]));
-                    else
-                        total[i][b] = fmaf(scl[i].s, acc[i][b],
-                                           fmaf(scl[i].b, sx[b], total[i][b]));
-                } else if constexpr (FMT == FMT_NVFP4) {
-                    total[i][b] = fmaf(scl[i].hi, acc[i][b], total[i][b]);
-                } else {
-                    total[i][b] = fmaf(scl[i].s, acc[i][b], total[i][b]);
-                }
-            }
-    };
-
-    // 16 bytes of x (8 values of a 16-bit type) as stored in LDS: reordered to
-    // pairs (x[k], x[k+4]) where the packed affine path expects them
-    auto stage_vec = [](v4u v) __attribute__((always_inline)) {
-        if constexpr (Packed<FMT, BITS, DT>::kPerm) {
-            v4u r;
-            r.x = __builtin_amdgcn_perm(v.z, v.x, 0x05040100u);  // x4 | x0
-            r.y = __builtin_amdgcn_perm(v.z, v.x, 0x07060302u);  // x5 | x1
-            r.z = __builtin_amdgcn_perm(v.w, v.y, 0x05040100u);  // x6 | x2
-            r.w = __builtin_amdgcn_perm(v.w, v.y, 0x07060302u);  // x7 | x3
-            return r;
-        } else {
-            return v;
-        }
+        unit_fma<DT, FMT, BITS, NB, R>(u_raw, scl, lds, ul, ks, us, total);
     };
 
     for (int64_t slab = 0; slab < K; slab += g.ks) {
@@ -334,17 +351,18 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
             constexpr int j = decltype(j_c)::value;
             const int v = tid + j * kThreads;
             if (v < vec_per_row)
-                *reinterpret_cast<v4u*>(lds + lds_slot(v * kPerVec, us)) = stage_vec(xs[j]);
+                *reinterpret_cast<v4u*>(lds + x_lds_slot(v * kPerVec, us)) =
+                    stage_vec<FMT, BITS, DT>(xs[j]);
         });
         for (int v = tid + kXAhead * kThreads; v < vec_per_row; v += kThreads)
-            *reinterpret_cast<v4u*>(lds + lds_slot(v * kPerVec, us)) =
-                stage_vec(reinterpret_cast<const v4u*>(xr.row(0) + slab)[v]);
+            *reinterpret_cast<v4u*>(lds + x_lds_slot(v * kPerVec, us)) =
+                stage_vec<FMT, BITS, DT>(reinterpret_cast<const v4u*>(xr.row(0) + slab)[v]);
 #pragma unroll
         for (int b = 1; b < NB; ++b) {
             const S* src = xr.row(b) + slab;
             for (int v = tid; v < vec_per_row; v += kThreads)
-                *reinterpret_cast<v4u*>(lds + b * ks + lds_slot(v * kPerVec, us)) =
-                    stage_vec(reinterpret_cast<const v4u*>(src)[v]);
+                *reinterpret_cast<v4u*>(lds + b * ks + x_lds_slot(v * kPerVec, us)) =
+                    stage_vec<FMT, BITS, DT>(reinterpret_cast<const v4u*>(src)[v]);
         }
         // (3b) scale segment to LDS
         if (nw > 0) {
@@ -423,34 +441,204 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(LaunchParams p, Geom g) {
 }
 
 // ---------------------------------------------------------------------------
-// Routed-expert gather. Grid (row tiles, n_experts + 1). Block (t, e) finds
+// Routed-expert gather. Grid (tile groups, n_experts + 1). Block (t, e) finds
 // the slots routed to expert e (a ballot scan over rhs_indices, in slot
-// order) and runs the tile on chunks of up to two of them; each expert's
-// weights come from HBM once per call (further chunks of the same tile re-read
-// them from L2). The extra column e = n_experts writes the zero rows of slots
-// whose expert or x row is out of range.
+// order) and runs its group of consecutive row tiles on chunks of up to two of
+// those slots. When K fits one slab, a chunk's x rows are staged in LDS once
+// and serve every tile of the group, so the scan and the x staging are paid
+// once per group rather than once per tile. Each expert's weights come from
+// HBM once per call (further chunks of the same tiles re-read them from L2).
+// The extra column e = n_experts writes the zero rows of slots whose expert or
+// x row is out of range.
 // ---------------------------------------------------------------------------
 // Slots per chunk. A kernel carries the register budget of its largest
 // instantiated tile, so chunks stay at two activation rows (the tile of a
 // one- or two-row QMV); an expert with more slots runs several chunks over the
-// same tile, whose weights the repeat reads find in L2.
+// same tiles, whose weights the repeat reads find in L2.
 constexpr int kGatherChunkMax = 2;
 __host__ __device__ constexpr int gather_chunk_for(int) { return kGatherChunkMax; }
 constexpr int kGatherStageBytes = 32 * 1024;
 
-template <int DT, int FMT, int BITS, int R>
-__device__ inline void gather_chunk(const LaunchParams& p, const Geom& g, int64_t row_base,
-                                    const uint8_t* w, const void* sc, const void* bi, float gmul,
-                                    const uint32_t* list, const int64_t* xoff, int cnt,
+// Units in flight per lane in the gather tile loop.
+constexpr int kGatherDepth = 2;
+
+// Gather tile loop for a one-slab geometry, with the chunk's NB x rows
+// already staged in LDS for all of K. Each lane group walks its R-row set in
+// tiles tile0 .. tile_end-1 and, within each tile, its units, as one sequence:
+// the weight words and raw scales of the next units come straight from
+// global memory and stay in flight across tile boundaries, and no barrier is
+// taken, so each wave moves on at its own pace. A row's units, their order and
+// the final reduction are those of qmv_tile, so results match it bit for bit.
+template <int DT, int FMT, int BITS, int NB, int R>
+__device__ inline void gather_tiles(const LaunchParams& p, const Geom& g, int64_t tile0,
+                                    int64_t tile_end, const uint8_t* __restrict__ w,
+                                    const void* sc, const void* bi,
+                                    typename Store<DT>::S* const (&yrow)[NB], float gmul,
+                                    const typename Store<DT>::S* lds) {
+    using F = Fmt<FMT, BITS>;
+    using U = UnitRaw<FMT, BITS, R>;
+    constexpr int W = F::kWords;
+    constexpr int kUnitBytes = 4 * W;
+    struct Item {
+        U u;
+        typename F::Raw raw[R];
+    };
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int grp = lane >> g.lpr_log2;
+    const int gl = lane & (g.lpr - 1);
+    const int lpr = g.lpr;
+    const int64_t N = p.N;
+    const int ks = (int)p.K;
+    const int us = ks >> 5;
+    const int iters = (us + lpr - 1) >> g.lpr_log2;   // >= 1 (K > 0)
+    const int64_t RB = g.rows_per_block;
+    const int64_t rofs = (int64_t)(wave * (64 >> g.lpr_log2) + grp) * R;
+    const int64_t n_items = (tile_end - tile0) * iters;
+
+    // Load cursor. Addresses are a per-tile base (uniform) plus 32-bit
+    // per-lane row offsets, refreshed when the cursor enters a tile; rows past
+    // N re-read row N-1 and units past the row end re-read its last unit, like
+    // qmv_tile. The cursor stops at the last item (later loads repeat it).
+    const int64_t sc_row_bytes = p.sc_per_row * F::template elem_bytes<DT>();
+    const uint8_t* const sc8 = static_cast<const uint8_t*>(sc);
+    const uint8_t* const bi8 = static_cast<const uint8_t*>(bi);
+    int64_t lt = tile0;
+    int lit = 0;
+    const uint8_t* wt;   // weights of the cursor tile's first row
+    const uint8_t* st;   // its scales (and, for affine, biases at bt)
+    const uint8_t* bt;
+    uint32_t wro[R];     // lane's row offsets from those, in weight bytes
+    uint32_t sro[R];     // and in scale bytes
+    auto enter_tile = [&](int64_t t) __attribute__((always_inline)) {
+        const int64_t first = t * RB;
+        const int64_t lim = N - 1 - first;   // last valid row, tile-relative
+        wt = w + first * p.row_bytes;
+        st = sc8 + first * sc_row_bytes;
+        bt = FMT == FMT_AFFINE ? bi8 + first * sc_row_bytes : st;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int64_t r = rofs + i;
+            const uint32_t rr = (uint32_t)(r < lim ? r : lim);
+            wro[i] = rr * (uint32_t)p.row_bytes;
+            sro[i] = rr * (uint32_t)sc_row_bytes;
+        }
+    };
+    enter_tile(lt);
+    auto load_next = [&](Item& x) __attribute__((always_inline)) {
+        const int u = min(gl + lit * lpr, us - 1);
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            load_words<W>(wt + (wro[i] + (uint32_t)u * kUnitBytes), x.u.d[i]);
+            x.raw[i] = F::template global_raw<DT>(st, bt, sro[i], u, g.glog2);
+        }
+        if (++lit == iters) {
+            if (lt + 1 < tile_end) {
+                lit = 0;
+                enter_tile(++lt);
+            } else {
+                lit = iters - 1;
+            }
+        }
+    };
+
+    float total[R][NB];
+#pragma unroll
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) total[i][b] = 0.0f;
+    int64_t ct = tile0;
+    int cit = 0;
+    auto consume = [&](const Item& x) __attribute__((always_inline)) {
+        const int u = gl + cit * lpr;
+        if (u < us) {
+            typename F::Scale scl[R];
+#pragma unroll
+            for (int i = 0; i < R; ++i) scl[i] = F::template decode<DT>(x.raw[i]);
+            unit_fma<DT, FMT, BITS, NB, R>(x.u, scl, lds, u, ks, us, total);
+        }
+        if (++cit == iters) {
+            // tile done: reduce over the row group, store, restart
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) total[i][b] = group_sum(total[i][b], lpr);
+            if (gl == lpr - 1) {
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    const int64_t r = ct * RB + rofs + i;
+                    if (r < N) {
+#pragma unroll
+                        for (int b = 0; b < NB; ++b) {
+                            float v = total[i][b];
+                            if constexpr (FMT == FMT_NVFP4) v = v * gmul;
+                            yrow[b][r] = Store<DT>::from_f32(v);
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < R; ++i)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) total[i][b] = 0.0f;
+            cit = 0;
+            ++ct;
+        }
+    };
+
+    // a ring of kGatherDepth items in flight; the last few are consumed by a
+    // load-free epilogue
+    Item ring[kGatherDepth];
+    static_for<0, kGatherDepth>([&](auto j_c) { load_next(ring[decltype(j_c)::value]); });
+    int64_t k = 0;
+    for (; k + kGatherDepth < n_items; k += kGatherDepth) {
+        static_for<0, kGatherDepth>([&](auto j_c) {
+            constexpr int j = decltype(j_c)::value;
+            consume(ring[j]);
+            load_next(ring[j]);
+        });
+    }
+    static_for<0, kGatherDepth>([&](auto j_c) {
+        constexpr int j = decltype(j_c)::value;
+        if (k + j < n_items) consume(ring[j]);
+    });
+}
+
+template <int DT, int FMT, int BITS, int R, bool kOneSlab>
+__device__ inline void gather_chunk(const LaunchParams& p, const Geom& g, int64_t tile0,
+                                    int64_t tile_end, const uint8_t* w, const void* sc,
+                                    const void* bi, float gmul, const uint32_t* list,
+                                    const int64_t* xoff, int cnt,
                                     typename Store<DT>::S* lds) {
     using S = typename Store<DT>::S;
+    constexpr int kPerVec = 16 / Store<DT>::kBytes;
     const XListed<S> xr{static_cast<const S*>(p.x), xoff};
+    const int64_t RB = g.rows_per_block;
     auto run = [&](auto nb_c) {
         constexpr int NB = decltype(nb_c)::value;
         S* yrow[NB];
 #pragma unroll
         for (int b = 0; b < NB; ++b) yrow[b] = static_cast<S*>(p.y) + (int64_t)list[b] * p.N;
-        qmv_tile<DT, FMT, BITS, NB, R>(p, g, row_base, w, sc, bi, xr, yrow, gmul, lds);
+        if constexpr (kOneSlab) {
+            // one slab: stage the chunk's x rows (whole K) once for the group
+            const int K = (int)p.K;
+            const int us = K >> 5;
+            const int vec_per_row = K / kPerVec;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const v4u* src = reinterpret_cast<const v4u*>(xr.row(b));
+                for (int v = threadIdx.x; v < vec_per_row; v += kThreads)
+                    *reinterpret_cast<v4u*>(lds + b * K + x_lds_slot(v * kPerVec, us)) =
+                        stage_vec<FMT, BITS, DT>(src[v]);
+            }
+            __syncthreads();
+            gather_tiles<DT, FMT, BITS, NB, R>(p, g, tile0, tile_end, w, sc, bi, yrow, gmul, lds);
+        } else {
+            for (int64_t t = tile0; t < tile_end; ++t)
+                qmv_tile<DT, FMT, BITS, NB, R>(p, g, t * RB, w, sc, bi, xr, yrow, gmul,
+                                               lds);
+        }
     };
     if (cnt == 1)
         run(std::integral_constant<int, 1>{});
@@ -458,13 +646,16 @@ __device__ inline void gather_chunk(const LaunchParams& p, const Geom& g, int64_
         run(std::integral_constant<int, 2>{});
 }
 
-template <int DT, int FMT, int BITS, int R>
+// kOneSlab: K > 0 and the geometry holds all of K in one slab (the launcher
+// checks), so the group runs gather_tiles; otherwise qmv_tile per tile.
+template <int DT, int FMT, int BITS, int R, bool kOneSlab>
 __global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g) {
     using S = typename Store<DT>::S;
     extern __shared__ __align__(16) unsigned char smem[];
     S* lds = reinterpret_cast<S*>(smem);
     constexpr int kChunk = gather_chunk_for(DT);
-    __shared__ uint32_t list[kChunk + kThreads];
+    __shared__ uint32_t list[kChunk + kThreads];   // matching slots, in slot order
+    __shared__ uint32_t xrow[kChunk + kThreads];   // their x rows
     __shared__ int64_t xoff[kChunk];
     __shared__ int wave_cnt[kWaves];
     __shared__ int count;
@@ -472,19 +663,25 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t row_base = (int64_t)blockIdx.x * g.rows_per_block;
+    const int64_t RB = g.rows_per_block;
+    const int64_t n_tiles = (p.N + RB - 1) / RB;
+    const int64_t tile0 = (int64_t)blockIdx.x * g.tiles_per_block;
+    const int64_t tile_end =
+        tile0 + g.tiles_per_block < n_tiles ? tile0 + g.tiles_per_block : n_tiles;
     const int64_t e = blockIdx.y;
 
     if (e == p.n_experts) {
-        // zero rows for slots with an out-of-range expert or x row
-        for (int64_t s = 0; s < p.n_slots; ++s) {
+        // Zero rows for slots with an out-of-range expert or x row: one thread
+        // per slot, all slots checked at once; such slots are rare, so the
+        // owning thread writes the group's rows of that slot itself.
+        const int64_t r0 = tile0 * RB;
+        const int64_t r1 = tile_end * RB < p.N ? tile_end * RB : p.N;
+        for (int64_t s = tid; s < p.n_slots; s += kThreads) {
             const uint32_t ex = p.rhs[s];
             const uint32_t xrw = p.lhs[s];
             if ((int64_t)ex < p.n_experts && (int64_t)xrw < p.n_x_rows) continue;
-            for (int r = tid; r < g.rows_per_block; r += kThreads) {
-                const int64_t n = row_base + r;
-                if (n < p.N) static_cast<S*>(p.y)[s * p.N + n] = Store<DT>::from_f32(0.0f);
-            }
+            S* yr = static_cast<S*>(p.y) + s * p.N;
+            for (int64_t r = r0; r < r1; ++r) yr[r] = Store<DT>::from_f32(0.0f);
         }
         return;
     }
@@ -501,9 +698,10 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g
     const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
 
     auto run_chunk = [&](int cnt) {
-        if (tid < cnt) xoff[tid] = (int64_t)p.lhs[list[tid]] * p.K;
+        if (tid < cnt) xoff[tid] = (int64_t)xrow[tid] * p.K;
         __syncthreads();
-        gather_chunk<DT, FMT, BITS, R>(p, g, row_base, w, sc, bi, gmul, list, xoff, cnt, lds);
+        gather_chunk<DT, FMT, BITS, R, kOneSlab>(p, g, tile0, tile_end, w, sc, bi, gmul, list,
+                                                 xoff, cnt, lds);
         __syncthreads();
     };
 
@@ -511,29 +709,42 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g
     __syncthreads();
     for (int64_t base = 0; base < p.n_slots; base += kThreads) {
         const int64_t s = base + tid;
-        bool match = false;
-        if (s < p.n_slots) {
-            match = (int64_t)p.rhs[s] == e && (int64_t)p.lhs[s] < p.n_x_rows;
-        }
+        // both indices are read together (clamped), so one round trip serves
+        const int64_t si = s < p.n_slots ? s : p.n_slots - 1;
+        const uint32_t ex = p.rhs[si];
+        const uint32_t xr = p.lhs[si];
+        const bool match = s < p.n_slots && (int64_t)ex == e && (int64_t)xr < p.n_x_rows;
         const uint64_t m = __ballot(match);
         const int before = __popcll(m & ((1ull << lane) - 1ull));
         if (lane == 0) wave_cnt[wave] = __popcll(m);
         __syncthreads();
-        int off = count;
+        // count is read only here, between the barriers that bracket its
+        // update by thread 0 below
+        const int prev = count;
+        int off = prev;
         for (int i = 0; i < wave; ++i) off += wave_cnt[i];
-        if (match) list[off + before] = (uint32_t)s;
+        if (match) {
+            list[off + before] = (uint32_t)s;
+            xrow[off + before] = xr;
+        }
         int added = 0;
         for (int i = 0; i < kWaves; ++i) added += wave_cnt[i];
         __syncthreads();
-        int cnt = count + added;
+        int cnt = prev + added;
         while (cnt >= kChunk) {
             run_chunk(kChunk);
             // move the leftovers to the front
             const int rest = cnt - kChunk;
-            uint32_t v = 0;
-            if (tid < rest) v = list[kChunk + tid];
+            uint32_t v = 0, vx = 0;
+            if (tid < rest) {
+                v = list[kChunk + tid];
+                vx = xrow[kChunk + tid];
+            }
             __syncthreads();
-            if (tid < rest) list[tid] = v;
+            if (tid < rest) {
+                list[tid] = v;
+                xrow[tid] = vx;
+            }
             __syncthreads();
             cnt = rest;
         }
@@ -616,11 +827,20 @@ __global__ void dequant_kernel(LaunchParams p, int glog2, float* __restrict__ ou
 // ---------------------------------------------------------------------------
 // Host-side launch helpers.
 // ---------------------------------------------------------------------------
-// Rows per lane group. Fewer rows per wave means more waves and a shorter
-// compute tail after the last bytes arrive; more rows reuse each x slice read
-// from LDS more often. Measured on MI355X (MXFP4, B=1, K=4096, N=14336):
-// R=2 beats R=1, 3 and 4. Larger batches keep R=4 for the x reuse.
-template <int NB> constexpr int rows_for() { return NB <= 2 ? 2 : 4; }
+// Rows per lane group, chosen per launch between two instantiations. Measured
+// on MI355X (bf16 x; MXFP4 and 3/4/8-bit affine; K from 1536 to 14336, N from
+// 1536 to 14336):
+//  - B <= 2: one row per lane group is fastest while every wave of the launch
+//    fits on the chip at once (256 CUs x 32 waves); beyond that two rows win,
+//    as each x slice staged in LDS then serves twice the weight bytes.
+//  - 3 <= B <= 7: two rows (four rows cost occupancy: 155+ VGPRs).
+//  - B = 8: four rows for MXFP4 and 8-bit affine (MXFP4 K=4096 N=14336: 30.9
+//    vs 37.2 us), two for the narrower affine codes (4-bit: 14.2 vs 15.9 us).
+template <int NB> constexpr int rows_small() { return 1; }
+template <int FMT, int BITS, int NB> constexpr int rows_large() {
+    return NB < 8 ? 2 : ((FMT == FMT_AFFINE && BITS < 8) ? 2 : 4);
+}
+constexpr int64_t kResidentWaves = 256 * 32;
 constexpr int kGatherRows = 2;
 
 int ilog2(int v) {
@@ -629,17 +849,25 @@ int ilog2(int v) {
     return r;
 }
 
-// Lanes per row: the widest of 64/32/16 that keeps every lane busy (at least
-// 90% of lane-unit slots used), else the one that wastes least.
+// Lanes per row, from K alone, so a row's sum is formed in the same order at
+// any N, batch or expert. Rows of at least 64 units: the widest of 64/32/16
+// that leaves at most 40% of the lane-unit slots idle. Measured on MI355X,
+// spreading a row over more lanes wins even at 62% lane use (8-bit affine,
+// K=N=2560: 4.6 us at 64 lanes, 7.4 us at 16). Shorter rows would give each
+// lane one partly idle unit and a full cross-lane reduction per unit, so they
+// take the widest width that keeps 90% of the slots busy (single calls at
+// K=1536 time within 5% across widths; the gathered down projection is 25%
+// faster at 16 lanes). Else the least wasteful width.
 int pick_lpr(int64_t K) {
     const int64_t U = K >> 5;
     if (U == 0) return 64;
+    const double need = U >= 64 ? 0.6 : 0.9;
     int best = 64;
     double best_eff = -1.0;
     for (int lpr : {64, 32, 16}) {
         const int64_t iters = (U + lpr - 1) / lpr;
         const double eff = (double)U / (double)(iters * lpr);
-        if (eff >= 0.9) return lpr;
+        if (eff >= need) return lpr;
         if (eff > best_eff + 1e-12) { best_eff = eff; best = lpr; }
     }
     return best;
@@ -651,7 +879,8 @@ int pick_lpr(int64_t K) {
 template <int DT, int FMT, int BITS>
 Geom make_geom(const LaunchParams& p, int nb, int budget, int rows) {
     using F = Fmt<FMT, BITS>;
-    Geom g;
+    Geom g{};
+    g.tiles_per_block = 1;
     g.lpr = pick_lpr(p.K);
     g.lpr_log2 = ilog2(g.lpr);
     g.glog2 = FMT == FMT_AFFINE ? ilog2(p.group / 32) : 0;
@@ -695,17 +924,37 @@ size_t stage_bytes(const LaunchParams& p, const Geom& g) {
 }
 
 // Dynamic LDS above 64 KB must be requested per kernel (gfx950 has 160 KB
-// per workgroup); done once per instance.
+// per workgroup). `granted` is the caller's per-instantiation record of the
+// largest size already requested.
 template <class Kern>
-int allow_lds(Kern* kern, size_t bytes) {
-    if (bytes <= 64 * 1024) return 0;
-    static size_t granted = 0;
-    if (bytes <= granted) return 0;
+int allow_lds(Kern* kern, size_t bytes, std::atomic<size_t>& granted) {
+    if (bytes <= 64 * 1024 || bytes <= granted.load(std::memory_order_relaxed)) return 0;
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)bytes);
-    if (e == hipSuccess) granted = bytes;
-    return (int)e;
+    if (e != hipSuccess) return (int)e;
+    size_t cur = granted.load(std::memory_order_relaxed);
+    while (cur < bytes && !granted.compare_exchange_weak(cur, bytes)) {
+    }
+    return 0;
+}
+
+// Waves a plain QMV launch of R rows per lane group runs.
+int64_t launch_waves(const LaunchParams& p, int rows) {
+    const int64_t rpb = (int64_t)kWaves * (64 / pick_lpr(p.K)) * rows;
+    return (p.N + rpb - 1) / rpb * kWaves;
+}
+
+template <int DT, int FMT, int BITS, int NB, int R>
+int launch_qmv_r(const LaunchParams& p, hipStream_t st) {
+    const Geom g = make_geom<DT, FMT, BITS>(p, NB, kMaxStageBytes, R);
+    const dim3 grid((unsigned)((p.N + g.rows_per_block - 1) / g.rows_per_block));
+    const size_t lds = stage_bytes<DT, FMT, BITS>(p, g);
+    auto* kern = &qmv_kernel<DT, FMT, BITS, NB, R>;
+    static std::atomic<size_t> granted{0};
+    if (const int e = allow_lds(kern, lds, granted)) return e;
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, p, g);
+    return (int)hipGetLastError();
 }
 
 template <int DT, int FMT, int BITS>
@@ -713,15 +962,12 @@ int launch_qmv_t(const LaunchParams& p, hipStream_t st) {
     const int nb = (int)p.B;
     switch (nb) {
 #define QMV_CASE(n)                                                                         \
-    case n: {                                                                               \
-        const Geom g = make_geom<DT, FMT, BITS>(p, n, kMaxStageBytes, rows_for<n>());       \
-        const dim3 grid((unsigned)((p.N + g.rows_per_block - 1) / g.rows_per_block));      \
-        const size_t lds = stage_bytes<DT, FMT, BITS>(p, g);                                \
-        auto* kern = &qmv_kernel<DT, FMT, BITS, n, rows_for<n>()>;                          \
-        if (const int e = allow_lds(kern, lds)) return e;                                   \
-        hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, p, g);                      \
-        break;                                                                              \
-    }
+    case n:                                                                                 \
+        if constexpr (n <= 2) {                                                             \
+            if (launch_waves(p, rows_small<n>()) <= kResidentWaves)                         \
+                return launch_qmv_r<DT, FMT, BITS, n, rows_small<n>()>(p, st);              \
+        }                                                                                   \
+        return launch_qmv_r<DT, FMT, BITS, n, rows_large<FMT, BITS, n>()>(p, st);
         QMV_CASE(1) QMV_CASE(2) QMV_CASE(3) QMV_CASE(4)
         QMV_CASE(5) QMV_CASE(6) QMV_CASE(7) QMV_CASE(8)
 #undef QMV_CASE
@@ -730,15 +976,29 @@ int launch_qmv_t(const LaunchParams& p, hipStream_t st) {
     return (int)hipGetLastError();
 }
 
+// Blocks a gather launch aims for across the experts that can be active
+// (at most min(n_experts, n_slots) of them): about two rounds of resident
+// blocks, so each block runs a group of several tiles.
+constexpr int64_t kGatherBlocks = 8192;
+
 template <int DT, int FMT, int BITS>
 int launch_gather_t(const LaunchParams& p, hipStream_t st) {
     constexpr int kChunk = gather_chunk_for(DT);
-    const Geom g = make_geom<DT, FMT, BITS>(p, kChunk, kGatherStageBytes, kGatherRows);
-    const dim3 grid((unsigned)((p.N + g.rows_per_block - 1) / g.rows_per_block),
-                    (unsigned)(p.n_experts + 1));
+    Geom g = make_geom<DT, FMT, BITS>(p, kChunk, kGatherStageBytes, kGatherRows);
+    const int64_t n_tiles = (p.N + g.rows_per_block - 1) / g.rows_per_block;
+    const int64_t active = p.n_experts < p.n_slots ? p.n_experts : p.n_slots;
+    int64_t tpb = (n_tiles * active + kGatherBlocks - 1) / kGatherBlocks;
+    if (tpb < 1) tpb = 1;
+    if (tpb > n_tiles) tpb = n_tiles > 0 ? n_tiles : 1;
+    g.tiles_per_block = (int)tpb;
+    const dim3 grid((unsigned)((n_tiles + tpb - 1) / tpb), (unsigned)(p.n_experts + 1));
     const size_t lds = stage_bytes<DT, FMT, BITS>(p, g);
-    hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kGatherRows>), grid, dim3(kThreads), lds,
-                       st, p, g);
+    if (g.ks >= p.K && p.K > 0)
+        hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kGatherRows, true>), grid,
+                           dim3(kThreads), lds, st, p, g);
+    else
+        hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kGatherRows, false>), grid,
+                           dim3(kThreads), lds, st, p, g);
     return (int)hipGetLastError();
 }
 

@@ -35,7 +35,8 @@
  * - Requirements checked before any HIP call (a failed check returns an
  *   error, leaves every output untouched and records a message):
  *     B in [0, 8]; K >= 0, K % 32 == 0 (affine: also K % group == 0);
- *     N >= 0; bits in {2,3,4,5,6,8}; group in {32,64,128};
+ *     N >= 0; K <= 2^24 and N <= 2^28 (else QMV_ERR_UNSUPPORTED);
+ *     bits in {2,3,4,5,6,8}; group in {32,64,128};
  *     w and x 16-byte aligned, y / scales / biases aligned to their element;
  *     pointers may be NULL only where the tensor is empty.
  *   B == 0 or N == 0 is a successful no-op. K == 0 writes y = 0.

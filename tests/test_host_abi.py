@@ -50,6 +50,8 @@ def _affine(lib, **kw):
     (dict(K=48), INVAL, "multiple of 32"),
     (dict(K=96, group=64), INVAL, "group"),
     (dict(B=9), UNSUP, "batch"),
+    (dict(K=(1 << 24) + 64), UNSUP, "2^24"),
+    (dict(N=(1 << 28) + 1), UNSUP, "2^28"),
     (dict(B=-1), INVAL, "negative"),
     (dict(N=-2), INVAL, "negative"),
     (dict(x=None), INVAL, "x is NULL"),
