@@ -298,7 +298,7 @@ def committed_traffic():
     except OSError:
         return None
     vals = {}
-    for line in text.splitlines():
+    for line in (l.strip() for l in text.splitlines()):
         if line.startswith("traffic_bytes_per_launch:"):
             vals["t"] = float(line.split(":", 1)[1])
         if line.startswith("kernel_fingerprint:"):
@@ -355,6 +355,25 @@ def summarize_trace(trace_csv: str, kernel_substr: str) -> str:
         f"VGPRs {rows[0]['VGPR_Count'] if rows else '-'}, grid {rows[0]['Grid_Size_X'] if rows else '-'}"
         f", workgroup {rows[0]['Workgroup_Size_X'] if rows else '-'}",
     ])
+
+
+def summarize_trace_table(trace_csv: str) -> str:
+    """Markdown table of every kernel in a rocprofv3 kernel trace, one line per
+    (kernel, grid): dispatches and duration statistics in microseconds."""
+    import csv
+    import re
+    groups = {}
+    for r in csv.DictReader(open(trace_csv)):
+        key = (r["Kernel_Name"], r["Grid_Size_X"], r["Grid_Size_Y"])
+        groups.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    out = ["| kernel | grid | dispatches | mean us | p10 | p50 | p90 |", "|---|---|---|---|---|---|---|"]
+    for (name, gx, gy), d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        d = np.array(d)
+        short = re.sub(r"\(qmv::LaunchParams.*", "", name).replace("qmv::(anonymous namespace)::", "")
+        short = short.replace("void ", "")
+        out.append(f"| `{short[:70]}` | {gx}x{gy} | {len(d)} | {d.mean():.2f} | "
+                   f"{np.percentile(d, 10):.2f} | {np.median(d):.2f} | {np.percentile(d, 90):.2f} |")
+    return "\n".join(out)
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, copy_bytes: int, alg_bytes: int) -> str:
@@ -449,6 +468,8 @@ def main() -> int:
                     help="only sweep the streaming-read ceiling over sizes and exit")
     ap.add_argument("--pmc-workload", type=int, default=0, metavar="N",
                     help="only run the counter workload (N copies, N headline launches)")
+    ap.add_argument("--summarize-trace-table", metavar="TRACE_CSV",
+                    help="print a per-kernel duration table of a rocprofv3 kernel trace")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "KERNEL"),
                     help="print a summary of a rocprofv3 kernel trace and exit (no GPU)")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -456,6 +477,9 @@ def main() -> int:
     args = ap.parse_args()
     if args.summarize_trace:
         print(summarize_trace(*args.summarize_trace))
+        return 0
+    if args.summarize_trace_table:
+        print(summarize_trace_table(args.summarize_trace_table))
         return 0
     if args.summarize_counters:
         import workloads
