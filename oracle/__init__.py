@@ -28,6 +28,9 @@ passage it follows):
   of each slot picks the weight matrix; no per-expert host dispatch).
 * "ferrum-kernels - primitives.rs" tests: an out-of-range index yields a row
   of zeros rather than a fault.
+* Quantize-from-float (``quantize.py``): the audit's Track-2 min/max encoder
+  and the fp_quantized / kv_cache rows' max-scale element rounding, with the
+  readings its docstring states.
 
 Pins that tie this oracle to something other than itself live in
 ``tests/test_oracle_pins.py`` (run with ``-m "not gpu"``).
@@ -49,6 +52,13 @@ from .formats import (
     e4m3_value,
     e8m0_value,
     e4m3_encode_nearest,
+)
+from .quantize import (
+    e2m1_encode_nearest,
+    floor_log2,
+    quantize_affine,
+    quantize_mx,
+    quantize_nvfp4,
 )
 from .qmv import (
     dequant_affine,
