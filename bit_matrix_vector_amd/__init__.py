@@ -71,6 +71,10 @@ def load() -> ctypes.CDLL:
         "qmv_encode_e4m3": [vp, i64, vp],
         "qmv_unpack_codes_device": [vp, vp, i64, i64, i32, vp],
         "qmv_dequant_device": [vp, i32, ctypes.POINTER(QmvWeights), vp],
+        "qmv_quantize_affine": [vp, i32, i64, i64, vp, i32, i32, vp, vp, vp],
+        "qmv_quantize_mxfp4": [vp, i32, i64, i64, vp, vp, vp],
+        "qmv_quantize_mxfp8": [vp, i32, i64, i64, vp, vp, vp],
+        "qmv_quantize_nvfp4": [vp, i32, i64, i64, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)
@@ -264,6 +268,59 @@ def qmv_dequant_device(weights: QmvWeights, dtype_code: int, device, out=None):
     _check(load().qmv_dequant_device(_stream(out.device), dtype_code, ctypes.byref(weights),
                                      _ptr(out)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# quantize from float (device tensors; outputs allocated here unless given)
+# ---------------------------------------------------------------------------
+
+def _qin(w):
+    w = _dev(w, "w")
+    if w.dim() != 2:
+        raise ValueError("w must be [N, K]")
+    return w, w.shape[0], w.shape[1]
+
+
+def qmv_quantize_affine(w, bits: int, group_size: int):
+    """Affine codes of w [N, K] (float32/float16/bfloat16): returns (packed
+    [N, K*bits/8] uint8, scales [N, K/group_size], biases) with scales and
+    biases in w's dtype. See include/qmv.h for the exact rule."""
+    torch = _torch()
+    w, N, K = _qin(w)
+    packed = torch.empty((N, K * bits // 8), dtype=torch.uint8, device=w.device)
+    sc = torch.empty((N, K // group_size), dtype=w.dtype, device=w.device)
+    bi = torch.empty_like(sc)
+    _check(load().qmv_quantize_affine(_stream(w.device), _dtype_code(w), N, K, _ptr(w), bits,
+                                      group_size, _ptr(packed), _ptr(sc), _ptr(bi)))
+    return packed, sc, bi
+
+
+def qmv_quantize_mx(w, fmt: str):
+    """MXFP4 ('mxfp4') or MXFP8 ('mxfp8') codes of w [N, K]: returns (packed,
+    E8M0 scales [N, K/32] uint8)."""
+    torch = _torch()
+    w, N, K = _qin(w)
+    if fmt not in ("mxfp4", "mxfp8"):
+        raise ValueError(fmt)
+    rb = K // 2 if fmt == "mxfp4" else K
+    packed = torch.empty((N, rb), dtype=torch.uint8, device=w.device)
+    sc = torch.empty((N, K // 32), dtype=torch.uint8, device=w.device)
+    fn = load().qmv_quantize_mxfp4 if fmt == "mxfp4" else load().qmv_quantize_mxfp8
+    _check(fn(_stream(w.device), _dtype_code(w), N, K, _ptr(w), _ptr(packed), _ptr(sc)))
+    return packed, sc
+
+
+def qmv_quantize_nvfp4(w):
+    """NVFP4 codes of w [N, K]: returns (packed [N, K/2], E4M3 scales [N, K/16]
+    uint8, global scale as a one-element float32 tensor)."""
+    torch = _torch()
+    w, N, K = _qin(w)
+    packed = torch.empty((N, K // 2), dtype=torch.uint8, device=w.device)
+    sc = torch.empty((N, K // 16), dtype=torch.uint8, device=w.device)
+    gs = torch.empty((1,), dtype=torch.float32, device=w.device)
+    _check(load().qmv_quantize_nvfp4(_stream(w.device), _dtype_code(w), N, K, _ptr(w),
+                                     _ptr(packed), _ptr(sc), _ptr(gs)))
+    return packed, sc, gs
 
 
 # ---------------------------------------------------------------------------

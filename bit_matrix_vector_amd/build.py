@@ -27,6 +27,8 @@ ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
+    # fp32 division and square root correctly rounded (the quantizers rely on it)
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
     # keep hipcc from forming packed fp32 VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}",
@@ -44,6 +46,8 @@ def _jobs() -> list[tuple[list[str], str]]:
     obj = os.path.join(BUILD, "qmv_dispatch.o")
     jobs.append(([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "qmv_dispatch.hip"), "-o", obj],
                  obj))
+    obj = os.path.join(BUILD, "qmv_quant.o")
+    jobs.append(([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "qmv_quant.hip"), "-o", obj], obj))
     obj = os.path.join(BUILD, "qmv_bench.o")
     jobs.append(([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "qmv_bench.hip"), "-o", obj], obj))
     obj = os.path.join(BUILD, "qmv_api.o")

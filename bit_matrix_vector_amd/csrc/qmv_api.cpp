@@ -138,9 +138,58 @@ qmv_status_t run_qmv(const char* fn, void* stream, int dtype, int format, int bi
     return launch_status(qmv::launch_qmv(lp, stream), fn);
 }
 
+qmv_status_t run_quantize(const char* fn, void* stream, int dtype, int format, int bits,
+                          int group, int64_t N, int64_t K, const void* w, uint8_t* packed,
+                          void* scales, void* biases, float* gscale) {
+    QMV_TRY(check_common(fn, dtype, 1, K, N, 1));
+    qmv::LaunchParams lp{};
+    QMV_TRY(format_geometry(fn, format, bits, group, K, lp));
+    if (N == 0 || K == 0) return QMV_OK;
+    const int tb = dtype_bytes(dtype);
+    QMV_TRY(check_ptr(fn, "w", w, true, 16));
+    QMV_TRY(check_ptr(fn, "packed", packed, true, 16));
+    if (format == QMV_AFFINE) {
+        QMV_TRY(check_ptr(fn, "scales", scales, true, tb));
+        QMV_TRY(check_ptr(fn, "biases", biases, true, tb));
+    } else {
+        QMV_TRY(check_ptr(fn, "scales", scales, true, 1));
+    }
+    QMV_TRY(check_ptr(fn, "global_scale", gscale, format == QMV_NVFP4, 4));
+    qmv::QuantParams q{};
+    q.dtype = dtype; q.format = format; q.bits = lp.bits; q.group = lp.group;
+    q.N = N; q.K = K; q.w = w; q.packed = packed; q.scales = scales; q.biases = biases;
+    q.global_scale = gscale;
+    return launch_status(qmv::launch_quantize(q, stream), fn);
+}
+
 }  // namespace
 
 extern "C" {
+
+qmv_status_t qmv_quantize_affine(void* stream, int dtype, int64_t N, int64_t K, const void* w,
+                                 int bits, int group_size, uint8_t* packed, void* scales,
+                                 void* biases) {
+    return run_quantize("qmv_quantize_affine", stream, dtype, QMV_AFFINE, bits, group_size, N, K,
+                        w, packed, scales, biases, nullptr);
+}
+
+qmv_status_t qmv_quantize_mxfp4(void* stream, int dtype, int64_t N, int64_t K, const void* w,
+                                uint8_t* packed, uint8_t* scales) {
+    return run_quantize("qmv_quantize_mxfp4", stream, dtype, QMV_MXFP4, 4, 32, N, K, w, packed,
+                        scales, nullptr, nullptr);
+}
+
+qmv_status_t qmv_quantize_mxfp8(void* stream, int dtype, int64_t N, int64_t K, const void* w,
+                                uint8_t* packed, uint8_t* scales) {
+    return run_quantize("qmv_quantize_mxfp8", stream, dtype, QMV_MXFP8, 8, 32, N, K, w, packed,
+                        scales, nullptr, nullptr);
+}
+
+qmv_status_t qmv_quantize_nvfp4(void* stream, int dtype, int64_t N, int64_t K, const void* w,
+                                uint8_t* packed, uint8_t* scales, float* global_scale) {
+    return run_quantize("qmv_quantize_nvfp4", stream, dtype, QMV_NVFP4, 4, 16, N, K, w, packed,
+                        scales, nullptr, global_scale);
+}
 
 const char* qmv_last_error(void) { return g_last_error; }
 

@@ -31,8 +31,23 @@ struct LaunchParams {
     const uint32_t* rhs;
 };
 
+// One quantize-from-float call: w [N, K] in `dtype` to the packed format.
+struct QuantParams {
+    int dtype;
+    int format;
+    int bits;            // affine code width
+    int group;           // affine group size
+    int64_t N, K;
+    const void* w;
+    uint8_t* packed;
+    void* scales;        // T for affine, bytes for the block-scaled formats
+    void* biases;        // affine only
+    float* global_scale; // NVFP4 only: written (device fp32)
+};
+
 // Launchers (defined in the .hip translation units). Return 0 on success or
 // the hipError_t of a failed launch.
+int launch_quantize(const QuantParams& q, void* stream);
 int launch_qmv(const LaunchParams& p, void* stream);
 int launch_gather(const LaunchParams& p, void* stream);
 int launch_unpack_device(const uint8_t* packed, int64_t rows, int64_t K, int bits,

@@ -169,6 +169,45 @@ qmv_status_t qmv_unpack_codes_device(void* stream, const uint8_t* packed, int64_
  * `dtype` is the storage type of the affine scales/biases (ignored otherwise). */
 qmv_status_t qmv_dequant_device(void* stream, int dtype, const qmv_weights_t* w, float* out);
 
+/* ---------------- quantize from float: DEVICE memory, asynchronous ---------
+ * Encode a row-major [N, K] matrix w of `dtype` values (16-byte aligned) into
+ * the layout the QMV entry points read: packed rows [N, row_bytes] (16-byte
+ * aligned) and block scales. The pages ("wh-iron kernel-op coverage audit",
+ * "Quantization precision coverage": Track 2's min/max encoder, the
+ * fp_quantized / kv_cache rows' max-scale rounding, the Track-1 NVFP4 layout)
+ * leave steps open; the readings below fix them. Every step that decides a
+ * code is one fp32 operation in the order written (round to nearest even,
+ * correctly rounded division), so the output is defined bit for bit. Inputs
+ * must be finite. N == 0 or K == 0 is a successful no-op. K % 32 == 0 (affine:
+ * also K % group_size == 0); K <= 2^24. Outputs must not overlap w. */
+
+/* Affine, per group of group_size along K: lo, hi = group min, max (zero
+ * extremes count as +0);
+ * s32 = (hi - lo) / (2^bits - 1); scales = RN_T(s32), biases = RN_T(lo)
+ * ([N, K/group_size], in dtype); q = clamp(rint((w - b) / s), 0, 2^bits - 1)
+ * against the stored s and b, or 0 where the stored s is 0. */
+qmv_status_t qmv_quantize_affine(void* stream, int dtype, int64_t N, int64_t K, const void* w,
+                                 int bits, int group_size, uint8_t* packed, void* scales,
+                                 void* biases);
+
+/* MXFP4 / MXFP8, per block of 32: a = max |w|; scale byte (E8M0) = 0 if
+ * a == 0, else clamp(floor(log2 a) - emax + 127, 0, 254) with emax 2 (E2M1)
+ * or 8 (E4M3); element = nearest E2M1 / E4M3 to w / 2^(byte - 127), ties to
+ * even, saturating at 6 / 448, sign kept (so -0 encodes with the sign bit).
+ * scales [N, K/32] bytes. */
+qmv_status_t qmv_quantize_mxfp4(void* stream, int dtype, int64_t N, int64_t K, const void* w,
+                                uint8_t* packed, uint8_t* scales);
+qmv_status_t qmv_quantize_mxfp8(void* stream, int dtype, int64_t N, int64_t K, const void* w,
+                                uint8_t* packed, uint8_t* scales);
+
+/* NVFP4: global = A / 2688 with A = max |w| over the matrix (written to the
+ * device fp32 *global_scale, which is also used as the reduction's working
+ * word while the call runs); per block of 16: sb = (max |w| / 6) / global,
+ * scale byte = nearest E4M3 to sb (saturating); d = decoded scale * global;
+ * element = nearest E2M1 to w / d, or code 0 where d is 0. scales [N, K/16]. */
+qmv_status_t qmv_quantize_nvfp4(void* stream, int dtype, int64_t N, int64_t K, const void* w,
+                                uint8_t* packed, uint8_t* scales, float* global_scale);
+
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* qmv_last_error(void);
 

@@ -62,8 +62,23 @@ _E4M3_POS_CODES = np.arange(0x7F, dtype=np.int64)          # 0x00 .. 0x7E finite
 _E4M3_POS_VALUES = e4m3_value(_E4M3_POS_CODES)               # increasing
 
 
+def nearest_code(a, values) -> np.ndarray:
+    """Index of the entry of the increasing array `values` nearest to each
+    a >= 0 (a no larger than values[-1]); an exact tie between two entries goes
+    to the even index. With values listed in code order this is the nearest
+    code, ties to the code whose lowest bit is 0."""
+    a = np.asarray(a, dtype=np.float64)
+    idx = np.searchsorted(values, a)                 # first entry >= a
+    hi = np.clip(idx, 0, len(values) - 1)
+    lo = np.clip(idx - 1, 0, len(values) - 1)
+    dlo = a - values[lo]
+    dhi = values[hi] - a
+    tie = np.where(lo % 2 == 0, lo, hi)
+    return np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, tie))
+
+
 def e4m3_encode_nearest(v) -> np.ndarray:
-    """Reference for the host E4M3 encoder: the E4M3 byte nearest to v.
+    """Reference for the E4M3 encoders: the E4M3 byte nearest to v.
 
     Defined by search over the 127 non-negative finite values, not by bit
     manipulation: the nearest value wins; an exact tie goes to the even code
@@ -71,22 +86,7 @@ def e4m3_encode_nearest(v) -> np.ndarray:
     above 448 saturate to 448 (0x7E); the sign goes to bit 7 (so -0.0 gives
     0x80); NaN gives 0x7F. Infinities saturate like any large value."""
     v = np.asarray(v, dtype=np.float64)
-    out = np.empty(v.shape, dtype=np.uint8)
-    flat_v = v.reshape(-1)
-    flat_o = out.reshape(-1)
-    for i, x in enumerate(flat_v):
-        if np.isnan(x):
-            flat_o[i] = 0x7F
-            continue
-        a = min(abs(x), 448.0)
-        d = np.abs(_E4M3_POS_VALUES - a)
-        best = np.flatnonzero(d == d.min())
-        if best.size > 1:                 # exact tie between two codes
-            even = [c for c in best if (c & 1) == 0]
-            code = int(even[0])
-        else:
-            code = int(best[0])
-        if np.signbit(x):
-            code |= 0x80
-        flat_o[i] = code
-    return out
+    a = np.minimum(np.abs(np.nan_to_num(v, nan=0.0)), 448.0)
+    code = nearest_code(a, _E4M3_POS_VALUES).astype(np.uint8)
+    code = np.where(np.signbit(v), code | np.uint8(0x80), code).astype(np.uint8)
+    return np.where(np.isnan(v), np.uint8(0x7F), code).astype(np.uint8)

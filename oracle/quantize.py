@@ -38,7 +38,7 @@ from __future__ import annotations
 import numpy as np
 
 from .codes import storage_to_f64
-from .formats import e2m1_value, e4m3_value, e4m3_encode_nearest
+from .formats import e2m1_value, e4m3_value, e4m3_encode_nearest, nearest_code
 
 _F32 = np.float32
 
@@ -50,18 +50,8 @@ def e2m1_encode_nearest(v) -> np.ndarray:
     wins; an exact tie goes to the even code (mantissa bit 0); magnitudes above
     6 saturate to 6 (code 7); the sign (including that of -0.0) goes to bit 3."""
     v = np.asarray(v, dtype=np.float64)
-    out = np.empty(v.shape, dtype=np.uint8)
-    fv = v.reshape(-1)
-    fo = out.reshape(-1)
-    for i, x in enumerate(fv):
-        a = min(abs(x), 6.0)
-        d = np.abs(_E2M1_POS_VALUES - a)
-        best = np.flatnonzero(d == d.min())
-        code = int(best[0]) if best.size == 1 else int([c for c in best if c % 2 == 0][0])
-        if np.signbit(x):
-            code |= 0x8
-        fo[i] = code
-    return out
+    code = nearest_code(np.minimum(np.abs(v), 6.0), _E2M1_POS_VALUES).astype(np.uint8)
+    return np.where(np.signbit(v), code | np.uint8(8), code).astype(np.uint8)
 
 
 def _to_f32(w_stored, dtype: str) -> np.ndarray:
@@ -98,7 +88,7 @@ def quantize_affine(w_stored, dtype: str, bits: int, group: int):
     """Affine (Track 2) encoder of a [N, K] matrix in T.
 
     Per group of `group` consecutive elements of a row, in fp32:
-      lo, hi = min, max of the group
+      lo, hi = min, max of the group (each + 0, so a zero extreme is +0)
       s32 = (hi - lo) / (2^bits - 1)            (two fp32 operations)
       stored scale = RN_T(s32), stored bias = RN_T(lo)
       s, b = the stored values widened back to fp32
@@ -108,8 +98,8 @@ def quantize_affine(w_stored, dtype: str, bits: int, group: int):
     N, K = v.shape
     n = _F32(2 ** bits - 1)
     g = v.reshape(N, K // group, group)
-    lo = g.min(axis=2)
-    hi = g.max(axis=2)
+    lo = g.min(axis=2) + _F32(0)      # -0 + 0 = +0: zero extremes count as +0
+    hi = g.max(axis=2) + _F32(0)
     s32 = (hi - lo) / n
     s_st = _store(s32, dtype)
     b_st = _store(lo, dtype)

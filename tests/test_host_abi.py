@@ -26,7 +26,8 @@ def test_library_exports_every_header_function(lib):
     assert {"qmv_affine", "qmv_fp_mxfp4", "qmv_fp_nvfp4", "qmv_fp_mxfp8", "gather_qmv",
             "qmv_pack_codes", "qmv_unpack_codes", "qmv_encode_e4m3",
             "qmv_unpack_codes_device", "qmv_dequant_device", "qmv_packed_row_bytes",
-            "qmv_last_error"} <= set(names)
+            "qmv_quantize_affine", "qmv_quantize_mxfp4", "qmv_quantize_mxfp8",
+            "qmv_quantize_nvfp4", "qmv_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -103,6 +104,29 @@ def test_device_codec_validation(lib):
     assert lib.qmv_unpack_codes_device(None, W, 4, 64, 7, V(0x90000)) == UNSUP
     wt = bmv.QmvWeights(bmv.QMV_MXFP8, 8, 32, 2, 16, 64, 0x20000, 0x30000, None, None)
     assert lib.qmv_dequant_device(None, 2, ctypes.byref(wt), V(0x90000)) == INVAL
+
+
+def test_quantize_validation(lib):
+    P = V(0x90000)
+    qa = lib.qmv_quantize_affine
+    assert qa(None, 9, 16, 512, W, 4, 64, P, S, Bi) == INVAL
+    assert qa(None, 2, 16, 512, W, 7, 64, P, S, Bi) == UNSUP
+    assert qa(None, 2, 16, 512, W, 4, 48, P, S, Bi) == UNSUP
+    assert qa(None, 2, 16, 96, W, 4, 64, P, S, Bi) == INVAL
+    assert qa(None, 2, 16, 500, W, 4, 32, P, S, Bi) == INVAL
+    assert qa(None, 2, -1, 512, W, 4, 64, P, S, Bi) == INVAL
+    assert qa(None, 2, 16, 512, V(0x20008), 4, 64, P, S, Bi) == MISAL
+    assert "w is not 16-byte" in lib.qmv_last_error().decode()
+    assert qa(None, 2, 16, 512, W, 4, 64, V(0x90004), S, Bi) == MISAL
+    assert qa(None, 2, 16, 512, W, 4, 64, P, None, Bi) == INVAL
+    assert qa(None, 2, 16, 512, W, 4, 64, P, S, V(0x40001)) == MISAL
+    assert qa(None, 2, 0, 512, None, 4, 64, None, None, None) == OK
+    assert lib.qmv_quantize_mxfp4(None, 2, 16, 48, W, P, S) == INVAL
+    assert lib.qmv_quantize_mxfp8(None, 2, 16, 64, W, None, S) == INVAL
+    assert lib.qmv_quantize_nvfp4(None, 2, 16, 64, W, P, S, None) == INVAL
+    assert "global_scale" in lib.qmv_last_error().decode()
+    assert lib.qmv_quantize_nvfp4(None, 2, 16, 64, W, P, S, V(0x60002)) == MISAL
+    assert lib.qmv_quantize_nvfp4(None, 2, 16, 0, None, None, None, None) == OK
 
 
 @pytest.mark.parametrize("fmt,bits,K,expect", [

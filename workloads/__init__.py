@@ -316,3 +316,41 @@ def config5(fmt: str, proj: str, *, E: int = 64, hidden: int = 4096, ffn: int = 
     x = to_storage(rng.normal(0.0, 1.0, size=(n_x, K)), dtype)
     return MoeCase(fmt, dtype, E, K, N, w, scales, x, lhs, rhs, biases=biases, bits=bits,
                    group=group, key=key)
+
+
+# ---------------------------------------------------------------------------
+# Quantize-from-float inputs: float weight matrices [N, K] in T.
+# ---------------------------------------------------------------------------
+def quant_weights(cfg_id: int, key: str, N: int, K: int, dtype: str = "bf16",
+                  special_rows: bool = True) -> np.ndarray:
+    """Weights ~ N(0, sigma_n^2) with a log-normal spread of row scales
+    (sigma_n = 0.02 * exp(N(0, 1))), stored in T. With special_rows the first
+    rows (when N allows) are, in order: a constant row; an all-zero row with
+    signed zeros; a row of midpoints between neighbouring E2M1 values in blocks
+    whose largest magnitude is 6; the same for E4M3 with 448; a row whose
+    groups span [0, 3] with values k + 0.5 (midpoints of a unit step); and a
+    row of magnitudes near 2^-130 (fp32 subnormals)."""
+    rng = rng_for(cfg_id, key)
+    sig = 0.02 * np.exp(rng.normal(0.0, 1.0, size=(N, 1)))
+    w = rng.normal(0.0, 1.0, size=(N, K)) * sig
+    if special_rows and K >= 32:
+        rows = []
+        rows.append(np.full(K, 0.3125))
+        z = np.zeros(K)
+        z[1::2] = -0.0
+        rows.append(z)
+        mids_e2m1 = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -5.0])
+        r = np.resize(mids_e2m1, K)
+        r[::32] = 6.0
+        rows.append(r)
+        mids_e4m3 = np.array([1.0625, 2.125, 0.015625 * 1.5, 2.0 ** -10, 3.0 * 2.0 ** -10,
+                              -1.0625, 300.0, 432.0])
+        r = np.resize(mids_e4m3, K)
+        r[::32] = 448.0
+        rows.append(r)
+        r = np.resize(np.array([0.0, 3.0, 0.5, 1.5, 2.5, 1.0, 2.0]), K)
+        rows.append(r)
+        rows.append(rng.normal(0.0, 1.0, size=K) * 2.0 ** -130)
+        for i, r in enumerate(rows[:N]):
+            w[i] = r
+    return to_storage(w, dtype)
