@@ -126,6 +126,57 @@ class GatherRunner:
         self.keep = self.wts = None
 
 
+class QuantRunner:
+    """Pre-marshalled quantize-from-float calls: a bf16 [N, K] weight matrix
+    (rotating copies over >= 512 MiB, so every call reads from HBM) to one of
+    the packed formats. Bytes: the input read once plus packed codes and
+    scales written (NVFP4 reads the input twice, once for the tensor maximum;
+    only one read is counted)."""
+
+    def __init__(self, bmv, fmt: str, N: int = 14336, K: int = 4096, min_bytes: int = 1 << 29):
+        import torch
+        import workloads
+        self.lib = bmv.load()
+        self.fmt, self.N, self.K = fmt, N, K
+        w0 = _dev(workloads.quant_weights(30, f"bench-quant-{fmt}", N, K, "bf16",
+                                          special_rows=False), "bf16")
+        self.copies = max(2, -(-min_bytes // w0.nbytes))
+        self.ws = [w0] + [w0.clone() for _ in range(self.copies - 1)]
+        dev = "cuda:0"
+        bits = {"affine4": 4, "mxfp4": 4, "nvfp4": 4, "mxfp8": 8}[fmt]
+        self.packed = torch.empty((N, K * bits // 8), dtype=torch.uint8, device=dev)
+        if fmt == "affine4":
+            self.sc = torch.empty((N, K // 64), dtype=torch.bfloat16, device=dev)
+            self.bi = torch.empty_like(self.sc)
+            out = self.packed.nbytes + 2 * self.sc.nbytes
+        else:
+            blk = 16 if fmt == "nvfp4" else 32
+            self.sc = torch.empty((N, K // blk), dtype=torch.uint8, device=dev)
+            self.gs = torch.empty((1,), dtype=torch.float32, device=dev)
+            out = self.packed.nbytes + self.sc.nbytes
+        self.bytes = w0.nbytes + out
+
+    def call(self, i: int, stream) -> None:
+        vp = ctypes.c_void_p
+        w = vp(self.ws[i % self.copies].data_ptr())
+        P, S = vp(self.packed.data_ptr()), vp(self.sc.data_ptr())
+        if self.fmt == "affine4":
+            st = self.lib.qmv_quantize_affine(stream, 2, self.N, self.K, w, 4, 64, P, S,
+                                              vp(self.bi.data_ptr()))
+        elif self.fmt == "mxfp4":
+            st = self.lib.qmv_quantize_mxfp4(stream, 2, self.N, self.K, w, P, S)
+        elif self.fmt == "mxfp8":
+            st = self.lib.qmv_quantize_mxfp8(stream, 2, self.N, self.K, w, P, S)
+        else:
+            st = self.lib.qmv_quantize_nvfp4(stream, 2, self.N, self.K, w, P, S,
+                                             vp(self.gs.data_ptr()))
+        if st != 0:
+            raise RuntimeError(self.lib.qmv_last_error().decode())
+
+    def free(self):
+        self.ws = None
+
+
 def time_chain(bmv, steps: int = 100) -> dict:
     """Config 2: a dependent chain of 100 calls (8-bit affine g64, K=N=2560,
     bf16), each output the next input; same weights every call (warm), as in
@@ -545,6 +596,14 @@ def main() -> int:
         ch = time_chain(bmv)
         cases.append(ch)
         print(f"[bench] {ch['case']}: {json.dumps(ch)}", file=sys.stderr, flush=True)
+        for fmt in ("mxfp4", "nvfp4", "mxfp8", "affine4"):
+            r = QuantRunner(bmv, fmt)
+            cr = time_case(r, max(100, args.steps // 10), 10)
+            r.free()
+            cr["case"] = f"quantize bf16 [14336, 4096] -> {fmt}" + (" g64" if fmt == "affine4" else "")
+            cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
+            cases.append(cr)
+            print(f"[bench] {cr['case']}: {json.dumps(cr)}", file=sys.stderr, flush=True)
     if args.sweep:
         for bits in workloads.AFFINE_BITS:
             for group in workloads.AFFINE_GROUPS:
