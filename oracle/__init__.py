@@ -28,6 +28,9 @@ passage it follows):
   of each slot picks the weight matrix; no per-expert host dispatch).
 * "ferrum-kernels - primitives.rs" tests: an out-of-range index yields a row
   of zeros rather than a fault.
+* The fused routed-MoE decode block (``moe.py``): the ds4 moe.metal SwiGLU
+  activation and per-token down-projection sum, and the audit's two-dispatch
+  description of the block.
 * Quantize-from-float (``quantize.py``): the audit's Track-2 min/max encoder
   and the fp_quantized / kv_cache rows' max-scale element rounding, with the
   readings its docstring states.
@@ -59,6 +62,13 @@ from .quantize import (
     quantize_affine,
     quantize_mx,
     quantize_nvfp4,
+)
+from .moe import (
+    silu,
+    swiglu,
+    gate_up_projections,
+    moe_gate_up_swiglu,
+    moe_down_reduce,
 )
 from .qmv import (
     dequant_affine,
