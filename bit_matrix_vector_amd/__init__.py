@@ -71,6 +71,10 @@ def load() -> ctypes.CDLL:
         "qmv_encode_e4m3": [vp, i64, vp],
         "qmv_unpack_codes_device": [vp, vp, i64, i64, i32, vp],
         "qmv_dequant_device": [vp, i32, ctypes.POINTER(QmvWeights), vp],
+        "qmv_moe_gate_up_swiglu": [vp, i32, ctypes.POINTER(QmvWeights),
+                                   ctypes.POINTER(QmvWeights), vp, i64, vp, i64, ctypes.c_float,
+                                   vp],
+        "qmv_moe_down_reduce": [vp, i32, ctypes.POINTER(QmvWeights), vp, i64, vp, vp, i64, vp],
         "qmv_quantize_affine": [vp, i32, i64, i64, vp, i32, i32, vp, vp, vp],
         "qmv_quantize_mxfp4": [vp, i32, i64, i64, vp, vp, vp],
         "qmv_quantize_mxfp8": [vp, i32, i64, i64, vp, vp, vp],
@@ -268,6 +272,43 @@ def qmv_dequant_device(weights: QmvWeights, dtype_code: int, device, out=None):
     _check(load().qmv_dequant_device(_stream(out.device), dtype_code, ctypes.byref(weights),
                                      _ptr(out)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# fused routed-MoE decode block
+# ---------------------------------------------------------------------------
+
+def qmv_moe_gate_up_swiglu(x, gate: QmvWeights, up: QmvWeights, expert_ids, clamp: float = 0.0,
+                           mid=None):
+    """mid [T * top_k, ffn] = silu(clamp(gate . x)) * clamp(up . x) per routed
+    slot; expert_ids: int32 tensor [T, top_k] holding uint32 ids."""
+    torch = _torch()
+    x = _dev(x, "x")
+    _dev(expert_ids, "expert_ids", torch.int32)
+    T, k = expert_ids.shape
+    if mid is None:
+        mid = torch.empty((T * k, gate.N), dtype=x.dtype, device=x.device)
+    _dev(mid, "mid", x.dtype)
+    _check(load().qmv_moe_gate_up_swiglu(_stream(x.device), _dtype_code(x), ctypes.byref(gate),
+                                         ctypes.byref(up), _ptr(x), T, _ptr(expert_ids), k,
+                                         float(clamp), _ptr(mid)))
+    return mid
+
+
+def qmv_moe_down_reduce(mid, down: QmvWeights, expert_ids, route_weights, y=None):
+    """y [T, hidden] = sum_j route_weights[t, j] * (down[e] . mid[t * top_k + j])."""
+    torch = _torch()
+    mid = _dev(mid, "mid")
+    _dev(expert_ids, "expert_ids", torch.int32)
+    _dev(route_weights, "route_weights", torch.float32)
+    T, k = expert_ids.shape
+    if y is None:
+        y = torch.empty((T, down.N), dtype=mid.dtype, device=mid.device)
+    _dev(y, "y", mid.dtype)
+    _check(load().qmv_moe_down_reduce(_stream(mid.device), _dtype_code(mid), ctypes.byref(down),
+                                      _ptr(mid), T, _ptr(expert_ids), _ptr(route_weights), k,
+                                      _ptr(y)))
+    return y
 
 
 # ---------------------------------------------------------------------------

@@ -138,6 +138,34 @@ qmv_status_t run_qmv(const char* fn, void* stream, int dtype, int format, int bi
     return launch_status(qmv::launch_qmv(lp, stream), fn);
 }
 
+// Checks of an expert-stacked weights struct; fills the launch's format
+// geometry and weight pointers.
+qmv_status_t check_weights(const char* fn, const char* what, int dtype, const qmv_weights_t* wt,
+                           qmv::LaunchParams& lp) {
+    if (wt == nullptr)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: %s weights struct is NULL", fn, what);
+    if (wt->n_experts < 0) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: negative count", fn);
+    if (wt->n_experts > 65534)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: n_experts too large", fn);
+    QMV_TRY(check_common(fn, dtype, 1, wt->K, wt->N, 1));
+    lp.dtype = dtype;
+    QMV_TRY(format_geometry(fn, wt->format, wt->bits, wt->group_size, wt->K, lp));
+    const int tb = dtype_bytes(dtype);
+    const bool has_w = wt->K > 0 && wt->N > 0 && wt->n_experts > 0;
+    QMV_TRY(check_ptr(fn, "w", wt->w, has_w, 16));
+    if (wt->format == QMV_AFFINE) {
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, has_w, tb));
+        QMV_TRY(check_ptr(fn, "biases", wt->biases, has_w, tb));
+    } else {
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, has_w, wt->format == QMV_NVFP4 ? 2 : 1));
+    }
+    QMV_TRY(check_ptr(fn, "global_scale", wt->global_scale, wt->global_scale != nullptr, 4));
+    lp.K = wt->K; lp.N = wt->N; lp.n_experts = wt->n_experts;
+    lp.w = wt->w; lp.scales = wt->scales; lp.biases = wt->biases;
+    lp.gscale = wt->format == QMV_NVFP4 ? wt->global_scale : nullptr;
+    return QMV_OK;
+}
+
 qmv_status_t run_quantize(const char* fn, void* stream, int dtype, int format, int bits,
                           int group, int64_t N, int64_t K, const void* w, uint8_t* packed,
                           void* scales, void* biases, float* gscale) {
@@ -165,6 +193,76 @@ qmv_status_t run_quantize(const char* fn, void* stream, int dtype, int format, i
 }  // namespace
 
 extern "C" {
+
+qmv_status_t qmv_moe_gate_up_swiglu(void* stream, int dtype, const qmv_weights_t* gate,
+                                    const qmv_weights_t* up, const void* x, int64_t n_tokens,
+                                    const uint32_t* expert_ids, int64_t top_k, float clamp,
+                                    void* mid) {
+    const char* fn = "qmv_moe_gate_up_swiglu";
+    qmv::LaunchParams lp{};
+    QMV_TRY(check_weights(fn, "gate", dtype, gate, lp));
+    qmv::LaunchParams lu{};
+    QMV_TRY(check_weights(fn, "up", dtype, up, lu));
+    if (gate->format != up->format || gate->N != up->N || gate->K != up->K ||
+        gate->n_experts != up->n_experts ||
+        (gate->format == QMV_AFFINE && (gate->bits != up->bits ||
+                                        gate->group_size != up->group_size)))
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: gate and up weights differ in layout", fn);
+    if (n_tokens < 0 || top_k < 1)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: n_tokens >= 0 and top_k >= 1 required", fn);
+    if (n_tokens * top_k > ((int64_t)1 << 31))
+        return fail(QMV_ERR_UNSUPPORTED, "%s: too many slots", fn);
+    const int tb = dtype_bytes(dtype);
+    if (2 * gate->K * tb > 64 * 1024)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: K=%lld too large (two x rows of K must fit 64 KB)",
+                    fn, (long long)gate->K);
+    if (n_tokens == 0 || gate->N == 0) return QMV_OK;
+    QMV_TRY(check_ptr(fn, "mid", mid, true, tb));
+    QMV_TRY(check_ptr(fn, "expert_ids", expert_ids, true, 4));
+    QMV_TRY(check_ptr(fn, "x", x, gate->K > 0, 16));
+    if (!(clamp == clamp)) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: clamp is NaN", fn);
+    lp.B = 1; lp.x = x; lp.y = mid;
+    lp.n_x_rows = n_tokens; lp.n_slots = n_tokens * top_k;
+    lp.rhs = expert_ids; lp.lhs = nullptr;
+    qmv::MoeArgs ma{};
+    ma.w2 = lu.w; ma.scales2 = lu.scales; ma.biases2 = lu.biases; ma.gscale2 = lu.gscale;
+    ma.top_k = top_k; ma.act_clamp = clamp;
+    if (gate->K == 0)   // empty projections: silu(0) * 0 = 0 for every slot
+        return launch_status(qmv::launch_zero_fill(mid, n_tokens * top_k * gate->N * tb, stream),
+                             fn);
+    return launch_status(qmv::launch_moe_gate_up(lp, ma, stream), fn);
+}
+
+qmv_status_t qmv_moe_down_reduce(void* stream, int dtype, const qmv_weights_t* down,
+                                 const void* mid, int64_t n_tokens, const uint32_t* expert_ids,
+                                 const float* route_weights, int64_t top_k, void* y) {
+    const char* fn = "qmv_moe_down_reduce";
+    qmv::LaunchParams lp{};
+    QMV_TRY(check_weights(fn, "down", dtype, down, lp));
+    if (n_tokens < 0 || top_k < 1)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: n_tokens >= 0 and top_k >= 1 required", fn);
+    const int tb = dtype_bytes(dtype);
+    if (top_k > 16 || top_k * down->K * tb > 64 * 1024)
+        return fail(QMV_ERR_UNSUPPORTED,
+                    "%s: top_k=%lld with K=%lld exceeds the staging limit (top_k <= 16, "
+                    "top_k * K * sizeof(T) <= 64 KB)", fn, (long long)top_k, (long long)down->K);
+    if (n_tokens > 65535) return fail(QMV_ERR_UNSUPPORTED, "%s: n_tokens above 65535", fn);
+    if (n_tokens == 0 || down->N == 0) return QMV_OK;
+    QMV_TRY(check_ptr(fn, "y", y, true, tb));
+    QMV_TRY(check_ptr(fn, "expert_ids", expert_ids, true, 4));
+    QMV_TRY(check_ptr(fn, "route_weights", route_weights, true, 4));
+    QMV_TRY(check_ptr(fn, "mid", mid, down->K > 0, 16));
+    lp.B = 1; lp.x = mid; lp.y = y;
+    lp.n_x_rows = n_tokens; lp.n_slots = n_tokens * top_k;
+    lp.rhs = expert_ids;
+    qmv::MoeArgs ma{};
+    ma.top_k = top_k; ma.route_w = route_weights;
+    if (down->K == 0) {
+        // empty sums: y = 0 (the plain kernel with no slots of any expert)
+        lp.n_experts = 0; lp.lhs = nullptr;
+    }
+    return launch_status(qmv::launch_moe_down(lp, ma, stream), fn);
+}
 
 qmv_status_t qmv_quantize_affine(void* stream, int dtype, int64_t N, int64_t K, const void* w,
                                  int bits, int group_size, uint8_t* packed, void* scales,

@@ -31,6 +31,26 @@ struct LaunchParams {
     const uint32_t* rhs;
 };
 
+// Extra arguments of the fused routed-MoE kernels, kept out of LaunchParams:
+// every byte of kernel arguments costs scalar registers, and the QMV kernel
+// sits at the scalar-register limit. The up matrix of the gate/up pair (same
+// format and shape as w), slots per token (x row of slot s = s / top_k), the
+// activation clamp (off when <= 1e-6) and the router weights [T, top_k].
+struct MoeArgs {
+    const uint8_t* w2;
+    const void* scales2;
+    const void* biases2;
+    const float* gscale2;
+    int64_t top_k;
+    float act_clamp;
+    const float* route_w;
+};
+struct NoMoeArgs {};
+
+int launch_moe_gate_up(const LaunchParams& p, const MoeArgs& m, void* stream);
+int launch_zero_fill(void* p, int64_t bytes, void* stream);   // bytes % 2 == 0
+int launch_moe_down(const LaunchParams& p, const MoeArgs& m, void* stream);
+
 // One quantize-from-float call: w [N, K] in `dtype` to the packed format.
 struct QuantParams {
     int dtype;

@@ -7,6 +7,8 @@ namespace qmv {
 #define QMV_DECL_PART(dt, fam)                                                          \
     int launch_qmv_part_##dt##_##fam(const LaunchParams&, void*);                       \
     int launch_gather_part_##dt##_##fam(const LaunchParams&, void*);                    \
+    int launch_moe_gate_up_part_##dt##_##fam(const LaunchParams&, const MoeArgs&, void*); \
+    int launch_moe_down_part_##dt##_##fam(const LaunchParams&, const MoeArgs&, void*);  \
     int launch_dequant_part_##dt##_##fam(const LaunchParams&, float*, void*);
 QMV_DECL_PART(0, 0) QMV_DECL_PART(0, 1) QMV_DECL_PART(1, 0)
 QMV_DECL_PART(1, 1) QMV_DECL_PART(2, 0) QMV_DECL_PART(2, 1)
@@ -32,6 +34,32 @@ int launch_qmv(const LaunchParams& p, void* stream) {
 
 int launch_gather(const LaunchParams& p, void* stream) {
     QMV_ROUTE(launch_gather_part, p, stream);
+}
+
+int launch_moe_gate_up(const LaunchParams& p, const MoeArgs& m, void* stream) {
+    QMV_ROUTE(launch_moe_gate_up_part, p, m, stream);
+}
+
+int launch_moe_down(const LaunchParams& p, const MoeArgs& m, void* stream) {
+    QMV_ROUTE(launch_moe_down_part, p, m, stream);
+}
+
+namespace {
+__global__ void zero_fill_kernel(uint16_t* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * 256)
+        p[i] = 0;
+}
+}  // namespace
+
+int launch_zero_fill(void* p, int64_t bytes, void* stream) {
+    const int64_t n = bytes / 2;
+    if (n == 0) return 0;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0,
+                       static_cast<hipStream_t>(stream), static_cast<uint16_t*>(p), n);
+    return (int)hipGetLastError();
 }
 
 int launch_dequant_device(const LaunchParams& p, float* out, void* stream) {

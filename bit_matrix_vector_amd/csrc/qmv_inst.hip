@@ -47,6 +47,16 @@ template <int DT, int FMT, int BITS> struct GatherL {
         return launch_gather_t<DT, FMT, BITS>(p, s);
     }
 };
+template <int DT, int FMT, int BITS> struct MoeGateUpL {
+    static int run(const LaunchParams& p, const MoeArgs& m, hipStream_t s) {
+        return launch_moe_gate_up_t<DT, FMT, BITS>(p, m, s);
+    }
+};
+template <int DT, int FMT, int BITS> struct MoeDownL {
+    static int run(const LaunchParams& p, const MoeArgs& m, hipStream_t s) {
+        return launch_moe_down_t<DT, FMT, BITS>(p, m, s);
+    }
+};
 template <int DT, int FMT, int BITS> struct DequantL {
     static int run(const LaunchParams& p, float* out, hipStream_t s) {
         return launch_dequant_t<DT, FMT, BITS>(p, out, s);
@@ -60,6 +70,14 @@ int QMV_PART(launch_qmv_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, void* str
 }
 int QMV_PART(launch_gather_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, void* stream) {
     return dispatch_part<GatherL>(p, static_cast<hipStream_t>(stream));
+}
+int QMV_PART(launch_moe_gate_up_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, const MoeArgs& m,
+                                                        void* stream) {
+    return dispatch_part<MoeGateUpL>(p, m, static_cast<hipStream_t>(stream));
+}
+int QMV_PART(launch_moe_down_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, const MoeArgs& m,
+                                                     void* stream) {
+    return dispatch_part<MoeDownL>(p, m, static_cast<hipStream_t>(stream));
 }
 int QMV_PART(launch_dequant_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, float* out,
                                                      void* stream) {

@@ -55,6 +55,8 @@ struct Geom {
     int sc_lds_off;  // byte offset of the staged scales in LDS
     int sc_aligned4; // scale rows can be copied in 4-byte words
     int tiles_per_block;  // gather: consecutive row tiles one block runs
+    int out_rows;         // gather: output rows per tile (rows_per_block, or half
+                          // of it when each lane group computes a gate/up pair)
 };
 
 // x rows of a tile. Contiguous rows (qmv) or rows picked by an index list
@@ -469,8 +471,29 @@ constexpr int kGatherDepth = 2;
 // global memory and stay in flight across tile boundaries, and no barrier is
 // taken, so each wave moves on at its own pace. A row's units, their order and
 // the final reduction are those of qmv_tile, so results match it bit for bit.
-template <int DT, int FMT, int BITS, int NB, int R>
-__device__ inline void gather_tiles(const LaunchParams& p, const Geom& g, int64_t tile0,
+// Gather modes: plain rows, or (MODE 1, R = 2) a lane group computing the
+// gate row (from w) and the up row (from w2) of one output row, whose epilogue
+// stores the activation swiglu(gate, up) instead of the two projections.
+constexpr int kGatherPlain = 0;
+constexpr int kGatherSwiglu = 1;
+
+// silu(clamp(g)) * clamp(u): clamp g from above and u on both sides when the
+// clamp is positive; silu(g) = g / (1 + exp(-g)) (exp overflowing to infinity
+// for very negative g gives the limit 0).
+__device__ inline float swiglu_act(float g, float u, float c) {
+    if (c > 1.0e-6f) {
+        g = fminf(g, c);
+        u = fminf(fmaxf(u, -c), c);
+    }
+    return g / (1.0f + expf(-g)) * u;
+}
+
+template <int MODE>
+using MoeArgsOf = typename std::conditional<MODE == kGatherSwiglu, MoeArgs, NoMoeArgs>::type;
+
+template <int DT, int FMT, int BITS, int NB, int R, int MODE = kGatherPlain>
+__device__ inline void gather_tiles(const LaunchParams& p, const MoeArgsOf<MODE>& m,
+                                    const Geom& g, int64_t tile0,
                                     int64_t tile_end, const uint8_t* __restrict__ w,
                                     const void* sc, const void* bi,
                                     typename Store<DT>::S* const (&yrow)[NB], float gmul,
@@ -493,8 +516,10 @@ __device__ inline void gather_tiles(const LaunchParams& p, const Geom& g, int64_
     const int ks = (int)p.K;
     const int us = ks >> 5;
     const int iters = (us + lpr - 1) >> g.lpr_log2;   // >= 1 (K > 0)
-    const int64_t RB = g.rows_per_block;
-    const int64_t rofs = (int64_t)(wave * (64 >> g.lpr_log2) + grp) * R;
+    static_assert(MODE == kGatherPlain || R == 2, "a gate/up pair takes two rows");
+    constexpr bool kPair = MODE == kGatherSwiglu;
+    const int64_t RB = g.out_rows;   // output rows per tile
+    const int64_t rofs = (int64_t)(wave * (64 >> g.lpr_log2) + grp) * (kPair ? 1 : R);
     const int64_t n_items = (tile_end - tile0) * iters;
 
     // Load cursor. Addresses are a per-tile base (uniform) plus 32-bit
@@ -504,22 +529,35 @@ __device__ inline void gather_tiles(const LaunchParams& p, const Geom& g, int64_
     const int64_t sc_row_bytes = p.sc_per_row * F::template elem_bytes<DT>();
     const uint8_t* const sc8 = static_cast<const uint8_t*>(sc);
     const uint8_t* const bi8 = static_cast<const uint8_t*>(bi);
+    // pair mode: row i = 1 comes from the second matrix (same layout)
+    const uint8_t* w_of[2] = {w, w};
+    const uint8_t* sc_of[2] = {sc8, sc8};
+    const uint8_t* bi_of[2] = {bi8, bi8};
+    if constexpr (kPair) {
+        w_of[1] = m.w2;
+        sc_of[1] = static_cast<const uint8_t*>(m.scales2);
+        bi_of[1] = static_cast<const uint8_t*>(m.biases2);
+    }
+    constexpr int kBases = kPair ? 2 : 1;
     int64_t lt = tile0;
     int lit = 0;
-    const uint8_t* wt;   // weights of the cursor tile's first row
-    const uint8_t* st;   // its scales (and, for affine, biases at bt)
-    const uint8_t* bt;
+    const uint8_t* wt[kBases];   // weights of the cursor tile's first row
+    const uint8_t* st[kBases];   // its scales (and, for affine, biases at bt)
+    const uint8_t* bt[kBases];
     uint32_t wro[R];     // lane's row offsets from those, in weight bytes
     uint32_t sro[R];     // and in scale bytes
     auto enter_tile = [&](int64_t t) __attribute__((always_inline)) {
         const int64_t first = t * RB;
         const int64_t lim = N - 1 - first;   // last valid row, tile-relative
-        wt = w + first * p.row_bytes;
-        st = sc8 + first * sc_row_bytes;
-        bt = FMT == FMT_AFFINE ? bi8 + first * sc_row_bytes : st;
+#pragma unroll
+        for (int m = 0; m < kBases; ++m) {
+            wt[m] = w_of[m] + first * p.row_bytes;
+            st[m] = sc_of[m] + first * sc_row_bytes;
+            bt[m] = FMT == FMT_AFFINE ? bi_of[m] + first * sc_row_bytes : st[m];
+        }
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-            const int64_t r = rofs + i;
+            const int64_t r = rofs + (kPair ? 0 : i);
             const uint32_t rr = (uint32_t)(r < lim ? r : lim);
             wro[i] = rr * (uint32_t)p.row_bytes;
             sro[i] = rr * (uint32_t)sc_row_bytes;
@@ -530,8 +568,9 @@ __device__ inline void gather_tiles(const LaunchParams& p, const Geom& g, int64_
         const int u = min(gl + lit * lpr, us - 1);
 #pragma unroll
         for (int i = 0; i < R; ++i) {
-            load_words<W>(wt + (wro[i] + (uint32_t)u * kUnitBytes), x.u.d[i]);
-            x.raw[i] = F::template global_raw<DT>(st, bt, sro[i], u, g.glog2);
+            const int m = kPair ? i : 0;
+            load_words<W>(wt[m] + (wro[i] + (uint32_t)u * kUnitBytes), x.u.d[i]);
+            x.raw[i] = F::template global_raw<DT>(st[m], bt[m], sro[i], u, g.glog2);
         }
         if (++lit == iters) {
             if (lt + 1 < tile_end) {
@@ -565,15 +604,30 @@ __device__ inline void gather_tiles(const LaunchParams& p, const Geom& g, int64_
 #pragma unroll
                 for (int b = 0; b < NB; ++b) total[i][b] = group_sum(total[i][b], lpr);
             if (gl == lpr - 1) {
-#pragma unroll
-                for (int i = 0; i < R; ++i) {
-                    const int64_t r = ct * RB + rofs + i;
+                if constexpr (kPair) {
+                    const int64_t r = ct * RB + rofs;
                     if (r < N) {
 #pragma unroll
                         for (int b = 0; b < NB; ++b) {
-                            float v = total[i][b];
-                            if constexpr (FMT == FMT_NVFP4) v = v * gmul;
-                            yrow[b][r] = Store<DT>::from_f32(v);
+                            float gv = total[0][b], uv = total[1][b];
+                            if constexpr (FMT == FMT_NVFP4) {
+                                gv = gv * gmul;
+                                uv = uv * (m.gscale2 ? *m.gscale2 : 1.0f);
+                            }
+                            yrow[b][r] = Store<DT>::from_f32(swiglu_act(gv, uv, m.act_clamp));
+                        }
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < R; ++i) {
+                        const int64_t r = ct * RB + rofs + i;
+                        if (r < N) {
+#pragma unroll
+                            for (int b = 0; b < NB; ++b) {
+                                float v = total[i][b];
+                                if constexpr (FMT == FMT_NVFP4) v = v * gmul;
+                                yrow[b][r] = Store<DT>::from_f32(v);
+                            }
                         }
                     }
                 }
@@ -605,8 +659,9 @@ __device__ inline void gather_tiles(const LaunchParams& p, const Geom& g, int64_
     });
 }
 
-template <int DT, int FMT, int BITS, int R, bool kOneSlab>
-__device__ inline void gather_chunk(const LaunchParams& p, const Geom& g, int64_t tile0,
+template <int DT, int FMT, int BITS, int R, bool kOneSlab, int MODE>
+__device__ inline void gather_chunk(const LaunchParams& p, const MoeArgsOf<MODE>& m,
+                                    const Geom& g, int64_t tile0,
                                     int64_t tile_end, const uint8_t* w, const void* sc,
                                     const void* bi, float gmul, const uint32_t* list,
                                     const int64_t* xoff, int cnt,
@@ -614,7 +669,7 @@ __device__ inline void gather_chunk(const LaunchParams& p, const Geom& g, int64_
     using S = typename Store<DT>::S;
     constexpr int kPerVec = 16 / Store<DT>::kBytes;
     const XListed<S> xr{static_cast<const S*>(p.x), xoff};
-    const int64_t RB = g.rows_per_block;
+    const int64_t RB = g.out_rows;
     auto run = [&](auto nb_c) {
         constexpr int NB = decltype(nb_c)::value;
         S* yrow[NB];
@@ -633,8 +688,10 @@ __device__ inline void gather_chunk(const LaunchParams& p, const Geom& g, int64_
                         stage_vec<FMT, BITS, DT>(src[v]);
             }
             __syncthreads();
-            gather_tiles<DT, FMT, BITS, NB, R>(p, g, tile0, tile_end, w, sc, bi, yrow, gmul, lds);
+            gather_tiles<DT, FMT, BITS, NB, R, MODE>(p, m, g, tile0, tile_end, w, sc, bi, yrow,
+                                                     gmul, lds);
         } else {
+            static_assert(MODE == kGatherPlain, "the paired mode needs one slab");
             for (int64_t t = tile0; t < tile_end; ++t)
                 qmv_tile<DT, FMT, BITS, NB, R>(p, g, t * RB, w, sc, bi, xr, yrow, gmul,
                                                lds);
@@ -648,8 +705,12 @@ __device__ inline void gather_chunk(const LaunchParams& p, const Geom& g, int64_
 
 // kOneSlab: K > 0 and the geometry holds all of K in one slab (the launcher
 // checks), so the group runs gather_tiles; otherwise qmv_tile per tile.
-template <int DT, int FMT, int BITS, int R, bool kOneSlab>
-__global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g) {
+// MODE kGatherSwiglu: the fused gate/up projection of the routed-MoE block
+// (slot s reads x row s / top_k; w / w2 are the gate / up matrices; the output
+// is the activation, one row per slot).
+template <int DT, int FMT, int BITS, int R, bool kOneSlab, int MODE = kGatherPlain>
+__global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g,
+                                                          MoeArgsOf<MODE> m) {
     using S = typename Store<DT>::S;
     extern __shared__ __align__(16) unsigned char smem[];
     S* lds = reinterpret_cast<S*>(smem);
@@ -663,9 +724,16 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t RB = g.rows_per_block;
+    const int64_t RB = g.out_rows;
     const int64_t n_tiles = (p.N + RB - 1) / RB;
     const int64_t tile0 = (int64_t)blockIdx.x * g.tiles_per_block;
+    // x row of slot s
+    auto x_row_of = [&](int64_t s) __attribute__((always_inline)) {
+        if constexpr (MODE == kGatherSwiglu)
+            return (uint32_t)(s / m.top_k);
+        else
+            return p.lhs[s];
+    };
     const int64_t tile_end =
         tile0 + g.tiles_per_block < n_tiles ? tile0 + g.tiles_per_block : n_tiles;
     const int64_t e = blockIdx.y;
@@ -678,7 +746,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g
         const int64_t r1 = tile_end * RB < p.N ? tile_end * RB : p.N;
         for (int64_t s = tid; s < p.n_slots; s += kThreads) {
             const uint32_t ex = p.rhs[s];
-            const uint32_t xrw = p.lhs[s];
+            const uint32_t xrw = x_row_of(s);
             if ((int64_t)ex < p.n_experts && (int64_t)xrw < p.n_x_rows) continue;
             S* yr = static_cast<S*>(p.y) + s * p.N;
             for (int64_t r = r0; r < r1; ++r) yr[r] = Store<DT>::from_f32(0.0f);
@@ -696,12 +764,22 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g
         sc = static_cast<const uint8_t*>(p.scales) + e * p.N * p.sc_per_row;
     }
     const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
+    if constexpr (MODE == kGatherSwiglu) {
+        // the up matrix of expert e (the gate matrix is w above)
+        m.w2 = m.w2 + e * p.N * p.row_bytes;
+        if constexpr (FMT == FMT_AFFINE) {
+            m.scales2 = static_cast<const S*>(m.scales2) + e * p.N * p.sc_per_row;
+            m.biases2 = static_cast<const S*>(m.biases2) + e * p.N * p.sc_per_row;
+        } else {
+            m.scales2 = static_cast<const uint8_t*>(m.scales2) + e * p.N * p.sc_per_row;
+        }
+    }
 
     auto run_chunk = [&](int cnt) {
         if (tid < cnt) xoff[tid] = (int64_t)xrow[tid] * p.K;
         __syncthreads();
-        gather_chunk<DT, FMT, BITS, R, kOneSlab>(p, g, tile0, tile_end, w, sc, bi, gmul, list,
-                                                 xoff, cnt, lds);
+        gather_chunk<DT, FMT, BITS, R, kOneSlab, MODE>(p, m, g, tile0, tile_end, w, sc, bi,
+                                                       gmul, list, xoff, cnt, lds);
         __syncthreads();
     };
 
@@ -712,7 +790,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g
         // both indices are read together (clamped), so one round trip serves
         const int64_t si = s < p.n_slots ? s : p.n_slots - 1;
         const uint32_t ex = p.rhs[si];
-        const uint32_t xr = p.lhs[si];
+        const uint32_t xr = x_row_of(si);
         const bool match = s < p.n_slots && (int64_t)ex == e && (int64_t)xr < p.n_x_rows;
         const uint64_t m = __ballot(match);
         const int before = __popcll(m & ((1ull << lane) - 1ull));
@@ -753,6 +831,211 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g
     }
     const int cnt = count;
     if (cnt > 0) run_chunk(cnt);
+}
+
+// ---------------------------------------------------------------------------
+// Down projection of the routed-MoE block, summed over each token's slots:
+// y[t] = sum_j r[t, j] * (W[e[t, j]] . mid[t * top_k + j]). Grid (tile groups,
+// tokens). A block compacts its token's slots with an in-range expert (in slot
+// order), stages their mid rows in LDS (all of K), then each lane group walks
+// (tile, slot, unit) as one pipelined sequence: at a slot's end its partial
+// row sums are scaled by the slot's router weight and added to the row
+// totals; at a tile's end the totals are reduced over the lane group and
+// stored. Slots with an out-of-range expert add nothing.
+// ---------------------------------------------------------------------------
+constexpr int kMaxTopK = 16;
+
+template <int DT, int FMT, int BITS, int R>
+__global__ __launch_bounds__(kThreads) void moe_down_kernel(LaunchParams p, Geom g, MoeArgs m) {
+    using S = typename Store<DT>::S;
+    using F = Fmt<FMT, BITS>;
+    using U = UnitRaw<FMT, BITS, R>;
+    constexpr int W = F::kWords;
+    constexpr int kUnitBytes = 4 * W;
+    constexpr int kPerVec = 16 / Store<DT>::kBytes;
+    struct Item {
+        U u;
+        typename F::Raw raw[R];
+    };
+    extern __shared__ __align__(16) unsigned char smem[];
+    S* lds = reinterpret_cast<S*>(smem);
+    __shared__ uint32_t slot_e[kMaxTopK];
+    __shared__ float slot_r[kMaxTopK];
+    __shared__ uint32_t slot_j[kMaxTopK];
+    __shared__ int n_valid;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t t = blockIdx.y;
+    const int64_t N = p.N;
+    const int K = (int)p.K;
+    const int us = K >> 5;
+    const int64_t RB = g.out_rows;
+    const int64_t n_tiles = (N + RB - 1) / RB;
+    const int64_t tile0 = (int64_t)blockIdx.x * g.tiles_per_block;
+    const int64_t tile_end =
+        tile0 + g.tiles_per_block < n_tiles ? tile0 + g.tiles_per_block : n_tiles;
+
+    // (1) the token's valid slots, in slot order (wave 0, one lane per slot)
+    if (wave == 0) {
+        const int j = lane < m.top_k ? lane : (int)m.top_k - 1;
+        const uint32_t e = p.rhs[t * m.top_k + j];
+        const float r = m.route_w[t * m.top_k + j];
+        const bool ok = lane < m.top_k && (int64_t)e < p.n_experts;
+        const uint64_t m = __ballot(ok);
+        const int pos = __popcll(m & ((1ull << lane) - 1ull));
+        if (ok) {
+            slot_e[pos] = e;
+            slot_r[pos] = r;
+            slot_j[pos] = (uint32_t)j;
+        }
+        if (lane == 0) n_valid = __popcll(m);
+    }
+    __syncthreads();
+    const int nv = n_valid;
+
+    // (2) their mid rows into LDS, row v at v * K in the unit-interleaved layout
+    const int vec_per_row = K / kPerVec;
+    for (int v = 0; v < nv; ++v) {
+        const v4u* src = reinterpret_cast<const v4u*>(static_cast<const S*>(p.x) +
+                                                      (t * m.top_k + slot_j[v]) * (int64_t)K);
+        for (int c = tid; c < vec_per_row; c += kThreads)
+            *reinterpret_cast<v4u*>(lds + v * K + x_lds_slot(c * kPerVec, us)) =
+                stage_vec<FMT, BITS, DT>(src[c]);
+    }
+    __syncthreads();
+
+    const int grp = lane >> g.lpr_log2;
+    const int gl = lane & (g.lpr - 1);
+    const int lpr = g.lpr;
+    const int iters = (us + lpr - 1) >> g.lpr_log2;
+    const int64_t rofs = (int64_t)(wave * (64 >> g.lpr_log2) + grp) * R;
+    S* yrow = static_cast<S*>(p.y) + t * N;
+    const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
+
+    if (nv == 0) {
+        // no routed expert: the token's rows are zero
+        if (gl == lpr - 1) {
+            for (int64_t tt = tile0; tt < tile_end; ++tt)
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    const int64_t r = tt * RB + rofs + i;
+                    if (r < N) yrow[r] = Store<DT>::from_f32(0.0f);
+                }
+        }
+        return;
+    }
+
+    const int64_t sc_row_bytes = p.sc_per_row * F::template elem_bytes<DT>();
+    const int64_t w_mat = N * p.row_bytes;           // bytes of one expert's matrix
+    const int64_t s_mat = N * sc_row_bytes;
+    const uint8_t* const sc8 = static_cast<const uint8_t*>(p.scales);
+    const uint8_t* const bi8 = static_cast<const uint8_t*>(p.biases);
+    const int64_t n_items = (tile_end - tile0) * nv * iters;
+
+    // load cursor over (tile, slot, unit); stops at the last item
+    int64_t lt = tile0;
+    int lv = 0, lit = 0;
+    const uint8_t* wt;
+    const uint8_t* st;
+    const uint8_t* bt;
+    uint32_t wro[R], sro[R];
+    auto enter = [&]() __attribute__((always_inline)) {
+        const int64_t first = lt * RB;
+        const int64_t e = slot_e[lv];
+        wt = p.w + e * w_mat + first * p.row_bytes;
+        st = sc8 + e * s_mat + first * sc_row_bytes;
+        bt = FMT == FMT_AFFINE ? bi8 + e * s_mat + first * sc_row_bytes : st;
+        const int64_t lim = N - 1 - first;
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int64_t r = rofs + i;
+            const uint32_t rr = (uint32_t)(r < lim ? r : lim);
+            wro[i] = rr * (uint32_t)p.row_bytes;
+            sro[i] = rr * (uint32_t)sc_row_bytes;
+        }
+    };
+    enter();
+    auto load_next = [&](Item& x) __attribute__((always_inline)) {
+        const int u = min(gl + lit * lpr, us - 1);
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            load_words<W>(wt + (wro[i] + (uint32_t)u * kUnitBytes), x.u.d[i]);
+            x.raw[i] = F::template global_raw<DT>(st, bt, sro[i], u, g.glog2);
+        }
+        if (++lit == iters) {
+            if (lv + 1 < nv) {
+                lit = 0;
+                ++lv;
+                enter();
+            } else if (lt + 1 < tile_end) {
+                lit = 0;
+                lv = 0;
+                ++lt;
+                enter();
+            } else {
+                lit = iters - 1;
+            }
+        }
+    };
+
+    float part[R][1], total[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        part[i][0] = 0.0f;
+        total[i] = 0.0f;
+    }
+    int64_t ct = tile0;
+    int cv = 0, cit = 0;
+    auto consume = [&](const Item& x) __attribute__((always_inline)) {
+        const int u = gl + cit * lpr;
+        if (u < us) {
+            typename F::Scale scl[R];
+#pragma unroll
+            for (int i = 0; i < R; ++i) scl[i] = F::template decode<DT>(x.raw[i]);
+            unit_fma<DT, FMT, BITS, 1, R>(x.u, scl, lds + cv * K, u, K, us, part);
+        }
+        if (++cit == iters) {
+            const float r = slot_r[cv];
+#pragma unroll
+            for (int i = 0; i < R; ++i) {
+                total[i] = fmaf(r, part[i][0], total[i]);
+                part[i][0] = 0.0f;
+            }
+            cit = 0;
+            if (++cv == nv) {
+#pragma unroll
+                for (int i = 0; i < R; ++i) total[i] = group_sum(total[i], lpr);
+                if (gl == lpr - 1) {
+#pragma unroll
+                    for (int i = 0; i < R; ++i) {
+                        const int64_t row = ct * RB + rofs + i;
+                        if (row < N) yrow[row] = Store<DT>::from_f32(total[i] * gmul);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < R; ++i) total[i] = 0.0f;
+                cv = 0;
+                ++ct;
+            }
+        }
+    };
+
+    Item ring[kGatherDepth];
+    static_for<0, kGatherDepth>([&](auto j_c) { load_next(ring[decltype(j_c)::value]); });
+    int64_t k = 0;
+    for (; k + kGatherDepth < n_items; k += kGatherDepth) {
+        static_for<0, kGatherDepth>([&](auto j_c) {
+            constexpr int j = decltype(j_c)::value;
+            consume(ring[j]);
+            load_next(ring[j]);
+        });
+    }
+    static_for<0, kGatherDepth>([&](auto j_c) {
+        constexpr int j = decltype(j_c)::value;
+        if (k + j < n_items) consume(ring[j]);
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -981,24 +1264,97 @@ int launch_qmv_t(const LaunchParams& p, hipStream_t st) {
 // blocks, so each block runs a group of several tiles.
 constexpr int64_t kGatherBlocks = 8192;
 
-template <int DT, int FMT, int BITS>
-int launch_gather_t(const LaunchParams& p, hipStream_t st) {
-    constexpr int kChunk = gather_chunk_for(DT);
-    Geom g = make_geom<DT, FMT, BITS>(p, kChunk, kGatherStageBytes, kGatherRows);
-    const int64_t n_tiles = (p.N + g.rows_per_block - 1) / g.rows_per_block;
+// Tiles per block of a gather launch: about kGatherBlocks blocks across the
+// experts that can be active.
+inline int64_t gather_tiles_per_block(const LaunchParams& p, int64_t n_tiles) {
     const int64_t active = p.n_experts < p.n_slots ? p.n_experts : p.n_slots;
     int64_t tpb = (n_tiles * active + kGatherBlocks - 1) / kGatherBlocks;
     if (tpb < 1) tpb = 1;
     if (tpb > n_tiles) tpb = n_tiles > 0 ? n_tiles : 1;
+    return tpb;
+}
+
+template <int DT, int FMT, int BITS>
+int launch_gather_t(const LaunchParams& p, hipStream_t st) {
+    const NoMoeArgs none{};
+    constexpr int kChunk = gather_chunk_for(DT);
+    Geom g = make_geom<DT, FMT, BITS>(p, kChunk, kGatherStageBytes, kGatherRows);
+    g.out_rows = g.rows_per_block;
+    const int64_t n_tiles = (p.N + g.out_rows - 1) / g.out_rows;
+    const int64_t tpb = gather_tiles_per_block(p, n_tiles);
     g.tiles_per_block = (int)tpb;
     const dim3 grid((unsigned)((n_tiles + tpb - 1) / tpb), (unsigned)(p.n_experts + 1));
     const size_t lds = stage_bytes<DT, FMT, BITS>(p, g);
     if (g.ks >= p.K && p.K > 0)
         hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kGatherRows, true>), grid,
-                           dim3(kThreads), lds, st, p, g);
+                           dim3(kThreads), lds, st, p, g, none);
     else
         hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kGatherRows, false>), grid,
-                           dim3(kThreads), lds, st, p, g);
+                           dim3(kThreads), lds, st, p, g, none);
+    return (int)hipGetLastError();
+}
+
+// Fused gate/up + activation: the gather over slots s = t * top_k + j with
+// each lane group producing one output row from its gate and up rows. Needs
+// the chunk's x rows for all of K in LDS (up to 64 KB).
+template <int DT, int FMT, int BITS>
+int launch_moe_gate_up_t(const LaunchParams& p, const MoeArgs& m, hipStream_t st) {
+    constexpr int kChunk = gather_chunk_for(DT);
+    // one slab of all of K; the pipelined loop reads its scales from global
+    // memory, so LDS holds just the chunk's x rows
+    Geom g = make_geom<DT, FMT, BITS>(p, kChunk, 1 << 30, kGatherRows);
+    const size_t lds = (size_t)kChunk * (size_t)p.K * (DT == DT_F32 ? 4 : 2);
+    if (g.ks < p.K || p.K <= 0 || lds > (size_t)kMaxStageBytes) return (int)hipErrorInvalidValue;
+    g.out_rows = g.rows_per_block / kGatherRows;
+    const int64_t n_tiles = (p.N + g.out_rows - 1) / g.out_rows;
+    const int64_t tpb = gather_tiles_per_block(p, n_tiles);
+    g.tiles_per_block = (int)tpb;
+    const dim3 grid((unsigned)((n_tiles + tpb - 1) / tpb), (unsigned)(p.n_experts + 1));
+    auto* kern = &gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherSwiglu>;
+    static std::atomic<size_t> granted{0};
+    if (lds > 32 * 1024 && lds > granted.load(std::memory_order_relaxed)) {
+        // the static slot lists ride on top of the dynamic x stage
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return (int)e;
+        granted.store(lds, std::memory_order_relaxed);
+    }
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, p, g, m);
+    return (int)hipGetLastError();
+}
+
+// Down projection summed over each token's slots: all of K for up to top_k
+// mid rows in LDS (at most 64 KB).
+template <int DT, int FMT, int BITS>
+int launch_moe_down_t(const LaunchParams& p, const MoeArgs& m, hipStream_t st) {
+    constexpr int R = kGatherRows;
+    const int64_t tb = DT == DT_F32 ? 4 : 2;
+    const size_t lds = (size_t)(m.top_k * p.K * tb);
+    if (m.top_k > kMaxTopK || lds > (size_t)kMaxStageBytes) return (int)hipErrorInvalidValue;
+    Geom g{};
+    g.lpr = pick_lpr(p.K);
+    g.lpr_log2 = ilog2(g.lpr);
+    g.glog2 = FMT == FMT_AFFINE ? ilog2(p.group / 32) : 0;
+    g.rows_per_block = kWaves * (64 / g.lpr) * R;
+    g.out_rows = g.rows_per_block;
+    g.ks = (int)p.K;
+    const int64_t n_tiles = (p.N + g.out_rows - 1) / g.out_rows;
+    int64_t tpb = (n_tiles * p.n_x_rows + kGatherBlocks - 1) / kGatherBlocks;
+    if (tpb < 1) tpb = 1;
+    if (tpb > n_tiles) tpb = n_tiles;
+    g.tiles_per_block = (int)tpb;
+    const dim3 grid((unsigned)((n_tiles + tpb - 1) / tpb), (unsigned)p.n_x_rows);
+    auto* kern = &moe_down_kernel<DT, FMT, BITS, R>;
+    static std::atomic<size_t> granted{0};
+    if (lds > 32 * 1024 && lds > granted.load(std::memory_order_relaxed)) {
+        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return (int)e;
+        granted.store(lds, std::memory_order_relaxed);
+    }
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, p, g, m);
     return (int)hipGetLastError();
 }
 

@@ -169,6 +169,36 @@ qmv_status_t qmv_unpack_codes_device(void* stream, const uint8_t* packed, int64_
  * `dtype` is the storage type of the affine scales/biases (ignored otherwise). */
 qmv_status_t qmv_dequant_device(void* stream, int dtype, const qmv_weights_t* w, float* out);
 
+/* ---------------- fused routed-MoE decode block: DEVICE, asynchronous -------
+ * The decode step of a routed mixture-of-experts FFN in two calls
+ * ("@lgrammel/ds4-provider - moe.metal": the fused gate/up + activation
+ * kernel and the per-token down kernel over its expert slots; "wh-iron
+ * kernel-op coverage audit", op row "moe routed-expert decode fuse": two
+ * dispatches, router weights folded in the down step). Slot s = t * top_k + j
+ * of token t uses expert expert_ids[s] (uint32, [n_tokens, top_k]); a slot
+ * whose id is >= n_experts gives a zero mid row and adds nothing to y. */
+
+/* mid[s, :] = silu(g) * u in T, with g = gate[e] . x[t], u = up[e] . x[t]
+ * (fp32 accumulation as in qmv_*), each clamped first when clamp > 1e-6
+ * (g = min(g, clamp), u = clamp(u, -clamp, clamp)); silu(g) = g / (1 + exp(-g)).
+ * gate and up: same format / bits / group / n_experts / N (= ffn) / K
+ * (= hidden); x [n_tokens, K] (16-byte aligned); mid [n_tokens * top_k, N].
+ * Requires 2 * K * sizeof(T) <= 64 KB. */
+qmv_status_t qmv_moe_gate_up_swiglu(void* stream, int dtype, const qmv_weights_t* gate,
+                                    const qmv_weights_t* up, const void* x, int64_t n_tokens,
+                                    const uint32_t* expert_ids, int64_t top_k, float clamp,
+                                    void* mid);
+
+/* y[t, :] = sum_j route_weights[t, j] * (down[e] . mid[t * top_k + j, :]),
+ * accumulated in fp32 and rounded to T once. down: N = hidden, K = ffn;
+ * mid [n_tokens * top_k, K] in T (16-byte aligned); route_weights fp32
+ * [n_tokens, top_k]; y [n_tokens, N]. Requires top_k <= 16,
+ * top_k * K * sizeof(T) <= 64 KB and n_tokens <= 65535. Expert weights are read
+ * per token, so repeated experts across tokens are served from cache. */
+qmv_status_t qmv_moe_down_reduce(void* stream, int dtype, const qmv_weights_t* down,
+                                 const void* mid, int64_t n_tokens, const uint32_t* expert_ids,
+                                 const float* route_weights, int64_t top_k, void* y);
+
 /* ---------------- quantize from float: DEVICE memory, asynchronous ---------
  * Encode a row-major [N, K] matrix w of `dtype` values (16-byte aligned) into
  * the layout the QMV entry points read: packed rows [N, row_bytes] (16-byte

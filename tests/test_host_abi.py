@@ -27,7 +27,8 @@ def test_library_exports_every_header_function(lib):
             "qmv_pack_codes", "qmv_unpack_codes", "qmv_encode_e4m3",
             "qmv_unpack_codes_device", "qmv_dequant_device", "qmv_packed_row_bytes",
             "qmv_quantize_affine", "qmv_quantize_mxfp4", "qmv_quantize_mxfp8",
-            "qmv_quantize_nvfp4", "qmv_last_error"} <= set(names)
+            "qmv_quantize_nvfp4", "qmv_moe_gate_up_swiglu", "qmv_moe_down_reduce",
+            "qmv_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
 
@@ -104,6 +105,31 @@ def test_device_codec_validation(lib):
     assert lib.qmv_unpack_codes_device(None, W, 4, 64, 7, V(0x90000)) == UNSUP
     wt = bmv.QmvWeights(bmv.QMV_MXFP8, 8, 32, 2, 16, 64, 0x20000, 0x30000, None, None)
     assert lib.qmv_dequant_device(None, 2, ctypes.byref(wt), V(0x90000)) == INVAL
+
+
+def test_moe_validation(lib):
+    ids, r, M = V(0x70000), V(0x80000), V(0x90000)
+    g = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 64, 1536, 4096, 0x20000, 0x30000, None, None)
+    u8 = bmv.QmvWeights(bmv.QMV_MXFP8, 8, 32, 64, 1536, 4096, 0x20000, 0x30000, None, None)
+    f = lib.qmv_moe_gate_up_swiglu
+    assert f(None, 2, None, ctypes.byref(g), X, 16, ids, 8, 0.0, M) == INVAL
+    assert f(None, 2, ctypes.byref(g), ctypes.byref(u8), X, 16, ids, 8, 0.0, M) == INVAL
+    assert "differ" in lib.qmv_last_error().decode()
+    assert f(None, 2, ctypes.byref(g), ctypes.byref(g), X, 16, ids, 0, 0.0, M) == INVAL
+    assert f(None, 2, ctypes.byref(g), ctypes.byref(g), X, 16, None, 8, 0.0, M) == INVAL
+    assert f(None, 2, ctypes.byref(g), ctypes.byref(g), V(0x10008), 16, ids, 8, 0.0, M) == MISAL
+    big = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 4, 64, 32768, 0x20000, 0x30000, None, None)
+    assert f(None, 2, ctypes.byref(big), ctypes.byref(big), X, 2, ids, 2, 0.0, M) == UNSUP
+    assert f(None, 2, ctypes.byref(g), ctypes.byref(g), X, 0, ids, 8, 0.0, M) == OK
+    d = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 64, 4096, 1536, 0x20000, 0x30000, None, None)
+    h = lib.qmv_moe_down_reduce
+    assert h(None, 2, ctypes.byref(d), M, 16, ids, r, 17, Y) == UNSUP
+    d2 = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 64, 4096, 8192, 0x20000, 0x30000, None, None)
+    assert h(None, 2, ctypes.byref(d2), M, 16, ids, r, 8, Y) == UNSUP
+    assert h(None, 2, ctypes.byref(d), M, 16, ids, None, 8, Y) == INVAL
+    assert h(None, 2, ctypes.byref(d), M, 16, ids, V(0x80002), 8, Y) == MISAL
+    assert h(None, 2, ctypes.byref(d), M, -1, ids, r, 8, Y) == INVAL
+    assert h(None, 2, ctypes.byref(d), M, 0, ids, r, 8, Y) == OK
 
 
 def test_quantize_validation(lib):

@@ -354,3 +354,82 @@ def quant_weights(cfg_id: int, key: str, N: int, K: int, dtype: str = "bf16",
         for i, r in enumerate(rows[:N]):
             w[i] = r
     return to_storage(w, dtype)
+
+
+# ---------------------------------------------------------------------------
+# Fused routed-MoE decode block inputs.
+# ---------------------------------------------------------------------------
+@dataclass
+class MoeMatrix:
+    """One expert-stacked projection: w [E, N, row_bytes], scales [E, N, K/blk]
+    (+ biases for affine, + an fp32 global scale for NVFP4)."""
+    N: int
+    K: int
+    w: np.ndarray
+    scales: np.ndarray
+    biases: np.ndarray | None = None
+    global_scale: float | None = None
+
+
+@dataclass
+class MoeBlockCase:
+    fmt: str
+    dtype: str
+    E: int
+    hidden: int
+    ffn: int
+    x: np.ndarray          # [tokens, hidden] T
+    ids: np.ndarray        # [tokens, top_k] uint32
+    route: np.ndarray      # [tokens, top_k] float32
+    gate: MoeMatrix
+    up: MoeMatrix
+    down: MoeMatrix
+    bits: int = 4
+    group: int = 64
+
+    def matrix_bytes(self, m: MoeMatrix) -> int:
+        per = m.w[0].nbytes + m.scales[0].nbytes + (0 if m.biases is None else m.biases[0].nbytes)
+        return per
+
+
+def _moe_matrix(rng, fmt: str, E: int, N: int, K: int, dtype: str, bits: int, group: int,
+                gs: float) -> MoeMatrix:
+    """Expert weights for the fused-block cases, sized so that projections of
+    x ~ N(0, 1) land near 1 (where silu is curved): MXFP4 E8M0 exponents
+    116..122; affine scales U(0.001, 0.01) with biases -7.5 s + N(0, s);
+    NVFP4 block scales |N(0, 0.03)| as E4M3 with the given global scale."""
+    if fmt == "mxfp4":
+        w = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+        sc = rng.integers(116, 123, size=(E, N, K // 32), dtype=np.uint8)
+        return MoeMatrix(N, K, w, sc)
+    if fmt == "nvfp4":
+        w = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+        sc = _e4m3_byte_for(np.abs(rng.normal(0.0, 0.03, size=(E, N, K // 16))) / gs)
+        return MoeMatrix(N, K, w, sc, global_scale=gs)
+    if fmt == "affine":
+        w = rng.integers(0, 256, size=(E, N, K * bits // 8), dtype=np.uint8)
+        s = rng.uniform(0.001, 0.01, size=(E, N, K // group))
+        b = -7.5 * s + s * rng.normal(0.0, 1.0, size=s.shape)
+        return MoeMatrix(N, K, w, to_storage(s, dtype), to_storage(b, dtype))
+    raise ValueError(fmt)
+
+
+def moe_block_case(fmt: str, *, E: int = 64, hidden: int = 4096, ffn: int = 1536,
+                   tokens: int = 16, top_k: int = 8, dtype: str = "bf16", key: str = "",
+                   bits: int = 4, group: int = 64) -> MoeBlockCase:
+    """The routed-MoE block of config 5 (64 experts, hidden 4096, ffn 1536,
+    16 tokens, top-8) with separate gate / up / down stacks. Routing: logits
+    ~ N(0, 1) [tokens, E], top_k by logit, router weights = softmax of the
+    selected logits (renormalised over the top_k, fp64, stored fp32)."""
+    rng = rng_for(6, f"moe-block-{fmt}-{dtype}-{key}")
+    logits = rng.normal(0.0, 1.0, size=(tokens, E))
+    ids = route_topk(logits, top_k)
+    sel = np.take_along_axis(logits, ids, axis=1)
+    ex = np.exp(sel - sel.max(axis=1, keepdims=True))
+    route = (ex / ex.sum(axis=1, keepdims=True)).astype(np.float32)
+    gate = _moe_matrix(rng, fmt, E, ffn, hidden, dtype, bits, group, 0.5)
+    up = _moe_matrix(rng, fmt, E, ffn, hidden, dtype, bits, group, 0.25)
+    down = _moe_matrix(rng, fmt, E, hidden, ffn, dtype, bits, group, 0.5)
+    x = to_storage(rng.normal(0.0, 1.0, size=(tokens, hidden)), dtype)
+    return MoeBlockCase(fmt, dtype, E, hidden, ffn, x, ids.astype(np.uint32), route, gate, up,
+                        down, bits, group)
