@@ -177,6 +177,69 @@ class QuantRunner:
         self.ws = None
 
 
+class MoeBlockRunner:
+    """The fused routed-MoE decode block of config 5 (64 experts, hidden 4096,
+    ffn 1536, 16 tokens, top-8): gate/up + SwiGLU, then the per-token down sum
+    (two launches per call), over two copies of the three expert stacks
+    (~0.6 GB each for MXFP4, beyond the 256 MB Infinity Cache). Bytes: the
+    distinct experts' gate, up and down matrices once, x, mid written and read,
+    y, expert ids and router weights."""
+
+    def __init__(self, bmv, fmt: str, copies: int = 2):
+        import torch
+        import workloads
+        self.lib = bmv.load()
+        c = workloads.moe_block_case(fmt, key="bench")
+        self.c = c
+        dev = "cuda:0"
+        blk = {"affine": c.group, "mxfp4": 32, "nvfp4": 16}[fmt]
+        self.keep, self.wts = [], []
+        for i in range(copies):
+            trip = []
+            for m in (c.gate, c.up, c.down):
+                w = _dev(m.w)
+                sc = _dev(m.scales, c.dtype if fmt == "affine" else None)
+                bi = _dev(m.biases, c.dtype) if m.biases is not None else None
+                gs = (torch.tensor([m.global_scale], dtype=torch.float32, device=dev)
+                      if m.global_scale is not None else None)
+                self.keep.append((w, sc, bi, gs))
+                trip.append(bmv.make_weights(fmt, w, sc, bi, K=m.K, bits=c.bits,
+                                             group_size=blk, global_scale=gs))
+            self.wts.append(trip)
+        self.copies = copies
+        self.x = _dev(c.x, c.dtype)
+        self.ids = torch.from_numpy(c.ids.view(np.int32)).to(dev)
+        self.route = torch.from_numpy(c.route).to(dev)
+        T, k = c.ids.shape
+        self.T, self.k = T, k
+        self.mid = torch.empty((T * k, c.ffn), dtype=self.x.dtype, device=dev)
+        self.y = torch.empty((T, c.hidden), dtype=self.x.dtype, device=dev)
+        d = len(np.unique(c.ids))
+        tb = 2
+        self.bytes = (d * (c.matrix_bytes(c.gate) + c.matrix_bytes(c.up) + c.matrix_bytes(c.down))
+                      + T * c.hidden * tb + 2 * T * k * c.ffn * tb + T * c.hidden * tb
+                      + T * k * 8)
+        self.distinct = d
+
+    def call(self, i: int, stream) -> None:
+        vp = ctypes.c_void_p
+        g, u, d = self.wts[i % self.copies]
+        st = self.lib.qmv_moe_gate_up_swiglu(stream, 2, ctypes.byref(g), ctypes.byref(u),
+                                             vp(self.x.data_ptr()), self.T,
+                                             vp(self.ids.data_ptr()), self.k, 0.0,
+                                             vp(self.mid.data_ptr()))
+        if st == 0:
+            st = self.lib.qmv_moe_down_reduce(stream, 2, ctypes.byref(d), vp(self.mid.data_ptr()),
+                                              self.T, vp(self.ids.data_ptr()),
+                                              vp(self.route.data_ptr()), self.k,
+                                              vp(self.y.data_ptr()))
+        if st != 0:
+            raise RuntimeError(self.lib.qmv_last_error().decode())
+
+    def free(self):
+        self.keep = self.wts = None
+
+
 def time_chain(bmv, steps: int = 100) -> dict:
     """Config 2: a dependent chain of 100 calls (8-bit affine g64, K=N=2560,
     bf16), each output the next input; same weights every call (warm), as in
@@ -590,6 +653,16 @@ def main() -> int:
             r.free()
             cr["case"] = (f"config5 gather {fmt} {proj}: 64 experts, {m.lhs.size} slots, "
                           f"{len(m.distinct_experts())} distinct, K={m.K} N={m.N} bf16")
+            cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
+            cases.append(cr)
+            print(f"[bench] {cr['case']}: {json.dumps(cr)}", file=sys.stderr, flush=True)
+        for fmt in ("mxfp4", "affine"):
+            r = MoeBlockRunner(bmv, fmt)
+            cr = time_case(r, max(100, args.steps // 10), 10)
+            cr["case"] = (f"fused MoE block {fmt} (config 5: 64 experts, hidden 4096, ffn 1536, "
+                          f"16 tokens x top-8, {r.distinct} distinct): gate/up+SwiGLU, down sum; "
+                          "2 launches")
+            r.free()
             cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
             cases.append(cr)
             print(f"[bench] {cr['case']}: {json.dumps(cr)}", file=sys.stderr, flush=True)
