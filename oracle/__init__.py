@@ -28,6 +28,8 @@ passage it follows):
   of each slot picks the weight matrix; no per-expert host dispatch).
 * "ferrum-kernels - primitives.rs" tests: an out-of-range index yields a row
   of zeros rather than a fault.
+* The other Track-1 block-scaled formats (``blockfmt.py``): the audit's
+  element x block x scale matrix (E5M2 constants from its kv_cache row).
 * The fused routed-MoE decode block (``moe.py``): the ds4 moe.metal SwiGLU
   activation and per-token down-projection sum, and the audit's two-dispatch
   description of the block.
@@ -62,6 +64,16 @@ from .quantize import (
     quantize_affine,
     quantize_mx,
     quantize_nvfp4,
+)
+from .blockfmt import (
+    e5m2_value,
+    int_value,
+    element_value,
+    scale_value,
+    implicit_factor,
+    dequant_block,
+    FORMATS as BLOCK_FORMATS,
+    ELEMENTS as BLOCK_ELEMENTS,
 )
 from .moe import (
     silu,

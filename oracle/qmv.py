@@ -76,6 +76,9 @@ def dequant(fmt: str, K: int, w, scales, biases=None, bits: int = 4, group: int 
         return dequant_nvfp4(w, scales, K, global_scale)
     if fmt == "mxfp8":
         return dequant_mxfp8(w, scales, K)
+    from .blockfmt import FORMATS, dequant_block
+    if fmt in FORMATS:
+        return dequant_block(fmt, w, scales, K)
     raise ValueError(f"unknown format {fmt!r}")
 
 
