@@ -22,7 +22,33 @@ HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "qmv.h")
 
 QMV_F32, QMV_F16, QMV_BF16 = 0, 1, 2
 QMV_AFFINE, QMV_MXFP4, QMV_NVFP4, QMV_MXFP8 = 0, 1, 2, 3
+QMV_SB_E8M0, QMV_SB_F32, QMV_SB_F16 = 4, 5, 6
+QMV_EL_E2M1, QMV_EL_E4M3, QMV_EL_E5M2, QMV_EL_INT = 1, 2, 3, 10
 FORMATS = {"affine": QMV_AFFINE, "mxfp4": QMV_MXFP4, "nvfp4": QMV_NVFP4, "mxfp8": QMV_MXFP8}
+
+# The symmetric block-scaled formats by their names in the Track-1 table:
+# name -> (format family, element code, block), as include/qmv.h lists them.
+BLOCK_FORMATS = {
+    "mxfp8_e5m2": (QMV_SB_E8M0, QMV_EL_E5M2, 32),
+    "nvfp8": (QMV_SB_F32, QMV_EL_E4M3, 16),
+    "fp4": (QMV_SB_F32, QMV_EL_E2M1, 32),
+    "fp8_e4m3": (QMV_SB_F32, QMV_EL_E4M3, 32),
+    "fp8_e5m2": (QMV_SB_F32, QMV_EL_E5M2, 32),
+    "nvfp8_f16": (QMV_SB_F16, QMV_EL_E4M3, 16),
+    "fp4_f16": (QMV_SB_F16, QMV_EL_E2M1, 32),
+    "fp8_e4m3_f16": (QMV_SB_F16, QMV_EL_E4M3, 32),
+    "fp8_e5m2_f16": (QMV_SB_F16, QMV_EL_E5M2, 32),
+}
+for _n in (2, 3, 4, 5, 6, 8):
+    BLOCK_FORMATS[f"int{_n}"] = (QMV_SB_F32, QMV_EL_INT + _n, 64)
+    BLOCK_FORMATS[f"int{_n}_f16"] = (QMV_SB_F16, QMV_EL_INT + _n, 64)
+    BLOCK_FORMATS[f"mxint{_n}"] = (QMV_SB_E8M0, QMV_EL_INT + _n, 32)
+
+
+def block_format_bits(name: str) -> int:
+    """Code width of a block-scaled format's element."""
+    el = BLOCK_FORMATS[name][1]
+    return 4 if el == QMV_EL_E2M1 else (8 if el <= QMV_EL_E5M2 else el - QMV_EL_INT)
 STATUS = {0: "QMV_OK", 1: "QMV_ERR_INVALID_ARGUMENT", 2: "QMV_ERR_UNSUPPORTED",
           3: "QMV_ERR_MISALIGNED", 4: "QMV_ERR_HIP"}
 
@@ -65,6 +91,7 @@ def load() -> ctypes.CDLL:
         "qmv_fp_mxfp4": [vp, i32, i64, i64, i64, vp, vp, vp, vp],
         "qmv_fp_nvfp4": [vp, i32, i64, i64, i64, vp, vp, vp, vp, vp],
         "qmv_fp_mxfp8": [vp, i32, i64, i64, i64, vp, vp, vp, vp],
+        "qmv_fp_block": [vp, i32, i32, i32, i32, i64, i64, i64, vp, vp, vp, vp],
         "gather_qmv": [vp, i32, ctypes.POINTER(QmvWeights), vp, i64, vp, vp, i64, vp],
         "qmv_pack_codes": [vp, i64, i64, i32, vp],
         "qmv_unpack_codes": [vp, i64, i64, i32, vp],
@@ -218,15 +245,34 @@ def qmv_fp_mxfp8(x, w, scales, y=None):
     return y
 
 
+def qmv_fp_block(x, w, scales, fmt: str, y=None):
+    """y[B, N] = x . dequant(W)^T for a symmetric block-scaled format named in
+    BLOCK_FORMATS; scales are uint8 (E8M0), float32 or float16 by family."""
+    torch = _torch()
+    code, el, block = BLOCK_FORMATS[fmt]
+    _dev(w, "w", torch.uint8)
+    want = {QMV_SB_E8M0: torch.uint8, QMV_SB_F32: torch.float32, QMV_SB_F16: torch.float16}[code]
+    _dev(scales, "scales", want)
+    x, y = _xy(x, w.shape[0], y)
+    _check(load().qmv_fp_block(_stream(x.device), _dtype_code(x), code, el, block, x.shape[0],
+                               x.shape[1], w.shape[0], _ptr(x), _ptr(w), _ptr(scales), _ptr(y)))
+    return y
+
+
 def make_weights(fmt: str, w, scales, biases=None, *, K: int, bits: int = 4,
                  group_size: int = 32, global_scale=None) -> QmvWeights:
     """qmv_weights_t for expert-stacked (or single, 2-D) weights. The tensors
-    must stay alive while the struct is in use."""
+    must stay alive while the struct is in use. A block-scaled format name
+    (BLOCK_FORMATS) fixes the format, element and block itself."""
     torch = _torch()
     _dev(w, "w", torch.uint8)
     n_exp = 1 if w.dim() == 2 else w.shape[0]
     N = w.shape[-2]
-    return QmvWeights(FORMATS[fmt], bits, group_size, n_exp, N, K,
+    if fmt in BLOCK_FORMATS:
+        code, bits, group_size = BLOCK_FORMATS[fmt]
+    else:
+        code = FORMATS[fmt]
+    return QmvWeights(code, bits, group_size, n_exp, N, K,
                       w.data_ptr() if w.numel() else None,
                       scales.data_ptr() if scales is not None and scales.numel() else None,
                       biases.data_ptr() if biases is not None and biases.numel() else None,

@@ -39,7 +39,7 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 def _jobs() -> list[tuple[list[str], str]]:
     jobs = []
     for dt in (0, 1, 2):
-        for fam in (0, 1):
+        for fam in (0, 1, 2, 3, 4):
             obj = os.path.join(BUILD, f"qmv_inst_{dt}_{fam}.o")
             jobs.append(([HIPCC, *HIP_FLAGS, f"-DQMV_DT={dt}", f"-DQMV_FAM={fam}", "-c",
                           os.path.join(CSRC, "qmv_inst.hip"), "-o", obj], obj))

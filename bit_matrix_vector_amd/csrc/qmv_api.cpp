@@ -58,6 +58,11 @@ qmv_status_t check_common(const char* fn, int dtype, int64_t B, int64_t K, int64
     return QMV_OK;
 }
 
+// Bytes of one scale element of a block-scaled format.
+int scale_bytes(int format) {
+    return format == QMV_NVFP4 || format == QMV_SB_F16 ? 2 : (format == QMV_SB_F32 ? 4 : 1);
+}
+
 qmv_status_t check_ptr(const char* fn, const char* name, const void* p, bool needed,
                        uintptr_t align) {
     if (!needed) return QMV_OK;
@@ -102,6 +107,34 @@ qmv_status_t format_geometry(const char* fn, int format, int bits, int group, in
         case QMV_MXFP8:
             lp.bits = 8; lp.group = 32; lp.row_bytes = K; lp.sc_per_row = K / 32;
             return QMV_OK;
+        case QMV_SB_E8M0:
+        case QMV_SB_F32:
+        case QMV_SB_F16: {
+            // `bits` is the element code, `group` the block (the format table
+            // of qmv_fp_block)
+            const int el = bits;
+            const bool is_int = el >= QMV_EL_INT + 2 && el <= QMV_EL_INT + 8 &&
+                                valid_bits(el - QMV_EL_INT);
+            const bool is_fp = el == QMV_EL_E2M1 || el == QMV_EL_E4M3 || el == QMV_EL_E5M2;
+            bool ok;
+            if (format == QMV_SB_E8M0)
+                ok = group == 32 && (is_int || el == QMV_EL_E5M2);
+            else
+                ok = (group == 16 && el == QMV_EL_E4M3) || (group == 32 && is_fp) ||
+                     (group == 64 && is_int);
+            if (!ok)
+                return fail(QMV_ERR_UNSUPPORTED,
+                            "%s: element %d with block %d is not a format of family %d", fn, el,
+                            group, format);
+            if (K % group)
+                return fail(QMV_ERR_INVALID_ARGUMENT, "%s: K=%lld not a multiple of block %d",
+                            fn, (long long)K, group);
+            lp.bits = el;
+            lp.group = group;
+            lp.row_bytes = K * qmv::element_bits(el) / 8;
+            lp.sc_per_row = K / group;
+            return QMV_OK;
+        }
         default:
             return fail(QMV_ERR_INVALID_ARGUMENT, "%s: unknown format %d", fn, format);
     }
@@ -124,7 +157,7 @@ qmv_status_t run_qmv(const char* fn, void* stream, int dtype, int format, int bi
         QMV_TRY(check_ptr(fn, "scales", scales, has_k, tb));
         QMV_TRY(check_ptr(fn, "biases", biases, has_k, tb));
     } else {
-        QMV_TRY(check_ptr(fn, "scales", scales, has_k, format == QMV_NVFP4 ? 2 : 1));
+        QMV_TRY(check_ptr(fn, "scales", scales, has_k, scale_bytes(format)));
     }
     QMV_TRY(check_ptr(fn, "global_scale", gscale, gscale != nullptr, 4));
     if (x && y && has_k) {
@@ -150,6 +183,9 @@ qmv_status_t check_weights(const char* fn, const char* what, int dtype, const qm
     QMV_TRY(check_common(fn, dtype, 1, wt->K, wt->N, 1));
     lp.dtype = dtype;
     QMV_TRY(format_geometry(fn, wt->format, wt->bits, wt->group_size, wt->K, lp));
+    if (wt->format >= QMV_SB_E8M0)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: the MoE block takes the affine, MXFP4, NVFP4 and "
+                    "MXFP8 formats", fn);
     const int tb = dtype_bytes(dtype);
     const bool has_w = wt->K > 0 && wt->N > 0 && wt->n_experts > 0;
     QMV_TRY(check_ptr(fn, "w", wt->w, has_w, 16));
@@ -157,7 +193,7 @@ qmv_status_t check_weights(const char* fn, const char* what, int dtype, const qm
         QMV_TRY(check_ptr(fn, "scales", wt->scales, has_w, tb));
         QMV_TRY(check_ptr(fn, "biases", wt->biases, has_w, tb));
     } else {
-        QMV_TRY(check_ptr(fn, "scales", wt->scales, has_w, wt->format == QMV_NVFP4 ? 2 : 1));
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, has_w, scale_bytes(wt->format)));
     }
     QMV_TRY(check_ptr(fn, "global_scale", wt->global_scale, wt->global_scale != nullptr, 4));
     lp.K = wt->K; lp.N = wt->N; lp.n_experts = wt->n_experts;
@@ -311,6 +347,16 @@ qmv_status_t qmv_fp_nvfp4(void* stream, int dtype, int64_t B, int64_t K, int64_t
                    nullptr, global_scale, y);
 }
 
+qmv_status_t qmv_fp_block(void* stream, int dtype, int format, int element, int block,
+                          int64_t B, int64_t K, int64_t N, const void* x, const uint8_t* w,
+                          const void* scales, void* y) {
+    if (format < QMV_SB_E8M0 || format > QMV_SB_F16)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "qmv_fp_block: format %d is not a block-scaled "
+                    "family (QMV_SB_E8M0 / QMV_SB_F32 / QMV_SB_F16)", format);
+    return run_qmv("qmv_fp_block", stream, dtype, format, element, block, B, K, N, x, w, scales,
+                   nullptr, nullptr, y);
+}
+
 qmv_status_t qmv_fp_mxfp8(void* stream, int dtype, int64_t B, int64_t K, int64_t N,
                           const void* x, const uint8_t* w, const uint8_t* scales, void* y) {
     return run_qmv("qmv_fp_mxfp8", stream, dtype, QMV_MXFP8, 8, 32, B, K, N, x, w, scales,
@@ -330,6 +376,9 @@ qmv_status_t gather_qmv(void* stream, int dtype, const qmv_weights_t* wt, const 
     qmv::LaunchParams lp{};
     lp.dtype = dtype;
     QMV_TRY(format_geometry(fn, wt->format, wt->bits, wt->group_size, wt->K, lp));
+    if (wt->format >= QMV_SB_E8M0)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: the gather takes the affine, MXFP4, NVFP4 and "
+                    "MXFP8 formats", fn);
     if (n_slots == 0 || wt->N == 0) return QMV_OK;
     const int tb = dtype_bytes(dtype);
     const bool has_w = wt->K > 0 && wt->n_experts > 0;
@@ -342,7 +391,7 @@ qmv_status_t gather_qmv(void* stream, int dtype, const qmv_weights_t* wt, const 
         QMV_TRY(check_ptr(fn, "scales", wt->scales, has_w, tb));
         QMV_TRY(check_ptr(fn, "biases", wt->biases, has_w, tb));
     } else {
-        QMV_TRY(check_ptr(fn, "scales", wt->scales, has_w, wt->format == QMV_NVFP4 ? 2 : 1));
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, has_w, scale_bytes(wt->format)));
     }
     QMV_TRY(check_ptr(fn, "global_scale", wt->global_scale, wt->global_scale != nullptr, 4));
     lp.B = 1; lp.K = wt->K; lp.N = wt->N;
@@ -500,7 +549,7 @@ qmv_status_t qmv_dequant_device(void* stream, int dtype, const qmv_weights_t* wt
         QMV_TRY(check_ptr(fn, "scales", wt->scales, true, tb));
         QMV_TRY(check_ptr(fn, "biases", wt->biases, true, tb));
     } else {
-        QMV_TRY(check_ptr(fn, "scales", wt->scales, true, wt->format == QMV_NVFP4 ? 2 : 1));
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, true, scale_bytes(wt->format)));
     }
     QMV_TRY(check_ptr(fn, "global_scale", wt->global_scale, wt->global_scale != nullptr, 4));
     lp.B = 1; lp.K = wt->K; lp.N = wt->N;

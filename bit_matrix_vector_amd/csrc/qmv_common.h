@@ -7,7 +7,18 @@
 namespace qmv {
 
 enum Dtype { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
-enum Format { FMT_AFFINE = 0, FMT_MXFP4 = 1, FMT_NVFP4 = 2, FMT_MXFP8 = 3 };
+enum Format {
+    FMT_AFFINE = 0, FMT_MXFP4 = 1, FMT_NVFP4 = 2, FMT_MXFP8 = 3,
+    // symmetric block-scaled family, by scale storage; the element is the
+    // "bits" field (an Element code) and the block length the "group" field
+    FMT_SB_E8M0 = 4, FMT_SB_F32 = 5, FMT_SB_F16 = 6
+};
+// Element codes of the symmetric block-scaled family: micro-floats, or
+// two's-complement integers of width n (code 10 + n).
+enum Element { EL_E2M1 = 1, EL_E4M3 = 2, EL_E5M2 = 3, EL_INT = 10 };
+constexpr int element_bits(int el) {
+    return el == EL_E2M1 ? 4 : (el <= EL_E5M2 ? 8 : el - EL_INT);
+}
 
 // Everything one launch needs. Filled and validated by the host API.
 struct LaunchParams {

@@ -194,6 +194,7 @@ template <int FMT, int BITS> struct Fmt;
 template <int BITS> struct Fmt<FMT_AFFINE, BITS> {
     static constexpr int kWords = BITS;
     static constexpr bool kNeedsSumX = true;
+    static constexpr bool kTwoScales = false;
     struct Raw { uint32_t s, b; };
     struct Scale { float s, b; };
     template <int DT>
@@ -296,6 +297,7 @@ __device__ inline void decode_e2m1_8(const uint32_t word, float (&q)[8]) {
 template <> struct Fmt<FMT_MXFP4, 4> {
     static constexpr int kWords = 4;
     static constexpr bool kNeedsSumX = false;
+    static constexpr bool kTwoScales = false;
     struct Raw { uint32_t e; };
     struct Scale { float s; };
     template <int DT>
@@ -332,6 +334,7 @@ template <> struct Fmt<FMT_MXFP4, 4> {
 template <> struct Fmt<FMT_NVFP4, 4> {
     static constexpr int kWords = 4;
     static constexpr bool kNeedsSumX = false;
+    static constexpr bool kTwoScales = true;   // one scale per 16 codes
     struct Raw { uint32_t e; };      // two E4M3 bytes: blocks of codes 0..15, 16..31
     struct Scale { float lo, hi; };
     template <int DT>
@@ -372,6 +375,7 @@ template <> struct Fmt<FMT_NVFP4, 4> {
 template <> struct Fmt<FMT_MXFP8, 8> {
     static constexpr int kWords = 8;
     static constexpr bool kNeedsSumX = false;
+    static constexpr bool kTwoScales = false;
     struct Raw { uint32_t e; };
     struct Scale { float s; };
     template <int DT>
@@ -452,8 +456,139 @@ __device__ inline float group_sum(float v, int lpr) {
 // Which instantiations take the packed 16-bit path: 16-bit activations with
 // block-scaled formats or 4-bit affine codes. kPerm: x pairs in LDS are
 // (x[k], x[k+4]) instead of (x[2k], x[2k+1]).
+// ---------------------------------------------------------------------------
+// Symmetric block-scaled family (the rest of the Track-1 format matrix):
+// element code x block scale, no zero point. EL is the element (E2M1, E4M3,
+// E5M2 or a two's-complement int of width n); FMT fixes the scale storage
+// (E8M0 byte, FP32 or FP16). The block (16, 32 or 64 codes along K) is a
+// run-time value carried in glog2 = log2(block / 32) in {-1, 0, 1}: every unit
+// gets two scales, one per half (equal for blocks of 32 and 64), so one code
+// path serves all three. Integer elements under an E8M0 scale (mxint) read as
+// fixed point with one integer bit: code * 2^-(n-2).
+// ---------------------------------------------------------------------------
+template <int FMT, int EL> struct SbFmt {
+    static constexpr int kBits = element_bits(EL);
+    static constexpr bool kInt = EL > EL_E5M2;
+    static constexpr int kWords = kBits;
+    static constexpr bool kNeedsSumX = false;
+    static constexpr bool kTwoScales = true;
+    static constexpr int kEB = FMT == FMT_SB_E8M0 ? 1 : (FMT == FMT_SB_F32 ? 4 : 2);
+    struct Raw { uint32_t lo, hi; };
+    struct Scale { float lo, hi; };
+    __host__ __device__ static inline int64_t elem_lo(int64_t u, int gl) {
+        return gl < 0 ? 2 * u : u >> gl;
+    }
+    __host__ __device__ static inline int64_t elem_hi(int64_t u, int gl) {
+        return gl < 0 ? 2 * u + 1 : u >> gl;
+    }
+    __device__ static inline uint32_t read_elem(const uint8_t* p) {
+        if constexpr (kEB == 1) return *p;
+        else if constexpr (kEB == 2) return *reinterpret_cast<const uint16_t*>(p);
+        else return *reinterpret_cast<const uint32_t*>(p);
+    }
+    template <int DT>
+    __device__ static inline Raw load_raw(const void* sc, const void*, int64_t row,
+                                          int64_t sc_per_row, int64_t u, int gl) {
+        const uint8_t* b = static_cast<const uint8_t*>(sc) + row * sc_per_row * kEB;
+        return Raw{read_elem(b + elem_lo(u, gl) * kEB), read_elem(b + elem_hi(u, gl) * kEB)};
+    }
+    template <int DT>
+    __device__ static inline Raw global_raw(const uint8_t* sc, const uint8_t*, uint32_t row_off,
+                                            int u, int gl) {
+        return Raw{read_elem(sc + (row_off + (uint32_t)elem_lo(u, gl) * kEB)),
+                   read_elem(sc + (row_off + (uint32_t)elem_hi(u, gl) * kEB))};
+    }
+    __device__ static inline float scale_of(uint32_t r) {
+        if constexpr (FMT == FMT_SB_E8M0) {
+            const float s = e8m0_to_f32(r);
+            if constexpr (kInt) return s * __uint_as_float((uint32_t)(127 - (kBits - 2)) << 23);
+            else return s;
+        } else if constexpr (FMT == FMT_SB_F32) {
+            return __uint_as_float(r);
+        } else {
+            return (float)__builtin_bit_cast(_Float16, (uint16_t)r);
+        }
+    }
+    template <int DT>
+    __device__ static inline Scale decode(const Raw& r) {
+        return Scale{scale_of(r.lo), scale_of(r.hi)};
+    }
+    static constexpr int kArrays = 1;
+    template <int DT> __host__ __device__ static constexpr int elem_bytes() { return kEB; }
+    __host__ __device__ static inline int64_t elem_of_unit(int64_t u, int gl) {
+        return gl < 0 ? 2 * u : u >> gl;
+    }
+    template <int DT>
+    __device__ static inline Raw lds_raw(const uint8_t* row, int, int ul, int gl) {
+        return Raw{read_elem(row + elem_lo(ul, gl) * kEB), read_elem(row + elem_hi(ul, gl) * kEB)};
+    }
+    template <int SC>
+    __device__ static inline void decode8(const uint32_t (&d)[kWords], float (&q)[8]) {
+        if constexpr (EL == EL_E2M1) {
+            decode_e2m1_8(d[SC], q);
+        } else if constexpr (EL == EL_E4M3 || EL == EL_E5M2) {
+            f32x2 a, b, c, e;
+            if constexpr (EL == EL_E4M3) {
+                a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d[2 * SC], 1.0f, false);
+                b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d[2 * SC], 1.0f, true);
+                c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d[2 * SC + 1], 1.0f, false);
+                e = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(d[2 * SC + 1], 1.0f, true);
+            } else {
+                a = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(d[2 * SC], 1.0f, false);
+                b = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(d[2 * SC], 1.0f, true);
+                c = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(d[2 * SC + 1], 1.0f, false);
+                e = __builtin_amdgcn_cvt_scalef32_pk_f32_bf8(d[2 * SC + 1], 1.0f, true);
+            }
+            q[0] = a.x; q[1] = a.y; q[2] = b.x; q[3] = b.y;
+            q[4] = c.x; q[5] = c.y; q[6] = e.x; q[7] = e.y;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int32_t v = (int32_t)(affine_code<kBits>(d, SC * 8 + j) << (32 - kBits));
+                q[j] = (float)(v >> (32 - kBits));
+            }
+        }
+    }
+    // packed 16-bit pairs of the float elements (every E2M1 / E4M3 / E5M2 value
+    // is exact in bf16 and f16)
+    template <int SC, int DT>
+    __device__ static inline void pairs(const uint32_t (&d)[kWords], uint32_t (&wp)[4]) {
+        if constexpr (EL == EL_E2M1) {
+            e2m1_pairs<DT>(d[SC], wp);
+        } else {
+            static_for<0, 4>([&](auto k_c) {
+                constexpr int k = decltype(k_c)::value;
+                const uint32_t w = d[2 * SC + (k >> 1)];
+                constexpr bool hi = (k & 1) != 0;
+                if constexpr (EL == EL_E4M3) {
+                    if constexpr (DT == DT_BF16)
+                        wp[k] = __builtin_bit_cast(
+                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, hi));
+                    else
+                        wp[k] = __builtin_bit_cast(
+                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, hi));
+                } else {
+                    if constexpr (DT == DT_BF16)
+                        wp[k] = __builtin_bit_cast(
+                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, hi));
+                    else
+                        wp[k] = __builtin_bit_cast(
+                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, hi));
+                }
+            });
+        }
+    }
+    __device__ static inline float pair_code(float v) { return v; }
+};
+template <int EL> struct Fmt<FMT_SB_E8M0, EL> : SbFmt<FMT_SB_E8M0, EL> {};
+template <int EL> struct Fmt<FMT_SB_F32, EL> : SbFmt<FMT_SB_F32, EL> {};
+template <int EL> struct Fmt<FMT_SB_F16, EL> : SbFmt<FMT_SB_F16, EL> {};
+
 template <int FMT, int BITS, int DT> struct Packed {
-    static constexpr bool kOn = DT != DT_F32 && (FMT != FMT_AFFINE || BITS == 4);
+    // 16-bit activations take the packed pair path for the float elements and
+    // 4-bit affine codes; f32 activations and the other integers use fp32 FMAs
+    static constexpr bool kOn =
+        DT != DT_F32 && (FMT == FMT_AFFINE ? BITS == 4 : (FMT <= FMT_MXFP8 || BITS <= EL_E5M2));
     static constexpr bool kPerm = kOn && FMT == FMT_AFFINE;
 };
 

@@ -4,6 +4,13 @@
 
 namespace qmv {
 
+#define QMV_DECL_SB(dt, fam)                                                            \
+    int launch_qmv_part_##dt##_##fam(const LaunchParams&, void*);                       \
+    int launch_dequant_part_##dt##_##fam(const LaunchParams&, float*, void*);
+QMV_DECL_SB(0, 2) QMV_DECL_SB(0, 3) QMV_DECL_SB(0, 4) QMV_DECL_SB(1, 2) QMV_DECL_SB(1, 3)
+QMV_DECL_SB(1, 4) QMV_DECL_SB(2, 2) QMV_DECL_SB(2, 3) QMV_DECL_SB(2, 4)
+#undef QMV_DECL_SB
+
 #define QMV_DECL_PART(dt, fam)                                                          \
     int launch_qmv_part_##dt##_##fam(const LaunchParams&, void*);                       \
     int launch_gather_part_##dt##_##fam(const LaunchParams&, void*);                    \
@@ -28,19 +35,41 @@ QMV_DECL_PART(1, 1) QMV_DECL_PART(2, 0) QMV_DECL_PART(2, 1)
         }                                                                               \
     } while (0)
 
+// The symmetric block-scaled family (QMV and dequant only): one slice per
+// (dtype, scale storage).
+#define QMV_ROUTE_SB(name, ...)                                                         \
+    do {                                                                                \
+        switch (p.dtype * 3 + (p.format - FMT_SB_E8M0)) {                               \
+            case 0: return name##_0_2(__VA_ARGS__);                                     \
+            case 1: return name##_0_3(__VA_ARGS__);                                     \
+            case 2: return name##_0_4(__VA_ARGS__);                                     \
+            case 3: return name##_1_2(__VA_ARGS__);                                     \
+            case 4: return name##_1_3(__VA_ARGS__);                                     \
+            case 5: return name##_1_4(__VA_ARGS__);                                     \
+            case 6: return name##_2_2(__VA_ARGS__);                                     \
+            case 7: return name##_2_3(__VA_ARGS__);                                     \
+            case 8: return name##_2_4(__VA_ARGS__);                                     \
+            default: return (int)hipErrorInvalidValue;                                  \
+        }                                                                               \
+    } while (0)
+
 int launch_qmv(const LaunchParams& p, void* stream) {
+    if (p.format >= FMT_SB_E8M0) QMV_ROUTE_SB(launch_qmv_part, p, stream);
     QMV_ROUTE(launch_qmv_part, p, stream);
 }
 
 int launch_gather(const LaunchParams& p, void* stream) {
+    if (p.format >= FMT_SB_E8M0) return (int)hipErrorInvalidValue;
     QMV_ROUTE(launch_gather_part, p, stream);
 }
 
 int launch_moe_gate_up(const LaunchParams& p, const MoeArgs& m, void* stream) {
+    if (p.format >= FMT_SB_E8M0) return (int)hipErrorInvalidValue;
     QMV_ROUTE(launch_moe_gate_up_part, p, m, stream);
 }
 
 int launch_moe_down(const LaunchParams& p, const MoeArgs& m, void* stream) {
+    if (p.format >= FMT_SB_E8M0) return (int)hipErrorInvalidValue;
     QMV_ROUTE(launch_moe_down_part, p, m, stream);
 }
 
@@ -63,6 +92,7 @@ int launch_zero_fill(void* p, int64_t bytes, void* stream) {
 }
 
 int launch_dequant_device(const LaunchParams& p, float* out, void* stream) {
+    if (p.format >= FMT_SB_E8M0) QMV_ROUTE_SB(launch_dequant_part, p, out, stream);
     QMV_ROUTE(launch_dequant_part, p, out, stream);
 }
 

@@ -1,6 +1,8 @@
 // One slice of the kernel instantiations: the dtype QMV_DT (0 f32, 1 f16,
-// 2 bf16) and the format family QMV_FAM (0 affine, 1 block-scaled). The
-// build compiles this file once per (dtype, family) pair, in parallel.
+// 2 bf16) and the format family QMV_FAM (0 affine; 1 MXFP4 / NVFP4 / MXFP8;
+// 2, 3, 4 the symmetric block-scaled family with E8M0, FP32 and FP16 scales,
+// QMV and dequant only). The build compiles this file once per (dtype,
+// family) pair, in parallel.
 #include "qmv_kernels.cuh"
 
 #ifndef QMV_DT
@@ -29,11 +31,29 @@ int dispatch_part(const LaunchParams& p, A... a) {
         case 8: return L<QMV_DT, FMT_AFFINE, 8>::run(p, a...);
         default: return (int)hipErrorInvalidValue;
     }
-#else
+#elif QMV_FAM == 1
     switch (p.format) {
         case FMT_MXFP4: return L<QMV_DT, FMT_MXFP4, 4>::run(p, a...);
         case FMT_NVFP4: return L<QMV_DT, FMT_NVFP4, 4>::run(p, a...);
         case FMT_MXFP8: return L<QMV_DT, FMT_MXFP8, 8>::run(p, a...);
+        default: return (int)hipErrorInvalidValue;
+    }
+#else
+    constexpr int F = FMT_SB_E8M0 + (QMV_FAM - 2);
+    if (p.format != F) return (int)hipErrorInvalidValue;
+    switch (p.bits) {   // the element code
+#if QMV_FAM != 2
+        // (E2M1 and E4M3 under E8M0 are MXFP4 and MXFP8)
+        case EL_E2M1: return L<QMV_DT, F, EL_E2M1>::run(p, a...);
+        case EL_E4M3: return L<QMV_DT, F, EL_E4M3>::run(p, a...);
+#endif
+        case EL_E5M2: return L<QMV_DT, F, EL_E5M2>::run(p, a...);
+        case EL_INT + 2: return L<QMV_DT, F, EL_INT + 2>::run(p, a...);
+        case EL_INT + 3: return L<QMV_DT, F, EL_INT + 3>::run(p, a...);
+        case EL_INT + 4: return L<QMV_DT, F, EL_INT + 4>::run(p, a...);
+        case EL_INT + 5: return L<QMV_DT, F, EL_INT + 5>::run(p, a...);
+        case EL_INT + 6: return L<QMV_DT, F, EL_INT + 6>::run(p, a...);
+        case EL_INT + 8: return L<QMV_DT, F, EL_INT + 8>::run(p, a...);
         default: return (int)hipErrorInvalidValue;
     }
 #endif
@@ -68,6 +88,7 @@ template <int DT, int FMT, int BITS> struct DequantL {
 int QMV_PART(launch_qmv_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, void* stream) {
     return dispatch_part<QmvL>(p, static_cast<hipStream_t>(stream));
 }
+#if QMV_FAM <= 1
 int QMV_PART(launch_gather_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, void* stream) {
     return dispatch_part<GatherL>(p, static_cast<hipStream_t>(stream));
 }
@@ -79,6 +100,7 @@ int QMV_PART(launch_moe_down_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, cons
                                                      void* stream) {
     return dispatch_part<MoeDownL>(p, m, static_cast<hipStream_t>(stream));
 }
+#endif
 int QMV_PART(launch_dequant_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, float* out,
                                                      void* stream) {
     return dispatch_part<DequantL>(p, out, static_cast<hipStream_t>(stream));

@@ -50,7 +50,7 @@ struct Geom {
     int lpr;        // lanes per row group (16, 32, 64)
     int lpr_log2;
     int ks;         // x slab length in elements (multiple of 32*lpr, or K)
-    int glog2;      // affine: log2(group / 32)
+    int glog2;      // scale elements per unit (scale_glog2)
     int rows_per_block;
     int sc_lds_off;  // byte offset of the staged scales in LDS
     int sc_aligned4; // scale rows can be copied in 4-byte words
@@ -164,9 +164,9 @@ __device__ inline void unit_fma(const UnitRaw<FMT, BITS, R>& u_raw,
                     for (int j = 0; j < 8; ++j) acc[i][b] = fmaf(q[j], xv[b][j], acc[i][b]);
             }
         }
-        if constexpr (FMT == FMT_NVFP4) {
+        if constexpr (F::kTwoScales) {
             if constexpr (SC == 1) {
-                // first block of 16 done: fold it with its E4M3 scale
+                // first half (codes 0..15) done: fold it with its own scale
 #pragma unroll
                 for (int i = 0; i < R; ++i)
 #pragma unroll
@@ -191,7 +191,7 @@ __device__ inline void unit_fma(const UnitRaw<FMT, BITS, R>& u_raw,
                 else
                     total[i][b] = fmaf(scl[i].s, acc[i][b],
                                        fmaf(scl[i].b, sx[b], total[i][b]));
-            } else if constexpr (FMT == FMT_NVFP4) {
+            } else if constexpr (F::kTwoScales) {
                 total[i][b] = fmaf(scl[i].hi, acc[i][b], total[i][b]);
             } else {
                 total[i][b] = fmaf(scl[i].s, acc[i][b], total[i][b]);
@@ -1056,10 +1056,10 @@ __global__ void unpack_kernel(const uint8_t* __restrict__ packed, int64_t rows, 
     for (int j = 0; j < 32; ++j) out[j] = (uint8_t)affine_code<BITS>(d, j);
 }
 
-template <int FMT, int SC, class Sc>
+template <int FMT, int BITS, int SC, class Sc>
 __device__ inline float dequant_value(const Sc& s, float q, float gmul) {
     if constexpr (FMT == FMT_AFFINE) return fmaf(s.s, q, s.b);
-    else if constexpr (FMT == FMT_NVFP4) return (q * (SC < 2 ? s.lo : s.hi)) * gmul;
+    else if constexpr (Fmt<FMT, BITS>::kTwoScales) return (q * (SC < 2 ? s.lo : s.hi)) * gmul;
     else return q * s.s;
 }
 
@@ -1102,7 +1102,7 @@ __global__ void dequant_kernel(LaunchParams p, int glog2, float* __restrict__ ou
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            o[SC * 8 + j] = dequant_value<FMT, SC>(s, q[j], gmul);
+            o[SC * 8 + j] = dequant_value<FMT, BITS, SC>(s, q[j], gmul);
         }
     });
 }
@@ -1130,6 +1130,15 @@ int ilog2(int v) {
     int r = 0;
     while ((1 << r) < v) ++r;
     return r;
+}
+
+// Scale elements per unit, as the formats' glog2 argument: affine
+// log2(group / 32); the symmetric block-scaled family log2(block / 32) (-1 for
+// blocks of 16); the fixed formats 0.
+int scale_glog2(const LaunchParams& p) {
+    if (p.format == FMT_AFFINE) return ilog2(p.group / 32);
+    if (p.format >= FMT_SB_E8M0) return p.group == 16 ? -1 : ilog2(p.group / 32);
+    return 0;
 }
 
 // Lanes per row, from K alone, so a row's sum is formed in the same order at
@@ -1166,7 +1175,7 @@ Geom make_geom(const LaunchParams& p, int nb, int budget, int rows) {
     g.tiles_per_block = 1;
     g.lpr = pick_lpr(p.K);
     g.lpr_log2 = ilog2(g.lpr);
-    g.glog2 = FMT == FMT_AFFINE ? ilog2(p.group / 32) : 0;
+    g.glog2 = scale_glog2(p);
     g.rows_per_block = kWaves * (64 / g.lpr) * rows;
     const int64_t t = DT == DT_F32 ? 4 : 2;
     const int64_t eb = F::template elem_bytes<DT>();
@@ -1335,7 +1344,7 @@ int launch_moe_down_t(const LaunchParams& p, const MoeArgs& m, hipStream_t st) {
     Geom g{};
     g.lpr = pick_lpr(p.K);
     g.lpr_log2 = ilog2(g.lpr);
-    g.glog2 = FMT == FMT_AFFINE ? ilog2(p.group / 32) : 0;
+    g.glog2 = scale_glog2(p);
     g.rows_per_block = kWaves * (64 / g.lpr) * R;
     g.out_rows = g.rows_per_block;
     g.ks = (int)p.K;
@@ -1361,7 +1370,7 @@ int launch_moe_down_t(const LaunchParams& p, const MoeArgs& m, hipStream_t st) {
 template <int DT, int FMT, int BITS>
 int launch_dequant_t(const LaunchParams& p, float* out, hipStream_t st) {
     const int64_t n = p.N * (p.K >> 5);
-    const int glog2 = p.format == FMT_AFFINE ? ilog2(p.group / 32) : 0;
+    const int glog2 = scale_glog2(p);
     hipLaunchKernelGGL((dequant_kernel<DT, FMT, BITS>), dim3((unsigned)((n + 255) / 256)),
                        dim3(256), 0, st, p, glog2, out);
     return (int)hipGetLastError();

@@ -58,7 +58,16 @@ extern "C" {
 
 typedef enum { QMV_F32 = 0, QMV_F16 = 1, QMV_BF16 = 2 } qmv_dtype_t;
 
-typedef enum { QMV_AFFINE = 0, QMV_MXFP4 = 1, QMV_NVFP4 = 2, QMV_MXFP8 = 3 } qmv_format_t;
+typedef enum {
+    QMV_AFFINE = 0, QMV_MXFP4 = 1, QMV_NVFP4 = 2, QMV_MXFP8 = 3,
+    /* symmetric block-scaled family, by scale storage (qmv_fp_block; in
+     * qmv_weights_t: bits = the element code, group_size = the block) */
+    QMV_SB_E8M0 = 4, QMV_SB_F32 = 5, QMV_SB_F16 = 6
+} qmv_format_t;
+
+/* Elements of the symmetric block-scaled family: OCP E2M1 / E4M3 (fn) / E5M2
+ * micro-floats, or two's-complement integers of n bits (QMV_EL_INT + n). */
+typedef enum { QMV_EL_E2M1 = 1, QMV_EL_E4M3 = 2, QMV_EL_E5M2 = 3, QMV_EL_INT = 10 } qmv_element_t;
 
 typedef enum {
     QMV_OK = 0,
@@ -95,6 +104,28 @@ qmv_status_t qmv_fp_mxfp4(void* stream, int dtype, int64_t B, int64_t K, int64_t
 qmv_status_t qmv_fp_nvfp4(void* stream, int dtype, int64_t B, int64_t K, int64_t N,
                           const void* x, const uint8_t* w, const uint8_t* scales,
                           const float* global_scale, void* y);
+
+/* Symmetric block-scaled QMV: the rest of the Track-1 format matrix ("wh-iron
+ * kernel-op coverage audit", "Quantization precision coverage": element x
+ * block x scale storage, no zero point). w [N, K*bits/8] packed codes (LSB
+ * first; 8-bit codes are bytes), scales [N, K/block] of the format's storage:
+ *   format         element             block    name on the page
+ *   QMV_SB_E8M0    E5M2                32       mxfp8_e5m2
+ *   QMV_SB_E8M0    int2..int8          32       mxint2..mxint8
+ *   QMV_SB_F32     E4M3                16       nvfp8
+ *   QMV_SB_F32     E2M1 / E4M3 / E5M2  32       fp4 / fp8_e4m3 / fp8_e5m2
+ *   QMV_SB_F32     int2..int8          64       int2..int8
+ *   QMV_SB_F16     as QMV_SB_F32                the *_f16 twins
+ * Value of a code: element(code) * scale of its block; an mxint element is
+ * read as fixed point with one integer bit, code * 2^-(n-2) (OCP MXINT8's
+ * reading, which the audit extends to the other widths). E5M2 is OCP's (bias
+ * 15; exponent 31 holds infinity and NaN). Other (element, block, format)
+ * combinations are QMV_ERR_UNSUPPORTED; K % block == 0. Alignment: scales to
+ * their element (1, 4 or 2 bytes). fp32 accumulation; each unit of 32 codes
+ * folds one scale per 16-code half. */
+qmv_status_t qmv_fp_block(void* stream, int dtype, int format, int element, int block,
+                          int64_t B, int64_t K, int64_t N, const void* x, const uint8_t* w,
+                          const void* scales, void* y);
 
 /* MXFP8 (E4M3 elements) QMV.  w [N, K] uint8 (E4M3), scales [N, K/32] uint8
  * (E8M0). x [B, K], y [B, N] in dtype. */

@@ -63,6 +63,8 @@ def run_qmv(bmv, c, dev=None, y=None):
         return bmv.qmv_fp_nvfp4(dev["x"], dev["w"], dev["scales"], dev.get("gscale"), y=y)
     if c.fmt == "mxfp8":
         return bmv.qmv_fp_mxfp8(dev["x"], dev["w"], dev["scales"], y=y)
+    if c.fmt in bmv.BLOCK_FORMATS:
+        return bmv.qmv_fp_block(dev["x"], dev["w"], dev["scales"], c.fmt, y=y)
     raise ValueError(c.fmt)
 
 
@@ -72,6 +74,10 @@ def case_to_dev(c):
     if c.fmt == "affine":
         d["scales"] = to_dev(c.scales, c.dtype)
         d["biases"] = to_dev(c.biases, c.dtype)
+    elif c.scales.dtype == np.float32:
+        d["scales"] = to_dev(c.scales, "f32")
+    elif c.scales.dtype == np.float16:
+        d["scales"] = to_dev(c.scales, "f16")
     else:
         d["scales"] = to_dev(c.scales)
     if c.fmt == "nvfp4" and c.global_scale is not None:

@@ -27,7 +27,7 @@ def test_library_exports_every_header_function(lib):
             "qmv_pack_codes", "qmv_unpack_codes", "qmv_encode_e4m3",
             "qmv_unpack_codes_device", "qmv_dequant_device", "qmv_packed_row_bytes",
             "qmv_quantize_affine", "qmv_quantize_mxfp4", "qmv_quantize_mxfp8",
-            "qmv_quantize_nvfp4", "qmv_moe_gate_up_swiglu", "qmv_moe_down_reduce",
+            "qmv_quantize_nvfp4", "qmv_moe_gate_up_swiglu", "qmv_moe_down_reduce", "qmv_fp_block",
             "qmv_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -105,6 +105,24 @@ def test_device_codec_validation(lib):
     assert lib.qmv_unpack_codes_device(None, W, 4, 64, 7, V(0x90000)) == UNSUP
     wt = bmv.QmvWeights(bmv.QMV_MXFP8, 8, 32, 2, 16, 64, 0x20000, 0x30000, None, None)
     assert lib.qmv_dequant_device(None, 2, ctypes.byref(wt), V(0x90000)) == INVAL
+
+
+def test_block_format_validation(lib):
+    f = lib.qmv_fp_block
+    E8, F32, F16 = 4, 5, 6
+    assert f(None, 2, 3, 2, 32, 1, 512, 16, X, W, S, Y) == INVAL          # not the family
+    assert f(None, 2, E8, 2, 32, 1, 512, 16, X, W, S, Y) == UNSUP         # E4M3/E8M0 is mxfp8
+    assert f(None, 2, E8, 1, 32, 1, 512, 16, X, W, S, Y) == UNSUP         # E2M1/E8M0 is mxfp4
+    assert f(None, 2, F32, 2, 64, 1, 512, 16, X, W, S, Y) == UNSUP        # floats use 16 / 32
+    assert f(None, 2, F32, 14, 32, 1, 512, 16, X, W, S, Y) == UNSUP       # ints use 64 (F32)
+    assert f(None, 2, F32, 17, 64, 1, 512, 16, X, W, S, Y) == UNSUP       # int7 does not exist
+    assert f(None, 2, F32, 14, 64, 1, 544, 16, X, W, S, Y) == INVAL       # K % block
+    assert f(None, 2, F32, 14, 64, 1, 512, 16, X, W, V(0x30002), Y) == MISAL   # FP32 scales
+    assert f(None, 2, F16, 14, 64, 1, 512, 16, X, W, V(0x30001), Y) == MISAL   # FP16 scales
+    assert f(None, 2, F16, 2, 16, 1, 512, 0, X, W, S, Y) == OK            # N = 0
+    wt = bmv.QmvWeights(F32, 14, 64, 4, 16, 512, 0x20000, 0x30000, None, None)
+    assert lib.gather_qmv(None, 2, ctypes.byref(wt), X, 16, V(0x70000), V(0x80000), 8,
+                          Y) == UNSUP
 
 
 def test_moe_validation(lib):

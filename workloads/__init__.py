@@ -433,3 +433,47 @@ def moe_block_case(fmt: str, *, E: int = 64, hidden: int = 4096, ffn: int = 1536
     x = to_storage(rng.normal(0.0, 1.0, size=(tokens, hidden)), dtype)
     return MoeBlockCase(fmt, dtype, E, hidden, ffn, x, ids.astype(np.uint32), route, gate, up,
                         down, bits, group)
+
+
+# ---------------------------------------------------------------------------
+# The other Track-1 block-scaled formats (symmetric: element x block scale).
+# ---------------------------------------------------------------------------
+SB_FORMATS = {  # name -> (element, block, scale storage); as in the audit's table
+    "mxfp8_e5m2": ("e5m2", 32, "e8m0"), "nvfp8": ("e4m3", 16, "f32"),
+    "fp4": ("e2m1", 32, "f32"), "fp8_e4m3": ("e4m3", 32, "f32"),
+    "fp8_e5m2": ("e5m2", 32, "f32"), "nvfp8_f16": ("e4m3", 16, "f16"),
+    "fp4_f16": ("e2m1", 32, "f16"), "fp8_e4m3_f16": ("e4m3", 32, "f16"),
+    "fp8_e5m2_f16": ("e5m2", 32, "f16"),
+    **{f"int{n}": (f"int{n}", 64, "f32") for n in (2, 3, 4, 5, 6, 8)},
+    **{f"int{n}_f16": (f"int{n}", 64, "f16") for n in (2, 3, 4, 5, 6, 8)},
+    **{f"mxint{n}": (f"int{n}", 32, "e8m0") for n in (2, 3, 4, 5, 6, 8)},
+}
+
+# scale ranges per element, so products stay near 1: U(lo, hi) for FP32 / FP16
+# scales (E5M2's reach f16 subnormals); E8M0 bytes for the mxfp8 / mxint forms
+_SB_SCALE_RANGE = {"e2m1": (0.01, 0.1), "e4m3": (5e-4, 5e-3), "e5m2": (2e-6, 2e-5)}
+
+
+def sb_case(fmt: str, *, K: int, N: int, B: int, dtype: str = "bf16", key: str = "") -> QmvCase:
+    """A symmetric block-scaled QMV case: codes uniform over the element's
+    finite codes (E4M3 without 0x7F/0xFF, E5M2 without exponent 31), scales
+    drawn per element, x ~ N(0, 1) in T."""
+    elem, block, kind = SB_FORMATS[fmt]
+    bits = 4 if elem == "e2m1" else (8 if elem.startswith("e") else int(elem[3:]))
+    rng = rng_for(7, f"sb-{fmt}-{dtype}-{key}")
+    w = rng.integers(0, 256, size=(N, K * bits // 8), dtype=np.uint8)
+    if elem == "e4m3":
+        w[(w & 0x7F) == 0x7F] = 0x7E
+    if elem == "e5m2":
+        bad = ((w >> 2) & 0x1F) == 31
+        w[bad] = w[bad] & 0x83        # exponent 0: a subnormal
+    nb = K // block
+    if kind == "e8m0":
+        lo, hi = (114, 122) if elem == "e5m2" else (120, 130)
+        scales = rng.integers(lo, hi, size=(N, nb), dtype=np.uint8)
+    else:
+        a, b = _SB_SCALE_RANGE.get(elem, (0.005, 0.05))
+        s = rng.uniform(a, b, size=(N, nb))
+        scales = s.astype(np.float32) if kind == "f32" else s.astype(np.float16)
+    x = to_storage(rng.normal(0.0, 1.0, size=(B, K)), dtype)
+    return QmvCase(fmt, dtype, B, K, N, w, scales, x, bits=bits, group=block, key=fmt)
