@@ -70,8 +70,16 @@ class Runner:
                                            vp(self.y.data_ptr())))
             else:
                 self.args.append(common + (vp(self.y.data_ptr()),))
-        self.fn = {"affine": self.lib.qmv_affine, "mxfp4": self.lib.qmv_fp_mxfp4,
-                   "nvfp4": self.lib.qmv_fp_nvfp4, "mxfp8": self.lib.qmv_fp_mxfp8}[case.fmt]
+        if case.fmt in bmv.BLOCK_FORMATS:
+            code, el, block = bmv.BLOCK_FORMATS[case.fmt]
+            lib = self.lib
+
+            def fn(stream, dt, B, K, N, x, w, s, y):
+                return lib.qmv_fp_block(stream, dt, code, el, block, B, K, N, x, w, s, y)
+            self.fn = fn
+        else:
+            self.fn = {"affine": self.lib.qmv_affine, "mxfp4": self.lib.qmv_fp_mxfp4,
+                       "nvfp4": self.lib.qmv_fp_nvfp4, "mxfp8": self.lib.qmv_fp_mxfp8}[case.fmt]
         self.bytes = case.algorithmic_bytes()
 
     def call(self, i: int, stream) -> None:
@@ -635,7 +643,10 @@ def main() -> int:
         for name, c in (("nvfp4 B1 K4096 N14336 bf16", workloads.config3("nvfp4", 1)),
                         ("mxfp8 B1 K4096 N14336 bf16", workloads.config3("mxfp8", 1)),
                         ("affine 4b g64 B1 K4096 N4096 bf16", workloads.config4(4, 64, 1, "bf16")),
-                        ("mxfp4 B4 K4096 N14336 bf16", workloads.config3("mxfp4", 4))):
+                        ("mxfp4 B4 K4096 N14336 bf16", workloads.config3("mxfp4", 4)),
+                        *((f"{f} B1 K4096 N14336 bf16",
+                           workloads.sb_case(f, K=4096, N=14336, B=1, key="bench"))
+                          for f in ("mxfp8_e5m2", "nvfp8", "fp8_e5m2_f16", "int4", "mxint8"))):
             r = Runner(bmv, c)
             cr = time_case(r, max(200, args.steps // 4), args.warmup)
             r.free()
