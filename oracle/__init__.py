@@ -90,6 +90,8 @@ from .qmv import (
     dequant,
     qmv,
     qmv_rows,
+    qvm,
+    qvm_abs,
     gather_qmv,
     abs_dot,
 )

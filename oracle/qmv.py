@@ -143,3 +143,16 @@ def abs_dot(x, x_dtype: str, W64: np.ndarray) -> np.ndarray:
     if x64.ndim == 1:
         x64 = x64[None, :]
     return x64 @ np.abs(W64).T
+
+
+def qvm(x, x_dtype: str, W64: np.ndarray) -> np.ndarray:
+    """The transposed product y[b, k] = sum_n x[b, n] * W[n, k] in fp64, with W
+    the [N, K] dequantized matrix in the same packed layout the QMV reads
+    ("mlx 1.0.0 - quantized_nax.h", `qouter`: each row n adds x[n] times its
+    dequantized row, scale*q + bias per element). x is [B, N]."""
+    return storage_to_f64(x, x_dtype) @ np.asarray(W64, dtype=np.float64)
+
+
+def qvm_abs(x, x_dtype: str, W64: np.ndarray) -> np.ndarray:
+    """sum_n |x[b, n] * W[n, k]| (for error bounds)."""
+    return np.abs(storage_to_f64(x, x_dtype)) @ np.abs(np.asarray(W64, dtype=np.float64))
