@@ -102,6 +102,7 @@ def load() -> ctypes.CDLL:
                                    ctypes.POINTER(QmvWeights), vp, i64, vp, i64, ctypes.c_float,
                                    vp],
         "qmv_moe_down_reduce": [vp, i32, ctypes.POINTER(QmvWeights), vp, i64, vp, vp, i64, vp],
+        "qmv_qvm": [vp, i32, ctypes.POINTER(QmvWeights), i64, vp, vp, vp, ctypes.c_size_t],
         "qmv_quantize_affine": [vp, i32, i64, i64, vp, i32, i32, vp, vp, vp],
         "qmv_quantize_mxfp4": [vp, i32, i64, i64, vp, vp, vp],
         "qmv_quantize_mxfp8": [vp, i32, i64, i64, vp, vp, vp],
@@ -111,6 +112,8 @@ def load() -> ctypes.CDLL:
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = ctypes.c_int
+    lib.qmv_qvm_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.qmv_qvm_workspace_bytes.restype = ctypes.c_size_t
     lib.qmv_packed_row_bytes.argtypes = [i32, i32, i64]
     lib.qmv_packed_row_bytes.restype = i64
     lib.qmv_bench_stream_read.argtypes = [vp, vp, i64, vp, i32]
@@ -318,6 +321,29 @@ def qmv_dequant_device(weights: QmvWeights, dtype_code: int, device, out=None):
     _check(load().qmv_dequant_device(_stream(out.device), dtype_code, ctypes.byref(weights),
                                      _ptr(out)))
     return out
+
+
+# ---------------------------------------------------------------------------
+# qvm
+# ---------------------------------------------------------------------------
+
+def qmv_qvm(x, weights: QmvWeights, y=None, workspace=None):
+    """y[B, K] = x[B, N] . dequant(W)[N, K] (W one [N, K] matrix). The fp32
+    workspace is allocated here unless given (see qmv_qvm_workspace_bytes)."""
+    torch = _torch()
+    x = _dev(x, "x")
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    B = x.shape[0]
+    if y is None:
+        y = torch.empty((B, weights.K), dtype=x.dtype, device=x.device)
+    _dev(y, "y", x.dtype)
+    need = int(load().qmv_qvm_workspace_bytes(B, weights.K, weights.N))
+    if workspace is None:
+        workspace = torch.empty((max(need, 4) // 4,), dtype=torch.float32, device=x.device)
+    _check(load().qmv_qvm(_stream(x.device), _dtype_code(x), ctypes.byref(weights), B, _ptr(x),
+                          _ptr(y), _ptr(workspace), workspace.numel() * 4))
+    return y
 
 
 # ---------------------------------------------------------------------------

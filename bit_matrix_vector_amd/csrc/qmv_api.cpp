@@ -300,6 +300,57 @@ qmv_status_t qmv_moe_down_reduce(void* stream, int dtype, const qmv_weights_t* d
     return launch_status(qmv::launch_moe_down(lp, ma, stream), fn);
 }
 
+size_t qmv_qvm_workspace_bytes(int64_t B, int64_t K, int64_t N) {
+    if (B <= 0 || K <= 0 || N <= 0) return 0;
+    return (size_t)qmv::qvm_splits(K, N, nullptr) * (size_t)B * (size_t)K * sizeof(float);
+}
+
+qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* wt, int64_t B, const void* x,
+                     void* y, void* workspace, size_t workspace_bytes) {
+    const char* fn = "qmv_qvm";
+    if (wt == nullptr) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: weights struct is NULL", fn);
+    if (wt->n_experts != 1)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: n_experts must be 1", fn);
+    QMV_TRY(check_common(fn, dtype, B, wt->K, wt->N, 8));
+    qmv::LaunchParams lp{};
+    QMV_TRY(format_geometry(fn, wt->format, wt->bits, wt->group_size, wt->K, lp));
+    if (wt->format >= QMV_SB_E8M0)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: qvm takes the affine, MXFP4, NVFP4 and MXFP8 "
+                    "formats", fn);
+    if (B == 0 || wt->K == 0) return QMV_OK;
+    const int tb = dtype_bytes(dtype);
+    QMV_TRY(check_ptr(fn, "y", y, true, tb));
+    if (wt->N == 0)   // empty sums
+        return launch_status(qmv::launch_zero_fill(y, B * wt->K * tb, stream), fn);
+    QMV_TRY(check_ptr(fn, "x", x, true, tb));
+    QMV_TRY(check_ptr(fn, "w", wt->w, true, 16));
+    if (wt->format == QMV_AFFINE) {
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, true, tb));
+        QMV_TRY(check_ptr(fn, "biases", wt->biases, true, tb));
+    } else {
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, true, scale_bytes(wt->format)));
+    }
+    QMV_TRY(check_ptr(fn, "global_scale", wt->global_scale, wt->global_scale != nullptr, 4));
+    QMV_TRY(check_ptr(fn, "workspace", workspace, true, 4));
+    const size_t need = qmv_qvm_workspace_bytes(B, wt->K, wt->N);
+    if (workspace_bytes < need)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: workspace of %zu bytes, %zu needed", fn,
+                    workspace_bytes, need);
+    {
+        const uintptr_t xs = (uintptr_t)x, xe = xs + (uintptr_t)(B * wt->N * tb);
+        const uintptr_t ys = (uintptr_t)y, ye = ys + (uintptr_t)(B * wt->K * tb);
+        if (xs < ye && ys < xe) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: x and y overlap", fn);
+    }
+    qmv::QvmParams q{};
+    q.dtype = dtype; q.format = wt->format; q.bits = lp.bits; q.group = lp.group;
+    q.B = B; q.K = wt->K; q.N = wt->N; q.row_bytes = lp.row_bytes; q.sc_per_row = lp.sc_per_row;
+    q.x = x; q.w = wt->w; q.scales = wt->scales; q.biases = wt->biases;
+    q.gscale = wt->format == QMV_NVFP4 ? wt->global_scale : nullptr;
+    q.y = y; q.ws = static_cast<float*>(workspace);
+    q.splits = qmv::qvm_splits(q.K, q.N, &q.rows_per_split);
+    return launch_status(qmv::launch_qvm(q, stream), fn);
+}
+
 qmv_status_t qmv_quantize_affine(void* stream, int dtype, int64_t N, int64_t K, const void* w,
                                  int bits, int group_size, uint8_t* packed, void* scales,
                                  void* biases) {

@@ -62,6 +62,40 @@ int launch_moe_gate_up(const LaunchParams& p, const MoeArgs& m, void* stream);
 int launch_zero_fill(void* p, int64_t bytes, void* stream);   // bytes % 2 == 0
 int launch_moe_down(const LaunchParams& p, const MoeArgs& m, void* stream);
 
+// One qvm call: y[B, K] = x[B, N] . W[N, K] (W packed as for QMV). Row splits
+// write fp32 partials to ws ([splits, B, K]); a second pass adds them.
+struct QvmParams {
+    int dtype;
+    int format;
+    int bits;
+    int group;
+    int64_t B, K, N;
+    int64_t row_bytes, sc_per_row;
+    const void* x;
+    const uint8_t* w;
+    const void* scales;
+    const void* biases;
+    const float* gscale;
+    void* y;
+    float* ws;
+    int64_t rows_per_split;
+    int splits;
+};
+int launch_qvm(const QvmParams& q, void* stream);
+// Row splits of a qvm launch: about 2048 blocks over the 512-column tiles,
+// at least 4 rows each, at most 1024 splits; depends on K and N alone.
+inline int qvm_splits(int64_t K, int64_t N, int64_t* rows_per_split) {
+    const int64_t tiles = (K + 511) / 512;
+    int64_t s = tiles > 0 ? (2048 + tiles - 1) / tiles : 1;
+    const int64_t max_s = (N + 3) / 4;
+    if (s > max_s) s = max_s;
+    if (s > 1024) s = 1024;
+    if (s < 1) s = 1;
+    const int64_t rps = N > 0 ? (N + s - 1) / s : 1;
+    if (rows_per_split) *rows_per_split = rps;
+    return N > 0 ? (int)((N + rps - 1) / rps) : 1;
+}
+
 // One quantize-from-float call: w [N, K] in `dtype` to the packed format.
 struct QuantParams {
     int dtype;

@@ -73,6 +73,19 @@ int launch_moe_down(const LaunchParams& p, const MoeArgs& m, void* stream) {
     QMV_ROUTE(launch_moe_down_part, p, m, stream);
 }
 
+int launch_qvm_dt_0(const QvmParams&, void*);
+int launch_qvm_dt_1(const QvmParams&, void*);
+int launch_qvm_dt_2(const QvmParams&, void*);
+
+int launch_qvm(const QvmParams& q, void* stream) {
+    switch (q.dtype) {
+        case DT_F32: return launch_qvm_dt_0(q, stream);
+        case DT_F16: return launch_qvm_dt_1(q, stream);
+        case DT_BF16: return launch_qvm_dt_2(q, stream);
+    }
+    return (int)hipErrorInvalidValue;
+}
+
 namespace {
 __global__ void zero_fill_kernel(uint16_t* p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;

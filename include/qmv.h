@@ -50,6 +50,7 @@
 #ifndef QMV_H
 #define QMV_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -199,6 +200,21 @@ qmv_status_t qmv_unpack_codes_device(void* stream, const uint8_t* packed, int64_
  * MXFP8 e4m3*2^(e-127). Each value is the fp32 rounding of the exact one.
  * `dtype` is the storage type of the affine scales/biases (ignored otherwise). */
 qmv_status_t qmv_dequant_device(void* stream, int dtype, const qmv_weights_t* w, float* out);
+
+/* ---------------- qvm: DEVICE, asynchronous ---------------------------------
+ * The transposed product y[b, k] = sum_n x[b, n] * dequant(W)[n, k] over the
+ * same packed weights ("mlx 1.0.0 - quantized_nax.h", `qouter`: row n adds
+ * x[n] * (scale * q + bias) across its columns). w: one matrix
+ * (n_experts = 1) of the affine, MXFP4, NVFP4 or MXFP8 format, N rows of K
+ * codes; x [B, N], y [B, K] in dtype, 1 <= B <= 8 (B = 0 is a no-op).
+ * workspace: caller-owned device memory of at least
+ * qmv_qvm_workspace_bytes(B, K, N) bytes (4-byte aligned), which the call
+ * overwrites: row splits write fp32 partial sums there and a second kernel
+ * adds them in split order, so repeated calls give identical results. Calls
+ * that share a workspace must not overlap. N == 0 writes y = 0. */
+size_t qmv_qvm_workspace_bytes(int64_t B, int64_t K, int64_t N);
+qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* w, int64_t B, const void* x,
+                     void* y, void* workspace, size_t workspace_bytes);
 
 /* ---------------- fused routed-MoE decode block: DEVICE, asynchronous -------
  * The decode step of a routed mixture-of-experts FFN in two calls

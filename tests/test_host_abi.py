@@ -28,6 +28,7 @@ def test_library_exports_every_header_function(lib):
             "qmv_unpack_codes_device", "qmv_dequant_device", "qmv_packed_row_bytes",
             "qmv_quantize_affine", "qmv_quantize_mxfp4", "qmv_quantize_mxfp8",
             "qmv_quantize_nvfp4", "qmv_moe_gate_up_swiglu", "qmv_moe_down_reduce", "qmv_fp_block",
+            "qmv_qvm", "qmv_qvm_workspace_bytes",
             "qmv_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -105,6 +106,23 @@ def test_device_codec_validation(lib):
     assert lib.qmv_unpack_codes_device(None, W, 4, 64, 7, V(0x90000)) == UNSUP
     wt = bmv.QmvWeights(bmv.QMV_MXFP8, 8, 32, 2, 16, 64, 0x20000, 0x30000, None, None)
     assert lib.qmv_dequant_device(None, 2, ctypes.byref(wt), V(0x90000)) == INVAL
+
+
+def test_qvm_validation(lib):
+    ws = V(0xA0000)
+    wt = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 1, 300, 1024, 0x20000, 0x30000, None, None)
+    need = lib.qmv_qvm_workspace_bytes(2, 1024, 300)
+    assert need > 0 and need % 4 == 0
+    assert lib.qmv_qvm(None, 2, ctypes.byref(wt), 2, X, Y, ws, need - 4) == INVAL
+    assert "workspace" in lib.qmv_last_error().decode()
+    assert lib.qmv_qvm(None, 2, ctypes.byref(wt), 9, X, Y, ws, need) == UNSUP
+    assert lib.qmv_qvm(None, 2, ctypes.byref(wt), 2, X, Y, None, need) == INVAL
+    assert lib.qmv_qvm(None, 2, ctypes.byref(wt), 2, X, V(0x10000), ws, need) == INVAL  # overlap
+    two = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 2, 300, 1024, 0x20000, 0x30000, None, None)
+    assert lib.qmv_qvm(None, 2, ctypes.byref(two), 2, X, Y, ws, need) == INVAL
+    sb = bmv.QmvWeights(5, 14, 64, 1, 300, 1024, 0x20000, 0x30000, None, None)
+    assert lib.qmv_qvm(None, 2, ctypes.byref(sb), 2, X, Y, ws, need) == UNSUP
+    assert lib.qmv_qvm(None, 2, ctypes.byref(wt), 0, X, Y, None, 0) == OK
 
 
 def test_block_format_validation(lib):
