@@ -134,6 +134,55 @@ class GatherRunner:
         self.keep = self.wts = None
 
 
+class QvmRunner:
+    """Pre-marshalled qvm calls (y[1, K] = x[1, N] . W[N, K]) over rotating
+    weight copies (>= 1 GiB) and one workspace. Bytes: weights + scales once,
+    x, y, and the fp32 row-split partials written and read back."""
+
+    def __init__(self, bmv, case, min_bytes: int = 1 << 30):
+        import torch
+        self.lib = bmv.load()
+        c = case
+        self.c = c
+        w0 = _dev(c.w)
+        s0 = _dev(c.scales, c.dtype if c.fmt == "affine" else None)
+        b0 = _dev(c.biases, c.dtype) if c.biases is not None else None
+        per = w0.nbytes + s0.nbytes + (b0.nbytes if b0 is not None else 0)
+        self.copies = max(2, -(-min_bytes // per))
+        blk = {"affine": c.group, "mxfp4": 32, "nvfp4": 16, "mxfp8": 32}[c.fmt]
+        self.keep, self.wts = [], []
+        for i in range(self.copies):
+            w = w0 if i == 0 else w0.clone()
+            sc = s0 if i == 0 else s0.clone()
+            bi = None if b0 is None else (b0 if i == 0 else b0.clone())
+            self.keep.append((w, sc, bi))
+            self.wts.append(bmv.make_weights(c.fmt, w, sc, bi, K=c.K, bits=c.bits,
+                                             group_size=blk))
+        self.x = _dev(workloads_x(c.N, c.dtype), c.dtype)
+        self.y = torch.empty((1, c.K), dtype=self.x.dtype, device="cuda:0")
+        self.need = int(self.lib.qmv_qvm_workspace_bytes(1, c.K, c.N))
+        self.ws = torch.empty((self.need // 4,), dtype=torch.float32, device="cuda:0")
+        self.dt = {"f32": 0, "f16": 1, "bf16": 2}[c.dtype]
+        tb = 4 if c.dtype == "f32" else 2
+        self.bytes = per + c.N * tb + c.K * tb + 2 * self.need
+
+    def call(self, i: int, stream) -> None:
+        vp = ctypes.c_void_p
+        st = self.lib.qmv_qvm(stream, self.dt, ctypes.byref(self.wts[i % self.copies]), 1,
+                              vp(self.x.data_ptr()), vp(self.y.data_ptr()),
+                              vp(self.ws.data_ptr()), self.need)
+        if st != 0:
+            raise RuntimeError(self.lib.qmv_last_error().decode())
+
+    def free(self):
+        self.keep = self.wts = None
+
+
+def workloads_x(n: int, dtype: str):
+    import workloads
+    return workloads.to_storage(workloads.rng_for(8, "bench-qvm-x").normal(size=(1, n)), dtype)
+
+
 class QuantRunner:
     """Pre-marshalled quantize-from-float calls: a bf16 [N, K] weight matrix
     (rotating copies over >= 512 MiB, so every call reads from HBM) to one of
@@ -680,6 +729,15 @@ def main() -> int:
         ch = time_chain(bmv)
         cases.append(ch)
         print(f"[bench] {ch['case']}: {json.dumps(ch)}", file=sys.stderr, flush=True)
+        for name, c in (("qvm mxfp4 N=14336 K=4096 B1 bf16", workloads.config3("mxfp4", 1)),
+                        ("qvm affine 4b g64 N=K=4096 B1 bf16", workloads.config4(4, 64, 1, "bf16"))):
+            r = QvmRunner(bmv, c)
+            cr = time_case(r, max(200, args.steps // 4), args.warmup)
+            r.free()
+            cr["case"] = name
+            cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
+            cases.append(cr)
+            print(f"[bench] {name}: {json.dumps(cr)}", file=sys.stderr, flush=True)
         for fmt in ("mxfp4", "nvfp4", "mxfp8", "affine4"):
             r = QuantRunner(bmv, fmt)
             cr = time_case(r, max(100, args.steps // 10), 10)

@@ -302,7 +302,7 @@ qmv_status_t qmv_moe_down_reduce(void* stream, int dtype, const qmv_weights_t* d
 
 size_t qmv_qvm_workspace_bytes(int64_t B, int64_t K, int64_t N) {
     if (B <= 0 || K <= 0 || N <= 0) return 0;
-    return (size_t)qmv::qvm_splits(K, N, nullptr) * (size_t)B * (size_t)K * sizeof(float);
+    return (size_t)qmv::qvm_splits(B, K, N, nullptr) * (size_t)B * (size_t)K * sizeof(float);
 }
 
 qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* wt, int64_t B, const void* x,
@@ -333,6 +333,9 @@ qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* wt, int64_t B
     QMV_TRY(check_ptr(fn, "global_scale", wt->global_scale, wt->global_scale != nullptr, 4));
     QMV_TRY(check_ptr(fn, "workspace", workspace, true, 4));
     const size_t need = qmv_qvm_workspace_bytes(B, wt->K, wt->N);
+    if (qmv::qvm_splits(B, wt->K, wt->N, nullptr) > 65535)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: N = %lld needs more than 65535 row splits at B = %lld",
+                    fn, (long long)wt->N, (long long)B);
     if (workspace_bytes < need)
         return fail(QMV_ERR_INVALID_ARGUMENT, "%s: workspace of %zu bytes, %zu needed", fn,
                     workspace_bytes, need);
@@ -347,7 +350,7 @@ qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* wt, int64_t B
     q.x = x; q.w = wt->w; q.scales = wt->scales; q.biases = wt->biases;
     q.gscale = wt->format == QMV_NVFP4 ? wt->global_scale : nullptr;
     q.y = y; q.ws = static_cast<float*>(workspace);
-    q.splits = qmv::qvm_splits(q.K, q.N, &q.rows_per_split);
+    q.splits = qmv::qvm_splits(q.B, q.K, q.N, &q.rows_per_split);
     return launch_status(qmv::launch_qvm(q, stream), fn);
 }
 

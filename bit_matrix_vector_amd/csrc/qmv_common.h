@@ -82,14 +82,26 @@ struct QvmParams {
     int splits;
 };
 int launch_qvm(const QvmParams& q, void* stream);
-// Row splits of a qvm launch: about 2048 blocks over the 512-column tiles,
-// at least 4 rows each, at most 1024 splits; depends on K and N alone.
-inline int qvm_splits(int64_t K, int64_t N, int64_t* rows_per_split) {
-    const int64_t tiles = (K + 511) / 512;
-    int64_t s = tiles > 0 ? (2048 + tiles - 1) / tiles : 1;
-    const int64_t max_s = (N + 3) / 4;
-    if (s > max_s) s = max_s;
-    if (s > 1024) s = 1024;
+// Output columns per qvm block: a lane owns a whole 32-code unit for B <= 2,
+// 8 columns of one for larger B (8 accumulators per batch row).
+inline int64_t qvm_tile_cols(int64_t B) { return B <= 2 ? 2048 : 512; }
+
+// Row splits of a qvm launch: about 224 blocks of 8 waves (B <= 2) or 512
+// blocks of 4 waves (B > 2) over the column tiles, each split between 64 * B
+// rows (a batch of 8 rows per wave at least, and fp32 partials a small
+// fraction of the weight bytes) and 8192 / B rows (its x rows fit 32 KB of LDS
+// as fp32); depends on B, K and N alone.
+inline int qvm_splits(int64_t B, int64_t K, int64_t N, int64_t* rows_per_split) {
+    const int64_t bb = B < 1 ? 1 : B;
+    const int64_t tc = qvm_tile_cols(bb);
+    const int64_t tiles = (K + tc - 1) / tc;
+    const int64_t target = bb <= 2 ? 224 : 512;
+    int64_t s = tiles > 0 ? (target + tiles - 1) / tiles : 1;
+    const int64_t lo = (N + 64 * bb - 1) / (64 * bb);     // splits at >= 64 B rows
+    const int64_t hi_rows = 8192 / bb;
+    const int64_t need = (N + hi_rows - 1) / hi_rows;     // splits at <= 8192 / B rows
+    if (s > lo) s = lo;
+    if (s < need) s = need;
     if (s < 1) s = 1;
     const int64_t rps = N > 0 ? (N + s - 1) / s : 1;
     if (rows_per_split) *rows_per_split = rps;

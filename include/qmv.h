@@ -211,7 +211,9 @@ qmv_status_t qmv_dequant_device(void* stream, int dtype, const qmv_weights_t* w,
  * qmv_qvm_workspace_bytes(B, K, N) bytes (4-byte aligned), which the call
  * overwrites: row splits write fp32 partial sums there and a second kernel
  * adds them in split order, so repeated calls give identical results. Calls
- * that share a workspace must not overlap. N == 0 writes y = 0. */
+ * that share a workspace must not overlap. N == 0 writes y = 0. A split holds
+ * at most 8192 / B rows and a launch at most 65535 splits, so N above
+ * 65535 * 8192 / B returns QMV_ERR_UNSUPPORTED. */
 size_t qmv_qvm_workspace_bytes(int64_t B, int64_t K, int64_t N);
 qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* w, int64_t B, const void* x,
                      void* y, void* workspace, size_t workspace_bytes);

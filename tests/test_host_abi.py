@@ -233,3 +233,17 @@ def test_host_e4m3_encoder_matches_oracle():
     ref = oracle.e4m3_encode_nearest(v.astype(np.float64))
     bad = np.flatnonzero(got != ref)
     assert bad.size == 0, [(float(v[i]), hex(got[i]), hex(ref[i])) for i in bad[:10]]
+
+
+def test_qvm_split_bounds(lib):
+    # a split holds between 64 * B and 8192 / B rows (when N allows), so the
+    # workspace stays a small fraction of the weights and x fits LDS
+    for B, K, N in ((1, 4096, 14336), (8, 4096, 14336), (1, 512, 1 << 20), (3, 14336, 4096),
+                    (1, 4096, 100), (8, 512, 1 << 22)):
+        ws = lib.qmv_qvm_workspace_bytes(B, K, N)
+        splits = ws // (B * K * 4)
+        rps = -(-N // splits)
+        assert rps <= 8192 // B
+        assert splits <= max(-(-N // (64 * B)), -(-N // (8192 // B)))
+    assert lib.qmv_qvm_workspace_bytes(1, 4096, 14336) == 112 * 4096 * 4
+    assert lib.qmv_qvm_workspace_bytes(1, 4096, 4096) == 64 * 4096 * 4
