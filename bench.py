@@ -178,6 +178,53 @@ class QvmRunner:
         self.keep = self.wts = None
 
 
+class QmmRunner:
+    """Pre-marshalled qmm calls (y[M, N] = x[M, K] . W[N, K]^T) over rotating
+    weight copies (>= 1 GiB). Bytes: weights + scales once, x, y, and the fp32
+    split partials written and read back; flops 2 M N K."""
+
+    def __init__(self, bmv, case, M: int, min_bytes: int = 1 << 30):
+        import torch
+        import workloads
+        self.lib = bmv.load()
+        c = case
+        w0 = _dev(c.w)
+        s0 = _dev(c.scales, c.dtype if c.fmt == "affine" else None)
+        b0 = _dev(c.biases, c.dtype) if c.biases is not None else None
+        per = w0.nbytes + s0.nbytes + (b0.nbytes if b0 is not None else 0)
+        self.copies = max(2, -(-min_bytes // per))
+        blk = {"affine": c.group, "mxfp4": 32, "nvfp4": 16, "mxfp8": 32}[c.fmt]
+        self.keep, self.wts = [], []
+        for i in range(self.copies):
+            w = w0 if i == 0 else w0.clone()
+            sc = s0 if i == 0 else s0.clone()
+            bi = None if b0 is None else (b0 if i == 0 else b0.clone())
+            self.keep.append((w, sc, bi))
+            self.wts.append(bmv.make_weights(c.fmt, w, sc, bi, K=c.K, bits=c.bits,
+                                             group_size=blk))
+        xs = workloads.rng_for(8, "bench-qmm-x").normal(size=(M, c.K))
+        self.x = _dev(workloads.to_storage(xs, c.dtype), c.dtype)
+        self.y = torch.empty((M, c.N), dtype=self.x.dtype, device="cuda:0")
+        self.M = M
+        self.dt = {"f16": 1, "bf16": 2}[c.dtype]
+        self.need = int(self.lib.qmv_qmm_workspace_bytes(M, c.K, c.N))
+        self.ws = torch.empty((max(self.need, 4) // 4,), dtype=torch.float32, device="cuda:0")
+        # partials written and read back when K is split
+        self.bytes = per + 2 * M * (c.K + c.N) + 2 * self.need
+        self.flops = 2 * M * c.N * c.K
+
+    def call(self, i: int, stream) -> None:
+        vp = ctypes.c_void_p
+        st = self.lib.qmv_qmm(stream, self.dt, ctypes.byref(self.wts[i % self.copies]), self.M,
+                              vp(self.x.data_ptr()), vp(self.y.data_ptr()),
+                              vp(self.ws.data_ptr()), self.need)
+        if st != 0:
+            raise RuntimeError(self.lib.qmv_last_error().decode())
+
+    def free(self):
+        self.keep = self.wts = None
+
+
 def workloads_x(n: int, dtype: str):
     import workloads
     return workloads.to_storage(workloads.rng_for(8, "bench-qvm-x").normal(size=(1, n)), dtype)
@@ -736,6 +783,18 @@ def main() -> int:
             r.free()
             cr["case"] = name
             cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
+            cases.append(cr)
+            print(f"[bench] {name}: {json.dumps(cr)}", file=sys.stderr, flush=True)
+        for name, c, M in (("qmm mxfp4 M=32 K=4096 N=14336 bf16", workloads.config3("mxfp4", 1), 32),
+                           ("qmm mxfp4 M=256 K=4096 N=14336 bf16", workloads.config3("mxfp4", 1), 256),
+                           ("qmm affine 4b g64 M=256 K=N=4096 bf16",
+                            workloads.config4(4, 64, 1, "bf16"), 256)):
+            r = QmmRunner(bmv, c, M)
+            cr = time_case(r, max(200, args.steps // 4), args.warmup)
+            r.free()
+            cr["case"] = name
+            cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
+            cr["tflops"] = round(r.flops / (cr["us_per_call"] * 1e-6) / 1e12, 1)
             cases.append(cr)
             print(f"[bench] {name}: {json.dumps(cr)}", file=sys.stderr, flush=True)
         for fmt in ("mxfp4", "nvfp4", "mxfp8", "affine4"):

@@ -103,6 +103,7 @@ def load() -> ctypes.CDLL:
                                    vp],
         "qmv_moe_down_reduce": [vp, i32, ctypes.POINTER(QmvWeights), vp, i64, vp, vp, i64, vp],
         "qmv_qvm": [vp, i32, ctypes.POINTER(QmvWeights), i64, vp, vp, vp, ctypes.c_size_t],
+        "qmv_qmm": [vp, i32, ctypes.POINTER(QmvWeights), i64, vp, vp, vp, ctypes.c_size_t],
         "qmv_quantize_affine": [vp, i32, i64, i64, vp, i32, i32, vp, vp, vp],
         "qmv_quantize_mxfp4": [vp, i32, i64, i64, vp, vp, vp],
         "qmv_quantize_mxfp8": [vp, i32, i64, i64, vp, vp, vp],
@@ -114,6 +115,8 @@ def load() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.qmv_qvm_workspace_bytes.argtypes = [i64, i64, i64]
     lib.qmv_qvm_workspace_bytes.restype = ctypes.c_size_t
+    lib.qmv_qmm_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.qmv_qmm_workspace_bytes.restype = ctypes.c_size_t
     lib.qmv_packed_row_bytes.argtypes = [i32, i32, i64]
     lib.qmv_packed_row_bytes.restype = i64
     lib.qmv_bench_stream_read.argtypes = [vp, vp, i64, vp, i32]
@@ -343,6 +346,28 @@ def qmv_qvm(x, weights: QmvWeights, y=None, workspace=None):
         workspace = torch.empty((max(need, 4) // 4,), dtype=torch.float32, device=x.device)
     _check(load().qmv_qvm(_stream(x.device), _dtype_code(x), ctypes.byref(weights), B, _ptr(x),
                           _ptr(y), _ptr(workspace), workspace.numel() * 4))
+    return y
+
+
+def qmv_qmm(x, weights: QmvWeights, y=None, workspace=None):
+    """y[M, N] = x[M, K] . dequant(W)[N, K]^T for any M (bf16 or f16
+    activations, matrix cores). The fp32 workspace (qmv_qmm_workspace_bytes,
+    often 0) is allocated here unless given."""
+    torch = _torch()
+    x = _dev(x, "x")
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, weights.N), dtype=x.dtype, device=x.device)
+    _dev(y, "y", x.dtype)
+    need = int(load().qmv_qmm_workspace_bytes(M, weights.K, weights.N))
+    if workspace is None and need > 0:
+        workspace = torch.empty((need // 4,), dtype=torch.float32, device=x.device)
+    ws_ptr = _ptr(workspace) if workspace is not None else None
+    ws_bytes = workspace.numel() * 4 if workspace is not None else 0
+    _check(load().qmv_qmm(_stream(x.device), _dtype_code(x), ctypes.byref(weights), M, _ptr(x),
+                          _ptr(y), ws_ptr, ws_bytes))
     return y
 
 

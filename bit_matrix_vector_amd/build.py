@@ -50,6 +50,10 @@ def _jobs() -> list[tuple[list[str], str]]:
         obj = os.path.join(BUILD, f"qmv_qvm_{dt}.o")
         jobs.append(([HIPCC, *HIP_FLAGS, f"-DQVM_DT={dt}", "-c",
                       os.path.join(CSRC, "qmv_qvm.hip"), "-o", obj], obj))
+    for dt in (1, 2):
+        obj = os.path.join(BUILD, f"qmv_qmm_{dt}.o")
+        jobs.append(([HIPCC, *HIP_FLAGS, f"-DQMM_DT={dt}", "-c",
+                      os.path.join(CSRC, "qmv_qmm.hip"), "-o", obj], obj))
     obj = os.path.join(BUILD, "qmv_quant.o")
     jobs.append(([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "qmv_quant.hip"), "-o", obj], obj))
     obj = os.path.join(BUILD, "qmv_bench.o")

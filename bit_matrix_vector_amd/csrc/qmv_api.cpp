@@ -354,6 +354,66 @@ qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* wt, int64_t B
     return launch_status(qmv::launch_qvm(q, stream), fn);
 }
 
+size_t qmv_qmm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+    if (M <= 0 || K <= 0 || N <= 0) return 0;
+    const int s = qmv::qmm_splits(M, K, N);
+    return s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+qmv_status_t qmv_qmm(void* stream, int dtype, const qmv_weights_t* wt, int64_t M, const void* x,
+                     void* y, void* workspace, size_t workspace_bytes) {
+    const char* fn = "qmv_qmm";
+    if (wt == nullptr) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: weights struct is NULL", fn);
+    if (wt->n_experts != 1)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: n_experts must be 1", fn);
+    QMV_TRY(check_common(fn, dtype, 1, wt->K, wt->N, 1));
+    if (dtype != QMV_BF16 && dtype != QMV_F16)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: activations must be bf16 or f16", fn);
+    if (M < 0) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: M=%lld < 0", fn, (long long)M);
+    if (M > (int64_t)65535 * 64)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: M=%lld above %d", fn, (long long)M, 65535 * 64);
+    qmv::LaunchParams lp{};
+    QMV_TRY(format_geometry(fn, wt->format, wt->bits, wt->group_size, wt->K, lp));
+    if (wt->format >= QMV_SB_E8M0)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: qmm takes the affine, MXFP4, NVFP4 and MXFP8 "
+                    "formats", fn);
+    if (M == 0 || wt->N == 0) return QMV_OK;
+    const int tb = dtype_bytes(dtype);
+    QMV_TRY(check_ptr(fn, "y", y, true, tb));
+    if (wt->K == 0)   // empty sums
+        return launch_status(qmv::launch_zero_fill(y, M * wt->N * tb, stream), fn);
+    QMV_TRY(check_ptr(fn, "x", x, true, 16));
+    QMV_TRY(check_ptr(fn, "w", wt->w, true, 16));
+    if (wt->format == QMV_AFFINE) {
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, true, tb));
+        QMV_TRY(check_ptr(fn, "biases", wt->biases, true, tb));
+    } else {
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, true, scale_bytes(wt->format)));
+    }
+    QMV_TRY(check_ptr(fn, "global_scale", wt->global_scale, wt->global_scale != nullptr, 4));
+    {
+        const uintptr_t xs = (uintptr_t)x, xe = xs + (uintptr_t)(M * wt->K * tb);
+        const uintptr_t ys = (uintptr_t)y, ye = ys + (uintptr_t)(M * wt->N * tb);
+        if (xs < ye && ys < xe) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: x and y overlap", fn);
+    }
+    const size_t need = qmv_qmm_workspace_bytes(M, wt->K, wt->N);
+    if (need > 0) {
+        QMV_TRY(check_ptr(fn, "workspace", workspace, true, 4));
+        if (workspace_bytes < need)
+            return fail(QMV_ERR_INVALID_ARGUMENT, "%s: workspace of %zu bytes, %zu needed", fn,
+                        workspace_bytes, need);
+    }
+    qmv::QmmParams q{};
+    q.dtype = dtype; q.format = wt->format; q.bits = lp.bits; q.group = lp.group;
+    q.M = M; q.N = wt->N; q.K = wt->K; q.row_bytes = lp.row_bytes; q.sc_per_row = lp.sc_per_row;
+    q.x = x; q.w = wt->w; q.scales = wt->scales; q.biases = wt->biases;
+    q.gscale = wt->format == QMV_NVFP4 ? wt->global_scale : nullptr;
+    q.y = y;
+    q.ws = static_cast<float*>(workspace);
+    q.splits = qmv::qmm_splits(M, wt->K, wt->N);
+    return launch_status(qmv::launch_qmm(q, stream), fn);
+}
+
 qmv_status_t qmv_quantize_affine(void* stream, int dtype, int64_t N, int64_t K, const void* w,
                                  int bits, int group_size, uint8_t* packed, void* scales,
                                  void* biases) {

@@ -108,6 +108,40 @@ inline int qvm_splits(int64_t B, int64_t K, int64_t N, int64_t* rows_per_split) 
     return N > 0 ? (int)((N + rps - 1) / rps) : 1;
 }
 
+// One qmm call: y[M, N] = x[M, K] . W[N, K]^T (W packed as for QMV), 16-bit
+// activations on the matrix cores.
+struct QmmParams {
+    int dtype;
+    int format;
+    int bits;
+    int group;
+    int64_t M, N, K;
+    int64_t row_bytes, sc_per_row;
+    const void* x;
+    const uint8_t* w;
+    const void* scales;
+    const void* biases;
+    const float* gscale;
+    void* y;
+    float* ws;    // [splits, M, N] fp32 partials when splits > 1
+    int splits;   // K slices split over blocks (1 = none)
+};
+int launch_qmm(const QmmParams& q, void* stream);
+// K splits of a qmm launch: none once the 64 x 128 output tiles reach 256
+// (one per compute unit); else enough to reach about 512 blocks, at most 8
+// and with at least 8 slices of 64 codes each. Depends on M, K and N alone.
+inline int qmm_splits(int64_t M, int64_t K, int64_t N) {
+    const int64_t tiles = ((N + 127) / 128) * ((M + 63) / 64);
+    const int64_t nk = (K + 63) / 64;
+    if (tiles <= 0 || tiles >= 256) return 1;
+    int64_t s = (512 + tiles - 1) / tiles;
+    if (s > 8) s = 8;
+    if (s > nk / 8) s = nk / 8;
+    if (s < 1) return 1;
+    const int64_t per = (nk + s - 1) / s;   // slices per split; no split is empty
+    return (int)((nk + per - 1) / per);
+}
+
 // One quantize-from-float call: w [N, K] in `dtype` to the packed format.
 struct QuantParams {
     int dtype;

@@ -86,6 +86,17 @@ int launch_qvm(const QvmParams& q, void* stream) {
     return (int)hipErrorInvalidValue;
 }
 
+int launch_qmm_dt_1(const QmmParams&, void*);
+int launch_qmm_dt_2(const QmmParams&, void*);
+
+int launch_qmm(const QmmParams& q, void* stream) {
+    switch (q.dtype) {
+        case DT_F16: return launch_qmm_dt_1(q, stream);
+        case DT_BF16: return launch_qmm_dt_2(q, stream);
+    }
+    return (int)hipErrorInvalidValue;
+}
+
 namespace {
 __global__ void zero_fill_kernel(uint16_t* p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;

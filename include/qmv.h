@@ -218,6 +218,31 @@ size_t qmv_qvm_workspace_bytes(int64_t B, int64_t K, int64_t N);
 qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* w, int64_t B, const void* x,
                      void* y, void* workspace, size_t workspace_bytes);
 
+/* ---------------- qmm (batched product): DEVICE memory, asynchronous ---------
+ * y[m, n] = sum_k x[m, k] * W[n, k] for M rows of activations at once (the
+ * transposed qmm of "mlx 1.0.0 - quantized_nax.h": activations against the
+ * packed [N, K] matrix the QMV entry points read; "wh-iron kernel-op coverage
+ * audit", op row "quantized (affine_qmv / qvm / qmm)": the M-batched prefill
+ * product), for batches past the QMV's eight rows. w: one matrix
+ * (n_experts == 1) of the affine, MXFP4, NVFP4 or MXFP8 formats; x [M, K]
+ * (16-byte aligned) and y [M, N] in dtype, which must be QMV_BF16 or QMV_F16
+ * (QMV_F32 returns QMV_ERR_UNSUPPORTED); 0 <= M <= 65535 * 64 (M == 0 or
+ * N == 0 is a no-op, K == 0 writes y = 0). Products run on the matrix cores
+ * with fp32 accumulation: MXFP4 / MXFP8 / NVFP4 weights enter them as
+ * code * block scale rounded to dtype, which is exact in bf16 (and in f16
+ * while the value lies in f16's normal range); affine codes enter as integers
+ * and scale and bias are applied per group in fp32 (s * sum x q + b * sum x);
+ * NVFP4's global scale multiplies the fp32 result; y is rounded to dtype once.
+ * workspace: caller-owned device memory of qmv_qmm_workspace_bytes(M, K, N)
+ * bytes (4-byte aligned; may be NULL when that is 0). When M and N give too
+ * few output tiles to fill the GPU, K is split over blocks that write fp32
+ * partial sums there and a second kernel adds them in split order, so
+ * repeated calls give identical results; calls that share a workspace must
+ * not overlap. */
+size_t qmv_qmm_workspace_bytes(int64_t M, int64_t K, int64_t N);
+qmv_status_t qmv_qmm(void* stream, int dtype, const qmv_weights_t* w, int64_t M, const void* x,
+                     void* y, void* workspace, size_t workspace_bytes);
+
 /* ---------------- fused routed-MoE decode block: DEVICE, asynchronous -------
  * The decode step of a routed mixture-of-experts FFN in two calls
  * ("@lgrammel/ds4-provider - moe.metal": the fused gate/up + activation

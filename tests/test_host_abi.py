@@ -28,7 +28,7 @@ def test_library_exports_every_header_function(lib):
             "qmv_unpack_codes_device", "qmv_dequant_device", "qmv_packed_row_bytes",
             "qmv_quantize_affine", "qmv_quantize_mxfp4", "qmv_quantize_mxfp8",
             "qmv_quantize_nvfp4", "qmv_moe_gate_up_swiglu", "qmv_moe_down_reduce", "qmv_fp_block",
-            "qmv_qvm", "qmv_qvm_workspace_bytes",
+            "qmv_qvm", "qmv_qvm_workspace_bytes", "qmv_qmm", "qmv_qmm_workspace_bytes",
             "qmv_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -247,3 +247,45 @@ def test_qvm_split_bounds(lib):
         assert splits <= max(-(-N // (64 * B)), -(-N // (8192 // B)))
     assert lib.qmv_qvm_workspace_bytes(1, 4096, 14336) == 112 * 4096 * 4
     assert lib.qmv_qvm_workspace_bytes(1, 4096, 4096) == 64 * 4096 * 4
+
+
+def test_qmm_validation(lib):
+    wt = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 1, 300, 1024, 0x20000, 0x30000, None, None)
+    ws = V(0xA0000)
+    need = lib.qmv_qmm_workspace_bytes(16, 1024, 300)
+    assert need > 0 and need % (16 * 300 * 4) == 0          # few tiles: K is split
+    assert lib.qmv_qmm_workspace_bytes(4096, 4096, 14336) == 0  # many tiles: no split
+    assert lib.qmv_qmm(None, 0, ctypes.byref(wt), 16, X, Y, ws, need) == UNSUP    # f32
+    assert lib.qmv_qmm(None, 7, ctypes.byref(wt), 16, X, Y, ws, need) == INVAL    # not a dtype
+    assert lib.qmv_qmm(None, 2, ctypes.byref(wt), -1, X, Y, ws, need) == INVAL
+    assert lib.qmv_qmm(None, 2, ctypes.byref(wt), 65535 * 64 + 1, X, Y, ws, need) == UNSUP
+    assert lib.qmv_qmm(None, 2, ctypes.byref(wt), 16, V(0x100008), Y, ws, need) == MISAL
+    assert lib.qmv_qmm(None, 2, ctypes.byref(wt), 16, X, X, ws, need) == INVAL    # overlap
+    assert lib.qmv_qmm(None, 2, ctypes.byref(wt), 16, X, Y, ws, need - 4) == INVAL
+    assert "workspace" in lib.qmv_last_error().decode()
+    assert lib.qmv_qmm(None, 2, ctypes.byref(wt), 16, X, Y, None, need) == INVAL
+    two = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 2, 300, 1024, 0x20000, 0x30000, None, None)
+    assert lib.qmv_qmm(None, 2, ctypes.byref(two), 16, X, Y, ws, need) == INVAL
+    sb = bmv.QmvWeights(5, 14, 64, 1, 300, 1024, 0x20000, 0x30000, None, None)
+    assert lib.qmv_qmm(None, 2, ctypes.byref(sb), 16, X, Y, ws, need) == UNSUP
+    odd = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 1, 300, 1000, 0x20000, 0x30000, None, None)
+    assert lib.qmv_qmm(None, 2, ctypes.byref(odd), 16, X, Y, ws, need) == INVAL   # K % 32
+    assert lib.qmv_qmm(None, 2, ctypes.byref(wt), 0, X, Y, None, 0) == OK         # M == 0
+    assert lib.qmv_qmm(None, 2, None, 16, X, Y, ws, need) == INVAL
+
+
+def test_qmm_split_rule(lib):
+    # splits only when the output tiles are fewer than 256, at most 8, each
+    # split at least 8 slices of 64 codes, none empty
+    for M, K, N in ((32, 4096, 14336), (9, 1056, 300), (256, 4096, 4096), (1, 512, 64),
+                    (64, 8192, 4096), (2000, 4096, 14336)):
+        ws = lib.qmv_qmm_workspace_bytes(M, K, N)
+        s = ws // (M * N * 4) if ws else 1
+        tiles = -(-N // 128) * -(-M // 64)
+        nk = -(-K // 64)
+        assert 1 <= s <= 8
+        if tiles >= 256:
+            assert s == 1
+        if s > 1:
+            per = -(-nk // s)
+            assert per >= 8 and (s - 1) * per < nk
