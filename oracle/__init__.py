@@ -33,6 +33,8 @@ passage it follows):
 * The fused routed-MoE decode block (``moe.py``): the ds4 moe.metal SwiGLU
   activation and per-token down-projection sum, and the audit's two-dispatch
   description of the block.
+* RMSNorm in front of the QMV (``norm.py``): the audit's rms_norm and
+  rms_norm_qgemv rows, with the readings its docstring states.
 * Quantize-from-float (``quantize.py``): the audit's Track-2 min/max encoder
   and the fp_quantized / kv_cache rows' max-scale element rounding, with the
   readings its docstring states.
@@ -82,6 +84,7 @@ from .moe import (
     moe_gate_up_swiglu,
     moe_down_reduce,
 )
+from .norm import rmsnorm, rmsnorm_stored
 from .qmv import (
     dequant_affine,
     dequant_mxfp4,

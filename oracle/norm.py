@@ -1,0 +1,40 @@
+"""RMSNorm in front of the QMV (the fused "RMSNorm + quantized GEMV").
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Source: "wh-iron kernel-op coverage audit", the op-coverage rows "rms_norm"
+and "rms_norm_qgemv (RMSNorm + quantized GEMV fused)", and the block-scaled
+family's "fused RMSNorm + GEMV": a root-mean-square normalization of the
+activation row, scaled per element by a weight vector, feeding the quantized
+matrix-vector product in one dispatch.
+
+Readings (the pages name the operation but print no formula): the usual
+RMSNorm, xn[k] = x[k] / sqrt(mean_k x^2 + eps) * gamma[k], with eps an
+argument; the normalized row is rounded to the activation type T, as a
+separate RMSNorm kernel would store it, and the QMV then runs on that row.
+Here everything up to that rounding is fp64.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .codes import round_f64_to, storage_to_f64
+
+
+def rmsnorm(x, x_dtype: str, gamma, eps: float) -> np.ndarray:
+    """fp64 xn[b, k] = x[b, k] * (1 / sqrt(mean_k x[b, k]^2 + eps)) * gamma[k]
+    for stored x [B, K] and gamma [K] (eps taken as the fp32 the caller
+    passes)."""
+    x64 = storage_to_f64(x, x_dtype)
+    if x64.ndim == 1:
+        x64 = x64[None, :]
+    g64 = storage_to_f64(gamma, x_dtype).reshape(-1)
+    ms = np.mean(x64 * x64, axis=1)
+    r = 1.0 / np.sqrt(ms + float(np.float32(eps)))
+    return x64 * r[:, None] * g64[None, :]
+
+
+def rmsnorm_stored(x, x_dtype: str, gamma, eps: float) -> np.ndarray:
+    """The normalized rows rounded to T (stored form), the QMV's input."""
+    return round_f64_to(rmsnorm(x, x_dtype, gamma, eps), x_dtype)
