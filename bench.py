@@ -178,6 +178,32 @@ class QvmRunner:
         self.keep = self.wts = None
 
 
+class NormRunner(Runner):
+    """The fused RMSNorm + QMV over the same rotating weight copies as the
+    plain QMV case; bytes add gamma once."""
+
+    def __init__(self, bmv, case, min_bytes: int = 1 << 30):
+        super().__init__(bmv, case, min_bytes)
+        import workloads
+        g = workloads.rng_for(8, "bench-gamma").uniform(0.5, 1.5, size=case.K)
+        self.gamma = _dev(workloads.to_storage(g, case.dtype), case.dtype)
+        blk = {"affine": case.group, "mxfp4": 32, "nvfp4": 16, "mxfp8": 32}[case.fmt]
+        self.wts = [bmv.make_weights(case.fmt, self.w[i], self.s[i],
+                                     None if self.b is None else self.b[i], K=case.K,
+                                     bits=case.bits, group_size=blk, global_scale=self.g)
+                    for i in range(self.copies)]
+        self.bytes += case.K * (2 if case.dtype != "f32" else 4)
+
+    def call(self, i: int, stream) -> None:
+        vp = ctypes.c_void_p
+        st = self.lib.qmv_rmsnorm_qmv(stream, self.dt, ctypes.byref(self.wts[i % self.copies]),
+                                      self.case.B, vp(self.x.data_ptr()),
+                                      vp(self.gamma.data_ptr()), ctypes.c_float(1e-6),
+                                      vp(self.y.data_ptr()))
+        if st != 0:
+            raise RuntimeError(self.lib.qmv_last_error().decode())
+
+
 class QmmRunner:
     """Pre-marshalled qmm calls (y[M, N] = x[M, K] . W[N, K]^T) over rotating
     weight copies (>= 1 GiB). Bytes: weights + scales once, x, y, and the fp32
@@ -776,6 +802,16 @@ def main() -> int:
         ch = time_chain(bmv)
         cases.append(ch)
         print(f"[bench] {ch['case']}: {json.dumps(ch)}", file=sys.stderr, flush=True)
+        for name, c in (("rmsnorm+qmv mxfp4 B1 K=4096 N=14336 bf16", workloads.config3("mxfp4", 1)),
+                        ("rmsnorm+qmv affine 4b g64 B1 K=N=4096 bf16",
+                         workloads.config4(4, 64, 1, "bf16"))):
+            r = NormRunner(bmv, c)
+            cr = time_case(r, max(200, args.steps // 4), args.warmup)
+            r.free()
+            cr["case"] = name
+            cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
+            cases.append(cr)
+            print(f"[bench] {name}: {json.dumps(cr)}", file=sys.stderr, flush=True)
         for name, c in (("qvm mxfp4 N=14336 K=4096 B1 bf16", workloads.config3("mxfp4", 1)),
                         ("qvm affine 4b g64 N=K=4096 B1 bf16", workloads.config4(4, 64, 1, "bf16"))):
             r = QvmRunner(bmv, c)

@@ -104,6 +104,7 @@ def load() -> ctypes.CDLL:
         "qmv_moe_down_reduce": [vp, i32, ctypes.POINTER(QmvWeights), vp, i64, vp, vp, i64, vp],
         "qmv_qvm": [vp, i32, ctypes.POINTER(QmvWeights), i64, vp, vp, vp, ctypes.c_size_t],
         "qmv_qmm": [vp, i32, ctypes.POINTER(QmvWeights), i64, vp, vp, vp, ctypes.c_size_t],
+        "qmv_rmsnorm_qmv": [vp, i32, ctypes.POINTER(QmvWeights), i64, vp, vp, ctypes.c_float, vp],
         "qmv_quantize_affine": [vp, i32, i64, i64, vp, i32, i32, vp, vp, vp],
         "qmv_quantize_mxfp4": [vp, i32, i64, i64, vp, vp, vp],
         "qmv_quantize_mxfp8": [vp, i32, i64, i64, vp, vp, vp],
@@ -346,6 +347,22 @@ def qmv_qvm(x, weights: QmvWeights, y=None, workspace=None):
         workspace = torch.empty((max(need, 4) // 4,), dtype=torch.float32, device=x.device)
     _check(load().qmv_qvm(_stream(x.device), _dtype_code(x), ctypes.byref(weights), B, _ptr(x),
                           _ptr(y), _ptr(workspace), workspace.numel() * 4))
+    return y
+
+
+def qmv_rmsnorm_qmv(x, weights: QmvWeights, gamma, eps: float, y=None):
+    """y[B, N] = W . RN_T(rmsnorm(x) * gamma), one fused dispatch."""
+    torch = _torch()
+    x = _dev(x, "x")
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    _dev(gamma, "gamma", x.dtype)
+    B = x.shape[0]
+    if y is None:
+        y = torch.empty((B, weights.N), dtype=x.dtype, device=x.device)
+    _dev(y, "y", x.dtype)
+    _check(load().qmv_rmsnorm_qmv(_stream(x.device), _dtype_code(x), ctypes.byref(weights), B,
+                                  _ptr(x), _ptr(gamma), float(eps), _ptr(y)))
     return y
 
 

@@ -354,6 +354,51 @@ qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* wt, int64_t B
     return launch_status(qmv::launch_qvm(q, stream), fn);
 }
 
+qmv_status_t qmv_rmsnorm_qmv(void* stream, int dtype, const qmv_weights_t* wt, int64_t B,
+                             const void* x, const void* gamma, float eps, void* y) {
+    const char* fn = "qmv_rmsnorm_qmv";
+    if (wt == nullptr) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: weights struct is NULL", fn);
+    if (wt->n_experts != 1)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: n_experts must be 1", fn);
+    QMV_TRY(check_common(fn, dtype, B, wt->K, wt->N, 8));
+    qmv::LaunchParams lp{};
+    lp.dtype = dtype;
+    QMV_TRY(format_geometry(fn, wt->format, wt->bits, wt->group_size, wt->K, lp));
+    if (wt->format >= QMV_SB_E8M0)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: takes the affine, MXFP4, NVFP4 and MXFP8 formats",
+                    fn);
+    if (!(eps >= 0.0f) || eps > 3.0e38f)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: eps must be finite and >= 0", fn);
+    if (B == 0 || wt->N == 0) return QMV_OK;
+    const int tb = dtype_bytes(dtype);
+    QMV_TRY(check_ptr(fn, "y", y, true, tb));
+    if (wt->K == 0)   // empty sums
+        return launch_status(qmv::launch_zero_fill(y, B * wt->N * tb, stream), fn);
+    QMV_TRY(check_ptr(fn, "x", x, true, 16));
+    QMV_TRY(check_ptr(fn, "gamma", gamma, true, 16));
+    QMV_TRY(check_ptr(fn, "w", wt->w, true, 16));
+    if (wt->format == QMV_AFFINE) {
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, true, tb));
+        QMV_TRY(check_ptr(fn, "biases", wt->biases, true, tb));
+    } else {
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, true, scale_bytes(wt->format)));
+    }
+    QMV_TRY(check_ptr(fn, "global_scale", wt->global_scale, wt->global_scale != nullptr, 4));
+    {
+        const uintptr_t xs = (uintptr_t)x, xe = xs + (uintptr_t)(B * wt->K * tb);
+        const uintptr_t ys = (uintptr_t)y, ye = ys + (uintptr_t)(B * wt->N * tb);
+        if (xs < ye && ys < xe) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: x and y overlap", fn);
+        const uintptr_t gs = (uintptr_t)gamma, ge = gs + (uintptr_t)(wt->K * tb);
+        if (gs < ye && ys < ge)
+            return fail(QMV_ERR_INVALID_ARGUMENT, "%s: gamma and y overlap", fn);
+    }
+    lp.B = B; lp.K = wt->K; lp.N = wt->N;
+    lp.x = x; lp.w = wt->w; lp.scales = wt->scales; lp.biases = wt->biases; lp.y = y;
+    lp.gscale = wt->format == QMV_NVFP4 ? wt->global_scale : nullptr;
+    qmv::NormArgs na{gamma, eps};
+    return launch_status(qmv::launch_qmv_norm(lp, na, stream), fn);
+}
+
 size_t qmv_qmm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
     if (M <= 0 || K <= 0 || N <= 0) return 0;
     const int s = qmv::qmm_splits(M, K, N);

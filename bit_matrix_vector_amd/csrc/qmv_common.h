@@ -58,6 +58,13 @@ struct MoeArgs {
 };
 struct NoMoeArgs {};
 
+// Fused RMSNorm in front of a QMV: gamma [K] in T (16-byte aligned), eps >= 0.
+struct NormArgs {
+    const void* gamma;
+    float eps;
+};
+int launch_qmv_norm(const LaunchParams& p, const NormArgs& na, void* stream);
+
 int launch_moe_gate_up(const LaunchParams& p, const MoeArgs& m, void* stream);
 int launch_zero_fill(void* p, int64_t bytes, void* stream);   // bytes % 2 == 0
 int launch_moe_down(const LaunchParams& p, const MoeArgs& m, void* stream);

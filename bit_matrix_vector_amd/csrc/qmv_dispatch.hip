@@ -13,6 +13,7 @@ QMV_DECL_SB(1, 4) QMV_DECL_SB(2, 2) QMV_DECL_SB(2, 3) QMV_DECL_SB(2, 4)
 
 #define QMV_DECL_PART(dt, fam)                                                          \
     int launch_qmv_part_##dt##_##fam(const LaunchParams&, void*);                       \
+    int launch_qmv_norm_part_##dt##_##fam(const LaunchParams&, const NormArgs&, void*);  \
     int launch_gather_part_##dt##_##fam(const LaunchParams&, void*);                    \
     int launch_moe_gate_up_part_##dt##_##fam(const LaunchParams&, const MoeArgs&, void*); \
     int launch_moe_down_part_##dt##_##fam(const LaunchParams&, const MoeArgs&, void*);  \
@@ -52,6 +53,11 @@ QMV_DECL_PART(1, 1) QMV_DECL_PART(2, 0) QMV_DECL_PART(2, 1)
             default: return (int)hipErrorInvalidValue;                                  \
         }                                                                               \
     } while (0)
+
+int launch_qmv_norm(const LaunchParams& p, const NormArgs& na, void* stream) {
+    if (p.format >= FMT_SB_E8M0) return (int)hipErrorInvalidValue;
+    QMV_ROUTE(launch_qmv_norm_part, p, na, stream);
+}
 
 int launch_qmv(const LaunchParams& p, void* stream) {
     if (p.format >= FMT_SB_E8M0) QMV_ROUTE_SB(launch_qmv_part, p, stream);

@@ -62,6 +62,11 @@ int dispatch_part(const LaunchParams& p, A... a) {
 template <int DT, int FMT, int BITS> struct QmvL {
     static int run(const LaunchParams& p, hipStream_t s) { return launch_qmv_t<DT, FMT, BITS>(p, s); }
 };
+template <int DT, int FMT, int BITS> struct QmvNormL {
+    static int run(const LaunchParams& p, const NormArgs& na, hipStream_t s) {
+        return launch_qmv_norm_t<DT, FMT, BITS>(p, na, s);
+    }
+};
 template <int DT, int FMT, int BITS> struct GatherL {
     static int run(const LaunchParams& p, hipStream_t s) {
         return launch_gather_t<DT, FMT, BITS>(p, s);
@@ -89,6 +94,10 @@ int QMV_PART(launch_qmv_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, void* str
     return dispatch_part<QmvL>(p, static_cast<hipStream_t>(stream));
 }
 #if QMV_FAM <= 1
+int QMV_PART(launch_qmv_norm_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, const NormArgs& na,
+                                                      void* stream) {
+    return dispatch_part<QmvNormL>(p, na, static_cast<hipStream_t>(stream));
+}
 int QMV_PART(launch_gather_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, void* stream) {
     return dispatch_part<GatherL>(p, static_cast<hipStream_t>(stream));
 }

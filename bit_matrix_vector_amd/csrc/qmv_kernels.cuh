@@ -61,15 +61,91 @@ struct Geom {
 
 // x rows of a tile. Contiguous rows (qmv) or rows picked by an index list
 // held in LDS (gather); `row(b)` is called with a run-time b.
+// x row accessors of a tile: row(b) is batch row b; stage(b, k, v) is the
+// 16-byte chunk v of that row starting at element k as it goes into LDS (each
+// element of the block's rows is staged exactly once, by one thread);
+// finish() runs in every thread after the tile's sums and before its stores;
+// out(b, v) is row b's fp32 result before the final rounding.
 template <class S> struct XContig {
     const S* x;
     int64_t K;
     __device__ const S* row(int b) const { return x + (int64_t)b * K; }
+    __device__ v4u stage(int, int64_t, v4u v) const { return v; }
+    __device__ void finish() const {}
+    __device__ float out(int, float v) const { return v; }
 };
 template <class S> struct XListed {
     const S* x;
     const int64_t* off;  // LDS: element offset of each staged row
     __device__ const S* row(int b) const { return x + off[b]; }
+    __device__ v4u stage(int, int64_t, v4u v) const { return v; }
+    __device__ void finish() const {}
+    __device__ float out(int, float v) const { return v; }
+};
+// Fused RMSNorm. The row's normalization r[b] = 1 / sqrt(mean_k x^2 + eps) is
+// one scalar, so it multiplies the fp32 dot products at the end; element k
+// enters LDS as RN_T(x[b, k] * gamma[k]) — the product of two T values is
+// exact in fp32, so that is one rounding of the exact product. The squares
+// are summed as the elements are staged (fp32, each thread in its staging
+// order), then over lanes and waves in a fixed order in finish(), so every
+// block of a launch forms the same r.
+template <int DT, int NB> struct XNorm {
+    using S = typename Store<DT>::S;
+    const S* x;
+    int64_t K;
+    const S* gamma;   // [K], 16-byte aligned
+    float eps;
+    float* red;       // LDS [NB][kWaves]
+    mutable float ss[NB];
+    mutable float r[NB];
+    __device__ const S* row(int b) const { return x + (int64_t)b * K; }
+    __device__ v4u stage(int b, int64_t k, v4u v) const {
+        const v4u gv = *reinterpret_cast<const v4u*>(gamma + k);
+        const uint32_t xi[4] = {v.x, v.y, v.z, v.w};
+        const uint32_t gi[4] = {gv.x, gv.y, gv.z, gv.w};
+        uint32_t o[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (Store<DT>::kBytes == 4) {
+                const float xv = __uint_as_float(xi[j]);
+                ss[b] = fmaf(xv, xv, ss[b]);
+                o[j] = __float_as_uint(xv * __uint_as_float(gi[j]));
+            } else {
+                const float x0 = Store<DT>::bits_to_f32(xi[j] & 0xFFFFu);
+                const float x1 = Store<DT>::bits_to_f32(xi[j] >> 16);
+                ss[b] = fmaf(x0, x0, ss[b]);
+                ss[b] = fmaf(x1, x1, ss[b]);
+                const f32x2 p = {x0 * Store<DT>::bits_to_f32(gi[j] & 0xFFFFu),
+                                 x1 * Store<DT>::bits_to_f32(gi[j] >> 16)};
+                // the pair converts (round to nearest even) in one instruction
+                if constexpr (DT == DT_BF16)
+                    o[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, bf16x2_t));
+                else
+                    o[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p, f16x2_t));
+            }
+        }
+        return v4u{o[0], o[1], o[2], o[3]};
+    }
+    __device__ void finish() const {
+        const int lane = threadIdx.x & 63;
+        const int wave = threadIdx.x >> 6;
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float t = ss[b];
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
+            if (lane == 0) red[b * kWaves + wave] = t;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            float t = red[b * kWaves];
+#pragma unroll
+            for (int w = 1; w < kWaves; ++w) t += red[b * kWaves + w];
+            r[b] = 1.0f / sqrtf(t / (float)K + eps);
+        }
+    }
+    __device__ float out(int b, float v) const { return v * r[b]; }
 };
 
 // LDS layout of a staged x row: the 8-value sub-chunk sc of unit u sits at
@@ -354,17 +430,19 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
             const int v = tid + j * kThreads;
             if (v < vec_per_row)
                 *reinterpret_cast<v4u*>(lds + x_lds_slot(v * kPerVec, us)) =
-                    stage_vec<FMT, BITS, DT>(xs[j]);
+                    stage_vec<FMT, BITS, DT>(xr.stage(0, slab + v * kPerVec, xs[j]));
         });
         for (int v = tid + kXAhead * kThreads; v < vec_per_row; v += kThreads)
             *reinterpret_cast<v4u*>(lds + x_lds_slot(v * kPerVec, us)) =
-                stage_vec<FMT, BITS, DT>(reinterpret_cast<const v4u*>(xr.row(0) + slab)[v]);
+                stage_vec<FMT, BITS, DT>(xr.stage(
+                    0, slab + v * kPerVec, reinterpret_cast<const v4u*>(xr.row(0) + slab)[v]));
 #pragma unroll
         for (int b = 1; b < NB; ++b) {
             const S* src = xr.row(b) + slab;
             for (int v = tid; v < vec_per_row; v += kThreads)
                 *reinterpret_cast<v4u*>(lds + b * ks + x_lds_slot(v * kPerVec, us)) =
-                    stage_vec<FMT, BITS, DT>(reinterpret_cast<const v4u*>(src)[v]);
+                    stage_vec<FMT, BITS, DT>(
+                        xr.stage(b, slab + v * kPerVec, reinterpret_cast<const v4u*>(src)[v]));
         }
         // (3b) scale segment to LDS
         if (nw > 0) {
@@ -412,6 +490,7 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
             total[i][b] = group_sum(total[i][b], lpr);
         }
 
+    xr.finish();
     if (gl == lpr - 1) {
 #pragma unroll
         for (int i = 0; i < R; ++i) {
@@ -419,7 +498,7 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
             if (r < N) {
 #pragma unroll
                 for (int b = 0; b < NB; ++b) {
-                    float v = total[i][b];
+                    float v = xr.out(b, total[i][b]);
                     if constexpr (FMT == FMT_NVFP4) v = v * gmul;
                     yrow[b][r] = Store<DT>::from_f32(v);
                 }
@@ -437,6 +516,25 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(LaunchParams p, Geom g) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) yrow[b] = static_cast<S*>(p.y) + b * p.N;
     const XContig<S> xr{static_cast<const S*>(p.x), p.K};
+    const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
+    qmv_tile<DT, FMT, BITS, NB, R>(p, g, (int64_t)blockIdx.x * g.rows_per_block, p.w, p.scales,
+                                   p.biases, xr, yrow, gmul, lds);
+}
+
+// Fused RMSNorm + QMV: y[b] = r[b] * (W . RN_T(x[b] * gamma)), the QMV tile
+// with the XNorm accessor (x times gamma staged, the squares summed on the
+// way, r applied to each row's result).
+template <int DT, int FMT, int BITS, int NB, int R>
+__global__ __launch_bounds__(kThreads) void qmv_norm_kernel(LaunchParams p, Geom g, NormArgs na) {
+    using S = typename Store<DT>::S;
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ float red[NB * kWaves];
+    S* lds = reinterpret_cast<S*>(smem);
+    XNorm<DT, NB> xr{static_cast<const S*>(p.x), p.K, static_cast<const S*>(na.gamma), na.eps,
+                     red, {}, {}};
+    S* yrow[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) yrow[b] = static_cast<S*>(p.y) + b * p.N;
     const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
     qmv_tile<DT, FMT, BITS, NB, R>(p, g, (int64_t)blockIdx.x * g.rows_per_block, p.w, p.scales,
                                    p.biases, xr, yrow, gmul, lds);
@@ -1247,6 +1345,35 @@ int launch_qmv_r(const LaunchParams& p, hipStream_t st) {
     if (const int e = allow_lds(kern, lds, granted)) return e;
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, p, g);
     return (int)hipGetLastError();
+}
+
+template <int DT, int FMT, int BITS, int NB, int R>
+int launch_qmv_norm_r(const LaunchParams& p, const NormArgs& na, hipStream_t st) {
+    const Geom g = make_geom<DT, FMT, BITS>(p, NB, kMaxStageBytes, R);
+    const dim3 grid((unsigned)((p.N + g.rows_per_block - 1) / g.rows_per_block));
+    const size_t lds = stage_bytes<DT, FMT, BITS>(p, g);
+    auto* kern = &qmv_norm_kernel<DT, FMT, BITS, NB, R>;
+    static std::atomic<size_t> granted{0};
+    if (const int e = allow_lds(kern, lds, granted)) return e;
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, p, g, na);
+    return (int)hipGetLastError();
+}
+
+// The fused RMSNorm + QMV takes four rows per lane group while that still
+// launches 2048 waves, else two: every block redoes the row's x work (x *
+// gamma and the squares), so fewer, taller blocks do less of it.
+template <int DT, int FMT, int BITS>
+int launch_qmv_norm_t(const LaunchParams& p, const NormArgs& na, hipStream_t st) {
+    switch ((int)p.B) {
+#define QMV_CASE(n)                                                                         \
+    case n:                                                                                 \
+        if (launch_waves(p, 4) >= 2048) return launch_qmv_norm_r<DT, FMT, BITS, n, 4>(p, na, st); \
+        return launch_qmv_norm_r<DT, FMT, BITS, n, 2>(p, na, st);
+        QMV_CASE(1) QMV_CASE(2) QMV_CASE(3) QMV_CASE(4)
+        QMV_CASE(5) QMV_CASE(6) QMV_CASE(7) QMV_CASE(8)
+#undef QMV_CASE
+        default: return (int)hipErrorInvalidValue;
+    }
 }
 
 template <int DT, int FMT, int BITS>

@@ -218,6 +218,22 @@ size_t qmv_qvm_workspace_bytes(int64_t B, int64_t K, int64_t N);
 qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* w, int64_t B, const void* x,
                      void* y, void* workspace, size_t workspace_bytes);
 
+/* ---------------- fused RMSNorm + QMV: DEVICE memory, asynchronous ----------
+ * y[b, :] = W . (x[b, :] * r[b] * gamma) with r[b] = 1 / sqrt(mean_k x[b, k]^2
+ * + eps) ("wh-iron kernel-op coverage audit", op rows "rms_norm" and
+ * "rms_norm_qgemv (RMSNorm + quantized GEMV fused)", and the block-scaled
+ * family's "fused RMSNorm + GEMV"), in one dispatch. r is one scalar per row,
+ * so it multiplies the fp32 dot products before the final rounding; the
+ * matrix-vector step reads RN_T(x[b, k] * gamma[k]) (the product of two T
+ * values is exact in fp32, so this is one rounding). r is formed in fp32
+ * (squares summed in fp32 in a fixed order, correctly rounded division and
+ * square root). w: one matrix of the affine, MXFP4, NVFP4 or MXFP8 formats
+ * (n_experts == 1); x [B, K] and gamma [K] in dtype (16-byte aligned);
+ * y [B, N]; 1 <= B <= 8 (B = 0 is a no-op); eps finite and >= 0. K == 0 writes
+ * y = 0. */
+qmv_status_t qmv_rmsnorm_qmv(void* stream, int dtype, const qmv_weights_t* w, int64_t B,
+                             const void* x, const void* gamma, float eps, void* y);
+
 /* ---------------- qmm (batched product): DEVICE memory, asynchronous ---------
  * y[m, n] = sum_k x[m, k] * W[n, k] for M rows of activations at once (the
  * transposed qmm of "mlx 1.0.0 - quantized_nax.h": activations against the

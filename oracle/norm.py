@@ -9,10 +9,11 @@ activation row, scaled per element by a weight vector, feeding the quantized
 matrix-vector product in one dispatch.
 
 Readings (the pages name the operation but print no formula): the usual
-RMSNorm, xn[k] = x[k] / sqrt(mean_k x^2 + eps) * gamma[k], with eps an
-argument; the normalized row is rounded to the activation type T, as a
-separate RMSNorm kernel would store it, and the QMV then runs on that row.
-Here everything up to that rounding is fp64.
+RMSNorm, xn[k] = x[k] * r * gamma[k] with r = 1 / sqrt(mean_k x^2 + eps) and
+eps an argument. r is one scalar per row, so W . xn = r * (W . (x * gamma)):
+the fused product stages x * gamma rounded once to the activation type T (the
+product of two T values is exact, so this is a single rounding of an exact
+value, the same on any machine) and multiplies each row's result by r.
 """
 
 from __future__ import annotations
@@ -38,3 +39,20 @@ def rmsnorm(x, x_dtype: str, gamma, eps: float) -> np.ndarray:
 def rmsnorm_stored(x, x_dtype: str, gamma, eps: float) -> np.ndarray:
     """The normalized rows rounded to T (stored form), the QMV's input."""
     return round_f64_to(rmsnorm(x, x_dtype, gamma, eps), x_dtype)
+
+
+def rms_factor(x, x_dtype: str, eps: float) -> np.ndarray:
+    """fp64 r[b] = 1 / sqrt(mean_k x[b, k]^2 + eps) for stored x [B, K]."""
+    x64 = storage_to_f64(x, x_dtype)
+    if x64.ndim == 1:
+        x64 = x64[None, :]
+    return 1.0 / np.sqrt(np.mean(x64 * x64, axis=1) + float(np.float32(eps)))
+
+
+def gamma_stored(x, x_dtype: str, gamma) -> np.ndarray:
+    """RN_T(x[b, k] * gamma[k]) in stored form: what the fused product stages."""
+    x64 = storage_to_f64(x, x_dtype)
+    if x64.ndim == 1:
+        x64 = x64[None, :]
+    g64 = storage_to_f64(gamma, x_dtype).reshape(-1)
+    return round_f64_to(x64 * g64[None, :], x_dtype)

@@ -29,6 +29,7 @@ def test_library_exports_every_header_function(lib):
             "qmv_quantize_affine", "qmv_quantize_mxfp4", "qmv_quantize_mxfp8",
             "qmv_quantize_nvfp4", "qmv_moe_gate_up_swiglu", "qmv_moe_down_reduce", "qmv_fp_block",
             "qmv_qvm", "qmv_qvm_workspace_bytes", "qmv_qmm", "qmv_qmm_workspace_bytes",
+            "qmv_rmsnorm_qmv",
             "qmv_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -289,3 +290,24 @@ def test_qmm_split_rule(lib):
         if s > 1:
             per = -(-nk // s)
             assert per >= 8 and (s - 1) * per < nk
+
+
+def test_rmsnorm_qmv_validation(lib):
+    f = lib.qmv_rmsnorm_qmv
+    G = V(0x180000)
+    wt = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 1, 300, 1024, 0x20000, 0x30000, None, None)
+    assert f(None, 2, ctypes.byref(wt), 9, X, G, 1e-6, Y) == UNSUP          # B > 8
+    assert f(None, 2, ctypes.byref(wt), -1, X, G, 1e-6, Y) == INVAL
+    assert f(None, 2, ctypes.byref(wt), 2, X, G, -1.0, Y) == INVAL          # eps < 0
+    assert f(None, 2, ctypes.byref(wt), 2, X, G, float("nan"), Y) == INVAL
+    assert f(None, 2, ctypes.byref(wt), 2, X, G, float("inf"), Y) == INVAL
+    assert f(None, 2, ctypes.byref(wt), 2, X, None, 1e-6, Y) == INVAL       # gamma missing
+    assert f(None, 2, ctypes.byref(wt), 2, X, V(0x180008), 1e-6, Y) == MISAL
+    assert f(None, 2, ctypes.byref(wt), 2, X, G, 1e-6, X) == INVAL          # x and y overlap
+    assert f(None, 2, ctypes.byref(wt), 2, X, Y, 1e-6, Y) == INVAL          # gamma and y overlap
+    sb = bmv.QmvWeights(5, 14, 64, 1, 300, 1024, 0x20000, 0x30000, None, None)
+    assert f(None, 2, ctypes.byref(sb), 2, X, G, 1e-6, Y) == UNSUP
+    two = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 2, 300, 1024, 0x20000, 0x30000, None, None)
+    assert f(None, 2, ctypes.byref(two), 2, X, G, 1e-6, Y) == INVAL
+    assert f(None, 2, ctypes.byref(wt), 0, X, G, 1e-6, Y) == OK             # B == 0
+    assert f(None, 2, None, 2, X, G, 1e-6, Y) == INVAL

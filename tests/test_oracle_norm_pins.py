@@ -59,3 +59,45 @@ def test_stored_rounding_is_round_to_nearest():
     st = oracle.storage_to_f64(oracle.rmsnorm_stored(x, "bf16", g, 1e-6), "bf16")
     ulp = oracle.ulp_of(oracle.rmsnorm_stored(x, "bf16", g, 1e-6), "bf16")
     assert np.all(np.abs(st - xn) <= ulp / 2)
+
+
+def test_rms_factor_closed_forms():
+    # (3, 4): r = 1 / sqrt(12.5); a constant row c with eps: 1 / sqrt(c^2 + eps)
+    r = oracle.rms_factor(np.array([[3.0, 4.0], [0.5, 0.5]], np.float32), "f32", 0.0)
+    assert r[0] == pytest.approx(1.0 / math.sqrt(12.5), rel=1e-15)
+    assert r[1] == pytest.approx(2.0, rel=1e-15)
+    r = oracle.rms_factor(np.full((1, 32), 0.5, np.float32), "f32", 0.25)
+    assert r[0] == pytest.approx(1.0 / math.sqrt(0.5), rel=1e-15)
+
+
+def test_rms_factor_times_gamma_product_is_the_norm():
+    # r * (x * gamma) reproduces the plain RMSNorm row (to fp64 rounding)
+    rng = np.random.default_rng(8)
+    x = rng.normal(size=(2, 64)).astype(np.float32)
+    g = rng.uniform(0.5, 1.5, size=64).astype(np.float32)
+    xn = oracle.rmsnorm(x, "f32", g, 1e-4)
+    r = oracle.rms_factor(x, "f32", 1e-4)
+    assert np.allclose(xn, r[:, None] * x.astype(np.float64) * g.astype(np.float64), rtol=1e-15)
+
+
+def test_gamma_stored_identity_and_powers_of_two():
+    rng = np.random.default_rng(9)
+    x = oracle.round_f64_to(rng.normal(size=(2, 32)), "bf16")
+    one = oracle.round_f64_to(np.ones(32), "bf16")
+    assert np.array_equal(oracle.gamma_stored(x, "bf16", one), x)
+    four = oracle.round_f64_to(np.full(32, 4.0), "bf16")
+    assert np.array_equal(oracle.storage_to_f64(oracle.gamma_stored(x, "bf16", four), "bf16"),
+                          4.0 * oracle.storage_to_f64(x, "bf16"))
+
+
+def test_gamma_stored_matches_torch_rounding():
+    # the product of two bf16 values is exact in fp32; torch's fp32 -> bf16
+    # conversion (round to nearest even) must give the same stored values
+    import torch
+    rng = np.random.default_rng(10)
+    xf = torch.from_numpy(rng.normal(size=(3, 64)).astype(np.float32)).to(torch.bfloat16)
+    gf = torch.from_numpy(rng.uniform(0.3, 3.0, size=64).astype(np.float32)).to(torch.bfloat16)
+    want = (xf.float() * gf.float()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    x = xf.view(torch.int16).numpy().view(np.uint16)
+    g = gf.view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.gamma_stored(x, "bf16", g), want)
