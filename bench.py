@@ -233,7 +233,7 @@ class QmmRunner:
         self.y = torch.empty((M, c.N), dtype=self.x.dtype, device="cuda:0")
         self.M = M
         self.dt = {"f16": 1, "bf16": 2}[c.dtype]
-        self.need = int(self.lib.qmv_qmm_workspace_bytes(M, c.K, c.N))
+        self.need = int(self.lib.qmv_qmm_workspace_bytes(M, c.K, c.N, self.wts[0].format))
         self.ws = torch.empty((max(self.need, 4) // 4,), dtype=torch.float32, device="cuda:0")
         # partials written and read back when K is split
         self.bytes = per + 2 * M * (c.K + c.N) + 2 * self.need

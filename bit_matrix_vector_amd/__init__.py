@@ -116,7 +116,7 @@ def load() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.qmv_qvm_workspace_bytes.argtypes = [i64, i64, i64]
     lib.qmv_qvm_workspace_bytes.restype = ctypes.c_size_t
-    lib.qmv_qmm_workspace_bytes.argtypes = [i64, i64, i64]
+    lib.qmv_qmm_workspace_bytes.argtypes = [i64, i64, i64, i32]
     lib.qmv_qmm_workspace_bytes.restype = ctypes.c_size_t
     lib.qmv_packed_row_bytes.argtypes = [i32, i32, i64]
     lib.qmv_packed_row_bytes.restype = i64
@@ -378,7 +378,7 @@ def qmv_qmm(x, weights: QmvWeights, y=None, workspace=None):
     if y is None:
         y = torch.empty((M, weights.N), dtype=x.dtype, device=x.device)
     _dev(y, "y", x.dtype)
-    need = int(load().qmv_qmm_workspace_bytes(M, weights.K, weights.N))
+    need = int(load().qmv_qmm_workspace_bytes(M, weights.K, weights.N, weights.format))
     if workspace is None and need > 0:
         workspace = torch.empty((need // 4,), dtype=torch.float32, device=x.device)
     ws_ptr = _ptr(workspace) if workspace is not None else None

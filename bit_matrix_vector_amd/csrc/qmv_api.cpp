@@ -399,9 +399,9 @@ qmv_status_t qmv_rmsnorm_qmv(void* stream, int dtype, const qmv_weights_t* wt, i
     return launch_status(qmv::launch_qmv_norm(lp, na, stream), fn);
 }
 
-size_t qmv_qmm_workspace_bytes(int64_t M, int64_t K, int64_t N) {
+size_t qmv_qmm_workspace_bytes(int64_t M, int64_t K, int64_t N, int format) {
     if (M <= 0 || K <= 0 || N <= 0) return 0;
-    const int s = qmv::qmm_splits(M, K, N);
+    const int s = qmv::qmm_splits(M, K, N, format);
     return s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
@@ -441,7 +441,7 @@ qmv_status_t qmv_qmm(void* stream, int dtype, const qmv_weights_t* wt, int64_t M
         const uintptr_t ys = (uintptr_t)y, ye = ys + (uintptr_t)(M * wt->N * tb);
         if (xs < ye && ys < xe) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: x and y overlap", fn);
     }
-    const size_t need = qmv_qmm_workspace_bytes(M, wt->K, wt->N);
+    const size_t need = qmv_qmm_workspace_bytes(M, wt->K, wt->N, wt->format);
     if (need > 0) {
         QMV_TRY(check_ptr(fn, "workspace", workspace, true, 4));
         if (workspace_bytes < need)
@@ -455,7 +455,7 @@ qmv_status_t qmv_qmm(void* stream, int dtype, const qmv_weights_t* wt, int64_t M
     q.gscale = wt->format == QMV_NVFP4 ? wt->global_scale : nullptr;
     q.y = y;
     q.ws = static_cast<float*>(workspace);
-    q.splits = qmv::qmm_splits(M, wt->K, wt->N);
+    q.splits = qmv::qmm_splits(M, wt->K, wt->N, wt->format);
     return launch_status(qmv::launch_qmm(q, stream), fn);
 }
 

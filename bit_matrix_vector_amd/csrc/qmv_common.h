@@ -134,11 +134,20 @@ struct QmmParams {
     int splits;   // K slices split over blocks (1 = none)
 };
 int launch_qmm(const QmmParams& q, void* stream);
-// K splits of a qmm launch: none once the 64 x 128 output tiles reach 256
-// (one per compute unit); else enough to reach about 512 blocks, at most 8
-// and with at least 8 slices of 64 codes each. Depends on M, K and N alone.
-inline int qmm_splits(int64_t M, int64_t K, int64_t N) {
-    const int64_t tiles = ((N + 127) / 128) * ((M + 63) / 64);
+// Rows of a qmm block tile: 128 when 128-row tiles alone give at least 256
+// tiles (one per compute unit), else 64 (affine codes: always 64, their group
+// accumulators would double the registers).
+inline int qmm_block_rows(int64_t M, int64_t N, int format) {
+    const int64_t tiles128 = ((M + 127) / 128) * ((N + 127) / 128);
+    return format != 0 && M > 64 && tiles128 >= 256 ? 128 : 64;
+}
+// K splits of a qmm launch: none once the output tiles (block rows x 128)
+// reach 256 (one per compute unit); else enough to reach about 512 blocks, at
+// most 8 and with at least 8 slices of 64 codes each. Depends on M, K, N and
+// the format.
+inline int qmm_splits(int64_t M, int64_t K, int64_t N, int format) {
+    const int64_t bm = qmm_block_rows(M, N, format);
+    const int64_t tiles = ((N + 127) / 128) * ((M + bm - 1) / bm);
     const int64_t nk = (K + 63) / 64;
     if (tiles <= 0 || tiles >= 256) return 1;
     int64_t s = (512 + tiles - 1) / tiles;

@@ -5,10 +5,12 @@
 // "quantized (affine_qmv / qvm / qmm)": the M-batched prefill product).
 // Compiled once per 16-bit activation type (QMM_DT: bf16 or f16).
 //
-// A block computes a 64 x 128 tile of y over K in slices of 64 codes. Per
-// slice it copies the x tile into LDS and dequantizes the W tile into LDS as
-// the activation type, one 32-code unit per thread; its four waves (2 x 2)
-// then each run 2 x 4 32x32x16 MFMAs with fp32 accumulators. The x and W
+// A block computes a (64 * MT) x 128 tile of y over K in slices of 64 codes
+// (MT = 2 when 128-row tiles still give one per compute unit, except for
+// affine codes, whose group accumulators would double the registers). Per slice it copies the x tile
+// into LDS and dequantizes the W tile into LDS as the activation type, one
+// 32-code unit per thread; its four waves (2 x 2) then each run MT x 2 x 4
+// 32x32x16 MFMAs with fp32 accumulators. The x and W
 // bytes (and scales) of the next four slices are in flight in a register
 // ring while a slice is computed. When the output tiles alone are too few to
 // fill the chip, the K slices are split over blocks (grid z): each split
@@ -38,7 +40,6 @@
 namespace qmv {
 namespace {
 
-constexpr int kBM = 64;
 constexpr int kBN = 128;
 constexpr int kBK = 64;
 constexpr int kLd = kBK + 8;   // LDS row stride in elements (16 bytes of padding)
@@ -130,7 +131,8 @@ __device__ inline void dequant_unit(const uint32_t (&w)[Fmt<FMT, BITS>::kWords],
 }
 
 
-template <int DT, int FMT, int BITS>
+// MT: 32-row sub-tiles per wave, so the block tile is (64 * MT) x 128
+template <int DT, int FMT, int BITS, int MT>
 __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
     using F = Fmt<FMT, BITS>;
     using S = typename Store<DT>::S;
@@ -140,6 +142,8 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
     constexpr bool kAffine = FMT == FMT_AFFINE;
     constexpr int kSpans = kAffine ? 2 : 1;
     constexpr int kDepth = 4;   // slices in flight per block (a register ring)
+    constexpr int kBM = 64 * MT;
+    constexpr int kXH = 2 * MT;  // x chunks per thread and slice
 
     __shared__ __align__(16) uint16_t xs[kBM * kLd];
     __shared__ __align__(16) uint16_t wsm[kBN * kLd];
@@ -163,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
     const S* scs = static_cast<const S*>(q.scales);
     const S* bis = static_cast<const S*>(q.biases);
 
-    // loaders: x rows tid/8 and tid/8 + 32, 16-byte chunk tid%8 of the slice;
+    // loaders: x rows tid/8 + 32 h (h < kXH), 16-byte chunk tid%8 of the slice;
     // W row tid/2 of the tile (clamped to N - 1), unit tid%2 of the slice
     const int xr = tid >> 3, xc = tid & 7;
     const int wr = tid >> 1, wu = tid & 1;
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
     }
 
     struct Slice {
-        v4u x[2];
+        v4u x[kXH];
         uint32_t w[W];
         typename F::Raw s;
         uint32_t aff[2][kSpans][2];   // affine: raw scale, bias per column tile and span
@@ -186,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
     auto load_slice = [&](Slice& b, int kb) __attribute__((always_inline)) {
         const int64_t k0 = (int64_t)kb * kBK;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
+        for (int h = 0; h < kXH; ++h) {
             const int64_t m = m0 + xr + 32 * h;
             const int64_t k = k0 + xc * 8;
             if (m < M && k < K) b.x[h] = *reinterpret_cast<const v4u*>(x + m * K + k);
@@ -215,13 +219,13 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
     };
     auto store_slice = [&](const Slice& b) __attribute__((always_inline)) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < kXH; ++h)
             *reinterpret_cast<v4u*>(xs + (xr + 32 * h) * kLd + xc * 8) = b.x[h];
         if constexpr (kAffine) {
             // sum of this thread's 8 x values, then over the 4 threads of a
             // 32-code half (lanes differing in bits 0..1), in a fixed order
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < kXH; ++h) {
                 const uint32_t w4[4] = {b.x[h].x, b.x[h].y, b.x[h].z, b.x[h].w};
                 float t = 0.0f;
 #pragma unroll
@@ -243,13 +247,17 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
         dequant_unit<DT, FMT, BITS>(b.w, b.s, reinterpret_cast<v4u*>(dst));
     };
 
-    f32x16 acc[2], tmp[2];
+    // accumulators per (M sub-tile, N sub-tile); affine keeps a second set
+    // for the current group
+    f32x16 acc[MT][2], tmp[MT][2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int tm = 0; tm < MT; ++tm)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[t][i] = tmp[t][i] = 0.0f;
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[tm][t][i] = tmp[tm][t][i] = 0.0f;
 
-    const uint16_t* arow = xs + (32 * wm + ln) * kLd + 8 * (lane >> 5);
+    const uint16_t* arow = xs + (32 * MT * wm + ln) * kLd + 8 * (lane >> 5);
     const uint16_t* brow0 = wsm + (64 * wn + ln) * kLd + 8 * (lane >> 5);
     const uint16_t* brow1 = brow0 + 32 * kLd;
     // affine: a slice's scales and biases per column tile and span, as fp32
@@ -273,21 +281,24 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
     // slice; larger groups: SP = 0 and the whole slice)
     auto epilogue = [&](const Aff& af, auto sp_c, bool whole) __attribute__((always_inline)) {
         constexpr int SP = decltype(sp_c)::value;
-        float sxv[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int ml = 32 * wm + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            sxv[i] = whole ? sx[0][ml] + sx[1][ml] : sx[SP][ml];
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const float s = af.s[t][SP];
-            const float bb = af.b[t][SP];
+        for (int tm = 0; tm < MT; ++tm) {
+            float sxv[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                acc[t][i] = fmaf(s, tmp[t][i], acc[t][i]);
-                acc[t][i] = fmaf(bb, sxv[i], acc[t][i]);
-                tmp[t][i] = 0.0f;
+                const int ml = 32 * MT * wm + 32 * tm + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                sxv[i] = whole ? sx[0][ml] + sx[1][ml] : sx[SP][ml];
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const float s = af.s[t][SP];
+                const float bb = af.b[t][SP];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    acc[tm][t][i] = fmaf(s, tmp[tm][t][i], acc[tm][t][i]);
+                    acc[tm][t][i] = fmaf(bb, sxv[i], acc[tm][t][i]);
+                    tmp[tm][t][i] = 0.0f;
+                }
             }
         }
     };
@@ -296,12 +307,18 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
         const int64_t k0 = (int64_t)kb * kBK;
         static_for<0, 4>([&](auto ks_c) {
             constexpr int ks = decltype(ks_c)::value;
-            const V8 a = *reinterpret_cast<const V8*>(arow + 16 * ks);
+            V8 a[MT];
+#pragma unroll
+            for (int tm = 0; tm < MT; ++tm)
+                a[tm] = *reinterpret_cast<const V8*>(arow + 32 * tm * kLd + 16 * ks);
             const V8 b0 = *reinterpret_cast<const V8*>(brow0 + 16 * ks);
             const V8 b1 = *reinterpret_cast<const V8*>(brow1 + 16 * ks);
             if constexpr (kAffine) {
-                tmp[0] = Mma<DT>::run(a, b0, tmp[0]);
-                tmp[1] = Mma<DT>::run(a, b1, tmp[1]);
+#pragma unroll
+                for (int tm = 0; tm < MT; ++tm) {
+                    tmp[tm][0] = Mma<DT>::run(a[tm], b0, tmp[tm][0]);
+                    tmp[tm][1] = Mma<DT>::run(a[tm], b1, tmp[tm][1]);
+                }
                 if (q.group == 32) {
                     if constexpr ((ks & 1) == 1) {
                         if (k0 + 32 * (ks >> 1) < K)
@@ -311,8 +328,11 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
                     epilogue(af, std::integral_constant<int, 0>{}, true);
                 }
             } else {
-                acc[0] = Mma<DT>::run(a, b0, acc[0]);
-                acc[1] = Mma<DT>::run(a, b1, acc[1]);
+#pragma unroll
+                for (int tm = 0; tm < MT; ++tm) {
+                    acc[tm][0] = Mma<DT>::run(a[tm], b0, acc[tm][0]);
+                    acc[tm][1] = Mma<DT>::run(a[tm], b1, acc[tm][1]);
+                }
             }
         });
     };
@@ -350,17 +370,21 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
 
     const float gs = (FMT == FMT_NVFP4 && q.gscale) ? *q.gscale : 1.0f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-        const int64_t n = n0 + 64 * wn + 32 * t + ln;
-        if (n >= N) continue;
+    for (int tm = 0; tm < MT; ++tm) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int64_t m = m0 + 32 * wm + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            if (m >= M) continue;
-            if (q.splits == 1)
-                static_cast<S*>(q.y)[m * N + n] = Store<DT>::from_f32(acc[t][i] * gs);
-            else
-                q.ws[((int64_t)blockIdx.z * M + m) * N + n] = acc[t][i];
+        for (int t = 0; t < 2; ++t) {
+            const int64_t n = n0 + 64 * wn + 32 * t + ln;
+            if (n >= N) continue;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int64_t m =
+                    m0 + 32 * MT * wm + 32 * tm + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                if (m >= M) continue;
+                if (q.splits == 1)
+                    static_cast<S*>(q.y)[m * N + n] = Store<DT>::from_f32(acc[tm][t][i] * gs);
+                else
+                    q.ws[((int64_t)blockIdx.z * M + m) * N + n] = acc[tm][t][i];
+            }
         }
     }
 }
@@ -390,11 +414,21 @@ __global__ __launch_bounds__(256) void qmm_reduce_kernel(QmmParams q) {
 
 template <int DT, int FMT, int BITS>
 int launch_qmm_f(const QmmParams& q, hipStream_t st) {
-    const dim3 grid((unsigned)((q.N + kBN - 1) / kBN), (unsigned)((q.M + kBM - 1) / kBM),
+    const int bm = qmm_block_rows(q.M, q.N, q.format);
+    const dim3 grid((unsigned)((q.N + kBN - 1) / kBN), (unsigned)((q.M + bm - 1) / bm),
                     (unsigned)q.splits);
     int glog2 = 0;
     if (FMT == FMT_AFFINE) glog2 = q.group == 128 ? 2 : (q.group == 64 ? 1 : 0);
-    hipLaunchKernelGGL((qmm_kernel<DT, FMT, BITS>), grid, dim3(kThreads), 0, st, q, glog2);
+    if constexpr (FMT != FMT_AFFINE) {
+        if (bm == 128)
+            hipLaunchKernelGGL((qmm_kernel<DT, FMT, BITS, 2>), grid, dim3(kThreads), 0, st, q,
+                               glog2);
+        else
+            hipLaunchKernelGGL((qmm_kernel<DT, FMT, BITS, 1>), grid, dim3(kThreads), 0, st, q,
+                               glog2);
+    } else {
+        hipLaunchKernelGGL((qmm_kernel<DT, FMT, BITS, 1>), grid, dim3(kThreads), 0, st, q, glog2);
+    }
     if (q.splits > 1) {
         const int64_t n = q.M * q.N;
         hipLaunchKernelGGL((qmm_reduce_kernel<DT>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,

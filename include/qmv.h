@@ -249,13 +249,13 @@ qmv_status_t qmv_rmsnorm_qmv(void* stream, int dtype, const qmv_weights_t* w, in
  * while the value lies in f16's normal range); affine codes enter as integers
  * and scale and bias are applied per group in fp32 (s * sum x q + b * sum x);
  * NVFP4's global scale multiplies the fp32 result; y is rounded to dtype once.
- * workspace: caller-owned device memory of qmv_qmm_workspace_bytes(M, K, N)
+ * workspace: caller-owned device memory of qmv_qmm_workspace_bytes(M, K, N, format)
  * bytes (4-byte aligned; may be NULL when that is 0). When M and N give too
  * few output tiles to fill the GPU, K is split over blocks that write fp32
  * partial sums there and a second kernel adds them in split order, so
  * repeated calls give identical results; calls that share a workspace must
  * not overlap. */
-size_t qmv_qmm_workspace_bytes(int64_t M, int64_t K, int64_t N);
+size_t qmv_qmm_workspace_bytes(int64_t M, int64_t K, int64_t N, int format);
 qmv_status_t qmv_qmm(void* stream, int dtype, const qmv_weights_t* w, int64_t M, const void* x,
                      void* y, void* workspace, size_t workspace_bytes);
 

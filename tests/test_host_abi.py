@@ -253,9 +253,9 @@ def test_qvm_split_bounds(lib):
 def test_qmm_validation(lib):
     wt = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 1, 300, 1024, 0x20000, 0x30000, None, None)
     ws = V(0xA0000)
-    need = lib.qmv_qmm_workspace_bytes(16, 1024, 300)
+    need = lib.qmv_qmm_workspace_bytes(16, 1024, 300, bmv.QMV_MXFP4)
     assert need > 0 and need % (16 * 300 * 4) == 0          # few tiles: K is split
-    assert lib.qmv_qmm_workspace_bytes(4096, 4096, 14336) == 0  # many tiles: no split
+    assert lib.qmv_qmm_workspace_bytes(4096, 4096, 14336, bmv.QMV_MXFP4) == 0  # many tiles
     assert lib.qmv_qmm(None, 0, ctypes.byref(wt), 16, X, Y, ws, need) == UNSUP    # f32
     assert lib.qmv_qmm(None, 7, ctypes.byref(wt), 16, X, Y, ws, need) == INVAL    # not a dtype
     assert lib.qmv_qmm(None, 2, ctypes.byref(wt), -1, X, Y, ws, need) == INVAL
@@ -276,38 +276,21 @@ def test_qmm_validation(lib):
 
 
 def test_qmm_split_rule(lib):
-    # splits only when the output tiles are fewer than 256, at most 8, each
-    # split at least 8 slices of 64 codes, none empty
-    for M, K, N in ((32, 4096, 14336), (9, 1056, 300), (256, 4096, 4096), (1, 512, 64),
-                    (64, 8192, 4096), (2000, 4096, 14336)):
-        ws = lib.qmv_qmm_workspace_bytes(M, K, N)
-        s = ws // (M * N * 4) if ws else 1
-        tiles = -(-N // 128) * -(-M // 64)
-        nk = -(-K // 64)
-        assert 1 <= s <= 8
-        if tiles >= 256:
-            assert s == 1
-        if s > 1:
-            per = -(-nk // s)
-            assert per >= 8 and (s - 1) * per < nk
-
-
-def test_rmsnorm_qmv_validation(lib):
-    f = lib.qmv_rmsnorm_qmv
-    G = V(0x180000)
-    wt = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 1, 300, 1024, 0x20000, 0x30000, None, None)
-    assert f(None, 2, ctypes.byref(wt), 9, X, G, 1e-6, Y) == UNSUP          # B > 8
-    assert f(None, 2, ctypes.byref(wt), -1, X, G, 1e-6, Y) == INVAL
-    assert f(None, 2, ctypes.byref(wt), 2, X, G, -1.0, Y) == INVAL          # eps < 0
-    assert f(None, 2, ctypes.byref(wt), 2, X, G, float("nan"), Y) == INVAL
-    assert f(None, 2, ctypes.byref(wt), 2, X, G, float("inf"), Y) == INVAL
-    assert f(None, 2, ctypes.byref(wt), 2, X, None, 1e-6, Y) == INVAL       # gamma missing
-    assert f(None, 2, ctypes.byref(wt), 2, X, V(0x180008), 1e-6, Y) == MISAL
-    assert f(None, 2, ctypes.byref(wt), 2, X, G, 1e-6, X) == INVAL          # x and y overlap
-    assert f(None, 2, ctypes.byref(wt), 2, X, Y, 1e-6, Y) == INVAL          # gamma and y overlap
-    sb = bmv.QmvWeights(5, 14, 64, 1, 300, 1024, 0x20000, 0x30000, None, None)
-    assert f(None, 2, ctypes.byref(sb), 2, X, G, 1e-6, Y) == UNSUP
-    two = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 2, 300, 1024, 0x20000, 0x30000, None, None)
-    assert f(None, 2, ctypes.byref(two), 2, X, G, 1e-6, Y) == INVAL
-    assert f(None, 2, ctypes.byref(wt), 0, X, G, 1e-6, Y) == OK             # B == 0
-    assert f(None, 2, None, 2, X, G, 1e-6, Y) == INVAL
+    # splits only when the output tiles (128 or 64 rows x 128 columns) are
+    # fewer than 256, at most 8, each split at least 8 slices of 64 codes,
+    # none empty; affine codes always take 64-row tiles
+    for fmt in (bmv.QMV_MXFP4, bmv.QMV_AFFINE):
+        for M, K, N in ((32, 4096, 14336), (9, 1056, 300), (256, 4096, 4096), (1, 512, 64),
+                        (64, 8192, 4096), (2000, 4096, 14336), (256, 4096, 14336)):
+            ws = lib.qmv_qmm_workspace_bytes(M, K, N, fmt)
+            s = ws // (M * N * 4) if ws else 1
+            t128 = -(-M // 128) * -(-N // 128)
+            bm = 128 if M > 64 and fmt != bmv.QMV_AFFINE and t128 >= 256 else 64
+            tiles = -(-N // 128) * -(-M // bm)
+            nk = -(-K // 64)
+            assert 1 <= s <= 8
+            if tiles >= 256:
+                assert s == 1
+            if s > 1:
+                per = -(-nk // s)
+                assert per >= 8 and (s - 1) * per < nk
