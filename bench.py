@@ -251,6 +251,48 @@ class QmmRunner:
         self.keep = self.wts = None
 
 
+class GatherQmmRunner:
+    """gather_qmm over the MoE workload's gate/up stack (64 experts, hidden
+    4096, ffn 1536) with `tokens` x top-8 slots sorted by expert, over
+    rotating copies of the stack. Bytes: the distinct experts' matrices once,
+    x rows per slot, y; flops 2 slots N K."""
+
+    def __init__(self, bmv, tokens: int, min_bytes: int = 1 << 30):
+        import numpy as np
+        import torch
+        import workloads
+        self.lib = bmv.load()
+        m = workloads.config5("mxfp4", "gate_up", tokens=tokens)
+        order = np.argsort(m.rhs, kind="stable")
+        lhs, rhs = m.lhs[order], m.rhs[order]
+        w0, s0 = _dev(m.w), _dev(m.scales)
+        per = w0.nbytes + s0.nbytes
+        self.copies = max(2, -(-min_bytes // per))
+        self.keep = [(w0, s0)] + [(w0.clone(), s0.clone()) for _ in range(self.copies - 1)]
+        self.wts = [bmv.make_weights("mxfp4", w, sc, None, K=m.K, bits=4, group_size=32)
+                    for (w, sc) in self.keep]
+        self.x = _dev(m.x, "bf16")
+        self.lhs = torch.from_numpy(lhs.view(np.int32).copy()).cuda()
+        self.rhs = torch.from_numpy(rhs.view(np.int32).copy()).cuda()
+        self.n_slots = int(lhs.size)
+        self.y = torch.empty((self.n_slots, m.N), dtype=torch.bfloat16, device="cuda:0")
+        d = len(np.unique(rhs))
+        self.bytes = d * (per // m.E) + self.n_slots * 2 * (m.K + m.N)
+        self.flops = 2 * self.n_slots * m.N * m.K
+        self.n_x = m.x.shape[0]
+
+    def call(self, i: int, stream) -> None:
+        vp = ctypes.c_void_p
+        st = self.lib.gather_qmm(stream, 2, ctypes.byref(self.wts[i % self.copies]),
+                                 vp(self.x.data_ptr()), self.n_x, vp(self.lhs.data_ptr()),
+                                 vp(self.rhs.data_ptr()), self.n_slots, vp(self.y.data_ptr()))
+        if st != 0:
+            raise RuntimeError(self.lib.qmv_last_error().decode())
+
+    def free(self):
+        self.keep = self.wts = None
+
+
 def workloads_x(n: int, dtype: str):
     import workloads
     return workloads.to_storage(workloads.rng_for(8, "bench-qvm-x").normal(size=(1, n)), dtype)
@@ -833,6 +875,14 @@ def main() -> int:
             cr["tflops"] = round(r.flops / (cr["us_per_call"] * 1e-6) / 1e12, 1)
             cases.append(cr)
             print(f"[bench] {name}: {json.dumps(cr)}", file=sys.stderr, flush=True)
+        r = GatherQmmRunner(bmv, 256)
+        cr = time_case(r, max(100, args.steps // 10), args.warmup)
+        r.free()
+        cr["case"] = "gather_qmm mxfp4 MoE gate/up (64 experts, K=4096, N=1536), 2048 slots sorted"
+        cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
+        cr["tflops"] = round(r.flops / (cr["us_per_call"] * 1e-6) / 1e12, 1)
+        cases.append(cr)
+        print(f"[bench] {cr['case']}: {json.dumps(cr)}", file=sys.stderr, flush=True)
         for fmt in ("mxfp4", "nvfp4", "mxfp8", "affine4"):
             r = QuantRunner(bmv, fmt)
             cr = time_case(r, max(100, args.steps // 10), 10)

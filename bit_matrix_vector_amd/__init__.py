@@ -105,6 +105,7 @@ def load() -> ctypes.CDLL:
         "qmv_qvm": [vp, i32, ctypes.POINTER(QmvWeights), i64, vp, vp, vp, ctypes.c_size_t],
         "qmv_qmm": [vp, i32, ctypes.POINTER(QmvWeights), i64, vp, vp, vp, ctypes.c_size_t],
         "qmv_rmsnorm_qmv": [vp, i32, ctypes.POINTER(QmvWeights), i64, vp, vp, ctypes.c_float, vp],
+        "gather_qmm": [vp, i32, ctypes.POINTER(QmvWeights), vp, i64, vp, vp, i64, vp],
         "qmv_quantize_affine": [vp, i32, i64, i64, vp, i32, i32, vp, vp, vp],
         "qmv_quantize_mxfp4": [vp, i32, i64, i64, vp, vp, vp],
         "qmv_quantize_mxfp8": [vp, i32, i64, i64, vp, vp, vp],
@@ -138,7 +139,7 @@ def header_functions() -> list[str]:
         if fn.endswith(".h"):
             text = open(os.path.join(inc, fn)).read()
             text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-            names.update(re.findall(r"\b(qmv_\w+|gather_qmv)\s*\(", text))
+            names.update(re.findall(r"\b(qmv_\w+|gather_qm[vm])\s*\(", text))
     return sorted(names)
 
 
@@ -302,6 +303,24 @@ def gather_qmv(x, weights: QmvWeights, lhs_indices, rhs_indices, y=None):
     _check(load().gather_qmv(_stream(x.device), _dtype_code(x), ctypes.byref(weights), _ptr(x),
                              x.shape[0], _ptr(lhs_indices), _ptr(rhs_indices), n_slots,
                              _ptr(y)))
+    return y
+
+
+def gather_qmm(x, weights: QmvWeights, lhs_indices, rhs_indices, y=None):
+    """y[s] = W[rhs[s]] . x[lhs[s]] for many slots on the matrix cores (bf16 or
+    f16; indices: uint32 stored in int32 tensors; sorted rhs is fastest)."""
+    torch = _torch()
+    x = _dev(x, "x")
+    _dev(lhs_indices, "lhs_indices", torch.int32)
+    _dev(rhs_indices, "rhs_indices", torch.int32)
+    n_slots = lhs_indices.numel()
+    if rhs_indices.numel() != n_slots:
+        raise ValueError("lhs_indices and rhs_indices differ in length")
+    if y is None:
+        y = torch.empty((n_slots, weights.N), dtype=x.dtype, device=x.device)
+    _dev(y, "y", x.dtype)
+    _check(load().gather_qmm(_stream(x.device), _dtype_code(x), ctypes.byref(weights), _ptr(x),
+                             x.shape[0], _ptr(lhs_indices), _ptr(rhs_indices), n_slots, _ptr(y)))
     return y
 
 

@@ -562,6 +562,57 @@ qmv_status_t gather_qmv(void* stream, int dtype, const qmv_weights_t* wt, const 
     return launch_status(qmv::launch_gather(lp, stream), fn);
 }
 
+qmv_status_t gather_qmm(void* stream, int dtype, const qmv_weights_t* wt, const void* x,
+                        int64_t n_x_rows, const uint32_t* lhs_indices,
+                        const uint32_t* rhs_indices, int64_t n_slots, void* y) {
+    const char* fn = "gather_qmm";
+    if (wt == nullptr) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: weights struct is NULL", fn);
+    if (n_slots < 0 || n_x_rows < 0 || wt->n_experts < 0)
+        return fail(QMV_ERR_INVALID_ARGUMENT, "%s: negative count", fn);
+    if (n_slots > (int64_t)65535 * 64 || wt->n_experts > 65534)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: n_slots or n_experts too large", fn);
+    QMV_TRY(check_common(fn, dtype, 1, wt->K, wt->N, 1));
+    if (dtype != QMV_BF16 && dtype != QMV_F16)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: activations must be bf16 or f16", fn);
+    qmv::LaunchParams lp{};
+    QMV_TRY(format_geometry(fn, wt->format, wt->bits, wt->group_size, wt->K, lp));
+    if (wt->format >= QMV_SB_E8M0)
+        return fail(QMV_ERR_UNSUPPORTED, "%s: takes the affine, MXFP4, NVFP4 and MXFP8 formats",
+                    fn);
+    if (n_slots == 0 || wt->N == 0) return QMV_OK;
+    const int tb = dtype_bytes(dtype);
+    QMV_TRY(check_ptr(fn, "y", y, true, tb));
+    if (wt->K == 0 || wt->n_experts == 0 || n_x_rows == 0)   // every row is empty or out of range
+        return launch_status(qmv::launch_zero_fill(y, n_slots * wt->N * tb, stream), fn);
+    QMV_TRY(check_ptr(fn, "lhs_indices", lhs_indices, true, 4));
+    QMV_TRY(check_ptr(fn, "rhs_indices", rhs_indices, true, 4));
+    QMV_TRY(check_ptr(fn, "x", x, true, 16));
+    QMV_TRY(check_ptr(fn, "w", wt->w, true, 16));
+    if (wt->format == QMV_AFFINE) {
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, true, tb));
+        QMV_TRY(check_ptr(fn, "biases", wt->biases, true, tb));
+    } else {
+        QMV_TRY(check_ptr(fn, "scales", wt->scales, true, scale_bytes(wt->format)));
+    }
+    QMV_TRY(check_ptr(fn, "global_scale", wt->global_scale, wt->global_scale != nullptr, 4));
+    {
+        const uintptr_t xs = (uintptr_t)x, xe = xs + (uintptr_t)(n_x_rows * wt->K * tb);
+        const uintptr_t ys = (uintptr_t)y, ye = ys + (uintptr_t)(n_slots * wt->N * tb);
+        if (xs < ye && ys < xe) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: x and y overlap", fn);
+    }
+    qmv::QmmParams q{};
+    q.dtype = dtype; q.format = wt->format; q.bits = lp.bits; q.group = lp.group;
+    q.M = n_slots; q.N = wt->N; q.K = wt->K; q.row_bytes = lp.row_bytes;
+    q.sc_per_row = lp.sc_per_row;
+    q.x = x; q.w = wt->w; q.scales = wt->scales; q.biases = wt->biases;
+    q.gscale = wt->format == QMV_NVFP4 ? wt->global_scale : nullptr;
+    q.y = y;
+    q.splits = 1;
+    q.lhs = lhs_indices; q.rhs = rhs_indices;
+    q.n_experts = wt->n_experts; q.n_x_rows = n_x_rows;
+    return launch_status(qmv::launch_qmm(q, stream), fn);
+}
+
 // ------------------------------- codecs ----------------------------------
 
 int64_t qmv_packed_row_bytes(int format, int bits, int64_t K) {

@@ -132,6 +132,12 @@ struct QmmParams {
     void* y;
     float* ws;    // [splits, M, N] fp32 partials when splits > 1
     int splits;   // K slices split over blocks (1 = none)
+    // gather (rhs != nullptr): M = slots, x row lhs[s], expert rhs[s] of
+    // n_experts stacked matrices; splits must be 1
+    const uint32_t* lhs;
+    const uint32_t* rhs;
+    int64_t n_experts;
+    int64_t n_x_rows;
 };
 int launch_qmm(const QmmParams& q, void* stream);
 // Rows of a qmm block tile: 128 when 128-row tiles alone give at least 256

@@ -131,8 +131,11 @@ __device__ inline void dequant_unit(const uint32_t (&w)[Fmt<FMT, BITS>::kWords],
 }
 
 
-// MT: 32-row sub-tiles per wave, so the block tile is (64 * MT) x 128
-template <int DT, int FMT, int BITS, int MT>
+// MT: 32-row sub-tiles per wave, so the block tile is (64 * MT) x 128.
+// GATHER: rows are routed slots (x row lhs[s], expert rhs[s]); the block runs
+// the K loop once per distinct expert of its tile, in increasing order, with
+// the x rows of other experts' slots zero, accumulating into the same tiles.
+template <int DT, int FMT, int BITS, int MT, bool GATHER>
 __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
     using F = Fmt<FMT, BITS>;
     using S = typename Store<DT>::S;
@@ -164,14 +167,23 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
     const int kb0 = (int)blockIdx.z * per;
     const int nks = (kb0 + per < nk ? kb0 + per : nk) - kb0;
     const S* x = static_cast<const S*>(q.x);
-    const S* scs = static_cast<const S*>(q.scales);
-    const S* bis = static_cast<const S*>(q.biases);
+    // the matrix of the current run (gather: of expert e), its scales and biases
+    const uint8_t* wcur = q.w;
+    const void* sccur = q.scales;
+    const void* bicur = q.biases;
 
     // loaders: x rows tid/8 + 32 h (h < kXH), 16-byte chunk tid%8 of the slice;
     // W row tid/2 of the tile (clamped to N - 1), unit tid%2 of the slice
     const int xr = tid >> 3, xc = tid & 7;
     const int wr = tid >> 1, wu = tid & 1;
     const int64_t wrow = n0 + wr < N ? n0 + wr : N - 1;
+    // x row of each of this thread's tile rows (-1: a row of zeros)
+    int64_t xrow[kXH];
+#pragma unroll
+    for (int h = 0; h < kXH; ++h) {
+        const int64_t m = m0 + xr + 32 * h;
+        xrow[h] = m < M ? m : -1;
+    }
     // affine: this lane's two output columns (clamped) for the scale loads
     int64_t ncol[2];
 #pragma unroll
@@ -191,17 +203,16 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
         const int64_t k0 = (int64_t)kb * kBK;
 #pragma unroll
         for (int h = 0; h < kXH; ++h) {
-            const int64_t m = m0 + xr + 32 * h;
             const int64_t k = k0 + xc * 8;
-            if (m < M && k < K) b.x[h] = *reinterpret_cast<const v4u*>(x + m * K + k);
+            if (xrow[h] >= 0 && k < K) b.x[h] = *reinterpret_cast<const v4u*>(x + xrow[h] * K + k);
             else b.x[h] = v4u{0u, 0u, 0u, 0u};
         }
         const int64_t u = (k0 >> 5) + wu;
         b.valid = u < units;
         const int64_t uc = b.valid ? u : units - 1;
-        load_words<W>(q.w + wrow * q.row_bytes + uc * kUnitBytes, b.w);
+        load_words<W>(wcur + wrow * q.row_bytes + uc * kUnitBytes, b.w);
         if constexpr (!kAffine) {
-            b.s = F::template load_raw<DT>(q.scales, q.biases, wrow, q.sc_per_row, uc, glog2);
+            b.s = F::template load_raw<DT>(sccur, bicur, wrow, q.sc_per_row, uc, glog2);
         } else {
 #pragma unroll
             for (int sp = 0; sp < kSpans; ++sp) {
@@ -211,8 +222,10 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
                 const int64_t g = kk / q.group;
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
-                    b.aff[t][sp][0] = Store<DT>::load_bits(scs + ncol[t] * q.sc_per_row + g);
-                    b.aff[t][sp][1] = Store<DT>::load_bits(bis + ncol[t] * q.sc_per_row + g);
+                    b.aff[t][sp][0] = Store<DT>::load_bits(static_cast<const S*>(sccur) +
+                                                           ncol[t] * q.sc_per_row + g);
+                    b.aff[t][sp][1] = Store<DT>::load_bits(static_cast<const S*>(bicur) +
+                                                           ncol[t] * q.sc_per_row + g);
                 }
             }
         }
@@ -337,36 +350,92 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
         });
     };
 
-    // ring of kDepth slices: slice it + d sits in ring[d]; every load is
-    // issued (clamped to the split's last slice) so the number in flight is
-    // the same on every path
-    Slice ring[kDepth];
-    static_for<0, kDepth>([&](auto d_c) {
-        constexpr int d = decltype(d_c)::value;
-        load_slice(ring[d], kb0 + (d < nks ? d : nks - 1));
-    });
-    int it = 0;
-    for (; it + kDepth <= nks; it += kDepth) {
+    // the K loop over this block's slices, for the current run
+    auto run_k = [&]() __attribute__((always_inline)) {
+        // ring of kDepth slices: slice it + d sits in ring[d]; every load is
+        // issued (clamped to the split's last slice) so the number in flight is
+        // the same on every path
+        Slice ring[kDepth];
         static_for<0, kDepth>([&](auto d_c) {
             constexpr int d = decltype(d_c)::value;
-            store_slice(ring[d]);
-            __syncthreads();
-            const Aff af = aff_of(ring[d]);
-            const int nxt = it + d + kDepth;
-            load_slice(ring[d], kb0 + (nxt < nks ? nxt : nks - 1));
-            compute(af, kb0 + it + d);
-            __syncthreads();
+            load_slice(ring[d], kb0 + (d < nks ? d : nks - 1));
         });
-    }
-    static_for<0, kDepth>([&](auto d_c) {
-        constexpr int d = decltype(d_c)::value;
-        if (it + d < nks) {
-            store_slice(ring[d]);
-            __syncthreads();
-            compute(aff_of(ring[d]), kb0 + it + d);
-            __syncthreads();
+        int it = 0;
+        for (; it + kDepth <= nks; it += kDepth) {
+            static_for<0, kDepth>([&](auto d_c) {
+                constexpr int d = decltype(d_c)::value;
+                store_slice(ring[d]);
+                __syncthreads();
+                const Aff af = aff_of(ring[d]);
+                const int nxt = it + d + kDepth;
+                load_slice(ring[d], kb0 + (nxt < nks ? nxt : nks - 1));
+                compute(af, kb0 + it + d);
+                __syncthreads();
+            });
         }
-    });
+        static_for<0, kDepth>([&](auto d_c) {
+            constexpr int d = decltype(d_c)::value;
+            if (it + d < nks) {
+                store_slice(ring[d]);
+                __syncthreads();
+                compute(aff_of(ring[d]), kb0 + it + d);
+                __syncthreads();
+            }
+        });
+    };
+
+    if constexpr (!GATHER) {
+        run_k();
+    } else {
+        // the tile's expert ids (ids >= n_experts, and rows past the end,
+        // never match); experts run in increasing order, each once
+        __shared__ uint32_t tile_e[kBM];
+        __shared__ uint32_t next_e;
+        constexpr uint32_t kNone = 0xFFFFFFFFu;
+        const int64_t S_ = M;
+        for (int r = tid; r < kBM; r += kThreads) {
+            const int64_t sl = m0 + r;
+            uint32_t e = kNone;
+            if (sl < S_) {
+                e = q.rhs[sl];
+                if ((int64_t)e >= q.n_experts) e = kNone;
+            }
+            tile_e[r] = e;
+        }
+        uint32_t lo = 0;
+        const int64_t estride_w = N * q.row_bytes;
+        const int64_t estride_s =
+            N * q.sc_per_row * (kAffine ? (int64_t)Store<DT>::kBytes : (int64_t)F::template elem_bytes<DT>());
+        for (;;) {
+            if (tid == 0) next_e = kNone;
+            __syncthreads();
+            for (int r = tid; r < kBM; r += kThreads) {
+                const uint32_t e = tile_e[r];
+                if (e != kNone && e >= lo) atomicMin(&next_e, e);
+            }
+            __syncthreads();
+            const uint32_t e = next_e;
+            __syncthreads();   // every thread has read next_e before it is reset
+            if (e == kNone) break;
+#pragma unroll
+            for (int h = 0; h < kXH; ++h) {
+                const int r = xr + 32 * h;
+                const int64_t sl = m0 + r;
+                int64_t xi = -1;
+                if (tile_e[r] == e) {
+                    const uint32_t l = q.lhs[sl];
+                    if ((int64_t)l < q.n_x_rows) xi = l;
+                }
+                xrow[h] = xi;
+            }
+            wcur = q.w + (int64_t)e * estride_w;
+            sccur = static_cast<const uint8_t*>(q.scales) + (int64_t)e * estride_s;
+            if constexpr (kAffine)
+                bicur = static_cast<const uint8_t*>(q.biases) + (int64_t)e * estride_s;
+            run_k();
+            lo = e + 1;
+        }
+    }
 
     const float gs = (FMT == FMT_NVFP4 && q.gscale) ? *q.gscale : 1.0f;
 #pragma unroll
@@ -412,8 +481,8 @@ __global__ __launch_bounds__(256) void qmm_reduce_kernel(QmmParams q) {
     static_cast<S*>(q.y)[i] = Store<DT>::from_f32(t);
 }
 
-template <int DT, int FMT, int BITS>
-int launch_qmm_f(const QmmParams& q, hipStream_t st) {
+template <int DT, int FMT, int BITS, bool GATHER>
+int launch_qmm_g(const QmmParams& q, hipStream_t st) {
     const int bm = qmm_block_rows(q.M, q.N, q.format);
     const dim3 grid((unsigned)((q.N + kBN - 1) / kBN), (unsigned)((q.M + bm - 1) / bm),
                     (unsigned)q.splits);
@@ -421,13 +490,14 @@ int launch_qmm_f(const QmmParams& q, hipStream_t st) {
     if (FMT == FMT_AFFINE) glog2 = q.group == 128 ? 2 : (q.group == 64 ? 1 : 0);
     if constexpr (FMT != FMT_AFFINE) {
         if (bm == 128)
-            hipLaunchKernelGGL((qmm_kernel<DT, FMT, BITS, 2>), grid, dim3(kThreads), 0, st, q,
-                               glog2);
+            hipLaunchKernelGGL((qmm_kernel<DT, FMT, BITS, 2, GATHER>), grid, dim3(kThreads), 0,
+                               st, q, glog2);
         else
-            hipLaunchKernelGGL((qmm_kernel<DT, FMT, BITS, 1>), grid, dim3(kThreads), 0, st, q,
-                               glog2);
+            hipLaunchKernelGGL((qmm_kernel<DT, FMT, BITS, 1, GATHER>), grid, dim3(kThreads), 0,
+                               st, q, glog2);
     } else {
-        hipLaunchKernelGGL((qmm_kernel<DT, FMT, BITS, 1>), grid, dim3(kThreads), 0, st, q, glog2);
+        hipLaunchKernelGGL((qmm_kernel<DT, FMT, BITS, 1, GATHER>), grid, dim3(kThreads), 0, st, q,
+                           glog2);
     }
     if (q.splits > 1) {
         const int64_t n = q.M * q.N;
@@ -435,6 +505,11 @@ int launch_qmm_f(const QmmParams& q, hipStream_t st) {
                            st, q);
     }
     return (int)hipGetLastError();
+}
+
+template <int DT, int FMT, int BITS>
+int launch_qmm_f(const QmmParams& q, hipStream_t st) {
+    return q.rhs ? launch_qmm_g<DT, FMT, BITS, true>(q, st) : launch_qmm_g<DT, FMT, BITS, false>(q, st);
 }
 
 }  // namespace

@@ -166,6 +166,24 @@ qmv_status_t gather_qmv(void* stream, int dtype, const qmv_weights_t* w, const v
                         int64_t n_x_rows, const uint32_t* lhs_indices,
                         const uint32_t* rhs_indices, int64_t n_slots, void* y);
 
+/* Routed-expert gathered qmm: the gather_qmv product for many slots at once,
+ * on the matrix cores (the MoE prefill form: "mlx 1.0.0 - quantized_nax.h",
+ * `affine_gather_qmm_rhs_nax`, whose expert indices are sorted so that runs
+ * of rows share an expert; "@lgrammel/ds4-provider - moe.metal",
+ * `kernel_mul_mm_id`). Same arguments, semantics and out-of-range rule as
+ * gather_qmv; dtype QMV_BF16 or QMV_F16 (QMV_F32 returns
+ * QMV_ERR_UNSUPPORTED); n_slots <= 65535 * 64. Arithmetic as in qmv_qmm
+ * (weights enter the MFMAs as dtype: exact for MXFP4 / NVFP4 / MXFP8 in bf16;
+ * affine per group in fp32). A block of 64 or 128 consecutive slots runs its
+ * K loop once per distinct expert among them, so rhs_indices sorted by expert
+ * (runs of equal ids) is the fast order; any order is correct. Within such a
+ * block the other experts' slots take zero x rows, so the weights must be
+ * finite (an infinite or NaN weight of one expert would turn those rows into
+ * NaN). */
+qmv_status_t gather_qmm(void* stream, int dtype, const qmv_weights_t* w, const void* x,
+                        int64_t n_x_rows, const uint32_t* lhs_indices,
+                        const uint32_t* rhs_indices, int64_t n_slots, void* y);
+
 /* ---------------- codecs: HOST memory, synchronous, no GPU needed -------- */
 
 /* Bytes of one packed row: K*bits/8 for QMV_AFFINE, K/2 for the fp4 formats,

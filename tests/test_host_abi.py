@@ -29,7 +29,7 @@ def test_library_exports_every_header_function(lib):
             "qmv_quantize_affine", "qmv_quantize_mxfp4", "qmv_quantize_mxfp8",
             "qmv_quantize_nvfp4", "qmv_moe_gate_up_swiglu", "qmv_moe_down_reduce", "qmv_fp_block",
             "qmv_qvm", "qmv_qvm_workspace_bytes", "qmv_qmm", "qmv_qmm_workspace_bytes",
-            "qmv_rmsnorm_qmv",
+            "qmv_rmsnorm_qmv", "gather_qmm",
             "qmv_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -294,3 +294,20 @@ def test_qmm_split_rule(lib):
             if s > 1:
                 per = -(-nk // s)
                 assert per >= 8 and (s - 1) * per < nk
+
+
+def test_gather_qmm_validation(lib):
+    f = lib.gather_qmm
+    lhs, rhs = V(0x60000), V(0x70000)
+    wt = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 4, 300, 1024, 0x20000, 0x30000, None, None)
+    assert f(None, 0, ctypes.byref(wt), X, 16, lhs, rhs, 64, Y) == UNSUP      # f32
+    assert f(None, 2, ctypes.byref(wt), X, 16, lhs, rhs, -1, Y) == INVAL
+    assert f(None, 2, ctypes.byref(wt), X, -1, lhs, rhs, 64, Y) == INVAL
+    assert f(None, 2, ctypes.byref(wt), X, 16, lhs, rhs, 65535 * 64 + 1, Y) == UNSUP
+    assert f(None, 2, ctypes.byref(wt), X, 16, None, rhs, 64, Y) == INVAL
+    assert f(None, 2, ctypes.byref(wt), X, 16, lhs, V(0x70002), 64, Y) == MISAL
+    assert f(None, 2, ctypes.byref(wt), X, 16, lhs, rhs, 64, X) == INVAL      # x and y overlap
+    sb = bmv.QmvWeights(5, 14, 64, 4, 300, 1024, 0x20000, 0x30000, None, None)
+    assert f(None, 2, ctypes.byref(sb), X, 16, lhs, rhs, 64, Y) == UNSUP
+    assert f(None, 2, ctypes.byref(wt), X, 16, lhs, rhs, 0, Y) == OK          # no slots
+    assert f(None, 2, None, X, 16, lhs, rhs, 64, Y) == INVAL
