@@ -610,6 +610,17 @@ qmv_status_t gather_qmm(void* stream, int dtype, const qmv_weights_t* wt, const 
     q.splits = 1;
     q.lhs = lhs_indices; q.rhs = rhs_indices;
     q.n_experts = wt->n_experts; q.n_x_rows = n_x_rows;
+    // blocks per tile along z: about the distinct experts a tile of
+    // consecutive slots sorted by expert holds (any count is correct: the
+    // last one takes the rest)
+    {
+        const int64_t bm = qmv::qmm_block_rows(n_slots, wt->N, wt->format);
+        int64_t runs = (wt->n_experts * bm + n_slots - 1) / n_slots + 1;
+        if (runs > bm) runs = bm;
+        if (runs > wt->n_experts) runs = wt->n_experts;
+        if (runs > 64) runs = 64;
+        q.runs = (int)(runs < 1 ? 1 : runs);
+    }
     return launch_status(qmv::launch_qmm(q, stream), fn);
 }
 

@@ -138,6 +138,7 @@ struct QmmParams {
     const uint32_t* rhs;
     int64_t n_experts;
     int64_t n_x_rows;
+    int runs;     // gather: blocks per tile along z (the last takes any further experts)
 };
 int launch_qmm(const QmmParams& q, void* stream);
 // Rows of a qmm block tile: 128 when 128-row tiles alone give at least 256

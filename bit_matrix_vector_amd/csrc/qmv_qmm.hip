@@ -132,9 +132,9 @@ __device__ inline void dequant_unit(const uint32_t (&w)[Fmt<FMT, BITS>::kWords],
 
 
 // MT: 32-row sub-tiles per wave, so the block tile is (64 * MT) x 128.
-// GATHER: rows are routed slots (x row lhs[s], expert rhs[s]); the block runs
-// the K loop once per distinct expert of its tile, in increasing order, with
-// the x rows of other experts' slots zero, accumulating into the same tiles.
+// GATHER: rows are routed slots (x row lhs[s], expert rhs[s]); the distinct
+// experts of a tile are spread over grid z, each block running the K loop on
+// its expert's matrix with the x rows of other experts' slots zero.
 template <int DT, int FMT, int BITS, int MT, bool GATHER>
 __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
     using F = Fmt<FMT, BITS>;
@@ -162,9 +162,10 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
     const int64_t n0 = (int64_t)blockIdx.x * kBN;
     const int64_t units = K >> 5;
     const int nk = (int)((K + kBK - 1) / kBK);
-    // this block's split of the K slices: [kb0, kb0 + nks), nks >= 1
+    // this block's split of the K slices: [kb0, kb0 + nks), nks >= 1 (grid z
+    // is the split outside gather mode; a gather never splits K)
     const int per = (nk + q.splits - 1) / q.splits;
-    const int kb0 = (int)blockIdx.z * per;
+    const int kb0 = GATHER ? 0 : (int)blockIdx.z * per;
     const int nks = (kb0 + per < nk ? kb0 + per : nk) - kb0;
     const S* x = static_cast<const S*>(q.x);
     // the matrix of the current run (gather: of expert e), its scales and biases
@@ -384,29 +385,29 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
         });
     };
 
+    // gather: the tile's expert ids (ids >= n_experts, and rows past the
+    // end, are kNone); block z of a tile runs the tile's z-th smallest
+    // expert, the last z block also every larger one, and each stores only
+    // the rows of the experts it ran (block 0 also the kNone rows, as zeros)
+    constexpr uint32_t kNone = 0xFFFFFFFFu;
+    __shared__ uint32_t tile_e[GATHER ? kBM : 1];
+    __shared__ uint32_t next_e;
+    uint32_t e_sel = kNone;
+    const bool last_z = blockIdx.z + 1 == gridDim.z;
     if constexpr (!GATHER) {
         run_k();
     } else {
-        // the tile's expert ids (ids >= n_experts, and rows past the end,
-        // never match); experts run in increasing order, each once
-        __shared__ uint32_t tile_e[kBM];
-        __shared__ uint32_t next_e;
-        constexpr uint32_t kNone = 0xFFFFFFFFu;
-        const int64_t S_ = M;
         for (int r = tid; r < kBM; r += kThreads) {
             const int64_t sl = m0 + r;
             uint32_t e = kNone;
-            if (sl < S_) {
+            if (sl < M) {
                 e = q.rhs[sl];
                 if ((int64_t)e >= q.n_experts) e = kNone;
             }
             tile_e[r] = e;
         }
-        uint32_t lo = 0;
-        const int64_t estride_w = N * q.row_bytes;
-        const int64_t estride_s =
-            N * q.sc_per_row * (kAffine ? (int64_t)Store<DT>::kBytes : (int64_t)F::template elem_bytes<DT>());
-        for (;;) {
+        // smallest expert id >= lo in the tile, or kNone
+        auto tile_min = [&](uint32_t lo) __attribute__((always_inline)) {
             if (tid == 0) next_e = kNone;
             __syncthreads();
             for (int r = tid; r < kBM; r += kThreads) {
@@ -416,7 +417,20 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
             __syncthreads();
             const uint32_t e = next_e;
             __syncthreads();   // every thread has read next_e before it is reset
-            if (e == kNone) break;
+            return e;
+        };
+        uint32_t lo = 0;
+        for (unsigned z = 0; z <= blockIdx.z; ++z) {
+            e_sel = tile_min(lo);
+            if (e_sel == kNone) break;
+            lo = e_sel + 1;
+        }
+        const int64_t estride_w = N * q.row_bytes;
+        const int64_t estride_s =
+            N * q.sc_per_row *
+            (kAffine ? (int64_t)Store<DT>::kBytes : (int64_t)F::template elem_bytes<DT>());
+        uint32_t e = e_sel;
+        while (e != kNone) {
 #pragma unroll
             for (int h = 0; h < kXH; ++h) {
                 const int r = xr + 32 * h;
@@ -433,9 +447,21 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
             if constexpr (kAffine)
                 bicur = static_cast<const uint8_t*>(q.biases) + (int64_t)e * estride_s;
             run_k();
-            lo = e + 1;
+            if (!last_z) break;
+            e = tile_min(e + 1);
         }
     }
+    // gather: does this block store local row r?
+    auto mine = [&](int r) __attribute__((always_inline)) {
+        if constexpr (!GATHER) {
+            return true;
+        } else {
+            const uint32_t e = tile_e[r];
+            if (e == kNone) return blockIdx.z == 0;
+            if (e_sel == kNone) return false;
+            return last_z ? e >= e_sel : e == e_sel;
+        }
+    };
 
     const float gs = (FMT == FMT_NVFP4 && q.gscale) ? *q.gscale : 1.0f;
 #pragma unroll
@@ -446,10 +472,10 @@ __global__ __launch_bounds__(kThreads) void qmm_kernel(QmmParams q, int glog2) {
             if (n >= N) continue;
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                const int64_t m =
-                    m0 + 32 * MT * wm + 32 * tm + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                if (m >= M) continue;
-                if (q.splits == 1)
+                const int rl = 32 * MT * wm + 32 * tm + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                const int64_t m = m0 + rl;
+                if (m >= M || !mine(rl)) continue;
+                if (GATHER || q.splits == 1)
                     static_cast<S*>(q.y)[m * N + n] = Store<DT>::from_f32(acc[tm][t][i] * gs);
                 else
                     q.ws[((int64_t)blockIdx.z * M + m) * N + n] = acc[tm][t][i];
@@ -485,7 +511,7 @@ template <int DT, int FMT, int BITS, bool GATHER>
 int launch_qmm_g(const QmmParams& q, hipStream_t st) {
     const int bm = qmm_block_rows(q.M, q.N, q.format);
     const dim3 grid((unsigned)((q.N + kBN - 1) / kBN), (unsigned)((q.M + bm - 1) / bm),
-                    (unsigned)q.splits);
+                    (unsigned)(GATHER ? q.runs : q.splits));
     int glog2 = 0;
     if (FMT == FMT_AFFINE) glog2 = q.group == 128 ? 2 : (q.group == 64 ? 1 : 0);
     if constexpr (FMT != FMT_AFFINE) {
