@@ -159,18 +159,34 @@ __device__ inline uint32_t affine_code(const uint32_t* d, int j) {
     return __builtin_amdgcn_alignbit(d[w + 1], d[w], off) & mask;
 }
 
-template <int WORDS>
+// One vector load of a value read once (NT: the nontemporal hint, so a
+// stream of weights does not displace what the caches hold for reuse).
+template <bool NT, class V>
+__device__ inline V load_vec(const uint8_t* p) {
+    if constexpr (NT)
+        return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+    else
+        return *reinterpret_cast<const V*>(p);
+}
+
+// The WORDS dwords of one unit. Units of 2, 4 and 8 dwords are 8- or 16-byte
+// aligned and take vector loads; the 3-, 5- and 6-dword units of 3/5/6-bit
+// codes are only 4-byte aligned and take plain loads. NT applies to units of
+// at most 16 bytes, where each load instruction of a wave covers whole cache
+// lines; the two 16-byte halves of an 8-dword unit share their lines, and
+// with the hint the 8-bit QMV ran ~10 % slower (measured), so they load plainly.
+template <int WORDS, bool NT = false>
 __device__ inline void load_words(const uint8_t* p, uint32_t (&d)[WORDS]) {
     if constexpr (WORDS == 4) {
-        const v4u a = *reinterpret_cast<const v4u*>(p);
+        const v4u a = load_vec<NT, v4u>(p);
         d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
     } else if constexpr (WORDS == 8) {
-        const v4u a = *reinterpret_cast<const v4u*>(p);
-        const v4u b = *reinterpret_cast<const v4u*>(p + 16);
+        const v4u a = load_vec<false, v4u>(p);
+        const v4u b = load_vec<false, v4u>(p + 16);
         d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w;
         d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
     } else if constexpr (WORDS == 2) {
-        const v2u a = *reinterpret_cast<const v2u*>(p);
+        const v2u a = load_vec<NT, v2u>(p);
         d[0] = a.x; d[1] = a.y;
     } else {
         __builtin_memcpy(d, __builtin_assume_aligned(p, 4), 4 * WORDS);

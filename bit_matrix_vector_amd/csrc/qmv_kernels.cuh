@@ -285,7 +285,16 @@ __device__ inline void unit_fma(const UnitRaw<FMT, BITS, R>& u_raw,
 // out first). Scale bytes stay undecoded until the unit is computed, and the
 // next unit's loads are issued under uniform branches before the current unit
 // is consumed, so two units per lane are in flight at every point.
-template <int DT, int FMT, int BITS, int NB, int R, class XR>
+//
+// kStream: the weights and scales are read once (plain QMV), so their loads
+// carry the nontemporal hint. kShort: the caller guarantees one slab (K fits
+// the stage), 4-byte-aligned scale segments and at most two units per lane
+// per row; the tile then has no slab loop, no steady-state refill loop and no
+// byte-wise scale copy, which the register allocation would otherwise carry
+// (62 instead of 78 VGPRs for the MXFP4 bf16 one-row tile: 8 waves per SIMD
+// instead of 6). The arithmetic, and so every result, is the same either way.
+template <int DT, int FMT, int BITS, int NB, int R, bool kStream = false, bool kShort = false,
+          class XR>
 __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t row_base,
                                 const uint8_t* __restrict__ w, const void* sc, const void* bi,
                                 const XR& xr, typename Store<DT>::S* const (&yrow)[NB],
@@ -329,7 +338,7 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
     auto load_unit = [&](U& u_raw, int64_t u) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < R; ++i)
-            load_words<W>(wblk + (wo[i] + (uint32_t)(u * kUnitBytes)), u_raw.d[i]);
+            load_words<W, kStream>(wblk + (wo[i] + (uint32_t)(u * kUnitBytes)), u_raw.d[i]);
     };
 
     // Staged scales: per array, per block row, the scale elements of the
@@ -349,7 +358,7 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
         unit_fma<DT, FMT, BITS, NB, R>(u_raw, scl, lds, ul, ks, us, total);
     };
 
-    for (int64_t slab = 0; slab < K; slab += g.ks) {
+    for (int64_t slab = 0; slab < (kShort ? (int64_t)1 : K); slab += g.ks) {
         const int ks = (int)((K - slab) < g.ks ? (K - slab) : g.ks);
         const int us = ks >> 5;                          // units in this slab
         const int iters = (us + lpr - 1) >> g.lpr_log2;  // per lane, uniform
@@ -375,7 +384,7 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
         const int seg = (int)F::elem_of_unit(us, g.glog2) * kEB;   // bytes per row per array
         const int64_t e0 = F::elem_of_unit(u0, g.glog2);
         const int wpr = seg >> 2;
-        const int nw = g.sc_aligned4 ? F::kArrays * RB * wpr : 0;
+        const int nw = (kShort || g.sc_aligned4) ? F::kArrays * RB * wpr : 0;
         auto sc_src = [&](int c) __attribute__((always_inline)) {   // byte c of the segment copy
             const int per_arr = RB * seg;
             const int a = c / per_arr;
@@ -391,7 +400,7 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
         // the block is one contiguous range and a word's source needs no
         // division; a word past the array end (rows >= N) is clamped to its
         // last word.
-        const bool whole_rows = g.ks >= K;
+        const bool whole_rows = kShort || g.ks >= K;
         const int64_t row_stride = p.sc_per_row * kEB;
         auto sc_word = [&](int c) __attribute__((always_inline)) {
             const uint8_t* q;
@@ -406,7 +415,10 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
             } else {
                 q = sc_src(4 * c);
             }
-            return *reinterpret_cast<const uint32_t*>(q);
+            if constexpr (kStream)
+                return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(q));
+            else
+                return *reinterpret_cast<const uint32_t*>(q);
         };
         uint32_t sw[kScAhead];
         static_for<0, kScAhead>([&](auto j_c) {
@@ -453,7 +465,7 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
             });
             for (int c = tid + kScAhead * kThreads; c < nw; c += kThreads)
                 reinterpret_cast<uint32_t*>(lds_sc)[c] = sc_word(c);
-        } else {
+        } else if constexpr (!kShort) {
             const int nbytes = F::kArrays * RB * seg;
             for (int c = tid; c < nbytes; c += kThreads) lds_sc[c] = *sc_src(c);
         }
@@ -465,13 +477,15 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
         // clamped); the last one or two units are consumed by a load-free
         // epilogue, so no wave ends waiting on loads it does not use.
         int it = 0;
-        for (; it + 2 < iters; it += 2) {
-            const int ua = gl + it * lpr;
-            const int ub = ua + lpr;
-            if (ua < us) compute_unit(A, ua, ks, us, seg);
-            load_unit(A, u0 + min(ua + 2 * lpr, us - 1));
-            if (ub < us) compute_unit(Bq, ub, ks, us, seg);
-            load_unit(Bq, u0 + min(ub + 2 * lpr, us - 1));
+        if constexpr (!kShort) {
+            for (; it + 2 < iters; it += 2) {
+                const int ua = gl + it * lpr;
+                const int ub = ua + lpr;
+                if (ua < us) compute_unit(A, ua, ks, us, seg);
+                load_unit(A, u0 + min(ua + 2 * lpr, us - 1));
+                if (ub < us) compute_unit(Bq, ub, ks, us, seg);
+                load_unit(Bq, u0 + min(ub + 2 * lpr, us - 1));
+            }
         }
         {
             const int ua = gl + it * lpr;
@@ -507,7 +521,7 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
     }
 }
 
-template <int DT, int FMT, int BITS, int NB, int R>
+template <int DT, int FMT, int BITS, int NB, int R, bool SHORT>
 __global__ __launch_bounds__(kThreads) void qmv_kernel(LaunchParams p, Geom g) {
     using S = typename Store<DT>::S;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -517,8 +531,8 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(LaunchParams p, Geom g) {
     for (int b = 0; b < NB; ++b) yrow[b] = static_cast<S*>(p.y) + b * p.N;
     const XContig<S> xr{static_cast<const S*>(p.x), p.K};
     const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
-    qmv_tile<DT, FMT, BITS, NB, R>(p, g, (int64_t)blockIdx.x * g.rows_per_block, p.w, p.scales,
-                                   p.biases, xr, yrow, gmul, lds);
+    qmv_tile<DT, FMT, BITS, NB, R, true, SHORT>(p, g, (int64_t)blockIdx.x * g.rows_per_block, p.w,
+                                                p.scales, p.biases, xr, yrow, gmul, lds);
 }
 
 // Fused RMSNorm + QMV: y[b] = r[b] * (W . RN_T(x[b] * gamma)), the QMV tile
@@ -536,8 +550,8 @@ __global__ __launch_bounds__(kThreads) void qmv_norm_kernel(LaunchParams p, Geom
 #pragma unroll
     for (int b = 0; b < NB; ++b) yrow[b] = static_cast<S*>(p.y) + b * p.N;
     const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
-    qmv_tile<DT, FMT, BITS, NB, R>(p, g, (int64_t)blockIdx.x * g.rows_per_block, p.w, p.scales,
-                                   p.biases, xr, yrow, gmul, lds);
+    qmv_tile<DT, FMT, BITS, NB, R, true>(p, g, (int64_t)blockIdx.x * g.rows_per_block, p.w,
+                                         p.scales, p.biases, xr, yrow, gmul, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1335,14 +1349,21 @@ int64_t launch_waves(const LaunchParams& p, int rows) {
     return (p.N + rpb - 1) / rpb * kWaves;
 }
 
+// The short tile applies when K fits one slab, the scale segments are 4-byte
+// aligned and a lane holds at most two units of a row.
+inline bool short_tile(const LaunchParams& p, const Geom& g) {
+    return p.K > 0 && g.ks >= p.K && g.sc_aligned4 && p.K / 32 <= 2 * (int64_t)g.lpr;
+}
+
 template <int DT, int FMT, int BITS, int NB, int R>
 int launch_qmv_r(const LaunchParams& p, hipStream_t st) {
     const Geom g = make_geom<DT, FMT, BITS>(p, NB, kMaxStageBytes, R);
     const dim3 grid((unsigned)((p.N + g.rows_per_block - 1) / g.rows_per_block));
     const size_t lds = stage_bytes<DT, FMT, BITS>(p, g);
-    auto* kern = &qmv_kernel<DT, FMT, BITS, NB, R>;
-    static std::atomic<size_t> granted{0};
-    if (const int e = allow_lds(kern, lds, granted)) return e;
+    auto* kern = short_tile(p, g) ? &qmv_kernel<DT, FMT, BITS, NB, R, true>
+                                  : &qmv_kernel<DT, FMT, BITS, NB, R, false>;
+    static std::atomic<size_t> granted_s{0}, granted_l{0};
+    if (const int e = allow_lds(kern, lds, short_tile(p, g) ? granted_s : granted_l)) return e;
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, p, g);
     return (int)hipGetLastError();
 }
