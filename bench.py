@@ -94,7 +94,7 @@ class Runner:
 
 class GatherRunner:
     """Pre-marshalled gather_qmv calls over rotating copies of the expert-
-    stacked weights (config 5)."""
+    stacked weights (the MoE workload)."""
 
     def __init__(self, bmv, m, min_bytes: int = 1 << 29):
         import torch
@@ -262,7 +262,7 @@ class GatherQmmRunner:
         import torch
         import workloads
         self.lib = bmv.load()
-        m = workloads.config5("mxfp4", "gate_up", tokens=tokens)
+        m = workloads.moe_case("mxfp4", "gate_up", tokens=tokens)
         order = np.argsort(m.rhs, kind="stable")
         lhs, rhs = m.lhs[order], m.rhs[order]
         w0, s0 = _dev(m.w), _dev(m.scales)
@@ -350,7 +350,7 @@ class QuantRunner:
 
 
 class MoeBlockRunner:
-    """The fused routed-MoE decode block of config 5 (64 experts, hidden 4096,
+    """The fused routed-MoE decode block of the MoE workload (64 experts, hidden 4096,
     ffn 1536, 16 tokens, top-8): gate/up + SwiGLU, then the per-token down sum
     (two launches per call), over two copies of the three expert stacks
     (~0.6 GB each for MXFP4, beyond the 256 MB Infinity Cache). Bytes: the
@@ -412,17 +412,18 @@ class MoeBlockRunner:
         self.keep = self.wts = None
 
 
-def time_chain(bmv, steps: int = 100) -> dict:
-    """Config 2: a dependent chain of 100 calls (8-bit affine g64, K=N=2560,
-    bf16), each output the next input; same weights every call (warm), as in
-    a decode loop. Timed as plain launches and as one HIP graph."""
+def time_chain(bmv, N: int = 2560, steps: int = 100) -> dict:
+    """A dependent chain of 100 calls (8-bit affine g64, K=2560, bf16), each
+    output the next input (for N < K it overwrites the first N values of the
+    other buffer); same weights every call (warm), as in a decode loop. Timed
+    as plain launches and as one HIP graph."""
     import torch
     import workloads
-    c = workloads.config2(2560)
+    c = workloads.chain_case(N)
     lib = bmv.load()
     x = _dev(c.x, "bf16")
     w, s, b = _dev(c.w), _dev(c.scales, "bf16"), _dev(c.biases, "bf16")
-    bufs = [x.clone(), torch.empty_like(x)]
+    bufs = [x.clone(), x.clone()]
     vp = ctypes.c_void_p
 
     def chain(stream):
@@ -461,7 +462,7 @@ def time_chain(bmv, steps: int = 100) -> dict:
     torch.cuda.synchronize()
     graph = t0.elapsed_time(t1) * 1e3 / (reps * steps)
     del g
-    return {"case": "config2 chain of 100: affine 8b g64 K=N=2560 bf16, warm weights",
+    return {"case": f"chain of 100: affine 8b g64 K=2560 N={N} bf16, warm weights",
             "bytes": c.algorithmic_bytes(), "us_per_call_plain": plain,
             "us_per_call_graph": graph, "gbps_graph": c.algorithmic_bytes() / graph / 1e3}
 
@@ -610,7 +611,7 @@ def pmc_workload(bmv, n: int) -> None:
         assert st == 0
     torch.cuda.synchronize()
     del src, dst
-    r = Runner(bmv, workloads.config3("mxfp4", 1))
+    r = Runner(bmv, workloads.mlp_up_case("mxfp4", 1))
     for i in range(n):
         r.call(i, sp)
     torch.cuda.synchronize()
@@ -749,7 +750,7 @@ def main() -> int:
     ap.add_argument("--headline-only", action="store_true")
     ap.add_argument("--no-ceiling", action="store_true")
     ap.add_argument("--sweep", action="store_true",
-                    help="also time the whole affine sweep (config 4) to stderr")
+                    help="also time the whole affine sweep (K=N=4096) to stderr")
     ap.add_argument("--ceiling-sweep", action="store_true",
                     help="only sweep the streaming-read ceiling over sizes and exit")
     ap.add_argument("--pmc-workload", type=int, default=0, metavar="N",
@@ -790,7 +791,7 @@ def main() -> int:
     if args.pmc_workload:
         pmc_workload(bmv, args.pmc_workload)
         return 0
-    head = workloads.config3("mxfp4", 1)
+    head = workloads.mlp_up_case("mxfp4", 1)
     check_once(bmv, head)
     runner = Runner(bmv, head)
     res = time_case(runner, args.steps, args.warmup)
@@ -804,10 +805,10 @@ def main() -> int:
 
     cases = []
     if not args.headline_only:
-        for name, c in (("nvfp4 B1 K4096 N14336 bf16", workloads.config3("nvfp4", 1)),
-                        ("mxfp8 B1 K4096 N14336 bf16", workloads.config3("mxfp8", 1)),
-                        ("affine 4b g64 B1 K4096 N4096 bf16", workloads.config4(4, 64, 1, "bf16")),
-                        ("mxfp4 B4 K4096 N14336 bf16", workloads.config3("mxfp4", 4)),
+        for name, c in (("nvfp4 B1 K4096 N14336 bf16", workloads.mlp_up_case("nvfp4", 1)),
+                        ("mxfp8 B1 K4096 N14336 bf16", workloads.mlp_up_case("mxfp8", 1)),
+                        ("affine 4b g64 B1 K4096 N4096 bf16", workloads.affine_sweep_case(4, 64, 1, "bf16")),
+                        ("mxfp4 B4 K4096 N14336 bf16", workloads.mlp_up_case("mxfp4", 4)),
                         *((f"{f} B1 K4096 N14336 bf16",
                            workloads.sb_case(f, K=4096, N=14336, B=1, key="bench"))
                           for f in ("mxfp8_e5m2", "nvfp8", "fp8_e5m2_f16", "int4", "mxint8"))):
@@ -822,11 +823,11 @@ def main() -> int:
     if not args.headline_only:
         for fmt, proj in (("mxfp4", "gate_up"), ("mxfp4", "down"), ("affine", "gate_up"),
                           ("affine", "down")):
-            m = workloads.config5(fmt, proj)
+            m = workloads.moe_case(fmt, proj)
             r = GatherRunner(bmv, m)
             cr = time_case(r, max(100, args.steps // 10), 10)
             r.free()
-            cr["case"] = (f"config5 gather {fmt} {proj}: 64 experts, {m.lhs.size} slots, "
+            cr["case"] = (f"MoE gather {fmt} {proj}: 64 experts, {m.lhs.size} slots, "
                           f"{len(m.distinct_experts())} distinct, K={m.K} N={m.N} bf16")
             cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
             cases.append(cr)
@@ -834,19 +835,20 @@ def main() -> int:
         for fmt in ("mxfp4", "affine"):
             r = MoeBlockRunner(bmv, fmt)
             cr = time_case(r, max(100, args.steps // 10), 10)
-            cr["case"] = (f"fused MoE block {fmt} (config 5: 64 experts, hidden 4096, ffn 1536, "
+            cr["case"] = (f"fused MoE block {fmt} (64 experts, hidden 4096, ffn 1536, "
                           f"16 tokens x top-8, {r.distinct} distinct): gate/up+SwiGLU, down sum; "
                           "2 launches")
             r.free()
             cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
             cases.append(cr)
             print(f"[bench] {cr['case']}: {json.dumps(cr)}", file=sys.stderr, flush=True)
-        ch = time_chain(bmv)
-        cases.append(ch)
-        print(f"[bench] {ch['case']}: {json.dumps(ch)}", file=sys.stderr, flush=True)
-        for name, c in (("rmsnorm+qmv mxfp4 B1 K=4096 N=14336 bf16", workloads.config3("mxfp4", 1)),
+        for n in (2560,) + workloads.CHAIN_TAILS:
+            ch = time_chain(bmv, n)
+            cases.append(ch)
+            print(f"[bench] {ch['case']}: {json.dumps(ch)}", file=sys.stderr, flush=True)
+        for name, c in (("rmsnorm+qmv mxfp4 B1 K=4096 N=14336 bf16", workloads.mlp_up_case("mxfp4", 1)),
                         ("rmsnorm+qmv affine 4b g64 B1 K=N=4096 bf16",
-                         workloads.config4(4, 64, 1, "bf16"))):
+                         workloads.affine_sweep_case(4, 64, 1, "bf16"))):
             r = NormRunner(bmv, c)
             cr = time_case(r, max(200, args.steps // 4), args.warmup)
             r.free()
@@ -854,8 +856,8 @@ def main() -> int:
             cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
             cases.append(cr)
             print(f"[bench] {name}: {json.dumps(cr)}", file=sys.stderr, flush=True)
-        for name, c in (("qvm mxfp4 N=14336 K=4096 B1 bf16", workloads.config3("mxfp4", 1)),
-                        ("qvm affine 4b g64 N=K=4096 B1 bf16", workloads.config4(4, 64, 1, "bf16"))):
+        for name, c in (("qvm mxfp4 N=14336 K=4096 B1 bf16", workloads.mlp_up_case("mxfp4", 1)),
+                        ("qvm affine 4b g64 N=K=4096 B1 bf16", workloads.affine_sweep_case(4, 64, 1, "bf16"))):
             r = QvmRunner(bmv, c)
             cr = time_case(r, max(200, args.steps // 4), args.warmup)
             r.free()
@@ -863,10 +865,10 @@ def main() -> int:
             cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
             cases.append(cr)
             print(f"[bench] {name}: {json.dumps(cr)}", file=sys.stderr, flush=True)
-        for name, c, M in (("qmm mxfp4 M=32 K=4096 N=14336 bf16", workloads.config3("mxfp4", 1), 32),
-                           ("qmm mxfp4 M=256 K=4096 N=14336 bf16", workloads.config3("mxfp4", 1), 256),
+        for name, c, M in (("qmm mxfp4 M=32 K=4096 N=14336 bf16", workloads.mlp_up_case("mxfp4", 1), 32),
+                           ("qmm mxfp4 M=256 K=4096 N=14336 bf16", workloads.mlp_up_case("mxfp4", 1), 256),
                            ("qmm affine 4b g64 M=256 K=N=4096 bf16",
-                            workloads.config4(4, 64, 1, "bf16"), 256)):
+                            workloads.affine_sweep_case(4, 64, 1, "bf16"), 256)):
             r = QmmRunner(bmv, c, M)
             cr = time_case(r, max(200, args.steps // 4), args.warmup)
             r.free()
@@ -896,11 +898,11 @@ def main() -> int:
             for group in workloads.AFFINE_GROUPS:
                 for B in (1, 2, 4, 8):
                     for dt in workloads.DTYPES:
-                        c = workloads.config4(bits, group, B, dt)
+                        c = workloads.affine_sweep_case(bits, group, B, dt)
                         r = Runner(bmv, c, min_bytes=1 << 29)
                         cr = time_case(r, 200, 10)
                         r.free()
-                        cr["case"] = f"config4 affine b{bits} g{group} B{B} {dt} K=N=4096"
+                        cr["case"] = f"affine sweep b{bits} g{group} B{B} {dt} K=N=4096"
                         cr["pct_peak"] = round(100 * cr["gbps"] / PEAK_HBM_GBPS, 1)
                         print(f"[sweep] {json.dumps(cr)}", file=sys.stderr, flush=True)
 

@@ -538,7 +538,7 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(LaunchParams p, Geom g) {
 // Fused RMSNorm + QMV: y[b] = r[b] * (W . RN_T(x[b] * gamma)), the QMV tile
 // with the XNorm accessor (x times gamma staged, the squares summed on the
 // way, r applied to each row's result).
-template <int DT, int FMT, int BITS, int NB, int R>
+template <int DT, int FMT, int BITS, int NB, int R, bool SHORT>
 __global__ __launch_bounds__(kThreads) void qmv_norm_kernel(LaunchParams p, Geom g, NormArgs na) {
     using S = typename Store<DT>::S;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -550,8 +550,8 @@ __global__ __launch_bounds__(kThreads) void qmv_norm_kernel(LaunchParams p, Geom
 #pragma unroll
     for (int b = 0; b < NB; ++b) yrow[b] = static_cast<S*>(p.y) + b * p.N;
     const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
-    qmv_tile<DT, FMT, BITS, NB, R, true>(p, g, (int64_t)blockIdx.x * g.rows_per_block, p.w,
-                                         p.scales, p.biases, xr, yrow, gmul, lds);
+    qmv_tile<DT, FMT, BITS, NB, R, true, SHORT>(p, g, (int64_t)blockIdx.x * g.rows_per_block, p.w,
+                                                p.scales, p.biases, xr, yrow, gmul, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1373,9 +1373,10 @@ int launch_qmv_norm_r(const LaunchParams& p, const NormArgs& na, hipStream_t st)
     const Geom g = make_geom<DT, FMT, BITS>(p, NB, kMaxStageBytes, R);
     const dim3 grid((unsigned)((p.N + g.rows_per_block - 1) / g.rows_per_block));
     const size_t lds = stage_bytes<DT, FMT, BITS>(p, g);
-    auto* kern = &qmv_norm_kernel<DT, FMT, BITS, NB, R>;
-    static std::atomic<size_t> granted{0};
-    if (const int e = allow_lds(kern, lds, granted)) return e;
+    auto* kern = short_tile(p, g) ? &qmv_norm_kernel<DT, FMT, BITS, NB, R, true>
+                                  : &qmv_norm_kernel<DT, FMT, BITS, NB, R, false>;
+    static std::atomic<size_t> granted_s{0}, granted_l{0};
+    if (const int e = allow_lds(kern, lds, short_tile(p, g) ? granted_s : granted_l)) return e;
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, p, g, na);
     return (int)hipGetLastError();
 }

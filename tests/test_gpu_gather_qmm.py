@@ -122,13 +122,13 @@ def test_gather_qmm_large_tiles(bmv):
     assert np.isfinite(oracle.storage_to_f64(yh, "bf16")).all()
 
 
-def test_gather_qmm_config5_shape(bmv):
+def test_gather_qmm_moe_shape(bmv):
     # the MoE workload's gate/up projection (64 experts, hidden 4096, ffn
     # 1536), 64 tokens x top-8, slots sorted by expert; sampled slots checked
-    m = workloads.config5("mxfp4", "gate_up", tokens=64)
+    m = workloads.moe_case("mxfp4", "gate_up", tokens=64)
     order = np.argsort(m.rhs, kind="stable")
     lhs, rhs = m.lhs[order], m.rhs[order]
-    say("gather_qmm config5 gate/up mxfp4 64 tokens top-8 sorted")
+    say("gather_qmm MoE gate/up mxfp4 64 tokens top-8 sorted")
     dev = [to_dev(m.w), to_dev(m.scales)]   # kept alive while the struct is used
     wt = bmv.make_weights("mxfp4", dev[0], dev[1], None, K=m.K, bits=4, group_size=32)
     y = bmv.gather_qmm(to_dev(m.x, "bf16"), wt, indices_dev(lhs), indices_dev(rhs))
@@ -141,4 +141,4 @@ def test_gather_qmm_config5_shape(bmv):
         We = oracle.dequant_mxfp4(m.w[e], m.scales[e], m.K)
         y64 = oracle.qmv(m.x[r][None, :], "bf16", We)
         A = oracle.abs_dot(m.x[r][None, :], "bf16", We)
-        check(yh[s:s + 1], y64, A, "bf16", f"config5 gather_qmm slot {s}")
+        check(yh[s:s + 1], y64, A, "bf16", f"MoE gather_qmm slot {s}")

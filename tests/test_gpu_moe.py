@@ -163,7 +163,7 @@ def test_moe_block_out_of_range_ids(bmv):
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "affine"])
 def test_moe_block_full_size_sampled(bmv, fmt):
-    # config 5's block (64 experts, hidden 4096, ffn 1536, 16 tokens, top-8);
+    # the MoE workload's block (64 experts, hidden 4096, ffn 1536, 16 tokens, top-8);
     # the oracle checks tokens 0, 7 and 15
     say(f"moe block {fmt} bf16 full size")
     c = workloads.moe_block_case(fmt, key="full")

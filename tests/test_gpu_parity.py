@@ -153,8 +153,8 @@ def _full_check(bmv, c, what):
     return check(y, oracle.qmv(c.x, c.dtype, W), oracle.abs_dot(c.x, c.dtype, W), c.dtype, what)
 
 
-def test_config1_full(bmv):
-    _full_check(bmv, workloads.config1(), "config1 affine b4 g64 K512 N256 f32")
+def test_small_affine_full(bmv):
+    _full_check(bmv, workloads.small_affine_case(), "small affine b4 g64 K512 N256 f32")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
@@ -188,17 +188,17 @@ def test_nvfp4_without_global_scale(bmv):
 
 
 # ---------------------------------------------------------------------------
-# config 2: 8-bit g64 K=2560 bf16, tails, dependent chain
+# the chain workload: 8-bit g64 K=2560 bf16, tails, dependent chain
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("N", [2560, *workloads.C2_TAILS])
-def test_config2_full(bmv, N):
-    _full_check(bmv, workloads.config2(N), f"config2 N{N}")
+@pytest.mark.parametrize("N", [2560, *workloads.CHAIN_TAILS])
+def test_chain_full(bmv, N):
+    _full_check(bmv, workloads.chain_case(N), f"chain workload N{N}")
 
 
 def test_tail_rows_equal_padded_call_bitwise(bmv):
     import torch
-    c = workloads.config2(2560)
+    c = workloads.chain_case(2560)
     d = case_to_dev(c)
     say("tail vs padded, affine 8-bit")
     full = bmv.qmv_affine(d["x"], d["w"], d["scales"], d["biases"], 8, 64)
@@ -207,7 +207,7 @@ def test_tail_rows_equal_padded_call_bitwise(bmv):
                               d["biases"][:n].contiguous(), 8, 64)
         assert torch.equal(part.view(torch.int16), full[:, :n].view(torch.int16)), n
     for fmt in ("mxfp4", "nvfp4", "mxfp8"):
-        c3 = workloads.config3(fmt, 2, N=300)
+        c3 = workloads.mlp_up_case(fmt, 2, N=300)
         d3 = case_to_dev(c3)
         say(f"tail vs padded, {fmt}")
         full = run_qmv(bmv, c3, d3)
@@ -219,13 +219,13 @@ def test_tail_rows_equal_padded_call_bitwise(bmv):
             assert torch.equal(part.view(torch.int16), full[:, :n].view(torch.int16)), (fmt, n)
 
 
-def test_config2_dependent_chain(bmv):
+def test_chain_dependent(bmv):
     import torch
-    c = workloads.config2(2560)
+    c = workloads.chain_case(2560)
     d = case_to_dev(c)
     W = oracle.dequant_affine(c.w, c.scales, c.biases, c.K, 8, 64, "bf16")
     bufs = [d["x"].clone(), torch.empty_like(d["x"])]
-    say("config2 chain of 100")
+    say("chain of 100")
     ys = []
     for t in range(100):
         bmv.qmv_affine(bufs[t % 2], d["w"], d["scales"], d["biases"], 8, 64, y=bufs[(t + 1) % 2])
@@ -246,30 +246,30 @@ def test_config2_dependent_chain(bmv):
 
 
 # ---------------------------------------------------------------------------
-# config 3: K=4096, N=14336, MXFP4 / NVFP4 / MXFP8, B in {1, 4}
+# the MLP projection: K=4096, N=14336, MXFP4 / NVFP4 / MXFP8, B in {1, 4}
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
 @pytest.mark.parametrize("B", [1, 4])
-def test_config3_sampled(bmv, fmt, B):
-    c = workloads.config3(fmt, B)
-    say(f"config3 {fmt} B{B} K4096 N14336")
+def test_mlp_up_sampled(bmv, fmt, B):
+    c = workloads.mlp_up_case(fmt, B)
+    say(f"{fmt} B{B} K4096 N14336")
     y = to_host(run_qmv(bmv, c), c.dtype)
     rows = sample_rows(c.N, 256, seed=B)
     y64, A = oracle_rows(c, rows)
-    check(y[:, rows], y64, A, c.dtype, f"config3 {fmt} B{B}")
+    check(y[:, rows], y64, A, c.dtype, f"{fmt} B{B} K4096 N14336")
 
 
 def test_block_scale_equivariance_bitwise(bmv):
     import torch
-    c = workloads.config3("mxfp4", 2, N=512)
+    c = workloads.mlp_up_case("mxfp4", 2, N=512)
     say("mxfp4 exponent +1 doubles y")
     y1 = run_qmv(bmv, c)
     c2 = workloads.QmvCase("mxfp4", c.dtype, c.B, c.K, c.N, c.w, (c.scales + 1).astype(np.uint8),
                            c.x)
     y2 = run_qmv(bmv, c2)
     assert torch.equal(y2.float(), 2 * y1.float())
-    n = workloads.config3("nvfp4", 2, N=512)
+    n = workloads.mlp_up_case("nvfp4", 2, N=512)
     say("nvfp4 global 0.5 vs 1.0")
     ya = run_qmv(bmv, workloads.QmvCase("nvfp4", n.dtype, n.B, n.K, n.N, n.w, n.scales, n.x,
                                         global_scale=1.0))
@@ -282,29 +282,29 @@ def test_block_scale_equivariance_bitwise(bmv):
 
 
 # ---------------------------------------------------------------------------
-# config 4: the affine sweep at full size (sampled rows)
+# the affine sweep at full size (sampled rows)
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
 @pytest.mark.parametrize("B", [1, 2, 4, 8])
 @pytest.mark.parametrize("group", [32, 64, 128])
 @pytest.mark.parametrize("bits", [2, 3, 4, 5, 6, 8])
-def test_config4_sampled(bmv, bits, group, B, dtype):
-    c = workloads.config4(bits, group, B, dtype)
-    say(f"config4 b{bits} g{group} B{B} {dtype}")
+def test_affine_sweep_sampled(bmv, bits, group, B, dtype):
+    c = workloads.affine_sweep_case(bits, group, B, dtype)
+    say(f"affine b{bits} g{group} B{B} {dtype} K=N=4096")
     y = to_host(run_qmv(bmv, c), dtype)
     rows = sample_rows(c.N, 48, seed=bits * 100 + group + B)
     y64, A = oracle_rows(c, rows)
-    check(y[:, rows], y64, A, dtype, f"config4 b{bits} g{group} B{B} {dtype}")
+    check(y[:, rows], y64, A, dtype, f"affine b{bits} g{group} B{B} {dtype} K=N=4096")
 
 
 def test_batch_rows_equal_single_row_calls_bitwise(bmv):
     import torch
     for fmt in ("affine", "mxfp4", "nvfp4", "mxfp8"):
         if fmt == "affine":
-            c = workloads.config4(3, 64, 8, "bf16", N=256)
+            c = workloads.affine_sweep_case(3, 64, 8, "bf16", N=256)
         else:
-            c = workloads.config3(fmt, 8, N=256)
+            c = workloads.mlp_up_case(fmt, 8, N=256)
         d = case_to_dev(c)
         say(f"batch invariance {fmt}")
         yb = run_qmv(bmv, c, d)
@@ -315,7 +315,7 @@ def test_batch_rows_equal_single_row_calls_bitwise(bmv):
 
 
 # ---------------------------------------------------------------------------
-# config 5: routed-MoE gathered QMV
+# the MoE workload: routed-MoE gathered QMV
 # ---------------------------------------------------------------------------
 
 def _moe_dev(m):
@@ -333,10 +333,10 @@ def _moe_weights(bmv, m, d):
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "affine"])
 @pytest.mark.parametrize("proj", ["gate_up", "down"])
-def test_config5_gather(bmv, fmt, proj):
-    m = workloads.config5(fmt, proj)
+def test_moe_gather(bmv, fmt, proj):
+    m = workloads.moe_case(fmt, proj)
     d = _moe_dev(m)
-    say(f"config5 gather {fmt} {proj}")
+    say(f"MoE gather {fmt} {proj}")
     y = to_host(bmv.gather_qmv(d["x"], _moe_weights(bmv, m, d), d["lhs"], d["rhs"]), m.dtype)
     rows = sample_rows(m.N, 24, seed=5)
     for s in range(m.lhs.size):
@@ -350,7 +350,7 @@ def test_config5_gather(bmv, fmt, proj):
 @pytest.mark.parametrize("fmt", ["mxfp4", "affine"])
 def test_gather_equals_single_calls_bitwise(bmv, fmt):
     import torch
-    m = workloads.config5(fmt, "gate_up", E=16, hidden=1024, ffn=96, tokens=12, top_k=4)
+    m = workloads.moe_case(fmt, "gate_up", E=16, hidden=1024, ffn=96, tokens=12, top_k=4)
     d = _moe_dev(m)
     say(f"gather vs single calls {fmt}")
     yg = bmv.gather_qmv(d["x"], _moe_weights(bmv, m, d), d["lhs"], d["rhs"])
@@ -366,7 +366,7 @@ def test_gather_equals_single_calls_bitwise(bmv, fmt):
 
 def test_gather_out_of_range_rows_are_zero(bmv):
     import torch
-    m = workloads.config5("mxfp4", "gate_up", E=8, hidden=512, ffn=64, tokens=5, top_k=3)
+    m = workloads.moe_case("mxfp4", "gate_up", E=8, hidden=512, ffn=64, tokens=5, top_k=3)
     m.rhs = m.rhs.copy()
     m.lhs = m.lhs.copy()
     m.rhs[2] = 8               # expert == n_experts
@@ -428,7 +428,7 @@ def test_bias_sum_precision(bmv, dtype, bits):
 
 def test_output_guard_bytes_untouched(bmv):
     import torch
-    c = workloads.config2(17)
+    c = workloads.chain_case(17)
     d = case_to_dev(c)
     say("guard bytes around y")
     buf = torch.full((1, 17 + 64), -7.0, dtype=torch.bfloat16, device="cuda:0")

@@ -319,7 +319,7 @@ def test_precision_regression_input_is_sensitive():
 
 
 def test_gather_equals_per_slot_and_zero_rows():
-    m = workloads.config5("affine", "gate_up", E=6, hidden=64, ffn=16, tokens=3, top_k=2)
+    m = workloads.moe_case("affine", "gate_up", E=6, hidden=64, ffn=16, tokens=3, top_k=2)
     Wd = lambda e: oracle.dequant_affine(m.w[e], m.scales[e], m.biases[e], m.K, 4, 64, "bf16")
     lhs = m.lhs.copy()
     rhs = m.rhs.copy()
@@ -350,23 +350,23 @@ def test_abs_dot_brute_force():
 # ---------------------------------------------------------------------------
 
 def test_generators_follow_recipes():
-    c1 = workloads.config1()
+    c1 = workloads.small_affine_case()
     assert (c1.K, c1.N, c1.B, c1.bits, c1.group, c1.dtype) == (512, 256, 1, 4, 64, "f32")
     codes = oracle.unpack_codes(c1.w, 512, 4)
     assert set(np.unique(codes)) == set(range(16))
     s = c1.scales.astype(np.float64)
     assert s.min() >= 0.01 and s.max() <= 0.1
     assert np.all(np.abs(c1.biases.astype(np.float64) + 8 * s) <= 0.0100001)
-    m3 = workloads.config3("mxfp8", 1, N=64)
+    m3 = workloads.mlp_up_case("mxfp8", 1, N=64)
     assert not np.any((m3.w & 0x7F) == 0x7F)
     assert m3.scales.min() >= 120 and m3.scales.max() <= 130
-    n3 = workloads.config3("nvfp4", 1, N=64)
+    n3 = workloads.mlp_up_case("nvfp4", 1, N=64)
     v = oracle.e4m3_value(n3.scales)
     assert np.all(v >= 0) and np.isfinite(v).all() and n3.global_scale == 0.5
-    g = workloads.config5("mxfp4", "gate_up")
+    g = workloads.moe_case("mxfp4", "gate_up")
     assert g.lhs.shape == (128,) and g.w.shape == (64, 1536, 2048)
     per_tok = g.rhs.reshape(16, 8)
     assert all(len(set(r)) == 8 for r in per_tok.tolist())
-    d = workloads.config5("mxfp4", "down")
+    d = workloads.moe_case("mxfp4", "down")
     assert np.array_equal(d.rhs, g.rhs) and d.w.shape == (64, 4096, 768)
     assert np.array_equal(workloads.route_topk(np.array([[1.0, 3.0, 3.0, 0.0]]), 2), [[1, 2]])

@@ -198,20 +198,25 @@ def mxfp8_case(cfg_id: int, key: str, *, K: int, N: int, B: int, dtype: str = "b
 # the five workloads
 # ---------------------------------------------------------------------------
 
-def config1() -> QmvCase:
+def small_affine_case() -> QmvCase:
+    """Affine 4-bit g64, K=512, N=256, one f32 activation row."""
     return affine_case(1, "c1", bits=4, group=64, K=512, N=256, B=1, dtype="f32",
                        scale_range=(0.01, 0.1), bias_mode="centred8")
 
 
-C2_TAILS = (1, 3, 5, 12, 17)
+CHAIN_TAILS = (1, 3, 5, 12, 17)
 
 
-def config2(N: int = 2560) -> QmvCase:
+def chain_case(N: int = 2560) -> QmvCase:
+    """Affine 8-bit g64, K=2560, bf16: the decode-chain matrix (N=2560, or a
+    narrow tail N), with norm-preserving weights so 100 chained calls stay finite."""
     return affine_case(2, f"c2-N{N}", bits=8, group=64, K=2560, N=N, B=1, dtype="bf16",
                        bias_mode="chain")
 
 
-def config3(fmt: str, B: int, K: int = 4096, N: int = 14336) -> QmvCase:
+def mlp_up_case(fmt: str, B: int, K: int = 4096, N: int = 14336) -> QmvCase:
+    """An MLP up projection (K=4096, N=14336) in MXFP4, NVFP4 (global 0.5) or
+    MXFP8, B bf16 activation rows."""
     key = f"c3-{fmt}-B{B}"
     if fmt == "mxfp4":
         return mxfp4_case(3, key, K=K, N=N, B=B)
@@ -222,7 +227,9 @@ def config3(fmt: str, B: int, K: int = 4096, N: int = 14336) -> QmvCase:
     raise ValueError(fmt)
 
 
-def config4(bits: int, group: int, B: int, dtype: str, K: int = 4096, N: int = 4096) -> QmvCase:
+def affine_sweep_case(bits: int, group: int, B: int, dtype: str, K: int = 4096,
+                      N: int = 4096) -> QmvCase:
+    """One point of the affine sweep: bits x group x B x activation dtype at K=N=4096."""
     return affine_case(4, f"c4-b{bits}-g{group}-B{B}-{dtype}", bits=bits, group=group, K=K,
                        N=N, B=B, dtype=dtype)
 
@@ -277,8 +284,8 @@ def route_topk(logits: np.ndarray, k: int) -> np.ndarray:
     return order[:, :k]
 
 
-def config5(fmt: str, proj: str, *, E: int = 64, hidden: int = 4096, ffn: int = 1536,
-            tokens: int = 16, top_k: int = 8, dtype: str = "bf16") -> MoeCase:
+def moe_case(fmt: str, proj: str, *, E: int = 64, hidden: int = 4096, ffn: int = 1536,
+             tokens: int = 16, top_k: int = 8, dtype: str = "bf16") -> MoeCase:
     """proj 'gate_up': K=hidden, N=ffn, x = token activations [tokens, hidden],
     slot s = (token s // top_k, its (s % top_k)-th expert). proj 'down':
     K=ffn, N=hidden, x = per-slot hidden states [tokens*top_k, ffn] ~ N(0,1),
@@ -417,7 +424,7 @@ def _moe_matrix(rng, fmt: str, E: int, N: int, K: int, dtype: str, bits: int, gr
 def moe_block_case(fmt: str, *, E: int = 64, hidden: int = 4096, ffn: int = 1536,
                    tokens: int = 16, top_k: int = 8, dtype: str = "bf16", key: str = "",
                    bits: int = 4, group: int = 64) -> MoeBlockCase:
-    """The routed-MoE block of config 5 (64 experts, hidden 4096, ffn 1536,
+    """The routed-MoE block of the MoE workload (64 experts, hidden 4096, ffn 1536,
     16 tokens, top-8) with separate gate / up / down stacks. Routing: logits
     ~ N(0, 1) [tokens, E], top_k by logit, router weights = softmax of the
     selected logits (renormalised over the top_k, fp64, stored fp32)."""
