@@ -305,7 +305,14 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
     constexpr int W = F::kWords;
     constexpr int kUnitBytes = 4 * W;
     constexpr int kPerVec = 16 / Store<DT>::kBytes;   // x values per 16-byte chunk
-    constexpr int kXAhead = 2;                        // x chunks per thread issued first
+    // x chunks per row and thread issued ahead of the weights. The short
+    // tile needs at most two (16-bit x) or four (f32) per row; f32 rows take
+    // four while B <= 2 (with more rows the 16 extra VGPRs cost occupancy).
+    // Longer rows take eight per row for B <= 2, four for B <= 4, two beyond
+    // (measured at K=14336: B=1 9.1 -> 8.2 us, B=2 14.2 -> 13.1 us); indices
+    // past the row clamp to its last chunk.
+    constexpr int kXAhead = kShort ? ((DT == DT_F32 && NB <= 2) ? 4 : 2)
+                                   : (NB <= 2 ? 8 : NB <= 4 ? 4 : 2);
     constexpr int kScAhead = 2;                       // scale words per thread issued first
 
     const int tid = threadIdx.x;
@@ -371,11 +378,18 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
         // it costs one cache line), which keeps the number of loads in flight
         // the same on every path and lets each wait name exactly the loads it
         // needs.
-        v4u xs[kXAhead];
-        static_for<0, kXAhead>([&](auto j_c) {
-            constexpr int j = decltype(j_c)::value;
-            const int v = min(tid + j * kThreads, vec_per_row - 1);
-            xs[j] = reinterpret_cast<const v4u*>(xr.row(0) + slab)[v];
+        // The first chunks of every activation row go out here, ahead of the
+        // weights: a chunk issued after them could only be staged once the
+        // weights had arrived (the counters retire in order), which put an
+        // HBM round trip in front of the x staging (B=4: 16.6 -> 12.9 us).
+        v4u xs[NB][kXAhead];
+        static_for<0, NB>([&](auto b_c) {
+            constexpr int b = decltype(b_c)::value;
+            static_for<0, kXAhead>([&](auto j_c) {
+                constexpr int j = decltype(j_c)::value;
+                const int v = min(tid + j * kThreads, vec_per_row - 1);
+                xs[b][j] = reinterpret_cast<const v4u*>(xr.row(b) + slab)[v];
+            });
         });
 
         // (1b) the first words of the tile's scale segment (when the scale
@@ -435,27 +449,22 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
         load_unit(A, u0 + min(gl, us - 1));
         load_unit(Bq, u0 + min(gl + lpr, us - 1));
 
-        // (3) x chunks to LDS; the rest of row 0 and the other rows are
-        // loaded and stored here
-        static_for<0, kXAhead>([&](auto j_c) {
-            constexpr int j = decltype(j_c)::value;
-            const int v = tid + j * kThreads;
-            if (v < vec_per_row)
-                *reinterpret_cast<v4u*>(lds + x_lds_slot(v * kPerVec, us)) =
-                    stage_vec<FMT, BITS, DT>(xr.stage(0, slab + v * kPerVec, xs[j]));
-        });
-        for (int v = tid + kXAhead * kThreads; v < vec_per_row; v += kThreads)
-            *reinterpret_cast<v4u*>(lds + x_lds_slot(v * kPerVec, us)) =
-                stage_vec<FMT, BITS, DT>(xr.stage(
-                    0, slab + v * kPerVec, reinterpret_cast<const v4u*>(xr.row(0) + slab)[v]));
-#pragma unroll
-        for (int b = 1; b < NB; ++b) {
-            const S* src = xr.row(b) + slab;
-            for (int v = tid; v < vec_per_row; v += kThreads)
+        // (3) x chunks to LDS; the rest of each row (slabs longer than
+        // kXAhead chunks per thread) is loaded and stored here
+        static_for<0, NB>([&](auto b_c) {
+            constexpr int b = decltype(b_c)::value;
+            static_for<0, kXAhead>([&](auto j_c) {
+                constexpr int j = decltype(j_c)::value;
+                const int v = tid + j * kThreads;
+                if (v < vec_per_row)
+                    *reinterpret_cast<v4u*>(lds + b * ks + x_lds_slot(v * kPerVec, us)) =
+                        stage_vec<FMT, BITS, DT>(xr.stage(b, slab + v * kPerVec, xs[b][j]));
+            });
+            for (int v = tid + kXAhead * kThreads; v < vec_per_row; v += kThreads)
                 *reinterpret_cast<v4u*>(lds + b * ks + x_lds_slot(v * kPerVec, us)) =
-                    stage_vec<FMT, BITS, DT>(
-                        xr.stage(b, slab + v * kPerVec, reinterpret_cast<const v4u*>(src)[v]));
-        }
+                    stage_vec<FMT, BITS, DT>(xr.stage(
+                        b, slab + v * kPerVec, reinterpret_cast<const v4u*>(xr.row(b) + slab)[v]));
+        });
         // (3b) scale segment to LDS
         if (nw > 0) {
             static_for<0, kScAhead>([&](auto j_c) {
