@@ -61,24 +61,34 @@ struct Geom {
 
 // x rows of a tile. Contiguous rows (qmv) or rows picked by an index list
 // held in LDS (gather); `row(b)` is called with a run-time b.
-// x row accessors of a tile: row(b) is batch row b; stage(b, k, v) is the
-// 16-byte chunk v of that row starting at element k as it goes into LDS (each
-// element of the block's rows is staged exactly once, by one thread);
-// finish() runs in every thread after the tile's sums and before its stores;
-// out(b, v) is row b's fp32 result before the final rounding.
+// x row accessors of a tile: row(b) is batch row b; load(b, k) issues the
+// global loads of the 16-byte chunk of that row starting at element k (and of
+// whatever its staging needs) and returns them as a Chunk; stage(b, k, c) is
+// that chunk as it goes into LDS (each element of the block's rows is staged
+// exactly once, by one thread); finish() runs in every thread after the
+// tile's sums and before its stores; out(b, v) is row b's fp32 result before
+// the final rounding.
 template <class S> struct XContig {
+    using Chunk = v4u;
     const S* x;
     int64_t K;
     __device__ const S* row(int b) const { return x + (int64_t)b * K; }
-    __device__ v4u stage(int, int64_t, v4u v) const { return v; }
+    __device__ Chunk load(int b, int64_t k) const {
+        return *reinterpret_cast<const v4u*>(row(b) + k);
+    }
+    __device__ v4u stage(int, int64_t, const Chunk& c) const { return c; }
     __device__ void finish() const {}
     __device__ float out(int, float v) const { return v; }
 };
 template <class S> struct XListed {
+    using Chunk = v4u;
     const S* x;
     const int64_t* off;  // LDS: element offset of each staged row
     __device__ const S* row(int b) const { return x + off[b]; }
-    __device__ v4u stage(int, int64_t, v4u v) const { return v; }
+    __device__ Chunk load(int b, int64_t k) const {
+        return *reinterpret_cast<const v4u*>(row(b) + k);
+    }
+    __device__ v4u stage(int, int64_t, const Chunk& c) const { return c; }
     __device__ void finish() const {}
     __device__ float out(int, float v) const { return v; }
 };
@@ -98,9 +108,18 @@ template <int DT, int NB> struct XNorm {
     float* red;       // LDS [NB][kWaves]
     mutable float ss[NB];
     mutable float r[NB];
+    // gamma is loaded with x, so both are in flight before the weights
+    struct Chunk {
+        v4u x, g;
+    };
     __device__ const S* row(int b) const { return x + (int64_t)b * K; }
-    __device__ v4u stage(int b, int64_t k, v4u v) const {
-        const v4u gv = *reinterpret_cast<const v4u*>(gamma + k);
+    __device__ Chunk load(int b, int64_t k) const {
+        return Chunk{*reinterpret_cast<const v4u*>(row(b) + k),
+                     *reinterpret_cast<const v4u*>(gamma + k)};
+    }
+    __device__ v4u stage(int b, int64_t, const Chunk& c) const {
+        const v4u v = c.x;
+        const v4u gv = c.g;
         const uint32_t xi[4] = {v.x, v.y, v.z, v.w};
         const uint32_t gi[4] = {gv.x, gv.y, gv.z, gv.w};
         uint32_t o[4];
@@ -382,13 +401,13 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
         // weights: a chunk issued after them could only be staged once the
         // weights had arrived (the counters retire in order), which put an
         // HBM round trip in front of the x staging (B=4: 16.6 -> 12.9 us).
-        v4u xs[NB][kXAhead];
+        typename XR::Chunk xs[NB][kXAhead];
         static_for<0, NB>([&](auto b_c) {
             constexpr int b = decltype(b_c)::value;
             static_for<0, kXAhead>([&](auto j_c) {
                 constexpr int j = decltype(j_c)::value;
                 const int v = min(tid + j * kThreads, vec_per_row - 1);
-                xs[b][j] = reinterpret_cast<const v4u*>(xr.row(b) + slab)[v];
+                xs[b][j] = xr.load(b, slab + (int64_t)v * kPerVec);
             });
         });
 
@@ -463,7 +482,7 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
             for (int v = tid + kXAhead * kThreads; v < vec_per_row; v += kThreads)
                 *reinterpret_cast<v4u*>(lds + b * ks + x_lds_slot(v * kPerVec, us)) =
                     stage_vec<FMT, BITS, DT>(xr.stage(
-                        b, slab + v * kPerVec, reinterpret_cast<const v4u*>(xr.row(b) + slab)[v]));
+                        b, slab + v * kPerVec, xr.load(b, slab + (int64_t)v * kPerVec)));
         });
         // (3b) scale segment to LDS
         if (nw > 0) {
