@@ -23,7 +23,7 @@ def bmv():
     import torch
     import bit_matrix_vector_amd as m
     assert torch.cuda.is_available()
-    m.load()  # a GPU machine without the built library must fail here, loudly
+    m.load()  # a machine without the built library must fail here, loudly
     return m
 
 
