@@ -1426,8 +1426,258 @@ int launch_qmv_norm_t(const LaunchParams& p, const NormArgs& na, hipStream_t st)
     }
 }
 
+// ---------------------------------------------------------------------------
+// QMV on the matrix cores for several activation rows of the block-scaled
+// formats (16-bit activations). With B rows the VALU tile does B dot products
+// per decoded code pair, which makes it issue-bound from B = 3 on; here the
+// products run on v_mfma_f32_32x32x16 with the weights as the A operand and
+// the x rows as the B operand (columns past B repeat row B - 1 and are never
+// stored), so the VALU only decodes. A block owns 32 weight rows; its four
+// waves take contiguous quarters of the row's 64-code segments, so each wave
+// reads whole 128-byte lines over consecutive segments (with segments dealt
+// round-robin, four waves shared every line and the kernel fetched most of
+// it several times). In a segment a lane (row r = lane % 32, half h = lane / 32) holds
+// the 32 codes [32 h, 32 h + 32), one scale block (NVFP4: two), converted in
+// registers; k-step s of the MFMA takes codes 32 h + 8 s .. + 8 from both
+// operands, so every k slot pairs x and W at the same code. x is staged in
+// LDS, zero-padded to whole segments; the four waves' fp32 tiles are added
+// in LDS in wave order, then rounded once. The weights load plainly: a line
+// is read by four consecutive segment loads of one wave. The sum over a row's K therefore
+// runs in a fixed order (per segment inside the MFMA, segments in each wave's
+// order, waves 0..3) and every launch gives the same bits.
+// ---------------------------------------------------------------------------
+typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
+template <int DT> struct Mfma;
+template <> struct Mfma<DT_BF16> {
+    typedef __bf16 v8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+    __device__ static inline f32x16_t run(v8 a, v8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mfma<DT_F16> {
+    typedef _Float16 v8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
+    __device__ static inline f32x16_t run(v8 a, v8 b, f32x16_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+constexpr int kMfmaRows = 32;    // weight rows per block
+constexpr int kMfmaDepth = 4;    // segments in flight per lane (a register ring)
+constexpr int kMfmaXAhead = 8;   // x chunks per thread loaded ahead of the weights
+constexpr int kMfmaRedBytes = kWaves * 32 * 32 * 4;   // the waves' fp32 tiles
+
+// LDS of one launch: x padded to whole 64-code segments, then the waves' tiles
+inline size_t mfma_lds_bytes(const LaunchParams& p) {
+    const int64_t kpad = (p.K + 63) / 64 * 64;
+    return (size_t)(p.B * kpad * 2) + kMfmaRedBytes;
+}
+
+template <int DT, int FMT>
+__global__ __launch_bounds__(kThreads) void qmv_mfma_kernel(LaunchParams p) {
+    static_assert(FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8, "block-scaled only");
+    using S = typename Store<DT>::S;
+    using V8 = typename Mfma<DT>::v8;
+    constexpr int kCW = FMT == FMT_MXFP8 ? 8 : 4;   // code words per lane and segment
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int ln = lane & 31;
+    const int hf = lane >> 5;
+    const int wave = tid >> 6;
+    const int B = (int)p.B;
+    const int64_t K = p.K, N = p.N;
+    const int kpad = (int)((K + 63) / 64 * 64);
+    const int nseg = kpad / 64;
+    const int64_t n0 = (int64_t)blockIdx.x * kMfmaRows;
+    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                     // [B][kpad]
+    float* red = reinterpret_cast<float*>(smem + (size_t)B * kpad * 2);   // [kWaves][32 * 32]
+    const S* x = static_cast<const S*>(p.x);
+
+    // x chunks: chunk v of the staged [B][kpad] block is row v / (kpad / 8),
+    // elements 8 (v % (kpad / 8)) ..; chunks past K are zeros
+    const int cpr = kpad / 8;
+    const int nchunks = B * cpr;
+    auto x_src = [&](int v) __attribute__((always_inline)) {
+        const int b = v / cpr;
+        const int64_t k = (int64_t)(v - b * cpr) * 8;
+        return reinterpret_cast<const v4u*>(x + (int64_t)b * K + (k < K ? k : K - 8));
+    };
+    auto x_ok = [&](int v) __attribute__((always_inline)) {
+        return (int64_t)(v - (v / cpr) * cpr) * 8 < K;
+    };
+    v4u xa[kMfmaXAhead];
+#pragma unroll
+    for (int j = 0; j < kMfmaXAhead; ++j) xa[j] = *x_src(min(tid + j * kThreads, nchunks - 1));
+
+    // this lane's weight row (clamped to N - 1) and its segments g = g0 + i,
+    // i < cnt: the wave's contiguous quarter of the row
+    const int64_t row = n0 + ln < N ? n0 + ln : N - 1;
+    const uint8_t* wrow = p.w + row * p.row_bytes;
+    const uint8_t* srow = static_cast<const uint8_t*>(p.scales) + row * p.sc_per_row;
+    const int per = (nseg + kWaves - 1) / kWaves;
+    const int g0 = wave * per;
+    const int cnt = nseg > g0 ? (nseg - g0 < per ? nseg - g0 : per) : 0;
+    struct Seg {
+        uint32_t w[kCW];
+        uint32_t s;
+    };
+    auto load = [&](Seg& b, int i) __attribute__((always_inline)) {
+        const int ic = i < cnt ? i : (cnt > 0 ? cnt - 1 : 0);
+        const int64_t hk0 = (int64_t)(g0 + ic) * 64 + 32 * hf;
+        const int64_t hk = hk0 < K ? hk0 : K - 32;   // first code of the lane's half
+        load_words<kCW>(wrow + (FMT == FMT_MXFP8 ? hk : hk / 2), b.w);
+        if constexpr (FMT == FMT_NVFP4)   // two E4M3 bytes (the scales may be byte-aligned)
+            b.s = (uint32_t)srow[hk / 16] | ((uint32_t)srow[hk / 16 + 1] << 8);
+        else
+            b.s = srow[hk / 32];
+    };
+    Seg ring[kMfmaDepth];
+    static_for<0, kMfmaDepth>([&](auto d_c) { load(ring[decltype(d_c)::value], decltype(d_c)::value); });
+
+    // x to LDS (the loads above went out before the weights)
+#pragma unroll
+    for (int j = 0; j < kMfmaXAhead; ++j) {
+        const int v = tid + j * kThreads;
+        if (v < nchunks)
+            *reinterpret_cast<v4u*>(xs + (size_t)v * 8) = x_ok(v) ? xa[j] : v4u{0u, 0u, 0u, 0u};
+    }
+    for (int v = tid + kMfmaXAhead * kThreads; v < nchunks; v += kThreads)
+        *reinterpret_cast<v4u*>(xs + (size_t)v * 8) = x_ok(v) ? *x_src(v) : v4u{0u, 0u, 0u, 0u};
+    __syncthreads();
+
+    const uint16_t* xrow = xs + (size_t)(ln < B ? ln : B - 1) * kpad + 32 * hf;
+    f32x16_t acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    auto step = [&](int i, Seg& b) __attribute__((always_inline)) {
+        const int g = g0 + i;
+        const bool hv = (int64_t)g * 64 + 32 * hf < K;
+        uint32_t a[4][4];
+        if constexpr (FMT == FMT_MXFP4) {
+            const float sc = __uint_as_float(b.s << 23);
+            static_for<0, 4>([&](auto s_c) {
+                constexpr int s = decltype(s_c)::value;
+                static_for<0, 4>([&](auto e_c) {
+                    constexpr int e = decltype(e_c)::value;
+                    if constexpr (DT == DT_BF16)
+                        a[s][e] = __builtin_bit_cast(
+                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b.w[s], sc, e));
+                    else
+                        a[s][e] = __builtin_bit_cast(
+                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(b.w[s], sc, e));
+                });
+            });
+        } else if constexpr (FMT == FMT_MXFP8) {
+            const float sc = __uint_as_float(b.s << 23);
+            static_for<0, 4>([&](auto s_c) {
+                constexpr int s = decltype(s_c)::value;
+                static_for<0, 2>([&](auto e_c) {
+                    constexpr int e = decltype(e_c)::value;
+                    const uint32_t wd = b.w[2 * s + e];
+                    if constexpr (DT == DT_BF16) {
+                        a[s][2 * e] = __builtin_bit_cast(
+                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd, sc, false));
+                        a[s][2 * e + 1] = __builtin_bit_cast(
+                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd, sc, true));
+                    } else {
+                        a[s][2 * e] = __builtin_bit_cast(
+                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd, sc, false));
+                        a[s][2 * e + 1] = __builtin_bit_cast(
+                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd, sc, true));
+                    }
+                });
+            });
+        } else {
+            // E2M1 times its E4M3 block scale, exact in fp32 and in the 16-bit
+            // type (at most 6 significant bits); codes 0..15 take the first byte
+            const f32x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(b.s, 1.0f, false);
+            static_for<0, 4>([&](auto s_c) {
+                constexpr int s = decltype(s_c)::value;
+                const float scs = s < 2 ? sc.x : sc.y;
+                static_for<0, 4>([&](auto e_c) {
+                    constexpr int e = decltype(e_c)::value;
+                    const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(b.w[s], 1.0f, e);
+                    const f32x2 q = {v.x * scs, v.y * scs};
+                    if constexpr (DT == DT_BF16)
+                        a[s][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(q, bf16x2_t));
+                    else
+                        a[s][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(q, f16x2_t));
+                });
+            });
+        }
+        if (!hv) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) a[s][e] = 0u;
+        }
+        load(b, i + kMfmaDepth);
+        static_for<0, 4>([&](auto s_c) {
+            constexpr int s = decltype(s_c)::value;
+            const V8 xb = *reinterpret_cast<const V8*>(xrow + (size_t)g * 64 + 8 * s);
+            const V8 wa = __builtin_bit_cast(V8, v4u{a[s][0], a[s][1], a[s][2], a[s][3]});
+            acc = Mfma<DT>::run(wa, xb, acc);
+        });
+    };
+    int i = 0;
+    for (; i + kMfmaDepth <= cnt; i += kMfmaDepth) {
+        static_for<0, kMfmaDepth>([&](auto d_c) {
+            constexpr int d = decltype(d_c)::value;
+            step(i + d, ring[d]);
+        });
+    }
+    static_for<0, kMfmaDepth>([&](auto d_c) {
+        constexpr int d = decltype(d_c)::value;
+        if (i + d < cnt) step(i + d, ring[d]);
+    });
+
+    // the waves' tiles to LDS (element (m, n): weight row m, activation row n)
+    float* mine = red + wave * 32 * 32;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) mine[(8 * (e >> 2) + 4 * hf + (e & 3)) * 32 + ln] = acc[e];
+    __syncthreads();
+    const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
+    for (int idx = tid; idx < 32 * B; idx += kThreads) {
+        const int m = idx / B, b = idx - (idx / B) * B;
+        if (n0 + m >= N) continue;
+        float t = red[m * 32 + b];
+#pragma unroll
+        for (int w = 1; w < kWaves; ++w) t += red[w * 32 * 32 + m * 32 + b];
+        if constexpr (FMT == FMT_NVFP4) t = t * gmul;
+        static_cast<S*>(p.y)[(int64_t)b * N + n0 + m] = Store<DT>::from_f32(t);
+    }
+}
+
+// The matrix-core QMV replaces the VALU tile at B = 8 (bf16 activations,
+// MXFP4 / NVFP4 / MXFP8), where the VALU tile does eight dot products per
+// decoded pair: K=4096 N=14336 27.6 -> 16.7 us, N=4096 12.2 -> 10.9 us,
+// K=1088 N=300 16.6 -> 4.6 us. At B = 3..7 it also wins on some shapes (B=5
+// N=14336: 16.5 -> 14.7 us; launches of under 256 VALU waves) but loses on
+// others (N=4096: B=4 6.2 vs 9.1 us); it stays at B = 8 so that a row of a
+// batch of up to seven equals the same row computed alone, bit for bit (the
+// two paths sum in different orders).
+constexpr size_t kMfmaMaxLds = 144 * 1024;
+inline bool use_mfma_qmv(const LaunchParams& p) {
+    return p.B == 8 && p.K > 0 && mfma_lds_bytes(p) <= kMfmaMaxLds;
+}
+
+template <int DT, int FMT>
+int launch_qmv_mfma(const LaunchParams& p, hipStream_t st) {
+    const size_t lds = mfma_lds_bytes(p);
+    auto* kern = &qmv_mfma_kernel<DT, FMT>;
+    static std::atomic<size_t> granted{0};
+    if (const int e = allow_lds(kern, lds, granted)) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((p.N + kMfmaRows - 1) / kMfmaRows)), dim3(kThreads),
+                       lds, st, p);
+    return (int)hipGetLastError();
+}
+
 template <int DT, int FMT, int BITS>
 int launch_qmv_t(const LaunchParams& p, hipStream_t st) {
+    if constexpr (DT == DT_BF16 &&
+                  (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
+        if (use_mfma_qmv(p)) return launch_qmv_mfma<DT, FMT>(p, st);
+    }
     const int nb = (int)p.B;
     switch (nb) {
 #define QMV_CASE(n)                                                                         \

@@ -299,12 +299,14 @@ def test_affine_sweep_sampled(bmv, bits, group, B, dtype):
 
 
 def test_batch_rows_equal_single_row_calls_bitwise(bmv):
+    # on the VALU tile (affine at any B; the block-scaled formats up to B = 7:
+    # B = 8 with bf16 runs on the matrix cores, tested below)
     import torch
     for fmt in ("affine", "mxfp4", "nvfp4", "mxfp8"):
         if fmt == "affine":
             c = workloads.affine_sweep_case(3, 64, 8, "bf16", N=256)
         else:
-            c = workloads.mlp_up_case(fmt, 8, N=256)
+            c = workloads.mlp_up_case(fmt, 7, N=256)
         d = case_to_dev(c)
         say(f"batch invariance {fmt}")
         yb = run_qmv(bmv, c, d)
@@ -312,6 +314,54 @@ def test_batch_rows_equal_single_row_calls_bitwise(bmv):
             db = dict(d, x=d["x"][b:b + 1].contiguous())
             y1 = run_qmv(bmv, c, db)
             assert torch.equal(y1[0].view(torch.int16), yb[b].view(torch.int16)), (fmt, b)
+
+
+# ---------------------------------------------------------------------------
+# B = 8 with bf16 activations and block-scaled weights: the matrix-core QMV
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
+def test_b8_matrix_core_ragged(bmv, fmt):
+    # K % 64 == 32 (a half segment at the end of every row), N not a multiple
+    # of the 32-row block, K short enough that some waves get no segment
+    for K, N in ((1056, 301), (96, 70), (4096, 33)):
+        c = workloads.mlp_up_case(fmt, 8, K=K, N=N)
+        say(f"b8 matrix cores {fmt} K={K} N={N}")
+        y = to_host(run_qmv(bmv, c), c.dtype)
+        y64, A = oracle_rows(c, np.arange(N))
+        check(y, y64, A, c.dtype, f"b8 {fmt} K={K} N={N}")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
+def test_b8_matrix_core_full_size_sampled(bmv, fmt):
+    c = workloads.mlp_up_case(fmt, 8)
+    say(f"b8 matrix cores {fmt} K4096 N14336")
+    y = to_host(run_qmv(bmv, c), c.dtype)
+    rows = sample_rows(c.N, 128, seed=8)
+    y64, A = oracle_rows(c, rows)
+    check(y[:, rows], y64, A, c.dtype, f"b8 {fmt} K4096 N14336")
+
+
+def test_b8_matrix_core_bitwise_properties(bmv):
+    # same bits on every call; each activation row's result independent of
+    # the other rows (a permuted batch gives the permuted rows); rows < n of a
+    # call on the first n weight rows equal those of the full call
+    import torch
+    c = workloads.mlp_up_case("mxfp4", 8, K=2048, N=200)
+    d = case_to_dev(c)
+    say("b8 matrix cores: repeat, permutation, tail")
+    y1 = run_qmv(bmv, c, d)
+    y2 = run_qmv(bmv, c, d)
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    perm = torch.tensor([5, 2, 7, 0, 1, 6, 3, 4], device=d["x"].device)
+    yp = run_qmv(bmv, c, dict(d, x=d["x"][perm].contiguous()))
+    assert torch.equal(yp.view(torch.int16), y1[perm].view(torch.int16))
+    for n in (1, 31, 33, 100):
+        sub = dict(d, w=d["w"][:n].contiguous(), scales=d["scales"][:n].contiguous())
+        c_sub = workloads.QmvCase(c.fmt, c.dtype, c.B, c.K, n, c.w[:n], c.scales[:n], c.x,
+                                  global_scale=c.global_scale)
+        part = run_qmv(bmv, c_sub, sub)
+        assert torch.equal(part.view(torch.int16), y1[:, :n].view(torch.int16)), n
 
 
 # ---------------------------------------------------------------------------
