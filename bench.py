@@ -809,6 +809,7 @@ def main() -> int:
                         ("mxfp8 B1 K4096 N14336 bf16", workloads.mlp_up_case("mxfp8", 1)),
                         ("affine 4b g64 B1 K4096 N4096 bf16", workloads.affine_sweep_case(4, 64, 1, "bf16")),
                         ("mxfp4 B4 K4096 N14336 bf16", workloads.mlp_up_case("mxfp4", 4)),
+                        ("mxfp4 B8 K4096 N14336 bf16 (matrix cores)", workloads.mlp_up_case("mxfp4", 8)),
                         *((f"{f} B1 K4096 N14336 bf16",
                            workloads.sb_case(f, K=4096, N=14336, B=1, key="bench"))
                           for f in ("mxfp8_e5m2", "nvfp8", "fp8_e5m2_f16", "int4", "mxint8"))):
