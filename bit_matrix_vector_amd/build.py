@@ -38,8 +38,9 @@ CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 def _jobs() -> list[tuple[list[str], str]]:
     jobs = []
-    for dt in (0, 1, 2):
-        for fam in (0, 1, 2, 3, 4):
+    # the heaviest slices (affine codes) first, so the pool's tail is short
+    for fam in (0, 5, 1, 2, 3, 4):
+        for dt in (0, 1, 2):
             obj = os.path.join(BUILD, f"qmv_inst_{dt}_{fam}.o")
             jobs.append(([HIPCC, *HIP_FLAGS, f"-DQMV_DT={dt}", f"-DQMV_FAM={fam}", "-c",
                           os.path.join(CSRC, "qmv_inst.hip"), "-o", obj], obj))
@@ -63,11 +64,13 @@ def _jobs() -> list[tuple[list[str], str]]:
     return jobs
 
 
-def _run(cmd: list[str]) -> None:
+def _run(cmd: list[str]) -> float:
+    t0 = time.time()
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
         raise RuntimeError(f"build step failed ({r.returncode}): {' '.join(cmd)}\n{out}")
+    return time.time() - t0
 
 
 def build(verbose: bool = False) -> str:
@@ -81,8 +84,10 @@ def build(verbose: bool = False) -> str:
     workers = max(1, min(len(jobs), int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
     with cf.ThreadPoolExecutor(max_workers=workers) as ex:
         futs = [ex.submit(_run, cmd) for cmd, _ in jobs]
-        for f in futs:
-            f.result()
+        secs = [f.result() for f in futs]
+    if verbose:
+        for (cmd, obj), t in sorted(zip(jobs, secs), key=lambda js: -js[1]):
+            print(f"  {t:6.1f} s  {os.path.basename(obj)}", flush=True)
     objs = [o for _, o in jobs]
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])

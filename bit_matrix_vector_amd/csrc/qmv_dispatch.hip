@@ -20,10 +20,21 @@ QMV_DECL_SB(1, 4) QMV_DECL_SB(2, 2) QMV_DECL_SB(2, 3) QMV_DECL_SB(2, 4)
     int launch_dequant_part_##dt##_##fam(const LaunchParams&, float*, void*);
 QMV_DECL_PART(0, 0) QMV_DECL_PART(0, 1) QMV_DECL_PART(1, 0)
 QMV_DECL_PART(1, 1) QMV_DECL_PART(2, 0) QMV_DECL_PART(2, 1)
+QMV_DECL_PART(0, 5) QMV_DECL_PART(1, 5) QMV_DECL_PART(2, 5)
 #undef QMV_DECL_PART
 
+// affine codes of 5, 6 and 8 bits live in slice 5, those of 2, 3 and 4 bits
+// in slice 0, MXFP4 / NVFP4 / MXFP8 in slice 1
 #define QMV_ROUTE(name, ...)                                                            \
     do {                                                                                \
+        if (p.format == FMT_AFFINE && p.bits >= 5) {                                    \
+            switch (p.dtype) {                                                          \
+                case 0: return name##_0_5(__VA_ARGS__);                                 \
+                case 1: return name##_1_5(__VA_ARGS__);                                 \
+                case 2: return name##_2_5(__VA_ARGS__);                                 \
+                default: return (int)hipErrorInvalidValue;                              \
+            }                                                                           \
+        }                                                                               \
         const int fam = p.format == FMT_AFFINE ? 0 : 1;                                 \
         switch (p.dtype * 2 + fam) {                                                    \
             case 0: return name##_0_0(__VA_ARGS__);                                     \

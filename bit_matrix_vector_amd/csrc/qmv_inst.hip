@@ -1,7 +1,9 @@
 // One slice of the kernel instantiations: the dtype QMV_DT (0 f32, 1 f16,
-// 2 bf16) and the format family QMV_FAM (0 affine; 1 MXFP4 / NVFP4 / MXFP8;
-// 2, 3, 4 the symmetric block-scaled family with E8M0, FP32 and FP16 scales,
-// QMV and dequant only). The build compiles this file once per (dtype,
+// 2 bf16) and the format family QMV_FAM (0 affine codes of 2, 3 and 4 bits,
+// 5 affine codes of 5, 6 and 8 bits; 1 MXFP4 / NVFP4 / MXFP8; 2, 3, 4 the
+// symmetric block-scaled family with E8M0, FP32 and FP16 scales, QMV and
+// dequant only). The affine codes take two slices because they are the
+// heaviest to compile. The build compiles this file once per (dtype,
 // family) pair, in parallel.
 #include "qmv_kernels.cuh"
 
@@ -26,6 +28,11 @@ int dispatch_part(const LaunchParams& p, A... a) {
         case 2: return L<QMV_DT, FMT_AFFINE, 2>::run(p, a...);
         case 3: return L<QMV_DT, FMT_AFFINE, 3>::run(p, a...);
         case 4: return L<QMV_DT, FMT_AFFINE, 4>::run(p, a...);
+        default: return (int)hipErrorInvalidValue;
+    }
+#elif QMV_FAM == 5
+    if (p.format != FMT_AFFINE) return (int)hipErrorInvalidValue;
+    switch (p.bits) {
         case 5: return L<QMV_DT, FMT_AFFINE, 5>::run(p, a...);
         case 6: return L<QMV_DT, FMT_AFFINE, 6>::run(p, a...);
         case 8: return L<QMV_DT, FMT_AFFINE, 8>::run(p, a...);
@@ -93,7 +100,7 @@ template <int DT, int FMT, int BITS> struct DequantL {
 int QMV_PART(launch_qmv_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, void* stream) {
     return dispatch_part<QmvL>(p, static_cast<hipStream_t>(stream));
 }
-#if QMV_FAM <= 1
+#if QMV_FAM <= 1 || QMV_FAM == 5
 int QMV_PART(launch_qmv_norm_part_, QMV_DT, QMV_FAM)(const LaunchParams& p, const NormArgs& na,
                                                       void* stream) {
     return dispatch_part<QmvNormL>(p, na, static_cast<hipStream_t>(stream));
