@@ -1605,12 +1605,12 @@ __global__ __launch_bounds__(kThreads) void qmv_mfma_kernel(LaunchParams p) {
                 });
             });
         }
-        if (!hv) {
+        // a half past K enters as zeros: a select, since the two halves of a
+        // wave differ (as a branch it cost a wait for every load in flight)
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) a[s][e] = 0u;
-        }
+            for (int e = 0; e < 4; ++e) a[s][e] = hv ? a[s][e] : 0u;
         load(b, i + kMfmaDepth);
         static_for<0, 4>([&](auto s_c) {
             constexpr int s = decltype(s_c)::value;
