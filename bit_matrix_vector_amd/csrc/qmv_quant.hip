@@ -237,9 +237,23 @@ template <int DT>
 __global__ __launch_bounds__(kQThreads) void absmax_kernel(const typename Store<DT>::S* __restrict__ w,
                                                            int64_t n8, uint32_t* __restrict__ out) {
     __shared__ float part[kQThreads / 64];
+    // four 8-element loads in flight per thread before any is used (one at a
+    // time left the pass waiting on each load); fmaxf ignores NaN, so the
+    // maximum does not depend on the order it is taken in
+    constexpr int U = 4;
+    const int64_t stride = (int64_t)gridDim.x * kQThreads;
     float a = 0.0f;
-    for (int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x; i < n8;
-         i += (int64_t)gridDim.x * kQThreads) {
+    int64_t i = (int64_t)blockIdx.x * kQThreads + threadIdx.x;
+    for (; i + (U - 1) * stride < n8; i += U * stride) {
+        float v[U][8];
+#pragma unroll
+        for (int u = 0; u < U; ++u) load8<DT>(w + ((i + u * stride) << 3), v[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) a = fmaxf(a, fabsf(v[u][j]));
+    }
+    for (; i < n8; i += stride) {
         float v[8];
         load8<DT>(w + (i << 3), v);
 #pragma unroll
@@ -339,8 +353,10 @@ int launch_quant_t(const QuantParams& q, hipStream_t st) {
             uint32_t* g = reinterpret_cast<uint32_t*>(q.global_scale);
             hipLaunchKernelGGL(zero_word_kernel, dim3(1), dim3(1), 0, st, g);
             const int64_t n8 = q.N * (q.K >> 3);
+            // about four 8-element groups per thread: 2048 blocks cover the
+            // benchmark matrix; never more blocks than groups of 256 threads
             int64_t rb = (n8 + kQThreads - 1) / kQThreads;
-            if (rb > 4096) rb = 4096;
+            if (rb > 2048) rb = 2048;
             hipLaunchKernelGGL((absmax_kernel<DT>), dim3((unsigned)rb), dim3(kQThreads), 0, st, w,
                                n8, g);
             hipLaunchKernelGGL((quantize_nvfp4_kernel<DT>), grid, dim3(kQThreads), 0, st, w, q.N, q.K,
