@@ -206,17 +206,21 @@ __global__ __launch_bounds__(kQThreads) void quantize_mx_kernel(
     a = group_max<L>(a);
     int e = 0;
     if (a > 0.0f) e = min(max(floor_log2(a) - (kFp8 ? 8 : 2) + 127, 0), 254);
-    const float X = pow2(e - 127);
+    // w / 2^(e - 127) as w * 2^(127 - e): the reciprocal of a power of two in
+    // [2^-127, 2^127] is exact in fp32 (2^-127 as a subnormal), so the product
+    // is the correctly rounded quotient, bit for bit, at a fraction of the
+    // cost of an IEEE division
+    const float Xinv = pow2(127 - e);
     if (!live) return;
     if constexpr (kFp8) {
         uint64_t out = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) out |= (uint64_t)e4m3_encode(v[j] / X) << (8 * j);
+        for (int j = 0; j < 8; ++j) out |= (uint64_t)e4m3_encode(v[j] * Xinv) << (8 * j);
         *reinterpret_cast<uint64_t*>(packed + row * K + k0) = out;
     } else {
         uint32_t out = 0;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) out |= e2m1_encode(v[j] / X) << (4 * j);
+        for (int j = 0; j < 8; ++j) out |= e2m1_encode(v[j] * Xinv) << (4 * j);
         *reinterpret_cast<uint32_t*>(packed + row * (K / 2) + (k0 >> 1)) = out;
     }
     if ((threadIdx.x & (L - 1)) == 0) scales[row * (K / 32) + k0 / 32] = (uint8_t)e;
