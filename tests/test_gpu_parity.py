@@ -324,7 +324,8 @@ def test_batch_rows_equal_single_row_calls_bitwise(bmv):
 def test_b8_matrix_core_ragged(bmv, fmt):
     # K % 64 == 32 (a half segment at the end of every row), N not a multiple
     # of the 32-row block, K short enough that some waves get no segment
-    for K, N in ((1056, 301), (96, 70), (4096, 33)):
+    # (K = 8192: 128 KB of staged x, the largest that takes this path)
+    for K, N in ((1056, 301), (96, 70), (4096, 33), (8192, 40)):
         c = workloads.mlp_up_case(fmt, 8, K=K, N=N)
         say(f"b8 matrix cores {fmt} K={K} N={N}")
         y = to_host(run_qmv(bmv, c), c.dtype)
