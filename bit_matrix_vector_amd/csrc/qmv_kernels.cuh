@@ -35,6 +35,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "qmv_common.h"
@@ -1355,19 +1356,35 @@ size_t stage_bytes(const LaunchParams& p, const Geom& g) {
                                            F::template elem_bytes<DT>());
 }
 
-// Dynamic LDS above 64 KB must be requested per kernel (gfx950 has 160 KB
-// per workgroup). `granted` is the caller's per-instantiation record of the
-// largest size already requested.
+// Dynamic LDS above `free_bytes` (64 KB, less what a kernel holds
+// statically) must be requested per kernel and device (gfx950 has 160 KB per
+// workgroup). `granted` is the caller's per-instantiation record, per device,
+// of the largest size already requested. Requests are made under one lock and
+// only ever raise the attribute, so the recorded size is always covered, also
+// when threads launch the same kernel with different sizes at once.
+constexpr int kMaxDevices = 64;
+struct LdsGrant {
+    std::atomic<size_t> dev[kMaxDevices];
+};
+inline std::mutex& lds_grant_mutex() {
+    static std::mutex m;
+    return m;
+}
 template <class Kern>
-int allow_lds(Kern* kern, size_t bytes, std::atomic<size_t>& granted) {
-    if (bytes <= 64 * 1024 || bytes <= granted.load(std::memory_order_relaxed)) return 0;
+int allow_lds(Kern* kern, size_t bytes, LdsGrant& granted, size_t free_bytes = 64 * 1024) {
+    if (bytes <= free_bytes) return 0;
+    int d = 0;
+    if (const hipError_t e = hipGetDevice(&d); e != hipSuccess) return (int)e;
+    if (d < 0 || d >= kMaxDevices) return (int)hipErrorInvalidDevice;
+    std::atomic<size_t>& slot = granted.dev[d];
+    if (bytes <= slot.load(std::memory_order_acquire)) return 0;
+    std::lock_guard<std::mutex> lock(lds_grant_mutex());
+    if (bytes <= slot.load(std::memory_order_relaxed)) return 0;
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize,
                                              (int)bytes);
     if (e != hipSuccess) return (int)e;
-    size_t cur = granted.load(std::memory_order_relaxed);
-    while (cur < bytes && !granted.compare_exchange_weak(cur, bytes)) {
-    }
+    slot.store(bytes, std::memory_order_release);
     return 0;
 }
 
@@ -1390,7 +1407,7 @@ int launch_qmv_r(const LaunchParams& p, hipStream_t st) {
     const size_t lds = stage_bytes<DT, FMT, BITS>(p, g);
     auto* kern = short_tile(p, g) ? &qmv_kernel<DT, FMT, BITS, NB, R, true>
                                   : &qmv_kernel<DT, FMT, BITS, NB, R, false>;
-    static std::atomic<size_t> granted_s{0}, granted_l{0};
+    static LdsGrant granted_s, granted_l;
     if (const int e = allow_lds(kern, lds, short_tile(p, g) ? granted_s : granted_l)) return e;
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, p, g);
     return (int)hipGetLastError();
@@ -1403,7 +1420,7 @@ int launch_qmv_norm_r(const LaunchParams& p, const NormArgs& na, hipStream_t st)
     const size_t lds = stage_bytes<DT, FMT, BITS>(p, g);
     auto* kern = short_tile(p, g) ? &qmv_norm_kernel<DT, FMT, BITS, NB, R, true>
                                   : &qmv_norm_kernel<DT, FMT, BITS, NB, R, false>;
-    static std::atomic<size_t> granted_s{0}, granted_l{0};
+    static LdsGrant granted_s, granted_l;
     if (const int e = allow_lds(kern, lds, short_tile(p, g) ? granted_s : granted_l)) return e;
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, p, g, na);
     return (int)hipGetLastError();
@@ -1665,7 +1682,7 @@ template <int DT, int FMT>
 int launch_qmv_mfma(const LaunchParams& p, hipStream_t st) {
     const size_t lds = mfma_lds_bytes(p);
     auto* kern = &qmv_mfma_kernel<DT, FMT>;
-    static std::atomic<size_t> granted{0};
+    static LdsGrant granted;
     if (const int e = allow_lds(kern, lds, granted)) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)((p.N + kMfmaRows - 1) / kMfmaRows)), dim3(kThreads),
                        lds, st, p);
@@ -1747,15 +1764,9 @@ int launch_moe_gate_up_t(const LaunchParams& p, const MoeArgs& m, hipStream_t st
     g.tiles_per_block = (int)tpb;
     const dim3 grid((unsigned)((n_tiles + tpb - 1) / tpb), (unsigned)(p.n_experts + 1));
     auto* kern = &gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherSwiglu>;
-    static std::atomic<size_t> granted{0};
-    if (lds > 32 * 1024 && lds > granted.load(std::memory_order_relaxed)) {
-        // the static slot lists ride on top of the dynamic x stage
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)lds);
-        if (e != hipSuccess) return (int)e;
-        granted.store(lds, std::memory_order_relaxed);
-    }
+    // the static slot lists ride on top of the dynamic x stage
+    static LdsGrant granted;
+    if (const int e = allow_lds(kern, lds, granted, 32 * 1024)) return e;
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, p, g, m);
     return (int)hipGetLastError();
 }
@@ -1782,14 +1793,8 @@ int launch_moe_down_t(const LaunchParams& p, const MoeArgs& m, hipStream_t st) {
     g.tiles_per_block = (int)tpb;
     const dim3 grid((unsigned)((n_tiles + tpb - 1) / tpb), (unsigned)p.n_x_rows);
     auto* kern = &moe_down_kernel<DT, FMT, BITS, R>;
-    static std::atomic<size_t> granted{0};
-    if (lds > 32 * 1024 && lds > granted.load(std::memory_order_relaxed)) {
-        const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize,
-                                                 (int)lds);
-        if (e != hipSuccess) return (int)e;
-        granted.store(lds, std::memory_order_relaxed);
-    }
+    static LdsGrant granted;
+    if (const int e = allow_lds(kern, lds, granted, 32 * 1024)) return e;
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, p, g, m);
     return (int)hipGetLastError();
 }

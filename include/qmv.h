@@ -45,7 +45,9 @@
  *   gives the message of the last failure on the calling thread. A launch
  *   failure reported by the HIP runtime maps to QMV_ERR_HIP (asynchronous
  *   faults surface at the caller's next synchronization, as with any kernel).
- * - Thread safety: the only state is a thread-local error message.
+ * - Thread safety: the state is a thread-local error message and, per kernel
+ *   and device, the largest dynamic LDS size already requested from the HIP
+ *   runtime (raised under a lock). Calls from several threads are safe.
  */
 #ifndef QMV_H
 #define QMV_H
