@@ -293,29 +293,52 @@ def test_scale_equivariance_powers_of_two():
     assert np.array_equal(yc, ya)
 
 
-def test_precision_regression_input_is_sensitive():
+# the tiny value of each 16-bit type: below half an ulp of 1.0 (bf16 ulp
+# 2^-7, f16 ulp 2^-10), so 1 + tiny rounds back to 1 in that type
+TINY = {"bf16": 2.0 ** -9, "f16": 2.0 ** -12}
+
+
+def _sum_in_type(xs, dtype):
+    """sum of stored values accumulated in the 16-bit type itself, each
+    partial sum rounded to it (the behaviour before the fix)."""
+    acc = 0.0
+    for k in range(xs.shape[-1]):
+        a = acc + oracle.storage_to_f64(xs[0, k:k + 1], dtype)[0]
+        acc = oracle.storage_to_f64(oracle.round_f64_to(np.array([a]), dtype), dtype)[0]
+    return acc
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_precision_regression_input_is_sensitive(dtype):
     # mlx pull request 4516: sum(x) for the affine bias term must widen each
-    # element before adding. Build a bf16 group with one large and many tiny x:
-    # summing in bf16 first drops the tiny ones, the oracle keeps them exactly.
+    # element before adding. One large and many tiny x in a group: summing in
+    # the 16-bit type first drops the tiny ones, the oracle keeps them exactly.
     K, group = 64, 64
-    x = np.full((1, K), 2.0 ** -9, dtype=np.float64)
+    tiny = TINY[dtype]
+    x = np.full((1, K), tiny, dtype=np.float64)
     x[0, 0] = 1.0
-    xs = workloads.to_storage(x, "bf16")
+    xs = workloads.to_storage(x, dtype)
     w = np.zeros((1, K // 2), dtype=np.uint8)             # q = 0 everywhere: y = bias * sum(x)
-    scales = workloads.to_storage(np.array([[0.01]]), "bf16")
-    biases = workloads.to_storage(np.array([[1.0]]), "bf16")
-    W = oracle.dequant_affine(w, scales, biases, K, 4, group, "bf16")
-    y = oracle.qmv(xs, "bf16", W)[0, 0]
-    exact = 1.0 + 63 * 2.0 ** -9
+    scales = workloads.to_storage(np.array([[0.01]]), dtype)
+    biases = workloads.to_storage(np.array([[1.0]]), dtype)
+    W = oracle.dequant_affine(w, scales, biases, K, 4, group, dtype)
+    y = oracle.qmv(xs, dtype, W)[0, 0]
+    exact = 1.0 + 63 * tiny
     assert y == exact
-    # the same sum accumulated in bf16 (the behaviour before the fix) loses it all
-    acc = np.uint16(0)
-    for k in range(K):
-        a = oracle.storage_to_f64(np.array([acc]), "bf16")[0] + oracle.storage_to_f64(xs[0, k:k + 1], "bf16")[0]
-        acc = oracle.round_f64_to_bf16_bits(np.array([a]))[0]
-    pre_fix = oracle.storage_to_f64(np.array([acc]), "bf16")[0]
-    ulp = oracle.ulp_of(oracle.round_f64_to_bf16_bits(np.array([exact])), "bf16")[0]
+    # the same sum accumulated in the 16-bit type loses every tiny value
+    pre_fix = _sum_in_type(xs, dtype)
+    assert pre_fix == 1.0
+    r = oracle.round_f64_to(np.array([exact]), dtype)
+    ulp = oracle.ulp_of(r, dtype)[0]
     assert abs(pre_fix - exact) > ulp
+    # and so does the GPU test's input (large x first in each group of 64)
+    K2 = 512
+    x2 = np.full((1, K2), tiny)
+    x2[0, ::group] = 1.0
+    xs2 = workloads.to_storage(x2, dtype)
+    for g in range(K2 // group):
+        assert _sum_in_type(xs2[:, g * group:(g + 1) * group], dtype) == 1.0
+        assert oracle.storage_to_f64(xs2[:, g * group:(g + 1) * group], dtype).sum() == exact
 
 
 def test_gather_equals_per_slot_and_zero_rows():
@@ -370,3 +393,72 @@ def test_generators_follow_recipes():
     d = workloads.moe_case("mxfp4", "down")
     assert np.array_equal(d.rhs, g.rhs) and d.w.shape == (64, 4096, 768)
     assert np.array_equal(workloads.route_topk(np.array([[1.0, 3.0, 3.0, 0.0]]), 2), [[1, 2]])
+
+
+# ---------------------------------------------------------------------------
+# qmv_rows: the product restricted to chosen output rows (sampled checks of
+# full-size problems use it)
+# ---------------------------------------------------------------------------
+
+def _rows_case(fmt, dtype, seed, K=96, N=11, B=2, bits=4, group=32):
+    key = f"rows-{fmt}-{dtype}-{bits}-{group}-{seed}"
+    if fmt == "affine":
+        return workloads.affine_case(98, key, bits=bits, group=group, K=K, N=N, B=B, dtype=dtype)
+    if fmt == "mxfp4":
+        return workloads.mxfp4_case(98, key, K=K, N=N, B=B, dtype=dtype)
+    if fmt == "nvfp4":
+        return workloads.nvfp4_case(98, key, K=K, N=N, B=B, dtype=dtype)
+    if fmt == "nvfp4-noglobal":
+        return workloads.nvfp4_case(98, key, K=K, N=N, B=B, dtype=dtype, global_scale=None)
+    if fmt == "mxfp8":
+        return workloads.mxfp8_case(98, key, K=K, N=N, B=B, dtype=dtype)
+    return workloads.sb_case(fmt, K=K, N=N, B=B, dtype=dtype, key=key)
+
+
+ROWS_FORMATS = ([("affine", b, g) for b in (2, 3, 4, 5, 6, 8) for g in (32, 64)] +
+                [(f, 4, 32) for f in ("mxfp4", "nvfp4", "nvfp4-noglobal", "mxfp8",
+                                      "mxfp8_e5m2", "nvfp8", "int4", "mxint8", "fp4_f16")])
+ROWS = np.array([10, 0, 3, 3, 7, 10, 1])   # permuted, repeated, first and last row
+
+
+@pytest.mark.parametrize("fmt,bits,group", ROWS_FORMATS)
+def test_qmv_rows_equals_columns_of_full_product(fmt, bits, group):
+    # exactly representable inputs (small-integer x; power-of-two affine
+    # scales with integer biases): every fp64 sum is exact, so the restricted
+    # product must equal the chosen columns of the full one bit for bit, and
+    # a row picked with the wrong scale row, an axis mix-up or a dropped
+    # global scale shows as a difference
+    c = _rows_case(fmt, "f32", 0, K=64 if group == 32 else 128, bits=bits, group=group)
+    rng = np.random.default_rng(bits * 100 + group)
+    if c.fmt == "affine":
+        c.scales = np.ldexp(1.0, rng.integers(-3, 2, size=c.scales.shape)).astype(np.float32)
+        c.biases = rng.integers(-8, 9, size=c.biases.shape).astype(np.float32)
+    elif c.scales.dtype in (np.float32, np.float16):
+        c.scales = np.ldexp(1.0, rng.integers(-6, -2, size=c.scales.shape)).astype(c.scales.dtype)
+    c.x = rng.integers(-3, 4, size=c.x.shape).astype(np.float32)
+    W = oracle.dequant(c.fmt, c.K, c.w, c.scales, c.biases, bits=c.bits, group=c.group,
+                       dtype="f32", global_scale=c.global_scale)
+    full = oracle.qmv(c.x, "f32", W)
+    part = oracle.qmv_rows(c.fmt, c.x, "f32", c.K, ROWS, c.w, c.scales, c.biases,
+                           bits=c.bits, group=c.group, global_scale=c.global_scale)
+    assert part.shape == (c.B, ROWS.size)
+    assert np.array_equal(part, full[:, ROWS])
+    # each chosen column is the loop-by-loop dot product of its own row
+    for j, n in enumerate(ROWS):
+        for b in range(c.B):
+            assert part[b, j] == math.fsum(float(c.x[b, k]) * W[n, k] for k in range(c.K))
+
+
+@pytest.mark.parametrize("fmt,bits,group", ROWS_FORMATS)
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_qmv_rows_random_inputs(fmt, bits, group, dtype):
+    # the workload generators' own distributions: equal to the full product's
+    # columns up to fp64 summation order
+    c = _rows_case(fmt, dtype, 1, K=3 * group if fmt == "affine" else 192, bits=bits, group=group)
+    W = oracle.dequant(c.fmt, c.K, c.w, c.scales, c.biases, bits=c.bits, group=c.group,
+                       dtype=dtype, global_scale=c.global_scale)
+    full = oracle.qmv(c.x, dtype, W)
+    A = oracle.abs_dot(c.x, dtype, W)
+    part = oracle.qmv_rows(c.fmt, c.x, dtype, c.K, ROWS, c.w, c.scales, c.biases,
+                           bits=c.bits, group=c.group, global_scale=c.global_scale)
+    assert np.all(np.abs(part - full[:, ROWS]) <= 1e-13 * A[:, ROWS])

@@ -2,6 +2,8 @@
 indexing), an exact small-integer case worked element by element in the
 `qouter` form x * (s*q + b), and the transpose relation to the QMV oracle."""
 
+import math
+
 import numpy as np
 
 import oracle
@@ -41,3 +43,25 @@ def test_qvm_is_qmv_of_the_transpose():
     W = rng.normal(size=(50, 96))
     x = workloads.to_storage(rng.normal(size=(3, 50)), "bf16")
     assert np.allclose(oracle.qvm(x, "bf16", W), oracle.qmv(x, "bf16", W.T), rtol=1e-13, atol=0)
+
+
+def test_qvm_abs_brute_force():
+    # sum_n |x[b, n] * W[n, k]| by loops; negative x and W, and a non-square
+    # W, so a dropped absolute value or a transposed operand fails
+    rng = np.random.default_rng(2)
+    N, K = 7, 12
+    W = rng.normal(size=(N, K))
+    x = workloads.to_storage(rng.normal(size=(3, N)), "f16")
+    X = oracle.storage_to_f64(x, "f16")
+    A = oracle.qvm_abs(x, "f16", W)
+    assert A.shape == (3, K)
+    for b in range(3):
+        for k in range(K):
+            want = sum(abs(X[b, n] * W[n, k]) for n in range(N))
+            assert math.isclose(A[b, k], want, rel_tol=1e-14), (b, k)
+    # it bounds the product, with equality where every term has one sign
+    assert np.all(np.abs(oracle.qvm(x, "f16", W)) <= A * (1 + 1e-14))
+    xp = workloads.to_storage(np.abs(rng.normal(size=(2, N))), "bf16")
+    Wp = np.abs(W)
+    assert np.allclose(oracle.qvm(xp, "bf16", Wp), oracle.qvm_abs(xp, "bf16", Wp),
+                       rtol=1e-15, atol=0)
