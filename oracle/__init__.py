@@ -84,7 +84,8 @@ from .moe import (
     moe_gate_up_swiglu,
     moe_down_reduce,
 )
-from .norm import gamma_stored, rms_factor, rmsnorm, rmsnorm_stored
+from .norm import (gamma_stored, rms_factor, rmsnorm, rmsnorm_qmv, rmsnorm_qmv_abs,
+                   rmsnorm_stored)
 from .qmv import (
     dequant_affine,
     dequant_mxfp4,

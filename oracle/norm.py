@@ -8,12 +8,16 @@ family's "fused RMSNorm + GEMV": a root-mean-square normalization of the
 activation row, scaled per element by a weight vector, feeding the quantized
 matrix-vector product in one dispatch.
 
-Readings (the pages name the operation but print no formula): the usual
+Reading (the pages name the operation but print no formula): the usual
 RMSNorm, xn[k] = x[k] * r * gamma[k] with r = 1 / sqrt(mean_k x^2 + eps) and
-eps an argument. r is one scalar per row, so W . xn = r * (W . (x * gamma)):
-the fused product stages x * gamma rounded once to the activation type T (the
-product of two T values is exact, so this is a single rounding of an exact
-value, the same on any machine) and multiplies each row's result by r.
+eps an argument, and the fused product is y = W . xn. `rmsnorm_qmv` is that
+plain definition in fp64, with no intermediate rounding: the parity target.
+
+A fused kernel has to hand the product a stored activation, so it rounds once
+somewhere. `gamma_stored` and `rms_factor` describe one such choice (stage
+RN_T(x * gamma), whose product of two T values is exact before the rounding,
+and multiply the row's result by r); they serve as an extra, tighter check
+of a kernel that makes that choice, never as the definition.
 """
 
 from __future__ import annotations
@@ -56,3 +60,16 @@ def gamma_stored(x, x_dtype: str, gamma) -> np.ndarray:
         x64 = x64[None, :]
     g64 = storage_to_f64(gamma, x_dtype).reshape(-1)
     return round_f64_to(x64 * g64[None, :], x_dtype)
+
+
+def rmsnorm_qmv(x, x_dtype: str, gamma, eps: float, W64: np.ndarray) -> np.ndarray:
+    """The fused product's plain definition in fp64: y[b, n] = sum_k
+    W[n, k] * xn[b, k] with xn = rmsnorm(x) unrounded. W64 is the
+    dequantized [N, K] matrix. Returns fp64 [B, N]."""
+    return rmsnorm(x, x_dtype, gamma, eps) @ np.asarray(W64, dtype=np.float64).T
+
+
+def rmsnorm_qmv_abs(x, x_dtype: str, gamma, eps: float, W64: np.ndarray) -> np.ndarray:
+    """sum_k |W[n, k] * xn[b, k]| in fp64: the magnitude scale of each fused
+    dot product (for error bounds)."""
+    return np.abs(rmsnorm(x, x_dtype, gamma, eps)) @ np.abs(np.asarray(W64, np.float64)).T

@@ -28,3 +28,21 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_terminal_summary(terminalreporter, exitstatus, config):
+    # elements that passed only through a documented tolerance allowance
+    # (near-cancellation, the f32 floor, a fused kernel's staging bound)
+    mod = sys.modules.get("gpu_util")
+    notes = getattr(mod, "TOLERANCE_NOTES", None) if mod is not None else None
+    if not notes:
+        return
+    terminalreporter.section("parity tolerance report")
+    by_kind = {}
+    for what, kind, count, total in notes:
+        terminalreporter.write_line(f"{what}: {count} of {total} elements {kind}")
+        c, t, n = by_kind.get(kind, (0, 0, 0))
+        by_kind[kind] = (c + count, t + total, n + 1)
+    for kind, (c, t, n) in sorted(by_kind.items()):
+        terminalreporter.write_line(f"total {kind}: {c} elements in {n} cases "
+                                    f"({c} of {t} checked there)")

@@ -18,6 +18,19 @@ def say(msg: str) -> None:
     sys.stdout.flush()
 
 
+# Elements that passed only through a documented allowance, per case: the
+# suite's terminal summary prints them (tests/conftest.py), so they reach the
+# run's record even under `pytest -q`.
+TOLERANCE_NOTES: list[tuple[str, str, int, int]] = []
+
+
+def note(what: str, kind: str, count: int, total: int) -> None:
+    """Record `count` of `total` elements of case `what` that took allowance
+    `kind`; also printed at once."""
+    TOLERANCE_NOTES.append((what, kind, int(count), int(total)))
+    say(f"{what}: {count} of {total} elements {kind}")
+
+
 def torch_dtype(dtype: str):
     import torch
     return {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[dtype]
@@ -125,7 +138,7 @@ def check(y_stored: np.ndarray, y64: np.ndarray, A: np.ndarray, dtype: str, what
         assert not bad.any(), f"{what}: {int(bad.sum())} elements outside 1e-5 rel + 2^-18 A"
         tight = int((err > 1e-5 * np.abs(y64) + 2.0 ** -22 * A).sum())
         if tight:
-            say(f"{what}: {tight} f32 elements beyond the 2^-22 A floor (within 2^-18 A)")
+            note(what, "f32 beyond 1e-5 rel + 2^-22 A (within 2^-18 A)", tight, y.size)
         return 0
     r = oracle.round_f64_to(y64, dtype)
     r64 = oracle.storage_to_f64(r, dtype)
@@ -137,6 +150,47 @@ def check(y_stored: np.ndarray, y64: np.ndarray, A: np.ndarray, dtype: str, what
         f"{np.argwhere(bad)[:3].tolist()} got {y[bad][:3]} want {y64[bad][:3]}")
     n_near = int(near.sum())
     if n_near:
-        say(f"{what}: {n_near} near-cancellation elements (|y^| << sum|xw|) accepted")
+        note(what, "near-cancellation (beyond 1 ulp, within ulp/2 + 2^-22 A)", n_near, y.size)
     assert n_near <= max(2, y.size // 100), f"{what}: too many near-cancellation elements"
     return n_near
+
+
+# unit roundoff of each activation type: one rounding to it moves a value by
+# at most this fraction of its magnitude
+UNIT_ROUNDOFF = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+
+
+def check_fused_norm(y_stored: np.ndarray, y_def: np.ndarray, A_def: np.ndarray, dtype: str,
+                     what: str) -> None:
+    """Parity of a fused RMSNorm + QMV against the plain fp64 definition
+    y_def = W . rmsnorm(x) (no intermediate rounding), A_def = sum_k |W xn|.
+
+    A fused kernel stages the normalized activation in T once: each staged
+    value differs from the exact one by at most the unit roundoff u_T of T,
+    which moves a dot product by at most u_T * A_def. The fp32 sums (the
+    dot product, the row's sum of squares and r) add at most 2^-17 * A_def
+    (a chain of fewer than 128 fp32 additions); 2^-15 keeps a factor 4 of
+    margin. Then the result is rounded to T once (ulp_T(y)/2). So every
+    element must satisfy |y - y_def| <= ulp_T(y)/2 + (u_T + 2^-15) A_def, and
+    f32 outputs also the normwise 1e-5 bar. Elements beyond one ulp of
+    RN_T(y_def) are counted and reported."""
+    y = oracle.storage_to_f64(y_stored, dtype)
+    assert y.shape == y_def.shape, (y.shape, y_def.shape)
+    assert np.isfinite(y).all(), f"{what}: non-finite output"
+    err = np.abs(y - y_def)
+    half = 0.0 if dtype == "f32" else oracle.ulp_of(y_stored, dtype) / 2
+    bound = half + (UNIT_ROUNDOFF[dtype] + 2.0 ** -15) * A_def
+    bad = err > bound
+    assert not bad.any(), (
+        f"{what}: {int(bad.sum())} elements beyond the staging bound; first at "
+        f"{np.argwhere(bad)[:3].tolist()} got {y[bad][:3]} want {y_def[bad][:3]}")
+    if dtype == "f32":
+        scale = max(float(np.max(np.abs(y_def))), 1e-300)
+        norm = float(np.max(err)) / scale
+        assert norm <= 1e-5, f"{what}: normwise relative error {norm:.3g} > 1e-5"
+        return
+    r = oracle.round_f64_to(y_def, dtype)
+    beyond = int((np.abs(y - oracle.storage_to_f64(r, dtype)) > oracle.ulp_of(r, dtype)).sum())
+    if beyond:
+        note(what, "beyond 1 ulp of RN_T(plain definition), within the staging bound",
+             beyond, y.size)

@@ -101,3 +101,76 @@ def test_gamma_stored_matches_torch_rounding():
     x = xf.view(torch.int16).numpy().view(np.uint16)
     g = gf.view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(oracle.gamma_stored(x, "bf16", g), want)
+
+
+def test_rmsnorm_qmv_closed_form_and_one_hot():
+    # x = (3, 4), gamma = 1, eps = 0: xn = (0.6, 0.8) * sqrt(2); one-hot
+    # weight rows pick each element, a row (1, -1) gives their difference
+    W = np.array([[1.0, 0.0], [0.0, 1.0], [1.0, -1.0], [2.0, 2.0]])
+    y = oracle.rmsnorm_qmv(np.array([[3.0, 4.0]], np.float32), "f32", np.ones(2, np.float32),
+                           0.0, W)
+    s2 = math.sqrt(2.0)
+    assert np.allclose(y[0], [0.6 * s2, 0.8 * s2, -0.2 * s2, 2.8 * s2], rtol=1e-15)
+    A = oracle.rmsnorm_qmv_abs(np.array([[3.0, 4.0]], np.float32), "f32",
+                               np.ones(2, np.float32), 0.0, W)
+    assert np.allclose(A[0], [0.6 * s2, 0.8 * s2, 1.4 * s2, 2.8 * s2], rtol=1e-15)
+
+
+def test_rmsnorm_qmv_brute_force_loops():
+    # y[b, n] = sum_k W[n, k] x[b, k] r[b] gamma[k] by loops, bf16 storage,
+    # W not square (a transposed operand fails on shape or value)
+    rng = np.random.default_rng(11)
+    B, K, N = 2, 6, 4
+    x = oracle.round_f64_to(rng.normal(size=(B, K)), "bf16")
+    g = oracle.round_f64_to(rng.uniform(0.5, 1.5, size=K), "bf16")
+    W = rng.normal(size=(N, K))
+    eps = 1e-2
+    y = oracle.rmsnorm_qmv(x, "bf16", g, eps, W)
+    A = oracle.rmsnorm_qmv_abs(x, "bf16", g, eps, W)
+    X = oracle.storage_to_f64(x, "bf16")
+    G = oracle.storage_to_f64(g, "bf16")
+    assert y.shape == (B, N)
+    for b in range(B):
+        ms = sum(float(X[b, k]) ** 2 for k in range(K)) / K
+        r = 1.0 / math.sqrt(ms + float(np.float32(eps)))
+        for n in range(N):
+            terms = [W[n, k] * X[b, k] * r * G[k] for k in range(K)]
+            assert y[b, n] == pytest.approx(math.fsum(terms), rel=1e-13, abs=1e-15)
+            assert A[b, n] == pytest.approx(math.fsum(abs(t) for t in terms), rel=1e-13)
+
+
+def test_rmsnorm_qmv_is_r_times_the_unrounded_gamma_product():
+    # W . xn = r * (W . (x * gamma)) in exact arithmetic; the unrounded
+    # product, not RN_T(x * gamma), is what the definition takes
+    rng = np.random.default_rng(12)
+    x = oracle.round_f64_to(rng.normal(size=(3, 64)), "f16")
+    g = oracle.round_f64_to(rng.uniform(0.3, 3.0, size=64), "f16")
+    W = rng.normal(size=(5, 64))
+    y = oracle.rmsnorm_qmv(x, "f16", g, 1e-5, W)
+    r = oracle.rms_factor(x, "f16", 1e-5)
+    xg = oracle.storage_to_f64(x, "f16") * oracle.storage_to_f64(g, "f16")[None, :]
+    assert np.allclose(y, r[:, None] * (xg @ W.T), rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_staging_bound_admits_one_rounding_and_rejects_a_dropped_r(dtype):
+    # the GPU tests' bound for the fused product (gpu_util.check_fused_norm):
+    # a computation that rounds the staged activation once and the result
+    # once, both to T, meets it; one that forgets r (a dropped term) does not
+    import workloads
+    from gpu_util import check_fused_norm
+    rng = np.random.default_rng(13)
+    B, K, N = 3, 1024, 200
+    x = workloads.to_storage(3.0 * rng.normal(size=(B, K)), dtype)
+    g = workloads.to_storage(rng.uniform(0.5, 1.5, size=K), dtype)
+    W = rng.normal(size=(N, K)) * 0.05
+    eps = 1e-6
+    y_def = oracle.rmsnorm_qmv(x, dtype, g, eps, W)
+    A_def = oracle.rmsnorm_qmv_abs(x, dtype, g, eps, W)
+    xs = oracle.rmsnorm_stored(x, dtype, g, eps)           # the normalized row stored in T
+    y_staged = oracle.round_f64_to(oracle.qmv(xs, dtype, W), dtype)
+    check_fused_norm(y_staged, y_def, A_def, dtype, f"staged {dtype}")
+    xg = oracle.gamma_stored(x, dtype, g)                   # r left out
+    y_bad = oracle.round_f64_to(oracle.qmv(xg, dtype, W), dtype)
+    with pytest.raises(AssertionError):
+        check_fused_norm(y_bad, y_def, A_def, dtype, f"no r {dtype}")
