@@ -84,6 +84,11 @@ def load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(
             f"libqmv.so is not built ({LIB_PATH}); run `python -m bit_matrix_vector_amd.build`")
+    # torch first: its HIP runtime is then the one the library binds to, so
+    # the streams and device pointers torch hands over belong to the runtime
+    # the library calls (loading the library first would bind it to the
+    # system runtime and leave two in the process)
+    _torch()
     lib = ctypes.CDLL(LIB_PATH)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     sig = {

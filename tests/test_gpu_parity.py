@@ -365,6 +365,68 @@ def test_b8_matrix_core_bitwise_properties(bmv):
         assert torch.equal(part.view(torch.int16), y1[:, :n].view(torch.int16)), n
 
 
+def _extreme_scale_case(fmt, B, dtype="bf16"):
+    """Rows whose scales sit at the ends of their code range: E8M0 0 (2^-127,
+    whose products with the smaller E2M1 / E4M3 values are subnormal in
+    bf16 and fp32), 1 and 2, and one block with the NaN code (255 for E8M0,
+    0x7F for E4M3); NVFP4 rows also hold E4M3 block scales 0x00 (zero) and
+    0x01 (2^-9). The other rows keep the workload's scales."""
+    K, N = 1088, 40
+    if fmt == "mxfp4":
+        c = workloads.mxfp4_case(72, f"extreme-{fmt}-{B}-{dtype}", K=K, N=N, B=B, dtype=dtype)
+    elif fmt == "mxfp8":
+        c = workloads.mxfp8_case(72, f"extreme-{fmt}-{B}-{dtype}", K=K, N=N, B=B, dtype=dtype)
+    else:
+        c = workloads.nvfp4_case(72, f"extreme-{fmt}-{B}-{dtype}", K=K, N=N, B=B, dtype=dtype)
+    sc = c.scales.copy()
+    if fmt == "nvfp4":
+        sc[0, :] = 0x01
+        sc[1, ::2] = 0x00
+        sc[2, :] = 0x08               # 2^-6, the smallest normal E4M3
+        sc[3, 5] = 0x7F               # NaN block
+        sc[4, :] = 0x7E               # 448, the largest
+        nan_rows = [3]
+    else:
+        sc[0, :] = 0
+        sc[1, :] = 1
+        sc[2, ::2] = 2
+        sc[3, 7] = 255                # NaN block
+        sc[4, :] = np.where(np.arange(sc.shape[1]) % 2 == 0, 0, 130)
+        nan_rows = [3]
+    c.scales = sc
+    return c, nan_rows
+
+
+def _check_with_nan_rows(y, c, nan_rows, what):
+    assert np.isnan(oracle.storage_to_f64(y[:, nan_rows], c.dtype)).all(), what
+    keep = np.setdiff1d(np.arange(c.N), nan_rows)
+    y64, A = oracle_rows(c, keep)
+    check(y[:, keep], y64, A, c.dtype, what)
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
+@pytest.mark.parametrize("B", [8, 1, 4])
+def test_extreme_scale_codes(bmv, fmt, B):
+    # B = 8 (bf16) runs on the matrix cores, B = 1 and 4 on the VALU tile;
+    # both must decode the end codes of the scale formats as the oracle does
+    c, nan_rows = _extreme_scale_case(fmt, B)
+    say(f"extreme scale codes {fmt} B={B} K={c.K} N={c.N}")
+    y = to_host(run_qmv(bmv, c), c.dtype)
+    _check_with_nan_rows(y, c, nan_rows, f"extreme scales {fmt} B={B}")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_extreme_scale_codes_other_dtypes(bmv, fmt, dtype):
+    c, nan_rows = _extreme_scale_case(fmt, 2, dtype)
+    say(f"extreme scale codes {fmt} B=2 {dtype}")
+    # (f16 outputs of the 2^-127-scaled rows underflow to zeros and
+    # subnormals; the 1-ulp bar, with the smallest subnormal as the ulp at
+    # zero, still applies)
+    y = to_host(run_qmv(bmv, c), c.dtype)
+    _check_with_nan_rows(y, c, nan_rows, f"extreme scales {fmt} B=2 {dtype}")
+
+
 # ---------------------------------------------------------------------------
 # the MoE workload: routed-MoE gathered QMV
 # ---------------------------------------------------------------------------
@@ -440,6 +502,78 @@ def test_gather_out_of_range_rows_are_zero(bmv):
     check(yh[keep], y64[keep], A[keep], "bf16", "gather with invalid slots")
 
 
+def _moe_dev_any(m):
+    d = _moe_dev(m)
+    if m.fmt == "nvfp4" and m.global_scale is not None:
+        import torch
+        d["gscale"] = torch.tensor([m.global_scale], dtype=torch.float32, device="cuda:0")
+    return d
+
+
+def _single_call(bmv, m, d, e, x1):
+    """One-row QMV of expert e through the plain entry point of its format."""
+    if m.fmt == "affine":
+        return bmv.qmv_affine(x1, d["w"][e], d["scales"][e], d["biases"][e], m.bits, m.group)
+    if m.fmt == "mxfp4":
+        return bmv.qmv_fp_mxfp4(x1, d["w"][e], d["scales"][e])
+    if m.fmt == "nvfp4":
+        return bmv.qmv_fp_nvfp4(x1, d["w"][e], d["scales"][e], d.get("gscale"))
+    return bmv.qmv_fp_mxfp8(x1, d["w"][e], d["scales"][e])
+
+
+def _gather_case_check(bmv, m, what, bad_slots=()):
+    """gather_qmv on m: every valid slot against the oracle and bit for bit
+    against a one-row call of its expert; slots in bad_slots (an index out
+    of range) must be zero rows."""
+    import torch
+    d = _moe_dev_any(m)
+    wt = bmv.make_weights(m.fmt, d["w"], d["scales"], d["biases"], K=m.K, bits=m.bits,
+                          group_size=m.group, global_scale=d.get("gscale"))
+    say(f"{what}: {m.fmt} {m.dtype} E={m.E} K={m.K} N={m.N} slots={m.lhs.size}")
+    yg = bmv.gather_qmv(d["x"], wt, d["lhs"], d["rhs"])
+    yh = to_host(yg, m.dtype)
+    for s in range(m.lhs.size):
+        if s in bad_slots:
+            assert not np.any(yh[s]), s
+            continue
+        e, r = int(m.rhs[s]), int(m.lhs[s])
+        c = m.expert_case(e)
+        c.x = m.x[r][None, :]
+        c.B = 1
+        y64, A = oracle_rows(c, np.arange(m.N))
+        check(yh[s:s + 1], y64, A, m.dtype, f"{what} slot {s}")
+        y1 = _single_call(bmv, m, d, e, d["x"][r:r + 1].contiguous())
+        a = y1[0].view(torch.int32 if m.dtype == "f32" else torch.int16)
+        b = yg[s].view(torch.int32 if m.dtype == "f32" else torch.int16)
+        assert torch.equal(a, b), f"{what}: slot {s} differs from the one-row call"
+
+
+@pytest.mark.parametrize("fmt,gscale", [("nvfp4", 0.5), ("nvfp4", None), ("mxfp8", None),
+                                        ("mxfp4", None), ("affine", None)])
+@pytest.mark.parametrize("dtype", ["f16", "f32", "bf16"])
+def test_gather_formats_and_dtypes(bmv, fmt, gscale, dtype):
+    m = workloads.moe_case(fmt, "gate_up", E=8, hidden=1024, ffn=96, tokens=6, top_k=3,
+                           dtype=dtype, global_scale=gscale)
+    _gather_case_check(bmv, m, f"gather {fmt} g={gscale} {dtype}")
+
+
+@pytest.mark.parametrize("fmt,dtype,K", [("mxfp4", "f32", 4096), ("nvfp4", "f32", 4096),
+                                         ("affine", "f32", 4096), ("mxfp8", "bf16", 10240),
+                                         ("mxfp4", "bf16", 10240), ("affine", "f16", 10240)])
+def test_gather_multi_slab(bmv, fmt, dtype, K):
+    # a chunk of two x rows of K values no longer fits the gather's LDS stage
+    # (f32 K=4096: 32 KB of x plus the scales; 16-bit K=10240: 40 KB), so the
+    # gather runs the tile slab by slab; out-of-range ids must still give
+    # zero rows
+    m = workloads.moe_case(fmt, "gate_up", E=6, hidden=K, ffn=70, tokens=5, top_k=2,
+                           dtype=dtype)
+    m.rhs = m.rhs.copy()
+    m.lhs = m.lhs.copy()
+    m.rhs[3] = m.E            # expert == n_experts
+    m.lhs[7] = 5              # x row == n_x_rows
+    _gather_case_check(bmv, m, f"gather multi-slab K={K}", bad_slots=(3, 7))
+
+
 # ---------------------------------------------------------------------------
 # layout, precision and edge cases
 # ---------------------------------------------------------------------------
@@ -464,9 +598,11 @@ def test_one_hot_reads_each_weight(bmv):
 def test_bias_sum_precision(bmv, dtype, bits):
     # one large and many small x in each group: summing x in the 16-bit type
     # before widening loses the small ones (mlx pull request 4516)
+    # the small value lies below half an ulp of 1.0 in each type (bf16 2^-9,
+    # f16 2^-12), so every 16-bit partial sum drops it
     K, N, group = 512, 16, 64
     rng = np.random.default_rng(bits)
-    x64 = np.full((1, K), 2.0 ** -9)
+    x64 = np.full((1, K), 2.0 ** -9 if dtype == "bf16" else 2.0 ** -12)
     x64[0, ::group] = 1.0
     w = rng.integers(0, 256, size=(N, K * bits // 8), dtype=np.uint8)
     s64 = np.full((N, K // group), 1e-3)

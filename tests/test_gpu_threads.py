@@ -6,9 +6,17 @@ with four row lengths (96 to 144 KB of LDS) and two formats. All the calls are
 released together from one thread each. Every call must succeed, and each
 result must equal, bit for bit, the same call made alone afterwards. A few
 sampled rows are also checked against the oracle.
+
+The body runs in a fresh child process, so these launches are the first of
+their kernel instances in that process and the locked raise of the LDS limit
+really happens there (in the suite's own process an earlier test may already
+have raised it).
 """
 from __future__ import annotations
 
+import os
+import subprocess
+import sys
 import threading
 
 import numpy as np
@@ -20,16 +28,7 @@ from gpu_util import case_to_dev, check, oracle_rows, run_qmv, sample_rows, say,
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(scope="module")
-def bmv():
-    import torch
-    import bit_matrix_vector_amd as m
-    assert torch.cuda.is_available()
-    m.load()  # a machine without the built library must fail here, loudly
-    return m
-
-
-def test_concurrent_launches_with_large_lds(bmv):
+def _concurrent_launches_with_large_lds(bmv):
     import torch
     cases = []
     for fmt in ("mxfp8", "nvfp4"):
@@ -69,3 +68,23 @@ def test_concurrent_launches_with_large_lds(bmv):
         y = to_host(outs[i], c.dtype)
         y64, A = oracle_rows(c, rows)
         check(y[:, rows], y64, A, c.dtype, f"threads {c.fmt} K={c.K}")
+
+
+def test_concurrent_launches_with_large_lds():
+    here = os.path.dirname(os.path.abspath(__file__))
+    env = dict(os.environ)
+    env["PYTHONPATH"] = os.pathsep.join([os.path.dirname(here), here,
+                                         env.get("PYTHONPATH", "")])
+    say("child process: first launches of the large-LDS matrix-core QMV from 8 threads")
+    r = subprocess.run([sys.executable, os.path.abspath(__file__)], env=env,
+                       stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=300)
+    print(r.stdout)
+    assert r.returncode == 0, f"child exited with {r.returncode}:\n{r.stdout[-3000:]}"
+    assert "CONCURRENT-LAUNCHES-OK" in r.stdout
+
+
+if __name__ == "__main__":
+    import bit_matrix_vector_amd as _m
+    _m.load()
+    _concurrent_launches_with_large_lds(_m)
+    print("CONCURRENT-LAUNCHES-OK", flush=True)

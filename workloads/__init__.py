@@ -252,13 +252,15 @@ class MoeCase:
     bits: int = 4
     group: int = 64
     key: str = ""
+    global_scale: float | None = None   # NVFP4: one fp32 scale shared by all experts
 
     def expert_case(self, e: int) -> QmvCase:
         """Expert e's matrix as a QMV problem with x rows all of x."""
         return QmvCase(self.fmt, self.dtype, self.x.shape[0], self.K, self.N, self.w[e],
                        self.scales[e], self.x,
                        biases=None if self.biases is None else self.biases[e],
-                       bits=self.bits, group=self.group, key=f"{self.key}-e{e}")
+                       bits=self.bits, group=self.group, global_scale=self.global_scale,
+                       key=f"{self.key}-e{e}")
 
     def distinct_experts(self) -> np.ndarray:
         r = self.rhs.astype(np.int64)
@@ -285,12 +287,16 @@ def route_topk(logits: np.ndarray, k: int) -> np.ndarray:
 
 
 def moe_case(fmt: str, proj: str, *, E: int = 64, hidden: int = 4096, ffn: int = 1536,
-             tokens: int = 16, top_k: int = 8, dtype: str = "bf16") -> MoeCase:
+             tokens: int = 16, top_k: int = 8, dtype: str = "bf16",
+             global_scale: float | None = 0.5) -> MoeCase:
     """proj 'gate_up': K=hidden, N=ffn, x = token activations [tokens, hidden],
     slot s = (token s // top_k, its (s % top_k)-th expert). proj 'down':
     K=ffn, N=hidden, x = per-slot hidden states [tokens*top_k, ffn] ~ N(0,1),
     lhs[s] = s. The routing (router logits ~ N(0,1), top_k) is drawn from its
-    own stream so both projections share it."""
+    own stream so both projections share it. Formats: 'mxfp4' and 'affine'
+    (4-bit g64) as the MoE workload states, and for wider parity coverage
+    'nvfp4' (E4M3 |N(0,1)| block scales, `global_scale`) and 'mxfp8' (finite
+    E4M3 codes, E8M0 120..130), drawn like the MLP projection's weights."""
     route_rng = rng_for(5, "c5-router")
     logits = route_rng.normal(0.0, 1.0, size=(tokens, E))
     experts = route_topk(logits, top_k)                      # [tokens, top_k]
@@ -318,11 +324,22 @@ def moe_case(fmt: str, proj: str, *, E: int = 64, hidden: int = 4096, ffn: int =
         w = rng.integers(0, 256, size=(E, N, K * bits // 8), dtype=np.uint8)
         scales = to_storage(rng.uniform(0.005, 0.05, size=(E, N, K // group)), dtype)
         biases = to_storage(rng.normal(0.0, 0.05, size=(E, N, K // group)), dtype)
+    elif fmt == "nvfp4":
+        w = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+        scales = _e4m3_byte_for(np.abs(rng.normal(0.0, 1.0, size=(E, N, K // 16))))
+        biases = None
+        bits, group = 4, 16
+    elif fmt == "mxfp8":
+        r = rng.integers(0, 254, size=(E, N, K), dtype=np.int64)   # the 254 finite bytes
+        w = (r + (r >= 0x7F)).astype(np.uint8)
+        scales = rng.integers(120, 131, size=(E, N, K // 32), dtype=np.uint8)
+        biases = None
+        bits, group = 8, 32
     else:
         raise ValueError(fmt)
     x = to_storage(rng.normal(0.0, 1.0, size=(n_x, K)), dtype)
     return MoeCase(fmt, dtype, E, K, N, w, scales, x, lhs, rhs, biases=biases, bits=bits,
-                   group=group, key=key)
+                   group=group, key=key, global_scale=global_scale if fmt == "nvfp4" else None)
 
 
 # ---------------------------------------------------------------------------
