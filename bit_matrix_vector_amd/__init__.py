@@ -108,6 +108,7 @@ def load() -> ctypes.CDLL:
                                    vp],
         "qmv_moe_down_reduce": [vp, i32, ctypes.POINTER(QmvWeights), vp, i64, vp, vp, i64, vp],
         "qmv_qvm": [vp, i32, ctypes.POINTER(QmvWeights), i64, vp, vp, vp, ctypes.c_size_t],
+        "qmv_qvm_noalloc": [vp, i32, ctypes.POINTER(QmvWeights), i64, vp, vp],
         "qmv_qmm": [vp, i32, ctypes.POINTER(QmvWeights), i64, vp, vp, vp, ctypes.c_size_t],
         "qmv_rmsnorm_qmv": [vp, i32, ctypes.POINTER(QmvWeights), i64, vp, vp, ctypes.c_float, vp],
         "gather_qmm": [vp, i32, ctypes.POINTER(QmvWeights), vp, i64, vp, vp, i64, vp],
@@ -122,6 +123,8 @@ def load() -> ctypes.CDLL:
         fn.restype = ctypes.c_int
     lib.qmv_qvm_workspace_bytes.argtypes = [i64, i64, i64]
     lib.qmv_qvm_workspace_bytes.restype = ctypes.c_size_t
+    lib.qmv_qvm_noalloc_max_workspace_bytes.argtypes = []
+    lib.qmv_qvm_noalloc_max_workspace_bytes.restype = ctypes.c_size_t
     lib.qmv_qmm_workspace_bytes.argtypes = [i64, i64, i64, i32]
     lib.qmv_qmm_workspace_bytes.restype = ctypes.c_size_t
     lib.qmv_packed_row_bytes.argtypes = [i32, i32, i64]
@@ -371,6 +374,19 @@ def qmv_qvm(x, weights: QmvWeights, y=None, workspace=None):
         workspace = torch.empty((max(need, 4) // 4,), dtype=torch.float32, device=x.device)
     _check(load().qmv_qvm(_stream(x.device), _dtype_code(x), ctypes.byref(weights), B, _ptr(x),
                           _ptr(y), _ptr(workspace), workspace.numel() * 4))
+    return y
+
+
+def qmv_qvm_noalloc(x, weights: QmvWeights, y):
+    """qmv_qvm through the entry point that allocates nothing: the split
+    partials go to the library's device scratch (qmv_qvm_noalloc in qmv.h);
+    y [B, K] must be given."""
+    x = _dev(x, "x")
+    if x.dim() == 1:
+        x = x.unsqueeze(0)
+    _dev(y, "y", x.dtype)
+    _check(load().qmv_qvm_noalloc(_stream(x.device), _dtype_code(x), ctypes.byref(weights),
+                                  x.shape[0], _ptr(x), _ptr(y)))
     return y
 
 

@@ -57,6 +57,9 @@ def _jobs() -> list[tuple[list[str], str]]:
                       os.path.join(CSRC, "qmv_qmm.hip"), "-o", obj], obj))
     obj = os.path.join(BUILD, "qmv_quant.o")
     jobs.append(([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "qmv_quant.hip"), "-o", obj], obj))
+    obj = os.path.join(BUILD, "qmv_scratch.o")
+    jobs.append(([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "qmv_scratch.hip"), "-o", obj],
+                 obj))
     obj = os.path.join(BUILD, "qmv_bench.o")
     jobs.append(([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "qmv_bench.hip"), "-o", obj], obj))
     obj = os.path.join(BUILD, "qmv_api.o")

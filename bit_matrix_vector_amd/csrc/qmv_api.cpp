@@ -305,9 +305,11 @@ size_t qmv_qvm_workspace_bytes(int64_t B, int64_t K, int64_t N) {
     return (size_t)qmv::qvm_splits(B, K, N, nullptr) * (size_t)B * (size_t)K * sizeof(float);
 }
 
-qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* wt, int64_t B, const void* x,
-                     void* y, void* workspace, size_t workspace_bytes) {
-    const char* fn = "qmv_qvm";
+// qvm with the caller's workspace, or (library_scratch) with the library's
+// device scratch, looked up only after every argument has been validated.
+static qmv_status_t qvm_impl(const char* fn, void* stream, int dtype, const qmv_weights_t* wt,
+                             int64_t B, const void* x, void* y, void* workspace,
+                             size_t workspace_bytes, bool library_scratch) {
     if (wt == nullptr) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: weights struct is NULL", fn);
     if (wt->n_experts != 1)
         return fail(QMV_ERR_INVALID_ARGUMENT, "%s: n_experts must be 1", fn);
@@ -331,12 +333,17 @@ qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* wt, int64_t B
         QMV_TRY(check_ptr(fn, "scales", wt->scales, true, scale_bytes(wt->format)));
     }
     QMV_TRY(check_ptr(fn, "global_scale", wt->global_scale, wt->global_scale != nullptr, 4));
-    QMV_TRY(check_ptr(fn, "workspace", workspace, true, 4));
+    if (!library_scratch) QMV_TRY(check_ptr(fn, "workspace", workspace, true, 4));
     const size_t need = qmv_qvm_workspace_bytes(B, wt->K, wt->N);
     if (qmv::qvm_splits(B, wt->K, wt->N, nullptr) > 65535)
         return fail(QMV_ERR_UNSUPPORTED, "%s: N = %lld needs more than 65535 row splits at B = %lld",
                     fn, (long long)wt->N, (long long)B);
-    if (workspace_bytes < need)
+    if (library_scratch && need > qmv::kScratchBytes)
+        return fail(QMV_ERR_UNSUPPORTED,
+                    "%s: B = %lld, K = %lld, N = %lld needs %zu bytes of scratch; the library "
+                    "holds %zu (call qmv_qvm with a workspace instead)", fn, (long long)B,
+                    (long long)wt->K, (long long)wt->N, need, qmv::kScratchBytes);
+    if (!library_scratch && workspace_bytes < need)
         return fail(QMV_ERR_INVALID_ARGUMENT, "%s: workspace of %zu bytes, %zu needed", fn,
                     workspace_bytes, need);
     {
@@ -349,9 +356,26 @@ qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* wt, int64_t B
     q.B = B; q.K = wt->K; q.N = wt->N; q.row_bytes = lp.row_bytes; q.sc_per_row = lp.sc_per_row;
     q.x = x; q.w = wt->w; q.scales = wt->scales; q.biases = wt->biases;
     q.gscale = wt->format == QMV_NVFP4 ? wt->global_scale : nullptr;
+    if (library_scratch) {
+        if (const int e = qmv::scratch_for_current_device(&workspace))
+            return fail(QMV_ERR_HIP, "%s: device scratch lookup failed: %s", fn,
+                        qmv::hip_error_string(e));
+    }
     q.y = y; q.ws = static_cast<float*>(workspace);
     q.splits = qmv::qvm_splits(q.B, q.K, q.N, &q.rows_per_split);
     return launch_status(qmv::launch_qvm(q, stream), fn);
+}
+
+qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* wt, int64_t B, const void* x,
+                     void* y, void* workspace, size_t workspace_bytes) {
+    return qvm_impl("qmv_qvm", stream, dtype, wt, B, x, y, workspace, workspace_bytes, false);
+}
+
+size_t qmv_qvm_noalloc_max_workspace_bytes(void) { return qmv::kScratchBytes; }
+
+qmv_status_t qmv_qvm_noalloc(void* stream, int dtype, const qmv_weights_t* wt, int64_t B,
+                             const void* x, void* y) {
+    return qvm_impl("qmv_qvm_noalloc", stream, dtype, wt, B, x, y, nullptr, 0, true);
 }
 
 qmv_status_t qmv_rmsnorm_qmv(void* stream, int dtype, const qmv_weights_t* wt, int64_t B,

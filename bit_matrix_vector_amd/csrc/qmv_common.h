@@ -2,6 +2,7 @@
 // Not part of the public ABI (that is include/qmv.h).
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 namespace qmv {
@@ -191,5 +192,12 @@ const char* hip_error_string(int err);
 
 // Largest LDS footprint of the x staging buffer, in bytes.
 constexpr int kMaxStageBytes = 64 * 1024;
+
+// Size of the library-held device scratch of the entry points that allocate
+// nothing (one copy per device, held until the process ends).
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+// Device address of that scratch on the current device (looked up once per
+// device and recorded). Returns 0 or a hipError_t.
+int scratch_for_current_device(void** out);
 
 }  // namespace qmv

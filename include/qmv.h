@@ -238,6 +238,23 @@ size_t qmv_qvm_workspace_bytes(int64_t B, int64_t K, int64_t N);
 qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* w, int64_t B, const void* x,
                      void* y, void* workspace, size_t workspace_bytes);
 
+/* qvm without a workspace argument and without any allocation, for callers
+ * that cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation. Same arguments, kernels and
+ * results as qmv_qvm (bit for bit), but the fp32 split partials go to a
+ * library-held device scratch of qmv_qvm_noalloc_max_workspace_bytes() bytes
+ * (16 MiB; one copy per device, held until the process ends, its address
+ * looked up once per device on the first call there). A problem whose
+ * qmv_qvm_workspace_bytes(B, K, N) exceeds that returns QMV_ERR_UNSUPPORTED
+ * before any HIP call. Every call on a device shares that device's scratch:
+ * calls that overlap on one device (two streams, or two threads) race and
+ * must be serialized by the caller. The scratch keeps the last call's
+ * partials; each call overwrites every element it reads, so nothing needs
+ * clearing. Calls nothing that allocates (no hipMalloc / hipFree). */
+size_t qmv_qvm_noalloc_max_workspace_bytes(void);
+qmv_status_t qmv_qvm_noalloc(void* stream, int dtype, const qmv_weights_t* w, int64_t B,
+                             const void* x, void* y);
+
 /* ---------------- fused RMSNorm + QMV: DEVICE memory, asynchronous ----------
  * y[b, :] = W . (x[b, :] * r[b] * gamma) with r[b] = 1 / sqrt(mean_k x[b, k]^2
  * + eps) ("wh-iron kernel-op coverage audit", op rows "rms_norm" and

@@ -29,6 +29,7 @@ def test_library_exports_every_header_function(lib):
             "qmv_quantize_affine", "qmv_quantize_mxfp4", "qmv_quantize_mxfp8",
             "qmv_quantize_nvfp4", "qmv_moe_gate_up_swiglu", "qmv_moe_down_reduce", "qmv_fp_block",
             "qmv_qvm", "qmv_qvm_workspace_bytes", "qmv_qmm", "qmv_qmm_workspace_bytes",
+            "qmv_qvm_noalloc", "qmv_qvm_noalloc_max_workspace_bytes",
             "qmv_rmsnorm_qmv", "gather_qmm",
             "qmv_last_error"} <= set(names)
     for n in names:
@@ -124,6 +125,24 @@ def test_qvm_validation(lib):
     sb = bmv.QmvWeights(5, 14, 64, 1, 300, 1024, 0x20000, 0x30000, None, None)
     assert lib.qmv_qvm(None, 2, ctypes.byref(sb), 2, X, Y, ws, need) == UNSUP
     assert lib.qmv_qvm(None, 2, ctypes.byref(wt), 0, X, Y, None, 0) == OK
+
+
+def test_qvm_noalloc_validation(lib):
+    # the entry point without a workspace: same checks as qmv_qvm, plus the
+    # library scratch's limit, all before any HIP call
+    lim = lib.qmv_qvm_noalloc_max_workspace_bytes()
+    assert lim == 16 << 20
+    wt = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 1, 300, 1024, 0x20000, 0x30000, None, None)
+    assert lib.qmv_qvm_noalloc(None, 2, ctypes.byref(wt), 9, X, Y) == UNSUP
+    assert lib.qmv_qvm_noalloc(None, 2, ctypes.byref(wt), 2, None, Y) == INVAL
+    assert lib.qmv_qvm_noalloc(None, 2, ctypes.byref(wt), 2, X, V(0x10000)) == INVAL
+    assert lib.qmv_qvm_noalloc(None, 2, ctypes.byref(wt), 0, X, Y) == OK
+    # K = 16384, N = 32769 at B = 8 needs more split partials than the scratch
+    big = bmv.QmvWeights(bmv.QMV_MXFP4, 4, 32, 1, 32769, 16384, 0x20000, 0x30000, None, None)
+    assert lib.qmv_qvm_workspace_bytes(8, 16384, 32769) > lim
+    assert lib.qmv_qvm_noalloc(None, 2, ctypes.byref(big), 8, X, V(0x10000000)) == UNSUP
+    msg = lib.qmv_last_error().decode()
+    assert "scratch" in msg and "qmv_qvm_noalloc" in msg
 
 
 def test_block_format_validation(lib):
