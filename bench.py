@@ -467,35 +467,54 @@ def time_chain(bmv, N: int = 2560, steps: int = 100) -> dict:
             "us_per_call_graph": graph, "gbps_graph": c.algorithmic_bytes() / graph / 1e3}
 
 
-def time_case(runner: Runner, steps: int, warmup: int) -> dict:
-    import torch
-    stream = torch.cuda.current_stream()
-    sp = ctypes.c_void_p(stream.cuda_stream)
-    for i in range(warmup):
-        runner.call(i, sp)
-    torch.cuda.synchronize()
+GRAPH_LAUNCHES = 256     # launches captured in one HIP graph
+MIN_REPLAYS = 8          # graph replays timed (each on its own event pair)
 
-    # (1) whole-job rate: `steps` back-to-back launches, plain stream order
+
+def time_chain_cold(bmv, N: int = 2560, steps: int = 100) -> dict:
+    """The dependent chain of 100 calls (8-bit affine g64, K=2560, bf16) with
+    100 distinct weight matrices, call t reading matrix t (about 700 MB in
+    all, beyond the 256 MB Infinity Cache, so each call streams its weights
+    from HBM). Timed as plain launches and as one HIP graph."""
+    import torch
+    import workloads
+    c = workloads.chain_case(N)
+    lib = bmv.load()
+    x = _dev(c.x, "bf16")
+    w0, s0, b0 = _dev(c.w), _dev(c.scales, "bf16"), _dev(c.biases, "bf16")
+    ws = [w0] + [w0.clone() for _ in range(steps - 1)]
+    ss = [s0] + [s0.clone() for _ in range(steps - 1)]
+    bs = [b0] + [b0.clone() for _ in range(steps - 1)]
+    bufs = [x.clone(), x.clone()]
+    vp = ctypes.c_void_p
+
+    def chain(stream):
+        for t in range(steps):
+            st = lib.qmv_affine(stream, 2, 1, c.K, c.N, vp(bufs[t % 2].data_ptr()),
+                                vp(ws[t].data_ptr()), vp(ss[t].data_ptr()), vp(bs[t].data_ptr()),
+                                8, 64, vp(bufs[(t + 1) % 2].data_ptr()))
+            if st != 0:
+                raise RuntimeError(lib.qmv_last_error().decode())
+
+    sp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(3):
+        chain(sp)
+    torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
+    reps = 20
     t0.record()
-    for i in range(steps):
-        runner.call(i, sp)
+    for _ in range(reps):
+        chain(sp)
     t1.record()
     torch.cuda.synchronize()
-    wall_us = t0.elapsed_time(t1) * 1e3 / steps
-
-    # (2) the same launches captured once in a HIP graph and replayed
+    plain = t0.elapsed_time(t1) * 1e3 / (reps * steps)
     g = torch.cuda.CUDAGraph()
-    n_cap = min(steps, 256)
-    cap_stream = torch.cuda.Stream()
-    cap_stream.wait_stream(stream)
-    with torch.cuda.graph(g, stream=cap_stream):
-        csp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
-        for i in range(n_cap):
-            runner.call(i, csp)
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(g, stream=cs):
+        chain(ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     torch.cuda.synchronize()
-    reps = max(1, steps // n_cap)
     g.replay()
     torch.cuda.synchronize()
     t0.record()
@@ -503,13 +522,71 @@ def time_case(runner: Runner, steps: int, warmup: int) -> dict:
         g.replay()
     t1.record()
     torch.cuda.synchronize()
-    graph_us = t0.elapsed_time(t1) * 1e3 / (reps * n_cap)
+    graph = t0.elapsed_time(t1) * 1e3 / (reps * steps)
+    del g, ws, ss, bs
+    return {"case": f"chain of 100: affine 8b g64 K=2560 N={N} bf16, 100 distinct weights (cold)",
+            "bytes": c.algorithmic_bytes(), "us_per_call_plain": plain,
+            "us_per_call_graph": graph, "gbps_graph": c.algorithmic_bytes() / graph / 1e3,
+            "pct_peak": round(100 * c.algorithmic_bytes() / graph / 1e3 / PEAK_HBM_GBPS, 1)}
+
+
+def time_case(runner: Runner, steps: int, warmup: int) -> dict:
+    """Per-call time of back-to-back launches on one stream.
+
+    us_per_call: a HIP graph of GRAPH_LAUNCHES launches (rotating weight
+    copies) is replayed max(MIN_REPLAYS, ceil(steps / GRAPH_LAUNCHES))
+    times, each replay between its own pair of events on the launch stream;
+    the figure is the median replay's time per launch. `steps` is a minimum,
+    so a small --steps still times whole 256-launch graphs.
+    us_per_call_plain: max(steps, 512) plain launches, one event pair."""
+    import torch
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    for i in range(warmup):
+        runner.call(i, sp)
+    torch.cuda.synchronize()
+
+    # (1) plain stream order
+    n_plain = max(steps, 512)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(n_plain):
+        runner.call(i, sp)
+    t1.record()
+    torch.cuda.synchronize()
+    wall_us = t0.elapsed_time(t1) * 1e3 / n_plain
+
+    # (2) the launches captured once in a HIP graph and replayed
+    g = torch.cuda.CUDAGraph()
+    cap_stream = torch.cuda.Stream()
+    cap_stream.wait_stream(stream)
+    with torch.cuda.graph(g, stream=cap_stream):
+        csp = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for i in range(GRAPH_LAUNCHES):
+            runner.call(i, csp)
+    torch.cuda.synchronize()
+    reps = max(MIN_REPLAYS, -(-steps // GRAPH_LAUNCHES))
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) * 1e3 / GRAPH_LAUNCHES for a, b in ev)
+    graph_us = per[len(per) // 2]
 
     del g
     return {
         "bytes": runner.bytes,
         "us_per_call_plain": wall_us,
         "us_per_call": graph_us,
+        "us_per_call_replays": [round(v, 3) for v in (per[0], per[-1])],
+        "timed": f"median of {reps} replays of a {GRAPH_LAUNCHES}-launch graph; "
+                 f"{n_plain} plain launches",
         "gbps": runner.bytes / graph_us / 1e3,
         "gbps_plain": runner.bytes / wall_us / 1e3,
         "copies": runner.copies,
@@ -709,19 +786,28 @@ def check_once(bmv, case) -> None:
         raise RuntimeError(f"bench case disagrees with the oracle (rel {rel:.3g})")
 
 
-def cpu_baseline(case, budget_s: float = 12.0) -> dict:
-    """The fp64 oracle on the host: whole calls of the headline case (decode
-    every weight row to fp64, then the product), single-threaded, repeated
-    until `budget_s` seconds have passed."""
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_calls(case, budget_s: float, threads: int | None) -> tuple[int, float, int]:
+    """Whole calls of the oracle on `case` (decode every weight row to fp64,
+    then the product, in chunks of 2048 rows) until `budget_s` seconds have
+    passed, with the BLAS/OpenMP pools limited to `threads` (None: as the
+    process starts them). Returns (calls, seconds, threads the pools used)."""
     import oracle
+    from threadpoolctl import threadpool_info, threadpool_limits
+    ctx = threadpool_limits(threads) if threads is not None else None
     try:
-        from threadpoolctl import threadpool_limits
-    except Exception:  # pragma: no cover
-        threadpool_limits = None
-    ctx = threadpool_limits(1) if threadpool_limits else None
-    calls = 0
-    t0 = time.perf_counter()
-    try:
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        calls = 0
+        t0 = time.perf_counter()
         while True:
             for r0 in range(0, case.N, 2048):
                 rows = np.arange(r0, min(case.N, r0 + 2048))
@@ -731,14 +817,29 @@ def cpu_baseline(case, budget_s: float = 12.0) -> dict:
             calls += 1
             if time.perf_counter() - t0 >= budget_s:
                 break
+        return calls, time.perf_counter() - t0, used
     finally:
         if ctx is not None:
             ctx.__exit__(None, None, None)
-    el = time.perf_counter() - t0
-    return {"value": round(case.algorithmic_bytes() * calls / el / 1e9, 4), "unit": "GB/s",
-            "cores": 1, "kind": "oracle",
-            "sample": f"{calls} whole calls of the headline case ({case.N} rows x K={case.K}), "
-                      f"{el:.1f} s, {el / calls * 1e6:.0f} us/call"}
+
+
+def cpu_baseline(case, budget_s: float = 10.0) -> dict:
+    """The fp64 oracle on the host, timed on whole calls of the headline case:
+    once with the BLAS/OpenMP pools at every core the process may use, once
+    on one core. The oracle is a plain NumPy reference: its decode runs on
+    one thread either way, only its final product uses the BLAS pool."""
+    nproc = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    legs = {}
+    for name, threads in (("all", nproc), ("one", 1)):
+        calls, el, used = _oracle_calls(case, budget_s, threads)
+        legs[name] = {"value": round(case.algorithmic_bytes() * calls / el / 1e9, 4),
+                      "unit": "GB/s", "cores": used, "us_per_call": round(el / calls * 1e6),
+                      "calls": calls, "seconds": round(el, 1)}
+    a = legs["all"]
+    return {"value": a["value"], "unit": "GB/s", "cores": a["cores"], "kind": "oracle",
+            "sample": f"{a['calls']} whole calls of the headline case ({case.N} rows x "
+                      f"K={case.K}) in {a['seconds']} s, {a['us_per_call']} us/call",
+            "single_core": legs["one"], "nproc": nproc, "cpu_model": _cpu_model()}
 
 
 def main() -> int:
@@ -847,6 +948,9 @@ def main() -> int:
             ch = time_chain(bmv, n)
             cases.append(ch)
             print(f"[bench] {ch['case']}: {json.dumps(ch)}", file=sys.stderr, flush=True)
+        ch = time_chain_cold(bmv, 2560)
+        cases.append(ch)
+        print(f"[bench] {ch['case']}: {json.dumps(ch)}", file=sys.stderr, flush=True)
         for name, c in (("rmsnorm+qmv mxfp4 B1 K=4096 N=14336 bf16", workloads.mlp_up_case("mxfp4", 1)),
                         ("rmsnorm+qmv affine 4b g64 B1 K=N=4096 bf16",
                          workloads.affine_sweep_case(4, 64, 1, "bf16"))):
@@ -927,6 +1031,8 @@ def main() -> int:
                    "B": 1, "K": 4096, "N": 14336, "format": "mxfp4"},
         "us_per_call": round(res["us_per_call"], 3),
         "us_per_call_plain_launch": round(res["us_per_call_plain"], 3),
+        "us_per_call_replay_range": res["us_per_call_replays"],
+        "timed": res["timed"],
         "pct_peak": round(100 * res["gbps"] / PEAK_HBM_GBPS, 1),
         "roofline": {"bound": "hbm", "achieved": round(res["gbps"], 1),
                      "peak": PEAK_HBM_GBPS, "unit": "GB/s",
