@@ -33,7 +33,11 @@ HIP_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}",
 ]
-CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", f"-I{INCLUDE}", f"-I{CSRC}"]
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+# the host API is plain C++ (g++); the public header names hipStream_t, so it
+# sees the HIP runtime API header of the AMD platform
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
+             f"-I{os.path.join(ROCM, 'include')}", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
 def _jobs() -> list[tuple[list[str], str]]:

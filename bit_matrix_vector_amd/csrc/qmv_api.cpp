@@ -230,7 +230,7 @@ qmv_status_t run_quantize(const char* fn, void* stream, int dtype, int format, i
 
 extern "C" {
 
-qmv_status_t qmv_moe_gate_up_swiglu(void* stream, int dtype, const qmv_weights_t* gate,
+qmv_status_t qmv_moe_gate_up_swiglu(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* gate,
                                     const qmv_weights_t* up, const void* x, int64_t n_tokens,
                                     const uint32_t* expert_ids, int64_t top_k, float clamp,
                                     void* mid) {
@@ -269,7 +269,7 @@ qmv_status_t qmv_moe_gate_up_swiglu(void* stream, int dtype, const qmv_weights_t
     return launch_status(qmv::launch_moe_gate_up(lp, ma, stream), fn);
 }
 
-qmv_status_t qmv_moe_down_reduce(void* stream, int dtype, const qmv_weights_t* down,
+qmv_status_t qmv_moe_down_reduce(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* down,
                                  const void* mid, int64_t n_tokens, const uint32_t* expert_ids,
                                  const float* route_weights, int64_t top_k, void* y) {
     const char* fn = "qmv_moe_down_reduce";
@@ -366,19 +366,19 @@ static qmv_status_t qvm_impl(const char* fn, void* stream, int dtype, const qmv_
     return launch_status(qmv::launch_qvm(q, stream), fn);
 }
 
-qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* wt, int64_t B, const void* x,
+qmv_status_t qmv_qvm(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* wt, int64_t B, const void* x,
                      void* y, void* workspace, size_t workspace_bytes) {
     return qvm_impl("qmv_qvm", stream, dtype, wt, B, x, y, workspace, workspace_bytes, false);
 }
 
 size_t qmv_qvm_noalloc_max_workspace_bytes(void) { return qmv::kScratchBytes; }
 
-qmv_status_t qmv_qvm_noalloc(void* stream, int dtype, const qmv_weights_t* wt, int64_t B,
+qmv_status_t qmv_qvm_noalloc(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* wt, int64_t B,
                              const void* x, void* y) {
     return qvm_impl("qmv_qvm_noalloc", stream, dtype, wt, B, x, y, nullptr, 0, true);
 }
 
-qmv_status_t qmv_rmsnorm_qmv(void* stream, int dtype, const qmv_weights_t* wt, int64_t B,
+qmv_status_t qmv_rmsnorm_qmv(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* wt, int64_t B,
                              const void* x, const void* gamma, float eps, void* y) {
     const char* fn = "qmv_rmsnorm_qmv";
     if (wt == nullptr) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: weights struct is NULL", fn);
@@ -423,13 +423,13 @@ qmv_status_t qmv_rmsnorm_qmv(void* stream, int dtype, const qmv_weights_t* wt, i
     return launch_status(qmv::launch_qmv_norm(lp, na, stream), fn);
 }
 
-size_t qmv_qmm_workspace_bytes(int64_t M, int64_t K, int64_t N, int format) {
+size_t qmv_qmm_workspace_bytes(int64_t M, int64_t K, int64_t N, qmv_format_t format) {
     if (M <= 0 || K <= 0 || N <= 0) return 0;
     const int s = qmv::qmm_splits(M, K, N, format);
     return s > 1 ? (size_t)s * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
-qmv_status_t qmv_qmm(void* stream, int dtype, const qmv_weights_t* wt, int64_t M, const void* x,
+qmv_status_t qmv_qmm(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* wt, int64_t M, const void* x,
                      void* y, void* workspace, size_t workspace_bytes) {
     const char* fn = "qmv_qmm";
     if (wt == nullptr) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: weights struct is NULL", fn);
@@ -483,26 +483,26 @@ qmv_status_t qmv_qmm(void* stream, int dtype, const qmv_weights_t* wt, int64_t M
     return launch_status(qmv::launch_qmm(q, stream), fn);
 }
 
-qmv_status_t qmv_quantize_affine(void* stream, int dtype, int64_t N, int64_t K, const void* w,
+qmv_status_t qmv_quantize_affine(hipStream_t stream, qmv_dtype_t dtype, int64_t N, int64_t K, const void* w,
                                  int bits, int group_size, uint8_t* packed, void* scales,
                                  void* biases) {
     return run_quantize("qmv_quantize_affine", stream, dtype, QMV_AFFINE, bits, group_size, N, K,
                         w, packed, scales, biases, nullptr);
 }
 
-qmv_status_t qmv_quantize_mxfp4(void* stream, int dtype, int64_t N, int64_t K, const void* w,
+qmv_status_t qmv_quantize_mxfp4(hipStream_t stream, qmv_dtype_t dtype, int64_t N, int64_t K, const void* w,
                                 uint8_t* packed, uint8_t* scales) {
     return run_quantize("qmv_quantize_mxfp4", stream, dtype, QMV_MXFP4, 4, 32, N, K, w, packed,
                         scales, nullptr, nullptr);
 }
 
-qmv_status_t qmv_quantize_mxfp8(void* stream, int dtype, int64_t N, int64_t K, const void* w,
+qmv_status_t qmv_quantize_mxfp8(hipStream_t stream, qmv_dtype_t dtype, int64_t N, int64_t K, const void* w,
                                 uint8_t* packed, uint8_t* scales) {
     return run_quantize("qmv_quantize_mxfp8", stream, dtype, QMV_MXFP8, 8, 32, N, K, w, packed,
                         scales, nullptr, nullptr);
 }
 
-qmv_status_t qmv_quantize_nvfp4(void* stream, int dtype, int64_t N, int64_t K, const void* w,
+qmv_status_t qmv_quantize_nvfp4(hipStream_t stream, qmv_dtype_t dtype, int64_t N, int64_t K, const void* w,
                                 uint8_t* packed, uint8_t* scales, float* global_scale) {
     return run_quantize("qmv_quantize_nvfp4", stream, dtype, QMV_NVFP4, 4, 16, N, K, w, packed,
                         scales, nullptr, global_scale);
@@ -510,27 +510,28 @@ qmv_status_t qmv_quantize_nvfp4(void* stream, int dtype, int64_t N, int64_t K, c
 
 const char* qmv_last_error(void) { return g_last_error; }
 
-qmv_status_t qmv_affine(void* stream, int dtype, int64_t B, int64_t K, int64_t N, const void* x,
+qmv_status_t qmv_affine(hipStream_t stream, qmv_dtype_t dtype, int64_t B, int64_t K, int64_t N, const void* x,
                         const uint8_t* w, const void* scales, const void* biases, int bits,
                         int group_size, void* y) {
     return run_qmv("qmv_affine", stream, dtype, QMV_AFFINE, bits, group_size, B, K, N, x, w,
                    scales, biases, nullptr, y);
 }
 
-qmv_status_t qmv_fp_mxfp4(void* stream, int dtype, int64_t B, int64_t K, int64_t N,
+qmv_status_t qmv_fp_mxfp4(hipStream_t stream, qmv_dtype_t dtype, int64_t B, int64_t K, int64_t N,
                           const void* x, const uint8_t* w, const uint8_t* scales, void* y) {
     return run_qmv("qmv_fp_mxfp4", stream, dtype, QMV_MXFP4, 4, 32, B, K, N, x, w, scales,
                    nullptr, nullptr, y);
 }
 
-qmv_status_t qmv_fp_nvfp4(void* stream, int dtype, int64_t B, int64_t K, int64_t N,
+qmv_status_t qmv_fp_nvfp4(hipStream_t stream, qmv_dtype_t dtype, int64_t B, int64_t K, int64_t N,
                           const void* x, const uint8_t* w, const uint8_t* scales,
                           const float* global_scale, void* y) {
     return run_qmv("qmv_fp_nvfp4", stream, dtype, QMV_NVFP4, 4, 16, B, K, N, x, w, scales,
                    nullptr, global_scale, y);
 }
 
-qmv_status_t qmv_fp_block(void* stream, int dtype, int format, int element, int block,
+qmv_status_t qmv_fp_block(hipStream_t stream, qmv_dtype_t dtype, qmv_format_t format,
+                          qmv_element_t element, int block,
                           int64_t B, int64_t K, int64_t N, const void* x, const uint8_t* w,
                           const void* scales, void* y) {
     if (format < QMV_SB_E8M0 || format > QMV_SB_F16)
@@ -540,13 +541,13 @@ qmv_status_t qmv_fp_block(void* stream, int dtype, int format, int element, int 
                    nullptr, nullptr, y);
 }
 
-qmv_status_t qmv_fp_mxfp8(void* stream, int dtype, int64_t B, int64_t K, int64_t N,
+qmv_status_t qmv_fp_mxfp8(hipStream_t stream, qmv_dtype_t dtype, int64_t B, int64_t K, int64_t N,
                           const void* x, const uint8_t* w, const uint8_t* scales, void* y) {
     return run_qmv("qmv_fp_mxfp8", stream, dtype, QMV_MXFP8, 8, 32, B, K, N, x, w, scales,
                    nullptr, nullptr, y);
 }
 
-qmv_status_t gather_qmv(void* stream, int dtype, const qmv_weights_t* wt, const void* x,
+qmv_status_t gather_qmv(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* wt, const void* x,
                         int64_t n_x_rows, const uint32_t* lhs_indices,
                         const uint32_t* rhs_indices, int64_t n_slots, void* y) {
     const char* fn = "gather_qmv";
@@ -586,7 +587,7 @@ qmv_status_t gather_qmv(void* stream, int dtype, const qmv_weights_t* wt, const 
     return launch_status(qmv::launch_gather(lp, stream), fn);
 }
 
-qmv_status_t gather_qmm(void* stream, int dtype, const qmv_weights_t* wt, const void* x,
+qmv_status_t gather_qmm(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* wt, const void* x,
                         int64_t n_x_rows, const uint32_t* lhs_indices,
                         const uint32_t* rhs_indices, int64_t n_slots, void* y) {
     const char* fn = "gather_qmm";
@@ -650,7 +651,7 @@ qmv_status_t gather_qmm(void* stream, int dtype, const qmv_weights_t* wt, const 
 
 // ------------------------------- codecs ----------------------------------
 
-int64_t qmv_packed_row_bytes(int format, int bits, int64_t K) {
+int64_t qmv_packed_row_bytes(qmv_format_t format, int bits, int64_t K) {
     if (K < 0) return -1;
     switch (format) {
         case QMV_AFFINE:
@@ -765,7 +766,7 @@ qmv_status_t qmv_encode_e4m3(const float* v, int64_t n, uint8_t* out) {
     return QMV_OK;
 }
 
-qmv_status_t qmv_unpack_codes_device(void* stream, const uint8_t* packed, int64_t rows,
+qmv_status_t qmv_unpack_codes_device(hipStream_t stream, const uint8_t* packed, int64_t rows,
                                      int64_t K, int bits, uint8_t* codes) {
     const char* fn = "qmv_unpack_codes_device";
     if (!valid_bits(bits)) return fail(QMV_ERR_UNSUPPORTED, "%s: bits=%d", fn, bits);
@@ -777,7 +778,7 @@ qmv_status_t qmv_unpack_codes_device(void* stream, const uint8_t* packed, int64_
     return launch_status(qmv::launch_unpack_device(packed, rows, K, bits, codes, stream), fn);
 }
 
-qmv_status_t qmv_dequant_device(void* stream, int dtype, const qmv_weights_t* wt, float* out) {
+qmv_status_t qmv_dequant_device(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* wt, float* out) {
     const char* fn = "qmv_dequant_device";
     if (wt == nullptr) return fail(QMV_ERR_INVALID_ARGUMENT, "%s: weights struct is NULL", fn);
     if (wt->n_experts != 1)

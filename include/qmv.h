@@ -23,7 +23,8 @@
  * - Tensor pointers of the compute calls are DEVICE pointers to row-major,
  *   contiguous data. The caller owns all memory; nothing here allocates.
  * - `stream` is a hipStream_t (NULL = the default stream). Compute calls are
- *   asynchronous on it and never synchronize.
+ *   asynchronous on it and never synchronize. `dtype` is a qmv_dtype_t;
+ *   values outside the enum are rejected (QMV_ERR_INVALID_ARGUMENT).
  * - x, y and the affine scales/biases share one element type `dtype`
  *   (f32, f16 or bf16); y is written in that type, rounded to nearest-even
  *   from an fp32 accumulation.
@@ -54,6 +55,8 @@
 
 #include <stddef.h>
 #include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -91,20 +94,20 @@ typedef enum {
  * Output rows are independent: the result for row n does not depend on N,
  * so a call with N not a multiple of any tile gives, for rows < N, the same
  * bits as a padded call ("ml-explore/mlx pull request 4516", Correctness). */
-qmv_status_t qmv_affine(void* stream, int dtype, int64_t B, int64_t K, int64_t N,
+qmv_status_t qmv_affine(hipStream_t stream, qmv_dtype_t dtype, int64_t B, int64_t K, int64_t N,
                         const void* x, const uint8_t* w, const void* scales,
                         const void* biases, int bits, int group_size, void* y);
 
 /* MXFP4 QMV.  w [N, K/2] uint8 (E2M1 codes, even k in the low nibble),
  * scales [N, K/32] uint8 (E8M0). x [B, K], y [B, N] in dtype. */
-qmv_status_t qmv_fp_mxfp4(void* stream, int dtype, int64_t B, int64_t K, int64_t N,
+qmv_status_t qmv_fp_mxfp4(hipStream_t stream, qmv_dtype_t dtype, int64_t B, int64_t K, int64_t N,
                           const void* x, const uint8_t* w, const uint8_t* scales, void* y);
 
 /* NVFP4 QMV.  w [N, K/2] uint8 (E2M1), scales [N, K/16] uint8 (E4M3),
  * global_scale: DEVICE pointer to one fp32, or NULL for 1.0; it multiplies
  * each fp32 row sum once ("ml-explore/mlx pull request 4516": NVFP4 calls with
  * a global scale). K % 32 == 0 is required (two scale blocks per 32 codes). */
-qmv_status_t qmv_fp_nvfp4(void* stream, int dtype, int64_t B, int64_t K, int64_t N,
+qmv_status_t qmv_fp_nvfp4(hipStream_t stream, qmv_dtype_t dtype, int64_t B, int64_t K, int64_t N,
                           const void* x, const uint8_t* w, const uint8_t* scales,
                           const float* global_scale, void* y);
 
@@ -126,13 +129,14 @@ qmv_status_t qmv_fp_nvfp4(void* stream, int dtype, int64_t B, int64_t K, int64_t
  * combinations are QMV_ERR_UNSUPPORTED; K % block == 0. Alignment: scales to
  * their element (1, 4 or 2 bytes). fp32 accumulation; each unit of 32 codes
  * folds one scale per 16-code half. */
-qmv_status_t qmv_fp_block(void* stream, int dtype, int format, int element, int block,
+qmv_status_t qmv_fp_block(hipStream_t stream, qmv_dtype_t dtype, qmv_format_t format,
+                          qmv_element_t element, int block,
                           int64_t B, int64_t K, int64_t N, const void* x, const uint8_t* w,
                           const void* scales, void* y);
 
 /* MXFP8 (E4M3 elements) QMV.  w [N, K] uint8 (E4M3), scales [N, K/32] uint8
  * (E8M0). x [B, K], y [B, N] in dtype. */
-qmv_status_t qmv_fp_mxfp8(void* stream, int dtype, int64_t B, int64_t K, int64_t N,
+qmv_status_t qmv_fp_mxfp8(hipStream_t stream, qmv_dtype_t dtype, int64_t B, int64_t K, int64_t N,
                           const void* x, const uint8_t* w, const uint8_t* scales, void* y);
 
 /* Expert-stacked quantized weights for gather_qmv. Expert e's N x K matrix
@@ -141,7 +145,7 @@ qmv_status_t qmv_fp_mxfp8(void* stream, int dtype, int64_t B, int64_t K, int64_t
  * `bits` and `group_size` are read for QMV_AFFINE only; `global_scale`
  * (device fp32 or NULL) for QMV_NVFP4 only and is shared by all experts. */
 typedef struct {
-    int format;              /* qmv_format_t */
+    qmv_format_t format;
     int bits;
     int group_size;
     int64_t n_experts;
@@ -164,7 +168,7 @@ typedef struct {
  * zeros, not a fault). Each slot's row equals, bit for bit, a one-row
  * qmv_* call on that expert and x row. `w` points to host memory (the struct
  * itself); the pointers inside it are device pointers. */
-qmv_status_t gather_qmv(void* stream, int dtype, const qmv_weights_t* w, const void* x,
+qmv_status_t gather_qmv(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* w, const void* x,
                         int64_t n_x_rows, const uint32_t* lhs_indices,
                         const uint32_t* rhs_indices, int64_t n_slots, void* y);
 
@@ -182,7 +186,7 @@ qmv_status_t gather_qmv(void* stream, int dtype, const qmv_weights_t* w, const v
  * block the other experts' slots take zero x rows, so the weights must be
  * finite (an infinite or NaN weight of one expert would turn those rows into
  * NaN). */
-qmv_status_t gather_qmm(void* stream, int dtype, const qmv_weights_t* w, const void* x,
+qmv_status_t gather_qmm(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* w, const void* x,
                         int64_t n_x_rows, const uint32_t* lhs_indices,
                         const uint32_t* rhs_indices, int64_t n_slots, void* y);
 
@@ -191,35 +195,59 @@ qmv_status_t gather_qmm(void* stream, int dtype, const qmv_weights_t* w, const v
 /* Bytes of one packed row: K*bits/8 for QMV_AFFINE, K/2 for the fp4 formats,
  * K for MXFP8 ("mlx 1.0.0 - quantized_nax.h", `get_pack_factor` /
  * `get_bytes_per_pack`). Returns -1 for invalid arguments. */
-int64_t qmv_packed_row_bytes(int format, int bits, int64_t K);
+int64_t qmv_packed_row_bytes(qmv_format_t format, int bits, int64_t K);
 
 /* Pack codes [rows, K] (uint8, each < 2^bits) into rows of K*bits/8 bytes,
- * LSB first. Requires K*bits % 8 == 0. Errors: a code that does not fit. */
+ * LSB first: code j at bits [j*bits, (j+1)*bits) of the row's little-endian
+ * bit stream ("wh-iron kernel-op coverage audit", "Quantization precision
+ * coverage", Track 1: sub-byte codes packed tightly, least significant bit
+ * first; the per-width masks of `dequantize` in "mlx 1.0.0 -
+ * quantized_nax.h" read this layout). HOST pointers; codes [rows, K] and
+ * packed [rows, K*bits/8] are caller-owned. Requires bits in {2,3,4,5,6,8}
+ * and K*bits % 8 == 0 (QMV_ERR_INVALID_ARGUMENT / QMV_ERR_UNSUPPORTED
+ * otherwise); a code >= 2^bits is QMV_ERR_INVALID_ARGUMENT, found before
+ * anything is written, so packed is left untouched. */
 qmv_status_t qmv_pack_codes(const uint8_t* codes, int64_t rows, int64_t K, int bits,
                             uint8_t* packed);
 
-/* Inverse of qmv_pack_codes. */
+/* Inverse of qmv_pack_codes (same layout and passages): packed [rows,
+ * K*bits/8] -> codes [rows, K], HOST pointers, caller-owned. Same argument
+ * checks as qmv_pack_codes. */
 qmv_status_t qmv_unpack_codes(const uint8_t* packed, int64_t rows, int64_t K, int bits,
                               uint8_t* codes);
 
-/* fp32 -> E4M3 (fn) bytes: round to nearest, ties to even; magnitudes above
- * 448 (and infinities) saturate to +-448; NaN gives 0x7F; the sign of zero is
- * kept. For building NVFP4 block scales. */
+/* fp32 -> E4M3 (fn) bytes, for building NVFP4 block scales (the E4M3 block
+ * scale of the NVFP4 row of the "wh-iron kernel-op coverage audit" Track-1
+ * table; the E4M3 constants of its kv_cache op row: 3 mantissa bits, largest
+ * value 448, a NaN sentinel). Round to nearest, ties to even; magnitudes
+ * above 448 (and infinities) saturate to +-448; NaN gives 0x7F; the sign of
+ * zero is kept. v [n] fp32 and out [n] bytes are HOST pointers, caller-owned;
+ * NULL with n > 0 or n < 0 is QMV_ERR_INVALID_ARGUMENT. */
 qmv_status_t qmv_encode_e4m3(const float* v, int64_t n, uint8_t* out);
 
 /* ---------------- codecs: DEVICE memory, asynchronous ---------------------
  * These run the same decode functions as the QMV kernels, so their bit-exact
  * agreement with the definitions covers the hot path's decode. */
 
-/* Device unpack: codes [rows, K] uint8 from packed rows (device pointers). */
-qmv_status_t qmv_unpack_codes_device(void* stream, const uint8_t* packed, int64_t rows,
+/* Device unpack: codes [rows, K] uint8 from packed rows [rows, K*bits/8]
+ * (DEVICE pointers, caller-owned; asynchronous on stream), the layout of
+ * qmv_pack_codes (audit Track 1, LSB first; "mlx 1.0.0 - quantized_nax.h"
+ * `dequantize` masks), through the kernels' own code extraction. Same
+ * argument checks as qmv_pack_codes, before any HIP call; a failed launch is
+ * QMV_ERR_HIP. */
+qmv_status_t qmv_unpack_codes_device(hipStream_t stream, const uint8_t* packed, int64_t rows,
                                      int64_t K, int bits, uint8_t* codes);
 
-/* Device dequant of one matrix (w->n_experts must be 1) to fp32 [N, K]:
- * affine fmaf(s, q, beta); MXFP4 e2m1*2^(e-127); NVFP4 (e2m1*e4m3)*global;
- * MXFP8 e4m3*2^(e-127). Each value is the fp32 rounding of the exact one.
- * `dtype` is the storage type of the affine scales/biases (ignored otherwise). */
-qmv_status_t qmv_dequant_device(void* stream, int dtype, const qmv_weights_t* w, float* out);
+/* Device dequant of one matrix (w->n_experts must be 1) to fp32 [N, K]
+ * (DEVICE out, caller-owned; asynchronous on stream): affine fmaf(s, q, beta)
+ * (`dequantize` of "mlx 1.0.0 - quantized_nax.h": scale * q + bias); MXFP4
+ * e2m1*2^(e-127); NVFP4 (e2m1*e4m3)*global; MXFP8 e4m3*2^(e-127) (the
+ * element and scale definitions of the "wh-iron kernel-op coverage audit"
+ * Track-1 table). Each value is the fp32 rounding of the exact one.
+ * `dtype` is the storage type of the affine scales/biases (ignored
+ * otherwise). The weight arguments are checked as for gather_qmv before any
+ * HIP call; a failed launch is QMV_ERR_HIP. */
+qmv_status_t qmv_dequant_device(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* w, float* out);
 
 /* ---------------- qvm: DEVICE, asynchronous ---------------------------------
  * The transposed product y[b, k] = sum_n x[b, n] * dequant(W)[n, k] over the
@@ -235,7 +263,7 @@ qmv_status_t qmv_dequant_device(void* stream, int dtype, const qmv_weights_t* w,
  * at most 8192 / B rows and a launch at most 65535 splits, so N above
  * 65535 * 8192 / B returns QMV_ERR_UNSUPPORTED. */
 size_t qmv_qvm_workspace_bytes(int64_t B, int64_t K, int64_t N);
-qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* w, int64_t B, const void* x,
+qmv_status_t qmv_qvm(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* w, int64_t B, const void* x,
                      void* y, void* workspace, size_t workspace_bytes);
 
 /* qvm without a workspace argument and without any allocation, for callers
@@ -252,7 +280,7 @@ qmv_status_t qmv_qvm(void* stream, int dtype, const qmv_weights_t* w, int64_t B,
  * partials; each call overwrites every element it reads, so nothing needs
  * clearing. Calls nothing that allocates (no hipMalloc / hipFree). */
 size_t qmv_qvm_noalloc_max_workspace_bytes(void);
-qmv_status_t qmv_qvm_noalloc(void* stream, int dtype, const qmv_weights_t* w, int64_t B,
+qmv_status_t qmv_qvm_noalloc(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* w, int64_t B,
                              const void* x, void* y);
 
 /* ---------------- fused RMSNorm + QMV: DEVICE memory, asynchronous ----------
@@ -268,7 +296,7 @@ qmv_status_t qmv_qvm_noalloc(void* stream, int dtype, const qmv_weights_t* w, in
  * (n_experts == 1); x [B, K] and gamma [K] in dtype (16-byte aligned);
  * y [B, N]; 1 <= B <= 8 (B = 0 is a no-op); eps finite and >= 0. K == 0 writes
  * y = 0. */
-qmv_status_t qmv_rmsnorm_qmv(void* stream, int dtype, const qmv_weights_t* w, int64_t B,
+qmv_status_t qmv_rmsnorm_qmv(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* w, int64_t B,
                              const void* x, const void* gamma, float eps, void* y);
 
 /* ---------------- qmm (batched product): DEVICE memory, asynchronous ---------
@@ -292,8 +320,8 @@ qmv_status_t qmv_rmsnorm_qmv(void* stream, int dtype, const qmv_weights_t* w, in
  * partial sums there and a second kernel adds them in split order, so
  * repeated calls give identical results; calls that share a workspace must
  * not overlap. */
-size_t qmv_qmm_workspace_bytes(int64_t M, int64_t K, int64_t N, int format);
-qmv_status_t qmv_qmm(void* stream, int dtype, const qmv_weights_t* w, int64_t M, const void* x,
+size_t qmv_qmm_workspace_bytes(int64_t M, int64_t K, int64_t N, qmv_format_t format);
+qmv_status_t qmv_qmm(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* w, int64_t M, const void* x,
                      void* y, void* workspace, size_t workspace_bytes);
 
 /* ---------------- fused routed-MoE decode block: DEVICE, asynchronous -------
@@ -311,7 +339,7 @@ qmv_status_t qmv_qmm(void* stream, int dtype, const qmv_weights_t* w, int64_t M,
  * gate and up: same format / bits / group / n_experts / N (= ffn) / K
  * (= hidden); x [n_tokens, K] (16-byte aligned); mid [n_tokens * top_k, N].
  * Requires 2 * K * sizeof(T) <= 64 KB. */
-qmv_status_t qmv_moe_gate_up_swiglu(void* stream, int dtype, const qmv_weights_t* gate,
+qmv_status_t qmv_moe_gate_up_swiglu(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* gate,
                                     const qmv_weights_t* up, const void* x, int64_t n_tokens,
                                     const uint32_t* expert_ids, int64_t top_k, float clamp,
                                     void* mid);
@@ -322,7 +350,7 @@ qmv_status_t qmv_moe_gate_up_swiglu(void* stream, int dtype, const qmv_weights_t
  * [n_tokens, top_k]; y [n_tokens, N]. Requires top_k <= 16,
  * top_k * K * sizeof(T) <= 64 KB and n_tokens <= 65535. Expert weights are read
  * per token, so repeated experts across tokens are served from cache. */
-qmv_status_t qmv_moe_down_reduce(void* stream, int dtype, const qmv_weights_t* down,
+qmv_status_t qmv_moe_down_reduce(hipStream_t stream, qmv_dtype_t dtype, const qmv_weights_t* down,
                                  const void* mid, int64_t n_tokens, const uint32_t* expert_ids,
                                  const float* route_weights, int64_t top_k, void* y);
 
@@ -343,7 +371,7 @@ qmv_status_t qmv_moe_down_reduce(void* stream, int dtype, const qmv_weights_t* d
  * s32 = (hi - lo) / (2^bits - 1); scales = RN_T(s32), biases = RN_T(lo)
  * ([N, K/group_size], in dtype); q = clamp(rint((w - b) / s), 0, 2^bits - 1)
  * against the stored s and b, or 0 where the stored s is 0. */
-qmv_status_t qmv_quantize_affine(void* stream, int dtype, int64_t N, int64_t K, const void* w,
+qmv_status_t qmv_quantize_affine(hipStream_t stream, qmv_dtype_t dtype, int64_t N, int64_t K, const void* w,
                                  int bits, int group_size, uint8_t* packed, void* scales,
                                  void* biases);
 
@@ -352,9 +380,9 @@ qmv_status_t qmv_quantize_affine(void* stream, int dtype, int64_t N, int64_t K, 
  * or 8 (E4M3); element = nearest E2M1 / E4M3 to w / 2^(byte - 127), ties to
  * even, saturating at 6 / 448, sign kept (so -0 encodes with the sign bit).
  * scales [N, K/32] bytes. */
-qmv_status_t qmv_quantize_mxfp4(void* stream, int dtype, int64_t N, int64_t K, const void* w,
+qmv_status_t qmv_quantize_mxfp4(hipStream_t stream, qmv_dtype_t dtype, int64_t N, int64_t K, const void* w,
                                 uint8_t* packed, uint8_t* scales);
-qmv_status_t qmv_quantize_mxfp8(void* stream, int dtype, int64_t N, int64_t K, const void* w,
+qmv_status_t qmv_quantize_mxfp8(hipStream_t stream, qmv_dtype_t dtype, int64_t N, int64_t K, const void* w,
                                 uint8_t* packed, uint8_t* scales);
 
 /* NVFP4: global = A / 2688 with A = max |w| over the matrix (written to the
@@ -362,10 +390,14 @@ qmv_status_t qmv_quantize_mxfp8(void* stream, int dtype, int64_t N, int64_t K, c
  * word while the call runs); per block of 16: sb = (max |w| / 6) / global,
  * scale byte = nearest E4M3 to sb (saturating); d = decoded scale * global;
  * element = nearest E2M1 to w / d, or code 0 where d is 0. scales [N, K/16]. */
-qmv_status_t qmv_quantize_nvfp4(void* stream, int dtype, int64_t N, int64_t K, const void* w,
+qmv_status_t qmv_quantize_nvfp4(hipStream_t stream, qmv_dtype_t dtype, int64_t N, int64_t K, const void* w,
                                 uint8_t* packed, uint8_t* scales, float* global_scale);
 
-/* Message for the last non-OK status returned on this thread ("" if none). */
+/* Message for the last non-OK status returned on this thread ("" if none):
+ * every entry point returns a typed status and records a readable message
+ * with it (the typed error results with a message of "ferrum-kernels 0.8.0 -
+ * primitives.rs"). The string is owned by the library and stays valid until
+ * the thread's next failing call. */
 const char* qmv_last_error(void);
 
 #ifdef __cplusplus
