@@ -595,9 +595,9 @@ def time_case(runner: Runner, steps: int, warmup: int) -> dict:
 
 def time_stream_read(bmv, nbytes: int, steps: int, warmup: int, min_bytes: int = 1 << 30,
                      unroll: int = 8):
-    """The measured ceiling: a plain 16-byte streaming read of `nbytes` per
-    launch over rotating, distinct buffers (same cold-HBM method as the QMV
-    timing), with an event pair around each launch."""
+    """A plain 16-byte streaming read of `nbytes` per launch over rotating,
+    distinct buffers (cold HBM), with an event pair around each launch; the
+    size sweep uses it."""
     import torch
     lib = bmv.load()
     nbytes = (nbytes + 15) // 16 * 16
@@ -627,6 +627,63 @@ def time_stream_read(bmv, nbytes: int, steps: int, warmup: int, min_bytes: int =
     del buf
     return {"bytes": nbytes, "us_per_call": us, "gbps": nbytes / us / 1e3, "copies": copies,
             "unroll": unroll}
+
+
+READ_DESIGNS = {
+    0: "one-shot, 256 threads x 2 loads", 1: "one-shot, 256 x 4", 2: "one-shot, 256 x 8",
+    3: "one-shot, 512 x 4", 4: "one-shot, 1024 x 2", 5: "one-shot, 64 x 8",
+    6: "one-shot, 256 x 4, XCD-contiguous blocks", 7: "32 contiguous bytes per lane",
+    8: "64 contiguous bytes per lane", 9: "grid-stride, 256 blocks x 4 loads",
+    10: "grid-stride, 512 x 4", 11: "grid-stride, 1024 x 4", 12: "grid-stride, 2048 x 4",
+    13: "grid-stride, 256 x 8", 14: "grid-stride, 512 x 8",
+    15: "rows: 8 lanes per 128-byte line", 16: "rows: 16x16 MFMA operand layout",
+}
+
+
+CEILING_DESIGN = 0
+
+
+class ReadRunner:
+    """One read design over rotating, distinct buffers (cold HBM), with the
+    Runner interface time_case expects."""
+
+    def __init__(self, bmv, nbytes: int, design: int, min_bytes: int = 1 << 30):
+        import torch
+        self.lib = bmv.load()
+        self.nbytes = nbytes
+        self.copies = max(2, -(-min_bytes // nbytes))
+        self.buf = torch.empty(self.copies * nbytes, dtype=torch.uint8, device="cuda:0")
+        self.buf.random_(0, 256)
+        self.sink = torch.zeros(65536, dtype=torch.int32, device="cuda:0")
+        self.design = design
+        self.bytes = nbytes
+
+    def call(self, i: int, stream) -> None:
+        st = self.lib.qmv_bench_read_design(
+            stream, ctypes.c_void_p(self.buf.data_ptr() + (i % self.copies) * self.nbytes),
+            self.nbytes, ctypes.c_void_p(self.sink.data_ptr()), self.design)
+        if st != 0:
+            raise RuntimeError(f"read design {self.design} failed: {st}")
+
+    def free(self):
+        self.buf = None
+
+
+def read_designs(bmv, steps: int) -> list[dict]:
+    """Every read design at the headline's byte counts: the 31,232,000
+    algorithmic bytes, and the 29,360,128 weight bytes for the row patterns
+    (which need whole 2048-byte rows); timed like the QMV (graph replays)."""
+    out = []
+    for d, name in READ_DESIGNS.items():
+        nbytes = 14336 * 2048 if d >= 15 else 31232000
+        r = ReadRunner(bmv, nbytes, d)
+        res = time_case(r, steps, 20)
+        r.free()
+        res.update(design=d, name=name)
+        out.append(res)
+        print(f"[read] design {d:2d} {name:42s} {nbytes / 1e6:7.3f} MB "
+              f"{res['us_per_call']:7.3f} us {res['gbps']:7.1f} GB/s", file=sys.stderr, flush=True)
+    return out
 
 
 def ceiling_sweep(bmv, steps: int, warmup: int) -> None:
@@ -854,6 +911,9 @@ def main() -> int:
                     help="also time the whole affine sweep (K=N=4096) to stderr")
     ap.add_argument("--ceiling-sweep", action="store_true",
                     help="only sweep the streaming-read ceiling over sizes and exit")
+    ap.add_argument("--read-designs", action="store_true",
+                    help="only time every read design at the headline's byte count, then the "
+                         "headline QMV, and exit")
     ap.add_argument("--pmc-workload", type=int, default=0, metavar="N",
                     help="only run the counter workload (N copies, N headline launches)")
     ap.add_argument("--summarize-trace-table", metavar="TRACE_CSV",
@@ -889,6 +949,14 @@ def main() -> int:
     if args.ceiling_sweep:
         ceiling_sweep(bmv, min(args.steps, 200), 10)
         return 0
+    if args.read_designs:
+        designs = read_designs(bmv, args.steps)
+        head = workloads.mlp_up_case("mxfp4", 1)
+        r = Runner(bmv, head)
+        q = time_case(r, args.steps, args.warmup)
+        r.free()
+        print(json.dumps({"read_designs": designs, "qmv_headline": q}), flush=True)
+        return 0
     if args.pmc_workload:
         pmc_workload(bmv, args.pmc_workload)
         return 0
@@ -901,7 +969,12 @@ def main() -> int:
 
     ceiling = None
     if not args.no_ceiling:
-        ceiling = time_stream_read(bmv, head.algorithmic_bytes(), args.steps, args.warmup)
+        # The fastest read design measured at this byte count (one-shot grid,
+        # 256 threads, two 16-byte loads per lane), timed like the QMV.
+        rr = ReadRunner(bmv, head.algorithmic_bytes(), CEILING_DESIGN)
+        ceiling = time_case(rr, args.steps, args.warmup)
+        rr.free()
+        ceiling.update(design=CEILING_DESIGN, name=READ_DESIGNS[CEILING_DESIGN])
         print(f"[bench] stream-read ceiling: {json.dumps(ceiling)}", file=sys.stderr, flush=True)
 
     cases = []
@@ -1041,6 +1114,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "stream_read_ceiling": None if ceiling is None else {
             "gbps": round(ceiling["gbps"], 1), "us_per_call": round(ceiling["us_per_call"], 3),
+            "design": ceiling["name"], "timed": ceiling["timed"],
             "qmv_frac_of_ceiling": round(res["gbps"] / ceiling["gbps"], 4)},
         "cases": cases,
     }

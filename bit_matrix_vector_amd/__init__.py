@@ -131,6 +131,8 @@ def load() -> ctypes.CDLL:
     lib.qmv_packed_row_bytes.restype = i64
     lib.qmv_bench_stream_read.argtypes = [vp, vp, i64, vp, i32]
     lib.qmv_bench_stream_read.restype = ctypes.c_int
+    lib.qmv_bench_read_design.argtypes = [vp, vp, i64, vp, i32]
+    lib.qmv_bench_read_design.restype = ctypes.c_int
     lib.qmv_bench_copy.argtypes = [vp, vp, vp, i64]
     lib.qmv_bench_copy.restype = ctypes.c_int
     lib.qmv_last_error.argtypes = []

@@ -46,7 +46,152 @@ int launch_read(hipStream_t st, const v4u* p, int64_t n, uint32_t* sink) {
     return (int)hipGetLastError();
 }
 
+// One-shot read with T threads per block, U 16-byte loads per lane; with
+// XCD the blocks run in XCD-contiguous order (block b of the 8-way
+// round-robin dispatch takes the b/8-th range of XCD b % 8's share).
+template <int T, int U, bool XCD>
+__global__ __launch_bounds__(T) void read_oneshot_kernel(const v4u* __restrict__ p, int64_t n,
+                                                         uint32_t* __restrict__ sink) {
+    int64_t b = blockIdx.x;
+    if (XCD) {
+        const int64_t nb = gridDim.x, q = nb / 8, r = nb % 8, x = b % 8;
+        b = x * q + (x < r ? x : r) + b / 8;
+    }
+    const int64_t base = b * T * U + threadIdx.x;
+    v4u v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        const int64_t i = base + (int64_t)j * T;
+        v[j] = __builtin_nontemporal_load(p + (i < n ? i : n - 1));
+    }
+    v4u a = v[0];
+#pragma unroll
+    for (int j = 1; j < U; ++j) a ^= v[j];
+    const uint32_t r = a.x ^ a.y ^ a.z ^ a.w;
+    if (r == 0x9E3779B9u) sink[blockIdx.x & 0xFFFF] = r;
+}
+
+// Each lane reads W consecutive 16-byte vectors (16 W bytes per lane).
+template <int W>
+__global__ __launch_bounds__(256) void read_wide_kernel(const v4u* __restrict__ p, int64_t n,
+                                                        uint32_t* __restrict__ sink) {
+    const int64_t base = ((int64_t)blockIdx.x * 256 + threadIdx.x) * W;
+    v4u v[W];
+#pragma unroll
+    for (int j = 0; j < W; ++j) {
+        const int64_t i = base + j;
+        v[j] = __builtin_nontemporal_load(p + (i < n ? i : n - 1));
+    }
+    v4u a = v[0];
+#pragma unroll
+    for (int j = 1; j < W; ++j) a ^= v[j];
+    const uint32_t r = a.x ^ a.y ^ a.z ^ a.w;
+    if (r == 0x9E3779B9u) sink[blockIdx.x & 0xFFFF] = r;
+}
+
+// Persistent grid-stride read: a fixed grid, U loads per lane in flight per
+// iteration; every lane runs the same number of iterations (clamped indices).
+template <int U>
+__global__ __launch_bounds__(256) void read_stride_kernel(const v4u* __restrict__ p, int64_t n,
+                                                          uint32_t* __restrict__ sink) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    const int64_t per_it = stride * U;
+    const int64_t iters = (n + per_it - 1) / per_it;
+    v4u a = {0u, 0u, 0u, 0u};
+    for (int64_t it = 0; it < iters; ++it) {
+        const int64_t base = it * per_it + (int64_t)blockIdx.x * 256 + threadIdx.x;
+        v4u v[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int64_t i = base + (int64_t)j * stride;
+            v[j] = __builtin_nontemporal_load(p + (i < n ? i : n - 1));
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) a ^= v[j];
+    }
+    const uint32_t r = a.x ^ a.y ^ a.z ^ a.w;
+    if (r == 0x9E3779B9u) sink[blockIdx.x & 0xFFFF] = r;
+}
+
+// Row patterns over [rows][2048 bytes] (the MXFP4 K=4096 row length): a wave
+// reads 16 rows x 256 bytes with four instructions. MODE 0: eight lanes per
+// 128-byte line (lane l: row l / 8 of an 8-row half, 16 bytes at l % 8);
+// MODE 1: the 16x16x32 MFMA operand layout (lane l: row l % 16, 16 bytes at
+// 16 (l / 16) of a 64-byte segment).
+template <int MODE>
+__global__ __launch_bounds__(256) void read_rows_kernel(const uint8_t* __restrict__ p,
+                                                        int64_t rows, uint32_t* __restrict__ sink) {
+    const int lane = threadIdx.x & 63;
+    const int64_t wv = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int64_t r0 = (wv / 8) * 16;            // 8 waves across a row group's 2048 bytes
+    const int64_t c0 = (wv % 8) * 256;
+    v4u v[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        int64_t r;
+        int64_t off;
+        if (MODE == 0) {
+            r = r0 + (s & 1) * 8 + lane / 8;
+            off = c0 + 128 * (s >> 1) + 16 * (lane % 8);
+        } else {
+            r = r0 + lane % 16;
+            off = c0 + 64 * s + 16 * (lane / 16);
+        }
+        r = r < rows ? r : rows - 1;
+        v[s] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p + r * 2048 + off));
+    }
+    v4u a = v[0] ^ v[1] ^ v[2] ^ v[3];
+    const uint32_t rr = a.x ^ a.y ^ a.z ^ a.w;
+    if (rr == 0x9E3779B9u) sink[blockIdx.x & 0xFFFF] = rr;
+}
+
+template <class Kern>
+int launch_blocks(Kern k, int64_t blocks, int threads, hipStream_t st, const v4u* p, int64_t n,
+                  uint32_t* sink) {
+    if (blocks > 0x7FFFFFFF) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(k, dim3((unsigned)blocks), dim3(threads), 0, st, p, n, sink);
+    return (int)hipGetLastError();
+}
+
 }  // namespace
+
+extern "C" int qmv_bench_read_design(void* stream, const void* buf, int64_t bytes,
+                                     uint32_t* sink, int design) {
+    if (bytes <= 0 || bytes % 16 || (reinterpret_cast<uintptr_t>(buf) & 15))
+        return (int)hipErrorInvalidValue;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const v4u* p = static_cast<const v4u*>(buf);
+    const int64_t n = bytes / 16;
+    auto nb = [&](int64_t per) { return (n + per - 1) / per; };
+    switch (design) {
+        case 0: return launch_blocks(read_oneshot_kernel<256, 2, false>, nb(512), 256, st, p, n, sink);
+        case 1: return launch_blocks(read_oneshot_kernel<256, 4, false>, nb(1024), 256, st, p, n, sink);
+        case 2: return launch_blocks(read_oneshot_kernel<256, 8, false>, nb(2048), 256, st, p, n, sink);
+        case 3: return launch_blocks(read_oneshot_kernel<512, 4, false>, nb(2048), 512, st, p, n, sink);
+        case 4: return launch_blocks(read_oneshot_kernel<1024, 2, false>, nb(2048), 1024, st, p, n, sink);
+        case 5: return launch_blocks(read_oneshot_kernel<64, 8, false>, nb(512), 64, st, p, n, sink);
+        case 6: return launch_blocks(read_oneshot_kernel<256, 4, true>, nb(1024), 256, st, p, n, sink);
+        case 7: return launch_blocks(read_wide_kernel<2>, nb(512), 256, st, p, n, sink);
+        case 8: return launch_blocks(read_wide_kernel<4>, nb(1024), 256, st, p, n, sink);
+        case 9: return launch_blocks(read_stride_kernel<4>, 256, 256, st, p, n, sink);
+        case 10: return launch_blocks(read_stride_kernel<4>, 512, 256, st, p, n, sink);
+        case 11: return launch_blocks(read_stride_kernel<4>, 1024, 256, st, p, n, sink);
+        case 12: return launch_blocks(read_stride_kernel<4>, 2048, 256, st, p, n, sink);
+        case 13: return launch_blocks(read_stride_kernel<8>, 256, 256, st, p, n, sink);
+        case 14: return launch_blocks(read_stride_kernel<8>, 512, 256, st, p, n, sink);
+        case 15:
+        case 16: {
+            if (bytes % (2048 * 16)) return (int)hipErrorInvalidValue;
+            const int64_t rows = bytes / 2048;
+            auto* k = design == 15 ? read_rows_kernel<0> : read_rows_kernel<1>;
+            // rows / 16 row groups x 8 waves, 4 waves per block
+            hipLaunchKernelGGL(k, dim3((unsigned)(rows / 16 * 2)), dim3(256), 0, st,
+                               static_cast<const uint8_t*>(buf), rows, sink);
+            return (int)hipGetLastError();
+        }
+        default: return (int)hipErrorInvalidValue;
+    }
+}
 
 extern "C" int qmv_bench_stream_read(void* stream, const void* buf, int64_t bytes,
                                      uint32_t* sink, int unroll) {

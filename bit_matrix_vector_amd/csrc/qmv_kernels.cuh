@@ -1444,248 +1444,306 @@ int launch_qmv_norm_t(const LaunchParams& p, const NormArgs& na, hipStream_t st)
 }
 
 // ---------------------------------------------------------------------------
-// QMV on the matrix cores for several activation rows of the block-scaled
-// formats (16-bit activations). With B rows the VALU tile does B dot products
+// QMV on the matrix cores for 3..8 activation rows of the block-scaled
+// formats (bf16 activations). With B rows the VALU tile does B dot products
 // per decoded code pair, which makes it issue-bound from B = 3 on; here the
-// products run on v_mfma_f32_32x32x16 with the weights as the A operand and
-// the x rows as the B operand (columns past B repeat row B - 1 and are never
-// stored), so the VALU only decodes. A block owns 32 weight rows; its four
-// waves take contiguous quarters of the row's 64-code segments, so each wave
-// reads whole 128-byte lines over consecutive segments (with segments dealt
-// round-robin, four waves shared every line and the kernel fetched most of
-// it several times). In a segment a lane (row r = lane % 32, half h = lane / 32) holds
-// the 32 codes [32 h, 32 h + 32), one scale block (NVFP4: two), converted in
-// registers; k-step s of the MFMA takes codes 32 h + 8 s .. + 8 from both
-// operands, so every k slot pairs x and W at the same code. x is staged in
-// LDS, zero-padded to whole segments; the four waves' fp32 tiles are added
-// in LDS in wave order, then rounded once. The weights load plainly: a line
-// is read by four consecutive segment loads of one wave. The sum over a row's K therefore
-// runs in a fixed order (per segment inside the MFMA, segments in each wave's
-// order, waves 0..3) and every launch gives the same bits.
+// products run on v_mfma_f32_16x16x32_bf16 with the weights as the A operand
+// (16 weight rows) and the activation rows as the B operand columns (16
+// columns, of which B are used), so the VALU only decodes.
+//
+// A block owns 32 weight rows (two 16-row tiles) and all of K; its waves take
+// chunks of 128 weight bytes per row (256 FP4 or 128 FP8 codes), chunk c
+// going to wave c mod W. A chunk is loaded with four coalesced loads (lane l
+// reads 16 bytes of row 8 i + l / 8, so eight consecutive lanes cover one
+// 128-byte line), written to the wave's own LDS area and read back in the
+// MFMA operand layout: lane 16 q + r holds the 32 codes [32 q, 32 q + 32) of
+// a 128-code segment of row r, one MX scale block, and MFMA t of the segment
+// takes codes 8 t .. 8 t + 7 of every lane's 32 (the same k order in A and
+// B). The 16-byte pieces are stored XOR-swizzled by row so the operand reads
+// hit distinct LDS banks. x values enter the B operand straight from global
+// memory (lanes of column b < B), scales are decoded from bytes loaded per
+// lane (one vector load per row and chunk when aligned). Codes at k >= K
+// enter as zeros, together with their x values.
+//
+// Each output is one MFMA accumulator element per wave, summed over that
+// wave's chunks in order; the W partial sums are added in wave order in LDS
+// and rounded once. A row's result depends on K and its own data only, and a
+// column's on its own x row only, so tail rows equal a padded call and every
+// activation row equals the same row in any other batch of 3..8 rows, bit
+// for bit.
 // ---------------------------------------------------------------------------
-typedef float f32x16_t __attribute__((__vector_size__(16 * sizeof(float))));
-template <int DT> struct Mfma;
-template <> struct Mfma<DT_BF16> {
+template <int DT> struct Mfma16;
+template <> struct Mfma16<DT_BF16> {
     typedef __bf16 v8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
-    __device__ static inline f32x16_t run(v8 a, v8 b, f32x16_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
 };
-template <> struct Mfma<DT_F16> {
-    typedef _Float16 v8 __attribute__((__vector_size__(8 * sizeof(_Float16))));
-    __device__ static inline f32x16_t run(v8 a, v8 b, f32x16_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
-};
+typedef float mf_f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
 
-constexpr int kMfmaRows = 32;    // weight rows per block
-constexpr int kMfmaDepth = 4;    // segments in flight per lane (a register ring)
-constexpr int kMfmaXAhead = 8;   // x chunks per thread loaded ahead of the weights
-constexpr int kMfmaRedBytes = kWaves * 32 * 32 * 4;   // the waves' fp32 tiles
+constexpr int kMfRows = 32;          // weight rows per block
+constexpr int kMfChunkBytes = 128;   // weight bytes per row and chunk
+constexpr int kMfMaxWaves = 16;
 
-// LDS of one launch: x padded to whole 64-code segments, then the waves' tiles
-inline size_t mfma_lds_bytes(const LaunchParams& p) {
-    const int64_t kpad = (p.K + 63) / 64 * 64;
-    return (size_t)(p.B * kpad * 2) + kMfmaRedBytes;
+// codes per chunk and 128-code segments per chunk
+template <int FMT> constexpr int mf_chunk_codes() { return FMT == FMT_MXFP8 ? 128 : 256; }
+
+// Waves per block: one per chunk, at most 16; at most 8 for the NVFP4 decode
+// (fp32 products: 88 VGPRs) and the general instances (82..108 VGPRs), so two
+// blocks still fit a compute unit.
+template <int FMT, bool kWhole> constexpr int mf_max_waves() {
+    return (kWhole && FMT != FMT_NVFP4) ? kMfMaxWaves : kMfMaxWaves / 2;
+}
+inline int mfma_waves(const LaunchParams& p, int max_waves) {
+    const int cc = p.format == FMT_MXFP8 ? 128 : 256;
+    const int64_t chunks = (p.K + cc - 1) / cc;
+    return (int)(chunks < max_waves ? (chunks > 0 ? chunks : 1) : max_waves);
 }
 
-template <int DT, int FMT>
-__global__ __launch_bounds__(kThreads) void qmv_mfma_kernel(LaunchParams p) {
+// kWhole: K is a multiple of the chunk and the scale rows allow vector loads
+// (every chunk is whole); otherwise codes past K are zeroed by selects and
+// the scale bytes are loaded one by one.
+template <int DT, int FMT, bool kWhole>
+__global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_kernel(LaunchParams p) {
     static_assert(FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8, "block-scaled only");
     using S = typename Store<DT>::S;
-    using V8 = typename Mfma<DT>::v8;
-    constexpr int kCW = FMT == FMT_MXFP8 ? 8 : 4;   // code words per lane and segment
+    using V8 = typename Mfma16<DT>::v8;
+    constexpr int kCodes = mf_chunk_codes<FMT>();        // codes per chunk
+    constexpr int kSegs = kCodes / 128;                  // 128-code segments per chunk
+    constexpr int kBlk = FMT == FMT_NVFP4 ? 16 : 32;     // codes per scale
+    constexpr int kScB = kCodes / kBlk;                  // scale bytes per row and chunk
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int ln = lane & 31;
-    const int hf = lane >> 5;
     const int wave = tid >> 6;
+    const int nw = (int)(blockDim.x >> 6);
+    const int r16 = lane & 15;
+    const int q = lane >> 4;
     const int B = (int)p.B;
     const int64_t K = p.K, N = p.N;
-    const int kpad = (int)((K + 63) / 64 * 64);
-    const int nseg = kpad / 64;
-    const int64_t n0 = (int64_t)blockIdx.x * kMfmaRows;
-    uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                     // [B][kpad]
-    float* red = reinterpret_cast<float*>(smem + (size_t)B * kpad * 2);   // [kWaves][32 * 32]
+    const int64_t row0 = (int64_t)blockIdx.x * kMfRows;
+    const int64_t nchunks = (K + kCodes - 1) / kCodes;
+    uint8_t* wl = smem + (size_t)wave * kMfRows * kMfChunkBytes;
     const S* x = static_cast<const S*>(p.x);
+    const uint8_t* scb = static_cast<const uint8_t*>(p.scales);
 
-    // x chunks: chunk v of the staged [B][kpad] block is row v / (kpad / 8),
-    // elements 8 (v % (kpad / 8)) ..; chunks past K are zeros
-    const int cpr = kpad / 8;
-    const int nchunks = B * cpr;
-    auto x_src = [&](int v) __attribute__((always_inline)) {
-        const int b = v / cpr;
-        const int64_t k = (int64_t)(v - b * cpr) * 8;
-        return reinterpret_cast<const v4u*>(x + (int64_t)b * K + (k < K ? k : K - 8));
-    };
-    auto x_ok = [&](int v) __attribute__((always_inline)) {
-        return (int64_t)(v - (v / cpr) * cpr) * 8 < K;
-    };
-    v4u xa[kMfmaXAhead];
+    // rows this lane loads (coalesced) and reads (operand layout), clamped
+    int64_t lrow[4];
 #pragma unroll
-    for (int j = 0; j < kMfmaXAhead; ++j) xa[j] = *x_src(min(tid + j * kThreads, nchunks - 1));
-
-    // this lane's weight row (clamped to N - 1) and its segments g = g0 + i,
-    // i < cnt: the wave's contiguous quarter of the row
-    const int64_t row = n0 + ln < N ? n0 + ln : N - 1;
-    const uint8_t* wrow = p.w + row * p.row_bytes;
-    const uint8_t* srow = static_cast<const uint8_t*>(p.scales) + row * p.sc_per_row;
-    const int per = (nseg + kWaves - 1) / kWaves;
-    const int g0 = wave * per;
-    const int cnt = nseg > g0 ? (nseg - g0 < per ? nseg - g0 : per) : 0;
-    struct Seg {
-        uint32_t w[kCW];
-        uint32_t s;
-    };
-    auto load = [&](Seg& b, int i) __attribute__((always_inline)) {
-        const int ic = i < cnt ? i : (cnt > 0 ? cnt - 1 : 0);
-        const int64_t hk0 = (int64_t)(g0 + ic) * 64 + 32 * hf;
-        const int64_t hk = hk0 < K ? hk0 : K - 32;   // first code of the lane's half
-        load_words<kCW>(wrow + (FMT == FMT_MXFP8 ? hk : hk / 2), b.w);
-        if constexpr (FMT == FMT_NVFP4)   // two E4M3 bytes (the scales may be byte-aligned)
-            b.s = (uint32_t)srow[hk / 16] | ((uint32_t)srow[hk / 16 + 1] << 8);
-        else
-            b.s = srow[hk / 32];
-    };
-    Seg ring[kMfmaDepth];
-    static_for<0, kMfmaDepth>([&](auto d_c) { load(ring[decltype(d_c)::value], decltype(d_c)::value); });
-
-    // x to LDS (the loads above went out before the weights)
-#pragma unroll
-    for (int j = 0; j < kMfmaXAhead; ++j) {
-        const int v = tid + j * kThreads;
-        if (v < nchunks)
-            *reinterpret_cast<v4u*>(xs + (size_t)v * 8) = x_ok(v) ? xa[j] : v4u{0u, 0u, 0u, 0u};
+    for (int i = 0; i < 4; ++i) {
+        const int64_t r = row0 + 8 * i + (lane >> 3);
+        lrow[i] = r < N ? r : N - 1;
     }
-    for (int v = tid + kMfmaXAhead * kThreads; v < nchunks; v += kThreads)
-        *reinterpret_cast<v4u*>(xs + (size_t)v * 8) = x_ok(v) ? *x_src(v) : v4u{0u, 0u, 0u, 0u};
-    __syncthreads();
-
-    const uint16_t* xrow = xs + (size_t)(ln < B ? ln : B - 1) * kpad + 32 * hf;
-    f32x16_t acc;
+    int64_t orow[2];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-    auto step = [&](int i, Seg& b) __attribute__((always_inline)) {
-        const int g = g0 + i;
-        const bool hv = (int64_t)g * 64 + 32 * hf < K;
-        uint32_t a[4][4];
-        if constexpr (FMT == FMT_MXFP4) {
-            const float sc = __uint_as_float(b.s << 23);
-            static_for<0, 4>([&](auto s_c) {
-                constexpr int s = decltype(s_c)::value;
-                static_for<0, 4>([&](auto e_c) {
-                    constexpr int e = decltype(e_c)::value;
-                    if constexpr (DT == DT_BF16)
-                        a[s][e] = __builtin_bit_cast(
-                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(b.w[s], sc, e));
-                    else
-                        a[s][e] = __builtin_bit_cast(
-                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(b.w[s], sc, e));
-                });
-            });
-        } else if constexpr (FMT == FMT_MXFP8) {
-            const float sc = __uint_as_float(b.s << 23);
-            static_for<0, 4>([&](auto s_c) {
-                constexpr int s = decltype(s_c)::value;
-                static_for<0, 2>([&](auto e_c) {
-                    constexpr int e = decltype(e_c)::value;
-                    const uint32_t wd = b.w[2 * s + e];
-                    if constexpr (DT == DT_BF16) {
-                        a[s][2 * e] = __builtin_bit_cast(
-                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd, sc, false));
-                        a[s][2 * e + 1] = __builtin_bit_cast(
-                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(wd, sc, true));
-                    } else {
-                        a[s][2 * e] = __builtin_bit_cast(
-                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd, sc, false));
-                        a[s][2 * e + 1] = __builtin_bit_cast(
-                            uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wd, sc, true));
-                    }
-                });
-            });
-        } else {
-            // E2M1 times its E4M3 block scale, exact in fp32 and in the 16-bit
-            // type (at most 6 significant bits); codes 0..15 take the first byte
-            const f32x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(b.s, 1.0f, false);
-            static_for<0, 4>([&](auto s_c) {
-                constexpr int s = decltype(s_c)::value;
-                const float scs = s < 2 ? sc.x : sc.y;
-                static_for<0, 4>([&](auto e_c) {
-                    constexpr int e = decltype(e_c)::value;
-                    const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(b.w[s], 1.0f, e);
-                    const f32x2 q = {v.x * scs, v.y * scs};
-                    if constexpr (DT == DT_BF16)
-                        a[s][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(q, bf16x2_t));
-                    else
-                        a[s][e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(q, f16x2_t));
-                });
-            });
+    for (int t = 0; t < 2; ++t) {
+        const int64_t r = row0 + 16 * t + r16;
+        orow[t] = r < N ? r : N - 1;
+    }
+    // columns past B repeat activation row B - 1: their results are never
+    // stored, so every lane loads a valid row and no load is predicated
+    const bool has = r16 < B;
+    const S* xrow = x + (int64_t)(has ? r16 : B - 1) * K;
+
+    mf_f32x4_t acc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) acc[t] = mf_f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    for (int64_t c = wave; c < nchunks; c += nw) {
+        const int64_t code0 = c * kCodes;                // first code of the chunk
+        const int64_t byte0 = FMT == FMT_MXFP8 ? code0 : code0 / 2;
+        // (1) weights: instruction i covers rows 8 i .. 8 i + 7 of the block;
+        // lane l takes piece (l % 8) ^ g(row) of its row's 128 bytes, so row r
+        // piece p lands in slot 8 (r % 8) + (p ^ g(r)), g(r) = (r / 2) % 8.
+        // Pieces past the row end read its last piece (zeroed below).
+        v4u raw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 8 * i + (lane >> 3);
+            const int piece = (lane & 7) ^ ((r >> 1) & 7);
+            int64_t off = byte0 + 16 * piece;
+            off = off + 16 <= p.row_bytes ? off : p.row_bytes - 16;
+            raw[i] = load_vec<true, v4u>(p.w + lrow[i] * p.row_bytes + off);
         }
-        // a half past K enters as zeros: a select, since the two halves of a
-        // wave differ (as a branch it cost a wait for every load in flight)
+        // (2) scales: the row's kScB bytes of this chunk
+        uint32_t sw[2][kScB / 4 > 0 ? kScB / 4 : 1];
+        const int64_t e0 = code0 / kBlk;
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int t = 0; t < 2; ++t) {
+            const uint8_t* srow = scb + orow[t] * p.sc_per_row;
+            if constexpr (kWhole) {
+                if constexpr (kScB == 16) {
+                    const v4u v = *reinterpret_cast<const v4u*>(srow + e0);
+                    sw[t][0] = v.x; sw[t][1] = v.y; sw[t][2] = v.z; sw[t][3] = v.w;
+                } else if constexpr (kScB == 8) {
+                    const v2u v = *reinterpret_cast<const v2u*>(srow + e0);
+                    sw[t][0] = v.x; sw[t][1] = v.y;
+                } else {
+                    sw[t][0] = *reinterpret_cast<const uint32_t*>(srow + e0);
+                }
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) a[s][e] = hv ? a[s][e] : 0u;
-        load(b, i + kMfmaDepth);
-        static_for<0, 4>([&](auto s_c) {
-            constexpr int s = decltype(s_c)::value;
-            const V8 xb = *reinterpret_cast<const V8*>(xrow + (size_t)g * 64 + 8 * s);
-            const V8 wa = __builtin_bit_cast(V8, v4u{a[s][0], a[s][1], a[s][2], a[s][3]});
-            acc = Mfma<DT>::run(wa, xb, acc);
-        });
-    };
-    int i = 0;
-    for (; i + kMfmaDepth <= cnt; i += kMfmaDepth) {
-        static_for<0, kMfmaDepth>([&](auto d_c) {
-            constexpr int d = decltype(d_c)::value;
-            step(i + d, ring[d]);
-        });
+                for (int j = 0; j < kScB / 4; ++j) {
+                    uint32_t v = 0;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const int64_t e = e0 + 4 * j + b;
+                        v |= (uint32_t)srow[e < p.sc_per_row ? e : p.sc_per_row - 1] << (8 * b);
+                    }
+                    sw[t][j] = v;
+                }
+            }
+        }
+        // (3) x: the B operand of MFMA t of segment s in lane (column r16, q)
+        // holds x[r16][code0 + 128 s + 32 q + 8 t .. + 8]
+        v4u xb[kSegs][4];
+#pragma unroll
+        for (int s = 0; s < kSegs; ++s) {
+            const int64_t k = code0 + 128 * s + 32 * q;
+            const bool kv = kWhole || k < K;
+            const int64_t kl = kv ? k : K - 32;          // a valid address; zeroed below
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                xb[s][t] = *reinterpret_cast<const v4u*>(xrow + kl + 8 * t);
+                if constexpr (!kWhole) {
+                    // x past K enters as zero with its zero weights (a
+                    // non-finite x there would otherwise turn 0 * x into NaN)
+                    xb[s][t].x = kv ? xb[s][t].x : 0u;
+                    xb[s][t].y = kv ? xb[s][t].y : 0u;
+                    xb[s][t].z = kv ? xb[s][t].z : 0u;
+                    xb[s][t].w = kv ? xb[s][t].w : 0u;
+                }
+            }
+        }
+        // (4) stage the chunk in the wave's LDS area (in program order with
+        // this wave's operand reads of the previous chunk)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u*>(wl + 1024 * i + 16 * lane) = raw[i];
+        // (5) the MFMAs
+#pragma unroll
+        for (int s = 0; s < kSegs; ++s) {
+            const bool kv = kWhole || code0 + 128 * s + 32 * q < K;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int r = 16 * t + r16;
+                const int g = (r >> 1) & 7;
+                const uint8_t* rp = wl + 1024 * (r >> 3) + 128 * (r & 7);
+                // decode four codes pairs at a time into the A operand of MFMA u
+                // and issue it right away, so one operand is live at a time
+                auto mfma = [&](int u, uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3)
+                                __attribute__((always_inline)) {
+                    if constexpr (!kWhole) {
+                        a0 = kv ? a0 : 0u;
+                        a1 = kv ? a1 : 0u;
+                        a2 = kv ? a2 : 0u;
+                        a3 = kv ? a3 : 0u;
+                    }
+                    acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(V8, v4u{a0, a1, a2, a3}),
+                        __builtin_bit_cast(V8, xb[s][u]), acc[t], 0, 0, 0);
+                };
+                if constexpr (FMT == FMT_MXFP8) {
+                    // the lane's 32 codes are pieces 2 q, 2 q + 1 of the row
+                    const v4u lo = *reinterpret_cast<const v4u*>(rp + 16 * ((2 * q) ^ g));
+                    const v4u hi = *reinterpret_cast<const v4u*>(rp + 16 * ((2 * q + 1) ^ g));
+                    const uint32_t d[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                    const float sc = __uint_as_float(((sw[t][0] >> (8 * q)) & 0xFFu) << 23);
+                    static_for<0, 4>([&](auto u_c) {
+                        constexpr int u = decltype(u_c)::value;
+                        mfma(u,
+                             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * u], sc, false)),
+                             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * u], sc, true)),
+                             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * u + 1], sc, false)),
+                             __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d[2 * u + 1], sc, true)));
+                    });
+                } else {
+                    const v4u dv = *reinterpret_cast<const v4u*>(rp + 16 * ((4 * s + q) ^ g));
+                    const uint32_t d[4] = {dv.x, dv.y, dv.z, dv.w};
+                    if constexpr (FMT == FMT_MXFP4) {
+                        const float sc = __uint_as_float(((sw[t][s] >> (8 * q)) & 0xFFu) << 23);
+                        static_for<0, 4>([&](auto u_c) {
+                            constexpr int u = decltype(u_c)::value;
+                            mfma(u,
+                                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[u], sc, 0)),
+                                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[u], sc, 1)),
+                                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[u], sc, 2)),
+                                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d[u], sc, 3)));
+                        });
+                    } else {
+                        // E2M1 times its E4M3 block scale, exact in fp32 and
+                        // in bf16 (at most 6 significant bits); codes 16 q ..
+                        // of the segment use scale byte 2 q, the next 16 2 q + 1
+                        const uint32_t sbytes = (sw[t][2 * s + (q >> 1)] >> (16 * (q & 1))) & 0xFFFFu;
+                        const f32x2 scv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(sbytes, 1.0f, false);
+                        static_for<0, 4>([&](auto u_c) {
+                            constexpr int u = decltype(u_c)::value;
+                            const float scs = u < 2 ? scv.x : scv.y;
+                            uint32_t o[4];
+                            static_for<0, 4>([&](auto e_c) {
+                                constexpr int e = decltype(e_c)::value;
+                                const f32x2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(d[u], 1.0f, e);
+                                const f32x2 pr = {v.x * scs, v.y * scs};
+                                o[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
+                            });
+                            mfma(u, o[0], o[1], o[2], o[3]);
+                        });
+                    }
+                }
+            }
+        }
     }
-    static_for<0, kMfmaDepth>([&](auto d_c) {
-        constexpr int d = decltype(d_c)::value;
-        if (i + d < cnt) step(i + d, ring[d]);
-    });
 
-    // the waves' tiles to LDS (element (m, n): weight row m, activation row n)
-    float* mine = red + wave * 32 * 32;
+    // the waves' partial tiles meet in LDS (the weight areas, once every wave
+    // is done with them): element (row m, column b) of wave w at
+    // red[(w * 32 + m) * 8 + b]; lane (r16, q) holds rows 4 q .. 4 q + 3 of each tile
+    float* red = reinterpret_cast<float*>(smem);
+    __syncthreads();
+    if (has) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) mine[(8 * (e >> 2) + 4 * hf + (e & 3)) * 32 + ln] = acc[e];
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[(wave * kMfRows + 16 * t + 4 * q + e) * 8 + r16] = acc[t][e];
+    }
     __syncthreads();
     const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
-    for (int idx = tid; idx < 32 * B; idx += kThreads) {
+    for (int idx = tid; idx < kMfRows * B; idx += (int)blockDim.x) {
         const int m = idx / B, b = idx - (idx / B) * B;
-        if (n0 + m >= N) continue;
-        float t = red[m * 32 + b];
-#pragma unroll
-        for (int w = 1; w < kWaves; ++w) t += red[w * 32 * 32 + m * 32 + b];
-        if constexpr (FMT == FMT_NVFP4) t = t * gmul;
-        static_cast<S*>(p.y)[(int64_t)b * N + n0 + m] = Store<DT>::from_f32(t);
+        if (row0 + m >= N) continue;
+        float v = red[m * 8 + b];
+        for (int w = 1; w < nw; ++w) v += red[(w * kMfRows + m) * 8 + b];
+        if constexpr (FMT == FMT_NVFP4) v = v * gmul;
+        static_cast<S*>(p.y)[(int64_t)b * N + row0 + m] = Store<DT>::from_f32(v);
     }
 }
 
-// The matrix-core QMV replaces the VALU tile at B = 8 (bf16 activations,
-// MXFP4 / NVFP4 / MXFP8), where the VALU tile does eight dot products per
-// decoded pair: K=4096 N=14336 27.6 -> 16.7 us, N=4096 12.2 -> 10.9 us,
-// K=1088 N=300 16.6 -> 4.6 us. At B = 3..7 it also wins on some shapes (B=5
-// N=14336: 16.5 -> 14.7 us; launches of under 256 VALU waves) but loses on
-// others (N=4096: B=4 6.2 vs 9.1 us); it stays at B = 8 so that a row of a
-// batch of up to seven equals the same row computed alone, bit for bit (the
-// two paths sum in different orders).
-constexpr size_t kMfmaMaxLds = 144 * 1024;
+// The matrix-core QMV takes bf16 activations from the batch size where it
+// beats the VALU tile, measured at K=4096, N=14336 (VALU tile -> matrix
+// cores; B=8 against the earlier 32x32 matrix-core kernel):
+//   MXFP4  B=3 10.6 -> 10.3, B=4 12.4 -> 10.7, B=5 15.3 -> 10.9, B=8 17.9 -> 12.6 us
+//   NVFP4  B=3 10.9 -> 11.2, B=4 12.7 -> 11.5, B=6 17.5 -> 11.8, B=8 18.6 -> 12.6 us
+//   MXFP8  B=4 15.3 -> 17.2, B=5 18.4 -> 17.9, B=7 24.1 -> 19.5, B=8 23.2 -> 20.2 us
+// (MXFP8's 128-code chunks give each wave two chunks in turn at K=4096). At
+// B <= 2 the VALU tile is faster for every format (MXFP4 B=1 7.5 against
+// 9.9 us).
+template <int FMT> constexpr int mf_min_batch() {
+    return FMT == FMT_MXFP4 ? 3 : (FMT == FMT_NVFP4 ? 4 : 5);
+}
+template <int FMT>
 inline bool use_mfma_qmv(const LaunchParams& p) {
-    return p.B == 8 && p.K > 0 && mfma_lds_bytes(p) <= kMfmaMaxLds;
+    return p.B >= mf_min_batch<FMT>() && p.B <= 8 && p.K > 0;
 }
 
 template <int DT, int FMT>
 int launch_qmv_mfma(const LaunchParams& p, hipStream_t st) {
-    const size_t lds = mfma_lds_bytes(p);
-    auto* kern = &qmv_mfma_kernel<DT, FMT>;
-    static LdsGrant granted;
-    if (const int e = allow_lds(kern, lds, granted)) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)((p.N + kMfmaRows - 1) / kMfmaRows)), dim3(kThreads),
-                       lds, st, p);
+    constexpr int kScB = mf_chunk_codes<FMT>() / (FMT == FMT_NVFP4 ? 16 : 32);
+    const bool whole = p.K % mf_chunk_codes<FMT>() == 0 && p.sc_per_row % kScB == 0 &&
+                       (reinterpret_cast<uintptr_t>(p.scales) % kScB) == 0;
+    const int nw = mfma_waves(p, whole ? mf_max_waves<FMT, true>() : mf_max_waves<FMT, false>());
+    // W waves stage 4 KB each; the reduction reuses that area (W * 32 rows *
+    // 8 columns * 4 bytes = W KB)
+    const size_t lds = (size_t)nw * kMfRows * kMfChunkBytes;
+    auto* kern = whole ? &qmv_mfma_kernel<DT, FMT, true> : &qmv_mfma_kernel<DT, FMT, false>;
+    static LdsGrant granted_w, granted_p;
+    if (const int e = allow_lds(kern, lds, whole ? granted_w : granted_p)) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((p.N + kMfRows - 1) / kMfRows)), dim3(64 * nw), lds,
+                       st, p);
     return (int)hipGetLastError();
 }
 
@@ -1693,7 +1751,7 @@ template <int DT, int FMT, int BITS>
 int launch_qmv_t(const LaunchParams& p, hipStream_t st) {
     if constexpr (DT == DT_BF16 &&
                   (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
-        if (use_mfma_qmv(p)) return launch_qmv_mfma<DT, FMT>(p, st);
+        if (use_mfma_qmv<FMT>(p)) return launch_qmv_mfma<DT, FMT>(p, st);
     }
     const int nb = (int)p.B;
     switch (nb) {

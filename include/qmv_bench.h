@@ -8,6 +8,17 @@
  *                           issued before any is used, and folds them into
  *                           one word per block: the measured ceiling of a
  *                           read-only stream of that size.
+ *   qmv_bench_read_design   reads `bytes` once with one of 17 read designs,
+ *                           to find the fastest single launch for a size:
+ *                           0-5 one-shot grids (threads x loads per lane:
+ *                           256x2, 256x4, 256x8, 512x4, 1024x2, 64x8), 6 the
+ *                           256x4 grid in XCD-contiguous block order, 7-8
+ *                           32 / 64 contiguous bytes per lane, 9-14
+ *                           persistent grid-stride (256 threads; 4 loads per
+ *                           iteration on 256/512/1024/2048 blocks, 8 loads on
+ *                           256/512), 15-16 [rows][2048] row patterns (eight
+ *                           lanes per 128-byte line; the 16x16 MFMA operand
+ *                           layout; bytes a multiple of 32 KB).
  *   qmv_bench_copy          copies `bytes` (a plain copy of known size, for
  *                           calibrating hardware byte counters).
  *
@@ -26,6 +37,8 @@ extern "C" {
 
 int qmv_bench_stream_read(void* stream, const void* buf, int64_t bytes, uint32_t* sink,
                           int unroll);
+int qmv_bench_read_design(void* stream, const void* buf, int64_t bytes, uint32_t* sink,
+                          int design);
 int qmv_bench_copy(void* stream, const void* src, void* dst, int64_t bytes);
 
 #ifdef __cplusplus

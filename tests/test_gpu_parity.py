@@ -298,17 +298,23 @@ def test_affine_sweep_sampled(bmv, bits, group, B, dtype):
     check(y[:, rows], y64, A, dtype, f"affine b{bits} g{group} B{B} {dtype} K=N=4096")
 
 
+# the matrix cores take bf16 batches from B = 3 (MXFP4), 4 (NVFP4), 5 (MXFP8)
+MC_FIRST = {"mxfp4": 3, "nvfp4": 4, "mxfp8": 5}
+
+
 def test_batch_rows_equal_single_row_calls_bitwise(bmv):
-    # on the VALU tile (affine at any B; the block-scaled formats up to B = 7:
-    # B = 8 with bf16 runs on the matrix cores, tested below)
+    # on the VALU tile: affine codes at any B, and the block-scaled formats
+    # with f16 activations at any B or bf16 activations below the batch size
+    # where the matrix cores take over (MC_FIRST; tested below)
     import torch
-    for fmt in ("affine", "mxfp4", "nvfp4", "mxfp8"):
-        if fmt == "affine":
-            c = workloads.affine_sweep_case(3, 64, 8, "bf16", N=256)
-        else:
-            c = workloads.mlp_up_case(fmt, 7, N=256)
+    cases = [("affine", workloads.affine_sweep_case(3, 64, 8, "bf16", N=256))]
+    for fmt in ("mxfp4", "nvfp4", "mxfp8"):
+        cases.append((fmt, getattr(workloads, f"{fmt}_case")(73, f"batch-{fmt}-f16", K=4096,
+                                                            N=256, B=7, dtype="f16")))
+        cases.append((fmt, workloads.mlp_up_case(fmt, MC_FIRST[fmt] - 1, N=256)))
+    for fmt, c in cases:
         d = case_to_dev(c)
-        say(f"batch invariance {fmt}")
+        say(f"batch invariance {fmt} {c.dtype} B={c.B}")
         yb = run_qmv(bmv, c, d)
         for b in range(c.B):
             db = dict(d, x=d["x"][b:b + 1].contiguous())
@@ -317,52 +323,64 @@ def test_batch_rows_equal_single_row_calls_bitwise(bmv):
 
 
 # ---------------------------------------------------------------------------
-# B = 8 with bf16 activations and block-scaled weights: the matrix-core QMV
+# B = 3..8 with bf16 activations and block-scaled weights: the matrix-core QMV
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
-def test_b8_matrix_core_ragged(bmv, fmt):
-    # K % 64 == 32 (a half segment at the end of every row), N not a multiple
-    # of the 32-row block, K short enough that some waves get no segment
-    # (K = 8192: 128 KB of staged x, the largest that takes this path)
-    for K, N in ((1056, 301), (96, 70), (4096, 33), (8192, 40)):
-        c = workloads.mlp_up_case(fmt, 8, K=K, N=N)
-        say(f"b8 matrix cores {fmt} K={K} N={N}")
+@pytest.mark.parametrize("B", ["first", 6, 8])
+def test_matrix_core_ragged(bmv, fmt, B):
+    B = MC_FIRST[fmt] if B == "first" else B
+    # K not a multiple of the 256 (FP4) / 128 (FP8) codes of a chunk (a
+    # partial chunk at the end of every row), K below one chunk, N not a
+    # multiple of the 32-row block, K long enough for several chunks per wave
+    for K, N in ((1056, 301), (96, 70), (160, 33), (4096, 33), (8192, 40), (2560, 65)):
+        c = workloads.mlp_up_case(fmt, B, K=K, N=N)
+        say(f"matrix cores {fmt} B={B} K={K} N={N}")
         y = to_host(run_qmv(bmv, c), c.dtype)
         y64, A = oracle_rows(c, np.arange(N))
-        check(y, y64, A, c.dtype, f"b8 {fmt} K={K} N={N}")
+        check(y, y64, A, c.dtype, f"matrix cores {fmt} B={B} K={K} N={N}")
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
-def test_b8_matrix_core_full_size_sampled(bmv, fmt):
-    c = workloads.mlp_up_case(fmt, 8)
-    say(f"b8 matrix cores {fmt} K4096 N14336")
+@pytest.mark.parametrize("B", [4, 8])
+def test_matrix_core_full_size_sampled(bmv, fmt, B):
+    c = workloads.mlp_up_case(fmt, B)
+    say(f"matrix cores {fmt} B={B} K4096 N14336")
     y = to_host(run_qmv(bmv, c), c.dtype)
     rows = sample_rows(c.N, 128, seed=8)
     y64, A = oracle_rows(c, rows)
-    check(y[:, rows], y64, A, c.dtype, f"b8 {fmt} K4096 N14336")
+    check(y[:, rows], y64, A, c.dtype, f"matrix cores {fmt} B={B} K4096 N14336")
 
 
-def test_b8_matrix_core_bitwise_properties(bmv):
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
+def test_matrix_core_bitwise_properties(bmv, fmt):
     # same bits on every call; each activation row's result independent of
-    # the other rows (a permuted batch gives the permuted rows); rows < n of a
-    # call on the first n weight rows equal those of the full call
+    # the other rows (a permuted batch gives the permuted rows, and a row gives
+    # the same bits in a batch of 3 as in a batch of 8); rows < n of a call on
+    # the first n weight rows equal those of the full call
     import torch
-    c = workloads.mlp_up_case("mxfp4", 8, K=2048, N=200)
-    d = case_to_dev(c)
-    say("b8 matrix cores: repeat, permutation, tail")
-    y1 = run_qmv(bmv, c, d)
-    y2 = run_qmv(bmv, c, d)
-    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
-    perm = torch.tensor([5, 2, 7, 0, 1, 6, 3, 4], device=d["x"].device)
-    yp = run_qmv(bmv, c, dict(d, x=d["x"][perm].contiguous()))
-    assert torch.equal(yp.view(torch.int16), y1[perm].view(torch.int16))
-    for n in (1, 31, 33, 100):
-        sub = dict(d, w=d["w"][:n].contiguous(), scales=d["scales"][:n].contiguous())
-        c_sub = workloads.QmvCase(c.fmt, c.dtype, c.B, c.K, n, c.w[:n], c.scales[:n], c.x,
-                                  global_scale=c.global_scale)
-        part = run_qmv(bmv, c_sub, sub)
-        assert torch.equal(part.view(torch.int16), y1[:, :n].view(torch.int16)), n
+    for K in (2048, 1056):
+        c = workloads.mlp_up_case(fmt, 8, K=K, N=200)
+        d = case_to_dev(c)
+        say(f"matrix cores {fmt} K={K}: repeat, permutation, batch size, tail")
+        y1 = run_qmv(bmv, c, d)
+        y2 = run_qmv(bmv, c, d)
+        assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+        perm = torch.tensor([5, 2, 7, 0, 1, 6, 3, 4], device=d["x"].device)
+        yp = run_qmv(bmv, c, dict(d, x=d["x"][perm].contiguous()))
+        assert torch.equal(yp.view(torch.int16), y1[perm].view(torch.int16))
+        for sel in ([6, 1, 3, 0, 2], [2, 4, 7, 0, 5, 1]):
+            idx = torch.tensor(sel, device=d["x"].device)
+            c_sub = workloads.QmvCase(c.fmt, c.dtype, len(sel), c.K, c.N, c.w, c.scales, c.x,
+                                      global_scale=c.global_scale)
+            ys = run_qmv(bmv, c_sub, dict(d, x=d["x"][idx].contiguous()))
+            assert torch.equal(ys.view(torch.int16), y1[idx].view(torch.int16)), sel
+        for n in (1, 31, 33, 100):
+            sub = dict(d, w=d["w"][:n].contiguous(), scales=d["scales"][:n].contiguous())
+            c_sub = workloads.QmvCase(c.fmt, c.dtype, c.B, c.K, n, c.w[:n], c.scales[:n], c.x,
+                                      global_scale=c.global_scale)
+            part = run_qmv(bmv, c_sub, sub)
+            assert torch.equal(part.view(torch.int16), y1[:, :n].view(torch.int16)), n
 
 
 def _extreme_scale_case(fmt, B, dtype="bf16"):

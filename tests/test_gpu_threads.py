@@ -1,11 +1,14 @@
 """Launches from several host threads at once.
 
 Kernels that stage more than 64 KB of dynamic LDS raise their limit on first
-use, per device, under a lock. Here the matrix-core QMV (B = 8, bf16) runs
-with four row lengths (96 to 144 KB of LDS) and two formats. All the calls are
-released together from one thread each. Every call must succeed, and each
-result must equal, bit for bit, the same call made alone afterwards. A few
-sampled rows are also checked against the oracle.
+use, per device, under a lock. Here the VALU QMV tile with eight f32
+activation rows (one lane group's slab of x alone fills 64 KB, so each
+launch asks for 64 KB plus the tile's scales: 65 KB for MXFP8, 66 KB for
+NVFP4) runs with four row lengths and two formats, so four threads race to
+raise each kernel's limit. All the calls are released together from one
+thread each. Every
+call must succeed, and each result must equal, bit for bit, the same call
+made alone afterwards. A few sampled rows are also checked against the oracle.
 
 The body runs in a fresh child process, so these launches are the first of
 their kernel instances in that process and the locked raise of the LDS limit
@@ -33,10 +36,11 @@ def _concurrent_launches_with_large_lds(bmv):
     cases = []
     for fmt in ("mxfp8", "nvfp4"):
         for K in (5120, 6144, 7168, 8192):
-            c = workloads.mlp_up_case(fmt, 8, K=K, N=96)
+            make = workloads.mxfp8_case if fmt == "mxfp8" else workloads.nvfp4_case
+            c = make(74, f"threads-{fmt}-{K}", K=K, N=96, B=8, dtype="f32")
             cases.append((c, case_to_dev(c)))
     torch.cuda.synchronize()
-    say(f"{len(cases)} threads: b8 matrix cores, K 5120..8192, mxfp8 and nvfp4")
+    say(f"{len(cases)} threads: f32 B=8 VALU tile, K 5120..8192, mxfp8 and nvfp4")
 
     outs = [None] * len(cases)
     errors = []
@@ -62,7 +66,7 @@ def _concurrent_launches_with_large_lds(bmv):
     for i, (c, d) in enumerate(cases):
         alone = run_qmv(bmv, c, d)
         torch.cuda.synchronize()
-        assert torch.equal(outs[i].view(torch.int16), alone.view(torch.int16)), \
+        assert torch.equal(outs[i].view(torch.int32), alone.view(torch.int32)), \
             f"{c.fmt} K={c.K}: the concurrent result differs from the call alone"
         rows = sample_rows(c.N, 8, seed=i)
         y = to_host(outs[i], c.dtype)
@@ -75,7 +79,7 @@ def test_concurrent_launches_with_large_lds():
     env = dict(os.environ)
     env["PYTHONPATH"] = os.pathsep.join([os.path.dirname(here), here,
                                          env.get("PYTHONPATH", "")])
-    say("child process: first launches of the large-LDS matrix-core QMV from 8 threads")
+    say("child process: first launches of the large-LDS QMV tile from 8 threads")
     r = subprocess.run([sys.executable, os.path.abspath(__file__)], env=env,
                        stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True, timeout=300)
     print(r.stdout)
