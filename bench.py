@@ -729,9 +729,10 @@ def committed_traffic():
     return round(vals["t"])
 
 
-def pmc_workload(bmv, n: int) -> None:
+def pmc_workload(bmv, n: int, batch: int = 1) -> None:
     """Launch sequence for hardware-counter runs: n copies of 64 MiB (the
-    calibration kernel of known size), then n headline QMV launches."""
+    calibration kernel of known size), then n launches of the MXFP4 QMV at
+    K=4096, N=14336, bf16, with `batch` activation rows (1: the headline)."""
     import torch
     import workloads
     lib = bmv.load()
@@ -745,11 +746,11 @@ def pmc_workload(bmv, n: int) -> None:
         assert st == 0
     torch.cuda.synchronize()
     del src, dst
-    r = Runner(bmv, workloads.mlp_up_case("mxfp4", 1))
+    r = Runner(bmv, workloads.mlp_up_case("mxfp4", batch))
     for i in range(n):
         r.call(i, sp)
     torch.cuda.synchronize()
-    print(f"[pmc] {n} copies of {nbytes} bytes, then {n} headline launches of {r.bytes} "
+    print(f"[pmc] {n} copies of {nbytes} bytes, then {n} MXFP4 B={batch} launches of {r.bytes} "
           f"algorithmic bytes; kernel fingerprint {kernel_fingerprint()}", flush=True)
 
 
@@ -797,9 +798,11 @@ def summarize_trace_table(trace_csv: str) -> str:
     return "\n".join(out)
 
 
-def summarize_counters(fetch_csv: str, write_csv: str, copy_bytes: int, alg_bytes: int) -> str:
+def summarize_counters(fetch_csv: str, write_csv: str, copy_bytes: int, alg_bytes: int,
+                       kernel: str = "qmv_kernel") -> str:
     """Markdown summary of FETCH_SIZE / WRITE_SIZE per dispatch for the copy
-    kernel (calibration, `copy_bytes` read and written) and the QMV kernel."""
+    kernel (calibration, `copy_bytes` read and written) and the QMV kernel
+    whose name contains `kernel`."""
     import csv
 
     def med(path, counter, sub):
@@ -808,9 +811,9 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_bytes: int, alg_byte
         return float(np.median(v)), len(v)
 
     fc, nfc = med(fetch_csv, "FETCH_SIZE", "copy_kernel")
-    fq, nfq = med(fetch_csv, "FETCH_SIZE", "qmv_kernel")
+    fq, nfq = med(fetch_csv, "FETCH_SIZE", kernel)
     wc, nwc = med(write_csv, "WRITE_SIZE", "copy_kernel")
-    wq, nwq = med(write_csv, "WRITE_SIZE", "qmv_kernel")
+    wq, nwq = med(write_csv, "WRITE_SIZE", kernel)
     kib = copy_bytes / 1024
     ff, wf = kib / fc, kib / wc
     t = (fq * ff + wq * wf) * 1024
@@ -818,13 +821,37 @@ def summarize_counters(fetch_csv: str, write_csv: str, copy_bytes: int, alg_byte
         f"copy kernel ({copy_bytes} bytes read, {copy_bytes} written): FETCH_SIZE {fc:.1f} KiB "
         f"(n={nfc}), WRITE_SIZE {wc:.1f} KiB (n={nwc}) -> scale factors fetch {ff:.4f}, "
         f"write {wf:.4f}",
-        f"qmv kernel: FETCH_SIZE {fq:.1f} KiB (n={nfq}), WRITE_SIZE {wq:.1f} KiB (n={nwq}) per "
+        f"{kernel}: FETCH_SIZE {fq:.1f} KiB (n={nfq}), WRITE_SIZE {wq:.1f} KiB (n={nwq}) per "
         f"dispatch (medians)",
         f"traffic_bytes_per_launch: {t:.0f}",
         f"algorithmic_bytes_per_launch: {alg_bytes}",
         f"traffic / algorithmic: {t / alg_bytes:.4f}",
         f"kernel_fingerprint: {kernel_fingerprint()}",
     ])
+
+
+def summarize_pmc_table(counter_csv: str) -> str:
+    """Markdown table of a rocprofv3 counter collection: for every kernel (by
+    name and grid), the median per dispatch of each counter collected."""
+    import csv
+    import re
+    groups = {}
+    names = []
+    for r in csv.DictReader(open(counter_csv)):
+        key = (r["Kernel_Name"], r.get("Grid_Size", r.get("Grid_Size_X", "")))
+        c = r["Counter_Name"]
+        if c not in names:
+            names.append(c)
+        groups.setdefault(key, {}).setdefault(c, []).append(float(r["Counter_Value"]))
+    out = ["| kernel | grid | dispatches | " + " | ".join(names) + " |",
+           "|---|---|---|" + "---|" * len(names)]
+    for (name, grid), by in sorted(groups.items(), key=lambda kv: kv[0]):
+        short = re.sub(r"\(qmv::.*", "", name).replace("qmv::(anonymous namespace)::", "")
+        short = short.replace("void ", "")
+        n = max(len(v) for v in by.values())
+        vals = [f"{np.median(by[c]):.0f}" if c in by else "-" for c in names]
+        out.append(f"| `{short[:60]}` | {grid} | {n} | " + " | ".join(vals) + " |")
+    return "\n".join(out)
 
 
 def check_once(bmv, case) -> None:
@@ -916,6 +943,11 @@ def main() -> int:
                          "headline QMV, and exit")
     ap.add_argument("--pmc-workload", type=int, default=0, metavar="N",
                     help="only run the counter workload (N copies, N headline launches)")
+    ap.add_argument("--pmc-batch", type=int, default=1, metavar="B",
+                    help="activation rows of the counter workload's QMV (default 1)")
+    ap.add_argument("--summarize-pmc-table", metavar="COUNTER_CSV",
+                    help="print per-kernel medians of every counter in a rocprofv3 counter "
+                         "collection and exit (no GPU)")
     ap.add_argument("--summarize-trace-table", metavar="TRACE_CSV",
                     help="print a per-kernel duration table of a rocprofv3 kernel trace")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_CSV", "KERNEL"),
@@ -929,11 +961,15 @@ def main() -> int:
     if args.summarize_trace_table:
         print(summarize_trace_table(args.summarize_trace_table))
         return 0
+    if args.summarize_pmc_table:
+        print(summarize_pmc_table(args.summarize_pmc_table))
+        return 0
     if args.summarize_counters:
-        import workloads
-        K, N, B = 4096, 14336, 1
+        K, N, B = 4096, 14336, args.pmc_batch
         alg = N * K // 2 + N * K // 32 + B * K * 2 + B * N * 2   # codes + E8M0 + x + y
-        print(summarize_counters(*args.summarize_counters, copy_bytes=64 << 20, alg_bytes=alg))
+        kernel = "qmv_mfma_kernel" if B >= 3 else "qmv_kernel"
+        print(summarize_counters(*args.summarize_counters, copy_bytes=64 << 20, alg_bytes=alg,
+                                 kernel=kernel))
         return 0
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the QMV path here has "
@@ -958,7 +994,7 @@ def main() -> int:
         print(json.dumps({"read_designs": designs, "qmv_headline": q}), flush=True)
         return 0
     if args.pmc_workload:
-        pmc_workload(bmv, args.pmc_workload)
+        pmc_workload(bmv, args.pmc_workload, args.pmc_batch)
         return 0
     head = workloads.mlp_up_case("mxfp4", 1)
     check_once(bmv, head)

@@ -564,6 +564,103 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(LaunchParams p, Geom g) {
                                                 p.scales, p.biases, xr, yrow, gmul, lds);
 }
 
+// ---------------------------------------------------------------------------
+// One activation row of 16-bit values against MXFP4 / NVFP4 / MXFP8 weights
+// with K = 2048 * NU: the tile above cut to what this case needs. Each wave
+// takes two rows (its row index is wave-uniform, so row addresses live in
+// scalar registers); lane l takes units l, l + 64, ... of both rows, exactly
+// the units and the order of the tile with 64 lanes per row, and folds them
+// with the tile's unit_fma against x staged in LDS in the tile's layout. The
+// scale bytes of a lane's units are loaded by the lane itself (64 lanes read
+// 64 consecutive scale elements of a row) instead of being staged, and no
+// clamped or predicated index is formed per lane. A
+// row's result is therefore the tile's bit for bit; the saving is the
+// staging and addressing work (VALU), which at one activation row is most of
+// what the tile does besides the decode and the dot products.
+// ---------------------------------------------------------------------------
+template <int FMT> constexpr int row_units_max() { return 2; }
+
+template <int DT, int FMT, int BITS, int NU>
+__global__ __launch_bounds__(kThreads) void qmv_row_kernel(LaunchParams p) {
+    using F = Fmt<FMT, BITS>;
+    using S = typename Store<DT>::S;
+    constexpr int R = 2;                      // rows per wave
+    constexpr int W = F::kWords;
+    constexpr int kUnitBytes = 4 * W;
+    constexpr int KR = 2048 * NU;             // elements per row
+    constexpr int US = KR / 32;               // units per row
+    constexpr int kEB = F::template elem_bytes<DT>();
+    __shared__ __align__(16) S xs[KR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t N = p.N;
+    const int64_t row0 = (int64_t)blockIdx.x * (kWaves * R) + wave * R;
+    const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
+
+    // (1) this thread's NU 16-byte chunks of x, ahead of the weights
+    const S* x = static_cast<const S*>(p.x);
+    v4u xc[NU];
+#pragma unroll
+    for (int j = 0; j < NU; ++j) xc[j] = *reinterpret_cast<const v4u*>(x + (tid + j * kThreads) * 8);
+
+    // (2) the lane's units of both rows and their scale elements (rows past
+    // the end re-read row N - 1; their results are not stored)
+    UnitRaw<FMT, BITS, R> u_raw[NU];
+    typename F::Raw s_raw[NU][R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int64_t r = row0 + i < N ? row0 + i : N - 1;
+        const uint8_t* wrow = p.w + r * p.row_bytes;
+        const uint8_t* srow = static_cast<const uint8_t*>(p.scales) + r * p.sc_per_row * kEB;
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+            load_words<W, true>(wrow + (lane + 64 * j) * kUnitBytes, u_raw[j].d[i]);
+            // the unit's scale elements (one E8M0 byte, or NVFP4's two E4M3
+            // bytes), read once: nontemporal like the weights
+            if constexpr (FMT == FMT_NVFP4)
+                s_raw[j][i].e = __builtin_nontemporal_load(
+                    reinterpret_cast<const uint16_t*>(srow) + (lane + 64 * j));
+            else
+                s_raw[j][i].e = __builtin_nontemporal_load(srow + (lane + 64 * j));
+        }
+    }
+
+    // (3) x to LDS, chunk v at the tile's slot
+#pragma unroll
+    for (int j = 0; j < NU; ++j) {
+        const int v = tid + j * kThreads;
+        *reinterpret_cast<v4u*>(xs + x_lds_slot(v * 8, US)) = xc[j];
+    }
+    __syncthreads();
+
+    // (4) the units in the tile's order, (5) the tile's reduction and store
+    float total[R][1];
+#pragma unroll
+    for (int i = 0; i < R; ++i) total[i][0] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NU; ++j) {
+        typename F::Scale scl[R];
+#pragma unroll
+        for (int i = 0; i < R; ++i) scl[i] = F::template decode<DT>(s_raw[j][i]);
+        unit_fma<DT, FMT, BITS, 1, R>(u_raw[j], scl, xs, lane + 64 * j, KR, US, total);
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) total[i][0] = group_sum(total[i][0], 64);
+    if (lane == 63) {
+        S* y = static_cast<S*>(p.y);
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            if (row0 + i < N) {
+                float v = total[i][0];
+                if constexpr (FMT == FMT_NVFP4) v = v * gmul;
+                y[row0 + i] = Store<DT>::from_f32(v);
+            }
+        }
+    }
+}
+
 // Fused RMSNorm + QMV: y[b] = r[b] * (W . RN_T(x[b] * gamma)), the QMV tile
 // with the XNorm accessor (x times gamma staged, the squares summed on the
 // way, r applied to each row's result).
@@ -1478,6 +1575,12 @@ template <> struct Mfma16<DT_BF16> {
 };
 typedef float mf_f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
 
+// Raw (unswizzled) buffer resources: the fourth descriptor word of gfx9
+// targets (32-bit data format), and an offset past every buffer this file
+// builds one for (such buffers hold fewer bytes; loads there return zeros).
+constexpr int kBufferWord3 = 0x00020000;
+constexpr int kBufferOutOfRange = 0x7FFFFF00;
+
 constexpr int kMfRows = 32;          // weight rows per block
 constexpr int kMfChunkBytes = 128;   // weight bytes per row and chunk
 constexpr int kMfMaxWaves = 16;
@@ -1537,10 +1640,13 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
         const int64_t r = row0 + 16 * t + r16;
         orow[t] = r < N ? r : N - 1;
     }
-    // columns past B repeat activation row B - 1: their results are never
-    // stored, so every lane loads a valid row and no load is predicated
+    // x through a buffer resource over its B rows: a load at an offset past
+    // the buffer returns zeros and makes no memory request, so the columns
+    // past B (never stored) and pieces past K cost nothing and read as zeros
+    const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<S*>(x), 0, (int)(B * K * (int64_t)sizeof(S)), kBufferWord3);
     const bool has = r16 < B;
-    const S* xrow = x + (int64_t)(has ? r16 : B - 1) * K;
+    const int xoff = (int)(r16 * K * (int64_t)sizeof(S));
 
     mf_f32x4_t acc[2];
 #pragma unroll
@@ -1593,24 +1699,17 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
         }
         // (3) x: the B operand of MFMA t of segment s in lane (column r16, q)
         // holds x[r16][code0 + 128 s + 32 q + 8 t .. + 8]
+        // (pieces past K enter as zeros, with their zeroed weights)
         v4u xb[kSegs][4];
 #pragma unroll
         for (int s = 0; s < kSegs; ++s) {
             const int64_t k = code0 + 128 * s + 32 * q;
-            const bool kv = kWhole || k < K;
-            const int64_t kl = kv ? k : K - 32;          // a valid address; zeroed below
+            const bool ok = has && (kWhole || k < K);
+            const int off = ok ? xoff + (int)(k * (int64_t)sizeof(S)) : kBufferOutOfRange;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                xb[s][t] = *reinterpret_cast<const v4u*>(xrow + kl + 8 * t);
-                if constexpr (!kWhole) {
-                    // x past K enters as zero with its zero weights (a
-                    // non-finite x there would otherwise turn 0 * x into NaN)
-                    xb[s][t].x = kv ? xb[s][t].x : 0u;
-                    xb[s][t].y = kv ? xb[s][t].y : 0u;
-                    xb[s][t].z = kv ? xb[s][t].z : 0u;
-                    xb[s][t].w = kv ? xb[s][t].w : 0u;
-                }
-            }
+            for (int t = 0; t < 4; ++t)
+                xb[s][t] = __builtin_bit_cast(
+                    v4u, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16 * t, 0, 0));
         }
         // (4) stage the chunk in the wave's LDS area (in program order with
         // this wave's operand reads of the previous chunk)
@@ -1727,7 +1826,9 @@ template <int FMT> constexpr int mf_min_batch() {
 }
 template <int FMT>
 inline bool use_mfma_qmv(const LaunchParams& p) {
-    return p.B >= mf_min_batch<FMT>() && p.B <= 8 && p.K > 0;
+    // (x must fit a buffer resource below kBufferOutOfRange bytes)
+    return p.B >= mf_min_batch<FMT>() && p.B <= 8 && p.K > 0 &&
+           p.B * p.K * 2 < (int64_t)kBufferOutOfRange;
 }
 
 template <int DT, int FMT>
@@ -1752,6 +1853,19 @@ int launch_qmv_t(const LaunchParams& p, hipStream_t st) {
     if constexpr (DT == DT_BF16 &&
                   (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
         if (use_mfma_qmv<FMT>(p)) return launch_qmv_mfma<DT, FMT>(p, st);
+    }
+    if constexpr (DT != DT_F32 && (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
+        if (p.B == 1 && p.N > 0 && p.K > 0 && p.K % 2048 == 0 &&
+            p.K / 2048 <= row_units_max<FMT>()) {
+            const dim3 grid((unsigned)((p.N + 2 * kWaves - 1) / (2 * kWaves)));
+            switch ((int)(p.K / 2048)) {
+                case 1: hipLaunchKernelGGL((qmv_row_kernel<DT, FMT, BITS, 1>), grid,
+                                           dim3(kThreads), 0, st, p); break;
+                default: hipLaunchKernelGGL((qmv_row_kernel<DT, FMT, BITS, 2>), grid,
+                                            dim3(kThreads), 0, st, p); break;
+            }
+            return (int)hipGetLastError();
+        }
     }
     const int nb = (int)p.B;
     switch (nb) {
