@@ -637,6 +637,7 @@ READ_DESIGNS = {
     10: "grid-stride, 512 x 4", 11: "grid-stride, 1024 x 4", 12: "grid-stride, 2048 x 4",
     13: "grid-stride, 256 x 8", 14: "grid-stride, 512 x 8",
     15: "rows: 8 lanes per 128-byte line", 16: "rows: 16x16 MFMA operand layout",
+    17: "rows: the one-row QMV's loads (weights + scales)",
 }
 
 
@@ -671,11 +672,12 @@ class ReadRunner:
 
 def read_designs(bmv, steps: int) -> list[dict]:
     """Every read design at the headline's byte counts: the 31,232,000
-    algorithmic bytes, and the 29,360,128 weight bytes for the row patterns
-    (which need whole 2048-byte rows); timed like the QMV (graph replays)."""
+    algorithmic bytes, the 29,360,128 weight bytes for the row patterns
+    (which need whole 2048-byte rows), and weights plus scales (31,195,136)
+    for the one-row QMV's pattern; timed like the QMV (graph replays)."""
     out = []
     for d, name in READ_DESIGNS.items():
-        nbytes = 14336 * 2048 if d >= 15 else 31232000
+        nbytes = 14336 * 2176 if d == 17 else 14336 * 2048 if d >= 15 else 31232000
         r = ReadRunner(bmv, nbytes, d)
         res = time_case(r, steps, 20)
         r.free()
@@ -729,10 +731,12 @@ def committed_traffic():
     return round(vals["t"])
 
 
-def pmc_workload(bmv, n: int, batch: int = 1) -> None:
+def pmc_workload(bmv, n: int, batch: int = 1, dtype: str = "bf16") -> None:
     """Launch sequence for hardware-counter runs: n copies of 64 MiB (the
     calibration kernel of known size), then n launches of the MXFP4 QMV at
-    K=4096, N=14336, bf16, with `batch` activation rows (1: the headline)."""
+    K=4096, N=14336 with `batch` activation rows of `dtype` (bf16, B=1: the
+    headline; f16 activations always take the VALU tile, for comparison with
+    the matrix-core kernel that bf16 takes from B=3)."""
     import torch
     import workloads
     lib = bmv.load()
@@ -746,11 +750,15 @@ def pmc_workload(bmv, n: int, batch: int = 1) -> None:
         assert st == 0
     torch.cuda.synchronize()
     del src, dst
-    r = Runner(bmv, workloads.mlp_up_case("mxfp4", batch))
+    case = (workloads.mlp_up_case("mxfp4", batch) if dtype == "bf16" else
+            workloads.mxfp4_case(3, f"c3-mxfp4-B{batch}-{dtype}", K=4096, N=14336, B=batch,
+                                 dtype=dtype))
+    r = Runner(bmv, case)
     for i in range(n):
         r.call(i, sp)
     torch.cuda.synchronize()
-    print(f"[pmc] {n} copies of {nbytes} bytes, then {n} MXFP4 B={batch} launches of {r.bytes} "
+    print(f"[pmc] {n} copies of {nbytes} bytes, then {n} MXFP4 B={batch} {dtype} launches of "
+          f"{r.bytes} "
           f"algorithmic bytes; kernel fingerprint {kernel_fingerprint()}", flush=True)
 
 
@@ -945,6 +953,8 @@ def main() -> int:
                     help="only run the counter workload (N copies, N headline launches)")
     ap.add_argument("--pmc-batch", type=int, default=1, metavar="B",
                     help="activation rows of the counter workload's QMV (default 1)")
+    ap.add_argument("--pmc-dtype", default="bf16", choices=("bf16", "f16"),
+                    help="activation type of the counter workload's QMV (default bf16)")
     ap.add_argument("--summarize-pmc-table", metavar="COUNTER_CSV",
                     help="print per-kernel medians of every counter in a rocprofv3 counter "
                          "collection and exit (no GPU)")
@@ -967,7 +977,11 @@ def main() -> int:
     if args.summarize_counters:
         K, N, B = 4096, 14336, args.pmc_batch
         alg = N * K // 2 + N * K // 32 + B * K * 2 + B * N * 2   # codes + E8M0 + x + y
-        kernel = "qmv_mfma_kernel" if B >= 3 else "qmv_kernel"
+        if args.pmc_dtype == "f16":
+            kernel = "qmv_row_kernel" if B == 1 else "qmv_kernel"
+        else:
+            kernel = ("qmv_mfma_kernel" if B >= 3 else "qmv_row_kernel" if B == 1 else
+                      "qmv_kernel")
         print(summarize_counters(*args.summarize_counters, copy_bytes=64 << 20, alg_bytes=alg,
                                  kernel=kernel))
         return 0
@@ -994,7 +1008,7 @@ def main() -> int:
         print(json.dumps({"read_designs": designs, "qmv_headline": q}), flush=True)
         return 0
     if args.pmc_workload:
-        pmc_workload(bmv, args.pmc_workload, args.pmc_batch)
+        pmc_workload(bmv, args.pmc_workload, args.pmc_batch, args.pmc_dtype)
         return 0
     head = workloads.mlp_up_case("mxfp4", 1)
     check_once(bmv, head)

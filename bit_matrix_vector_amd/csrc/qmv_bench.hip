@@ -145,6 +145,31 @@ __global__ __launch_bounds__(256) void read_rows_kernel(const uint8_t* __restric
     if (rr == 0x9E3779B9u) sink[blockIdx.x & 0xFFFF] = rr;
 }
 
+// The one-row QMV's loads over [rows][2048] weight bytes followed by
+// [rows][128] scale bytes (the MXFP4 K=4096 layout): a wave takes two rows;
+// lane l reads 16 bytes at 16 l and 1024 + 16 l of each row, and scale bytes
+// l and 64 + l of each row; four waves per block.
+__global__ __launch_bounds__(256) void read_rowpair_kernel(const uint8_t* __restrict__ p,
+                                                           int64_t rows,
+                                                           uint32_t* __restrict__ sink) {
+    const int lane = threadIdx.x & 63;
+    const int64_t r0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2;
+    const uint8_t* sc = p + rows * 2048;
+    v4u a = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t r = r0 + i < rows ? r0 + i : rows - 1;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            a ^= __builtin_nontemporal_load(
+                reinterpret_cast<const v4u*>(p + r * 2048 + 1024 * u + 16 * lane));
+            a.x ^= __builtin_nontemporal_load(sc + r * 128 + 64 * u + lane);
+        }
+    }
+    const uint32_t rr = a.x ^ a.y ^ a.z ^ a.w;
+    if (rr == 0x9E3779B9u) sink[blockIdx.x & 0xFFFF] = rr;
+}
+
 template <class Kern>
 int launch_blocks(Kern k, int64_t blocks, int threads, hipStream_t st, const v4u* p, int64_t n,
                   uint32_t* sink) {
@@ -186,6 +211,13 @@ extern "C" int qmv_bench_read_design(void* stream, const void* buf, int64_t byte
             auto* k = design == 15 ? read_rows_kernel<0> : read_rows_kernel<1>;
             // rows / 16 row groups x 8 waves, 4 waves per block
             hipLaunchKernelGGL(k, dim3((unsigned)(rows / 16 * 2)), dim3(256), 0, st,
+                               static_cast<const uint8_t*>(buf), rows, sink);
+            return (int)hipGetLastError();
+        }
+        case 17: {
+            if (bytes % (2176 * 8)) return (int)hipErrorInvalidValue;
+            const int64_t rows = bytes / 2176;   // 2048 weight + 128 scale bytes per row
+            hipLaunchKernelGGL(read_rowpair_kernel, dim3((unsigned)(rows / 8)), dim3(256), 0, st,
                                static_cast<const uint8_t*>(buf), rows, sink);
             return (int)hipGetLastError();
         }

@@ -589,8 +589,13 @@ __global__ __launch_bounds__(kThreads) void qmv_row_kernel(LaunchParams p) {
     constexpr int kUnitBytes = 4 * W;
     constexpr int KR = 2048 * NU;             // elements per row
     constexpr int US = KR / 32;               // units per row
+    // x sits in LDS in the tile's four planes (plane SC holds the 16-byte
+    // piece SC of every unit), each plane padded by 64 bytes so that the 16
+    // lanes of a staging write (4 units x 4 planes) hit all 64 banks once;
+    // unit_fma takes the plane stride in units
+    constexpr int USP = US + 4;
     constexpr int kEB = F::template elem_bytes<DT>();
-    __shared__ __align__(16) S xs[KR];
+    __shared__ __align__(16) S xs[USP * 32];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -631,7 +636,7 @@ __global__ __launch_bounds__(kThreads) void qmv_row_kernel(LaunchParams p) {
 #pragma unroll
     for (int j = 0; j < NU; ++j) {
         const int v = tid + j * kThreads;
-        *reinterpret_cast<v4u*>(xs + x_lds_slot(v * 8, US)) = xc[j];
+        *reinterpret_cast<v4u*>(xs + x_lds_slot(v * 8, USP)) = xc[j];
     }
     __syncthreads();
 
@@ -644,7 +649,7 @@ __global__ __launch_bounds__(kThreads) void qmv_row_kernel(LaunchParams p) {
         typename F::Scale scl[R];
 #pragma unroll
         for (int i = 0; i < R; ++i) scl[i] = F::template decode<DT>(s_raw[j][i]);
-        unit_fma<DT, FMT, BITS, 1, R>(u_raw[j], scl, xs, lane + 64 * j, KR, US, total);
+        unit_fma<DT, FMT, BITS, 1, R>(u_raw[j], scl, xs, lane + 64 * j, KR, USP, total);
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) total[i][0] = group_sum(total[i][0], 64);

@@ -8,7 +8,7 @@
  *                           issued before any is used, and folds them into
  *                           one word per block: the measured ceiling of a
  *                           read-only stream of that size.
- *   qmv_bench_read_design   reads `bytes` once with one of 17 read designs,
+ *   qmv_bench_read_design   reads `bytes` once with one of 18 read designs,
  *                           to find the fastest single launch for a size:
  *                           0-5 one-shot grids (threads x loads per lane:
  *                           256x2, 256x4, 256x8, 512x4, 1024x2, 64x8), 6 the
@@ -18,7 +18,11 @@
  *                           iteration on 256/512/1024/2048 blocks, 8 loads on
  *                           256/512), 15-16 [rows][2048] row patterns (eight
  *                           lanes per 128-byte line; the 16x16 MFMA operand
- *                           layout; bytes a multiple of 32 KB).
+ *                           layout; bytes a multiple of 32 KB), 17 the
+ *                           one-row QMV's loads over [rows][2048] weight
+ *                           bytes then [rows][128] scale bytes (two rows per
+ *                           wave, 64 lanes x 16 bytes per row and a scale
+ *                           byte per lane; bytes a multiple of 8 x 2176).
  *   qmv_bench_copy          copies `bytes` (a plain copy of known size, for
  *                           calibrating hardware byte counters).
  *
