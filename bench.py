@@ -731,7 +731,7 @@ def committed_traffic():
     return round(vals["t"])
 
 
-def pmc_workload(bmv, n: int, batch: int = 1, dtype: str = "bf16") -> None:
+def pmc_workload(bmv, n: int, batch: int = 1, dtype: str = "bf16", moe: str | None = None) -> None:
     """Launch sequence for hardware-counter runs: n copies of 64 MiB (the
     calibration kernel of known size), then n launches of the MXFP4 QMV at
     K=4096, N=14336 with `batch` activation rows of `dtype` (bf16, B=1: the
@@ -750,6 +750,16 @@ def pmc_workload(bmv, n: int, batch: int = 1, dtype: str = "bf16") -> None:
         assert st == 0
     torch.cuda.synchronize()
     del src, dst
+    if moe is not None:
+        # the MoE gather of one projection instead (`moe` = "fmt:proj")
+        fmt, proj = moe.split(":")
+        r = GatherRunner(bmv, workloads.moe_case(fmt, proj))
+        for i in range(n):
+            r.call(i, sp)
+        torch.cuda.synchronize()
+        print(f"[pmc] {n} copies of {nbytes} bytes, then {n} MoE gather {fmt} {proj} launches "
+              f"of {r.bytes} algorithmic bytes", flush=True)
+        return
     case = (workloads.mlp_up_case("mxfp4", batch) if dtype == "bf16" else
             workloads.mxfp4_case(3, f"c3-mxfp4-B{batch}-{dtype}", K=4096, N=14336, B=batch,
                                  dtype=dtype))
@@ -955,6 +965,9 @@ def main() -> int:
                     help="activation rows of the counter workload's QMV (default 1)")
     ap.add_argument("--pmc-dtype", default="bf16", choices=("bf16", "f16"),
                     help="activation type of the counter workload's QMV (default bf16)")
+    ap.add_argument("--pmc-moe", metavar="FMT:PROJ",
+                    help="counter workload: the MoE gather (e.g. mxfp4:gate_up) instead of "
+                         "the QMV")
     ap.add_argument("--summarize-pmc-table", metavar="COUNTER_CSV",
                     help="print per-kernel medians of every counter in a rocprofv3 counter "
                          "collection and exit (no GPU)")
@@ -1008,7 +1021,7 @@ def main() -> int:
         print(json.dumps({"read_designs": designs, "qmv_headline": q}), flush=True)
         return 0
     if args.pmc_workload:
-        pmc_workload(bmv, args.pmc_workload, args.pmc_batch, args.pmc_dtype)
+        pmc_workload(bmv, args.pmc_workload, args.pmc_batch, args.pmc_dtype, args.pmc_moe)
         return 0
     head = workloads.mlp_up_case("mxfp4", 1)
     check_once(bmv, head)

@@ -700,9 +700,9 @@ __global__ __launch_bounds__(kThreads) void qmv_norm_kernel(LaunchParams p, Geom
 // instantiated tile, so chunks stay at two activation rows (the tile of a
 // one- or two-row QMV); an expert with more slots runs several chunks over the
 // same tiles, whose weights the repeat reads find in L2.
-constexpr int kGatherChunkMax = 2;
-__host__ __device__ constexpr int gather_chunk_for(int) { return kGatherChunkMax; }
-constexpr int kGatherStageBytes = 32 * 1024;
+constexpr int kGatherChunkMax = 4;
+__host__ __device__ constexpr int gather_chunk_for(int dt) { return dt == DT_F32 ? 2 : kGatherChunkMax; }
+constexpr int kGatherStageBytes = 40 * 1024;
 
 // Units in flight per lane in the gather tile loop.
 constexpr int kGatherDepth = 2;
@@ -940,10 +940,19 @@ __device__ inline void gather_chunk(const LaunchParams& p, const MoeArgsOf<MODE>
                                                lds);
         }
     };
-    if (cnt == 1)
-        run(std::integral_constant<int, 1>{});
-    else
-        run(std::integral_constant<int, 2>{});
+    if constexpr (gather_chunk_for(DT) > 2) {
+        switch (cnt) {
+            case 1: run(std::integral_constant<int, 1>{}); break;
+            case 2: run(std::integral_constant<int, 2>{}); break;
+            case 3: run(std::integral_constant<int, 3>{}); break;
+            default: run(std::integral_constant<int, 4>{}); break;
+        }
+    } else {
+        if (cnt == 1)
+            run(std::integral_constant<int, 1>{});
+        else
+            run(std::integral_constant<int, 2>{});
+    }
 }
 
 // kOneSlab: K > 0 and the geometry holds all of K in one slab (the launcher
@@ -1553,9 +1562,11 @@ int launch_qmv_norm_t(const LaunchParams& p, const NormArgs& na, hipStream_t st)
 // (16 weight rows) and the activation rows as the B operand columns (16
 // columns, of which B are used), so the VALU only decodes.
 //
-// A block owns 32 weight rows (two 16-row tiles) and all of K; its waves take
-// chunks of 128 weight bytes per row (256 FP4 or 128 FP8 codes), chunk c
-// going to wave c mod W. A chunk is loaded with four coalesced loads (lane l
+// A block owns RT 16-row tiles of weight rows (mf_tiles: four for MXFP4, two
+// otherwise) and all of K; its W waves take chunks of 128 weight bytes per
+// row (256 FP4 or 128 FP8 codes), chunk c going to wave c mod W, and a wave's
+// activation pieces serve all its tiles. A chunk is loaded with 2 RT
+// coalesced loads (lane l
 // reads 16 bytes of row 8 i + l / 8, so eight consecutive lanes cover one
 // 128-byte line), written to the wave's own LDS area and read back in the
 // MFMA operand layout: lane 16 q + r holds the 32 codes [32 q, 32 q + 32) of
@@ -1586,18 +1597,26 @@ typedef float mf_f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
 constexpr int kBufferWord3 = 0x00020000;
 constexpr int kBufferOutOfRange = 0x7FFFFF00;
 
-constexpr int kMfRows = 32;          // weight rows per block
 constexpr int kMfChunkBytes = 128;   // weight bytes per row and chunk
-constexpr int kMfMaxWaves = 16;
 
 // codes per chunk and 128-code segments per chunk
 template <int FMT> constexpr int mf_chunk_codes() { return FMT == FMT_MXFP8 ? 128 : 256; }
 
-// Waves per block: one per chunk, at most 16; at most 8 for the NVFP4 decode
-// (fp32 products: 88 VGPRs) and the general instances (82..108 VGPRs), so two
-// blocks still fit a compute unit.
+// 16-row tiles per block and waves per block (one per chunk, at most this
+// many; each wave stages 2 KB per tile of its chunk in LDS). MXFP4 takes four
+// tiles and eight waves: every wave's activation pieces then serve 64 rows,
+// which halves the x bytes the launch moves from L2 (at B = 8 as many as the
+// weights) and measured 12.4 -> 10.8 us at B = 8 (K=4096, N=14336; 48-, 80-
+// and 128-row blocks and four waves were slower). NVFP4 and MXFP8, whose
+// decode is heavier and whose waves then run twice the work per chunk in
+// turn, measured slower that way (19.3 and 25.2 us against 12.6 and 20.2)
+// and keep two tiles: eight waves for NVFP4 (fp32 products, 88 VGPRs), 16
+// for MXFP8, 8 for the general instances (82..108 VGPRs).
+template <int FMT, bool kWhole> constexpr int mf_tiles() {
+    return (kWhole && FMT == FMT_MXFP4) ? 4 : 2;
+}
 template <int FMT, bool kWhole> constexpr int mf_max_waves() {
-    return (kWhole && FMT != FMT_NVFP4) ? kMfMaxWaves : kMfMaxWaves / 2;
+    return (kWhole && FMT == FMT_MXFP8) ? 16 : 8;
 }
 inline int mfma_waves(const LaunchParams& p, int max_waves) {
     const int cc = p.format == FMT_MXFP8 ? 128 : 256;
@@ -1617,6 +1636,8 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
     constexpr int kSegs = kCodes / 128;                  // 128-code segments per chunk
     constexpr int kBlk = FMT == FMT_NVFP4 ? 16 : 32;     // codes per scale
     constexpr int kScB = kCodes / kBlk;                  // scale bytes per row and chunk
+    constexpr int RT = mf_tiles<FMT, kWhole>();          // 16-row tiles per block
+    constexpr int kRows = 16 * RT;                       // weight rows per block
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -1626,22 +1647,22 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
     const int q = lane >> 4;
     const int B = (int)p.B;
     const int64_t K = p.K, N = p.N;
-    const int64_t row0 = (int64_t)blockIdx.x * kMfRows;
+    const int64_t row0 = (int64_t)blockIdx.x * kRows;
     const int64_t nchunks = (K + kCodes - 1) / kCodes;
-    uint8_t* wl = smem + (size_t)wave * kMfRows * kMfChunkBytes;
+    uint8_t* wl = smem + (size_t)wave * kRows * kMfChunkBytes;
     const S* x = static_cast<const S*>(p.x);
     const uint8_t* scb = static_cast<const uint8_t*>(p.scales);
 
     // rows this lane loads (coalesced) and reads (operand layout), clamped
-    int64_t lrow[4];
+    int64_t lrow[2 * RT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2 * RT; ++i) {
         const int64_t r = row0 + 8 * i + (lane >> 3);
         lrow[i] = r < N ? r : N - 1;
     }
-    int64_t orow[2];
+    int64_t orow[RT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < RT; ++t) {
         const int64_t r = row0 + 16 * t + r16;
         orow[t] = r < N ? r : N - 1;
     }
@@ -1653,9 +1674,9 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
     const bool has = r16 < B;
     const int xoff = (int)(r16 * K * (int64_t)sizeof(S));
 
-    mf_f32x4_t acc[2];
+    mf_f32x4_t acc[RT];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) acc[t] = mf_f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < RT; ++t) acc[t] = mf_f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     for (int64_t c = wave; c < nchunks; c += nw) {
         const int64_t code0 = c * kCodes;                // first code of the chunk
@@ -1664,9 +1685,9 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
         // lane l takes piece (l % 8) ^ g(row) of its row's 128 bytes, so row r
         // piece p lands in slot 8 (r % 8) + (p ^ g(r)), g(r) = (r / 2) % 8.
         // Pieces past the row end read its last piece (zeroed below).
-        v4u raw[4];
+        v4u raw[2 * RT];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 2 * RT; ++i) {
             const int r = 8 * i + (lane >> 3);
             const int piece = (lane & 7) ^ ((r >> 1) & 7);
             int64_t off = byte0 + 16 * piece;
@@ -1674,10 +1695,10 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
             raw[i] = load_vec<true, v4u>(p.w + lrow[i] * p.row_bytes + off);
         }
         // (2) scales: the row's kScB bytes of this chunk
-        uint32_t sw[2][kScB / 4 > 0 ? kScB / 4 : 1];
+        uint32_t sw[RT][kScB / 4 > 0 ? kScB / 4 : 1];
         const int64_t e0 = code0 / kBlk;
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < RT; ++t) {
             const uint8_t* srow = scb + orow[t] * p.sc_per_row;
             if constexpr (kWhole) {
                 if constexpr (kScB == 16) {
@@ -1719,13 +1740,13 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
         // (4) stage the chunk in the wave's LDS area (in program order with
         // this wave's operand reads of the previous chunk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *reinterpret_cast<v4u*>(wl + 1024 * i + 16 * lane) = raw[i];
+        for (int i = 0; i < 2 * RT; ++i) *reinterpret_cast<v4u*>(wl + 1024 * i + 16 * lane) = raw[i];
         // (5) the MFMAs
 #pragma unroll
         for (int s = 0; s < kSegs; ++s) {
             const bool kv = kWhole || code0 + 128 * s + 32 * q < K;
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
+            for (int t = 0; t < RT; ++t) {
                 const int r = 16 * t + r16;
                 const int g = (r >> 1) & 7;
                 const uint8_t* rp = wl + 1024 * (r >> 3) + 128 * (r & 7);
@@ -1796,22 +1817,22 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
 
     // the waves' partial tiles meet in LDS (the weight areas, once every wave
     // is done with them): element (row m, column b) of wave w at
-    // red[(w * 32 + m) * 8 + b]; lane (r16, q) holds rows 4 q .. 4 q + 3 of each tile
+    // red[(w * 16 RT + m) * 8 + b]; lane (r16, q) holds rows 4 q .. 4 q + 3 of each tile
     float* red = reinterpret_cast<float*>(smem);
     __syncthreads();
     if (has) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < RT; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) red[(wave * kMfRows + 16 * t + 4 * q + e) * 8 + r16] = acc[t][e];
+            for (int e = 0; e < 4; ++e) red[(wave * kRows + 16 * t + 4 * q + e) * 8 + r16] = acc[t][e];
     }
     __syncthreads();
     const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
-    for (int idx = tid; idx < kMfRows * B; idx += (int)blockDim.x) {
+    for (int idx = tid; idx < kRows * B; idx += (int)blockDim.x) {
         const int m = idx / B, b = idx - (idx / B) * B;
         if (row0 + m >= N) continue;
         float v = red[m * 8 + b];
-        for (int w = 1; w < nw; ++w) v += red[(w * kMfRows + m) * 8 + b];
+        for (int w = 1; w < nw; ++w) v += red[(w * kRows + m) * 8 + b];
         if constexpr (FMT == FMT_NVFP4) v = v * gmul;
         static_cast<S*>(p.y)[(int64_t)b * N + row0 + m] = Store<DT>::from_f32(v);
     }
@@ -1819,13 +1840,12 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
 
 // The matrix-core QMV takes bf16 activations from the batch size where it
 // beats the VALU tile, measured at K=4096, N=14336 (VALU tile -> matrix
-// cores; B=8 against the earlier 32x32 matrix-core kernel):
-//   MXFP4  B=3 10.6 -> 10.3, B=4 12.4 -> 10.7, B=5 15.3 -> 10.9, B=8 17.9 -> 12.6 us
+// cores):
+//   MXFP4  B=2 9.1 -> 10.3, B=3 10.6 -> 10.4, B=4 12.4 -> 10.4, B=8 27.6 -> 10.8 us
 //   NVFP4  B=3 10.9 -> 11.2, B=4 12.7 -> 11.5, B=6 17.5 -> 11.8, B=8 18.6 -> 12.6 us
 //   MXFP8  B=4 15.3 -> 17.2, B=5 18.4 -> 17.9, B=7 24.1 -> 19.5, B=8 23.2 -> 20.2 us
 // (MXFP8's 128-code chunks give each wave two chunks in turn at K=4096). At
-// B <= 2 the VALU tile is faster for every format (MXFP4 B=1 7.5 against
-// 9.9 us).
+// B <= 2 the VALU tile is faster for every format.
 template <int FMT> constexpr int mf_min_batch() {
     return FMT == FMT_MXFP4 ? 3 : (FMT == FMT_NVFP4 ? 4 : 5);
 }
@@ -1842,14 +1862,14 @@ int launch_qmv_mfma(const LaunchParams& p, hipStream_t st) {
     const bool whole = p.K % mf_chunk_codes<FMT>() == 0 && p.sc_per_row % kScB == 0 &&
                        (reinterpret_cast<uintptr_t>(p.scales) % kScB) == 0;
     const int nw = mfma_waves(p, whole ? mf_max_waves<FMT, true>() : mf_max_waves<FMT, false>());
-    // W waves stage 4 KB each; the reduction reuses that area (W * 32 rows *
-    // 8 columns * 4 bytes = W KB)
-    const size_t lds = (size_t)nw * kMfRows * kMfChunkBytes;
+    const int rows = 16 * (whole ? mf_tiles<FMT, true>() : mf_tiles<FMT, false>());
+    // W waves stage rows x 128 bytes each; the reduction reuses that area (W x
+    // rows x 8 columns x 4 bytes)
+    const size_t lds = (size_t)nw * rows * kMfChunkBytes;
     auto* kern = whole ? &qmv_mfma_kernel<DT, FMT, true> : &qmv_mfma_kernel<DT, FMT, false>;
     static LdsGrant granted_w, granted_p;
     if (const int e = allow_lds(kern, lds, whole ? granted_w : granted_p)) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)((p.N + kMfRows - 1) / kMfRows)), dim3(64 * nw), lds,
-                       st, p);
+    hipLaunchKernelGGL(kern, dim3((unsigned)((p.N + rows - 1) / rows)), dim3(64 * nw), lds, st, p);
     return (int)hipGetLastError();
 }
 
@@ -1890,15 +1910,19 @@ int launch_qmv_t(const LaunchParams& p, hipStream_t st) {
 }
 
 // Blocks a gather launch aims for across the experts that can be active
-// (at most min(n_experts, n_slots) of them): about two rounds of resident
-// blocks, so each block runs a group of several tiles.
-constexpr int64_t kGatherBlocks = 8192;
+// (at most min(n_experts, n_slots) of them), so each block runs a group of
+// several tiles: about one round of resident blocks for the plain gather
+// (64 experts, 128 slots: down projection 57.8 -> 52.4 us, affine 70.3 ->
+// 64.5 us against two rounds), two for the fused gate/up pair, whose
+// affine instance measured 210 -> 219 us with one.
+constexpr int64_t kGatherBlocks = 2048;
+constexpr int64_t kGatherPairBlocks = 8192;
 
-// Tiles per block of a gather launch: about kGatherBlocks blocks across the
+// Tiles per block of a gather launch: about `target` blocks across the
 // experts that can be active.
-inline int64_t gather_tiles_per_block(const LaunchParams& p, int64_t n_tiles) {
+inline int64_t gather_tiles_per_block(const LaunchParams& p, int64_t n_tiles, int64_t target) {
     const int64_t active = p.n_experts < p.n_slots ? p.n_experts : p.n_slots;
-    int64_t tpb = (n_tiles * active + kGatherBlocks - 1) / kGatherBlocks;
+    int64_t tpb = (n_tiles * active + target - 1) / target;
     if (tpb < 1) tpb = 1;
     if (tpb > n_tiles) tpb = n_tiles > 0 ? n_tiles : 1;
     return tpb;
@@ -1911,7 +1935,7 @@ int launch_gather_t(const LaunchParams& p, hipStream_t st) {
     Geom g = make_geom<DT, FMT, BITS>(p, kChunk, kGatherStageBytes, kGatherRows);
     g.out_rows = g.rows_per_block;
     const int64_t n_tiles = (p.N + g.out_rows - 1) / g.out_rows;
-    const int64_t tpb = gather_tiles_per_block(p, n_tiles);
+    const int64_t tpb = gather_tiles_per_block(p, n_tiles, kGatherBlocks);
     g.tiles_per_block = (int)tpb;
     const dim3 grid((unsigned)((n_tiles + tpb - 1) / tpb), (unsigned)(p.n_experts + 1));
     const size_t lds = stage_bytes<DT, FMT, BITS>(p, g);
@@ -1937,7 +1961,7 @@ int launch_moe_gate_up_t(const LaunchParams& p, const MoeArgs& m, hipStream_t st
     if (g.ks < p.K || p.K <= 0 || lds > (size_t)kMaxStageBytes) return (int)hipErrorInvalidValue;
     g.out_rows = g.rows_per_block / kGatherRows;
     const int64_t n_tiles = (p.N + g.out_rows - 1) / g.out_rows;
-    const int64_t tpb = gather_tiles_per_block(p, n_tiles);
+    const int64_t tpb = gather_tiles_per_block(p, n_tiles, kGatherPairBlocks);
     g.tiles_per_block = (int)tpb;
     const dim3 grid((unsigned)((n_tiles + tpb - 1) / tpb), (unsigned)(p.n_experts + 1));
     auto* kern = &gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherSwiglu>;
