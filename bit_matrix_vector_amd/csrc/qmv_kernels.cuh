@@ -1598,6 +1598,7 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kBufferOutOfRange = 0x7FFFFF00;
 
 constexpr int kMfChunkBytes = 128;   // weight bytes per row and chunk
+constexpr int kMfMaxScaleRow = 256;  // scale bytes per row the staged path takes
 
 // codes per chunk and 128-code segments per chunk
 template <int FMT> constexpr int mf_chunk_codes() { return FMT == FMT_MXFP8 ? 128 : 256; }
@@ -1617,6 +1618,14 @@ template <int FMT, bool kWhole> constexpr int mf_tiles() {
 }
 template <int FMT, bool kWhole> constexpr int mf_max_waves() {
     return (kWhole && FMT == FMT_MXFP8) ? 16 : 8;
+}
+// 16-byte scale pieces each thread stages (kWhole): a block's scale rows,
+// at most kMfMaxScaleRow bytes each, over at least 64 threads per wave of the
+// launch (the launcher checks that they fit)
+template <int FMT, bool kWhole> constexpr int mf_scale_pieces() {
+    constexpr int per = 16 * mf_tiles<FMT, kWhole>() * kMfMaxScaleRow / 16;
+    constexpr int thr = 64 * mf_max_waves<FMT, kWhole>();
+    return kWhole ? (per + thr - 1) / thr : 1;
 }
 inline int mfma_waves(const LaunchParams& p, int max_waves) {
     const int cc = p.format == FMT_MXFP8 ? 128 : 256;
@@ -1678,6 +1687,33 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
 #pragma unroll
     for (int t = 0; t < RT; ++t) acc[t] = mf_f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+    // kWhole: the block's scale rows (one contiguous range of kRows x
+    // sc_per_row bytes) are staged once in LDS after the weight area, each row
+    // padded by 16 bytes so the operand rows' reads hit distinct banks. The
+    // 16-byte pieces are loaded here, ahead of every weight load; their LDS
+    // writes wait for them alone (the counters retire in order) and happen
+    // after the first chunk's loads have gone out, before one barrier.
+    constexpr int kScPieces = mf_scale_pieces<FMT, kWhole>();
+    const int sc_row = (int)p.sc_per_row;
+    const int sc_stride = sc_row + 16;
+    uint8_t* sst = smem + (size_t)nw * kRows * kMfChunkBytes;
+    v4u scp[kScPieces];
+    if constexpr (kWhole) {
+        const int64_t base = row0 * p.sc_per_row;
+        const int64_t last = N * p.sc_per_row - 16;
+        const int n16 = kRows * sc_row / 16;
+#pragma unroll
+        for (int j = 0; j < kScPieces; ++j) {
+            const int pc = tid + j * (int)blockDim.x;
+            if (j == 0 || pc < n16) {
+                int64_t o = base + 16 * (int64_t)(pc < n16 ? pc : n16 - 1);
+                o = o < last ? o : last;   // rows past N: their results are not stored
+                scp[j] = *reinterpret_cast<const v4u*>(scb + o);
+            }
+        }
+    }
+    bool staged = false;
+
     for (int64_t c = wave; c < nchunks; c += nw) {
         const int64_t code0 = c * kCodes;                // first code of the chunk
         const int64_t byte0 = FMT == FMT_MXFP8 ? code0 : code0 / 2;
@@ -1697,19 +1733,36 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
         // (2) scales: the row's kScB bytes of this chunk
         uint32_t sw[RT][kScB / 4 > 0 ? kScB / 4 : 1];
         const int64_t e0 = code0 / kBlk;
+        if constexpr (kWhole) {
+            if (!staged) {
+                const int n16 = kRows * sc_row / 16;
+#pragma unroll
+                for (int j = 0; j < kScPieces; ++j) {
+                    const int pc = tid + j * (int)blockDim.x;
+                    if (pc < n16) {
+                        const int r = pc * 16 / sc_row, col = pc * 16 - r * sc_row;
+                        *reinterpret_cast<v4u*>(sst + r * sc_stride + col) = scp[j];
+                    }
+                }
+                __syncthreads();
+                staged = true;
+            }
+        }
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
             const uint8_t* srow = scb + orow[t] * p.sc_per_row;
             if constexpr (kWhole) {
+                const uint8_t* lrw = sst + (16 * t + r16) * sc_stride + e0;
                 if constexpr (kScB == 16) {
-                    const v4u v = *reinterpret_cast<const v4u*>(srow + e0);
+                    const v4u v = *reinterpret_cast<const v4u*>(lrw);
                     sw[t][0] = v.x; sw[t][1] = v.y; sw[t][2] = v.z; sw[t][3] = v.w;
                 } else if constexpr (kScB == 8) {
-                    const v2u v = *reinterpret_cast<const v2u*>(srow + e0);
+                    const v2u v = *reinterpret_cast<const v2u*>(lrw);
                     sw[t][0] = v.x; sw[t][1] = v.y;
                 } else {
-                    sw[t][0] = *reinterpret_cast<const uint32_t*>(srow + e0);
+                    sw[t][0] = *reinterpret_cast<const uint32_t*>(lrw);
                 }
+                (void)srow;
             } else {
 #pragma unroll
                 for (int j = 0; j < kScB / 4; ++j) {
@@ -1840,14 +1893,14 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
 
 // The matrix-core QMV takes bf16 activations from the batch size where it
 // beats the VALU tile, measured at K=4096, N=14336 (VALU tile -> matrix
-// cores):
-//   MXFP4  B=2 9.1 -> 10.3, B=3 10.6 -> 10.4, B=4 12.4 -> 10.4, B=8 27.6 -> 10.8 us
-//   NVFP4  B=3 10.9 -> 11.2, B=4 12.7 -> 11.5, B=6 17.5 -> 11.8, B=8 18.6 -> 12.6 us
-//   MXFP8  B=4 15.3 -> 17.2, B=5 18.4 -> 17.9, B=7 24.1 -> 19.5, B=8 23.2 -> 20.2 us
-// (MXFP8's 128-code chunks give each wave two chunks in turn at K=4096). At
-// B <= 2 the VALU tile is faster for every format.
+// cores, one process):
+//   MXFP4  B=2 9.3 -> 9.2, B=3 10.8 -> 9.4, B=4 12.5 -> 9.5, B=8 27.7 -> 10.0 us
+//   NVFP4  B=3 10.9 -> 11.5, B=4 12.6 -> 11.2, B=6 17.4 -> 11.3, B=8 28.6 -> 11.8 us
+//   MXFP8  B=3 14.2 -> 14.9, B=4 15.6 -> 15.0, B=6 19.8 -> 15.3, B=8 46.2 -> 16.0 us
+// (MXFP8's 128-code chunks give each wave two chunks in turn at K=4096;
+// MXFP4 at B = 2 is within noise and stays on the VALU tile).
 template <int FMT> constexpr int mf_min_batch() {
-    return FMT == FMT_MXFP4 ? 3 : (FMT == FMT_NVFP4 ? 4 : 5);
+    return FMT == FMT_MXFP4 ? 3 : 4;
 }
 template <int FMT>
 inline bool use_mfma_qmv(const LaunchParams& p) {
@@ -1859,13 +1912,23 @@ inline bool use_mfma_qmv(const LaunchParams& p) {
 template <int DT, int FMT>
 int launch_qmv_mfma(const LaunchParams& p, hipStream_t st) {
     constexpr int kScB = mf_chunk_codes<FMT>() / (FMT == FMT_NVFP4 ? 16 : 32);
-    const bool whole = p.K % mf_chunk_codes<FMT>() == 0 && p.sc_per_row % kScB == 0 &&
-                       (reinterpret_cast<uintptr_t>(p.scales) % kScB) == 0;
-    const int nw = mfma_waves(p, whole ? mf_max_waves<FMT, true>() : mf_max_waves<FMT, false>());
-    const int rows = 16 * (whole ? mf_tiles<FMT, true>() : mf_tiles<FMT, false>());
-    // W waves stage rows x 128 bytes each; the reduction reuses that area (W x
-    // rows x 8 columns x 4 bytes)
-    const size_t lds = (size_t)nw * rows * kMfChunkBytes;
+    // whole chunks, and scale rows the block can stage in 16-byte pieces
+    bool whole = p.K % mf_chunk_codes<FMT>() == 0 && p.sc_per_row % 16 == 0 &&
+                       p.sc_per_row <= kMfMaxScaleRow &&
+                       (reinterpret_cast<uintptr_t>(p.scales) % 16) == 0;
+    (void)kScB;
+    int nw = mfma_waves(p, whole ? mf_max_waves<FMT, true>() : mf_max_waves<FMT, false>());
+    int rows = 16 * (whole ? mf_tiles<FMT, true>() : mf_tiles<FMT, false>());
+    if (whole && (int64_t)rows * p.sc_per_row / 16 > (int64_t)mf_scale_pieces<FMT, true>() * 64 * nw) {
+        // the scale rows need more pieces per thread than the instance holds
+        whole = false;
+        nw = mfma_waves(p, mf_max_waves<FMT, false>());
+        rows = 16 * mf_tiles<FMT, false>();
+    }
+    // W waves stage rows x 128 bytes each (the reduction reuses that area: W x
+    // rows x 8 columns x 4 bytes); whole instances add the staged scale rows
+    const size_t lds = (size_t)nw * rows * kMfChunkBytes +
+                       (whole ? (size_t)rows * (size_t)(p.sc_per_row + 16) : 0);
     auto* kern = whole ? &qmv_mfma_kernel<DT, FMT, true> : &qmv_mfma_kernel<DT, FMT, false>;
     static LdsGrant granted_w, granted_p;
     if (const int e = allow_lds(kern, lds, whole ? granted_w : granted_p)) return e;

@@ -298,8 +298,8 @@ def test_affine_sweep_sampled(bmv, bits, group, B, dtype):
     check(y[:, rows], y64, A, dtype, f"affine b{bits} g{group} B{B} {dtype} K=N=4096")
 
 
-# the matrix cores take bf16 batches from B = 3 (MXFP4), 4 (NVFP4), 5 (MXFP8)
-MC_FIRST = {"mxfp4": 3, "nvfp4": 4, "mxfp8": 5}
+# the matrix cores take bf16 batches from B = 3 (MXFP4), 4 (NVFP4, MXFP8)
+MC_FIRST = {"mxfp4": 3, "nvfp4": 4, "mxfp8": 4}
 
 
 def test_batch_rows_equal_single_row_calls_bitwise(bmv):
