@@ -902,7 +902,129 @@ __device__ inline void gather_tiles(const LaunchParams& p, const MoeArgsOf<MODE>
     });
 }
 
-template <int DT, int FMT, int BITS, int R, bool kOneSlab, int MODE>
+// The gather tile loop for 16-bit activations and MXFP4 / NVFP4 / MXFP8
+// weights with K = 2048 * NU (one slab, 64 lanes per row): the one-row QMV
+// kernel's structure applied to the gather's tiles. Each wave owns the same
+// two rows of every tile of its group (plain mode: rows 2 w, 2 w + 1; pair
+// mode: output row w, its gate row from w and its up row from w2), with the
+// row addresses wave-uniform; lane l takes units l, l + 64, ... of both rows,
+// exactly the units and the order of gather_tiles, folded by the same
+// unit_fma and reduced by the same group_sum, so every result is bit for bit
+// that of gather_tiles. The next tile's weight and scale loads are issued
+// before the current tile is folded. What it removes is the generic loop's
+// per-unit bookkeeping (cursor, tile entry, per-lane offsets and clamps),
+// which at a few slots per expert is much of its VALU work.
+template <int DT, int FMT, int BITS, int NB, int NU, int MODE = kGatherPlain>
+__device__ inline void gather_row_tiles(const LaunchParams& p, const MoeArgsOf<MODE>& m,
+                                        const Geom& g, int64_t tile0, int64_t tile_end,
+                                        const uint8_t* __restrict__ w, const void* sc,
+                                        typename Store<DT>::S* const (&yrow)[NB], float gmul,
+                                        const typename Store<DT>::S* lds) {
+    using F = Fmt<FMT, BITS>;
+    constexpr int R = 2;
+    constexpr int W = F::kWords;
+    constexpr int kUnitBytes = 4 * W;
+    constexpr int KR = 2048 * NU;
+    constexpr int US = KR / 32;
+    constexpr bool kPair = MODE == kGatherSwiglu;
+    struct Item {
+        UnitRaw<FMT, BITS, R> u[NU];
+        typename F::Raw raw[NU][R];
+    };
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t N = p.N;
+    const int64_t RB = g.out_rows;
+    const int64_t sc_row_bytes = p.sc_per_row * F::template elem_bytes<DT>();
+    const uint8_t* w_of[2] = {w, w};
+    const uint8_t* sc_of[2] = {static_cast<const uint8_t*>(sc), static_cast<const uint8_t*>(sc)};
+    if constexpr (kPair) {
+        w_of[1] = m.w2;
+        sc_of[1] = static_cast<const uint8_t*>(m.scales2);
+    }
+    // row of operand row i in tile t (rows past N re-read row N - 1)
+    auto row_of = [&](int64_t t, int i) __attribute__((always_inline)) {
+        const int64_t r = kPair ? t * RB + wave : t * RB + R * wave + i;
+        return r < N ? r : N - 1;
+    };
+    auto load = [&](Item& it, int64_t t) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < R; ++i) {
+            const int64_t r = row_of(t, i);
+            const int mi = kPair ? i : 0;
+            const uint8_t* wr = w_of[mi] + r * p.row_bytes;
+            const uint8_t* sr = sc_of[mi] + r * sc_row_bytes;
+#pragma unroll
+            for (int j = 0; j < NU; ++j) {
+                load_words<W>(wr + (lane + 64 * j) * kUnitBytes, it.u[j].d[i]);
+                it.raw[j][i] = F::template global_raw<DT>(sr, nullptr, 0u, lane + 64 * j, 0);
+            }
+        }
+    };
+    auto fold_store = [&](const Item& it, int64_t t) __attribute__((always_inline)) {
+        float total[R][NB];
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) total[i][b] = 0.0f;
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+            typename F::Scale scl[R];
+#pragma unroll
+            for (int i = 0; i < R; ++i) scl[i] = F::template decode<DT>(it.raw[j][i]);
+            unit_fma<DT, FMT, BITS, NB, R>(it.u[j], scl, lds, lane + 64 * j, KR, US, total);
+            // keep each unit's LDS reads next to their use (hoisting them all
+            // ahead of the arithmetic doubles the register footprint)
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) total[i][b] = group_sum(total[i][b], 64);
+        if (lane == 63) {
+            if constexpr (kPair) {
+                const int64_t r = t * RB + wave;
+                if (r < N) {
+#pragma unroll
+                    for (int b = 0; b < NB; ++b) {
+                        float gv = total[0][b], uv = total[1][b];
+                        if constexpr (FMT == FMT_NVFP4) {
+                            gv = gv * gmul;
+                            uv = uv * (m.gscale2 ? *m.gscale2 : 1.0f);
+                        }
+                        yrow[b][r] = Store<DT>::from_f32(swiglu_act(gv, uv, m.act_clamp));
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < R; ++i) {
+                    const int64_t r = t * RB + R * wave + i;
+                    if (r < N) {
+#pragma unroll
+                        for (int b = 0; b < NB; ++b) {
+                            float v = total[i][b];
+                            if constexpr (FMT == FMT_NVFP4) v = v * gmul;
+                            yrow[b][r] = Store<DT>::from_f32(v);
+                        }
+                    }
+                }
+            }
+        }
+    };
+    // two tiles in flight: fold one while the next one's loads are out
+    Item a, b;
+    int64_t t = tile0;
+    load(a, t);
+    for (; t + 1 < tile_end; t += 2) {
+        load(b, t + 1);
+        fold_store(a, t);
+        if (t + 2 < tile_end) load(a, t + 2);
+        fold_store(b, t + 1);
+    }
+    if (t < tile_end) fold_store(a, t);
+}
+
+template <int DT, int FMT, int BITS, int R, bool kOneSlab, int MODE, int NUR = 0>
 __device__ inline void gather_chunk(const LaunchParams& p, const MoeArgsOf<MODE>& m,
                                     const Geom& g, int64_t tile0,
                                     int64_t tile_end, const uint8_t* w, const void* sc,
@@ -931,8 +1053,12 @@ __device__ inline void gather_chunk(const LaunchParams& p, const MoeArgsOf<MODE>
                         stage_vec<FMT, BITS, DT>(src[v]);
             }
             __syncthreads();
-            gather_tiles<DT, FMT, BITS, NB, R, MODE>(p, m, g, tile0, tile_end, w, sc, bi, yrow,
-                                                     gmul, lds);
+            if constexpr (NUR > 0)
+                gather_row_tiles<DT, FMT, BITS, NB, NUR, MODE>(p, m, g, tile0, tile_end, w, sc,
+                                                               yrow, gmul, lds);
+            else
+                gather_tiles<DT, FMT, BITS, NB, R, MODE>(p, m, g, tile0, tile_end, w, sc, bi,
+                                                         yrow, gmul, lds);
         } else {
             static_assert(MODE == kGatherPlain, "the paired mode needs one slab");
             for (int64_t t = tile0; t < tile_end; ++t)
@@ -960,7 +1086,7 @@ __device__ inline void gather_chunk(const LaunchParams& p, const MoeArgsOf<MODE>
 // MODE kGatherSwiglu: the fused gate/up projection of the routed-MoE block
 // (slot s reads x row s / top_k; w / w2 are the gate / up matrices; the output
 // is the activation, one row per slot).
-template <int DT, int FMT, int BITS, int R, bool kOneSlab, int MODE = kGatherPlain>
+template <int DT, int FMT, int BITS, int R, bool kOneSlab, int MODE = kGatherPlain, int NUR = 0>
 __global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g,
                                                           MoeArgsOf<MODE> m) {
     using S = typename Store<DT>::S;
@@ -1030,7 +1156,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(LaunchParams p, Geom g
     auto run_chunk = [&](int cnt) {
         if (tid < cnt) xoff[tid] = (int64_t)xrow[tid] * p.K;
         __syncthreads();
-        gather_chunk<DT, FMT, BITS, R, kOneSlab, MODE>(p, m, g, tile0, tile_end, w, sc, bi,
+        gather_chunk<DT, FMT, BITS, R, kOneSlab, MODE, NUR>(p, m, g, tile0, tile_end, w, sc, bi,
                                                        gmul, list, xoff, cnt, lds);
         __syncthreads();
     };
@@ -1991,6 +2117,24 @@ inline int64_t gather_tiles_per_block(const LaunchParams& p, int64_t n_tiles, in
     return tpb;
 }
 
+// Units per lane per row of the gather's one-row-style tile loop for this
+// launch (K = 2048 * NU, NU = 1 or 2; 16-bit activations; MXFP4 / NVFP4 /
+// MXFP8; one slab of K, 64 lanes per row), or 0 for the generic loop. For
+// the other instantiations gather_row_nu folds the template argument to 0,
+// so no extra kernel is built for them.
+template <int DT, int FMT>
+constexpr bool gather_row_ok() {
+    return DT != DT_F32 && (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8);
+}
+template <int DT, int FMT>
+constexpr int gather_row_nu(int nu) { return gather_row_ok<DT, FMT>() ? nu : 0; }
+template <int DT, int FMT>
+inline int gather_row_units(const LaunchParams& p, const Geom& g) {
+    if (!gather_row_ok<DT, FMT>()) return 0;
+    if (p.K <= 0 || p.K % 2048 != 0 || p.K / 2048 > 2 || g.ks < p.K || g.lpr != 64) return 0;
+    return (int)(p.K / 2048);
+}
+
 template <int DT, int FMT, int BITS>
 int launch_gather_t(const LaunchParams& p, hipStream_t st) {
     const NoMoeArgs none{};
@@ -2002,7 +2146,16 @@ int launch_gather_t(const LaunchParams& p, hipStream_t st) {
     g.tiles_per_block = (int)tpb;
     const dim3 grid((unsigned)((n_tiles + tpb - 1) / tpb), (unsigned)(p.n_experts + 1));
     const size_t lds = stage_bytes<DT, FMT, BITS>(p, g);
-    if (g.ks >= p.K && p.K > 0)
+    const int nur = gather_row_units<DT, FMT>(p, g);
+    if (nur == 1)
+        hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherPlain,
+                                          gather_row_nu<DT, FMT>(1)>),
+                           grid, dim3(kThreads), lds, st, p, g, none);
+    else if (nur == 2)
+        hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherPlain,
+                                          gather_row_nu<DT, FMT>(2)>),
+                           grid, dim3(kThreads), lds, st, p, g, none);
+    else if (g.ks >= p.K && p.K > 0)
         hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kGatherRows, true>), grid,
                            dim3(kThreads), lds, st, p, g, none);
     else
@@ -2027,10 +2180,17 @@ int launch_moe_gate_up_t(const LaunchParams& p, const MoeArgs& m, hipStream_t st
     const int64_t tpb = gather_tiles_per_block(p, n_tiles, kGatherPairBlocks);
     g.tiles_per_block = (int)tpb;
     const dim3 grid((unsigned)((n_tiles + tpb - 1) / tpb), (unsigned)(p.n_experts + 1));
-    auto* kern = &gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherSwiglu>;
+    const int nur = gather_row_units<DT, FMT>(p, g);
+    auto* kern = nur == 1 ? &gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherSwiglu,
+                                           gather_row_nu<DT, FMT>(1)>
+               : nur == 2 ? &gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherSwiglu,
+                                           gather_row_nu<DT, FMT>(2)>
+                          : &gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherSwiglu>;
     // the static slot lists ride on top of the dynamic x stage
-    static LdsGrant granted;
-    if (const int e = allow_lds(kern, lds, granted, 32 * 1024)) return e;
+    static LdsGrant granted, granted1, granted2;
+    if (const int e = allow_lds(kern, lds, nur == 1 ? granted1 : nur == 2 ? granted2 : granted,
+                                32 * 1024))
+        return e;
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, p, g, m);
     return (int)hipGetLastError();
 }
