@@ -580,8 +580,9 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(LaunchParams p, Geom g) {
 // ---------------------------------------------------------------------------
 template <int FMT> constexpr int row_units_max() { return 2; }
 
-template <int DT, int FMT, int BITS, int NU>
-__global__ __launch_bounds__(kThreads) void qmv_row_kernel(LaunchParams p) {
+template <int DT, int FMT, int BITS, int NU, class XR>
+__device__ inline void row_tiles(const LaunchParams& p, const XR& xr, float gmul,
+                                 typename Store<DT>::S* xs) {
     using F = Fmt<FMT, BITS>;
     using S = typename Store<DT>::S;
     constexpr int R = 2;                      // rows per wave
@@ -595,20 +596,18 @@ __global__ __launch_bounds__(kThreads) void qmv_row_kernel(LaunchParams p) {
     // unit_fma takes the plane stride in units
     constexpr int USP = US + 4;
     constexpr int kEB = F::template elem_bytes<DT>();
-    __shared__ __align__(16) S xs[USP * 32];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t N = p.N;
     const int64_t row0 = (int64_t)blockIdx.x * (kWaves * R) + wave * R;
-    const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
 
-    // (1) this thread's NU 16-byte chunks of x, ahead of the weights
-    const S* x = static_cast<const S*>(p.x);
-    v4u xc[NU];
+    // (1) this thread's NU 16-byte chunks of x (and whatever the accessor's
+    // staging reads with them), ahead of the weights
+    typename XR::Chunk xc[NU];
 #pragma unroll
-    for (int j = 0; j < NU; ++j) xc[j] = *reinterpret_cast<const v4u*>(x + (tid + j * kThreads) * 8);
+    for (int j = 0; j < NU; ++j) xc[j] = xr.load(0, (int64_t)(tid + j * kThreads) * 8);
 
     // (2) the lane's units of both rows and their scale elements (rows past
     // the end re-read row N - 1; their results are not stored)
@@ -632,11 +631,11 @@ __global__ __launch_bounds__(kThreads) void qmv_row_kernel(LaunchParams p) {
         }
     }
 
-    // (3) x to LDS, chunk v at the tile's slot
+    // (3) x to LDS, chunk v at the tile's slot, in the tile's staging order
 #pragma unroll
     for (int j = 0; j < NU; ++j) {
         const int v = tid + j * kThreads;
-        *reinterpret_cast<v4u*>(xs + x_lds_slot(v * 8, USP)) = xc[j];
+        *reinterpret_cast<v4u*>(xs + x_lds_slot(v * 8, USP)) = xr.stage(0, (int64_t)v * 8, xc[j]);
     }
     __syncthreads();
 
@@ -653,17 +652,27 @@ __global__ __launch_bounds__(kThreads) void qmv_row_kernel(LaunchParams p) {
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) total[i][0] = group_sum(total[i][0], 64);
+    xr.finish();
     if (lane == 63) {
         S* y = static_cast<S*>(p.y);
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             if (row0 + i < N) {
-                float v = total[i][0];
+                float v = xr.out(0, total[i][0]);
                 if constexpr (FMT == FMT_NVFP4) v = v * gmul;
                 y[row0 + i] = Store<DT>::from_f32(v);
             }
         }
     }
+}
+
+template <int DT, int FMT, int BITS, int NU>
+__global__ __launch_bounds__(kThreads) void qmv_row_kernel(LaunchParams p) {
+    using S = typename Store<DT>::S;
+    __shared__ __align__(16) S xs[(2048 * NU / 32 + 4) * 32];
+    const XContig<S> xr{static_cast<const S*>(p.x), p.K};
+    const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
+    row_tiles<DT, FMT, BITS, NU>(p, xr, gmul, xs);
 }
 
 // Fused RMSNorm + QMV: y[b] = r[b] * (W . RN_T(x[b] * gamma)), the QMV tile
@@ -683,6 +692,22 @@ __global__ __launch_bounds__(kThreads) void qmv_norm_kernel(LaunchParams p, Geom
     const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
     qmv_tile<DT, FMT, BITS, NB, R, true, SHORT>(p, g, (int64_t)blockIdx.x * g.rows_per_block, p.w,
                                                 p.scales, p.biases, xr, yrow, gmul, lds);
+}
+
+// The fused RMSNorm + QMV at one activation row on the one-row kernel's
+// structure (16-bit activations, MXFP4 / NVFP4 / MXFP8, K = 2048 or 4096):
+// the XNorm accessor stages x times gamma with the tile's chunk-to-thread
+// assignment and sums the squares in the same order, so r and every result
+// are bit for bit those of qmv_norm_kernel.
+template <int DT, int FMT, int BITS, int NU>
+__global__ __launch_bounds__(kThreads) void qmv_row_norm_kernel(LaunchParams p, NormArgs na) {
+    using S = typename Store<DT>::S;
+    __shared__ __align__(16) S xs[(2048 * NU / 32 + 4) * 32];
+    __shared__ float red[kWaves];
+    const XNorm<DT, 1> xr{static_cast<const S*>(p.x), p.K, static_cast<const S*>(na.gamma), na.eps,
+                          red, {}, {}};
+    const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
+    row_tiles<DT, FMT, BITS, NU>(p, xr, gmul, xs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1668,6 +1693,19 @@ int launch_qmv_norm_r(const LaunchParams& p, const NormArgs& na, hipStream_t st)
 // gamma and the squares), so fewer, taller blocks do less of it.
 template <int DT, int FMT, int BITS>
 int launch_qmv_norm_t(const LaunchParams& p, const NormArgs& na, hipStream_t st) {
+    if constexpr (DT != DT_F32 && (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
+        if (p.B == 1 && p.N > 0 && p.K > 0 && p.K % 2048 == 0 &&
+            p.K / 2048 <= row_units_max<FMT>()) {
+            const dim3 grid((unsigned)((p.N + 2 * kWaves - 1) / (2 * kWaves)));
+            if (p.K == 2048)
+                hipLaunchKernelGGL((qmv_row_norm_kernel<DT, FMT, BITS, 1>), grid, dim3(kThreads),
+                                   0, st, p, na);
+            else
+                hipLaunchKernelGGL((qmv_row_norm_kernel<DT, FMT, BITS, 2>), grid, dim3(kThreads),
+                                   0, st, p, na);
+            return (int)hipGetLastError();
+        }
+    }
     switch ((int)p.B) {
 #define QMV_CASE(n)                                                                         \
     case n:                                                                                 \
