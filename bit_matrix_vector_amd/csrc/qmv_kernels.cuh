@@ -939,7 +939,13 @@ __device__ inline void gather_tiles(const LaunchParams& p, const MoeArgsOf<MODE>
 // before the current tile is folded. What it removes is the generic loop's
 // per-unit bookkeeping (cursor, tile entry, per-lane offsets and clamps),
 // which at a few slots per expert is much of its VALU work.
-template <int DT, int FMT, int BITS, int NB, int NU, int MODE = kGatherPlain>
+// Variants of the lean gather loop (a kernel template argument, 0 = the
+// generic loop): 1 and 2 take 64 lanes per row and K = 2048 or 4096; 3 takes
+// 16 lanes per row and K = 1536 (three units per lane).
+__host__ __device__ constexpr int row_lpr(int nur) { return nur == 3 ? 16 : 64; }
+__host__ __device__ constexpr int row_nu(int nur) { return nur; }
+
+template <int DT, int FMT, int BITS, int NB, int NU, int LPR, int MODE = kGatherPlain>
 __device__ inline void gather_row_tiles(const LaunchParams& p, const MoeArgsOf<MODE>& m,
                                         const Geom& g, int64_t tile0, int64_t tile_end,
                                         const uint8_t* __restrict__ w, const void* sc,
@@ -949,8 +955,9 @@ __device__ inline void gather_row_tiles(const LaunchParams& p, const MoeArgsOf<M
     constexpr int R = 2;
     constexpr int W = F::kWords;
     constexpr int kUnitBytes = 4 * W;
-    constexpr int KR = 2048 * NU;
-    constexpr int US = KR / 32;
+    constexpr int US = LPR * NU;              // units per row
+    constexpr int KR = 32 * US;
+    constexpr int kGroups = 64 / LPR;         // lane groups (row pairs) per wave
     constexpr bool kPair = MODE == kGatherSwiglu;
     struct Item {
         UnitRaw<FMT, BITS, R> u[NU];
@@ -958,6 +965,9 @@ __device__ inline void gather_row_tiles(const LaunchParams& p, const MoeArgsOf<M
     };
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int grp = lane / LPR;               // this lane's row pair within the wave
+    const int gl = lane % LPR;
+    const int slot = wave * kGroups + grp;    // row pair (plain) or output row (pair) index
     const int64_t N = p.N;
     const int64_t RB = g.out_rows;
     const int64_t sc_row_bytes = p.sc_per_row * F::template elem_bytes<DT>();
@@ -969,7 +979,7 @@ __device__ inline void gather_row_tiles(const LaunchParams& p, const MoeArgsOf<M
     }
     // row of operand row i in tile t (rows past N re-read row N - 1)
     auto row_of = [&](int64_t t, int i) __attribute__((always_inline)) {
-        const int64_t r = kPair ? t * RB + wave : t * RB + R * wave + i;
+        const int64_t r = kPair ? t * RB + slot : t * RB + R * slot + i;
         return r < N ? r : N - 1;
     };
     auto load = [&](Item& it, int64_t t) __attribute__((always_inline)) {
@@ -981,8 +991,8 @@ __device__ inline void gather_row_tiles(const LaunchParams& p, const MoeArgsOf<M
             const uint8_t* sr = sc_of[mi] + r * sc_row_bytes;
 #pragma unroll
             for (int j = 0; j < NU; ++j) {
-                load_words<W>(wr + (lane + 64 * j) * kUnitBytes, it.u[j].d[i]);
-                it.raw[j][i] = F::template global_raw<DT>(sr, nullptr, 0u, lane + 64 * j, 0);
+                load_words<W>(wr + (gl + LPR * j) * kUnitBytes, it.u[j].d[i]);
+                it.raw[j][i] = F::template global_raw<DT>(sr, nullptr, 0u, gl + LPR * j, 0);
             }
         }
     };
@@ -997,7 +1007,7 @@ __device__ inline void gather_row_tiles(const LaunchParams& p, const MoeArgsOf<M
             typename F::Scale scl[R];
 #pragma unroll
             for (int i = 0; i < R; ++i) scl[i] = F::template decode<DT>(it.raw[j][i]);
-            unit_fma<DT, FMT, BITS, NB, R>(it.u[j], scl, lds, lane + 64 * j, KR, US, total);
+            unit_fma<DT, FMT, BITS, NB, R>(it.u[j], scl, lds, gl + LPR * j, KR, US, total);
             // keep each unit's LDS reads next to their use (hoisting them all
             // ahead of the arithmetic doubles the register footprint)
             __builtin_amdgcn_sched_barrier(0);
@@ -1005,10 +1015,10 @@ __device__ inline void gather_row_tiles(const LaunchParams& p, const MoeArgsOf<M
 #pragma unroll
         for (int i = 0; i < R; ++i)
 #pragma unroll
-            for (int b = 0; b < NB; ++b) total[i][b] = group_sum(total[i][b], 64);
-        if (lane == 63) {
+            for (int b = 0; b < NB; ++b) total[i][b] = group_sum(total[i][b], LPR);
+        if (gl == LPR - 1) {
             if constexpr (kPair) {
-                const int64_t r = t * RB + wave;
+                const int64_t r = t * RB + slot;
                 if (r < N) {
 #pragma unroll
                     for (int b = 0; b < NB; ++b) {
@@ -1023,7 +1033,7 @@ __device__ inline void gather_row_tiles(const LaunchParams& p, const MoeArgsOf<M
             } else {
 #pragma unroll
                 for (int i = 0; i < R; ++i) {
-                    const int64_t r = t * RB + R * wave + i;
+                    const int64_t r = t * RB + R * slot + i;
                     if (r < N) {
 #pragma unroll
                         for (int b = 0; b < NB; ++b) {
@@ -1079,8 +1089,8 @@ __device__ inline void gather_chunk(const LaunchParams& p, const MoeArgsOf<MODE>
             }
             __syncthreads();
             if constexpr (NUR > 0)
-                gather_row_tiles<DT, FMT, BITS, NB, NUR, MODE>(p, m, g, tile0, tile_end, w, sc,
-                                                               yrow, gmul, lds);
+                gather_row_tiles<DT, FMT, BITS, NB, row_nu(NUR), row_lpr(NUR), MODE>(
+                    p, m, g, tile0, tile_end, w, sc, yrow, gmul, lds);
             else
                 gather_tiles<DT, FMT, BITS, NB, R, MODE>(p, m, g, tile0, tile_end, w, sc, bi,
                                                          yrow, gmul, lds);
@@ -2168,9 +2178,10 @@ template <int DT, int FMT>
 constexpr int gather_row_nu(int nu) { return gather_row_ok<DT, FMT>() ? nu : 0; }
 template <int DT, int FMT>
 inline int gather_row_units(const LaunchParams& p, const Geom& g) {
-    if (!gather_row_ok<DT, FMT>()) return 0;
-    if (p.K <= 0 || p.K % 2048 != 0 || p.K / 2048 > 2 || g.ks < p.K || g.lpr != 64) return 0;
-    return (int)(p.K / 2048);
+    if (!gather_row_ok<DT, FMT>() || p.K <= 0 || g.ks < p.K) return 0;
+    if (g.lpr == 64 && (p.K == 2048 || p.K == 4096)) return (int)(p.K / 2048);
+    if (g.lpr == 16 && p.K == 1536) return 3;
+    return 0;
 }
 
 template <int DT, int FMT, int BITS>
@@ -2192,6 +2203,10 @@ int launch_gather_t(const LaunchParams& p, hipStream_t st) {
     else if (nur == 2)
         hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherPlain,
                                           gather_row_nu<DT, FMT>(2)>),
+                           grid, dim3(kThreads), lds, st, p, g, none);
+    else if (nur == 3)
+        hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherPlain,
+                                          gather_row_nu<DT, FMT>(3)>),
                            grid, dim3(kThreads), lds, st, p, g, none);
     else if (g.ks >= p.K && p.K > 0)
         hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kGatherRows, true>), grid,
@@ -2223,10 +2238,14 @@ int launch_moe_gate_up_t(const LaunchParams& p, const MoeArgs& m, hipStream_t st
                                            gather_row_nu<DT, FMT>(1)>
                : nur == 2 ? &gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherSwiglu,
                                            gather_row_nu<DT, FMT>(2)>
+               : nur == 3 ? &gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherSwiglu,
+                                           gather_row_nu<DT, FMT>(3)>
                           : &gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherSwiglu>;
     // the static slot lists ride on top of the dynamic x stage
-    static LdsGrant granted, granted1, granted2;
-    if (const int e = allow_lds(kern, lds, nur == 1 ? granted1 : nur == 2 ? granted2 : granted,
+    static LdsGrant granted, granted1, granted2, granted3;
+    if (const int e = allow_lds(kern, lds,
+                                nur == 1 ? granted1 : nur == 2 ? granted2
+                                         : nur == 3 ? granted3 : granted,
                                 32 * 1024))
         return e;
     hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, p, g, m);
