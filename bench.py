@@ -469,6 +469,7 @@ def time_chain(bmv, N: int = 2560, steps: int = 100) -> dict:
 
 GRAPH_LAUNCHES = 256     # launches captured in one HIP graph
 MIN_REPLAYS = 8          # graph replays timed (each on its own event pair)
+HEADLINE_WARM_S = 1.0    # untimed graph replays before the headline and ceilings
 
 
 def time_chain_cold(bmv, N: int = 2560, steps: int = 100) -> dict:
@@ -530,14 +531,19 @@ def time_chain_cold(bmv, N: int = 2560, steps: int = 100) -> dict:
             "pct_peak": round(100 * c.algorithmic_bytes() / graph / 1e3 / PEAK_HBM_GBPS, 1)}
 
 
-def time_case(runner: Runner, steps: int, warmup: int) -> dict:
+def time_case(runner: Runner, steps: int, warmup: int, warm_s: float = 0.0) -> dict:
     """Per-call time of back-to-back launches on one stream.
 
     us_per_call: a HIP graph of GRAPH_LAUNCHES launches (rotating weight
     copies) is replayed max(MIN_REPLAYS, ceil(steps / GRAPH_LAUNCHES))
     times, each replay between its own pair of events on the launch stream;
     the figure is the median replay's time per launch. `steps` is a minimum,
-    so a small --steps still times whole 256-launch graphs.
+    so a small --steps still times whole 256-launch graphs. With warm_s > 0
+    the graph is first replayed, untimed, for that many seconds, so the timed
+    replays run at the clocks of sustained work (a GPU that was idle, or
+    running the CPU-side checks, takes a while to reach them: the headline
+    measured 7.06 us as the first case of a run and 6.81 us after a minute of
+    other work, same library, same box).
     us_per_call_plain: max(steps, 512) plain launches, one event pair."""
     import torch
     stream = torch.cuda.current_stream()
@@ -569,6 +575,14 @@ def time_case(runner: Runner, steps: int, warmup: int) -> dict:
     reps = max(MIN_REPLAYS, -(-steps // GRAPH_LAUNCHES))
     g.replay()
     torch.cuda.synchronize()
+    warm_replays = 0
+    if warm_s > 0:
+        t_end = time.perf_counter() + warm_s
+        while time.perf_counter() < t_end:
+            for _ in range(8):
+                g.replay()
+            torch.cuda.synchronize()
+            warm_replays += 8
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
     for a, b in ev:
@@ -585,8 +599,9 @@ def time_case(runner: Runner, steps: int, warmup: int) -> dict:
         "us_per_call_plain": wall_us,
         "us_per_call": graph_us,
         "us_per_call_replays": [round(v, 3) for v in (per[0], per[-1])],
-        "timed": f"median of {reps} replays of a {GRAPH_LAUNCHES}-launch graph; "
-                 f"{n_plain} plain launches",
+        "timed": f"median of {reps} replays of a {GRAPH_LAUNCHES}-launch graph"
+                 + (f" after {warm_replays} untimed replays ({warm_s:g} s)" if warm_replays else "")
+                 + f"; {n_plain} plain launches",
         "gbps": runner.bytes / graph_us / 1e3,
         "gbps_plain": runner.bytes / wall_us / 1e3,
         "copies": runner.copies,
@@ -638,10 +653,16 @@ READ_DESIGNS = {
     13: "grid-stride, 256 x 8", 14: "grid-stride, 512 x 8",
     15: "rows: 8 lanes per 128-byte line", 16: "rows: 16x16 MFMA operand layout",
     17: "rows: the one-row QMV's loads (weights + scales)",
+    18: "rows: the one-row QMV's loads + its 2-byte-per-row write",
+    19: "rows: the one-row QMV's loads + write, XCD-chunked blocks",
 }
 
 
 CEILING_DESIGN = 0
+# The one-row QMV's own loads followed by the 2-byte-per-row write a QMV makes
+# (in its XCD-chunked block order): the same launch without the arithmetic.
+RW_CEILING_DESIGN = 19
+RW_CEILING_BYTES = 14336 * 2176
 
 
 class ReadRunner:
@@ -677,7 +698,7 @@ def read_designs(bmv, steps: int) -> list[dict]:
     for the one-row QMV's pattern; timed like the QMV (graph replays)."""
     out = []
     for d, name in READ_DESIGNS.items():
-        nbytes = 14336 * 2176 if d == 17 else 14336 * 2048 if d >= 15 else 31232000
+        nbytes = 14336 * 2176 if d >= 17 else 14336 * 2048 if d >= 15 else 31232000
         r = ReadRunner(bmv, nbytes, d)
         res = time_case(r, steps, 20)
         r.free()
@@ -1016,7 +1037,7 @@ def main() -> int:
         designs = read_designs(bmv, args.steps)
         head = workloads.mlp_up_case("mxfp4", 1)
         r = Runner(bmv, head)
-        q = time_case(r, args.steps, args.warmup)
+        q = time_case(r, args.steps, args.warmup, warm_s=HEADLINE_WARM_S)
         r.free()
         print(json.dumps({"read_designs": designs, "qmv_headline": q}), flush=True)
         return 0
@@ -1026,19 +1047,25 @@ def main() -> int:
     head = workloads.mlp_up_case("mxfp4", 1)
     check_once(bmv, head)
     runner = Runner(bmv, head)
-    res = time_case(runner, args.steps, args.warmup)
+    res = time_case(runner, args.steps, args.warmup, warm_s=HEADLINE_WARM_S)
     runner.free()
     print(f"[bench] headline mxfp4 B1: {json.dumps(res)}", file=sys.stderr, flush=True)
 
-    ceiling = None
+    ceiling = rw_ceiling = None
     if not args.no_ceiling:
         # The fastest read design measured at this byte count (one-shot grid,
         # 256 threads, two 16-byte loads per lane), timed like the QMV.
         rr = ReadRunner(bmv, head.algorithmic_bytes(), CEILING_DESIGN)
-        ceiling = time_case(rr, args.steps, args.warmup)
+        ceiling = time_case(rr, args.steps, args.warmup, warm_s=HEADLINE_WARM_S)
         rr.free()
         ceiling.update(design=CEILING_DESIGN, name=READ_DESIGNS[CEILING_DESIGN])
         print(f"[bench] stream-read ceiling: {json.dumps(ceiling)}", file=sys.stderr, flush=True)
+        rr = ReadRunner(bmv, RW_CEILING_BYTES, RW_CEILING_DESIGN)
+        rw_ceiling = time_case(rr, args.steps, args.warmup, warm_s=HEADLINE_WARM_S)
+        rr.free()
+        rw_ceiling.update(design=RW_CEILING_DESIGN, name=READ_DESIGNS[RW_CEILING_DESIGN])
+        print(f"[bench] read+write ceiling: {json.dumps(rw_ceiling)}", file=sys.stderr,
+              flush=True)
 
     cases = []
     if not args.headline_only:
@@ -1179,6 +1206,11 @@ def main() -> int:
             "gbps": round(ceiling["gbps"], 1), "us_per_call": round(ceiling["us_per_call"], 3),
             "design": ceiling["name"], "timed": ceiling["timed"],
             "qmv_frac_of_ceiling": round(res["gbps"] / ceiling["gbps"], 4)},
+        "read_write_ceiling": None if rw_ceiling is None else {
+            "us_per_call": round(rw_ceiling["us_per_call"], 3), "design": rw_ceiling["name"],
+            "bytes_read": RW_CEILING_BYTES, "bytes_written": 14336 * 2,
+            "timed": rw_ceiling["timed"],
+            "qmv_frac_of_ceiling": round(rw_ceiling["us_per_call"] / res["us_per_call"], 4)},
         "cases": cases,
     }
     print(json.dumps(line), flush=True)

@@ -170,6 +170,44 @@ __global__ __launch_bounds__(256) void read_rowpair_kernel(const uint8_t* __rest
     if (rr == 0x9E3779B9u) sink[blockIdx.x & 0xFFFF] = rr;
 }
 
+// The one-row QMV's loads (as read_rowpair_kernel) followed by the write a
+// QMV must make: each wave folds its 64 lanes' bytes (XOR across the wave, so
+// every load is used) and lane 63 writes one 4-byte word per row pair, i.e.
+// 2 bytes per row like a 16-bit y. With XCD, block b runs the row tile of the
+// one-row QMV's XCD-chunked order (the eight blocks an XCD receives from each
+// group of 64 own consecutive tiles).
+template <bool XCD>
+__global__ __launch_bounds__(256) void read_rowpair_write_kernel(const uint8_t* __restrict__ p,
+                                                                 int64_t rows,
+                                                                 uint32_t* __restrict__ out) {
+    const int lane = threadIdx.x & 63;
+    int64_t b = blockIdx.x;
+    if (XCD) {
+        const int64_t span = 64, grid = gridDim.x;
+        if (b < (grid / span) * span) {
+            const int64_t r = b % span;
+            b = (b - r) + (r % 8) * 8 + r / 8;
+        }
+    }
+    const int64_t r0 = (b * 4 + (threadIdx.x >> 6)) * 2;
+    const uint8_t* sc = p + rows * 2048;
+    v4u a = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t r = r0 + i < rows ? r0 + i : rows - 1;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            a ^= __builtin_nontemporal_load(
+                reinterpret_cast<const v4u*>(p + r * 2048 + 1024 * u + 16 * lane));
+            a.x ^= __builtin_nontemporal_load(sc + r * 128 + 64 * u + lane);
+        }
+    }
+    uint32_t rr = a.x ^ a.y ^ a.z ^ a.w;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) rr ^= (uint32_t)__shfl_xor((int)rr, off);
+    if (lane == 63 && r0 + 1 < rows) out[r0 / 2] = rr;
+}
+
 template <class Kern>
 int launch_blocks(Kern k, int64_t blocks, int threads, hipStream_t st, const v4u* p, int64_t n,
                   uint32_t* sink) {
@@ -218,6 +256,18 @@ extern "C" int qmv_bench_read_design(void* stream, const void* buf, int64_t byte
             if (bytes % (2176 * 8)) return (int)hipErrorInvalidValue;
             const int64_t rows = bytes / 2176;   // 2048 weight + 128 scale bytes per row
             hipLaunchKernelGGL(read_rowpair_kernel, dim3((unsigned)(rows / 8)), dim3(256), 0, st,
+                               static_cast<const uint8_t*>(buf), rows, sink);
+            return (int)hipGetLastError();
+        }
+        case 18:
+        case 19: {
+            // as 17, plus a 2-byte-per-row write to sink (65536 words: rows <= 131072)
+            if (bytes % (2176 * 8)) return (int)hipErrorInvalidValue;
+            const int64_t rows = bytes / 2176;
+            if (rows > 2 * 65536) return (int)hipErrorInvalidValue;
+            auto* k = design == 18 ? read_rowpair_write_kernel<false>
+                                   : read_rowpair_write_kernel<true>;
+            hipLaunchKernelGGL(k, dim3((unsigned)(rows / 8)), dim3(256), 0, st,
                                static_cast<const uint8_t*>(buf), rows, sink);
             return (int)hipGetLastError();
         }

@@ -8,7 +8,7 @@
  *                           issued before any is used, and folds them into
  *                           one word per block: the measured ceiling of a
  *                           read-only stream of that size.
- *   qmv_bench_read_design   reads `bytes` once with one of 18 read designs,
+ *   qmv_bench_read_design   reads `bytes` once with one of 20 read designs,
  *                           to find the fastest single launch for a size:
  *                           0-5 one-shot grids (threads x loads per lane:
  *                           256x2, 256x4, 256x8, 512x4, 1024x2, 64x8), 6 the
@@ -22,13 +22,20 @@
  *                           one-row QMV's loads over [rows][2048] weight
  *                           bytes then [rows][128] scale bytes (two rows per
  *                           wave, 64 lanes x 16 bytes per row and a scale
- *                           byte per lane; bytes a multiple of 8 x 2176).
+ *                           byte per lane; bytes a multiple of 8 x 2176),
+ *                           18-19 design 17 followed by the write a QMV
+ *                           makes (each wave folds its bytes and writes one
+ *                           4-byte word per row pair to `sink`, 2 bytes per
+ *                           row; at most 131072 rows), 19 in the one-row
+ *                           QMV's XCD-chunked block order.
  *   qmv_bench_copy          copies `bytes` (a plain copy of known size, for
  *                           calibrating hardware byte counters).
  *
  * Pointers are device pointers; `bytes` must be a multiple of 16 and buffers
- * 16-byte aligned. `sink` must hold 65536 uint32 (a word is written only
- * in the practically impossible case that the fold equals a fixed pattern). Asynchronous on `stream`. Returns 0 or a hipError_t.
+ * 16-byte aligned. `sink` must hold 65536 uint32 (designs 0-17 write a word
+ * only in the practically impossible case that the fold equals a fixed
+ * pattern; 18-19 write rows / 2 words). Asynchronous on `stream`. Returns 0
+ * or a hipError_t.
  */
 #ifndef QMV_BENCH_H
 #define QMV_BENCH_H
