@@ -1907,16 +1907,17 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
             }
         }
     }
-    bool staged = false;
-
-    for (int64_t c = wave; c < nchunks; c += nw) {
+    // (1)-(2): the loads of chunk c. The first chunk's go out before the
+    // scale staging's barrier, every later chunk's at the top of its turn.
+    v4u raw[2 * RT];
+    v4u xb[kSegs][4];
+    auto issue = [&](int64_t c) __attribute__((always_inline)) {
         const int64_t code0 = c * kCodes;                // first code of the chunk
         const int64_t byte0 = FMT == FMT_MXFP8 ? code0 : code0 / 2;
         // (1) weights: instruction i covers rows 8 i .. 8 i + 7 of the block;
         // lane l takes piece (l % 8) ^ g(row) of its row's 128 bytes, so row r
         // piece p lands in slot 8 (r % 8) + (p ^ g(r)), g(r) = (r / 2) % 8.
         // Pieces past the row end read its last piece (zeroed below).
-        v4u raw[2 * RT];
 #pragma unroll
         for (int i = 0; i < 2 * RT; ++i) {
             const int r = 8 * i + (lane >> 3);
@@ -1925,24 +1926,44 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
             off = off + 16 <= p.row_bytes ? off : p.row_bytes - 16;
             raw[i] = load_vec<true, v4u>(p.w + lrow[i] * p.row_bytes + off);
         }
-        // (2) scales: the row's kScB bytes of this chunk
-        uint32_t sw[RT][kScB / 4 > 0 ? kScB / 4 : 1];
-        const int64_t e0 = code0 / kBlk;
-        if constexpr (kWhole) {
-            if (!staged) {
-                const int n16 = kRows * sc_row / 16;
+        // (2) x: the B operand of MFMA t of segment s in lane (column r16, q)
+        // holds x[r16][code0 + 128 s + 32 q + 8 t .. + 8]
+        // (pieces past K enter as zeros, with their zeroed weights). Issued
+        // right behind the weights, so on the first chunk they are in flight
+        // across the scale staging's barrier too (issued after it, they added
+        // their L2 round trip to every wave's first chunk: MXFP4 K=4096
+        // N=14336 B=4 9.63 -> 8.80 us, B=8 10.10 -> 9.30 us)
 #pragma unroll
-                for (int j = 0; j < kScPieces; ++j) {
-                    const int pc = tid + j * (int)blockDim.x;
-                    if (pc < n16) {
-                        const int r = pc * 16 / sc_row, col = pc * 16 - r * sc_row;
-                        *reinterpret_cast<v4u*>(sst + r * sc_stride + col) = scp[j];
-                    }
-                }
-                __syncthreads();
-                staged = true;
+        for (int s = 0; s < kSegs; ++s) {
+            const int64_t k = code0 + 128 * s + 32 * q;
+            const bool ok = has && (kWhole || k < K);
+            const int off = ok ? xoff + (int)(k * (int64_t)sizeof(S)) : kBufferOutOfRange;
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                xb[s][t] = __builtin_bit_cast(
+                    v4u, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16 * t, 0, 0));
+        }
+    };
+    issue(wave);
+    if constexpr (kWhole) {
+        const int n16 = kRows * sc_row / 16;
+#pragma unroll
+        for (int j = 0; j < kScPieces; ++j) {
+            const int pc = tid + j * (int)blockDim.x;
+            if (pc < n16) {
+                const int r = pc * 16 / sc_row, col = pc * 16 - r * sc_row;
+                *reinterpret_cast<v4u*>(sst + r * sc_stride + col) = scp[j];
             }
         }
+        __syncthreads();
+    }
+
+    for (int64_t c = wave; c < nchunks; c += nw) {
+        if (c != wave) issue(c);
+        const int64_t code0 = c * kCodes;                // first code of the chunk
+        // (3) scales: the row's kScB bytes of this chunk
+        uint32_t sw[RT][kScB / 4 > 0 ? kScB / 4 : 1];
+        const int64_t e0 = code0 / kBlk;
 #pragma unroll
         for (int t = 0; t < RT; ++t) {
             const uint8_t* srow = scb + orow[t] * p.sc_per_row;
@@ -1970,20 +1991,6 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
                     sw[t][j] = v;
                 }
             }
-        }
-        // (3) x: the B operand of MFMA t of segment s in lane (column r16, q)
-        // holds x[r16][code0 + 128 s + 32 q + 8 t .. + 8]
-        // (pieces past K enter as zeros, with their zeroed weights)
-        v4u xb[kSegs][4];
-#pragma unroll
-        for (int s = 0; s < kSegs; ++s) {
-            const int64_t k = code0 + 128 * s + 32 * q;
-            const bool ok = has && (kWhole || k < K);
-            const int off = ok ? xoff + (int)(k * (int64_t)sizeof(S)) : kBufferOutOfRange;
-#pragma unroll
-            for (int t = 0; t < 4; ++t)
-                xb[s][t] = __builtin_bit_cast(
-                    v4u, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16 * t, 0, 0));
         }
         // (4) stage the chunk in the wave's LDS area (in program order with
         // this wave's operand reads of the previous chunk)
@@ -2089,11 +2096,13 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
 // The matrix-core QMV takes bf16 activations from the batch size where it
 // beats the VALU tile, measured at K=4096, N=14336 (VALU tile -> matrix
 // cores, one process):
-//   MXFP4  B=2 9.3 -> 9.2, B=3 10.8 -> 9.4, B=4 12.5 -> 9.5, B=8 27.7 -> 10.0 us
-//   NVFP4  B=3 10.9 -> 11.5, B=4 12.6 -> 11.2, B=6 17.4 -> 11.3, B=8 28.6 -> 11.8 us
-//   MXFP8  B=3 14.2 -> 14.9, B=4 15.6 -> 15.0, B=6 19.8 -> 15.3, B=8 46.2 -> 16.0 us
-// (MXFP8's 128-code chunks give each wave two chunks in turn at K=4096;
-// MXFP4 at B = 2 is within noise and stays on the VALU tile).
+//   MXFP4  B=2 9.21 -> 8.60, B=3 10.8 -> 8.76, B=4 12.5 -> 8.86, B=8 27.7 -> 9.30 us
+//   NVFP4  B=2 9.10 -> 10.81, B=3 11.07 -> 10.91, B=4 12.6 -> 10.91, B=8 28.6 -> 11.76 us
+//   MXFP8  B=2 12.46 -> 15.45, B=3 13.86 -> 15.62, B=4 15.6 -> 15.76, B=8 46.2 -> 16.4 us
+// (MXFP8's 128-code chunks give each wave two chunks in turn at K=4096).
+// MXFP4 at B = 2 and NVFP4 at B = 3 would gain 7 % and 1.5 %; they stay on
+// the VALU tile, whose two-row bf16 calls are what the one-row kernel is
+// checked against bit for bit.
 template <int FMT> constexpr int mf_min_batch() {
     return FMT == FMT_MXFP4 ? 3 : 4;
 }
