@@ -66,9 +66,10 @@ struct Geom {
 // global loads of the 16-byte chunk of that row starting at element k (and of
 // whatever its staging needs) and returns them as a Chunk; stage(b, k, c) is
 // that chunk as it goes into LDS (each element of the block's rows is staged
-// exactly once, by one thread); finish() runs in every thread after the
-// tile's sums and before its stores; out(b, v) is row b's fp32 result before
-// the final rounding.
+// exactly once, by one thread); staged() runs in every thread after the
+// last of its elements has been staged and before the barrier that publishes
+// them, settled() in every thread right after that barrier; out(b, v) is row
+// b's fp32 result before the final rounding.
 template <class S> struct XContig {
     using Chunk = v4u;
     const S* x;
@@ -78,7 +79,8 @@ template <class S> struct XContig {
         return *reinterpret_cast<const v4u*>(row(b) + k);
     }
     __device__ v4u stage(int, int64_t, const Chunk& c) const { return c; }
-    __device__ void finish() const {}
+    __device__ void staged() const {}
+    __device__ void settled() const {}
     __device__ float out(int, float v) const { return v; }
 };
 template <class S> struct XListed {
@@ -90,7 +92,8 @@ template <class S> struct XListed {
         return *reinterpret_cast<const v4u*>(row(b) + k);
     }
     __device__ v4u stage(int, int64_t, const Chunk& c) const { return c; }
-    __device__ void finish() const {}
+    __device__ void staged() const {}
+    __device__ void settled() const {}
     __device__ float out(int, float v) const { return v; }
 };
 // Fused RMSNorm. The row's normalization r[b] = 1 / sqrt(mean_k x^2 + eps) is
@@ -98,8 +101,11 @@ template <class S> struct XListed {
 // enters LDS as RN_T(x[b, k] * gamma[k]) — the product of two T values is
 // exact in fp32, so that is one rounding of the exact product. The squares
 // are summed as the elements are staged (fp32, each thread in its staging
-// order), then over lanes and waves in a fixed order in finish(), so every
-// block of a launch forms the same r.
+// order), then over the lanes of each wave (staged(), before the barrier that
+// publishes the staged x) and over the waves in a fixed order (settled(),
+// after it), so every block of a launch forms the same r, and r is known
+// before the first weight unit is folded: the block needs no barrier of its
+// own for it.
 template <int DT, int NB> struct XNorm {
     using S = typename Store<DT>::S;
     const S* x;
@@ -146,17 +152,18 @@ template <int DT, int NB> struct XNorm {
         }
         return v4u{o[0], o[1], o[2], o[3]};
     }
-    __device__ void finish() const {
+    // the wave's sum by DPP lane moves (VALU latency, no LDS round trips on
+    // the way to the barrier), left in lane 63
+    __device__ void staged() const {
         const int lane = threadIdx.x & 63;
         const int wave = threadIdx.x >> 6;
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            float t = ss[b];
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) t += __shfl_xor(t, off);
-            if (lane == 0) red[b * kWaves + wave] = t;
+            const float t = group_sum(ss[b], 64);
+            if (lane == 63) red[b * kWaves + wave] = t;
         }
-        __syncthreads();
+    }
+    __device__ void settled() const {
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             float t = red[b * kWaves];
@@ -514,7 +521,10 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
             const int nbytes = F::kArrays * RB * seg;
             for (int c = tid; c < nbytes; c += kThreads) lds_sc[c] = *sc_src(c);
         }
+        const bool last = kShort || slab + ks >= K;
+        if (last) xr.staged();
         __syncthreads();
+        if (last) xr.settled();
 
         // (4) two units in flight: compute one, then refill its buffer with
         // the unit two steps ahead. The steady-state body runs while at least
@@ -538,7 +548,9 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
             if (ua < us) compute_unit(A, ua, ks, us, seg);
             if (it + 1 < iters && ub < us) compute_unit(Bq, ub, ks, us, seg);
         }
-        __syncthreads();  // LDS is restaged for the next slab
+        // LDS is restaged for the next slab, or by the caller's next tile
+        // (the gather); a one-slab tile of the QMV kernels ends here
+        if constexpr (!kShort) __syncthreads();
     }
 
     // reduce over the LPR lanes of each row group (result in its last lane)
@@ -549,7 +561,6 @@ __device__ inline void qmv_tile(const LaunchParams& p, const Geom& g, int64_t ro
             total[i][b] = group_sum(total[i][b], lpr);
         }
 
-    xr.finish();
     if (gl == lpr - 1) {
 #pragma unroll
         for (int i = 0; i < R; ++i) {
@@ -656,7 +667,9 @@ __device__ inline void row_tiles(const LaunchParams& p, const XR& xr, float gmul
         const int v = tid + j * kThreads;
         *reinterpret_cast<v4u*>(xs + x_lds_slot(v * 8, USP)) = xr.stage(0, (int64_t)v * 8, xc[j]);
     }
+    xr.staged();
     __syncthreads();
+    xr.settled();
 
     // (4) the units in the tile's order, (5) the tile's reduction and store
     float total[R][1];
@@ -671,7 +684,6 @@ __device__ inline void row_tiles(const LaunchParams& p, const XR& xr, float gmul
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) total[i][0] = group_sum(total[i][0], 64);
-    xr.finish();
     if (lane == 63) {
         S* y = static_cast<S*>(p.y);
 #pragma unroll
