@@ -982,6 +982,7 @@ template <int DT, int FMT, int BITS, int NB, int NU, int LPR, int MODE = kGather
 __device__ inline void gather_row_tiles(const LaunchParams& p, const MoeArgsOf<MODE>& m,
                                         const Geom& g, int64_t tile0, int64_t tile_end,
                                         const uint8_t* __restrict__ w, const void* sc,
+                                        const void* bi,
                                         typename Store<DT>::S* const (&yrow)[NB], float gmul,
                                         const typename Store<DT>::S* lds) {
     using F = Fmt<FMT, BITS>;
@@ -1006,9 +1007,11 @@ __device__ inline void gather_row_tiles(const LaunchParams& p, const MoeArgsOf<M
     const int64_t sc_row_bytes = p.sc_per_row * F::template elem_bytes<DT>();
     const uint8_t* w_of[2] = {w, w};
     const uint8_t* sc_of[2] = {static_cast<const uint8_t*>(sc), static_cast<const uint8_t*>(sc)};
+    const uint8_t* bi_of[2] = {static_cast<const uint8_t*>(bi), static_cast<const uint8_t*>(bi)};
     if constexpr (kPair) {
         w_of[1] = m.w2;
         sc_of[1] = static_cast<const uint8_t*>(m.scales2);
+        bi_of[1] = static_cast<const uint8_t*>(m.biases2);
     }
     // row of operand row i in tile t (rows past N re-read row N - 1)
     auto row_of = [&](int64_t t, int i) __attribute__((always_inline)) {
@@ -1021,11 +1024,13 @@ __device__ inline void gather_row_tiles(const LaunchParams& p, const MoeArgsOf<M
             const int64_t r = row_of(t, i);
             const int mi = kPair ? i : 0;
             const uint8_t* wr = w_of[mi] + r * p.row_bytes;
-            const uint8_t* sr = sc_of[mi] + r * sc_row_bytes;
+            // (an expert's scale arrays hold at most N x 256 bytes: 32-bit offsets)
+            const uint32_t so = (uint32_t)(r * sc_row_bytes);
 #pragma unroll
             for (int j = 0; j < NU; ++j) {
                 load_words<W>(wr + (gl + LPR * j) * kUnitBytes, it.u[j].d[i]);
-                it.raw[j][i] = F::template global_raw<DT>(sr, nullptr, 0u, gl + LPR * j, 0);
+                it.raw[j][i] = F::template global_raw<DT>(sc_of[mi], bi_of[mi], so, gl + LPR * j,
+                                                          g.glog2);
             }
         }
     };
@@ -1123,7 +1128,7 @@ __device__ inline void gather_chunk(const LaunchParams& p, const MoeArgsOf<MODE>
             __syncthreads();
             if constexpr (NUR > 0)
                 gather_row_tiles<DT, FMT, BITS, NB, row_nu(NUR), row_lpr(NUR), MODE>(
-                    p, m, g, tile0, tile_end, w, sc, yrow, gmul, lds);
+                    p, m, g, tile0, tile_end, w, sc, bi, yrow, gmul, lds);
             else
                 gather_tiles<DT, FMT, BITS, NB, R, MODE>(p, m, g, tile0, tile_end, w, sc, bi,
                                                          yrow, gmul, lds);
@@ -2208,19 +2213,21 @@ inline int64_t gather_tiles_per_block(const LaunchParams& p, int64_t n_tiles, in
 }
 
 // Units per lane per row of the gather's one-row-style tile loop for this
-// launch (K = 2048 * NU, NU = 1 or 2; 16-bit activations; MXFP4 / NVFP4 /
-// MXFP8; one slab of K, 64 lanes per row), or 0 for the generic loop. For
-// the other instantiations gather_row_nu folds the template argument to 0,
-// so no extra kernel is built for them.
-template <int DT, int FMT>
+// launch (K = 2048 * NU, NU = 1 or 2, 64 lanes per row, or K = 1536 with 16
+// lanes per row; 16-bit activations; MXFP4 / NVFP4 / MXFP8 or 4-bit affine
+// codes; one slab of K), or 0 for the generic loop. For the other
+// instantiations gather_row_nu folds the template argument to 0, so no extra
+// kernel is built for them.
+template <int DT, int FMT, int BITS>
 constexpr bool gather_row_ok() {
-    return DT != DT_F32 && (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8);
+    return DT != DT_F32 && (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8 ||
+                            (FMT == FMT_AFFINE && BITS == 4));
 }
-template <int DT, int FMT>
-constexpr int gather_row_nu(int nu) { return gather_row_ok<DT, FMT>() ? nu : 0; }
-template <int DT, int FMT>
+template <int DT, int FMT, int BITS>
+constexpr int gather_row_nu(int nu) { return gather_row_ok<DT, FMT, BITS>() ? nu : 0; }
+template <int DT, int FMT, int BITS>
 inline int gather_row_units(const LaunchParams& p, const Geom& g) {
-    if (!gather_row_ok<DT, FMT>() || p.K <= 0 || g.ks < p.K) return 0;
+    if (!gather_row_ok<DT, FMT, BITS>() || p.K <= 0 || g.ks < p.K) return 0;
     if (g.lpr == 64 && (p.K == 2048 || p.K == 4096)) return (int)(p.K / 2048);
     if (g.lpr == 16 && p.K == 1536) return 3;
     return 0;
@@ -2237,18 +2244,18 @@ int launch_gather_t(const LaunchParams& p, hipStream_t st) {
     g.tiles_per_block = (int)tpb;
     const dim3 grid((unsigned)((n_tiles + tpb - 1) / tpb), (unsigned)(p.n_experts + 1));
     const size_t lds = stage_bytes<DT, FMT, BITS>(p, g);
-    const int nur = gather_row_units<DT, FMT>(p, g);
+    const int nur = gather_row_units<DT, FMT, BITS>(p, g);
     if (nur == 1)
         hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherPlain,
-                                          gather_row_nu<DT, FMT>(1)>),
+                                          gather_row_nu<DT, FMT, BITS>(1)>),
                            grid, dim3(kThreads), lds, st, p, g, none);
     else if (nur == 2)
         hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherPlain,
-                                          gather_row_nu<DT, FMT>(2)>),
+                                          gather_row_nu<DT, FMT, BITS>(2)>),
                            grid, dim3(kThreads), lds, st, p, g, none);
     else if (nur == 3)
         hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherPlain,
-                                          gather_row_nu<DT, FMT>(3)>),
+                                          gather_row_nu<DT, FMT, BITS>(3)>),
                            grid, dim3(kThreads), lds, st, p, g, none);
     else if (g.ks >= p.K && p.K > 0)
         hipLaunchKernelGGL((gather_kernel<DT, FMT, BITS, kGatherRows, true>), grid,
@@ -2275,13 +2282,13 @@ int launch_moe_gate_up_t(const LaunchParams& p, const MoeArgs& m, hipStream_t st
     const int64_t tpb = gather_tiles_per_block(p, n_tiles, kGatherPairBlocks);
     g.tiles_per_block = (int)tpb;
     const dim3 grid((unsigned)((n_tiles + tpb - 1) / tpb), (unsigned)(p.n_experts + 1));
-    const int nur = gather_row_units<DT, FMT>(p, g);
+    const int nur = gather_row_units<DT, FMT, BITS>(p, g);
     auto* kern = nur == 1 ? &gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherSwiglu,
-                                           gather_row_nu<DT, FMT>(1)>
+                                           gather_row_nu<DT, FMT, BITS>(1)>
                : nur == 2 ? &gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherSwiglu,
-                                           gather_row_nu<DT, FMT>(2)>
+                                           gather_row_nu<DT, FMT, BITS>(2)>
                : nur == 3 ? &gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherSwiglu,
-                                           gather_row_nu<DT, FMT>(3)>
+                                           gather_row_nu<DT, FMT, BITS>(3)>
                           : &gather_kernel<DT, FMT, BITS, kGatherRows, true, kGatherSwiglu>;
     // the static slot lists ride on top of the dynamic x stage
     static LdsGrant granted, granted1, granted2, granted3;
