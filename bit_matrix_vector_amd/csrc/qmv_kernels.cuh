@@ -1736,11 +1736,21 @@ int launch_qmv_norm_r(const LaunchParams& p, const NormArgs& na, hipStream_t st)
     return (int)hipGetLastError();
 }
 
-// The fused RMSNorm + QMV takes four rows per lane group while that still
-// launches 2048 waves, else two: every block redoes the row's x work (x *
-// gamma and the squares), so fewer, taller blocks do less of it.
+template <int FMT> inline bool use_mfma_qmv(const LaunchParams& p);
+template <int DT, int FMT, bool NORM>
+int launch_qmv_mfma(const LaunchParams& p, const NormArgs& na, hipStream_t st);
+
+// The fused RMSNorm + QMV takes the matrix cores where the plain QMV does
+// (bf16 batches of the MX formats from mf_min_batch rows); on the VALU tile it
+// takes four rows per lane group while that still launches 2048 waves, else
+// two: every block redoes the row's x work (x * gamma and the squares), so
+// fewer, taller blocks do less of it.
 template <int DT, int FMT, int BITS>
 int launch_qmv_norm_t(const LaunchParams& p, const NormArgs& na, hipStream_t st) {
+    if constexpr (DT == DT_BF16 &&
+                  (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
+        if (use_mfma_qmv<FMT>(p)) return launch_qmv_mfma<DT, FMT, true>(p, na, st);
+    }
     if constexpr (DT != DT_F32 && (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
         if (p.B == 1 && p.N > 0 && p.K > 0 && p.K % 2048 == 0 &&
             p.K / 2048 <= row_units_max<FMT>()) {
@@ -1848,8 +1858,17 @@ inline int mfma_waves(const LaunchParams& p, int max_waves) {
 // kWhole: K is a multiple of the chunk and the scale rows allow vector loads
 // (every chunk is whole); otherwise codes past K are zeroed by selects and
 // the scale bytes are loaded one by one.
-template <int DT, int FMT, bool kWhole>
-__global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_kernel(LaunchParams p) {
+//
+// NORM: the fused RMSNorm in front (y[b] = r[b] * (W . RN_T(x[b] * gamma)),
+// r[b] = 1 / sqrt(mean_k x[b, k]^2 + eps)). Each x piece is loaded with the
+// matching gamma piece and enters the B operand as RN_T(x * gamma) (one
+// rounding of the exact product, as the VALU tile stages it); each lane sums
+// the squares of its x values (fp32, in its chunk and piece order), and the
+// block adds the lanes' sums over the four lane quarters and the waves in a
+// fixed order with the partial tiles, so every block forms the same r[b],
+// which multiplies the row's sum before the NVFP4 global scale.
+template <int DT, int FMT, bool kWhole, bool NORM>
+__device__ inline void mfma_tile(const LaunchParams& p, const NormArgs& na) {
     static_assert(FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8, "block-scaled only");
     using S = typename Store<DT>::S;
     using V8 = typename Mfma16<DT>::v8;
@@ -1894,6 +1913,11 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
         const_cast<S*>(x), 0, (int)(B * K * (int64_t)sizeof(S)), kBufferWord3);
     const bool has = r16 < B;
     const int xoff = (int)(r16 * K * (int64_t)sizeof(S));
+    // gamma [K] through its own resource (NORM)
+    const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(NORM ? na.gamma : static_cast<const void*>(x)), 0,
+        (int)(K * (int64_t)sizeof(S)), kBufferWord3);
+    float ss = 0.0f;   // NORM: this lane's sum of x^2 (column r16)
 
     mf_f32x4_t acc[RT];
 #pragma unroll
@@ -1928,6 +1952,7 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
     // scale staging's barrier, every later chunk's at the top of its turn.
     v4u raw[2 * RT];
     v4u xb[kSegs][4];
+    v4u gb[NORM ? kSegs : 1][4];
     auto issue = [&](int64_t c) __attribute__((always_inline)) {
         const int64_t code0 = c * kCodes;                // first code of the chunk
         const int64_t byte0 = FMT == FMT_MXFP8 ? code0 : code0 / 2;
@@ -1959,6 +1984,13 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
             for (int t = 0; t < 4; ++t)
                 xb[s][t] = __builtin_bit_cast(
                     v4u, __builtin_amdgcn_raw_buffer_load_b128(xrs, off + 16 * t, 0, 0));
+            if constexpr (NORM) {
+                const int goff = ok ? (int)(k * (int64_t)sizeof(S)) : kBufferOutOfRange;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    gb[s][t] = __builtin_bit_cast(
+                        v4u, __builtin_amdgcn_raw_buffer_load_b128(grs, goff + 16 * t, 0, 0));
+            }
         }
     };
     issue(wave);
@@ -2013,6 +2045,28 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
         // this wave's operand reads of the previous chunk)
 #pragma unroll
         for (int i = 0; i < 2 * RT; ++i) *reinterpret_cast<v4u*>(wl + 1024 * i + 16 * lane) = raw[i];
+        if constexpr (NORM) {
+            // the x pieces become RN_T(x * gamma); their squares go into ss
+#pragma unroll
+            for (int s = 0; s < kSegs; ++s)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const uint32_t xv[4] = {xb[s][t].x, xb[s][t].y, xb[s][t].z, xb[s][t].w};
+                    const uint32_t gv[4] = {gb[s][t].x, gb[s][t].y, gb[s][t].z, gb[s][t].w};
+                    uint32_t o[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float x0 = Store<DT>::bits_to_f32(xv[j] & 0xFFFFu);
+                        const float x1 = Store<DT>::bits_to_f32(xv[j] >> 16);
+                        ss = fmaf(x0, x0, ss);
+                        ss = fmaf(x1, x1, ss);
+                        const f32x2 pr = {x0 * Store<DT>::bits_to_f32(gv[j] & 0xFFFFu),
+                                          x1 * Store<DT>::bits_to_f32(gv[j] >> 16)};
+                        o[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
+                    }
+                    xb[s][t] = v4u{o[0], o[1], o[2], o[3]};
+                }
+        }
         // (5) the MFMAs
 #pragma unroll
         for (int s = 0; s < kSegs; ++s) {
@@ -2092,11 +2146,16 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
     // red[(w * 16 RT + m) * 8 + b]; lane (r16, q) holds rows 4 q .. 4 q + 3 of each tile
     float* red = reinterpret_cast<float*>(smem);
     __syncthreads();
+    // NORM: lane (q, r16)'s sum of squares at ssl[(w * 4 + q) * 16 + r16],
+    // after the partial tiles (inside the weight areas: 24 kRows floats per
+    // wave are free there)
+    float* ssl = red + nw * kRows * 8;
     if (has) {
 #pragma unroll
         for (int t = 0; t < RT; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) red[(wave * kRows + 16 * t + 4 * q + e) * 8 + r16] = acc[t][e];
+        if constexpr (NORM) ssl[(wave * 4 + q) * 16 + r16] = ss;
     }
     __syncthreads();
     const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
@@ -2105,9 +2164,27 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_k
         if (row0 + m >= N) continue;
         float v = red[m * 8 + b];
         for (int w = 1; w < nw; ++w) v += red[(w * kRows + m) * 8 + b];
+        if constexpr (NORM) {
+            float t2 = 0.0f;
+            for (int w = 0; w < nw; ++w)
+#pragma unroll
+                for (int qq = 0; qq < 4; ++qq) t2 += ssl[(w * 4 + qq) * 16 + b];
+            v = v * (1.0f / sqrtf(t2 / (float)K + na.eps));
+        }
         if constexpr (FMT == FMT_NVFP4) v = v * gmul;
         static_cast<S*>(p.y)[(int64_t)b * N + row0 + m] = Store<DT>::from_f32(v);
     }
+}
+
+template <int DT, int FMT, bool kWhole>
+__global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_kernel(LaunchParams p) {
+    mfma_tile<DT, FMT, kWhole, false>(p, NormArgs{});
+}
+
+template <int DT, int FMT, bool kWhole>
+__global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_norm_kernel(
+    LaunchParams p, NormArgs na) {
+    mfma_tile<DT, FMT, kWhole, true>(p, na);
 }
 
 // The matrix-core QMV takes bf16 activations from the batch size where it
@@ -2130,8 +2207,8 @@ inline bool use_mfma_qmv(const LaunchParams& p) {
            p.B * p.K * 2 < (int64_t)kBufferOutOfRange;
 }
 
-template <int DT, int FMT>
-int launch_qmv_mfma(const LaunchParams& p, hipStream_t st) {
+template <int DT, int FMT, bool NORM>
+int launch_qmv_mfma(const LaunchParams& p, const NormArgs& na, hipStream_t st) {
     constexpr int kScB = mf_chunk_codes<FMT>() / (FMT == FMT_NVFP4 ? 16 : 32);
     // whole chunks, and scale rows the block can stage in 16-byte pieces
     bool whole = p.K % mf_chunk_codes<FMT>() == 0 && p.sc_per_row % 16 == 0 &&
@@ -2150,10 +2227,19 @@ int launch_qmv_mfma(const LaunchParams& p, hipStream_t st) {
     // rows x 8 columns x 4 bytes); whole instances add the staged scale rows
     const size_t lds = (size_t)nw * rows * kMfChunkBytes +
                        (whole ? (size_t)rows * (size_t)(p.sc_per_row + 16) : 0);
-    auto* kern = whole ? &qmv_mfma_kernel<DT, FMT, true> : &qmv_mfma_kernel<DT, FMT, false>;
     static LdsGrant granted_w, granted_p;
-    if (const int e = allow_lds(kern, lds, whole ? granted_w : granted_p)) return e;
-    hipLaunchKernelGGL(kern, dim3((unsigned)((p.N + rows - 1) / rows)), dim3(64 * nw), lds, st, p);
+    const dim3 grid((unsigned)((p.N + rows - 1) / rows));
+    if constexpr (NORM) {
+        auto* kern = whole ? &qmv_mfma_norm_kernel<DT, FMT, true>
+                           : &qmv_mfma_norm_kernel<DT, FMT, false>;
+        if (const int e = allow_lds(kern, lds, whole ? granted_w : granted_p)) return e;
+        hipLaunchKernelGGL(kern, grid, dim3(64 * nw), lds, st, p, na);
+    } else {
+        (void)na;
+        auto* kern = whole ? &qmv_mfma_kernel<DT, FMT, true> : &qmv_mfma_kernel<DT, FMT, false>;
+        if (const int e = allow_lds(kern, lds, whole ? granted_w : granted_p)) return e;
+        hipLaunchKernelGGL(kern, grid, dim3(64 * nw), lds, st, p);
+    }
     return (int)hipGetLastError();
 }
 
@@ -2161,7 +2247,7 @@ template <int DT, int FMT, int BITS>
 int launch_qmv_t(const LaunchParams& p, hipStream_t st) {
     if constexpr (DT == DT_BF16 &&
                   (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
-        if (use_mfma_qmv<FMT>(p)) return launch_qmv_mfma<DT, FMT>(p, st);
+        if (use_mfma_qmv<FMT>(p)) return launch_qmv_mfma<DT, FMT, false>(p, NormArgs{}, st);
     }
     if constexpr (DT != DT_F32 && (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
         if (p.B == 1 && p.N > 0 && p.K > 0 && p.K % 2048 == 0 &&

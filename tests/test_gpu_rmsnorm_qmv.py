@@ -141,3 +141,46 @@ def test_rmsnorm_qmv_k_zero(bmv):
     bmv.qmv_rmsnorm_qmv(x, wt, g, 1e-6, y=y)
     torch.cuda.synchronize()
     assert torch.count_nonzero(y).item() == 0
+
+
+# bf16 batches of the MX formats from the matrix-core threshold on (MXFP4 3,
+# NVFP4 and MXFP8 4) run the fused norm on the matrix cores: whole chunks
+# (K = 4096) and a partial last chunk (K = 1088), tail rows (N = 300)
+@pytest.mark.parametrize("fmt,bits,group", [("mxfp4", 4, 32), ("nvfp4", 4, 16), ("mxfp8", 8, 32)])
+@pytest.mark.parametrize("B", [4, 8])
+@pytest.mark.parametrize("K", [4096, 1088])
+def test_rmsnorm_qmv_matrix_cores(bmv, fmt, bits, group, B, K):
+    key = f"mc-{fmt}-{B}-{K}"
+    say(f"rmsnorm_qmv matrix cores {fmt} bf16 B={B} K={K} N=300")
+    c = _case(fmt, bits, group, B, K, 300, "bf16", key)
+    gamma = _gamma(K, "bf16", key)
+    y, plain, staged = _run(bmv, c, gamma, 1e-6)
+    _check(to_host(y, "bf16"), plain, staged, "bf16", f"rmsnorm_qmv {key}")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
+def test_rmsnorm_qmv_matrix_cores_unit_rms_equals_plain_qmv(bmv, fmt):
+    # as the VALU-tile case above, at B = 4: the fused and the plain call both
+    # run on the matrix cores, in the same order, so with r exactly 1 they
+    # must agree bit for bit
+    import torch
+    say(f"rmsnorm_qmv unit rms vs qmv {fmt} bf16 B=4 K=4096 N=300 (matrix cores)")
+    c = _case(fmt, 4 if fmt != "mxfp8" else 8, {"mxfp4": 32, "nvfp4": 16, "mxfp8": 32}[fmt], 4,
+              4096, 300, "bf16", f"unit-mc-{fmt}")
+    signs = workloads.rng_for(10, f"signs-mc-{fmt}").integers(0, 2, size=(4, 4096)) * 2 - 1
+    x = workloads.to_storage(signs.astype(np.float64), "bf16")
+    gamma = _gamma(4096, "bf16", f"unit-mc-{fmt}")
+    d = case_to_dev(c)
+    blk = {"mxfp4": 32, "nvfp4": 16, "mxfp8": 32}[fmt]
+    wt = bmv.make_weights(fmt, d["w"], d["scales"], None, K=c.K, bits=c.bits, group_size=blk,
+                          global_scale=d.get("gscale"))
+    y = bmv.qmv_rmsnorm_qmv(to_dev(x, "bf16"), wt, to_dev(gamma, "bf16"), 0.0)
+    xg = to_dev(oracle.gamma_stored(x, "bf16", gamma), "bf16")
+    if fmt == "mxfp4":
+        y0 = bmv.qmv_fp_mxfp4(xg, d["w"], d["scales"])
+    elif fmt == "nvfp4":
+        y0 = bmv.qmv_fp_nvfp4(xg, d["w"], d["scales"], d["gscale"])
+    else:
+        y0 = bmv.qmv_fp_mxfp8(xg, d["w"], d["scales"])
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y0.view(torch.int16)), fmt
