@@ -1796,9 +1796,12 @@ int launch_qmv_norm_t(const LaunchParams& p, const NormArgs& na, hipStream_t st)
 // takes codes 8 t .. 8 t + 7 of every lane's 32 (the same k order in A and
 // B). The 16-byte pieces are stored XOR-swizzled by row so the operand reads
 // hit distinct LDS banks. x values enter the B operand straight from global
-// memory (lanes of column b < B), scales are decoded from bytes loaded per
-// lane (one vector load per row and chunk when aligned). Codes at k >= K
-// enter as zeros, together with their x values.
+// memory (lanes of column b < B), loaded together with the chunk's weights.
+// When K is a whole number of chunks and the scale rows are short, the
+// block's scale rows are staged in LDS once (behind one barrier that the
+// first chunk's loads are already in flight across) and each chunk reads its
+// scale bytes from there; otherwise each lane gathers its scale bytes from
+// global memory. Codes at k >= K enter as zeros, together with their x values.
 //
 // Each output is one MFMA accumulator element per wave, summed over that
 // wave's chunks in order; the W partial sums are added in wave order in LDS
