@@ -1838,8 +1838,12 @@ template <int FMT> constexpr int mf_chunk_codes() { return FMT == FMT_MXFP8 ? 12
 // turn, measured slower that way (19.3 and 25.2 us against 12.6 and 20.2)
 // and keep two tiles: eight waves for NVFP4 (fp32 products, 88 VGPRs), 16
 // for MXFP8, 8 for the general instances (82..108 VGPRs).
-template <int FMT, bool kWhole> constexpr int mf_tiles() {
-    return (kWhole && FMT == FMT_MXFP4) ? 4 : 2;
+// The fused-RMSNorm form of NVFP4 takes four tiles as well: its x * gamma
+// work per chunk is then shared by twice the rows (K=4096 N=14336, B = 4 / 8:
+// 19.2 / 19.5 -> 15.4 / 15.4 us; the plain NVFP4 QMV with four tiles ran
+// 12.0 / 12.3 against 10.8 / 11.6 us).
+template <int FMT, bool kWhole, bool NORM = false> constexpr int mf_tiles() {
+    return (kWhole && (FMT == FMT_MXFP4 || (NORM && FMT == FMT_NVFP4))) ? 4 : 2;
 }
 template <int FMT, bool kWhole> constexpr int mf_max_waves() {
     return (kWhole && FMT == FMT_MXFP8) ? 16 : 8;
@@ -1847,8 +1851,8 @@ template <int FMT, bool kWhole> constexpr int mf_max_waves() {
 // 16-byte scale pieces each thread stages (kWhole): a block's scale rows,
 // at most kMfMaxScaleRow bytes each, over at least 64 threads per wave of the
 // launch (the launcher checks that they fit)
-template <int FMT, bool kWhole> constexpr int mf_scale_pieces() {
-    constexpr int per = 16 * mf_tiles<FMT, kWhole>() * kMfMaxScaleRow / 16;
+template <int FMT, bool kWhole, bool NORM = false> constexpr int mf_scale_pieces() {
+    constexpr int per = 16 * mf_tiles<FMT, kWhole, NORM>() * kMfMaxScaleRow / 16;
     constexpr int thr = 64 * mf_max_waves<FMT, kWhole>();
     return kWhole ? (per + thr - 1) / thr : 1;
 }
@@ -1879,7 +1883,7 @@ __device__ inline void mfma_tile(const LaunchParams& p, const NormArgs& na) {
     constexpr int kSegs = kCodes / 128;                  // 128-code segments per chunk
     constexpr int kBlk = FMT == FMT_NVFP4 ? 16 : 32;     // codes per scale
     constexpr int kScB = kCodes / kBlk;                  // scale bytes per row and chunk
-    constexpr int RT = mf_tiles<FMT, kWhole>();          // 16-row tiles per block
+    constexpr int RT = mf_tiles<FMT, kWhole, NORM>();    // 16-row tiles per block
     constexpr int kRows = 16 * RT;                       // weight rows per block
     extern __shared__ __align__(16) unsigned char smem[];
     const int tid = threadIdx.x;
@@ -1932,7 +1936,7 @@ __device__ inline void mfma_tile(const LaunchParams& p, const NormArgs& na) {
     // 16-byte pieces are loaded here, ahead of every weight load; their LDS
     // writes wait for them alone (the counters retire in order) and happen
     // after the first chunk's loads have gone out, before one barrier.
-    constexpr int kScPieces = mf_scale_pieces<FMT, kWhole>();
+    constexpr int kScPieces = mf_scale_pieces<FMT, kWhole, NORM>();
     const int sc_row = (int)p.sc_per_row;
     const int sc_stride = sc_row + 16;
     uint8_t* sst = smem + (size_t)nw * kRows * kMfChunkBytes;
@@ -2219,12 +2223,13 @@ int launch_qmv_mfma(const LaunchParams& p, const NormArgs& na, hipStream_t st) {
                        (reinterpret_cast<uintptr_t>(p.scales) % 16) == 0;
     (void)kScB;
     int nw = mfma_waves(p, whole ? mf_max_waves<FMT, true>() : mf_max_waves<FMT, false>());
-    int rows = 16 * (whole ? mf_tiles<FMT, true>() : mf_tiles<FMT, false>());
-    if (whole && (int64_t)rows * p.sc_per_row / 16 > (int64_t)mf_scale_pieces<FMT, true>() * 64 * nw) {
+    int rows = 16 * (whole ? mf_tiles<FMT, true, NORM>() : mf_tiles<FMT, false, NORM>());
+    if (whole && (int64_t)rows * p.sc_per_row / 16 >
+                     (int64_t)mf_scale_pieces<FMT, true, NORM>() * 64 * nw) {
         // the scale rows need more pieces per thread than the instance holds
         whole = false;
         nw = mfma_waves(p, mf_max_waves<FMT, false>());
-        rows = 16 * mf_tiles<FMT, false>();
+        rows = 16 * mf_tiles<FMT, false, NORM>();
     }
     // W waves stage rows x 128 bytes each (the reduction reuses that area: W x
     // rows x 8 columns x 4 bytes); whole instances add the staged scale rows
