@@ -120,7 +120,7 @@ def check(y_stored: np.ndarray, y64: np.ndarray, A: np.ndarray, dtype: str, what
     """The parity bar.
 
     f32: normwise max|y - y^| / max|y^| <= 1e-5, and elementwise
-         |y - y^| <= 1e-5 |y^| + 2^-18 A (A = sum_k |x w|, a floor that only
+         |y - y^| <= 1e-5 |y^| + 2^-22 A (A = sum_k |x w|, a floor that only
          matters under cancellation).
     f16 / bf16: |y - RN_T(y^)| <= ulp_T(RN_T(y^)); an element outside that
          passes only as a near-cancellation case, |y - y^| <= ulp_T(y)/2 +
@@ -134,11 +134,10 @@ def check(y_stored: np.ndarray, y64: np.ndarray, A: np.ndarray, dtype: str, what
         norm = float(np.max(np.abs(y - y64))) / scale
         assert norm <= 1e-5, f"{what}: normwise relative error {norm:.3g} > 1e-5"
         err = np.abs(y - y64)
-        bad = err > 1e-5 * np.abs(y64) + 2.0 ** -18 * A
-        assert not bad.any(), f"{what}: {int(bad.sum())} elements outside 1e-5 rel + 2^-18 A"
-        tight = int((err > 1e-5 * np.abs(y64) + 2.0 ** -22 * A).sum())
-        if tight:
-            note(what, "f32 beyond 1e-5 rel + 2^-22 A (within 2^-18 A)", tight, y.size)
+        bad = err > 1e-5 * np.abs(y64) + 2.0 ** -22 * A
+        assert not bad.any(), (
+            f"{what}: {int(bad.sum())} elements outside 1e-5 rel + 2^-22 A; first at "
+            f"{np.argwhere(bad)[:3].tolist()} got {y[bad][:3]} want {y64[bad][:3]}")
         return 0
     r = oracle.round_f64_to(y64, dtype)
     r64 = oracle.storage_to_f64(r, dtype)
