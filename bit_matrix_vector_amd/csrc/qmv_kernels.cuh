@@ -594,8 +594,10 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(LaunchParams p, Geom g) {
 }
 
 // ---------------------------------------------------------------------------
-// One activation row of 16-bit values against MXFP4 / NVFP4 / MXFP8 weights
-// with K = 2048 * NU: the tile above cut to what this case needs. Each wave
+// One to four activation rows of 16-bit values (NB) against MXFP4 / NVFP4 /
+// MXFP8 weights with K = 2048 * NU: the tile above cut to what this case
+// needs. The block stages its NB x rows in LDS, each in the layout the tile
+// gives one row, and every unit is folded against all of them. Each wave
 // takes two rows (its row index is wave-uniform, so row addresses live in
 // scalar registers); lane l takes units l, l + 64, ... of both rows, exactly
 // the units and the order of the tile with 64 lanes per row, and folds them
@@ -610,12 +612,11 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(LaunchParams p, Geom g) {
 template <int FMT> constexpr int row_units_max() { return 2; }
 
 
-template <int DT, int FMT, int BITS, int NU, class XR>
+template <int DT, int FMT, int BITS, int NU, class XR, int NB = 1, int R = 2>
 __device__ inline void row_tiles(const LaunchParams& p, const XR& xr, float gmul,
                                  typename Store<DT>::S* xs) {
     using F = Fmt<FMT, BITS>;
     using S = typename Store<DT>::S;
-    constexpr int R = 2;                      // rows per wave
     constexpr int W = F::kWords;
     constexpr int kUnitBytes = 4 * W;
     constexpr int KR = 2048 * NU;             // elements per row
@@ -625,6 +626,7 @@ __device__ inline void row_tiles(const LaunchParams& p, const XR& xr, float gmul
     // lanes of a staging write (4 units x 4 planes) hit all 64 banks once;
     // unit_fma takes the plane stride in units
     constexpr int USP = US + 4;
+    constexpr int XS = 32 * USP;              // LDS elements per staged x row
     constexpr int kEB = F::template elem_bytes<DT>();
 
     const int tid = threadIdx.x;
@@ -635,9 +637,11 @@ __device__ inline void row_tiles(const LaunchParams& p, const XR& xr, float gmul
 
     // (1) this thread's NU 16-byte chunks of x (and whatever the accessor's
     // staging reads with them), ahead of the weights
-    typename XR::Chunk xc[NU];
+    typename XR::Chunk xc[NB][NU];
 #pragma unroll
-    for (int j = 0; j < NU; ++j) xc[j] = xr.load(0, (int64_t)(tid + j * kThreads) * 8);
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < NU; ++j) xc[b][j] = xr.load(b, (int64_t)(tid + j * kThreads) * 8);
 
     // (2) the lane's units of both rows and their scale elements (rows past
     // the end re-read row N - 1; their results are not stored)
@@ -663,47 +667,57 @@ __device__ inline void row_tiles(const LaunchParams& p, const XR& xr, float gmul
 
     // (3) x to LDS, chunk v at the tile's slot, in the tile's staging order
 #pragma unroll
-    for (int j = 0; j < NU; ++j) {
-        const int v = tid + j * kThreads;
-        *reinterpret_cast<v4u*>(xs + x_lds_slot(v * 8, USP)) = xr.stage(0, (int64_t)v * 8, xc[j]);
-    }
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int j = 0; j < NU; ++j) {
+            const int v = tid + j * kThreads;
+            *reinterpret_cast<v4u*>(xs + b * XS + x_lds_slot(v * 8, USP)) =
+                xr.stage(b, (int64_t)v * 8, xc[b][j]);
+        }
     xr.staged();
     __syncthreads();
     xr.settled();
 
     // (4) the units in the tile's order, (5) the tile's reduction and store
-    float total[R][1];
+    float total[R][NB];
 #pragma unroll
-    for (int i = 0; i < R; ++i) total[i][0] = 0.0f;
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) total[i][b] = 0.0f;
 #pragma unroll
     for (int j = 0; j < NU; ++j) {
         typename F::Scale scl[R];
 #pragma unroll
         for (int i = 0; i < R; ++i) scl[i] = F::template decode<DT>(s_raw[j][i]);
-        unit_fma<DT, FMT, BITS, 1, R>(u_raw[j], scl, xs, lane + 64 * j, KR, USP, total);
+        unit_fma<DT, FMT, BITS, NB, R>(u_raw[j], scl, xs, lane + 64 * j, XS, USP, total);
     }
 #pragma unroll
-    for (int i = 0; i < R; ++i) total[i][0] = group_sum(total[i][0], 64);
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) total[i][b] = group_sum(total[i][b], 64);
     if (lane == 63) {
         S* y = static_cast<S*>(p.y);
 #pragma unroll
         for (int i = 0; i < R; ++i) {
             if (row0 + i < N) {
-                float v = xr.out(0, total[i][0]);
-                if constexpr (FMT == FMT_NVFP4) v = v * gmul;
-                y[row0 + i] = Store<DT>::from_f32(v);
+#pragma unroll
+                for (int b = 0; b < NB; ++b) {
+                    float v = xr.out(b, total[i][b]);
+                    if constexpr (FMT == FMT_NVFP4) v = v * gmul;
+                    y[b * N + row0 + i] = Store<DT>::from_f32(v);
+                }
             }
         }
     }
 }
 
-template <int DT, int FMT, int BITS, int NU>
+template <int DT, int FMT, int BITS, int NU, int NB = 1, int R = 2>
 __global__ __launch_bounds__(kThreads) void qmv_row_kernel(LaunchParams p) {
     using S = typename Store<DT>::S;
-    __shared__ __align__(16) S xs[(2048 * NU / 32 + 4) * 32];
+    __shared__ __align__(16) S xs[NB * (2048 * NU / 32 + 4) * 32];
     const XContig<S> xr{static_cast<const S*>(p.x), p.K};
     const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
-    row_tiles<DT, FMT, BITS, NU>(p, xr, gmul, xs);
+    row_tiles<DT, FMT, BITS, NU, XContig<S>, NB, R>(p, xr, gmul, xs);
 }
 
 // Fused RMSNorm + QMV: y[b] = r[b] * (W . RN_T(x[b] * gamma)), the QMV tile
@@ -2201,9 +2215,8 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_n
 //   NVFP4  B=2 9.10 -> 10.81, B=3 11.07 -> 10.91, B=4 12.6 -> 10.91, B=8 28.6 -> 11.76 us
 //   MXFP8  B=2 12.46 -> 15.45, B=3 13.86 -> 15.62, B=4 15.6 -> 15.76, B=8 46.2 -> 16.4 us
 // (MXFP8's 128-code chunks give each wave two chunks in turn at K=4096).
-// MXFP4 at B = 2 and NVFP4 at B = 3 would gain 7 % and 1.5 %; they stay on
-// the VALU tile, whose two-row bf16 calls are what the one-row kernel is
-// checked against bit for bit.
+// Where the one-row kernel takes a batch (K = 2048 or 4096, up to
+// row_max_batch rows) it runs first; these thresholds decide the other K.
 template <int FMT> constexpr int mf_min_batch() {
     return FMT == FMT_MXFP4 ? 3 : 4;
 }
@@ -2251,24 +2264,51 @@ int launch_qmv_mfma(const LaunchParams& p, const NormArgs& na, hipStream_t st) {
     return (int)hipGetLastError();
 }
 
+// Activation rows the one-row kernel takes (it folds each row exactly as a
+// one-row call does, so every batch row equals that call bit for bit). Picked
+// from measurements at K=4096, N=14336 against the matrix cores (bf16) and the
+// VALU tile (f16), in one process (row kernel / the path it replaced, us):
+//   bf16 MXFP4  B=2 7.68 / 8.68    B=3 8.95 / 8.73 (matrix cores kept)
+//   bf16 NVFP4  B=2 7.89 / 8.70    B=3 9.21 / 10.74   B=4 11.35 / 10.81 (kept)
+//   bf16 MXFP8  B=2 12.22 / 12.32  B=3 12.82 / 13.65  B=4 13.95 / 15.67
+// Two weight rows per wave at every batch size (four rows per wave at B=3 and
+// B=4 ran 9-15 % slower: half the waves, each with twice the loads and decode
+// before its first product).
+template <int DT, int FMT> constexpr int row_max_batch() {
+    if constexpr (DT == DT_BF16) return FMT == FMT_MXFP4 ? 2 : FMT == FMT_NVFP4 ? 3 : 4;
+    return 4;
+}
+template <int DT, int FMT, int BITS, int NU, int NB>
+int launch_row(const LaunchParams& p, hipStream_t st) {
+    constexpr int R = 2;
+    const dim3 grid((unsigned)((p.N + R * kWaves - 1) / (R * kWaves)));
+    hipLaunchKernelGGL((qmv_row_kernel<DT, FMT, BITS, NU, NB, R>), grid, dim3(kThreads), 0, st, p);
+    return (int)hipGetLastError();
+}
+template <int DT, int FMT, int BITS, int NU>
+int launch_row_nu(const LaunchParams& p, hipStream_t st) {
+    constexpr int kMax = row_max_batch<DT, FMT>();
+    switch ((int)p.B) {
+        case 2: if constexpr (kMax >= 2) return launch_row<DT, FMT, BITS, NU, 2>(p, st); break;
+        case 3: if constexpr (kMax >= 3) return launch_row<DT, FMT, BITS, NU, 3>(p, st); break;
+        case 4: if constexpr (kMax >= 4) return launch_row<DT, FMT, BITS, NU, 4>(p, st); break;
+        default: break;
+    }
+    return launch_row<DT, FMT, BITS, NU, 1>(p, st);
+}
+
 template <int DT, int FMT, int BITS>
 int launch_qmv_t(const LaunchParams& p, hipStream_t st) {
+    if constexpr (DT != DT_F32 && (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
+        if (p.B <= row_max_batch<DT, FMT>() && p.N > 0 && p.K > 0 && p.K % 2048 == 0 &&
+            p.K / 2048 <= row_units_max<FMT>()) {
+            if (p.K == 2048) return launch_row_nu<DT, FMT, BITS, 1>(p, st);
+            return launch_row_nu<DT, FMT, BITS, 2>(p, st);
+        }
+    }
     if constexpr (DT == DT_BF16 &&
                   (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
         if (use_mfma_qmv<FMT>(p)) return launch_qmv_mfma<DT, FMT, false>(p, NormArgs{}, st);
-    }
-    if constexpr (DT != DT_F32 && (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
-        if (p.B == 1 && p.N > 0 && p.K > 0 && p.K % 2048 == 0 &&
-            p.K / 2048 <= row_units_max<FMT>()) {
-            const dim3 grid((unsigned)((p.N + 2 * kWaves - 1) / (2 * kWaves)));
-            switch ((int)(p.K / 2048)) {
-                case 1: hipLaunchKernelGGL((qmv_row_kernel<DT, FMT, BITS, 1>), grid,
-                                           dim3(kThreads), 0, st, p); break;
-                default: hipLaunchKernelGGL((qmv_row_kernel<DT, FMT, BITS, 2>), grid,
-                                            dim3(kThreads), 0, st, p); break;
-            }
-            return (int)hipGetLastError();
-        }
     }
     const int nb = (int)p.B;
     switch (nb) {

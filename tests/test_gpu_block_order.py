@@ -43,8 +43,9 @@ def _case(fmt, dtype, B, K, N, key):
     return workloads.affine_case(78, key, bits=4, group=64, K=K, N=N, B=B, dtype=dtype)
 
 
-# (format, dtype, B, K, N): the one-row kernel takes 8 rows per block (N=2051:
-# 257 blocks = 4 whole groups + 1; N=1100: 138 blocks), the VALU tile
+# (format, dtype, B, K, N): the one-row kernel takes 8 rows per block at one to
+# four activation rows (N=2051: 257 blocks = 4 whole groups + 1; N=1100: 138
+# blocks), the VALU tile
 # 4 (64 / LPR) R rows per block: 4 for K = 4096 at B <= 2 (N=1100: 275
 # blocks), 32 for the 16-lane rows of K = 1536 at B = 3 (N=2200: 69 blocks)
 CASES = [
@@ -54,6 +55,9 @@ CASES = [
     ("affine", "bf16", 1, 4096, 1100),
     ("affine", "f32", 2, 4096, 1100),
     ("mxfp4", "f16", 3, 1536, 2200),
+    ("mxfp4", "f16", 2, 4096, 1100),
+    ("nvfp4", "bf16", 3, 4096, 2051),
+    ("mxfp8", "bf16", 4, 2048, 1100),
 ]
 
 

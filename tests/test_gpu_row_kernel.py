@@ -1,15 +1,17 @@
-"""The one-activation-row QMV kernel: 16-bit x against MXFP4, NVFP4 or MXFP8
-weights with K = 2048 or 4096 (qmv_row_kernel).
+"""The one-row QMV kernel: 16-bit x against MXFP4, NVFP4 or MXFP8 weights
+with K = 2048 or 4096 (qmv_row_kernel), at one to four activation rows.
 
-Every case is checked twice: against the fp64 oracle on sampled rows, and bit
-for bit against the same activation row computed by the VALU tile, which is
-what a two-row call of the same weights runs (below the matrix-core
-thresholds). The two kernels share the per-unit arithmetic and the reduction
-order, so a row's result must not depend on which of them computed it. The
-cases cover ragged N (the last block's rows past N re-read row N - 1 and are
-not stored), a single row, NVFP4 with and without its global scale, and rows
-whose scales take the end codes of their formats (E8M0 0, 1, 2 and the NaN
-code; E4M3 block scales 0x00, 0x01, 0x08, 0x7E and the NaN code).
+Each activation row is folded exactly as a one-row call folds it, so every
+batch row of a call the kernel takes (bf16: B <= 2 for MXFP4, <= 3 for NVFP4,
+<= 4 for MXFP8; f16: B <= 4) must equal the one-row call of that row bit for
+bit. The kernel shares the per-unit arithmetic and the reduction order with
+the VALU tile, which f16 calls of five rows run (f16 never takes the matrix
+cores): their rows must equal the one-row calls bit for bit too. Every case is
+also checked against the fp64 oracle on sampled rows. The cases cover ragged N
+(the last block's rows past N re-read row N - 1 and are not stored), a single
+row, NVFP4 with and without its global scale, and rows whose scales take the
+end codes of their formats (E8M0 0, 1, 2 and the NaN code; E4M3 block scales
+0x00, 0x01, 0x08, 0x7E and the NaN code).
 """
 from __future__ import annotations
 
@@ -32,77 +34,106 @@ def bmv():
     return m
 
 
-def _two_row_case(fmt, dtype, K, N, key, gscale=0.5, exp_range=(120, 130)):
+def _two_row_case(fmt, dtype, K, N, key, gscale=0.5, exp_range=(120, 130), B=2):
     if fmt == "mxfp4":
-        return workloads.mxfp4_case(75, key, K=K, N=N, B=2, dtype=dtype, exp_range=exp_range)
+        return workloads.mxfp4_case(75, key, K=K, N=N, B=B, dtype=dtype, exp_range=exp_range)
     if fmt == "mxfp8":
-        return workloads.mxfp8_case(75, key, K=K, N=N, B=2, dtype=dtype, exp_range=exp_range)
-    return workloads.nvfp4_case(75, key, K=K, N=N, B=2, dtype=dtype, global_scale=gscale)
+        return workloads.mxfp8_case(75, key, K=K, N=N, B=B, dtype=dtype, exp_range=exp_range)
+    return workloads.nvfp4_case(75, key, K=K, N=N, B=B, dtype=dtype, global_scale=gscale)
 
 
 def _bits(y, dtype):
     return y.view(np.uint16) if dtype in ("bf16", "f16") else y.view(np.uint32)
 
 
-def _row_and_tile(bmv, c2):
-    """(B=1 output [1, N], B=2 output [2, N]) for the case's first x row."""
-    c1 = dataclasses.replace(c2, B=1, x=c2.x[:1].copy())
-    y1 = to_host(run_qmv(bmv, c1), c1.dtype)
-    y2 = to_host(run_qmv(bmv, c2), c2.dtype)
-    return c1, y1, y2
+# activation rows the one-row kernel takes, per (dtype, format)
+ROW_MAX = {("bf16", "mxfp4"): 2, ("bf16", "nvfp4"): 3, ("bf16", "mxfp8"): 4,
+           ("f16", "mxfp4"): 4, ("f16", "nvfp4"): 4, ("f16", "mxfp8"): 4}
+
+
+def _one_row_calls(bmv, c):
+    """[B, N] output of one-row calls, one per activation row of case c."""
+    out = []
+    for b in range(c.B):
+        cb = dataclasses.replace(c, B=1, x=c.x[b:b + 1].copy())
+        out.append(to_host(run_qmv(bmv, cb), c.dtype)[0])
+    return np.stack(out)
+
+
+def _check_batches(bmv, c5, what):
+    """c5 has five activation rows. Every call of 2..ROW_MAX rows equals the
+    one-row calls bit for bit; for f16 so does the five-row call (the VALU
+    tile). Returns (the one-row case of row 0, one-row outputs [5, N])."""
+    dtype = c5.dtype
+    y1 = _one_row_calls(bmv, c5)
+    top = ROW_MAX[(dtype, c5.fmt)]
+    for B in range(2, top + 1):
+        cb = dataclasses.replace(c5, B=B, x=c5.x[:B].copy())
+        yb = to_host(run_qmv(bmv, cb), dtype)
+        assert np.array_equal(_bits(yb, dtype), _bits(y1[:B], dtype)), \
+            f"{what}: a row of the {B}-row call differs from its one-row call"
+    if dtype == "f16":
+        y5 = to_host(run_qmv(bmv, c5), dtype)
+        assert np.array_equal(_bits(y5, dtype), _bits(y1, dtype)), \
+            f"{what}: the VALU tile's rows differ from the one-row kernel's"
+    return dataclasses.replace(c5, B=1, x=c5.x[:1].copy()), y1
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("K,N", [(2048, 301), (4096, 1), (4096, 9), (4096, 2051)])
 def test_row_kernel_equals_tile_and_oracle(bmv, fmt, dtype, K, N):
-    c2 = _two_row_case(fmt, dtype, K, N, f"row-{fmt}-{dtype}-{K}-{N}")
+    # f16 outputs of MXFP8 rows with E8M0 up to 2^3 pass 65504 at K=4096
+    er = (116, 126) if (fmt, dtype) == ("mxfp8", "f16") else (120, 130)
+    c5 = _two_row_case(fmt, dtype, K, N, f"row-{fmt}-{dtype}-{K}-{N}", exp_range=er, B=5)
     say(f"row kernel {fmt} {dtype} K={K} N={N}")
-    c1, y1, y2 = _row_and_tile(bmv, c2)
-    assert np.array_equal(_bits(y1[0], dtype), _bits(y2[0], dtype)), \
-        f"{fmt} {dtype} K={K} N={N}: the one-row kernel differs from the tile's row"
+    c1, y1 = _check_batches(bmv, c5, f"{fmt} {dtype} K={K} N={N}")
     rows = sample_rows(N, 64, seed=K + N)
     y64, A = oracle_rows(c1, rows)
-    check(y1[:, rows], y64, A, dtype, f"row kernel {fmt} {dtype} K={K} N={N}")
+    check(y1[:1, rows], y64, A, dtype, f"row kernel {fmt} {dtype} K={K} N={N}")
+    # the last row of the widest call the kernel takes, against the oracle too
+    top = ROW_MAX[(dtype, fmt)]
+    cl = dataclasses.replace(c5, B=1, x=c5.x[top - 1:top].copy())
+    y64, A = oracle_rows(cl, rows)
+    check(y1[top - 1:top, rows], y64, A, dtype, f"row kernel {fmt} {dtype} K={K} N={N} row {top - 1}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_row_kernel_nvfp4_without_global_scale(bmv, dtype):
-    c2 = _two_row_case("nvfp4", dtype, 4096, 77, f"row-nvfp4-nogs-{dtype}", gscale=None)
+    c5 = _two_row_case("nvfp4", dtype, 4096, 77, f"row-nvfp4-nogs-{dtype}", gscale=None, B=5)
     say(f"row kernel nvfp4 without global scale {dtype}")
-    c1, y1, y2 = _row_and_tile(bmv, c2)
-    assert np.array_equal(_bits(y1[0], dtype), _bits(y2[0], dtype))
+    c1, y1 = _check_batches(bmv, c5, f"nvfp4 no global scale {dtype}")
     rows = np.arange(77)
     y64, A = oracle_rows(c1, rows)
-    check(y1, y64, A, dtype, f"row kernel nvfp4 no global scale {dtype}")
+    check(y1[:1], y64, A, dtype, f"row kernel nvfp4 no global scale {dtype}")
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("K", [2048, 4096])
-def test_row_kernel_extreme_scale_codes(bmv, fmt, K):
-    c2 = _two_row_case(fmt, "bf16", K, 24, f"row-extreme-{fmt}-{K}")
-    sc = c2.scales.copy()
+def test_row_kernel_extreme_scale_codes(bmv, fmt, dtype, K):
+    c5 = _two_row_case(fmt, dtype, K, 24, f"row-extreme-{fmt}-{dtype}-{K}", B=5)
+    sc = c5.scales.copy()
     if fmt == "nvfp4":
         sc[0, :] = 0x01
         sc[1, ::2] = 0x00
         sc[2, :] = 0x08
         sc[3, 5] = 0x7F               # NaN block
-        sc[4, :] = 0x7E
+        # the largest code; f16 outputs of K=4096 rows would overflow with it
+        sc[4, :] = 0x7E if dtype == "bf16" else 0x66
     else:
         sc[0, :] = 0
         sc[1, :] = 1
         sc[2, ::2] = 2
         sc[3, 7] = 255                # NaN block
-        sc[4, :] = np.where(np.arange(sc.shape[1]) % 2 == 0, 0, 130)
-    c2.scales = sc
-    say(f"row kernel extreme scale codes {fmt} K={K}")
-    c1, y1, y2 = _row_and_tile(bmv, c2)
-    assert np.array_equal(_bits(y1[0], "bf16"), _bits(y2[0], "bf16")), \
-        f"{fmt} K={K}: the one-row kernel differs from the tile's row"
-    assert np.isnan(oracle.storage_to_f64(y1[:, [3]], "bf16")).all()
+        sc[4, :] = np.where(np.arange(sc.shape[1]) % 2 == 0, 0, 130 if dtype == "bf16" else 118)
+    c5.scales = sc
+    say(f"row kernel extreme scale codes {fmt} {dtype} K={K}")
+    c1, y1 = _check_batches(bmv, c5, f"extreme scales {fmt} {dtype} K={K}")
+    assert np.isnan(oracle.storage_to_f64(y1[:, [3]], dtype)).all()
     keep = np.setdiff1d(np.arange(c1.N), [3])
     y64, A = oracle_rows(c1, keep)
-    check(y1[:, keep], y64, A, "bf16", f"row kernel extreme scales {fmt} K={K}")
+    check(y1[:1, keep], y64, A, dtype, f"row kernel extreme scales {fmt} {dtype} K={K}")
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
