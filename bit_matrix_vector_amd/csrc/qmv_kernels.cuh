@@ -746,15 +746,15 @@ __global__ __launch_bounds__(kThreads) void qmv_norm_kernel(LaunchParams p, Geom
 // the XNorm accessor stages x times gamma with the tile's chunk-to-thread
 // assignment and sums the squares in the same order, so r and every result
 // are bit for bit those of qmv_norm_kernel.
-template <int DT, int FMT, int BITS, int NU>
+template <int DT, int FMT, int BITS, int NU, int NB = 1>
 __global__ __launch_bounds__(kThreads) void qmv_row_norm_kernel(LaunchParams p, NormArgs na) {
     using S = typename Store<DT>::S;
-    __shared__ __align__(16) S xs[(2048 * NU / 32 + 4) * 32];
-    __shared__ float red[kWaves];
-    const XNorm<DT, 1> xr{static_cast<const S*>(p.x), p.K, static_cast<const S*>(na.gamma), na.eps,
-                          red, {}, {}};
+    __shared__ __align__(16) S xs[NB * (2048 * NU / 32 + 4) * 32];
+    __shared__ float red[NB * kWaves];
+    const XNorm<DT, NB> xr{static_cast<const S*>(p.x), p.K, static_cast<const S*>(na.gamma),
+                           na.eps, red, {}, {}};
     const float gmul = (FMT == FMT_NVFP4 && p.gscale) ? *p.gscale : 1.0f;
-    row_tiles<DT, FMT, BITS, NU>(p, xr, gmul, xs);
+    row_tiles<DT, FMT, BITS, NU, XNorm<DT, NB>, NB, 2>(p, xr, gmul, xs);
 }
 
 // ---------------------------------------------------------------------------
@@ -1759,24 +1759,61 @@ int launch_qmv_mfma(const LaunchParams& p, const NormArgs& na, hipStream_t st);
 // takes four rows per lane group while that still launches 2048 waves, else
 // two: every block redoes the row's x work (x * gamma and the squares), so
 // fewer, taller blocks do less of it.
+// Activation rows the one-row kernel takes (it folds each row exactly as a
+// one-row call does, so every batch row equals that call bit for bit). Picked
+// from measurements at K=4096, N=14336 against the matrix cores (bf16) and the
+// VALU tile (f16), in one process (row kernel / the path it replaced, us):
+//   bf16 MXFP4  B=2 7.68 / 8.68    B=3 8.95 / 8.73 (matrix cores kept)
+//   bf16 NVFP4  B=2 7.89 / 8.70    B=3 9.21 / 10.74   B=4 11.35 / 10.81 (kept)
+//   bf16 MXFP8  B=2 12.22 / 12.32  B=3 12.82 / 13.65  B=4 13.95 / 15.67
+// Two weight rows per wave at every batch size (four rows per wave at B=3 and
+// B=4 ran 9-15 % slower: half the waves, each with twice the loads and decode
+// before its first product).
+template <int DT, int FMT> constexpr int row_max_batch() {
+    if constexpr (DT == DT_BF16) return FMT == FMT_MXFP4 ? 2 : FMT == FMT_NVFP4 ? 3 : 4;
+    return 4;
+}
+// Activation rows the fused RMSNorm's one-row kernel takes (each batch row
+// equals its one-row call bit for bit, its r included): the plain kernel's
+// limits, which the same measurement gave (K=4096, N=14336, one process; us,
+// row kernel / the path it replaced):
+//   bf16 MXFP4  B=2 10.22 / 11.17  B=3 12.73 / 11.10 (matrix cores kept)
+//   bf16 NVFP4  B=2 10.33 / 13.07  B=3 13.15 / 16.68  B=4 15.92 / 15.45 (kept)
+//   bf16 MXFP8  B=2 13.69 / 15.11  B=3 16.15 / 18.96  B=4 17.92 / 19.51
+//   f16 (VALU tile replaced) MXFP4 B=4 15.61 / 15.67, NVFP4 16.36 / 18.16,
+//   MXFP8 18.01 / 19.93, and B = 2, 3 gain 2-21 %.
+template <int DT, int FMT> constexpr int row_norm_max_batch() { return row_max_batch<DT, FMT>(); }
+template <int DT, int FMT, int BITS, int NU, int NB>
+int launch_row_norm(const LaunchParams& p, const NormArgs& na, hipStream_t st) {
+    const dim3 grid((unsigned)((p.N + 2 * kWaves - 1) / (2 * kWaves)));
+    hipLaunchKernelGGL((qmv_row_norm_kernel<DT, FMT, BITS, NU, NB>), grid, dim3(kThreads), 0, st,
+                       p, na);
+    return (int)hipGetLastError();
+}
+template <int DT, int FMT, int BITS, int NU>
+int launch_row_norm_nu(const LaunchParams& p, const NormArgs& na, hipStream_t st) {
+    constexpr int kMax = row_norm_max_batch<DT, FMT>();
+    switch ((int)p.B) {
+        case 2: if constexpr (kMax >= 2) return launch_row_norm<DT, FMT, BITS, NU, 2>(p, na, st); break;
+        case 3: if constexpr (kMax >= 3) return launch_row_norm<DT, FMT, BITS, NU, 3>(p, na, st); break;
+        case 4: if constexpr (kMax >= 4) return launch_row_norm<DT, FMT, BITS, NU, 4>(p, na, st); break;
+        default: break;
+    }
+    return launch_row_norm<DT, FMT, BITS, NU, 1>(p, na, st);
+}
+
 template <int DT, int FMT, int BITS>
 int launch_qmv_norm_t(const LaunchParams& p, const NormArgs& na, hipStream_t st) {
+    if constexpr (DT != DT_F32 && (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
+        if (p.B <= row_norm_max_batch<DT, FMT>() && p.N > 0 && p.K > 0 && p.K % 2048 == 0 &&
+            p.K / 2048 <= row_units_max<FMT>()) {
+            if (p.K == 2048) return launch_row_norm_nu<DT, FMT, BITS, 1>(p, na, st);
+            return launch_row_norm_nu<DT, FMT, BITS, 2>(p, na, st);
+        }
+    }
     if constexpr (DT == DT_BF16 &&
                   (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
         if (use_mfma_qmv<FMT>(p)) return launch_qmv_mfma<DT, FMT, true>(p, na, st);
-    }
-    if constexpr (DT != DT_F32 && (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
-        if (p.B == 1 && p.N > 0 && p.K > 0 && p.K % 2048 == 0 &&
-            p.K / 2048 <= row_units_max<FMT>()) {
-            const dim3 grid((unsigned)((p.N + 2 * kWaves - 1) / (2 * kWaves)));
-            if (p.K == 2048)
-                hipLaunchKernelGGL((qmv_row_norm_kernel<DT, FMT, BITS, 1>), grid, dim3(kThreads),
-                                   0, st, p, na);
-            else
-                hipLaunchKernelGGL((qmv_row_norm_kernel<DT, FMT, BITS, 2>), grid, dim3(kThreads),
-                                   0, st, p, na);
-            return (int)hipGetLastError();
-        }
     }
     switch ((int)p.B) {
 #define QMV_CASE(n)                                                                         \
@@ -2264,20 +2301,6 @@ int launch_qmv_mfma(const LaunchParams& p, const NormArgs& na, hipStream_t st) {
     return (int)hipGetLastError();
 }
 
-// Activation rows the one-row kernel takes (it folds each row exactly as a
-// one-row call does, so every batch row equals that call bit for bit). Picked
-// from measurements at K=4096, N=14336 against the matrix cores (bf16) and the
-// VALU tile (f16), in one process (row kernel / the path it replaced, us):
-//   bf16 MXFP4  B=2 7.68 / 8.68    B=3 8.95 / 8.73 (matrix cores kept)
-//   bf16 NVFP4  B=2 7.89 / 8.70    B=3 9.21 / 10.74   B=4 11.35 / 10.81 (kept)
-//   bf16 MXFP8  B=2 12.22 / 12.32  B=3 12.82 / 13.65  B=4 13.95 / 15.67
-// Two weight rows per wave at every batch size (four rows per wave at B=3 and
-// B=4 ran 9-15 % slower: half the waves, each with twice the loads and decode
-// before its first product).
-template <int DT, int FMT> constexpr int row_max_batch() {
-    if constexpr (DT == DT_BF16) return FMT == FMT_MXFP4 ? 2 : FMT == FMT_NVFP4 ? 3 : 4;
-    return 4;
-}
 template <int DT, int FMT, int BITS, int NU, int NB>
 int launch_row(const LaunchParams& p, hipStream_t st) {
     constexpr int R = 2;

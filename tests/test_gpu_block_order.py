@@ -71,7 +71,8 @@ def test_block_order_every_row(bmv, fmt, dtype, B, K, N):
 
 
 @pytest.mark.parametrize("fmt,dtype,B,K,N", [("mxfp4", "bf16", 1, 4096, 2051),
-                                             ("affine", "f16", 1, 4096, 1100)])
+                                             ("affine", "f16", 1, 4096, 1100),
+                                             ("nvfp4", "bf16", 3, 4096, 2051)])
 def test_block_order_fused_norm_every_row(bmv, fmt, dtype, B, K, N):
     c = _case(fmt, dtype, B, K, N, f"order-norm-{fmt}-{dtype}-{K}-{N}")
     say(f"block order fused RMSNorm {fmt} {dtype} B={B} K={K} N={N}: all rows")

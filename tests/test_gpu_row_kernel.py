@@ -140,31 +140,43 @@ def test_row_kernel_extreme_scale_codes(bmv, fmt, dtype, K):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("K,N", [(2048, 77), (4096, 301)])
 def test_row_norm_kernel_equals_tile_and_definition(bmv, fmt, dtype, K, N):
-    """The fused RMSNorm + QMV at one activation row (the one-row kernel with
-    the norm accessor) against the tile's row inside a two-row fused call, bit
-    for bit, and against the plain fp64 definition W . rmsnorm(x) with the
+    """The fused RMSNorm + QMV on the one-row kernel (with the norm accessor):
+    every call of 2..ROW_MAX rows equals the one-row calls bit for bit (r
+    included), for f16 so does the five-row call (the fused VALU tile), and
+    the one-row calls meet the plain fp64 definition W . rmsnorm(x) within the
     staging bound."""
     from gpu_util import case_to_dev, check_fused_norm, to_dev
     # the normalized row has unit RMS whatever x's scale, so the outputs'
     # size is the weights'; E8M0 scales of 2^-13 .. 2^-3 keep every f16 output
     # finite (with scales up to 2^3, MXFP8 rows of K=4096 overflow f16)
-    c2 = _two_row_case(fmt, dtype, K, N, f"rownorm-{fmt}-{dtype}-{K}-{N}", exp_range=(114, 124))
+    c5 = _two_row_case(fmt, dtype, K, N, f"rownorm-{fmt}-{dtype}-{K}-{N}", exp_range=(114, 124),
+                       B=5)
     rng = workloads.rng_for(76, f"gamma-{fmt}-{dtype}-{K}")
     gamma = workloads.to_storage(rng.uniform(0.5, 1.5, size=K), dtype)
-    x2 = workloads.to_storage(oracle.storage_to_f64(c2.x, dtype) * 3.0, dtype)
-    d = case_to_dev(c2)
+    x5 = workloads.to_storage(oracle.storage_to_f64(c5.x, dtype) * 3.0, dtype)
+    d = case_to_dev(c5)
     blk = {"mxfp4": 32, "nvfp4": 16, "mxfp8": 32}[fmt]
-    wt = bmv.make_weights(fmt, d["w"], d["scales"], None, K=K, bits=c2.bits, group_size=blk,
+    wt = bmv.make_weights(fmt, d["w"], d["scales"], None, K=K, bits=c5.bits, group_size=blk,
                           global_scale=d.get("gscale"))
     eps = 1e-6
     say(f"row norm kernel {fmt} {dtype} K={K} N={N}")
-    y1 = to_host(bmv.qmv_rmsnorm_qmv(to_dev(x2[:1].copy(), dtype), wt, to_dev(gamma, dtype), eps),
-                 dtype)
-    y2 = to_host(bmv.qmv_rmsnorm_qmv(to_dev(x2, dtype), wt, to_dev(gamma, dtype), eps), dtype)
-    assert np.array_equal(_bits(y1[0], dtype), _bits(y2[0], dtype)), \
-        f"{fmt} {dtype} K={K}: the one-row fused kernel differs from the tile's row"
-    W = oracle.dequant(fmt, K, c2.w, c2.scales, None, bits=c2.bits, group=c2.group, dtype=dtype,
-                       global_scale=c2.global_scale)
-    y_def = oracle.rmsnorm_qmv(x2[:1], dtype, gamma, eps, W)
-    A_def = oracle.rmsnorm_qmv_abs(x2[:1], dtype, gamma, eps, W)
-    check_fused_norm(y1, y_def, A_def, dtype, f"row norm kernel {fmt} {dtype} K={K} N={N}")
+
+    def call(x):
+        return to_host(bmv.qmv_rmsnorm_qmv(to_dev(x.copy(), dtype), wt, to_dev(gamma, dtype), eps),
+                       dtype)
+
+    y1 = np.stack([call(x5[b:b + 1])[0] for b in range(5)])
+    top = ROW_MAX[(dtype, fmt)]
+    for B in range(2, top + 1):
+        assert np.array_equal(_bits(call(x5[:B]), dtype), _bits(y1[:B], dtype)), \
+            f"{fmt} {dtype} K={K}: a row of the {B}-row fused call differs from its one-row call"
+    if dtype == "f16":
+        assert np.array_equal(_bits(call(x5), dtype), _bits(y1, dtype)), \
+            f"{fmt} {dtype} K={K}: the fused VALU tile's rows differ from the one-row kernel's"
+    W = oracle.dequant(fmt, K, c5.w, c5.scales, None, bits=c5.bits, group=c5.group, dtype=dtype,
+                       global_scale=c5.global_scale)
+    for b in (0, top - 1):
+        y_def = oracle.rmsnorm_qmv(x5[b:b + 1], dtype, gamma, eps, W)
+        A_def = oracle.rmsnorm_qmv_abs(x5[b:b + 1], dtype, gamma, eps, W)
+        check_fused_norm(y1[b:b + 1], y_def, A_def, dtype,
+                         f"row norm kernel {fmt} {dtype} K={K} N={N} row {b}")
