@@ -1073,7 +1073,10 @@ def main() -> int:
         for name, c in (("nvfp4 B1 K4096 N14336 bf16", workloads.mlp_up_case("nvfp4", 1)),
                         ("mxfp8 B1 K4096 N14336 bf16", workloads.mlp_up_case("mxfp8", 1)),
                         ("affine 4b g64 B1 K4096 N4096 bf16", workloads.affine_sweep_case(4, 64, 1, "bf16")),
-                        ("mxfp4 B4 K4096 N14336 bf16", workloads.mlp_up_case("mxfp4", 4)),
+                        ("mxfp4 B2 K4096 N14336 bf16 (one-row kernel)", workloads.mlp_up_case("mxfp4", 2)),
+                        ("nvfp4 B3 K4096 N14336 bf16 (one-row kernel)", workloads.mlp_up_case("nvfp4", 3)),
+                        ("mxfp8 B4 K4096 N14336 bf16 (one-row kernel)", workloads.mlp_up_case("mxfp8", 4)),
+                        ("mxfp4 B4 K4096 N14336 bf16 (matrix cores)", workloads.mlp_up_case("mxfp4", 4)),
                         ("mxfp4 B8 K4096 N14336 bf16 (matrix cores)", workloads.mlp_up_case("mxfp4", 8)),
                         *((f"{f} B1 K4096 N14336 bf16",
                            workloads.sb_case(f, K=4096, N=14336, B=1, key="bench"))
