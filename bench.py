@@ -725,13 +725,24 @@ KERNEL_SOURCES = ("qmv_kernels.cuh", "qmv_device.h", "qmv_common.h", "qmv_inst.h
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mxfp4_b1_k4096_n14336.md")
 
 
+def _code_only(text: str) -> str:
+    """C++ source with its comments removed and whitespace runs collapsed (a
+    comment-only edit leaves the kernel's code, and so this text, unchanged).
+    String literals in these sources hold no comment markers."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_fingerprint() -> str:
-    """sha256 (first 16 hex digits) of the QMV kernel sources."""
+    """sha256 (first 16 hex digits) of the QMV kernel sources' code, comments
+    and layout left out."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "bit_matrix_vector_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "bit_matrix_vector_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1754,11 +1754,6 @@ template <int FMT> inline bool use_mfma_qmv(const LaunchParams& p);
 template <int DT, int FMT, bool NORM>
 int launch_qmv_mfma(const LaunchParams& p, const NormArgs& na, hipStream_t st);
 
-// The fused RMSNorm + QMV takes the matrix cores where the plain QMV does
-// (bf16 batches of the MX formats from mf_min_batch rows); on the VALU tile it
-// takes four rows per lane group while that still launches 2048 waves, else
-// two: every block redoes the row's x work (x * gamma and the squares), so
-// fewer, taller blocks do less of it.
 // Activation rows the one-row kernel takes (it folds each row exactly as a
 // one-row call does, so every batch row equals that call bit for bit). Picked
 // from measurements at K=4096, N=14336 against the matrix cores (bf16) and the
@@ -1802,6 +1797,12 @@ int launch_row_norm_nu(const LaunchParams& p, const NormArgs& na, hipStream_t st
     return launch_row_norm<DT, FMT, BITS, NU, 1>(p, na, st);
 }
 
+// The fused RMSNorm + QMV takes the one-row kernel and the matrix cores where
+// the plain QMV does (16-bit batches of the MX formats at K = 2048 / 4096 up
+// to row_norm_max_batch rows; bf16 batches from mf_min_batch rows otherwise);
+// on the VALU tile it takes four rows per lane group while that still launches
+// 2048 waves, else two: every block redoes the row's x work (x * gamma and the
+// squares), so fewer, taller blocks do less of it.
 template <int DT, int FMT, int BITS>
 int launch_qmv_norm_t(const LaunchParams& p, const NormArgs& na, hipStream_t st) {
     if constexpr (DT != DT_F32 && (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
