@@ -768,8 +768,9 @@ def pmc_workload(bmv, n: int, batch: int = 1, dtype: str = "bf16", moe: str | No
     """Launch sequence for hardware-counter runs: n copies of 64 MiB (the
     calibration kernel of known size), then n launches of the MXFP4 QMV at
     K=4096, N=14336 with `batch` activation rows of `dtype` (bf16, B=1: the
-    headline; f16 activations always take the VALU tile, for comparison with
-    the matrix-core kernel that bf16 takes from B=3)."""
+    headline; f16 activations take the one-row kernel up to B=4 and the VALU
+    tile or the split-operand matrix cores above it, for comparison with the
+    matrix-core kernel that bf16 takes from B=3)."""
     import torch
     import workloads
     lib = bmv.load()
@@ -1023,11 +1024,10 @@ def main() -> int:
     if args.summarize_counters:
         K, N, B = 4096, 14336, args.pmc_batch
         alg = N * K // 2 + N * K // 32 + B * K * 2 + B * N * 2   # codes + E8M0 + x + y
-        if args.pmc_dtype == "f16":
-            kernel = "qmv_row_kernel" if B == 1 else "qmv_kernel"
-        else:
-            kernel = ("qmv_mfma_kernel" if B >= 3 else "qmv_row_kernel" if B == 1 else
-                      "qmv_kernel")
+        # the MXFP4 K=4096 kernels: the one-row kernel up to B=2 (bf16) or 4
+        # (f16), the matrix cores above
+        kernel = "qmv_row_kernel" if B <= (4 if args.pmc_dtype == "f16" else 2) else \
+            "qmv_mfma_kernel"
         print(summarize_counters(*args.summarize_counters, copy_bytes=64 << 20, alg_bytes=alg,
                                  kernel=kernel))
         return 0
@@ -1089,6 +1089,9 @@ def main() -> int:
                         ("mxfp8 B4 K4096 N14336 bf16 (one-row kernel)", workloads.mlp_up_case("mxfp8", 4)),
                         ("mxfp4 B4 K4096 N14336 bf16 (matrix cores)", workloads.mlp_up_case("mxfp4", 4)),
                         ("mxfp4 B8 K4096 N14336 bf16 (matrix cores)", workloads.mlp_up_case("mxfp4", 8)),
+                        ("mxfp4 B8 K4096 N14336 f16 (matrix cores, split x)",
+                         workloads.mxfp4_case(3, "c3-mxfp4-B8-f16", K=4096, N=14336, B=8,
+                                              dtype="f16")),
                         *((f"{f} B1 K4096 N14336 bf16",
                            workloads.sb_case(f, K=4096, N=14336, B=1, key="bench"))
                           for f in ("mxfp8_e5m2", "nvfp8", "fp8_e5m2_f16", "int4", "mxint8"))):

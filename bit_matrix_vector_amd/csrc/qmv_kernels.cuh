@@ -1930,7 +1930,12 @@ template <int DT, int FMT, bool kWhole, bool NORM>
 __device__ inline void mfma_tile(const LaunchParams& p, const NormArgs& na) {
     static_assert(FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8, "block-scaled only");
     using S = typename Store<DT>::S;
-    using V8 = typename Mfma16<DT>::v8;
+    using V8 = typename Mfma16<DT_BF16>::v8;
+    // f16 activations: column c < 8 takes RN_bf16(x) of row c, column c + 8 the
+    // remainder x - RN_bf16(x) (at most 3 significant bits, exact in bf16), so
+    // every product is exact and the two columns' sums add up to the row's
+    static_assert(DT == DT_BF16 || (DT == DT_F16 && !NORM), "bf16, or f16 without the norm");
+    constexpr bool kSplit = DT == DT_F16;
     constexpr int kCodes = mf_chunk_codes<FMT>();        // codes per chunk
     constexpr int kSegs = kCodes / 128;                  // 128-code segments per chunk
     constexpr int kBlk = FMT == FMT_NVFP4 ? 16 : 32;     // codes per scale
@@ -1970,8 +1975,9 @@ __device__ inline void mfma_tile(const LaunchParams& p, const NormArgs& na) {
     // past B (never stored) and pieces past K cost nothing and read as zeros
     const __amdgpu_buffer_rsrc_t xrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<S*>(x), 0, (int)(B * K * (int64_t)sizeof(S)), kBufferWord3);
-    const bool has = r16 < B;
-    const int xoff = (int)(r16 * K * (int64_t)sizeof(S));
+    const int xr16 = kSplit ? (r16 & 7) : r16;          // the x row of this lane's column
+    const bool has = xr16 < B;
+    const int xoff = (int)(xr16 * K * (int64_t)sizeof(S));
     // gamma [K] through its own resource (NORM)
     const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(NORM ? na.gamma : static_cast<const void*>(x)), 0,
@@ -2126,6 +2132,28 @@ __device__ inline void mfma_tile(const LaunchParams& p, const NormArgs& na) {
                     xb[s][t] = v4u{o[0], o[1], o[2], o[3]};
                 }
         }
+        if constexpr (kSplit) {
+            // the f16 pieces become their bf16 head (columns 0..7) or the exact
+            // remainder (columns 8..15)
+            const bool tail = r16 >= 8;
+#pragma unroll
+            for (int s = 0; s < kSegs; ++s)
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const uint32_t xv[4] = {xb[s][t].x, xb[s][t].y, xb[s][t].z, xb[s][t].w};
+                    uint32_t o[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const f32x2 v = {Store<DT>::bits_to_f32(xv[j] & 0xFFFFu),
+                                         Store<DT>::bits_to_f32(xv[j] >> 16)};
+                        const bf16x2_t h = __builtin_convertvector(v, bf16x2_t);
+                        const f32x2 r = v - __builtin_convertvector(h, f32x2);
+                        const bf16x2_t l = __builtin_convertvector(r, bf16x2_t);
+                        o[j] = tail ? __builtin_bit_cast(uint32_t, l) : __builtin_bit_cast(uint32_t, h);
+                    }
+                    xb[s][t] = v4u{o[0], o[1], o[2], o[3]};
+                }
+        }
         // (5) the MFMAs
 #pragma unroll
         for (int s = 0; s < kSegs; ++s) {
@@ -2209,7 +2237,14 @@ __device__ inline void mfma_tile(const LaunchParams& p, const NormArgs& na) {
     // after the partial tiles (inside the weight areas: 24 kRows floats per
     // wave are free there)
     float* ssl = red + nw * kRows * 8;
-    if (has) {
+    if constexpr (kSplit) {
+        // column c's sum plus its remainder column's (lane r16 + 8)
+#pragma unroll
+        for (int t = 0; t < RT; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[t][e] = acc[t][e] + __shfl_xor(acc[t][e], 8);
+    }
+    if (has && (!kSplit || r16 < 8)) {
 #pragma unroll
         for (int t = 0; t < RT; ++t)
 #pragma unroll
@@ -2257,6 +2292,22 @@ __global__ __launch_bounds__((64 * mf_max_waves<FMT, kWhole>())) void qmv_mfma_n
 // row_max_batch rows) it runs first; these thresholds decide the other K.
 template <int FMT> constexpr int mf_min_batch() {
     return FMT == FMT_MXFP4 ? 3 : 4;
+}
+// f16 batches on the matrix cores, each activation row split into a bf16
+// head and its exact remainder (two MFMA columns per row), from the batch size
+// where that beats the VALU tile, measured at K=4096, N=14336 (VALU tile /
+// matrix cores, us, one process):
+//   MXFP4  B=5 14.07 / 11.22, B=6 15.89 / 11.39, B=8 25.63 / 11.74
+//   NVFP4  B=5 14.25 / 16.97, B=6 16.18 / 17.13, B=8 26.73 / 17.66
+//   MXFP8  B=5 17.17 / 18.28, B=6 18.41 / 18.44, B=8 42.16 / 18.72
+// and B=7 17.54 (NVFP4) / 18.67 us (MXFP8) on the matrix cores
+// (below B=5 the one-row kernel takes f16 batches at K = 2048 / 4096, and was
+// faster there than the split operand: MXFP4 B=3 8.57 / 10.97, B=4 10.02 / 11.17).
+template <int FMT> constexpr int mf_min_batch_f16() { return FMT == FMT_MXFP4 ? 5 : 7; }
+template <int FMT>
+inline bool use_mfma_qmv_f16(const LaunchParams& p) {
+    return p.B >= mf_min_batch_f16<FMT>() && p.B <= 8 && p.K > 0 &&
+           p.B * p.K * 2 < (int64_t)kBufferOutOfRange;
 }
 template <int FMT>
 inline bool use_mfma_qmv(const LaunchParams& p) {
@@ -2333,6 +2384,10 @@ int launch_qmv_t(const LaunchParams& p, hipStream_t st) {
     if constexpr (DT == DT_BF16 &&
                   (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
         if (use_mfma_qmv<FMT>(p)) return launch_qmv_mfma<DT, FMT, false>(p, NormArgs{}, st);
+    }
+    if constexpr (DT == DT_F16 &&
+                  (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
+        if (use_mfma_qmv_f16<FMT>(p)) return launch_qmv_mfma<DT, FMT, false>(p, NormArgs{}, st);
     }
     const int nb = (int)p.B;
     switch (nb) {

@@ -298,19 +298,22 @@ def test_affine_sweep_sampled(bmv, bits, group, B, dtype):
     check(y[:, rows], y64, A, dtype, f"affine b{bits} g{group} B{B} {dtype} K=N=4096")
 
 
-# the matrix cores take bf16 batches from B = 3 (MXFP4), 4 (NVFP4, MXFP8)
+# the matrix cores take bf16 batches from B = 3 (MXFP4), 4 (NVFP4, MXFP8), and
+# f16 batches from B = 5 (MXFP4), 7 (NVFP4, MXFP8)
 MC_FIRST = {"mxfp4": 3, "nvfp4": 4, "mxfp8": 4}
+MC_FIRST_F16 = {"mxfp4": 5, "nvfp4": 7, "mxfp8": 7}
 
 
 def test_batch_rows_equal_single_row_calls_bitwise(bmv):
-    # on the VALU tile: affine codes at any B, and the block-scaled formats
-    # with f16 activations at any B or bf16 activations below the batch size
-    # where the matrix cores take over (MC_FIRST; tested below)
+    # on the VALU tile and the one-row kernel: affine codes at any B, and the
+    # block-scaled formats below the batch size where the matrix cores take
+    # over (MC_FIRST, MC_FIRST_F16; tested below)
     import torch
     cases = [("affine", workloads.affine_sweep_case(3, 64, 8, "bf16", N=256))]
     for fmt in ("mxfp4", "nvfp4", "mxfp8"):
         cases.append((fmt, getattr(workloads, f"{fmt}_case")(73, f"batch-{fmt}-f16", K=4096,
-                                                            N=256, B=7, dtype="f16")))
+                                                            N=256, B=MC_FIRST_F16[fmt] - 1,
+                                                            dtype="f16")))
         cases.append((fmt, workloads.mlp_up_case(fmt, MC_FIRST[fmt] - 1, N=256)))
     for fmt, c in cases:
         d = case_to_dev(c)
@@ -383,6 +386,76 @@ def test_matrix_core_bitwise_properties(bmv, fmt):
             assert torch.equal(part.view(torch.int16), y1[:, :n].view(torch.int16)), n
 
 
+# ---------------------------------------------------------------------------
+# f16 batches on the matrix cores: each activation row enters as two bf16
+# columns, its head RN_bf16(x) and the exact remainder x - RN_bf16(x)
+# ---------------------------------------------------------------------------
+
+def _f16_case(fmt, B, K, N, key):
+    # E8M0 exponents 116..126 keep MXFP8 outputs of K = 4096 rows inside f16
+    if fmt == "nvfp4":
+        return workloads.nvfp4_case(79, key, K=K, N=N, B=B, dtype="f16", global_scale=0.5)
+    return getattr(workloads, f"{fmt}_case")(79, key, K=K, N=N, B=B, dtype="f16",
+                                             exp_range=(116, 126))
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
+@pytest.mark.parametrize("B", ["first", 8])
+def test_matrix_core_f16_split(bmv, fmt, B):
+    B = MC_FIRST_F16[fmt] if B == "first" else B
+    # a partial last chunk, K below one chunk, ragged N, several chunks per
+    # wave, and the row kernel's K values (which it hands on from these B)
+    for K, N in ((1056, 301), (96, 70), (8192, 40), (4096, 65), (2048, 33)):
+        c = _f16_case(fmt, B, K, N, f"mc16-{fmt}-{B}-{K}-{N}")
+        say(f"matrix cores f16 {fmt} B={B} K={K} N={N}")
+        y = to_host(run_qmv(bmv, c), "f16")
+        y64, A = oracle_rows(c, np.arange(N))
+        check(y, y64, A, "f16", f"matrix cores f16 {fmt} B={B} K={K} N={N}")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
+def test_matrix_core_f16_split_bitwise_properties(bmv, fmt):
+    # a row's two columns depend on that row alone: a permuted batch gives the
+    # permuted rows, a row gives the same bits in every batch size the matrix
+    # cores take, and repeated calls give the same bits
+    import torch
+    c = _f16_case(fmt, 8, 2048, 200, f"mc16-bits-{fmt}")
+    d = case_to_dev(c)
+    say(f"matrix cores f16 {fmt}: repeat, permutation, batch size")
+    y1 = run_qmv(bmv, c, d)
+    assert torch.equal(y1.view(torch.int16), run_qmv(bmv, c, d).view(torch.int16))
+    perm = torch.tensor([5, 2, 7, 0, 1, 6, 3, 4], device=d["x"].device)
+    yp = run_qmv(bmv, c, dict(d, x=d["x"][perm].contiguous()))
+    assert torch.equal(yp.view(torch.int16), y1[perm].view(torch.int16))
+    sel = [6, 1, 3, 0, 2, 7, 4][:max(MC_FIRST_F16[fmt], 5)]
+    idx = torch.tensor(sel, device=d["x"].device)
+    c_sub = workloads.QmvCase(c.fmt, c.dtype, len(sel), c.K, c.N, c.w, c.scales, c.x,
+                              global_scale=c.global_scale)
+    ys = run_qmv(bmv, c_sub, dict(d, x=d["x"][idx].contiguous()))
+    assert torch.equal(ys.view(torch.int16), y1[idx].view(torch.int16)), sel
+
+
+def test_matrix_core_f16_split_extreme_activations(bmv):
+    # activations whose remainders are the largest and smallest the split
+    # sees: f16 values with all 10 fraction bits set (remainder 3 bits), the
+    # largest finite f16 (65504 = 65536 - 32), subnormals and zeros
+    K, N, B = 1024, 64, 8
+    c = workloads.mxfp4_case(79, "mc16-extreme-x", K=K, N=N, B=B, dtype="f16",
+                             exp_range=(100, 110))
+    x = c.x.copy()
+    xb = x.view(np.uint16)
+    xb[0, :] = 0x3FFF                    # 1.9990234375
+    xb[1, ::3] = 0x7BFF                  # 65504
+    xb[2, :] = 0x0001                    # 2^-24, the smallest subnormal
+    xb[3, ::2] = 0x83FF                  # -(the largest subnormal)
+    xb[4, :] = 0
+    c.x = x
+    say("matrix cores f16: extreme activation values")
+    y = to_host(run_qmv(bmv, c), "f16")
+    y64, A = oracle_rows(c, np.arange(N))
+    check(y, y64, A, "f16", "matrix cores f16 extreme activations")
+
+
 def _extreme_scale_case(fmt, B, dtype="bf16"):
     """Rows whose scales sit at the ends of their code range: E8M0 0 (2^-127,
     whose products with the smaller E2M1 / E4M3 values are subnormal in
@@ -434,15 +507,16 @@ def test_extreme_scale_codes(bmv, fmt, B):
 
 
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
-@pytest.mark.parametrize("dtype", ["f32", "f16"])
-def test_extreme_scale_codes_other_dtypes(bmv, fmt, dtype):
-    c, nan_rows = _extreme_scale_case(fmt, 2, dtype)
-    say(f"extreme scale codes {fmt} B=2 {dtype}")
+@pytest.mark.parametrize("dtype,B", [("f32", 2), ("f16", 2), ("f16", 8)])
+def test_extreme_scale_codes_other_dtypes(bmv, fmt, dtype, B):
+    # f16 at B = 8: the matrix cores with the split activation operand
+    c, nan_rows = _extreme_scale_case(fmt, B, dtype)
+    say(f"extreme scale codes {fmt} B={B} {dtype}")
     # (f16 outputs of the 2^-127-scaled rows underflow to zeros and
     # subnormals; the 1-ulp bar, with the smallest subnormal as the ulp at
     # zero, still applies)
     y = to_host(run_qmv(bmv, c), c.dtype)
-    _check_with_nan_rows(y, c, nan_rows, f"extreme scales {fmt} B=2 {dtype}")
+    _check_with_nan_rows(y, c, nan_rows, f"extreme scales {fmt} B={B} {dtype}")
 
 
 # ---------------------------------------------------------------------------
