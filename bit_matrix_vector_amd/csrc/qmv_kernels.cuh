@@ -1751,6 +1751,7 @@ int launch_qmv_norm_r(const LaunchParams& p, const NormArgs& na, hipStream_t st)
 }
 
 template <int FMT> inline bool use_mfma_qmv(const LaunchParams& p);
+template <int FMT> inline bool use_mfma_norm_f16(const LaunchParams& p);
 template <int DT, int FMT, bool NORM>
 int launch_qmv_mfma(const LaunchParams& p, const NormArgs& na, hipStream_t st);
 
@@ -1815,6 +1816,10 @@ int launch_qmv_norm_t(const LaunchParams& p, const NormArgs& na, hipStream_t st)
     if constexpr (DT == DT_BF16 &&
                   (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
         if (use_mfma_qmv<FMT>(p)) return launch_qmv_mfma<DT, FMT, true>(p, na, st);
+    }
+    if constexpr (DT == DT_F16 &&
+                  (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
+        if (use_mfma_norm_f16<FMT>(p)) return launch_qmv_mfma<DT, FMT, true>(p, na, st);
     }
     switch ((int)p.B) {
 #define QMV_CASE(n)                                                                         \
@@ -1934,7 +1939,7 @@ __device__ inline void mfma_tile(const LaunchParams& p, const NormArgs& na) {
     // f16 activations: column c < 8 takes RN_bf16(x) of row c, column c + 8 the
     // remainder x - RN_bf16(x) (at most 3 significant bits, exact in bf16), so
     // every product is exact and the two columns' sums add up to the row's
-    static_assert(DT == DT_BF16 || (DT == DT_F16 && !NORM), "bf16, or f16 without the norm");
+    static_assert(DT == DT_BF16 || DT == DT_F16, "16-bit activations");
     constexpr bool kSplit = DT == DT_F16;
     constexpr int kCodes = mf_chunk_codes<FMT>();        // codes per chunk
     constexpr int kSegs = kCodes / 128;                  // 128-code segments per chunk
@@ -2127,7 +2132,10 @@ __device__ inline void mfma_tile(const LaunchParams& p, const NormArgs& na) {
                         ss = fmaf(x1, x1, ss);
                         const f32x2 pr = {x0 * Store<DT>::bits_to_f32(gv[j] & 0xFFFFu),
                                           x1 * Store<DT>::bits_to_f32(gv[j] >> 16)};
-                        o[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
+                        if constexpr (DT == DT_F16)
+                            o[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, f16x2_t));
+                        else
+                            o[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2_t));
                     }
                     xb[s][t] = v4u{o[0], o[1], o[2], o[3]};
                 }
@@ -2307,6 +2315,18 @@ template <int FMT> constexpr int mf_min_batch_f16() { return FMT == FMT_MXFP4 ? 
 template <int FMT>
 inline bool use_mfma_qmv_f16(const LaunchParams& p) {
     return p.B >= mf_min_batch_f16<FMT>() && p.B <= 8 && p.K > 0 &&
+           p.B * p.K * 2 < (int64_t)kBufferOutOfRange;
+}
+// The fused RMSNorm's f16 batches on the matrix cores: the staged
+// RN_f16(x * gamma) is split as x is. From B=5 (MXFP4, NVFP4) or 6 (MXFP8),
+// measured at K=4096, N=14336 (fused VALU tile / matrix cores, us):
+//   MXFP4  B=5 19.04 / 13.18, B=8 31.44 / 13.97
+//   NVFP4  B=5 22.52 / 17.79, B=8 32.59 / 18.08
+//   MXFP8  B=5 22.34 / 22.65, B=6 24.97 / 22.86, B=8 51.73 / 23.27
+template <int FMT> constexpr int mf_min_batch_norm_f16() { return FMT == FMT_MXFP8 ? 6 : 5; }
+template <int FMT>
+inline bool use_mfma_norm_f16(const LaunchParams& p) {
+    return p.B >= mf_min_batch_norm_f16<FMT>() && p.B <= 8 && p.K > 0 &&
            p.B * p.K * 2 < (int64_t)kBufferOutOfRange;
 }
 template <int FMT>

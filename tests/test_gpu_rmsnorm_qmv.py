@@ -158,6 +158,57 @@ def test_rmsnorm_qmv_matrix_cores(bmv, fmt, bits, group, B, K):
     _check(to_host(y, "bf16"), plain, staged, "bf16", f"rmsnorm_qmv {key}")
 
 
+# f16 batches from B = 5 (MXFP4, NVFP4) or 6 (MXFP8) run the fused norm on the
+# matrix cores too, the staged RN_f16(x * gamma) split into a bf16 head and its
+# exact remainder; E8M0 exponents 114..124 keep the f16 outputs finite
+@pytest.mark.parametrize("fmt,bits,group", [("mxfp4", 4, 32), ("nvfp4", 4, 16), ("mxfp8", 8, 32)])
+@pytest.mark.parametrize("B", ["first", 8])
+@pytest.mark.parametrize("K", [4096, 1088])
+def test_rmsnorm_qmv_matrix_cores_f16(bmv, fmt, bits, group, B, K):
+    B = {"mxfp4": 5, "nvfp4": 5, "mxfp8": 6}[fmt] if B == "first" else B
+    key = f"mc16-{fmt}-{B}-{K}"
+    say(f"rmsnorm_qmv matrix cores {fmt} f16 B={B} K={K} N=300")
+    if fmt == "nvfp4":
+        c = workloads.nvfp4_case(10, key, K=K, N=300, B=B, dtype="f16")
+    else:
+        c = getattr(workloads, f"{fmt}_case")(10, key, K=K, N=300, B=B, dtype="f16",
+                                             exp_range=(114, 124))
+    gamma = _gamma(K, "f16", key)
+    y, plain, staged = _run(bmv, c, gamma, 1e-6)
+    _check(to_host(y, "f16"), plain, staged, "f16", f"rmsnorm_qmv {key}")
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
+def test_rmsnorm_qmv_matrix_cores_f16_unit_rms_equals_plain_qmv(bmv, fmt):
+    # f16, B = 8: the fused and the plain call both split the same staged
+    # values on the matrix cores, so with r exactly 1 they agree bit for bit
+    import torch
+    say(f"rmsnorm_qmv unit rms vs qmv {fmt} f16 B=8 K=4096 N=300 (matrix cores)")
+    key = f"unit-mc16-{fmt}"
+    if fmt == "nvfp4":
+        c = workloads.nvfp4_case(10, key, K=4096, N=300, B=8, dtype="f16")
+    else:
+        c = getattr(workloads, f"{fmt}_case")(10, key, K=4096, N=300, B=8, dtype="f16",
+                                             exp_range=(114, 124))
+    signs = workloads.rng_for(10, f"signs-mc16-{fmt}").integers(0, 2, size=(8, 4096)) * 2 - 1
+    x = workloads.to_storage(signs.astype(np.float64), "f16")
+    gamma = _gamma(4096, "f16", key)
+    d = case_to_dev(c)
+    blk = {"mxfp4": 32, "nvfp4": 16, "mxfp8": 32}[fmt]
+    wt = bmv.make_weights(fmt, d["w"], d["scales"], None, K=c.K, bits=c.bits, group_size=blk,
+                          global_scale=d.get("gscale"))
+    y = bmv.qmv_rmsnorm_qmv(to_dev(x, "f16"), wt, to_dev(gamma, "f16"), 0.0)
+    xg = to_dev(oracle.gamma_stored(x, "f16", gamma), "f16")
+    if fmt == "mxfp4":
+        y0 = bmv.qmv_fp_mxfp4(xg, d["w"], d["scales"])
+    elif fmt == "nvfp4":
+        y0 = bmv.qmv_fp_nvfp4(xg, d["w"], d["scales"], d["gscale"])
+    else:
+        y0 = bmv.qmv_fp_mxfp8(xg, d["w"], d["scales"])
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y0.view(torch.int16)), fmt
+
+
 @pytest.mark.parametrize("fmt", ["mxfp4", "nvfp4", "mxfp8"])
 def test_rmsnorm_qmv_matrix_cores_unit_rms_equals_plain_qmv(bmv, fmt):
     # as the VALU-tile case above, at B = 4: the fused and the plain call both
