@@ -36,7 +36,7 @@ def bmv():
     return m
 
 
-def _two_row_case(fmt, dtype, K, N, key, gscale=0.5, exp_range=(120, 130), B=2):
+def _case(fmt, dtype, K, N, key, gscale=0.5, exp_range=(120, 130), B=2):
     if fmt == "mxfp4":
         return workloads.mxfp4_case(75, key, K=K, N=N, B=B, dtype=dtype, exp_range=exp_range)
     if fmt == "mxfp8":
@@ -88,24 +88,24 @@ def _check_batches(bmv, c6, what):
 def test_row_kernel_equals_tile_and_oracle(bmv, fmt, dtype, K, N):
     # f16 outputs of MXFP8 rows with E8M0 up to 2^3 pass 65504 at K=4096
     er = (116, 126) if (fmt, dtype) == ("mxfp8", "f16") else (120, 130)
-    c5 = _two_row_case(fmt, dtype, K, N, f"row-{fmt}-{dtype}-{K}-{N}", exp_range=er, B=6)
+    c6 = _case(fmt, dtype, K, N, f"row-{fmt}-{dtype}-{K}-{N}", exp_range=er, B=6)
     say(f"row kernel {fmt} {dtype} K={K} N={N}")
-    c1, y1 = _check_batches(bmv, c5, f"{fmt} {dtype} K={K} N={N}")
+    c1, y1 = _check_batches(bmv, c6, f"{fmt} {dtype} K={K} N={N}")
     rows = sample_rows(N, 64, seed=K + N)
     y64, A = oracle_rows(c1, rows)
     check(y1[:1, rows], y64, A, dtype, f"row kernel {fmt} {dtype} K={K} N={N}")
     # the last row of the widest call the kernel takes, against the oracle too
     top = ROW_MAX[(dtype, fmt)]
-    cl = dataclasses.replace(c5, B=1, x=c5.x[top - 1:top].copy())
+    cl = dataclasses.replace(c6, B=1, x=c6.x[top - 1:top].copy())
     y64, A = oracle_rows(cl, rows)
     check(y1[top - 1:top, rows], y64, A, dtype, f"row kernel {fmt} {dtype} K={K} N={N} row {top - 1}")
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_row_kernel_nvfp4_without_global_scale(bmv, dtype):
-    c5 = _two_row_case("nvfp4", dtype, 4096, 77, f"row-nvfp4-nogs-{dtype}", gscale=None, B=6)
+    c6 = _case("nvfp4", dtype, 4096, 77, f"row-nvfp4-nogs-{dtype}", gscale=None, B=6)
     say(f"row kernel nvfp4 without global scale {dtype}")
-    c1, y1 = _check_batches(bmv, c5, f"nvfp4 no global scale {dtype}")
+    c1, y1 = _check_batches(bmv, c6, f"nvfp4 no global scale {dtype}")
     rows = np.arange(77)
     y64, A = oracle_rows(c1, rows)
     check(y1[:1], y64, A, dtype, f"row kernel nvfp4 no global scale {dtype}")
@@ -115,8 +115,8 @@ def test_row_kernel_nvfp4_without_global_scale(bmv, dtype):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("K", [2048, 4096])
 def test_row_kernel_extreme_scale_codes(bmv, fmt, dtype, K):
-    c5 = _two_row_case(fmt, dtype, K, 24, f"row-extreme-{fmt}-{dtype}-{K}", B=6)
-    sc = c5.scales.copy()
+    c6 = _case(fmt, dtype, K, 24, f"row-extreme-{fmt}-{dtype}-{K}", B=6)
+    sc = c6.scales.copy()
     if fmt == "nvfp4":
         sc[0, :] = 0x01
         sc[1, ::2] = 0x00
@@ -130,9 +130,9 @@ def test_row_kernel_extreme_scale_codes(bmv, fmt, dtype, K):
         sc[2, ::2] = 2
         sc[3, 7] = 255                # NaN block
         sc[4, :] = np.where(np.arange(sc.shape[1]) % 2 == 0, 0, 130 if dtype == "bf16" else 118)
-    c5.scales = sc
+    c6.scales = sc
     say(f"row kernel extreme scale codes {fmt} {dtype} K={K}")
-    c1, y1 = _check_batches(bmv, c5, f"extreme scales {fmt} {dtype} K={K}")
+    c1, y1 = _check_batches(bmv, c6, f"extreme scales {fmt} {dtype} K={K}")
     assert np.isnan(oracle.storage_to_f64(y1[:, [3]], dtype)).all()
     keep = np.setdiff1d(np.arange(c1.N), [3])
     y64, A = oracle_rows(c1, keep)
@@ -153,7 +153,7 @@ def test_row_norm_kernel_equals_tile_and_definition(bmv, fmt, dtype, K, N):
     # the normalized row has unit RMS whatever x's scale, so the outputs'
     # size is the weights'; E8M0 scales of 2^-13 .. 2^-3 keep every f16 output
     # finite (with scales up to 2^3, MXFP8 rows of K=4096 overflow f16)
-    c5 = _two_row_case(fmt, dtype, K, N, f"rownorm-{fmt}-{dtype}-{K}-{N}", exp_range=(114, 124),
+    c5 = _case(fmt, dtype, K, N, f"rownorm-{fmt}-{dtype}-{K}-{N}", exp_range=(114, 124),
                        B=5)
     rng = workloads.rng_for(76, f"gamma-{fmt}-{dtype}-{K}")
     gamma = workloads.to_storage(rng.uniform(0.5, 1.5, size=K), dtype)
