@@ -595,8 +595,8 @@ __global__ __launch_bounds__(kThreads) void qmv_kernel(LaunchParams p, Geom g) {
 
 // ---------------------------------------------------------------------------
 // One to four activation rows of 16-bit values (NB) against MXFP4 / NVFP4 /
-// MXFP8 weights with K = 2048 * NU: the tile above cut to what this case
-// needs. The block stages its NB x rows in LDS, each in the layout the tile
+// MXFP8 weights or 4-bit affine codes with K = 2048 * NU: the tile above cut
+// to what this case needs. The block stages its NB x rows in LDS, each in the layout the tile
 // gives one row, and every unit is folded against all of them. Each wave
 // takes two rows (its row index is wave-uniform, so row addresses live in
 // scalar registers); lane l takes units l, l + 64, ... of both rows, exactly
@@ -647,6 +647,8 @@ __device__ inline void row_tiles(const LaunchParams& p, const XR& xr, float gmul
     // the end re-read row N - 1; their results are not stored)
     UnitRaw<FMT, BITS, R> u_raw[NU];
     typename F::Raw s_raw[NU][R];
+    // affine: units per scale group, log2 (groups of 32, 64 or 128 codes)
+    const int glog2 = FMT == FMT_AFFINE ? 31 - __builtin_clz((unsigned)p.group >> 5) : 0;
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         const int64_t r = row0 + i < N ? row0 + i : N - 1;
@@ -655,9 +657,14 @@ __device__ inline void row_tiles(const LaunchParams& p, const XR& xr, float gmul
 #pragma unroll
         for (int j = 0; j < NU; ++j) {
             load_words<W, true>(wrow + (lane + 64 * j) * kUnitBytes, u_raw[j].d[i]);
-            // the unit's scale elements (one E8M0 byte, or NVFP4's two E4M3
-            // bytes), read once: nontemporal like the weights
-            if constexpr (FMT == FMT_NVFP4)
+            // the unit's scale elements (one E8M0 byte, NVFP4's two E4M3
+            // bytes, nontemporal like the weights; or its group's affine
+            // scale and bias)
+            if constexpr (FMT == FMT_AFFINE)
+                s_raw[j][i] = F::template global_raw<DT>(
+                    static_cast<const uint8_t*>(p.scales), static_cast<const uint8_t*>(p.biases),
+                    (uint32_t)(r * p.sc_per_row * kEB), lane + 64 * j, glog2);
+            else if constexpr (FMT == FMT_NVFP4)
                 s_raw[j][i].e = __builtin_nontemporal_load(
                     reinterpret_cast<const uint16_t*>(srow) + (lane + 64 * j));
             else
@@ -672,7 +679,7 @@ __device__ inline void row_tiles(const LaunchParams& p, const XR& xr, float gmul
         for (int j = 0; j < NU; ++j) {
             const int v = tid + j * kThreads;
             *reinterpret_cast<v4u*>(xs + b * XS + x_lds_slot(v * 8, USP)) =
-                xr.stage(b, (int64_t)v * 8, xc[b][j]);
+                stage_vec<FMT, BITS, DT>(xr.stage(b, (int64_t)v * 8, xc[b][j]));
         }
     xr.staged();
     __syncthreads();
@@ -1765,7 +1772,18 @@ int launch_qmv_mfma(const LaunchParams& p, const NormArgs& na, hipStream_t st);
 // Two weight rows per wave at every batch size (four rows per wave at B=3 and
 // B=4 ran 9-15 % slower: half the waves, each with twice the loads and decode
 // before its first product).
+// The one-row kernel's instances: 16-bit x with the MX formats or 4-bit affine
+// codes (each lane loads its units' scale and bias elements; x is staged in
+// the packed path's pair order). 4-bit affine g64 at K = N = 4096 against the
+// VALU tile (us, tile / one-row kernel, one process): bf16 B=1 4.62 / 4.00,
+// B=2 5.38 / 4.78, B=3 6.24 / 5.39, B=4 7.03 / 6.10; f16 B=1 4.43 / 3.98, B=4
+// 6.63 / 5.67; the fused RMSNorm bf16 B=1 5.19 / 4.60, B=4 9.55 / 8.63.
+template <int DT, int FMT, int BITS> constexpr bool row_kernel_ok() {
+    return DT != DT_F32 && (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8 ||
+                            (FMT == FMT_AFFINE && BITS == 4));
+}
 template <int DT, int FMT> constexpr int row_max_batch() {
+    if constexpr (FMT == FMT_AFFINE) return 4;
     if constexpr (DT == DT_BF16) return FMT == FMT_MXFP4 ? 2 : FMT == FMT_NVFP4 ? 3 : 4;
     return 4;
 }
@@ -1806,7 +1824,7 @@ int launch_row_norm_nu(const LaunchParams& p, const NormArgs& na, hipStream_t st
 // squares), so fewer, taller blocks do less of it.
 template <int DT, int FMT, int BITS>
 int launch_qmv_norm_t(const LaunchParams& p, const NormArgs& na, hipStream_t st) {
-    if constexpr (DT != DT_F32 && (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
+    if constexpr (row_kernel_ok<DT, FMT, BITS>()) {
         if (p.B <= row_norm_max_batch<DT, FMT>() && p.N > 0 && p.K > 0 && p.K % 2048 == 0 &&
             p.K / 2048 <= row_units_max<FMT>()) {
             if (p.K == 2048) return launch_row_norm_nu<DT, FMT, BITS, 1>(p, na, st);
@@ -2394,7 +2412,7 @@ int launch_row_nu(const LaunchParams& p, hipStream_t st) {
 
 template <int DT, int FMT, int BITS>
 int launch_qmv_t(const LaunchParams& p, hipStream_t st) {
-    if constexpr (DT != DT_F32 && (FMT == FMT_MXFP4 || FMT == FMT_NVFP4 || FMT == FMT_MXFP8)) {
+    if constexpr (row_kernel_ok<DT, FMT, BITS>()) {
         if (p.B <= row_max_batch<DT, FMT>() && p.N > 0 && p.K > 0 && p.K % 2048 == 0 &&
             p.K / 2048 <= row_units_max<FMT>()) {
             if (p.K == 2048) return launch_row_nu<DT, FMT, BITS, 1>(p, st);

@@ -184,3 +184,59 @@ def test_row_norm_kernel_equals_tile_and_definition(bmv, fmt, dtype, K, N):
         A_def = oracle.rmsnorm_qmv_abs(x5[b:b + 1], dtype, gamma, eps, W)
         check_fused_norm(y1[b:b + 1], y_def, A_def, dtype,
                          f"row norm kernel {fmt} {dtype} K={K} N={N} row {b}")
+
+
+# ---------------------------------------------------------------------------
+# 4-bit affine codes with 16-bit x (groups of 32, 64 and 128) on the one-row
+# kernel at B <= 4; affine never takes the matrix cores, so a five-row call
+# runs the VALU tile, whose rows must equal the one-row calls bit for bit
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("group", [32, 64, 128])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("K,N", [(2048, 77), (4096, 301)])
+def test_row_kernel_affine4(bmv, group, dtype, K, N):
+    c = workloads.affine_case(75, f"row-aff-{group}-{dtype}-{K}-{N}", bits=4, group=group, K=K,
+                              N=N, B=5, dtype=dtype)
+    say(f"row kernel affine 4-bit g{group} {dtype} K={K} N={N}")
+    y1 = _one_row_calls(bmv, c)
+    for B in range(2, 6):
+        yb = to_host(run_qmv(bmv, dataclasses.replace(c, B=B, x=c.x[:B].copy())), dtype)
+        assert np.array_equal(_bits(yb, dtype), _bits(y1[:B], dtype)), \
+            f"affine g{group} {dtype} K={K}: a row of the {B}-row call differs from its one-row call"
+    rows = sample_rows(N, 64, seed=K + N + group)
+    for b in (0, 3):
+        cb = dataclasses.replace(c, B=1, x=c.x[b:b + 1].copy())
+        y64, A = oracle_rows(cb, rows)
+        check(y1[b:b + 1, rows], y64, A, dtype, f"row kernel affine g{group} {dtype} K={K} row {b}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_row_norm_kernel_affine4(bmv, dtype):
+    """The fused RMSNorm + QMV of 4-bit affine codes on the one-row kernel:
+    batch rows equal one-row calls bit for bit up to B = 4 and so do the
+    fused VALU tile's rows at B = 5; the one-row calls meet the plain
+    definition within the staging bound."""
+    from gpu_util import case_to_dev, check_fused_norm, to_dev
+    K, N = 4096, 301
+    c = workloads.affine_case(75, f"rownorm-aff-{dtype}", bits=4, group=64, K=K, N=N, B=5,
+                              dtype=dtype)
+    gamma = workloads.to_storage(workloads.rng_for(76, f"gamma-aff-{dtype}").uniform(0.5, 1.5, size=K),
+                                 dtype)
+    x5 = workloads.to_storage(oracle.storage_to_f64(c.x, dtype) * 3.0, dtype)
+    d = case_to_dev(c)
+    wt = bmv.make_weights("affine", d["w"], d["scales"], d["biases"], K=K, bits=4, group_size=64)
+    say(f"row norm kernel affine 4-bit g64 {dtype} K={K} N={N}")
+
+    def call(x):
+        return to_host(bmv.qmv_rmsnorm_qmv(to_dev(x.copy(), dtype), wt, to_dev(gamma, dtype), 1e-6),
+                       dtype)
+
+    y1 = np.stack([call(x5[b:b + 1])[0] for b in range(5)])
+    for B in range(2, 6):
+        assert np.array_equal(_bits(call(x5[:B]), dtype), _bits(y1[:B], dtype)), \
+            f"affine {dtype}: a row of the {B}-row fused call differs from its one-row call"
+    W = oracle.dequant("affine", K, c.w, c.scales, c.biases, bits=4, group=64, dtype=dtype)
+    y_def = oracle.rmsnorm_qmv(x5[:1], dtype, gamma, 1e-6, W)
+    A_def = oracle.rmsnorm_qmv_abs(x5[:1], dtype, gamma, 1e-6, W)
+    check_fused_norm(y1[:1], y_def, A_def, dtype, f"row norm kernel affine {dtype}")
